@@ -1,0 +1,276 @@
+"""Plain float64 CPU oracle (test infrastructure only; see the package docstring).
+
+Parity pins for every function here live in ``tests/test_oracle_pins.py``.
+
+Sources (pages as titled; section names as they appear there):
+- "Continuous Decode Batching - the transformer capture": the decode step
+  ("decode_step_batch - paint-by-numbers": per-sequence slab, RoPE at t_s,
+  append at t_s, keys [0..=t_s], lm_head per token, then t_s += 1) and the
+  segmented prefill ("REVISED: the hard kernel already exists": K segments in
+  one pass, segment-local causal attention, no cross-segment leakage).
+- mlx-bun "Batching" design note, section 5 ("per-sequence position"): one
+  position per row, captured once per step and used for both Q and K.
+- mlx-bun "Batching" design note (later revision), section 8: greedy argmax
+  selects the lowest vocabulary id among tied scores.
+
+Readings where the pages are silent (the pages never spell out the decoder
+body; the plainest Llama/Mistral reading is taken):
+- RMSNorm: y = x / sqrt(mean(x^2) + eps) * g.
+- RoPE: rotate-half pairing (i, i + Dh/2), angle t * theta^(-2i/Dh), no scaling.
+- GQA: query head h reads kv head floor(h / (Hq/Hkv)); scores scaled by 1/sqrt(Dh).
+- SwiGLU FFN: W_down (silu(W_gate b) * (W_up b)), silu(z) = z / (1 + e^-z).
+- Storage: K and V are rounded to bf16 (nearest-even) when written to a slab
+  and attention reads the rounded values, so a prefill and the same tokens
+  fed one at a time through decode attend to identical keys.
+- int4 affine weights: w = scale * code + bias per group of consecutive
+  input-dimension elements.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------- number formats
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as float64."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even, in one step.
+
+    bf16 keeps 8 significant bits. Writing |x| = m * 2^e with 0.5 <= m < 1,
+    the bf16 neighbours are multiples of 2^(e-8), so the result is
+    rint(m * 2^8) * 2^(e-8) (numpy's rint rounds half to even). Values below
+    the bf16 normal range are not expected here and are not treated
+    specially."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """bf16 bit pattern of float64 values (rounded with :func:`round_to_bf16`)."""
+    r = round_to_bf16(x).astype(np.float32)  # exact: bf16 values are fp32 values
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------- building blocks
+
+def rmsnorm(x, g, eps: float) -> np.ndarray:
+    """RMS normalisation over the last axis with gain g."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
+
+
+def rope_angles(position: int, head_dim: int, theta: float) -> np.ndarray:
+    """Rotation angles of the Dh/2 pairs at one position: t * theta^(-2i/Dh)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = np.power(float(theta), -2.0 * i / head_dim)
+    return float(position) * inv_freq
+
+
+def apply_rope(x, position: int, theta: float) -> np.ndarray:
+    """Rotate every head vector in x[..., Dh] to position t (rotate-half pairing).
+
+    Pair i is (x[i], x[i + Dh/2]); it is rotated by angle a_i:
+    (x1, x2) -> (x1 cos a - x2 sin a, x2 cos a + x1 sin a)."""
+    x = np.asarray(x, dtype=np.float64)
+    dh = x.shape[-1]
+    a = rope_angles(position, dh, theta)
+    c, s = np.cos(a), np.sin(a)
+    x1, x2 = x[..., : dh // 2], x[..., dh // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def attend_one_head(q, keys, values) -> np.ndarray:
+    """softmax(q . K^T / sqrt(Dh)) V for one query vector over all given keys."""
+    q = np.asarray(q, dtype=np.float64)
+    scores = keys @ q / np.sqrt(q.shape[-1])
+    m = np.max(scores)
+    p = np.exp(scores - m)
+    p = p / np.sum(p)
+    return p @ values
+
+
+def silu(z) -> np.ndarray:
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def dequant_int4(codes, scale_bits, bias_bits, group: int) -> np.ndarray:
+    """w[n, k] = scale[n, k // group] * code[n, k] + bias[n, k // group] (float64)."""
+    codes = np.asarray(codes)
+    s = np.repeat(bf16_bits_to_f64(scale_bits), group, axis=1)
+    b = np.repeat(bf16_bits_to_f64(bias_bits), group, axis=1)
+    return s * codes.astype(np.float64) + b
+
+
+def greedy(logits) -> np.ndarray:
+    """Per-row argmax; among equal maxima the lowest vocabulary id wins."""
+    logits = np.atleast_2d(np.asarray(logits))
+    out = np.empty(logits.shape[0], dtype=np.int64)
+    for r in range(logits.shape[0]):
+        row = logits[r]
+        best = 0
+        for v in range(1, row.shape[0]):
+            if row[v] > row[best]:
+                best = v
+        out[r] = best
+    return out
+
+
+# --------------------------------------------------------------------------- sequence state
+
+@dataclass
+class SeqState:
+    """One sequence's persistent slab: per-layer K and V (bf16 bits, [len, Hkv, Dh])."""
+    k: List[np.ndarray]
+    v: List[np.ndarray]
+
+    @property
+    def length(self) -> int:
+        return int(self.k[0].shape[0])
+
+
+# --------------------------------------------------------------------------- the model
+
+class OracleModel:
+    """Random-init decoder evaluated row by row in float64.
+
+    ``weights`` is the dict produced by ``synth.make_weights`` (bf16 bit
+    patterns, or int4 dicts with ``codes``/``scale``/``bias``)."""
+
+    def __init__(self, weights: Dict, cache_all_layers: bool = False):
+        self.w = weights
+        self.cfg = weights["shape"]
+        self.seqs: Dict[int, SeqState] = {}
+        self._next_id = 0
+        self._cache: Dict = {}
+        self._cache_all = cache_all_layers
+
+    # -- weights
+    def _matrix(self, m) -> np.ndarray:
+        if isinstance(m, dict):
+            return dequant_int4(m["codes"], m["scale"], m["bias"], self.cfg.group_size)
+        return bf16_bits_to_f64(m)
+
+    def dense(self, layer: int, name: str) -> np.ndarray:
+        key = (layer, name)
+        if key not in self._cache:
+            if not self._cache_all:
+                self._cache = {k: v for k, v in self._cache.items() if k[0] == layer}
+            src = self.w[name] if layer < 0 else self.w["layers"][layer][name]
+            self._cache[key] = self._matrix(src) if name not in ("attn_norm", "ffn_norm", "final_norm") \
+                else bf16_bits_to_f64(src)
+        return self._cache[key]
+
+    def embed_rows(self, tokens) -> np.ndarray:
+        return bf16_bits_to_f64(self.w["embed"][np.asarray(tokens, dtype=np.int64)])
+
+    # -- sequences
+    def new_sequence(self) -> int:
+        c = self.cfg
+        sid = self._next_id
+        self._next_id += 1
+        empty = lambda: np.zeros((0, c.n_kv_heads, c.head_dim), dtype=np.uint16)
+        self.seqs[sid] = SeqState([empty() for _ in range(c.n_layers)], [empty() for _ in range(c.n_layers)])
+        return sid
+
+    def free_sequence(self, sid: int) -> None:
+        del self.seqs[sid]
+
+    def append_history(self, sid: int, k_bits, v_bits) -> None:
+        """Append given K/V (bf16 bits, [L, n, Hkv, Dh]) to a slab."""
+        s = self.seqs[sid]
+        for l in range(self.cfg.n_layers):
+            s.k[l] = np.concatenate([s.k[l], np.asarray(k_bits[l], dtype=np.uint16)])
+            s.v[l] = np.concatenate([s.v[l], np.asarray(v_bits[l], dtype=np.uint16)])
+
+    def copy_state(self) -> Dict[int, SeqState]:
+        return {sid: SeqState([a.copy() for a in s.k], [a.copy() for a in s.v]) for sid, s in self.seqs.items()}
+
+    # -- one layer for a set of (row, position) queries
+    def _layer(self, l: int, h: np.ndarray, rows: Sequence[int], positions: Sequence[int]) -> np.ndarray:
+        """Apply decoder layer l to hidden rows h[i] of sequence rows[i] at positions[i].
+
+        Each query i writes its K/V at positions[i] of its own slab, then
+        attends to keys [0..=positions[i]] of that slab only. Queries of one
+        sequence must be listed in increasing position order and the slab
+        must already hold every earlier position."""
+        c = self.cfg
+        g = c.n_heads // c.n_kv_heads
+        a = rmsnorm(h, self.dense(l, "attn_norm"), c.rms_eps)
+        q = (a @ self.dense(l, "wq").T).reshape(len(rows), c.n_heads, c.head_dim)
+        k = (a @ self.dense(l, "wk").T).reshape(len(rows), c.n_kv_heads, c.head_dim)
+        v = (a @ self.dense(l, "wv").T).reshape(len(rows), c.n_kv_heads, c.head_dim)
+        # K/V of every query first (causal, so a later write is never read early)
+        for i, (sid, t) in enumerate(zip(rows, positions)):
+            s = self.seqs[sid]
+            if s.k[l].shape[0] != t:
+                raise ValueError("slab length %d != position %d" % (s.k[l].shape[0], t))
+            kb = f64_to_bf16_bits(apply_rope(k[i], t, c.rope_theta))[None]
+            vb = f64_to_bf16_bits(v[i])[None]
+            s.k[l] = np.concatenate([s.k[l], kb])
+            s.v[l] = np.concatenate([s.v[l], vb])
+        o = np.zeros((len(rows), c.n_heads, c.head_dim))
+        kv_f64 = {}
+        for i, (sid, t) in enumerate(zip(rows, positions)):
+            if sid not in kv_f64:
+                kv_f64[sid] = (bf16_bits_to_f64(self.seqs[sid].k[l]), bf16_bits_to_f64(self.seqs[sid].v[l]))
+            K, V = kv_f64[sid]
+            qr = apply_rope(q[i], t, c.rope_theta)
+            for hh in range(c.n_heads):
+                j = hh // g
+                o[i, hh] = attend_one_head(qr[hh], K[: t + 1, j], V[: t + 1, j])
+        h = h + o.reshape(len(rows), -1) @ self.dense(l, "wo").T
+        b = rmsnorm(h, self.dense(l, "ffn_norm"), c.rms_eps)
+        m = silu(b @ self.dense(l, "w_gate").T) * (b @ self.dense(l, "w_up").T)
+        return h + m @ self.dense(l, "w_down").T
+
+    def _head(self, h: np.ndarray) -> np.ndarray:
+        x = rmsnorm(h, self.dense(-1, "final_norm"), self.cfg.rms_eps)
+        return x @ self.dense(-1, "lm_head").T
+
+    # -- the two entry points
+    def decode_step_batch(self, seq_ids: Sequence[int], last_tokens: Sequence[int]) -> np.ndarray:
+        """One decode step for B distinct live sequences; returns logits [B, V].
+
+        Row i uses t = its slab length, writes its K/V at t, attends [0..=t],
+        and its length becomes t + 1."""
+        seq_ids = [int(s) for s in seq_ids]
+        if len(set(seq_ids)) != len(seq_ids):
+            raise ValueError("duplicate sequence id in one step")
+        if not seq_ids:
+            return np.zeros((0, self.cfg.vocab))
+        positions = [self.seqs[s].length for s in seq_ids]
+        h = self.embed_rows(last_tokens)
+        for l in range(self.cfg.n_layers):
+            h = self._layer(l, h, seq_ids, positions)
+        return self._head(h)
+
+    def prefill(self, sid: int, tokens) -> np.ndarray:
+        """Causal forward of one sequence's tokens from its current length; logits of the last token."""
+        tokens = np.asarray(tokens, dtype=np.int64)
+        if tokens.size == 0:
+            raise ValueError("empty segment")
+        t0 = self.seqs[sid].length
+        positions = list(range(t0, t0 + tokens.size))
+        h = self.embed_rows(tokens)
+        for l in range(self.cfg.n_layers):
+            h = self._layer(l, h, [sid] * tokens.size, positions)
+        return self._head(h[-1:])[0]
+
+    def prefill_segmented(self, seq_ids: Sequence[int], segments: Sequence) -> np.ndarray:
+        """K segments, each its own causal forward (no cross-segment attention); logits [K, V]."""
+        if len(set(int(s) for s in seq_ids)) != len(seq_ids):
+            raise ValueError("duplicate sequence id in one prefill")
+        out = [self.prefill(int(s), seg) for s, seg in zip(seq_ids, segments)]
+        return np.stack(out) if out else np.zeros((0, self.cfg.vocab))

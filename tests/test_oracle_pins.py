@@ -1,0 +1,292 @@
+"""Pins of the CPU oracle against closed forms, special cases and brute force.
+
+Each check is chosen so that a plausible mistake in the oracle (a dropped
+term, a wrong sign or index, a transposed operand, a wrong position) fails
+at least one of them. None of them runs the oracle against itself only.
+"""
+import math
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import (OracleModel, apply_rope, attend_one_head, bf16_bits_to_f64, dequant_int4,
+                    f64_to_bf16_bits, greedy, rmsnorm, round_to_bf16, rope_angles, silu)
+from bruteforce import BruteModel
+
+# micro shapes: small enough for the scalar brute force, big enough to have
+# GQA (2 query heads per kv head), non-square matrices and several layers
+MICRO = synth.ModelShape("micro", 2, 8, 4, 2, 4, 12, 19, 10000.0, weight_std=0.4)
+MICRO_INT4 = replace(MICRO, name="micro-int4", weight_format="int4", group_size=4)
+
+
+# --------------------------------------------------------------------------- number formats
+
+def test_bf16_rounding_hand_values():
+    one = 1.0
+    ulp = 2.0 ** -7  # bf16 spacing in [1, 2)
+    assert round_to_bf16(one) == one
+    assert round_to_bf16(one + ulp / 2) == one                # tie -> even (1.0)
+    assert round_to_bf16(one + 3 * ulp / 2) == one + 2 * ulp  # tie -> even (k = 2)
+    assert round_to_bf16(one + ulp / 2 + 1e-12) == one + ulp  # just above the tie
+    assert round_to_bf16(-(one + ulp / 2 + 1e-12)) == -(one + ulp)
+    assert round_to_bf16(3.0 * 2.0 ** 100) == 3.0 * 2.0 ** 100
+    assert f64_to_bf16_bits(1.0) == 0x3F80 and f64_to_bf16_bits(-2.0) == 0xC000
+
+
+def test_bf16_rounding_matches_independent_fp32_rne():
+    """On fp32 inputs the fp64 rounding must agree with the integer bit trick."""
+    x = synth.normal_f32(11, 1, (200_000,), std=3.0)
+    a = f64_to_bf16_bits(x.astype(np.float64))
+    b = synth.f32_to_bf16_bits(x)
+    assert np.array_equal(a, b)
+    assert np.array_equal(bf16_bits_to_f64(a), synth.bf16_bits_to_f32(b).astype(np.float64))
+
+
+def test_bf16_rounding_is_nearest_by_brute_force():
+    rng = np.random.default_rng(5)
+    for x in rng.normal(size=2000) * 10.0 ** rng.integers(-6, 6, size=2000):
+        r = float(round_to_bf16(x))
+        b = int(f64_to_bf16_bits(x))
+        for nb in (b - 1, b + 1):
+            alt = float(bf16_bits_to_f64(np.uint16(nb & 0xFFFF)))
+            assert abs(alt - x) >= abs(r - x)
+
+
+# --------------------------------------------------------------------------- blocks
+
+def test_rmsnorm_hand_example_and_invariant():
+    y = rmsnorm([3.0, 4.0], [1.0, 1.0], 0.0)
+    assert np.allclose(y, [3 / math.sqrt(12.5), 4 / math.sqrt(12.5)], rtol=0, atol=1e-15)
+    y = rmsnorm([3.0, 4.0], [2.0, -1.0], 0.0)
+    assert np.allclose(y, [6 / math.sqrt(12.5), -4 / math.sqrt(12.5)], rtol=0, atol=1e-15)
+    x = np.random.default_rng(0).normal(size=(5, 64)) * 7
+    y = rmsnorm(x, np.ones(64), 1e-5)
+    ms = (x * x).mean(-1)
+    assert np.allclose((y * y).mean(-1), ms / (ms + 1e-5), rtol=1e-12)
+    # eps is added inside the root: an all-zero-but-one vector
+    y = rmsnorm([1.0, 0.0, 0.0, 0.0], np.ones(4), 0.25)
+    assert abs(y[0] - 1.0 / math.sqrt(0.25 + 0.25)) < 1e-15
+
+
+def test_rope_closed_forms():
+    t, theta = 7, 10000.0
+    # Dh = 2: the single pair rotates by t radians
+    assert np.allclose(apply_rope([1.0, 0.0], t, theta), [math.cos(t), math.sin(t)], atol=1e-15)
+    assert np.allclose(apply_rope([0.0, 1.0], t, theta), [-math.sin(t), math.cos(t)], atol=1e-15)
+    # Dh = 4: pairs (0,2) at angle t and (1,3) at angle t * theta^(-1/2)
+    w = t * theta ** -0.5
+    assert np.allclose(apply_rope([1.0, 0, 0, 0], t, theta), [math.cos(t), 0, math.sin(t), 0], atol=1e-15)
+    assert np.allclose(apply_rope([0, 1.0, 0, 0], t, theta), [0, math.cos(w), 0, math.sin(w)], atol=1e-15)
+    assert np.allclose(rope_angles(3, 8, 100.0), [3, 3 / 100 ** 0.25, 3 / 100 ** 0.5, 3 / 100 ** 0.75])
+
+
+def test_rope_identity_norm_and_relative_position():
+    rng = np.random.default_rng(1)
+    q, k = rng.normal(size=128), rng.normal(size=128)
+    assert np.array_equal(apply_rope(q, 0, 5e5), q)
+    assert abs(np.linalg.norm(apply_rope(q, 31999, 5e5)) - np.linalg.norm(q)) < 1e-10
+    for t, u, d in [(5, 2, 100), (0, 9, 3000), (4000, 4000, 17)]:
+        a = apply_rope(q, t, 5e5) @ apply_rope(k, u, 5e5)
+        b = apply_rope(q, t + d, 5e5) @ apply_rope(k, u + d, 5e5)
+        assert abs(a - b) < 1e-9 * (1 + abs(a))
+    # the score genuinely depends on the offset (catches a rope that ignores t)
+    assert abs(apply_rope(q, 3, 5e5) @ apply_rope(k, 0, 5e5) - q @ k) > 1e-6
+
+
+def _brute_attention(q, K, V):
+    dh = len(q)
+    s = [sum(q[d] * K[u][d] for d in range(dh)) / math.sqrt(dh) for u in range(len(K))]
+    m = max(s)
+    e = [math.exp(x - m) for x in s]
+    z = sum(e)
+    return [sum(e[u] * V[u][d] for u in range(len(K))) / z for d in range(len(V[0]))]
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 18, 65])
+@pytest.mark.parametrize("dh", [1, 4, 16])
+def test_attention_brute_force(n, dh):
+    rng = np.random.default_rng(n * 100 + dh)
+    q, K, V = rng.normal(size=dh) * 2, rng.normal(size=(n, dh)), rng.normal(size=(n, dh))
+    o = attend_one_head(q, K, V)
+    ref = _brute_attention(list(q), K.tolist(), V.tolist())
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(2)
+    V = rng.normal(size=(6, 8))
+    assert np.array_equal(attend_one_head(rng.normal(size=8), rng.normal(size=(1, 8)), V[:1]), V[0])
+    K = np.tile(rng.normal(size=8), (6, 1))
+    assert np.allclose(attend_one_head(rng.normal(size=8), K, V), V.mean(0), atol=1e-14)
+    # a dominant key selects its value; scaling by 1/sqrt(Dh) is applied
+    K = np.zeros((3, 4)); K[1] = [100, 0, 0, 0]
+    assert np.allclose(attend_one_head([1.0, 0, 0, 0], K, V[:3, :4]), V[1, :4], atol=1e-20)
+    K = np.zeros((2, 4)); K[0] = [2 * math.log(3.0), 0, 0, 0]
+    p0 = 3.0 / 4.0  # exp(2 ln3 / sqrt(4)) = 3 against exp(0) = 1
+    assert np.allclose(attend_one_head([1.0, 0, 0, 0], K, V[:2, :4]), p0 * V[0, :4] + (1 - p0) * V[1, :4])
+
+
+def test_silu_closed_forms():
+    assert silu(0.0) == 0.0
+    assert abs(silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+    assert abs(silu(-2.0) - (-2.0) / (1.0 + math.exp(2.0))) < 1e-16
+    assert abs(silu(40.0) - 40.0) < 1e-12 and abs(silu(-800.0)) < 1e-300
+
+
+def test_greedy_lowest_id_on_ties():
+    assert list(greedy([[0.0, 2.0, 2.0, 1.0], [5.0, 5.0, 5.0, 5.0], [-3.0, -1.0, -2.0, -1.0]])) == [1, 0, 1]
+    x = np.random.default_rng(3).normal(size=(4, 1000))
+    assert np.array_equal(greedy(x), np.argmax(x, axis=1))
+
+
+def test_dequant_closed_form_and_group_index():
+    codes = np.array([[0, 1, 15, 7, 3, 3, 3, 3]], dtype=np.uint8)
+    scale = f64_to_bf16_bits(np.array([[0.5, 0.25]]))
+    bias = f64_to_bf16_bits(np.array([[-1.0, 2.0]]))
+    w = dequant_int4(codes, scale, bias, 4)
+    assert np.array_equal(w, [[-1.0, -0.5, 6.5, 2.5, 2.75, 2.75, 2.75, 2.75]])
+    m = synth._int4_matrix(1, 9, (16, 128), 64, 0.02)
+    w = dequant_int4(m["codes"], m["scale"], m["bias"], 64)
+    assert abs(w.std() - 0.02) < 0.004 and abs(w.mean()) < 0.002
+    # group 1 of row 3 uses scale[3, 1]
+    s = float(bf16_bits_to_f64(m["scale"][3, 1])); b = float(bf16_bits_to_f64(m["bias"][3, 1]))
+    assert w[3, 64 + 5] == s * int(m["codes"][3, 64 + 5]) + b
+
+
+# --------------------------------------------------------------------------- whole model vs brute force
+
+def _run_trajectory(weights, prompts, steps):
+    """Oracle: prefill each prompt, then greedy decode; brute: same tokens, one at a time."""
+    orc = OracleModel(weights, cache_all_layers=True)
+    ids = [orc.new_sequence() for _ in prompts]
+    lg0 = orc.prefill_segmented(ids, prompts)
+    bf = BruteModel(weights)
+    for i in ids:
+        bf.add_seq(i)
+    brute0 = []
+    for i, p in zip(ids, prompts):
+        for pos, tok in enumerate(p):
+            out = bf.forward_token(i, int(tok), pos)
+        brute0.append(out)
+    assert np.allclose(lg0, np.array(brute0), rtol=1e-10, atol=1e-12)
+    toks = greedy(lg0)
+    for step in range(steps):
+        lg = orc.decode_step_batch(ids, toks)
+        ref = [bf.forward_token(i, int(t), len(p) + step) for i, t, p in zip(ids, toks, prompts)]
+        assert np.allclose(lg, np.array(ref), rtol=1e-10, atol=1e-12)
+        toks = greedy(lg)
+    # slabs: every stored K/V entry equal to the brute force's bf16 values
+    for i in ids:
+        for l in range(weights["shape"].n_layers):
+            Kb = np.array([[kk for kk in ent[0]] for ent in bf.kv[i][l]])
+            assert np.array_equal(bf16_bits_to_f64(orc.seqs[i].k[l]), Kb)
+
+
+@pytest.mark.parametrize("gain_std", [0.0, 0.3])
+def test_oracle_matches_scalar_brute_force_bf16(gain_std):
+    w = synth.make_weights(MICRO, seed=4, gain_std=gain_std)
+    pr = synth.prompts(40, [3, 1, 5], MICRO.vocab)
+    _run_trajectory(w, pr, steps=3)
+
+
+def test_oracle_matches_scalar_brute_force_int4():
+    w = synth.make_weights(MICRO_INT4, seed=6)
+    pr = synth.prompts(41, [4, 2], MICRO_INT4.vocab)
+    _run_trajectory(w, pr, steps=2)
+
+
+# --------------------------------------------------------------------------- the pages' invariants
+
+def _tiny_state(seed=0, lengths=(17, 5, 33, 1)):
+    w = synth.make_weights(synth.TINY, seed=seed, gain_std=0.1)
+    orc = OracleModel(w, cache_all_layers=True)
+    pr = synth.prompts(seed + 100, lengths, synth.TINY.vocab)
+    ids = [orc.new_sequence() for _ in pr]
+    lg = orc.prefill_segmented(ids, pr)
+    return w, orc, ids, pr, lg
+
+
+def test_batched_step_equals_solo_steps():
+    """A batched step of K sequences equals K solo steps (row independence)."""
+    w, orc, ids, pr, lg = _tiny_state()
+    toks = greedy(lg)
+    snap = orc.copy_state()
+    batched = orc.decode_step_batch(ids, toks)
+    for r, (sid, t) in enumerate(zip(ids, toks)):
+        solo = OracleModel(w, cache_all_layers=True)
+        solo.seqs = {sid: snap[sid]}
+        solo_lg = solo.decode_step_batch([sid], [t])[0]
+        assert np.allclose(solo_lg, batched[r], rtol=1e-12, atol=1e-12)
+        for l in range(w["shape"].n_layers):
+            assert np.array_equal(solo.seqs[sid].k[l], orc.seqs[sid].k[l])
+
+
+def test_row_permutation():
+    w, orc, ids, pr, lg = _tiny_state()
+    toks = greedy(lg)
+    snap = orc.copy_state()
+    a = orc.decode_step_batch(ids, toks)
+    orc2 = OracleModel(w, cache_all_layers=True)
+    orc2.seqs = snap
+    perm = [2, 0, 3, 1]
+    b = orc2.decode_step_batch([ids[p] for p in perm], [toks[p] for p in perm])
+    assert np.allclose(b, a[perm], rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_equals_sequential_decode():
+    w = synth.make_weights(synth.TINY, seed=1, gain_std=0.1)
+    pr = synth.prompts(7, [23], synth.TINY.vocab)[0]
+    a = OracleModel(w, cache_all_layers=True)
+    sa = a.new_sequence()
+    la = a.prefill(sa, pr)
+    b = OracleModel(w, cache_all_layers=True)
+    sb = b.new_sequence()
+    for tok in pr:
+        lb = b.decode_step_batch([sb], [tok])[0]
+    assert np.allclose(la, lb, rtol=1e-9, atol=1e-9)
+    for l in range(synth.TINY.n_layers):
+        ka, kb = a.seqs[sa].k[l], b.seqs[sb].k[l]
+        assert ka.shape == kb.shape == (23, 2, 64)
+        diff = np.abs(ka.astype(np.int32) - kb.astype(np.int32))
+        assert (diff == 0).mean() >= 0.999 and diff.max() <= 1
+
+
+def test_no_cross_segment_leakage():
+    """Changing one segment's tokens leaves every other segment's logits and slab bitwise unchanged."""
+    w = synth.make_weights(synth.TINY, seed=2, gain_std=0.1)
+    pr = synth.prompts(8, [9, 14, 6], synth.TINY.vocab)
+    a = OracleModel(w, cache_all_layers=True)
+    ia = [a.new_sequence() for _ in pr]
+    la = a.prefill_segmented(ia, pr)
+    pr2 = [p.copy() for p in pr]
+    pr2[1] = (pr2[1] + 1) % synth.TINY.vocab
+    b = OracleModel(w, cache_all_layers=True)
+    ib = [b.new_sequence() for _ in pr2]
+    lb = b.prefill_segmented(ib, pr2)
+    assert np.array_equal(la[[0, 2]], lb[[0, 2]])
+    assert not np.allclose(la[1], lb[1])
+    for s in (0, 2):
+        for l in range(synth.TINY.n_layers):
+            assert np.array_equal(a.seqs[ia[s]].k[l], b.seqs[ib[s]].k[l])
+            assert np.array_equal(a.seqs[ia[s]].v[l], b.seqs[ib[s]].v[l])
+
+
+def test_decode_uses_own_position_and_history():
+    """Row t_s comes from its own slab; a row attends to nothing of another row."""
+    w = synth.make_weights(synth.TINY, seed=3)
+    o = OracleModel(w, cache_all_layers=True)
+    s0, s1 = o.new_sequence(), o.new_sequence()
+    k, v = synth.kv_history(synth.TINY, 3, 0, 10)
+    o.append_history(s0, k, v)
+    lg = o.decode_step_batch([s0, s1], [5, 5])
+    assert o.seqs[s0].length == 11 and o.seqs[s1].length == 1
+    # same token at different positions with different histories gives different logits
+    assert not np.allclose(lg[0], lg[1])
+    # a fresh row with an empty slab equals the same row run alone
+    solo = OracleModel(w, cache_all_layers=True)
+    t = solo.new_sequence()
+    assert np.allclose(solo.decode_step_batch([t], [5])[0], lg[1], rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        o.decode_step_batch([s0, s0], [1, 2])
