@@ -1,0 +1,753 @@
+// Host runtime of libcbd: slab arena, step planner and the C ABI (include/cbd.h).
+//
+// Page "Continuous Decode Batching - the transformer capture":
+//  - section "1. Native station": one KV slab per live sequence in an arena
+//    keyed by sequence id; admission = fresh slab at length 0; EOS = drop it;
+//    the arena size caps concurrency and the caller queues the rest.
+//  - section "decode_step_batch - paint-by-numbers": t_s is the sequence's
+//    own length, captured once per step on the host and used for RoPE, the
+//    append slot and the attention range; after the step t_s += 1.
+// Failure containment (page "Batching", section 4): arguments are validated
+// before anything is enqueued, so a rejected call changes no slab.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/cbd.h"
+#include "kernels.h"
+
+using namespace cbd;
+
+namespace {
+
+constexpr int kGranuleTokens = 256;
+constexpr int kStagingSlots = 4;
+constexpr int kMaxParts = 4096;
+constexpr int kExtraItems = kMaxParts + 64;
+
+thread_local std::string g_err;
+
+cbd_status fail(cbd_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+cbd_status hip_fail(hipError_t e, const char* what) {
+  return fail(CBD_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                       \
+  do {                                            \
+    hipError_t e_ = (expr);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+struct Mat {
+  const void* data;
+  const void* aux;
+};
+
+struct LayerW {
+  const uint16_t* attn_norm;
+  Mat wq, wk, wv, wo;
+  const uint16_t* ffn_norm;
+  Mat wg, wu, wd;
+};
+
+struct Slab {
+  int64_t off = 0;
+  int32_t cap = 0;
+  int32_t len = 0;
+  int64_t gran_begin = 0, gran_count = 0;
+  bool live = false;
+};
+
+template <class T>
+T* align_ptr(uint8_t*& p, size_t count) {
+  p = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255));
+  T* r = reinterpret_cast<T*>(p);
+  p += sizeof(T) * count;
+  return r;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+}  // namespace
+
+struct cbd_ctx {
+  cbd_model_config cfg{};
+  cbd_limits lim{};
+  int fmt = FMT_BF16;
+  int q_dim = 0, kv_dim = 0, qkv_dim = 0;
+  const uint16_t* embed = nullptr;
+  const uint16_t* final_norm = nullptr;
+  Mat lm_head{};
+  std::vector<LayerW> layers;
+
+  uint8_t* arena = nullptr;
+  size_t arena_bytes = 0;
+  int64_t granule_bytes = 0;
+  int64_t n_granules = 0;
+  std::map<int64_t, int64_t> free_runs;  // first granule -> run length
+  std::vector<Slab> slabs;
+  cbd_stats_t stats{};
+
+  bool host_only = true;
+  int rows_pad = 0;  // activation rows available (multiple of 64)
+  void* ws = nullptr;
+  float* h = nullptr;
+  uint16_t* xa = nullptr;
+  uint16_t* xo = nullptr;
+  uint16_t* xm = nullptr;
+  float* qkv = nullptr;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  float* rope_cs = nullptr;
+  uint8_t* meta_dev = nullptr;  // device copy of one staging slot
+  size_t slot_bytes = 0;
+  uint8_t* staging = nullptr;   // pinned host, kStagingSlots slots
+  hipEvent_t slot_ev[kStagingSlots] = {};
+  int next_slot = 0;
+};
+
+// ----------------------------------------------------------------------------- metadata staging
+
+namespace {
+
+struct MetaLayout {
+  size_t meta_off, items_off, parts_off, idx_off, total;
+};
+
+MetaLayout meta_layout(const cbd_ctx* c) {
+  MetaLayout m;
+  const size_t rows = (size_t)c->rows_pad;
+  m.meta_off = 0;
+  m.items_off = round_up(m.meta_off + rows * sizeof(RowMeta), 256);
+  m.parts_off = round_up(m.items_off + (rows + kExtraItems) * sizeof(AttnItem), 256);
+  m.idx_off = round_up(m.parts_off + rows * sizeof(int32_t) * 2, 256);
+  m.total = round_up(m.idx_off + 64 * sizeof(int32_t), 256);
+  return m;
+}
+
+// Reserve a pinned staging slot whose previous upload has completed.
+uint8_t* staging_slot(cbd_ctx* c, int* slot_out) {
+  const int s = c->next_slot;
+  c->next_slot = (c->next_slot + 1) % kStagingSlots;
+  (void)hipEventSynchronize(c->slot_ev[s]);
+  *slot_out = s;
+  return c->staging + (size_t)s * c->slot_bytes;
+}
+
+cbd_status upload(cbd_ctx* c, int slot, size_t bytes, hipStream_t st) {
+  HIP_TRY(hipMemcpyAsync(c->meta_dev, c->staging + (size_t)slot * c->slot_bytes, bytes, hipMemcpyHostToDevice, st),
+          "metadata upload");
+  HIP_TRY(hipEventRecord(c->slot_ev[slot], st), "event record");
+  return CBD_OK;
+}
+
+bool valid_model(const cbd_model_config* m, std::string* why) {
+  char buf[256];
+  auto bad = [&](const char* s) { *why = s; return false; };
+  if (m->n_layers < 1 || m->d_model < 1 || m->n_heads < 1 || m->n_kv_heads < 1 || m->ffn_dim < 1 || m->vocab < 1)
+    return bad("model sizes must be positive");
+  if (m->head_dim != 64 && m->head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (m->n_heads % m->n_kv_heads) return bad("n_heads must be a multiple of n_kv_heads");
+  const int G = m->n_heads / m->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4) return bad("n_heads / n_kv_heads must be 1, 2 or 4");
+  const int kmul = m->weight_format == CBD_WEIGHTS_INT4 ? 512 : 256;
+  if (m->weight_format != CBD_WEIGHTS_BF16 && m->weight_format != CBD_WEIGHTS_INT4) return bad("unknown weight_format");
+  if (m->d_model % kmul || m->ffn_dim % kmul || (m->n_heads * m->head_dim) % kmul) {
+    snprintf(buf, sizeof buf, "d_model, ffn_dim and n_heads*head_dim must be multiples of %d", kmul);
+    return bad(buf);
+  }
+  if (m->vocab % 16 || (m->n_kv_heads * m->head_dim) % 16) return bad("vocab and kv width must be multiples of 16");
+  if (m->max_position < 1) return bad("max_position must be positive");
+  if (!(m->rms_eps >= 0.f) || !(m->rope_theta > 0.f)) return bad("rms_eps >= 0 and rope_theta > 0 required");
+  return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Build the (row, key range) work items of one decode step: long histories
+// are split so that the grid covers the chip; each split gets a partial slot.
+int plan_decode_items(const cbd_ctx* c, const std::vector<RowMeta>& rows, AttnItem* items, int32_t* row_parts) {
+  int64_t total = 0;
+  for (const RowMeta& r : rows) total += r.pos + 1;
+  const int target_items = std::max<int>((int)rows.size(), 512 / c->cfg.n_kv_heads);
+  int64_t chunk = std::max<int64_t>(256, round_up((total + target_items - 1) / target_items, 64));
+  for (;;) {
+    int64_t slots = 0;
+    for (const RowMeta& r : rows) {
+      const int64_t s = (r.pos + 1 + chunk - 1) / chunk;
+      if (s > 1) slots += s;
+    }
+    if (slots <= kMaxParts) break;
+    chunk *= 2;
+  }
+  int n = 0, slot = 0;
+  for (size_t i = 0; i < rows.size(); ++i) {
+    const int nk = rows[i].pos + 1;
+    const int splits = (int)((nk + chunk - 1) / chunk);
+    if (splits <= 1) {
+      items[n++] = AttnItem{(int32_t)i, 0, nk, -1};
+      row_parts[2 * i] = 0;
+      row_parts[2 * i + 1] = 0;
+    } else {
+      row_parts[2 * i] = slot;
+      row_parts[2 * i + 1] = splits;
+      for (int s = 0; s < splits; ++s) {
+        const int b = (int)(s * chunk), e = (int)std::min<int64_t>(nk, (s + 1) * chunk);
+        items[n++] = AttnItem{(int32_t)i, b, e, slot++};
+      }
+    }
+  }
+  return n;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------- create / destroy
+
+extern "C" size_t cbd_kv_bytes_per_token(const cbd_model_config* cfg) {
+  if (!cfg) return 0;
+  return (size_t)cfg->n_layers * 2 * cfg->n_kv_heads * cfg->head_dim * 2;
+}
+
+extern "C" int32_t cbd_slab_granule_tokens(void) { return kGranuleTokens; }
+
+extern "C" const char* cbd_last_error(void) { return g_err.c_str(); }
+
+static cbd_status setup_weights(cbd_ctx* c, const cbd_weights* w) {
+  auto mat = [&](const cbd_matrix& m, const char* name, Mat* out) -> cbd_status {
+    if (!m.data || !aligned16(m.data)) return fail(CBD_E_INVAL, "weight %s: null or not 16-byte aligned", name);
+    if (c->fmt == FMT_INT4 && (!m.aux || !aligned16(m.aux)))
+      return fail(CBD_E_INVAL, "weight %s: int4 scale/bias pairs missing or misaligned", name);
+    *out = Mat{m.data, m.aux};
+    return CBD_OK;
+  };
+  auto vec = [&](const void* p, const char* name, const uint16_t** out) -> cbd_status {
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 7)) return fail(CBD_E_INVAL, "%s: null or not 8-byte aligned", name);
+    *out = static_cast<const uint16_t*>(p);
+    return CBD_OK;
+  };
+  cbd_status s;
+  if (!w || !w->layers) return fail(CBD_E_INVAL, "weights missing");
+  if ((s = vec(w->embed, "embed", &c->embed))) return s;
+  if ((s = vec(w->final_norm, "final_norm", &c->final_norm))) return s;
+  if ((s = mat(w->lm_head, "lm_head", &c->lm_head))) return s;
+  c->layers.resize(c->cfg.n_layers);
+  for (int l = 0; l < c->cfg.n_layers; ++l) {
+    const cbd_layer_weights& L = w->layers[l];
+    LayerW& o = c->layers[l];
+    if ((s = vec(L.attn_norm, "attn_norm", &o.attn_norm)) || (s = vec(L.ffn_norm, "ffn_norm", &o.ffn_norm)) ||
+        (s = mat(L.wq, "wq", &o.wq)) || (s = mat(L.wk, "wk", &o.wk)) || (s = mat(L.wv, "wv", &o.wv)) ||
+        (s = mat(L.wo, "wo", &o.wo)) || (s = mat(L.w_gate, "w_gate", &o.wg)) || (s = mat(L.w_up, "w_up", &o.wu)) ||
+        (s = mat(L.w_down, "w_down", &o.wd)))
+      return s;
+  }
+  return CBD_OK;
+}
+
+static cbd_status setup_device(cbd_ctx* c) {
+  const cbd_model_config& m = c->cfg;
+  const int rows = std::max(c->lim.max_batch, c->lim.max_prefill_tokens);
+  c->rows_pad = (int)round_up(std::max(rows, 64), 64);
+  const size_t R = (size_t)c->rows_pad;
+  const size_t G = (size_t)m.n_heads;
+  const size_t half = (size_t)m.head_dim / 2;
+  const MetaLayout ml = meta_layout(c);
+  c->slot_bytes = ml.total;
+  size_t bytes = 0;
+  bytes += R * m.d_model * 4 + 256;                 // h
+  bytes += R * m.d_model * 2 + 256;                 // xa
+  bytes += R * c->q_dim * 2 + 256;                  // xo
+  bytes += R * std::max(m.ffn_dim, m.d_model) * 2 + 256;  // xm (also the standalone-linear input)
+  bytes += R * c->qkv_dim * 4 + 256;                // qkv
+  bytes += (size_t)kMaxParts * G * m.head_dim * 4 + 256;  // partial outputs
+  bytes += (size_t)kMaxParts * G * 2 * 4 + 256;     // partial (max, sum)
+  bytes += (size_t)m.max_position * half * 2 * 4 + 256;  // rope table
+  bytes += ml.total + 256;                          // metadata
+  HIP_TRY(hipMalloc(&c->ws, bytes), "workspace allocation");
+  HIP_TRY(hipMemset(c->ws, 0, bytes), "workspace clear");
+  uint8_t* p = static_cast<uint8_t*>(c->ws);
+  c->h = align_ptr<float>(p, R * m.d_model);
+  c->xa = align_ptr<uint16_t>(p, R * m.d_model);
+  c->xo = align_ptr<uint16_t>(p, R * c->q_dim);
+  c->xm = align_ptr<uint16_t>(p, R * std::max(m.ffn_dim, m.d_model));
+  c->qkv = align_ptr<float>(p, R * c->qkv_dim);
+  c->part_o = align_ptr<float>(p, (size_t)kMaxParts * G * m.head_dim);
+  c->part_ml = align_ptr<float>(p, (size_t)kMaxParts * G * 2);
+  c->rope_cs = align_ptr<float>(p, (size_t)m.max_position * half * 2);
+  c->meta_dev = align_ptr<uint8_t>(p, ml.total);
+
+  // RoPE table: angles in double precision, stored as fp32 (cos, sin) pairs
+  std::vector<float> cs((size_t)m.max_position * half * 2);
+  for (int t = 0; t < m.max_position; ++t)
+    for (size_t i = 0; i < half; ++i) {
+      const double inv_freq = std::pow((double)m.rope_theta, -2.0 * (double)i / (double)m.head_dim);
+      const double a = (double)t * inv_freq;
+      cs[((size_t)t * half + i) * 2 + 0] = (float)std::cos(a);
+      cs[((size_t)t * half + i) * 2 + 1] = (float)std::sin(a);
+    }
+  HIP_TRY(hipMemcpy(c->rope_cs, cs.data(), cs.size() * 4, hipMemcpyHostToDevice), "rope table upload");
+  HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&c->staging), c->slot_bytes * kStagingSlots, hipHostMallocDefault),
+          "pinned staging allocation");
+  for (int i = 0; i < kStagingSlots; ++i)
+    HIP_TRY(hipEventCreateWithFlags(&c->slot_ev[i], hipEventDisableTiming), "event create");
+  return CBD_OK;
+}
+
+static void release(cbd_ctx* c) {
+  if (!c) return;
+  if (!c->host_only) {
+    (void)hipDeviceSynchronize();
+    for (int i = 0; i < kStagingSlots; ++i)
+      if (c->slot_ev[i]) (void)hipEventDestroy(c->slot_ev[i]);
+    if (c->staging) (void)hipHostFree(c->staging);
+    if (c->ws) (void)hipFree(c->ws);
+  }
+  delete c;
+}
+
+extern "C" cbd_status cbd_create(const cbd_model_config* cfg, const cbd_weights* weights, const cbd_limits* limits,
+                                 void* kv_arena_dev, size_t arena_bytes, cbd_ctx** out) {
+  if (!cfg || !limits || !out) return fail(CBD_E_INVAL, "cbd_create: null argument");
+  *out = nullptr;
+  std::string why;
+  if (!valid_model(cfg, &why)) return fail(CBD_E_INVAL, "cbd_create: %s", why.c_str());
+  if (limits->max_batch < 1 || limits->max_batch > 64) return fail(CBD_E_INVAL, "max_batch must be in 1..64");
+  if (limits->max_segments < 1 || limits->max_segments > 64) return fail(CBD_E_INVAL, "max_segments must be in 1..64");
+  if (limits->max_prefill_tokens < 1 || limits->max_prefill_tokens > (1 << 20))
+    return fail(CBD_E_INVAL, "max_prefill_tokens must be in 1..2^20");
+  cbd_ctx* c = new cbd_ctx();
+  c->cfg = *cfg;
+  c->lim = *limits;
+  c->host_only = limits->host_only != 0;
+  c->fmt = cfg->weight_format == CBD_WEIGHTS_INT4 ? FMT_INT4 : FMT_BF16;
+  c->q_dim = cfg->n_heads * cfg->head_dim;
+  c->kv_dim = cfg->n_kv_heads * cfg->head_dim;
+  c->qkv_dim = c->q_dim + 2 * c->kv_dim;
+  c->arena = static_cast<uint8_t*>(kv_arena_dev);
+  c->arena_bytes = arena_bytes;
+  c->granule_bytes = (int64_t)kGranuleTokens * (int64_t)cbd_kv_bytes_per_token(cfg);
+  c->n_granules = (int64_t)(arena_bytes / (size_t)c->granule_bytes);
+  if (c->n_granules > 0) c->free_runs[0] = c->n_granules;
+  c->stats.arena_bytes = (int64_t)arena_bytes;
+  cbd_status s = CBD_OK;
+  if (!c->host_only) {
+    if (!kv_arena_dev || (reinterpret_cast<uintptr_t>(kv_arena_dev) & 255)) {
+      s = fail(CBD_E_INVAL, "kv arena must be a 256-byte aligned device pointer");
+    } else if ((s = setup_weights(c, weights)) == CBD_OK) {
+      s = setup_device(c);
+    }
+  }
+  if (s != CBD_OK) {
+    release(c);
+    return s;
+  }
+  *out = c;
+  return CBD_OK;
+}
+
+extern "C" cbd_status cbd_destroy(cbd_ctx* ctx) {
+  if (!ctx) return fail(CBD_E_INVAL, "cbd_destroy: null context");
+  release(ctx);
+  return CBD_OK;
+}
+
+extern "C" cbd_status cbd_stats(const cbd_ctx* ctx, cbd_stats_t* out) {
+  if (!ctx || !out) return fail(CBD_E_INVAL, "cbd_stats: null argument");
+  *out = ctx->stats;
+  return CBD_OK;
+}
+
+// ----------------------------------------------------------------------------- slabs
+
+static cbd_status live_slab(const cbd_ctx* c, int32_t id, const Slab** out) {
+  if (id < 0 || (size_t)id >= c->slabs.size() || !c->slabs[id].live)
+    return fail(CBD_E_BADSEQ, "sequence id %d is not live", id);
+  *out = &c->slabs[id];
+  return CBD_OK;
+}
+
+extern "C" cbd_status kvslab_alloc(cbd_ctx* c, int32_t capacity_tokens, int32_t* seq_id_out) {
+  if (!c || !seq_id_out) return fail(CBD_E_INVAL, "kvslab_alloc: null argument");
+  if (capacity_tokens < 1) return fail(CBD_E_INVAL, "kvslab_alloc: capacity must be >= 1");
+  if (capacity_tokens > c->cfg.max_position)
+    return fail(CBD_E_CAPACITY, "kvslab_alloc: capacity %d exceeds max_position %d", capacity_tokens,
+                c->cfg.max_position);
+  const int64_t need = (capacity_tokens + kGranuleTokens - 1) / kGranuleTokens;
+  if (need > c->n_granules)
+    return fail(CBD_E_CAPACITY, "kvslab_alloc: %lld granules exceed the whole arena (%lld)", (long long)need,
+                (long long)c->n_granules);
+  auto it = c->free_runs.begin();
+  for (; it != c->free_runs.end(); ++it)
+    if (it->second >= need) break;
+  if (it == c->free_runs.end()) return fail(CBD_E_NOSPACE, "kvslab_alloc: no free run of %lld granules", (long long)need);
+  const int64_t first = it->first, run = it->second;
+  c->free_runs.erase(it);
+  if (run > need) c->free_runs[first + need] = run - need;
+  int32_t id = 0;
+  while ((size_t)id < c->slabs.size() && c->slabs[id].live) ++id;
+  if ((size_t)id == c->slabs.size()) c->slabs.emplace_back();
+  Slab& s = c->slabs[id];
+  s.live = true;
+  s.len = 0;
+  s.cap = (int32_t)std::min<int64_t>(need * kGranuleTokens, c->cfg.max_position);
+  s.gran_begin = first;
+  s.gran_count = need;
+  s.off = first * c->granule_bytes;
+  c->stats.live_seqs += 1;
+  c->stats.arena_bytes_used += need * c->granule_bytes;
+  *seq_id_out = id;
+  return CBD_OK;
+}
+
+extern "C" cbd_status kvslab_free(cbd_ctx* c, int32_t seq_id) {
+  if (!c) return fail(CBD_E_INVAL, "kvslab_free: null context");
+  const Slab* sp;
+  if (cbd_status st = live_slab(c, seq_id, &sp)) return st;
+  Slab& s = c->slabs[seq_id];
+  int64_t first = s.gran_begin, count = s.gran_count;
+  auto next = c->free_runs.lower_bound(first);
+  if (next != c->free_runs.end() && next->first == first + count) {
+    count += next->second;
+    c->free_runs.erase(next);
+  }
+  auto prev = c->free_runs.lower_bound(first);
+  if (prev != c->free_runs.begin()) {
+    --prev;
+    if (prev->first + prev->second == first) {
+      first = prev->first;
+      count += prev->second;
+      c->free_runs.erase(prev);
+    }
+  }
+  c->free_runs[first] = count;
+  c->stats.live_seqs -= 1;
+  c->stats.arena_bytes_used -= s.gran_count * c->granule_bytes;
+  s = Slab{};
+  return CBD_OK;
+}
+
+extern "C" cbd_status kvslab_len(const cbd_ctx* c, int32_t seq_id, int32_t* len_out) {
+  if (!c || !len_out) return fail(CBD_E_INVAL, "kvslab_len: null argument");
+  const Slab* s;
+  if (cbd_status st = live_slab(c, seq_id, &s)) return st;
+  *len_out = s->len;
+  return CBD_OK;
+}
+
+extern "C" cbd_status kvslab_capacity(const cbd_ctx* c, int32_t seq_id, int32_t* cap_out) {
+  if (!c || !cap_out) return fail(CBD_E_INVAL, "kvslab_capacity: null argument");
+  const Slab* s;
+  if (cbd_status st = live_slab(c, seq_id, &s)) return st;
+  *cap_out = s->cap;
+  return CBD_OK;
+}
+
+extern "C" cbd_status kvslab_append(cbd_ctx* c, int32_t seq_id, int32_t n_tokens, const void* k_dev,
+                                    const void* v_dev, cbd_stream stream) {
+  if (!c) return fail(CBD_E_INVAL, "kvslab_append: null context");
+  const Slab* s;
+  if (cbd_status st = live_slab(c, seq_id, &s)) return st;
+  if (n_tokens < 0) return fail(CBD_E_INVAL, "kvslab_append: negative count");
+  if ((int64_t)s->len + n_tokens > s->cap)
+    return fail(CBD_E_CAPACITY, "kvslab_append: %d + %d exceeds capacity %d", s->len, n_tokens, s->cap);
+  if (n_tokens == 0) return CBD_OK;
+  if (!k_dev || !v_dev || !aligned16(k_dev) || !aligned16(v_dev))
+    return fail(CBD_E_INVAL, "kvslab_append: K/V must be 16-byte aligned device pointers");
+  if (c->host_only) return fail(CBD_E_NODEVICE, "kvslab_append: host-only context");
+  HIP_TRY(launch_slab_copy(c->arena, s->off, s->cap, s->len, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
+                           c->cfg.head_dim, static_cast<const uint16_t*>(k_dev), static_cast<const uint16_t*>(v_dev),
+                           nullptr, nullptr, static_cast<hipStream_t>(stream)),
+          "kvslab_append launch");
+  c->slabs[seq_id].len += n_tokens;
+  return CBD_OK;
+}
+
+extern "C" cbd_status kvslab_read(const cbd_ctx* c, int32_t seq_id, int32_t start, int32_t n_tokens, void* k_out_dev,
+                                  void* v_out_dev, cbd_stream stream) {
+  if (!c) return fail(CBD_E_INVAL, "kvslab_read: null context");
+  const Slab* s;
+  if (cbd_status st = live_slab(c, seq_id, &s)) return st;
+  if (start < 0 || n_tokens < 0) return fail(CBD_E_INVAL, "kvslab_read: negative range");
+  if ((int64_t)start + n_tokens > s->len)
+    return fail(CBD_E_CAPACITY, "kvslab_read: [%d, %d) beyond length %d", start, start + n_tokens, s->len);
+  if (n_tokens == 0) return CBD_OK;
+  if (!k_out_dev || !v_out_dev || !aligned16(k_out_dev) || !aligned16(v_out_dev))
+    return fail(CBD_E_INVAL, "kvslab_read: outputs must be 16-byte aligned device pointers");
+  if (c->host_only) return fail(CBD_E_NODEVICE, "kvslab_read: host-only context");
+  HIP_TRY(launch_slab_copy(c->arena, s->off, s->cap, start, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
+                           c->cfg.head_dim, nullptr, nullptr, static_cast<uint16_t*>(k_out_dev),
+                           static_cast<uint16_t*>(v_out_dev), static_cast<hipStream_t>(stream)),
+          "kvslab_read launch");
+  return CBD_OK;
+}
+
+// ----------------------------------------------------------------------------- the layer stack
+
+namespace {
+
+SkinnyArgs gemm_args(const cbd_ctx* c, const uint16_t* x, int K, int rows, std::initializer_list<Mat> segs,
+                     std::initializer_list<int> seg_rows, int N) {
+  SkinnyArgs a{};
+  a.x = x;
+  a.ldx = K;
+  a.K = K;
+  a.rows = rows;
+  a.N = N;
+  int i = 0, acc = 0;
+  auto r = seg_rows.begin();
+  for (const Mat& m : segs) {
+    a.w[i] = m.data;
+    a.aux[i] = m.aux;
+    acc += *r++;
+    a.seg_end[i] = acc;
+    ++i;
+  }
+  for (; i < 3; ++i) a.seg_end[i] = 0x7FFFFFFF;
+  (void)c;
+  return a;
+}
+
+// Every layer for `rows` query rows whose metadata/items are already on the device.
+cbd_status run_layers(cbd_ctx* c, int rows, int x_blocks, const RowMeta* meta_d, const AttnItem* items_d, int n_items,
+                      const int32_t* row_parts_d, bool any_split, hipStream_t st) {
+  const cbd_model_config& m = c->cfg;
+  for (int l = 0; l < m.n_layers; ++l) {
+    const LayerW& L = c->layers[l];
+    SkinnyArgs a = gemm_args(c, c->xa, m.d_model, rows, {L.wq, L.wk, L.wv}, {c->q_dim, c->kv_dim, c->kv_dim},
+                             c->qkv_dim);
+    a.out = c->qkv;
+    a.ldo = c->qkv_dim;
+    HIP_TRY(launch_skinny_gemm(a, EPI_STORE, c->fmt, x_blocks, st), "qkv projection");
+    HIP_TRY(launch_rope_append(c->qkv, c->qkv_dim, meta_d, rows, m.n_heads, m.n_kv_heads, m.head_dim, l, c->arena,
+                               c->rope_cs, st),
+            "rope/append");
+    HIP_TRY(launch_attention(c->qkv, c->qkv_dim, meta_d, items_d, n_items, m.n_heads, m.n_kv_heads, m.head_dim, l,
+                             c->arena, c->xo, c->q_dim, c->part_o, c->part_ml, kMaxParts, st),
+            "attention");
+    if (any_split)
+      HIP_TRY(launch_attn_combine(c->part_o, c->part_ml, row_parts_d, rows, m.n_heads, m.head_dim, kMaxParts, c->xo,
+                                  c->q_dim, st),
+              "attention combine");
+    a = gemm_args(c, c->xo, c->q_dim, rows, {L.wo}, {m.d_model}, m.d_model);
+    a.out = c->h;
+    a.ldo = m.d_model;
+    HIP_TRY(launch_skinny_gemm(a, EPI_RESIDUAL, c->fmt, x_blocks, st), "o projection");
+    HIP_TRY(launch_rmsnorm(c->h, nullptr, rows, m.d_model, L.ffn_norm, m.rms_eps, c->xa, st), "ffn norm");
+    a = gemm_args(c, c->xa, m.d_model, rows, {L.wg, L.wu}, {m.ffn_dim, m.ffn_dim}, m.ffn_dim);
+    a.out_bf16 = c->xm;
+    a.ldo = m.ffn_dim;
+    HIP_TRY(launch_skinny_gemm(a, EPI_SWIGLU, c->fmt, x_blocks, st), "gate/up projection");
+    a = gemm_args(c, c->xm, m.ffn_dim, rows, {L.wd}, {m.d_model}, m.d_model);
+    a.out = c->h;
+    a.ldo = m.d_model;
+    HIP_TRY(launch_skinny_gemm(a, EPI_RESIDUAL, c->fmt, x_blocks, st), "down projection");
+    const uint16_t* next_gain = (l + 1 < m.n_layers) ? c->layers[l + 1].attn_norm : nullptr;
+    if (next_gain)
+      HIP_TRY(launch_rmsnorm(c->h, nullptr, rows, m.d_model, next_gain, m.rms_eps, c->xa, st), "attn norm");
+  }
+  return CBD_OK;
+}
+
+cbd_status run_head(cbd_ctx* c, const int32_t* row_idx_d, int rows, float* logits, int32_t* next_tokens,
+                    hipStream_t st) {
+  const cbd_model_config& m = c->cfg;
+  HIP_TRY(launch_rmsnorm(c->h, row_idx_d, rows, m.d_model, c->final_norm, m.rms_eps, c->xa, st), "final norm");
+  SkinnyArgs a = gemm_args(c, c->xa, m.d_model, rows, {c->lm_head}, {m.vocab}, m.vocab);
+  a.out = logits;
+  a.ldo = m.vocab;
+  HIP_TRY(launch_skinny_gemm(a, EPI_STORE, c->fmt, 1, st), "lm_head");
+  if (next_tokens) HIP_TRY(launch_argmax(logits, rows, m.vocab, next_tokens, st), "argmax");
+  return CBD_OK;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------- hot path
+
+extern "C" cbd_status decode_step_batch(cbd_ctx* c, const int32_t* seq_ids, int32_t B, const int32_t* last_tokens_dev,
+                                        float* logits_dev, int32_t* next_tokens_dev, cbd_stream stream) {
+  if (!c) return fail(CBD_E_INVAL, "decode_step_batch: null context");
+  if (B < 0 || B > c->lim.max_batch) return fail(CBD_E_INVAL, "decode_step_batch: B=%d outside 0..%d", B, c->lim.max_batch);
+  if (B == 0) return CBD_OK;
+  if (!seq_ids || !last_tokens_dev || !logits_dev) return fail(CBD_E_INVAL, "decode_step_batch: null pointer");
+  if (!aligned16(logits_dev)) return fail(CBD_E_INVAL, "decode_step_batch: logits must be 16-byte aligned");
+  std::vector<RowMeta> rows(B);
+  for (int i = 0; i < B; ++i) {
+    const Slab* s;
+    if (cbd_status st = live_slab(c, seq_ids[i], &s)) return st;
+    for (int j = 0; j < i; ++j)
+      if (seq_ids[j] == seq_ids[i]) return fail(CBD_E_INVAL, "decode_step_batch: duplicate sequence id %d", seq_ids[i]);
+    if (s->len + 1 > s->cap)
+      return fail(CBD_E_CAPACITY, "decode_step_batch: sequence %d is full (%d tokens)", seq_ids[i], s->cap);
+    if (s->len + 1 > c->cfg.max_position)
+      return fail(CBD_E_CAPACITY, "decode_step_batch: sequence %d reached max_position", seq_ids[i]);
+    rows[i] = RowMeta{s->off, s->cap, s->len};
+  }
+  if (c->host_only) return fail(CBD_E_NODEVICE, "decode_step_batch: host-only context");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int slot;
+  uint8_t* host = staging_slot(c, &slot);
+  // packed per-call layout: rows | items | row_parts (offsets rounded to 256 bytes)
+  const size_t items_off = round_up((int64_t)B * sizeof(RowMeta), 256);
+  AttnItem* items = reinterpret_cast<AttnItem*>(host + items_off);
+  std::vector<int32_t> row_parts(2 * B);
+  std::memcpy(host, rows.data(), B * sizeof(RowMeta));
+  const int n_items = plan_decode_items(c, rows, items, row_parts.data());
+  const size_t parts_off = round_up(items_off + (size_t)n_items * sizeof(AttnItem), 256);
+  std::memcpy(host + parts_off, row_parts.data(), row_parts.size() * sizeof(int32_t));
+  bool any_split = false;
+  for (int i = 0; i < B; ++i) any_split |= row_parts[2 * i + 1] > 0;
+  if (cbd_status s = upload(c, slot, parts_off + row_parts.size() * sizeof(int32_t), st)) return s;
+  const RowMeta* meta_d = reinterpret_cast<const RowMeta*>(c->meta_dev);
+  const AttnItem* items_d = reinterpret_cast<const AttnItem*>(c->meta_dev + items_off);
+  const int32_t* parts_d = reinterpret_cast<const int32_t*>(c->meta_dev + parts_off);
+
+  const cbd_model_config& m = c->cfg;
+  HIP_TRY(launch_embed_norm(last_tokens_dev, B, c->embed, m.vocab, m.d_model, c->layers[0].attn_norm, m.rms_eps,
+                            c->h, c->xa, st),
+          "embed");
+  if (cbd_status s = run_layers(c, B, 1, meta_d, items_d, n_items, parts_d, any_split, st)) return s;
+  if (cbd_status s = run_head(c, nullptr, B, logits_dev, next_tokens_dev, st)) return s;
+  for (int i = 0; i < B; ++i) c->slabs[seq_ids[i]].len += 1;
+  c->stats.decode_steps += 1;
+  c->stats.decode_rows += B;
+  return CBD_OK;
+}
+
+extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, const int32_t* seg_lens, int32_t K,
+                                        const int32_t* tokens_dev, float* last_logits_dev, int32_t* next_tokens_dev,
+                                        cbd_stream stream) {
+  if (!c) return fail(CBD_E_INVAL, "prefill_segmented: null context");
+  if (K < 0 || K > c->lim.max_segments)
+    return fail(CBD_E_INVAL, "prefill_segmented: K=%d outside 0..%d", K, c->lim.max_segments);
+  if (K == 0) return CBD_OK;
+  if (!seq_ids || !seg_lens || !tokens_dev || !last_logits_dev) return fail(CBD_E_INVAL, "prefill_segmented: null pointer");
+  if (!aligned16(last_logits_dev)) return fail(CBD_E_INVAL, "prefill_segmented: logits must be 16-byte aligned");
+  int64_t T = 0;
+  for (int i = 0; i < K; ++i) {
+    const Slab* s;
+    if (cbd_status st = live_slab(c, seq_ids[i], &s)) return st;
+    for (int j = 0; j < i; ++j)
+      if (seq_ids[j] == seq_ids[i]) return fail(CBD_E_INVAL, "prefill_segmented: duplicate sequence id %d", seq_ids[i]);
+    if (seg_lens[i] < 1) return fail(CBD_E_INVAL, "prefill_segmented: segment %d has length %d", i, seg_lens[i]);
+    if (s->len != 0) return fail(CBD_E_INVAL, "prefill_segmented: sequence %d is not empty", seq_ids[i]);
+    if (seg_lens[i] > s->cap || seg_lens[i] > c->cfg.max_position)
+      return fail(CBD_E_CAPACITY, "prefill_segmented: segment of %d tokens exceeds slab %d", seg_lens[i], seq_ids[i]);
+    T += seg_lens[i];
+  }
+  if (T > c->lim.max_prefill_tokens)
+    return fail(CBD_E_INVAL, "prefill_segmented: %lld tokens exceed max_prefill_tokens %d", (long long)T,
+                c->lim.max_prefill_tokens);
+  if (c->host_only) return fail(CBD_E_NODEVICE, "prefill_segmented: host-only context");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int slot;
+  uint8_t* host = staging_slot(c, &slot);
+  // packed per-call layout: rows | items | last-token row indices
+  const size_t items_off = round_up(T * (int64_t)sizeof(RowMeta), 256);
+  const size_t idx_off = round_up(items_off + T * sizeof(AttnItem), 256);
+  RowMeta* rows = reinterpret_cast<RowMeta*>(host);
+  AttnItem* items = reinterpret_cast<AttnItem*>(host + items_off);
+  int32_t* last_idx = reinterpret_cast<int32_t*>(host + idx_off);
+  int g = 0;
+  for (int i = 0; i < K; ++i) {
+    const Slab& s = c->slabs[seq_ids[i]];
+    for (int p = 0; p < seg_lens[i]; ++p, ++g) {
+      rows[g] = RowMeta{s.off, s.cap, p};
+      items[g] = AttnItem{g, 0, p + 1, -1};
+    }
+    last_idx[i] = g - 1;
+  }
+  if (cbd_status s = upload(c, slot, idx_off + K * sizeof(int32_t), st)) return s;
+  const RowMeta* meta_d = reinterpret_cast<const RowMeta*>(c->meta_dev);
+  const AttnItem* items_d = reinterpret_cast<const AttnItem*>(c->meta_dev + items_off);
+  const int32_t* idx_d = reinterpret_cast<const int32_t*>(c->meta_dev + idx_off);
+
+  const cbd_model_config& m = c->cfg;
+  const int x_blocks = (int)((T + 63) / 64);
+  HIP_TRY(launch_embed_norm(tokens_dev, (int)T, c->embed, m.vocab, m.d_model, c->layers[0].attn_norm, m.rms_eps,
+                            c->h, c->xa, st),
+          "embed");
+  if (cbd_status s = run_layers(c, (int)T, x_blocks, meta_d, items_d, (int)T, nullptr, false, st)) return s;
+  if (cbd_status s = run_head(c, idx_d, K, last_logits_dev, next_tokens_dev, st)) return s;
+  for (int i = 0; i < K; ++i) c->slabs[seq_ids[i]].len = seg_lens[i];
+  c->stats.prefill_calls += 1;
+  c->stats.prefill_tokens += T;
+  return CBD_OK;
+}
+
+extern "C" cbd_status greedy_argmax(cbd_ctx* c, const float* logits_dev, int32_t rows, int32_t* tokens_dev,
+                                    cbd_stream stream) {
+  if (!c) return fail(CBD_E_INVAL, "greedy_argmax: null context");
+  if (rows < 0 || rows > 64) return fail(CBD_E_INVAL, "greedy_argmax: rows must be in 0..64");
+  if (rows == 0) return CBD_OK;
+  if (!logits_dev || !tokens_dev || !aligned16(logits_dev)) return fail(CBD_E_INVAL, "greedy_argmax: bad pointer");
+  if (c->host_only) return fail(CBD_E_NODEVICE, "greedy_argmax: host-only context");
+  HIP_TRY(launch_argmax(logits_dev, rows, c->cfg.vocab, tokens_dev, static_cast<hipStream_t>(stream)), "argmax");
+  return CBD_OK;
+}
+
+extern "C" cbd_status cbd_linear(cbd_ctx* c, const cbd_matrix* w, int32_t N, int32_t K, const void* x_dev,
+                                 int32_t rows, float* y_dev, cbd_stream stream) {
+  if (!c || !w || !x_dev || !y_dev) return fail(CBD_E_INVAL, "cbd_linear: null argument");
+  if (rows < 1 || rows > 64) return fail(CBD_E_INVAL, "cbd_linear: rows must be in 1..64");
+  if (N < 16 || N % 16) return fail(CBD_E_INVAL, "cbd_linear: N must be a positive multiple of 16");
+  if (K < 1 || !skinny_shape_ok(c->fmt, K))
+    return fail(CBD_E_INVAL, "cbd_linear: K=%d not supported for this weight format", K);
+  if (K > std::max(c->cfg.ffn_dim, c->cfg.d_model)) return fail(CBD_E_INVAL, "cbd_linear: K above the model width");
+  if (!w->data || !aligned16(w->data) || (c->fmt == FMT_INT4 && (!w->aux || !aligned16(w->aux))) ||
+      !aligned16(y_dev) || !aligned16(x_dev))
+    return fail(CBD_E_INVAL, "cbd_linear: pointers must be 16-byte aligned");
+  if (c->host_only) return fail(CBD_E_NODEVICE, "cbd_linear: host-only context");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // copy the rows into the padded workspace so the column tile never reads past the caller's buffer
+  HIP_TRY(hipMemcpyAsync(c->xm, x_dev, (size_t)rows * K * 2, hipMemcpyDeviceToDevice, st), "cbd_linear input copy");
+  SkinnyArgs a = gemm_args(c, c->xm, K, rows, {Mat{w->data, w->aux}}, {N}, N);
+  a.out = y_dev;
+  a.ldo = N;
+  HIP_TRY(launch_skinny_gemm(a, EPI_STORE, c->fmt, 1, st), "cbd_linear");
+  return CBD_OK;
+}
+
+extern "C" cbd_status cbd_pack_int4(const uint8_t* codes, const uint16_t* scale, const uint16_t* bias, int64_t N,
+                                    int64_t K, uint32_t* packed_out, uint16_t* aux_out) {
+  if (!codes || !scale || !bias || !packed_out || !aux_out) return fail(CBD_E_INVAL, "cbd_pack_int4: null argument");
+  if (N < 1 || K < 128 || K % 128 || N % 16) return fail(CBD_E_INVAL, "cbd_pack_int4: need K % 128 == 0 and N % 16 == 0");
+  const int64_t G = K / 64;
+  for (int64_t n = 0; n < N; ++n) {
+    const uint8_t* row = codes + n * K;
+    uint32_t* out = packed_out + n * (K / 8);
+    for (int64_t b = 0; b < K / 128; ++b)
+      for (int g = 0; g < 4; ++g)
+        for (int j = 0; j < 4; ++j) {
+          uint32_t word = 0;
+          const int64_t base = b * 128 + 64 * (j / 2) + 16 * g + 8 * (j % 2);
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t q = row[base + e];
+            if (q > 15) return fail(CBD_E_INVAL, "cbd_pack_int4: code %u out of range", q);
+            word |= q << (4 * ((e >> 1) + 4 * (e & 1)));
+          }
+          out[b * 16 + 4 * g + j] = word;
+        }
+    for (int64_t gi = 0; gi < G; ++gi) {
+      aux_out[(gi * N + n) * 2 + 0] = scale[n * G + gi];
+      aux_out[(gi * N + n) * 2 + 1] = bias[n * G + gi];
+    }
+  }
+  return CBD_OK;
+}

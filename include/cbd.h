@@ -1,0 +1,268 @@
+/*
+ * cbd.h - C ABI of libcbd.so: continuous-batching transformer decode on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operations (as defined on the page "Continuous Decode Batching - the
+ * transformer capture"):
+ *  - decode_step_batch: section "decode_step_batch - paint-by-numbers" and
+ *    section "1. Native station: per-sequence KV + a batched decode step".
+ *    B live sequences take one step together. Every weight matrix is read
+ *    from HBM once for the whole batch (the page's "throughput law":
+ *    sharedCost = w + L*a instead of L*(w + a)); each row applies RoPE at its
+ *    own position t_s, appends its K/V to its own slab at t_s, attends to
+ *    [0..=t_s] of that slab only, and gets one row of lm_head logits; then
+ *    its length becomes t_s + 1.
+ *  - prefill_segmented: section "REVISED ... forward_batch_segmented". K
+ *    prompts packed into one pass; every projection runs once over all
+ *    tokens; attention is block-diagonal causal (a token attends only to
+ *    earlier tokens of its own segment); positions are segment-local from 0.
+ *    Returns the logits of each segment's last token only.
+ *  - kvslab_alloc / kvslab_free: section "1. Native station": an N-slot KV
+ *    arena keyed by sequence id; admission = fresh slab at length 0, EOS =
+ *    drop the slab; capacity is bounded and the caller queues what does
+ *    not fit (section "2. JS scheduler", "Backpressure").
+ *
+ * Model body (the pages do not spell it out; plainest Llama/Mistral reading):
+ * RMSNorm (y = x / sqrt(mean(x^2) + eps) * g), GQA attention with rotate-half
+ * RoPE (angle t * theta^(-2i/Dh)), scale 1/sqrt(Dh), SwiGLU FFN
+ * (W_down(silu(W_gate x) * W_up x)), final RMSNorm, untied lm_head.
+ *
+ * Numerics: residual stream, softmax and every accumulation in fp32; weight
+ * and activation operands of matrix products in bf16; K/V stored in the
+ * slabs as bf16 (round to nearest even); logits fp32.
+ *
+ * Memory ownership: the caller owns every device buffer it passes (weights,
+ * KV arena, token and logit buffers) and every stream. The library
+ * allocates its own fixed-size device workspace once, in cbd_create, and
+ * frees it in cbd_destroy; no entry point allocates device memory after
+ * that. Pointers named *_dev are device pointers; all others are host.
+ *
+ * Streams: every device operation is enqueued on the given stream (NULL =
+ * the null stream) and returns without waiting. All calls on one context
+ * must be serialized on one stream: the context's workspace is shared.
+ *
+ * Errors: every call returns a cbd_status. Arguments are validated on the
+ * host before anything is enqueued; when a call fails, no slab length and
+ * no slab content changes. cbd_last_error() gives a message for the last
+ * failure on the calling thread. Asynchronous device faults are reported by
+ * the HIP runtime on the next synchronizing call (CBD_E_HIP).
+ */
+#ifndef CBD_H
+#define CBD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct cbd_ctx cbd_ctx;
+typedef void* cbd_stream; /* a hipStream_t */
+
+typedef enum {
+  CBD_OK = 0,
+  CBD_E_INVAL = -1,    /* bad argument (null pointer, size out of range, duplicate id, ...) */
+  CBD_E_NOSPACE = -2,  /* arena cannot hold the slab now: queue the request and retry later */
+  CBD_E_CAPACITY = -3, /* the slab's capacity (or the RoPE table) would be exceeded */
+  CBD_E_BADSEQ = -4,   /* unknown or freed sequence id */
+  CBD_E_HIP = -5,      /* a HIP runtime call failed */
+  CBD_E_NODEVICE = -6  /* context was created host-only: bookkeeping works, device work does not */
+} cbd_status;
+
+enum { CBD_WEIGHTS_BF16 = 0, CBD_WEIGHTS_INT4 = 1 };
+
+typedef struct {
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_heads;      /* query heads */
+  int32_t n_kv_heads;   /* n_heads must be a multiple of n_kv_heads (GQA) */
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t ffn_dim;
+  int32_t vocab;
+  float rms_eps;
+  float rope_theta;
+  int32_t weight_format; /* CBD_WEIGHTS_BF16 or CBD_WEIGHTS_INT4 */
+  int32_t max_position;  /* length of the RoPE table: no slab may grow beyond it */
+} cbd_model_config;
+
+/*
+ * One weight matrix W [N, K] (N outputs, K inputs; y = W x).
+ *  bf16 format: data = bf16 [N, K] row-major; aux unused.
+ *  int4 format (4-bit affine, groups of 64 consecutive inputs of one row,
+ *  w = scale * code + bias with codes 0..15): data = packed codes and aux =
+ *  bf16 (scale, bias) pairs, both in the layout cbd_pack_int4 writes.
+ *  K must be a multiple of 128 for int4.
+ */
+typedef struct {
+  const void* data;
+  const void* aux;
+} cbd_matrix;
+
+typedef struct {
+  const void* attn_norm; /* bf16 [d_model] */
+  cbd_matrix wq;         /* [n_heads*head_dim, d_model] */
+  cbd_matrix wk;         /* [n_kv_heads*head_dim, d_model] */
+  cbd_matrix wv;         /* [n_kv_heads*head_dim, d_model] */
+  cbd_matrix wo;         /* [d_model, n_heads*head_dim] */
+  const void* ffn_norm;  /* bf16 [d_model] */
+  cbd_matrix w_gate;     /* [ffn_dim, d_model] */
+  cbd_matrix w_up;       /* [ffn_dim, d_model] */
+  cbd_matrix w_down;     /* [d_model, ffn_dim] */
+} cbd_layer_weights;
+
+typedef struct {
+  const void* embed;                /* bf16 [vocab, d_model]; gathered, never streamed */
+  const void* final_norm;           /* bf16 [d_model] */
+  cbd_matrix lm_head;               /* [vocab, d_model] */
+  const cbd_layer_weights* layers;  /* host array [n_layers]; copied by cbd_create */
+} cbd_weights;
+
+typedef struct {
+  int32_t max_batch;          /* rows per decode_step_batch call, 1..64 */
+  int32_t max_prefill_tokens; /* sum of segment lengths per prefill_segmented call */
+  int32_t max_segments;       /* segments per prefill_segmented call, 1..64 */
+  int32_t host_only;          /* nonzero: no device memory, no kernels (host bookkeeping tests) */
+} cbd_limits;
+
+typedef struct {
+  int64_t live_seqs;
+  int64_t arena_bytes;
+  int64_t arena_bytes_used;
+  int64_t decode_steps;
+  int64_t decode_rows;
+  int64_t prefill_calls;
+  int64_t prefill_tokens;
+} cbd_stats_t;
+
+/* Bytes of K and V (bf16) one token occupies in a slab, over all layers:
+ * n_layers * 2 * n_kv_heads * head_dim * 2. */
+size_t cbd_kv_bytes_per_token(const cbd_model_config* cfg);
+
+/* Tokens per arena granule: slab capacities are rounded up to a multiple. */
+int32_t cbd_slab_granule_tokens(void);
+
+/*
+ * Create a context. Weights are referenced, not copied: they must stay
+ * valid until cbd_destroy. kv_arena_dev (arena_bytes long, 256-byte
+ * aligned) is caller-owned device memory that the library carves into
+ * per-sequence slabs. Allocates the device workspace (sized by limits) and
+ * the RoPE table (built on the host in double precision, stored as fp32).
+ * Returns CBD_E_INVAL on inconsistent shapes, CBD_E_HIP if the workspace
+ * cannot be allocated. With limits->host_only the weight and arena pointers
+ * may be NULL (arena_bytes still sets the arena size).
+ */
+cbd_status cbd_create(const cbd_model_config* cfg, const cbd_weights* weights, const cbd_limits* limits,
+                      void* kv_arena_dev, size_t arena_bytes, cbd_ctx** out);
+
+/* Release the workspace (waits for the device). The arena and weights stay the caller's. */
+cbd_status cbd_destroy(cbd_ctx* ctx);
+
+/* Message for the last failed call on this thread ("" if none). Valid until the next call. */
+const char* cbd_last_error(void);
+
+/* Totals since cbd_create. */
+cbd_status cbd_stats(const cbd_ctx* ctx, cbd_stats_t* out);
+
+/*
+ * Admit a sequence: reserve a slab of capacity_tokens (rounded up to the
+ * granule) at length 0. Ids are small non-negative integers, reused after
+ * kvslab_free. CBD_E_NOSPACE if no contiguous run of the arena is free now;
+ * CBD_E_CAPACITY if the capacity exceeds max_position or the whole arena.
+ */
+cbd_status kvslab_alloc(cbd_ctx* ctx, int32_t capacity_tokens, int32_t* seq_id_out);
+
+/* Retire a sequence (EOS or length limit): its slab returns to the arena. */
+cbd_status kvslab_free(cbd_ctx* ctx, int32_t seq_id);
+
+/* Current length t_s (tokens held) and capacity of a live slab. */
+cbd_status kvslab_len(const cbd_ctx* ctx, int32_t seq_id, int32_t* len_out);
+cbd_status kvslab_capacity(const cbd_ctx* ctx, int32_t seq_id, int32_t* cap_out);
+
+/*
+ * Append n_tokens of given K and V to a slab at positions [len, len+n):
+ * k_dev, v_dev are bf16 [n_layers, n_tokens, n_kv_heads, head_dim]
+ * (K already rotated to its position). Used to seed long histories and to
+ * re-inject saved state. CBD_E_CAPACITY if len + n_tokens > capacity.
+ */
+cbd_status kvslab_append(cbd_ctx* ctx, int32_t seq_id, int32_t n_tokens, const void* k_dev,
+                         const void* v_dev, cbd_stream stream);
+
+/*
+ * Copy positions [start, start+n) of a slab out to k_out_dev, v_out_dev in the
+ * layout kvslab_append takes. CBD_E_CAPACITY if start + n > len.
+ */
+cbd_status kvslab_read(const cbd_ctx* ctx, int32_t seq_id, int32_t start, int32_t n_tokens,
+                       void* k_out_dev, void* v_out_dev, cbd_stream stream);
+
+/*
+ * One batched decode step over B distinct live sequences.
+ *  seq_ids          host int32 [B]
+ *  last_tokens_dev  device int32 [B]: the token each row feeds (ids outside
+ *                   [0, vocab) are clamped; they stay on the device so the
+ *                   previous step's argmax can feed this one directly)
+ *  logits_dev       device fp32 [B, vocab], written
+ *  next_tokens_dev  device int32 [B] or NULL: greedy argmax of each logits
+ *                   row (lowest id among equal maxima)
+ * Row i uses t = kvslab_len(seq_ids[i]) captured once on the host, writes
+ * its K/V at t, attends [0..=t], and its length becomes t + 1.
+ * B = 0 is a no-op. CBD_E_INVAL: B > max_batch, duplicate ids, null
+ * pointers; CBD_E_BADSEQ: unknown id; CBD_E_CAPACITY: a slab is full.
+ */
+cbd_status decode_step_batch(cbd_ctx* ctx, const int32_t* seq_ids, int32_t B, const int32_t* last_tokens_dev,
+                             float* logits_dev, int32_t* next_tokens_dev, cbd_stream stream);
+
+/*
+ * Segmented prefill of K distinct live sequences with empty slabs.
+ *  seq_ids     host int32 [K]
+ *  seg_lens    host int32 [K], each >= 1
+ *  tokens_dev  device int32 [sum(seg_lens)]: the segments back to back
+ *  last_logits_dev  device fp32 [K, vocab]: logits of each segment's last token
+ *  next_tokens_dev  device int32 [K] or NULL: their greedy argmax
+ * Segment s is written to its slab at positions 0..len_s-1 and its length
+ * becomes len_s. K = 0 is a no-op. CBD_E_INVAL: zero-length segment,
+ * duplicate id, a non-empty slab, K > max_segments, or the total above
+ * max_prefill_tokens; CBD_E_CAPACITY: a segment longer than its slab.
+ */
+cbd_status prefill_segmented(cbd_ctx* ctx, const int32_t* seq_ids, const int32_t* seg_lens, int32_t K,
+                             const int32_t* tokens_dev, float* last_logits_dev, int32_t* next_tokens_dev,
+                             cbd_stream stream);
+
+/*
+ * Greedy selection over rows of logits (page "Batching", later revision,
+ * section 8: the lowest vocabulary id wins among tied scores).
+ * logits_dev fp32 [rows, vocab] -> tokens_dev int32 [rows]. rows <= 64.
+ */
+cbd_status greedy_argmax(cbd_ctx* ctx, const float* logits_dev, int32_t rows, int32_t* tokens_dev,
+                         cbd_stream stream);
+
+/*
+ * The batched weight-streaming product alone (the page's batched matvec
+ * that shares one weight read across all lanes):
+ * y_dev[b, n] = sum_k W[n, k] * x_dev[b, k] for b < rows.
+ *  x_dev  bf16 [rows, K] row-major;  y_dev fp32 [rows, N].
+ * rows 1..64; N a multiple of 64; K a multiple of 128. Uses the context's
+ * weight format. Exposed for kernel-level parity tests and bandwidth
+ * measurements.
+ */
+cbd_status cbd_linear(cbd_ctx* ctx, const cbd_matrix* w, int32_t N, int32_t K, const void* x_dev,
+                      int32_t rows, float* y_dev, cbd_stream stream);
+
+/*
+ * Pack a 4-bit affine matrix into the int4 layout (host memory, any thread).
+ *  codes   uint8 [N, K], values 0..15 (w = scale * code + bias)
+ *  scale, bias  bf16 bits [N, K/64]
+ *  packed_out   uint32 [N, K/8]
+ *  aux_out      bf16 bits [K/64, N, 2]: (scale, bias) pairs, group-major
+ * Packed layout: each row is split into blocks of 128 inputs held in 16
+ * words. Word 4g+j of a block (g, j in 0..3) holds the 8 codes of inputs
+ * 64*(j/2) + 16*g + 8*(j%2) + e, e = 0..7, with input e in nibble
+ * (e/2) + 4*(e%2). K must be a multiple of 128 and N of 16.
+ */
+cbd_status cbd_pack_int4(const uint8_t* codes, const uint16_t* scale, const uint16_t* bias, int64_t N,
+                         int64_t K, uint32_t* packed_out, uint16_t* aux_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CBD_H */

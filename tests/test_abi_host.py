@@ -1,0 +1,173 @@
+"""Host-side tests of the C ABI: exports, slab bookkeeping and argument validation.
+
+A host-only context (no device memory, no kernels) runs the same validation
+and bookkeeping code as a device context, so every error path here is forced
+from the host; none of them launches anything.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def cbd():
+    import continuous_batching_decode_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from continuous_batching_decode_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "cbd.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_header_symbol(cbd):
+    names = header_functions()
+    assert len(names) >= 15
+    assert sorted(cbd.EXPORTS) == names
+    lib = cbd.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_kv_bytes_and_granule(cbd):
+    cfg = cbd.model_config(synth.LLAMA8B, 40000)
+    assert cbd.lib().cbd_kv_bytes_per_token(ctypes.byref(cfg)) == 131072
+    assert cbd.lib().cbd_slab_granule_tokens() == 256
+
+
+def make(cbd, shape=synth.TINY, granules=8, **kw):
+    g = cbd.lib().cbd_slab_granule_tokens()
+    return cbd.Engine({"shape": shape}, arena_bytes=granules * g * shape.kv_bytes_per_token(), host_only=True,
+                      max_position=kw.pop("max_position", 4096), **kw)
+
+
+def test_alloc_free_len_and_reuse(cbd):
+    e = make(cbd)
+    a = e.alloc(100)
+    b = e.alloc(300)
+    assert (a, b) == (0, 1)
+    assert e.length(a) == 0 and e.capacity(a) == 256 and e.capacity(b) == 512
+    st = e.stats()
+    assert st["live_seqs"] == 2 and st["arena_bytes_used"] == 3 * 256 * synth.TINY.kv_bytes_per_token()
+    e.free(a)
+    assert e.alloc(1) == 0  # ids are reused
+    with pytest.raises(cbd.CbdError) as ei:
+        e.length(7)
+    assert ei.value.status == cbd.CBD_E_BADSEQ
+    e.free(b)
+    with pytest.raises(cbd.CbdError) as ei:
+        e.free(b)
+    assert ei.value.status == cbd.CBD_E_BADSEQ
+
+
+def test_arena_exhaustion_and_coalescing(cbd):
+    e = make(cbd, granules=4)
+    ids = [e.alloc(256) for _ in range(4)]
+    with pytest.raises(cbd.CbdError) as ei:
+        e.alloc(1)
+    assert ei.value.status == cbd.CBD_E_NOSPACE  # caller queues and retries later
+    e.free(ids[1])
+    e.free(ids[2])
+    # the two freed neighbours coalesce into one run of 2 granules
+    big = e.alloc(512)
+    assert e.capacity(big) == 512
+    with pytest.raises(cbd.CbdError) as ei:
+        e.alloc(5 * 256)
+    assert ei.value.status == cbd.CBD_E_CAPACITY  # larger than the whole arena: can never fit
+    for i in (ids[0], ids[3], big):
+        e.free(i)
+    assert e.stats()["arena_bytes_used"] == 0
+    assert e.capacity(e.alloc(4 * 256)) == 1024
+
+
+def test_capacity_above_rope_table(cbd):
+    e = make(cbd, granules=64, max_position=1000)
+    with pytest.raises(cbd.CbdError) as ei:
+        e.alloc(1001)
+    assert ei.value.status == cbd.CBD_E_CAPACITY
+    assert e.capacity(e.alloc(1000)) == 1000  # rounded capacity is clipped to the table
+
+
+def test_decode_validation_without_state_change(cbd):
+    e = make(cbd, max_batch=4)
+    a, b = e.alloc(10), e.alloc(10)
+    P = 4096  # stands in for device pointers; a host-only context never dereferences them
+    assert e.decode_step_batch_raw([], P, P) == cbd.CBD_OK  # B = 0 is a no-op
+    assert e.decode_step_batch_raw([a, a], P, P) == cbd.CBD_E_INVAL  # duplicate id
+    assert e.decode_step_batch_raw([a, 9], P, P) == cbd.CBD_E_BADSEQ
+    assert e.decode_step_batch_raw([a, b, 0, 1, 0], P, P) == cbd.CBD_E_INVAL  # B > max_batch
+    assert e.decode_step_batch_raw([a], None, P) == cbd.CBD_E_INVAL
+    assert e.decode_step_batch_raw([a, b], P, P) == cbd.CBD_E_NODEVICE  # valid, but no device here
+    assert e.length(a) == 0 and e.length(b) == 0
+    e.free(b)
+    assert e.decode_step_batch_raw([a, b], P, P) == cbd.CBD_E_BADSEQ
+
+
+def test_prefill_validation(cbd):
+    e = make(cbd, max_prefill_tokens=100, max_segments=3)
+    a, b = e.alloc(50), e.alloc(300)
+    P = 4096
+    assert e.prefill_segmented_raw([], [], P, P) == cbd.CBD_OK
+    assert e.prefill_segmented_raw([a, b], [3, 0], P, P) == cbd.CBD_E_INVAL  # zero-length segment
+    assert e.prefill_segmented_raw([a, a], [3, 4], P, P) == cbd.CBD_E_INVAL  # duplicate
+    assert e.prefill_segmented_raw([a, b], [60, 41], P, P) == cbd.CBD_E_INVAL  # total above the limit
+    assert e.prefill_segmented_raw([a], [257], P, P) == cbd.CBD_E_CAPACITY  # longer than the slab
+    assert e.prefill_segmented_raw([a, b, 0, 1], [1, 1, 1, 1], P, P) == cbd.CBD_E_INVAL  # K > max_segments
+    assert e.prefill_segmented_raw([a, 5], [1, 1], P, P) == cbd.CBD_E_BADSEQ
+    assert e.prefill_segmented_raw([a, b], [10, 20], P, P) == cbd.CBD_E_NODEVICE
+    assert e.length(a) == 0 and e.length(b) == 0
+
+
+def test_create_rejects_bad_shapes(cbd):
+    from dataclasses import replace
+    for bad in (replace(synth.TINY, head_dim=96), replace(synth.TINY, n_heads=3),
+                replace(synth.TINY, d_model=200), replace(synth.TINY, vocab=1000),
+                replace(synth.TINY, n_heads=16, n_kv_heads=2)):
+        with pytest.raises(cbd.CbdError) as ei:
+            make(cbd, shape=bad)
+        assert ei.value.status == cbd.CBD_E_INVAL
+    with pytest.raises(cbd.CbdError):
+        make(cbd, max_batch=65)
+    with pytest.raises(cbd.CbdError):
+        make(cbd, max_segments=0)
+
+
+def unpack_int4_reference(packed, aux, n, k):
+    """Decode the packed layout as the header documents it (independent of the packer's loops)."""
+    codes = np.zeros((n, k), dtype=np.uint8)
+    words = packed.reshape(n, k // 128, 4, 4)  # [row, block, g, j]
+    for g in range(4):
+        for j in range(4):
+            w = words[:, :, g, j].astype(np.uint64)
+            for e in range(8):
+                nib = (e // 2) + 4 * (e % 2)
+                vals = ((w >> np.uint64(4 * nib)) & np.uint64(15)).astype(np.uint8)
+                cols = np.arange(k // 128) * 128 + 64 * (j // 2) + 16 * g + 8 * (j % 2) + e
+                codes[:, cols] = vals
+    scale = aux[:, :, 0].T.copy()
+    bias = aux[:, :, 1].T.copy()
+    return codes, scale, bias
+
+
+def test_int4_packing_layout(cbd):
+    m = synth._int4_matrix(3, 5, (32, 256), 64, 0.02)
+    packed, aux = cbd.pack_int4(m["codes"], m["scale"], m["bias"])
+    assert packed.shape == (32, 32) and aux.shape == (4, 32, 2)
+    codes, scale, bias = unpack_int4_reference(packed, aux, 32, 256)
+    assert np.array_equal(codes, m["codes"])
+    assert np.array_equal(scale, m["scale"]) and np.array_equal(bias, m["bias"])
+    with pytest.raises(cbd.CbdError):
+        cbd.pack_int4(np.full((16, 256), 16, np.uint8), m["scale"][:16], m["bias"][:16])

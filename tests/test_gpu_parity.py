@@ -1,0 +1,334 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+All inputs come from ``synth`` (seeded); expected values come only from the
+oracle (or from an fp64 matmul of the same bf16 / int4 values for the
+standalone weight-streaming product).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_common import MID, MID_INT4, assert_logits_close, check_greedy, compare_slab_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a visible GPU"
+    return t
+
+
+@pytest.fixture(scope="module")
+def cbd():
+    import continuous_batching_decode_amd as m
+    m.lib()
+    return m
+
+
+def to_dev_bits(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+# ----------------------------------------------------------------------------- weight-streaming product
+
+LINEAR_HOST = synth.ModelShape("linear-host", 1, 512, 4, 1, 128, 14336, 256, 10000.0)
+
+
+@pytest.fixture(scope="module")
+def linear_engines(torch, cbd):
+    from dataclasses import replace
+    engs = {}
+    for fmt in ("bf16", "int4"):
+        sh = replace(LINEAR_HOST, weight_format=fmt)
+        engs[fmt] = cbd.Engine(synth.make_weights(sh, seed=98), arena_bytes=1 << 20, max_batch=64,
+                               max_prefill_tokens=64, max_position=256)
+    yield engs
+    for e in engs.values():
+        e.close()
+
+
+@pytest.mark.parametrize("N,K", [(6144, 4096), (4096, 14336), (1024, 256), (512, 1024)])
+@pytest.mark.parametrize("rows", [1, 7, 16, 33, 64])
+def test_linear_bf16(torch, cbd, linear_engines, N, K, rows):
+    _say("linear bf16 N=%d K=%d rows=%d" % (N, K, rows))
+    eng = linear_engines["bf16"]
+    W = synth.normal_bf16(7, N + K, (N, K), 0.02)
+    X = synth.normal_bf16(8, rows, (rows, K), 1.0)
+    wd, xd = to_dev_bits(torch, W), to_dev_bits(torch, X)
+    y = torch.empty((rows, N), dtype=torch.float32, device="cuda")
+    eng.linear(cbd.Matrix(wd.data_ptr(), None), N, K, xd, y)
+    torch.cuda.synchronize()
+    ref = synth.bf16_bits_to_f32(X).astype(np.float64) @ synth.bf16_bits_to_f32(W).astype(np.float64).T
+    got = y.cpu().numpy()
+    err = np.max(np.abs(got - ref))
+    assert err <= 2e-5 * np.max(np.abs(ref)) + 1e-6, err
+
+
+@pytest.mark.parametrize("N,K", [(6144, 4096), (4096, 14336), (512, 512)])
+@pytest.mark.parametrize("rows", [1, 5, 16, 40, 64])
+def test_linear_int4(torch, cbd, linear_engines, N, K, rows):
+    _say("linear int4 N=%d K=%d rows=%d" % (N, K, rows))
+    eng = linear_engines["int4"]
+    m = synth._int4_matrix(9, N + K, (N, K), 64, 0.02)
+    packed, aux = cbd.pack_int4(m["codes"], m["scale"], m["bias"])
+    pd = torch.from_numpy(packed.view(np.int32)).cuda()
+    ad = to_dev_bits(torch, aux)
+    X = synth.normal_bf16(10, rows, (rows, K), 1.0)
+    xd = to_dev_bits(torch, X)
+    y = torch.empty((rows, N), dtype=torch.float32, device="cuda")
+    eng.linear(cbd.Matrix(pd.data_ptr(), ad.data_ptr()), N, K, xd, y)
+    torch.cuda.synchronize()
+    from oracle import dequant_int4
+    Wd = dequant_int4(m["codes"], m["scale"], m["bias"], 64)
+    ref = synth.bf16_bits_to_f32(X).astype(np.float64) @ Wd.T
+    err = np.max(np.abs(y.cpu().numpy() - ref))
+    assert err <= 2e-5 * np.max(np.abs(ref)) + 1e-6, err
+
+
+# ----------------------------------------------------------------------------- slabs and argmax
+
+def test_slab_append_read_roundtrip(torch, cbd):
+    _say("slab append/read roundtrip")
+    w = synth.make_weights(synth.TINY, seed=0)
+    eng = cbd.Engine(w, arena_bytes=16 * 256 * synth.TINY.kv_bytes_per_token(), max_position=4096)
+    a = eng.alloc(700)
+    b = eng.alloc(300)
+    k, v = synth.kv_history(synth.TINY, 5, 0, 650)
+    eng.append(a, to_dev_bits(torch, k[:, :400]), to_dev_bits(torch, v[:, :400]))
+    eng.append(a, to_dev_bits(torch, k[:, 400:]), to_dev_bits(torch, v[:, 400:]))
+    kb, vb = synth.kv_history(synth.TINY, 5, 1, 300)
+    eng.append(b, to_dev_bits(torch, kb), to_dev_bits(torch, vb))
+    assert eng.length(a) == 650 and eng.length(b) == 300
+    rk, rv = eng.read(a, 0, 650)
+    torch.cuda.synchronize()
+    assert np.array_equal(rk.cpu().numpy().view(np.uint16), k)
+    assert np.array_equal(rv.cpu().numpy().view(np.uint16), v)
+    rk, rv = eng.read(b, 17, 100)
+    assert np.array_equal(rk.cpu().numpy().view(np.uint16), kb[:, 17:117])
+    with pytest.raises(cbd.CbdError):
+        eng.append(b, to_dev_bits(torch, kb[:, :257]), to_dev_bits(torch, vb[:, :257]))  # 300 + 257 > 512
+    assert eng.length(b) == 300
+    eng.close()
+
+
+def test_greedy_argmax_ties(torch, cbd):
+    _say("argmax ties")
+    from oracle import greedy
+    w = synth.make_weights(synth.TINY, seed=0)
+    eng = cbd.Engine(w, arena_bytes=1 << 20, max_position=256)
+    V = synth.TINY.vocab
+    rng = np.random.default_rng(0)
+    L = rng.integers(-5, 5, size=(9, V)).astype(np.float32)  # many exact ties
+    L[3, :] = 2.0
+    L[4, 1000:] = 7.0
+    L[5, 17] = 100.0
+    L[5, 900] = 100.0
+    ld = torch.from_numpy(L).cuda()
+    out = torch.empty(9, dtype=torch.int32, device="cuda")
+    eng.greedy_argmax(ld, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), greedy(L.astype(np.float64)))
+    eng.close()
+
+
+# ----------------------------------------------------------------------------- whole step vs oracle
+
+def _prefill_both(torch, cbd, eng, orc, lengths, prompts, cap):
+    ids = [eng.alloc(cap) for _ in lengths]
+    oids = [orc.new_sequence() for _ in lengths]
+    toks = torch.from_numpy(np.concatenate(prompts).astype(np.int32)).cuda()
+    logits = torch.empty((len(lengths), eng.shape.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(len(lengths), dtype=torch.int32, device="cuda")
+    eng.prefill_segmented(ids, lengths, toks, logits, nxt)
+    ref = orc.prefill_segmented(oids, prompts)
+    torch.cuda.synchronize()
+    return ids, oids, logits.cpu().numpy(), nxt.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("gain_std", [0.0, 0.1])
+def test_tiny_prefill_and_decode_teacher_forced(torch, cbd, gain_std):
+    """The small decoder: segmented prefill {17,5,33,1} then 8 greedy decode steps at B=4."""
+    _say("tiny teacher-forced gain_std=%g" % gain_std)
+    from oracle import OracleModel, greedy
+    shape = synth.TINY
+    w = synth.make_weights(shape, seed=0, gain_std=gain_std)
+    lengths = [17, 5, 33, 1]
+    prompts = synth.prompts(100, lengths, shape.vocab)
+    eng = cbd.Engine(w, arena_bytes=32 * 256 * shape.kv_bytes_per_token(), max_batch=8, max_prefill_tokens=256,
+                     max_position=1024)
+    orc = OracleModel(w, cache_all_layers=True)
+    ids, oids, got, gtok, ref = _prefill_both(torch, cbd, eng, orc, lengths, prompts, 64)
+    errs = assert_logits_close(got, ref, "prefill")
+    check_greedy(gtok, ref, errs, "prefill")
+    tok = greedy(ref)
+    logits = torch.empty((4, shape.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(4, dtype=torch.int32, device="cuda")
+    for step in range(8):
+        eng.decode_step_batch(ids, torch.from_numpy(tok.astype(np.int32)).cuda(), logits, nxt)
+        ref = orc.decode_step_batch(oids, tok)
+        torch.cuda.synchronize()
+        errs = assert_logits_close(logits.cpu().numpy(), ref, "step %d" % step)
+        check_greedy(nxt.cpu().numpy(), ref, errs, "step %d" % step)
+        tok = greedy(ref)
+    for i, o, n in zip(ids, oids, lengths):
+        assert eng.length(i) == n + 8 == orc.seqs[o].length
+        k, v = eng.read(i, 0, n + 8)
+        torch.cuda.synchronize()
+        compare_slab_bits(k.cpu().numpy(), np.stack(orc.seqs[o].k), "K slab %d" % i)
+        compare_slab_bits(v.cpu().numpy(), np.stack(orc.seqs[o].v), "V slab %d" % i)
+    eng.close()
+
+
+def test_tiny_free_running_trajectory(torch, cbd):
+    """Free-running greedy: GPU feeds its own argmax (device-resident), oracle its own."""
+    _say("tiny free-running")
+    from oracle import OracleModel, greedy
+    shape = synth.TINY
+    w = synth.make_weights(shape, seed=0)
+    lengths = [17, 5, 33, 1]
+    prompts = synth.prompts(100, lengths, shape.vocab)
+    eng = cbd.Engine(w, arena_bytes=32 * 256 * shape.kv_bytes_per_token(), max_batch=8, max_prefill_tokens=256,
+                     max_position=1024)
+    orc = OracleModel(w, cache_all_layers=True)
+    ids, oids, got, gtok, ref = _prefill_both(torch, cbd, eng, orc, lengths, prompts, 64)
+    errs = assert_logits_close(got, ref, "prefill")
+    amb = check_greedy(gtok, ref, errs, "prefill")
+    gpu_traj, orc_traj = [gtok.copy()], [greedy(ref)]
+    tok_dev = torch.from_numpy(gtok.astype(np.int32)).cuda()
+    logits = torch.empty((4, shape.vocab), dtype=torch.float32, device="cuda")
+    tok = greedy(ref)
+    for step in range(8):
+        nxt = torch.empty(4, dtype=torch.int32, device="cuda")
+        eng.decode_step_batch(ids, tok_dev, logits, nxt)
+        tok_dev = nxt
+        ref = orc.decode_step_batch(oids, tok)
+        tok = greedy(ref)
+        torch.cuda.synchronize()
+        gpu_traj.append(nxt.cpu().numpy())
+        orc_traj.append(tok)
+    g, o = np.stack(gpu_traj), np.stack(orc_traj)
+    if amb == 0:
+        assert np.array_equal(g, o), (g, o)
+    _say("free-running tokens identical:", bool(np.array_equal(g, o)))
+    eng.close()
+
+
+def test_ragged_long_history_decode(torch, cbd):
+    """Seeded ragged histories (split attention path), GQA G=4, Dh=128; 2 teacher-forced steps."""
+    _say("ragged long-history decode")
+    from oracle import OracleModel, greedy
+    shape = MID
+    w = synth.make_weights(shape, seed=3, gain_std=0.1)
+    ctx = [0, 1, 63, 64, 65, 700, 2999, 4095]
+    eng = cbd.Engine(w, arena_bytes=64 * 256 * shape.kv_bytes_per_token(), max_batch=16, max_prefill_tokens=64,
+                     max_position=8192)
+    orc = OracleModel(w, cache_all_layers=True)
+    ids, oids = [], []
+    for r, n in enumerate(ctx):
+        i = eng.alloc(n + 4)
+        o = orc.new_sequence()
+        if n:
+            k, v = synth.kv_history(shape, 11, r, n)
+            eng.append(i, to_dev_bits(torch, k), to_dev_bits(torch, v))
+            orc.append_history(o, k, v)
+        ids.append(i)
+        oids.append(o)
+    tok = synth.prompts(12, [len(ctx)], shape.vocab)[0].astype(np.int64)
+    logits = torch.empty((len(ctx), shape.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(len(ctx), dtype=torch.int32, device="cuda")
+    for step in range(2):
+        eng.decode_step_batch(ids, torch.from_numpy(tok.astype(np.int32)).cuda(), logits, nxt)
+        ref = orc.decode_step_batch(oids, tok)
+        torch.cuda.synchronize()
+        errs = assert_logits_close(logits.cpu().numpy(), ref, "step %d" % step)
+        check_greedy(nxt.cpu().numpy(), ref, errs, "step %d" % step)
+        tok = greedy(ref)
+    for i, o, n in zip(ids, oids, ctx):
+        k, v = eng.read(i, n, 2)
+        torch.cuda.synchronize()
+        compare_slab_bits(k.cpu().numpy(), np.stack(orc.seqs[o].k)[:, n:n + 2], "K")
+        compare_slab_bits(v.cpu().numpy(), np.stack(orc.seqs[o].v)[:, n:n + 2], "V")
+    # a row's result does not depend on the other rows of the batch
+    solo = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
+    eng2 = cbd.Engine(w, arena_bytes=64 * 256 * shape.kv_bytes_per_token(), max_batch=16, max_position=8192)
+    i = eng2.alloc(ctx[5] + 4)
+    k, v = eng.read(ids[5], 0, ctx[5] + 2)
+    eng2.append(i, k, v)
+    eng2.decode_step_batch([i], torch.from_numpy(tok[5:6].astype(np.int32)).cuda(), solo)
+    eng.decode_step_batch(ids, torch.from_numpy(tok.astype(np.int32)).cuda(), logits, nxt)
+    torch.cuda.synchronize()
+    assert_logits_close(solo.cpu().numpy(), logits.cpu().numpy()[5:6], "batched vs solo")
+    eng.close()
+    eng2.close()
+
+
+def test_segmented_prefill_no_leakage_gpu(torch, cbd):
+    """Changing one segment's tokens leaves the others' logits and slabs unchanged on the GPU too."""
+    _say("segmented prefill leakage")
+    shape = MID
+    w = synth.make_weights(shape, seed=4)
+    lengths = [40, 1, 77, 130, 64]
+    pr = synth.prompts(13, lengths, shape.vocab)
+    pr2 = [p.copy() for p in pr]
+    pr2[2] = (pr2[2] + 7) % shape.vocab
+    outs = []
+    for prompts in (pr, pr2):
+        eng = cbd.Engine(w, arena_bytes=16 * 256 * shape.kv_bytes_per_token(), max_batch=8,
+                         max_prefill_tokens=512, max_position=1024)
+        ids = [eng.alloc(256) for _ in lengths]
+        toks = torch.from_numpy(np.concatenate(prompts).astype(np.int32)).cuda()
+        lg = torch.empty((len(lengths), shape.vocab), dtype=torch.float32, device="cuda")
+        eng.prefill_segmented(ids, lengths, toks, lg)
+        slabs = [eng.read(i, 0, n) for i, n in zip(ids, lengths)]
+        torch.cuda.synchronize()
+        outs.append((lg.cpu().numpy(), [(k.cpu().numpy(), v.cpu().numpy()) for k, v in slabs]))
+        eng.close()
+    (l1, s1), (l2, s2) = outs
+    for s in (0, 1, 3, 4):
+        assert np.array_equal(l1[s], l2[s])
+        assert np.array_equal(s1[s][0], s2[s][0]) and np.array_equal(s1[s][1], s2[s][1])
+    assert not np.allclose(l1[2], l2[2])
+    # and the prefill agrees with the oracle
+    from oracle import OracleModel
+    orc = OracleModel(w, cache_all_layers=True)
+    oids = [orc.new_sequence() for _ in lengths]
+    ref = orc.prefill_segmented(oids, pr)
+    assert_logits_close(l1, ref, "prefill")
+    for j, o in enumerate(oids):
+        compare_slab_bits(s1[j][0], np.stack(orc.seqs[o].k), "K")
+
+
+def test_int4_model_decode(torch, cbd):
+    """int4-affine weights through prefill and 3 teacher-forced steps."""
+    _say("int4 model")
+    from oracle import OracleModel, greedy
+    shape = MID_INT4
+    w = synth.make_weights(shape, seed=5, gain_std=0.1)
+    lengths = [9, 30, 2]
+    prompts = synth.prompts(14, lengths, shape.vocab)
+    eng = cbd.Engine(w, arena_bytes=16 * 256 * shape.kv_bytes_per_token(), max_batch=8, max_prefill_tokens=128,
+                     max_position=1024)
+    orc = OracleModel(w, cache_all_layers=True)
+    ids, oids, got, gtok, ref = _prefill_both(torch, cbd, eng, orc, lengths, prompts, 64)
+    errs = assert_logits_close(got, ref, "int4 prefill")
+    check_greedy(gtok, ref, errs, "int4 prefill")
+    tok = greedy(ref)
+    logits = torch.empty((3, shape.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(3, dtype=torch.int32, device="cuda")
+    for step in range(3):
+        eng.decode_step_batch(ids, torch.from_numpy(tok.astype(np.int32)).cuda(), logits, nxt)
+        ref = orc.decode_step_batch(oids, tok)
+        torch.cuda.synchronize()
+        errs = assert_logits_close(logits.cpu().numpy(), ref, "int4 step %d" % step)
+        check_greedy(nxt.cpu().numpy(), ref, errs, "int4 step %d" % step)
+        tok = greedy(ref)
+    eng.close()
