@@ -1,0 +1,248 @@
+#!/usr/bin/env python
+"""Aggregate decode throughput of decode_step_batch on one MI355X.
+
+Workload (synthetic, seeded): a Llama-3-8B-shaped random-init decoder in bf16
+(32 layers, d_model 4096, 32/8 heads of 128, SwiGLU 14336, vocab 128256,
+RoPE theta 500000), B = 8 live sequences whose contexts are uniform in
+[512, 4096] (K/V histories drawn by ``synth`` and appended to the slabs),
+greedy decoding with the next tokens kept on the device. A step is one
+``decode_step_batch`` over all B rows: embed, 32 layers (norm, QKV, RoPE +
+append, ragged attention, O + residual, norm, gate/up + SwiGLU, down +
+residual), final norm, lm_head, argmax.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+- value: aggregate tok/s = B * steps / timed seconds (inputs resident in HBM)
+- roofline: the dominant kernel (the weight-streaming product with the fused
+  SwiGLU epilogue) timed with HIP events on its own launch stream over the
+  timed region, against the 8 TB/s HBM peak
+- cpu_baseline: the CPU oracle timed on one decode step of the same rows
+- sweep: tok/s at B = 1..64 on the same model (scaling check)
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "aggregate decode tok/s at B=1..64, 8B-shape bf16; achieved HBM GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_llama8b_b8.md")
+KERNEL_SRC = os.path.join(ROOT, "continuous_batching_decode_amd", "csrc", "gemm_skinny.hip")
+
+
+def log(*a):
+    print("[bench %6.1fs]" % (time.time() - T0), *a, file=sys.stderr, flush=True)
+
+
+T0 = time.time()
+
+
+def source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary,
+    or None when absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != source_hash():
+        return None
+    return float(t.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--batch", type=int, default=8)
+    ap.add_argument("--sweep", default="1,2,4,8,16,32,64", help="batch sizes for the scaling sweep ('' = none)")
+    ap.add_argument("--sweep-steps", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--shape", default="llama3-8b-shape")
+    ap.add_argument("--ctx-lo", type=int, default=512)
+    ap.add_argument("--ctx-hi", type=int, default=4096)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (each GPU would run its own "
+              "independent engine; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import continuous_batching_decode_amd as cbd
+    import synth
+
+    shape = synth.SHAPES[args.shape]
+    B = args.batch
+    sweep = [int(x) for x in args.sweep.split(",") if x.strip()]
+    n_rows = max([B] + sweep)
+    ctx = synth.uniform_lengths(1, B, args.ctx_lo, args.ctx_hi).astype(int)
+    ctx_main = ctx.copy()
+    # sweep-only rows (beyond B) reuse the main rows' histories
+    ctx = np.array([ctx[r % B] for r in range(n_rows)], dtype=int)
+    grow = args.warmup + args.steps + 1 + (len(sweep) * (args.sweep_steps + 4))
+    caps = [int(c) + grow + 8 for c in ctx]
+    gran = 256
+    arena_tokens = sum((c + gran - 1) // gran * gran for c in caps)
+    kv_tok = shape.kv_bytes_per_token()
+    max_pos = int(max(caps)) + gran
+
+    log("generating %s weights (%.2f GB streamed per step)" % (shape.name, shape.streamed_params() * 2 / 1e9))
+    weights = synth.make_weights(shape, seed=0)
+    log("uploading weights; arena %.1f GB" % (arena_tokens * kv_tok / 1e9))
+    eng = cbd.Engine(weights, arena_bytes=arena_tokens * kv_tok, max_batch=64, max_prefill_tokens=64,
+                     max_position=max_pos)
+    dev = torch.device("cuda:0")
+    ids = [eng.alloc(c) for c in caps]
+    hist = []
+    for r in range(B):
+        k, v = synth.kv_history(shape, 1, r, int(ctx[r]))
+        hist.append((k, v))
+        eng.append(ids[r], torch.from_numpy(k.view(np.int16)).to(dev), torch.from_numpy(v.view(np.int16)).to(dev))
+    for r in range(B, n_rows):
+        # sweep-only rows reuse the histories of the main rows (device copies)
+        src = r % B
+        k, v = eng.read(ids[src], 0, int(ctx[src]))
+        eng.append(ids[r], k, v)
+    torch.cuda.synchronize()
+    log("slabs ready: contexts %s" % list(ctx_main))
+
+    V = shape.vocab
+    first_tok = synth.prompts(2, [n_rows], V)[0].astype(np.int32)
+    logits = torch.empty((64, V), dtype=torch.float32, device=dev)
+    tok_a = torch.from_numpy(first_tok).to(dev)
+    tok_b = torch.empty(64, dtype=torch.int32, device=dev)
+    main_ids = ids[:B]
+
+    # step 0 (first warmup step) doubles as a parity sample against the oracle below
+    eng.decode_step_batch(main_ids, tok_a[:B], logits[:B], tok_b[:B])
+    torch.cuda.synchronize()
+    first_logits = logits[:B].cpu().numpy().astype(np.float64)
+    tok_a, tok_b = tok_b, tok_a
+    for _ in range(max(0, args.warmup - 1)):
+        eng.decode_step_batch(main_ids, tok_a[:B], logits[:B], tok_b[:B])
+        tok_a, tok_b = tok_b, tok_a
+    torch.cuda.synchronize()
+
+    log("timing %d steps at B=%d" % (args.steps, B))
+    eng.profile_begin(["gate_up"], max_launches=shape.n_layers * args.steps + 64)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        eng.decode_step_batch(main_ids, tok_a[:B], logits[:B], tok_b[:B])
+        tok_a, tok_b = tok_b, tok_a
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = eng.profile_end()
+    secs = t1 - t0
+    ms_step = secs * 1e3 / args.steps
+    tokps = B * args.steps / secs
+
+    # algorithmic bytes per step, averaged over the timed steps
+    w_bytes = shape.streamed_params() * (2 if shape.weight_format == "bf16" else 0.5625)
+    mean_t = float(np.mean(ctx_main)) + args.warmup + (args.steps - 1) / 2.0
+    step_bytes = w_bytes + B * (mean_t + 1) * kv_tok + B * kv_tok + B * V * 4
+    step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+
+    gu = prof["gate_up"]
+    per_launch_bytes = gu["bytes"] / gu["launches"]
+    avg_ms = gu["total_ms"] / gu["launches"]
+    achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": committed_traffic(),
+                "kernel": "skinny_gemm_kernel (gate/up weight stream, fused SwiGLU), 8B shape, B=%d" % B,
+                "bytes_per_launch": per_launch_bytes, "avg_launch_us": round(avg_ms * 1e3, 2),
+                "launches": gu["launches"], "kernel_source_sha256_16": source_hash()}
+    log("B=%d: %.1f tok/s, %.3f ms/step, step %.0f GB/s; gate/up %.1f us -> %.0f GB/s" % (
+        B, tokps, ms_step, step_gbps, avg_ms * 1e3, achieved))
+
+    breakdown = None
+    if not args.no_breakdown:
+        nb = min(16, args.steps)
+        eng.profile_begin(cbd.KERNEL_KINDS, max_launches=nb * (shape.n_layers * 10 + 8))
+        for _ in range(nb):
+            eng.decode_step_batch(main_ids, tok_a[:B], logits[:B], tok_b[:B])
+            tok_a, tok_b = tok_b, tok_a
+        torch.cuda.synchronize()
+        p = eng.profile_end()
+        breakdown = {k: {"ms_per_step": round(v["total_ms"] / nb, 4),
+                         "GBps": round(v["bytes"] / (v["total_ms"] * 1e-3) / 1e9, 1) if v["total_ms"] else None,
+                         "launches_per_step": v["launches"] // nb} for k, v in p.items()}
+        log("breakdown (event-timed, %d steps): %s" % (nb, json.dumps(breakdown)))
+
+    sweep_out = {}
+    for b in sweep:
+        sids = ids[:b]
+        for _ in range(4):
+            eng.decode_step_batch(sids, tok_a[:b], logits[:b], tok_b[:b])
+            tok_a, tok_b = tok_b, tok_a
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        for _ in range(args.sweep_steps):
+            eng.decode_step_batch(sids, tok_a[:b], logits[:b], tok_b[:b])
+            tok_a, tok_b = tok_b, tok_a
+        torch.cuda.synchronize()
+        s = time.perf_counter() - s0
+        ms = s * 1e3 / args.sweep_steps
+        lens = np.array([eng.length(i) for i in sids], dtype=np.float64) - args.sweep_steps / 2.0
+        by = w_bytes + float(np.sum(lens + 1)) * kv_tok + b * kv_tok + b * V * 4
+        sweep_out[str(b)] = {"tok_s": round(b * args.sweep_steps / s, 1), "ms_per_step": round(ms, 4),
+                             "GBps": round(by / (ms * 1e-3) / 1e9, 1)}
+        log("sweep B=%d: %s" % (b, sweep_out[str(b)]))
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        from oracle import OracleModel, greedy
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            cores = 1
+        log("cpu baseline: oracle, one decode step of the %d rows (BLAS threads %d)" % (B, cores))
+        orc = OracleModel(weights)
+        oids = []
+        for r in range(B):
+            o = orc.new_sequence()
+            orc.append_history(o, hist[r][0], hist[r][1])
+            oids.append(o)
+        c0 = time.perf_counter()
+        ref = orc.decode_step_batch(oids, first_tok[:B].astype(np.int64))
+        csecs = time.perf_counter() - c0
+        cpu = {"value": round(B / csecs, 4), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+               "sample": "one decode_step_batch of the same %d rows at their seeded contexts (float64, all 32 "
+                         "layers + lm_head), %.1f s" % (B, csecs)}
+        errs = np.max(np.abs(first_logits - ref), axis=1) / np.max(np.abs(ref), axis=1)
+        parity = {"max_rel_err": float(np.max(errs)), "tol": 1e-2,
+                  "greedy_match": int(np.sum(greedy(first_logits) == greedy(ref))), "rows": B}
+        log("cpu baseline %.2f s/step; parity %s" % (csecs, parity))
+
+    out = {"metric": METRIC, "value": round(tokps, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if shape.weight_format == "bf16" else "int4-affine/bf16",
+           "data": "synthetic",
+           "config": {"workload": "%s decode_step_batch, B=%d, contexts U[%d,%d], greedy, %d layers" % (
+               shape.name, B, args.ctx_lo, args.ctx_hi, shape.n_layers),
+               "batch": B, "contexts": [int(c) for c in ctx_main], "parallelism": "single GPU"},
+           "achieved_hbm_GBps": round(step_gbps, 1), "step_bytes": step_bytes,
+           "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),
+           "roofline": roofline, "cpu_baseline": cpu, "parity_first_step": parity, "sweep": sweep_out,
+           "kernel_breakdown": breakdown}
+    eng.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,7 +24,11 @@ WEIGHTS_BF16, WEIGHTS_INT4 = 0, 1
 # every symbol include/cbd.h declares
 EXPORTS = ["cbd_kv_bytes_per_token", "cbd_slab_granule_tokens", "cbd_create", "cbd_destroy", "cbd_last_error",
            "cbd_stats", "kvslab_alloc", "kvslab_free", "kvslab_len", "kvslab_capacity", "kvslab_append",
-           "kvslab_read", "decode_step_batch", "prefill_segmented", "greedy_argmax", "cbd_linear", "cbd_pack_int4"]
+           "kvslab_read", "decode_step_batch", "prefill_segmented", "greedy_argmax", "cbd_linear", "cbd_pack_int4",
+           "cbd_profile_begin", "cbd_profile_end"]
+
+KERNEL_KINDS = ["embed", "norm", "qkv", "rope_append", "attention", "attn_combine", "o_proj", "gate_up", "down",
+                "lm_head", "argmax"]
 
 
 class CbdError(RuntimeError):
@@ -59,6 +63,11 @@ class Limits(ctypes.Structure):
                 ("max_segments", ctypes.c_int32), ("host_only", ctypes.c_int32)]
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64), ("total_ms", ctypes.c_double), ("bytes", ctypes.c_double),
+                ("flops", ctypes.c_double)]
+
+
 class Stats(ctypes.Structure):
     _fields_ = [("live_seqs", ctypes.c_int64), ("arena_bytes", ctypes.c_int64), ("arena_bytes_used", ctypes.c_int64),
                 ("decode_steps", ctypes.c_int64), ("decode_rows", ctypes.c_int64), ("prefill_calls", ctypes.c_int64),
@@ -87,8 +96,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "decode_step_batch": (i32, [ctx_p, P(i32), i32, vp, vp, vp, vp]),
         "prefill_segmented": (i32, [ctx_p, P(i32), P(i32), i32, vp, vp, vp, vp]),
         "greedy_argmax": (i32, [ctx_p, vp, i32, vp, vp]),
-        "cbd_linear": (i32, [ctx_p, P(Matrix), i32, i32, vp, i32, vp, vp]),
+        "cbd_linear": (i32, [ctx_p, P(Matrix), i32, i32, vp, i32, vp, i32, vp]),
         "cbd_pack_int4": (i32, [vp, vp, vp, i64, i64, vp, vp]),
+        "cbd_profile_begin": (i32, [ctx_p, ctypes.c_uint32, i32]),
+        "cbd_profile_end": (i32, [ctx_p, P(KernelTime)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -272,9 +283,23 @@ class Engine:
         _check(self.lib.greedy_argmax(self.ctx, logits_dev.data_ptr(), int(logits_dev.shape[0]),
                                       tokens_dev.data_ptr(), _stream_ptr(stream)))
 
-    def linear(self, w_ptrs: Matrix, N: int, K: int, x_dev, y_dev, stream=None) -> None:
+    def linear(self, w_ptrs: Matrix, N: int, K: int, x_dev, y_dev, splits: int = 0, stream=None) -> None:
+        """y_dev[b] = W x_dev[b]; x_dev fp32 [rows, K] device tensor, y_dev fp32 [rows, N]."""
         _check(self.lib.cbd_linear(self.ctx, ctypes.byref(w_ptrs), int(N), int(K), x_dev.data_ptr(),
-                                   int(x_dev.shape[0]), y_dev.data_ptr(), _stream_ptr(stream)))
+                                   int(x_dev.shape[0]), y_dev.data_ptr(), int(splits), _stream_ptr(stream)))
+
+    # -- per-kernel event timing
+    def profile_begin(self, kinds: Sequence[str], max_launches: int = 1 << 16) -> None:
+        mask = 0
+        for k in kinds:
+            mask |= 1 << KERNEL_KINDS.index(k)
+        _check(self.lib.cbd_profile_begin(self.ctx, mask, int(max_launches)))
+
+    def profile_end(self) -> Dict[str, Dict[str, float]]:
+        out = (KernelTime * len(KERNEL_KINDS))()
+        _check(self.lib.cbd_profile_end(self.ctx, out))
+        return {k: {"launches": out[i].launches, "total_ms": out[i].total_ms, "bytes": out[i].bytes,
+                    "flops": out[i].flops} for i, k in enumerate(KERNEL_KINDS) if out[i].launches}
 
     # -- host-only calls without torch (validation tests)
     def decode_step_batch_raw(self, seq_ids: Sequence[int], tokens_ptr=None, logits_ptr=None) -> int:

@@ -27,8 +27,8 @@ constexpr int TILE = 64;
 template <int DH, int G>
 __global__ __launch_bounds__(256) void attention_kernel(const float* qkv, int ld_qkv, const RowMeta* meta,
                                                         const AttnItem* items, int n_heads, int n_kv_heads, int layer,
-                                                        const uint8_t* arena, uint16_t* out, int ld_out,
-                                                        float* part_o, float* part_ml) {
+                                                        const uint8_t* arena, uint16_t* out, int64_t out_plane,
+                                                        int ld_out, float* part_o, float* part_ml) {
   constexpr int KROW = DH + 8;          // padded LDS row (elements) against bank conflicts
   constexpr int CH = DH / 8;            // 16-byte chunks per key row
   constexpr int QD = DH / 4;            // dims per thread in the score phase
@@ -155,7 +155,11 @@ __global__ __launch_bounds__(256) void attention_kernel(const float* qkv, int ld
     for (int g2 = 0; g2 < KGROUPS; ++g2) acc += red[g2][h][d];
     const int head = j * G + h;
     if (it.part < 0) {
-      out[(int64_t)it.row * ld_out + head * DH + d] = (uint16_t)f32_to_bf16(acc / ml_s[h][1]);
+      const float v = acc / ml_s[h][1];
+      const uint32_t hi = f32_to_bf16(v);
+      const int64_t o = (int64_t)it.row * ld_out + head * DH + d;
+      out[o] = (uint16_t)hi;
+      out[o + out_plane] = (uint16_t)f32_to_bf16(v - bf16_to_f32(hi));
     } else {
       part_o[((int64_t)it.part * n_heads + head) * DH + d] = acc;
       if (d == 0) {
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const float* qkv, int ld
 
 // row_parts[row] = (first partial slot, count); count 0 = row written directly.
 __global__ void attn_combine_kernel(const float* part_o, const float* part_ml, const int2* row_parts, int n_heads,
-                                    int head_dim, uint16_t* out, int ld_out) {
+                                    int head_dim, uint16_t* out, int64_t out_plane, int ld_out) {
   const int row = blockIdx.x, head = blockIdx.y;
   const int2 rp = row_parts[row];
   if (rp.y == 0) return;
@@ -182,26 +186,30 @@ __global__ void attn_combine_kernel(const float* part_o, const float* part_ml, c
       acc += w * part_o[slot * head_dim + d];
       l += w * part_ml[slot * 2 + 1];
     }
-    out[(int64_t)row * ld_out + head * head_dim + d] = (uint16_t)f32_to_bf16(acc / l);
+    const float v = acc / l;
+    const uint32_t hi = f32_to_bf16(v);
+    const int64_t o = (int64_t)row * ld_out + head * head_dim + d;
+    out[o] = (uint16_t)hi;
+    out[o + out_plane] = (uint16_t)f32_to_bf16(v - bf16_to_f32(hi));
   }
 }
 
 template <int DH>
 static hipError_t launch_attn_dh(int G, dim3 grid, hipStream_t st, const float* qkv, int ld_qkv, const RowMeta* meta,
                                  const AttnItem* items, int n_heads, int n_kv_heads, int layer, const uint8_t* arena,
-                                 uint16_t* out, int ld_out, float* part_o, float* part_ml) {
+                                 uint16_t* out, int64_t out_plane, int ld_out, float* part_o, float* part_ml) {
   switch (G) {
     case 1:
       hipLaunchKernelGGL((attention_kernel<DH, 1>), grid, dim3(256), 0, st, qkv, ld_qkv, meta, items, n_heads,
-                         n_kv_heads, layer, arena, out, ld_out, part_o, part_ml);
+                         n_kv_heads, layer, arena, out, out_plane, ld_out, part_o, part_ml);
       break;
     case 2:
       hipLaunchKernelGGL((attention_kernel<DH, 2>), grid, dim3(256), 0, st, qkv, ld_qkv, meta, items, n_heads,
-                         n_kv_heads, layer, arena, out, ld_out, part_o, part_ml);
+                         n_kv_heads, layer, arena, out, out_plane, ld_out, part_o, part_ml);
       break;
     case 4:
       hipLaunchKernelGGL((attention_kernel<DH, 4>), grid, dim3(256), 0, st, qkv, ld_qkv, meta, items, n_heads,
-                         n_kv_heads, layer, arena, out, ld_out, part_o, part_ml);
+                         n_kv_heads, layer, arena, out, out_plane, ld_out, part_o, part_ml);
       break;
     default:
       return hipErrorInvalidValue;
@@ -211,25 +219,24 @@ static hipError_t launch_attn_dh(int G, dim3 grid, hipStream_t st, const float* 
 
 hipError_t launch_attention(const float* qkv, int ld_qkv, const RowMeta* meta, const AttnItem* items, int n_items,
                             int n_heads, int n_kv_heads, int head_dim, int layer, const uint8_t* arena,
-                            uint16_t* out, int ld_out, float* part_o, float* part_ml, int max_parts,
+                            uint16_t* out, int64_t out_plane, int ld_out, float* part_o, float* part_ml,
                             hipStream_t st) {
-  (void)max_parts;
   const int G = n_heads / n_kv_heads;
   dim3 grid(n_items, n_kv_heads);
   if (head_dim == 128)
-    return launch_attn_dh<128>(G, grid, st, qkv, ld_qkv, meta, items, n_heads, n_kv_heads, layer, arena, out, ld_out,
-                               part_o, part_ml);
+    return launch_attn_dh<128>(G, grid, st, qkv, ld_qkv, meta, items, n_heads, n_kv_heads, layer, arena, out,
+                               out_plane, ld_out, part_o, part_ml);
   if (head_dim == 64)
-    return launch_attn_dh<64>(G, grid, st, qkv, ld_qkv, meta, items, n_heads, n_kv_heads, layer, arena, out, ld_out,
-                              part_o, part_ml);
+    return launch_attn_dh<64>(G, grid, st, qkv, ld_qkv, meta, items, n_heads, n_kv_heads, layer, arena, out,
+                              out_plane, ld_out, part_o, part_ml);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const int32_t* row_parts, int rows,
-                               int n_heads, int head_dim, int max_parts, uint16_t* out, int ld_out, hipStream_t st) {
-  (void)max_parts;
+                               int n_heads, int head_dim, uint16_t* out, int64_t out_plane, int ld_out,
+                               hipStream_t st) {
   hipLaunchKernelGGL(attn_combine_kernel, dim3(rows, n_heads), dim3(head_dim), 0, st, part_o, part_ml,
-                     reinterpret_cast<const int2*>(row_parts), n_heads, head_dim, out, ld_out);
+                     reinterpret_cast<const int2*>(row_parts), n_heads, head_dim, out, out_plane, ld_out);
   return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 
 // bf16 <-> fp32 on raw bit patterns. fp32 -> bf16 rounds to nearest even.
 CBD_DEVICE float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }

@@ -1,6 +1,7 @@
-// Row-wise kernels of the decode step: embedding gather + RMSNorm, RMSNorm,
-// RoPE at each row's own position + K/V append into its slab, greedy argmax,
-// and slab scatter/gather for seeding and inspection.
+// Row-wise kernels of the decode step: embedding gather (with the first
+// norm's gain and sums of squares), RoPE at each row's own position + K/V
+// append into its slab, greedy argmax, activation plane split, and slab
+// scatter/gather for seeding and inspection.
 //
 // Position discipline (page "Batching", section 5): a row's position is read
 // once per step from its metadata and used for both the query and the key
@@ -12,73 +13,45 @@ namespace cbd {
 
 namespace {
 
-// Sum over a 256-thread block in a fixed order (deterministic).
-CBD_DEVICE float block_sum_256(float v, float* scratch4) {
-  v = wave_sum(v);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) scratch4[wave] = v;
-  __syncthreads();
-  const float t = (scratch4[0] + scratch4[1]) + (scratch4[2] + scratch4[3]);
-  __syncthreads();
-  return t;
-}
-
-// xrow = bf16(row * inv_rms(row) * g) for an fp32 row (src_f32) or a bf16 row (src_bf16).
-template <bool BF16_SRC>
-CBD_DEVICE void norm_row_to_bf16(const void* src, int d, const uint16_t* gain, float eps, uint16_t* xrow,
-                                 float* scratch4) {
-  auto load4 = [&](int i) -> float4 {
-    if (BF16_SRC) {
-      const uint2 ev = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + i);
-      return make_float4(bf16_to_f32(ev.x & 0xFFFFu), bf16_to_f32(ev.x >> 16), bf16_to_f32(ev.y & 0xFFFFu),
-                         bf16_to_f32(ev.y >> 16));
-    }
-    return *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i);
-  };
-  float ss = 0.f;
-  for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
-    const float4 v = load4(i);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = block_sum_256(ss, scratch4);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
-    const float4 v = load4(i);
-    const uint2 gg = *reinterpret_cast<const uint2*>(gain + i);
-    uint2 o;
-    o.x = pack_bf16x2(v.x * inv * bf16_to_f32(gg.x & 0xFFFFu), v.y * inv * bf16_to_f32(gg.x >> 16));
-    o.y = pack_bf16x2(v.z * inv * bf16_to_f32(gg.y & 0xFFFFu), v.w * inv * bf16_to_f32(gg.y >> 16));
-    *reinterpret_cast<uint2*>(xrow + i) = o;
-  }
+CBD_DEVICE void split_store(uint16_t* hi, uint16_t* lo, float v) {
+  const uint32_t h = f32_to_bf16(v);
+  *hi = (uint16_t)h;
+  *lo = (uint16_t)f32_to_bf16(v - bf16_to_f32(h));
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tokens, const uint16_t* embed, int vocab,
-                                                         int d, const uint16_t* gain, float eps, float* h,
-                                                         uint16_t* xn) {
-  __shared__ float scratch[4];
+// One block per row. Thread i handles features [16i, 16i+16): it writes h,
+// the planes of gain * h and the partial sum of squares of its 16 features.
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, const uint16_t* embed, int vocab, int d,
+                                                    const uint16_t* gain, float* h, uint16_t* xp, int64_t plane,
+                                                    float* ss, int ss_ld) {
   const int r = blockIdx.x;
   int tok = tokens[r];
   tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);  // ids stay on the device: clamp out-of-range ids
   const uint16_t* e = embed + (int64_t)tok * d;
   float* hrow = h + (int64_t)r * d;
-  for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
-    const uint2 ev = *reinterpret_cast<const uint2*>(e + i);
-    float4 v = make_float4(bf16_to_f32(ev.x & 0xFFFFu), bf16_to_f32(ev.x >> 16), bf16_to_f32(ev.y & 0xFFFFu),
-                           bf16_to_f32(ev.y >> 16));
-    *reinterpret_cast<float4*>(hrow + i) = v;
+  uint16_t* xr = xp + (int64_t)r * d;
+  for (int t = threadIdx.x; t < d / 16; t += 256) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int f = 16 * t + i;
+      const float v = bf16_to_f32(e[f]);
+      hrow[f] = v;
+      s += v * v;
+      split_store(xr + f, xr + plane + f, v * bf16_to_f32(gain[f]));
+    }
+    ss[(int64_t)t * ss_ld + r] = s;
   }
-  // the norm reads the embedding row again (not h) so no thread reads another thread's global writes
-  norm_row_to_bf16<true>(e, d, gain, eps, xn + (int64_t)r * d, scratch);
 }
 
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const int32_t* row_idx, int d,
-                                                      const uint16_t* gain, float eps, uint16_t* xn) {
-  __shared__ float scratch[4];
+__global__ __launch_bounds__(256) void split_planes_kernel(const float* x, int K, uint16_t* out, int64_t plane) {
   const int r = blockIdx.x;
-  const int src = row_idx ? row_idx[r] : r;
-  norm_row_to_bf16<false>(h + (int64_t)src * d, d, gain, eps, xn + (int64_t)r * d, scratch);
+  for (int i = threadIdx.x; i < K; i += 256) {
+    const int64_t o = (int64_t)r * K + i;
+    split_store(out + o, out + plane + o, x[o]);
+  }
 }
 
 // rope_cs: [max_pos][head_dim/2] (cos, sin) pairs, fp32 values of angles computed in fp64.
@@ -176,15 +149,16 @@ __global__ __launch_bounds__(256) void slab_copy_kernel(uint8_t* arena, int64_t 
   }
 }
 
-hipError_t launch_embed_norm(const int32_t* tokens, int rows, const uint16_t* embed, int vocab, int d,
-                             const uint16_t* gain, float eps, float* h, uint16_t* xn, hipStream_t st) {
-  hipLaunchKernelGGL(embed_norm_kernel, dim3(rows), dim3(256), 0, st, tokens, embed, vocab, d, gain, eps, h, xn);
+hipError_t launch_embed(const int32_t* tokens, int rows, const uint16_t* embed, int vocab, int d,
+                        const uint16_t* gain, float* h, uint16_t* xplanes, int64_t plane, float* ss, int ss_ld,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(256), 0, st, tokens, embed, vocab, d, gain, h, xplanes, plane, ss,
+                     ss_ld);
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(const float* h, const int32_t* row_idx, int rows, int d, const uint16_t* gain, float eps,
-                          uint16_t* xn, hipStream_t st) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, st, h, row_idx, d, gain, eps, xn);
+hipError_t launch_split_planes(const float* x, int rows, int K, uint16_t* out, int64_t plane, hipStream_t st) {
+  hipLaunchKernelGGL(split_planes_kernel, dim3(rows), dim3(256), 0, st, x, K, out, plane);
   return hipGetLastError();
 }
 

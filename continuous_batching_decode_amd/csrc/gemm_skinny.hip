@@ -1,28 +1,43 @@
 // Batched weight-streaming product for the decode step and its prefill.
 //
-// y[b, n] = sum_k W[n, k] x[b, k] for up to 64 rows b per launch column-block.
+// y[b, n] = sum_k W[n, k] x[b, k] for up to 64 activation rows per column block.
 // The page "Continuous Decode Batching - the transformer capture" (section
 // "The throughput law") is the reason for the shape of this kernel: the
 // weight read w is paid once per launch whatever the number of rows, so the
-// kernel is organised around streaming W from HBM exactly once with wide,
-// coalesced loads, and every row of the batch rides on that single read.
+// kernel streams W from HBM exactly once with wide coalesced loads and every
+// row of the batch rides on that single read.
 //
 // Mapping (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
-//  - A operand = 16 consecutive weight rows x 32 inputs (one 16-byte load
-//    per lane: lane l reads row l%16, inputs 8*(l/16)..+7).
-//  - B operand = 16 batch rows x the same 32 inputs of the bf16 activations.
-//  - A workgroup (4 waves) owns RT row-subtiles of 16 weight rows and covers
-//    the whole input dimension; each wave takes a contiguous quarter of K,
-//    and the four partial sums are added in a fixed order through LDS, so the
-//    result does not depend on scheduling.
-//  - NB column tiles of 16 cover B <= 16*NB rows; padding rows of the
-//    activation buffer only affect padding outputs (an MFMA output column
-//    depends only on the same column of B), which are never stored.
+//  - A operand = 16 consecutive weight rows x 32 inputs, loaded straight from
+//    HBM (one 16-byte load per lane: lane l reads row l%16, inputs
+//    8*(l/16)..+7), double-buffered in registers.
+//  - B operand = 16 activation rows x the same 32 inputs, read from LDS: the
+//    workgroup stages each chunk of the activations once and its 4 waves
+//    share it, so the vector-memory path carries (almost) only weights.
+//  - A workgroup = 4 waves x RT subtiles of 16 weight rows. The input dim is
+//    split over S workgroups when the matrix is too small to fill the chip;
+//    their partial tiles go to a workspace and the last workgroup to finish
+//    (an atomic arrival counter, reset by that workgroup) adds them in a
+//    fixed order and runs the epilogue, so results are deterministic.
+//  - NB column tiles of 16 cover up to 16*NB activation rows; padding rows
+//    only affect padding outputs (an MFMA output column depends only on the
+//    same column of B), which are never stored.
+// Activations are carried as two bf16 planes, x = hi + lo with hi = bf16(x)
+// and lo = bf16(x - hi), so the product keeps about 16 significant bits of x
+// (two MFMAs per weight fragment; the products are exact in fp32).
+//
+// RMSNorm is folded in algebraically: the producer of x writes g * h (the
+// gain applied, the 1/rms scale not) together with per-16-feature partial
+// sums of squares of h; the consumer multiplies its fp32 accumulators by
+// 1/sqrt(sum/d + eps) in the epilogue, since W (g * h / rms) = (W (g * h)) / rms.
+//
 // int4 weights (4-bit affine, groups of 64 inputs): codes are widened to the
-// bf16 values 128+q with one and-or per pair and multiplied on the MFMA
-// unit; the affine map is applied once per group and output:
+// bf16 values 128+q with one and-or per pair and multiplied on the MFMA unit;
+// the affine map is applied once per group and output:
 //   sum_k x_k (s q_k + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * sum_k x_k,
 // where sum_k x_k over the group comes from one more MFMA with an all-ones A.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -30,14 +45,16 @@ namespace cbd {
 
 namespace {
 
-template <int N>
-struct Frag {
-  bf16x8_t v[N];
-};
-
-CBD_DEVICE bf16x8_t load_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
-
 CBD_DEVICE bf16x8_t as_frag(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+CBD_DEVICE bf16x8_t as_frag(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// weights are read once per launch: non-temporal loads keep them from
+// evicting the activations, partial tiles and K/V held in the caches
+CBD_DEVICE u32x4_t load_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+CBD_DEVICE bf16x8_t lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
 // 8 int4 codes of one packed word -> bf16 (128 + q) in input order.
 CBD_DEVICE bf16x8_t widen_codes(uint32_t w) {
@@ -55,44 +72,78 @@ CBD_DEVICE f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 
 CBD_DEVICE float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// Locate the first weight row of a 16-row subtile in the concatenated segments.
 CBD_DEVICE int seg_of(const SkinnyArgs& a, int grow) {
   return grow < a.seg_end[0] ? 0 : (grow < a.seg_end[1] ? 1 : 2);
 }
 CBD_DEVICE int seg_begin(const SkinnyArgs& a, int s) { return s == 0 ? 0 : a.seg_end[s - 1]; }
 
+// 4 consecutive values -> hi/lo bf16 planes (8 bytes each)
+CBD_DEVICE void store_split4(uint16_t* hi, uint16_t* lo, float v0, float v1, float v2, float v3) {
+  const uint32_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1), h2 = f32_to_bf16(v2), h3 = f32_to_bf16(v3);
+  uint2 H, L;
+  H.x = h0 | (h1 << 16);
+  H.y = h2 | (h3 << 16);
+  L.x = f32_to_bf16(v0 - bf16_to_f32(h0)) | (f32_to_bf16(v1 - bf16_to_f32(h1)) << 16);
+  L.y = f32_to_bf16(v2 - bf16_to_f32(h2)) | (f32_to_bf16(v3 - bf16_to_f32(h3)) << 16);
+  *reinterpret_cast<uint2*>(hi) = H;
+  *reinterpret_cast<uint2*>(lo) = L;
+}
+
 }  // namespace
+
+// LDS bytes of one launch: activation chunk (2 planes) + norm partial sums.
+size_t skinny_lds_bytes(int nb, int kc) { return (size_t)2 * 16 * nb * (kc + 8) * 2 + (size_t)16 * 16 * nb * 4; }
 
 template <int RT, int NB, int EPI, int FMT, int UC>
 __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int ROWS = 16 * NB;
+  constexpr int NACC = RT * NB * 4;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int tile = blockIdx.x;
-  const int xblk = blockIdx.y;
+  const int blk = blockIdx.x;
+  const int split = blockIdx.y;
+  const int S = gridDim.y;
+  const int xblk = blockIdx.z;
   const int K = a.K;
-  const int kw = K >> 2;  // each wave: a contiguous quarter of the inputs
-  const int k0 = wave * kw;
+  const int Kr = K / S;
+  const int kbeg = split * Kr;
+  const int KC = a.kc;
+  const int XROW = KC + 8;  // padded LDS row (elements): consecutive rows start 16 bytes apart mod the bank width
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  float* norm_part = reinterpret_cast<float*>(smem + (size_t)2 * ROWS * XROW * 2);  // [16][ROWS]
+  __shared__ int s_last;
 
-  const uint16_t* X = a.x + (int64_t)xblk * (16 * NB) * (int64_t)a.ldx;
-  const int rows_valid = min(16 * NB, a.rows - xblk * 16 * NB);
+  const int col0 = xblk * ROWS;
+  const int rows_valid = min(ROWS, a.rows - col0);
 
-  // weight-row subtiles of this workgroup
-  int sub_row[RT];   // concatenated row index of subtile i (first of 16)
-  int sub_seg[RT];
+  // -- 1/rms partial sums for this block's activation rows: 16 fixed groups of tiles
+  if (a.ss) {
+    const int per = a.ss_tiles / 16;
+    for (int i = threadIdx.x; i < 16 * ROWS; i += 256) {
+      const int c = i % ROWS, grp = i / ROWS;
+      float s = 0.f;
+      if (c < rows_valid) {
+        const int row = a.x_rows ? a.x_rows[col0 + c] : col0 + c;
+        const float* p = a.ss + (int64_t)grp * per * a.ss_ld + row;
+        for (int t = 0; t < per; ++t) s += p[(int64_t)t * a.ss_ld];
+      }
+      norm_part[grp * ROWS + c] = s;
+    }
+  }
+
+  // weight-row subtiles of this wave
+  int sub_row[RT];
 #pragma unroll
   for (int i = 0; i < RT; ++i) {
-    int grow;
-    if (EPI == EPI_SWIGLU) {
-      // first half of the subtiles from the gate segment, second half from up
-      const int half = RT / 2;
-      grow = (i < half) ? tile * 16 * half + 16 * i : a.seg_end[0] + tile * 16 * half + 16 * (i - half);
+    if constexpr (EPI == EPI_SWIGLU) {  // RT == 2: the gate and up rows of the same 16 features
+      const int f0 = blk * 64 + 16 * wave;
+      sub_row[i] = i == 0 ? f0 : a.seg_end[0] + f0;
     } else {
-      grow = tile * 16 * RT + 16 * i;
+      sub_row[i] = blk * 64 * RT + wave * 16 * RT + 16 * i;
     }
-    sub_row[i] = grow;
-    sub_seg[i] = seg_of(a, grow);
   }
 
   f32x4_t acc[RT][NB];
@@ -101,90 +152,121 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* xr[NB];
-#pragma unroll
-  for (int c = 0; c < NB; ++c) xr[c] = X + (int64_t)(16 * c + r16) * a.ldx;
+  // stage activation chunk [kc0, kc0 + KC) of this block's rows into LDS
+  auto stage_x = [&](int kc0) {
+    __syncthreads();  // the previous chunk has been consumed
+    const int per_row = KC / 8;
+    for (int idx = threadIdx.x; idx < 2 * ROWS * per_row; idx += 256) {
+      const int plane = idx / (ROWS * per_row);
+      const int rem = idx - plane * ROWS * per_row;
+      const int r = rem / per_row, c8 = rem - r * per_row;
+      const int b = min(col0 + r, a.rows - 1);
+      const int row = a.x_rows ? a.x_rows[b] : col0 + r;
+      const uint16_t* src = a.x + (int64_t)plane * a.x_plane + (int64_t)row * a.ldx + kc0 + 8 * c8;
+      *reinterpret_cast<uint4*>(xs + (plane * ROWS + r) * XROW + 8 * c8) = *reinterpret_cast<const uint4*>(src);
+    }
+    __syncthreads();
+  };
 
-  if (FMT == FMT_BF16) {
+  const int spc = KC / ((FMT == FMT_BF16 ? 32 : 128) * UC);  // k-steps per chunk
+  const int total = Kr / ((FMT == FMT_BF16 ? 32 : 128) * UC);
+
+  if constexpr (FMT == FMT_BF16) {
     const uint16_t* wr[RT];
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      const int s = sub_seg[i];
+      const int s = seg_of(a, sub_row[i]);
       const int local = sub_row[i] - seg_begin(a, s) + r16;
-      wr[i] = reinterpret_cast<const uint16_t*>(a.w[s]) + (int64_t)local * K + 8 * g;
+      wr[i] = reinterpret_cast<const uint16_t*>(a.w[s]) + (int64_t)local * K + kbeg + 8 * g;
     }
-    for (int k = k0; k < k0 + kw; k += 32 * UC) {
-      bf16x8_t A[UC][RT], Bv[UC][NB];
+    u32x4_t A0[UC][RT], A1[UC][RT];
+    auto loadw = [&](u32x4_t (&A)[UC][RT], int st) {
 #pragma unroll
       for (int u = 0; u < UC; ++u)
 #pragma unroll
-        for (int i = 0; i < RT; ++i) A[u][i] = load_frag(wr[i] + k + 32 * u);
+        for (int i = 0; i < RT; ++i) A[u][i] = load_stream(wr[i] + (st * UC + u) * 32);
+    };
+    auto compute = [&](const u32x4_t (&A)[UC][RT], int st) {
+      const int koff = ((st % spc) * UC) * 32 + 8 * g;
 #pragma unroll
       for (int u = 0; u < UC; ++u)
 #pragma unroll
-        for (int c = 0; c < NB; ++c) Bv[u][c] = load_frag(xr[c] + k + 32 * u + 8 * g);
+        for (int c = 0; c < NB; ++c) {
+          const bf16x8_t xh = lds_frag(xs + (16 * c + r16) * XROW + koff + 32 * u);
+          const bf16x8_t xl = lds_frag(xs + (ROWS + 16 * c + r16) * XROW + koff + 32 * u);
 #pragma unroll
-      for (int u = 0; u < UC; ++u)
-#pragma unroll
-        for (int i = 0; i < RT; ++i)
-#pragma unroll
-          for (int c = 0; c < NB; ++c) acc[i][c] = mfma(A[u][i], Bv[u][c], acc[i][c]);
+          for (int i = 0; i < RT; ++i) {
+            acc[i][c] = mfma(as_frag(A[u][i]), xh, acc[i][c]);
+            acc[i][c] = mfma(as_frag(A[u][i]), xl, acc[i][c]);
+          }
+        }
+    };
+    loadw(A0, 0);
+    for (int st = 0; st < total; st += 2) {
+      if (st % spc == 0) stage_x(kbeg + (st / spc) * KC);
+      if (st + 1 < total) loadw(A1, st + 1);
+      compute(A0, st);
+      if (st + 1 < total) {
+        if ((st + 1) % spc == 0) stage_x(kbeg + ((st + 1) / spc) * KC);
+        if (st + 2 < total) loadw(A0, st + 2);
+        compute(A1, st + 1);
+      }
     }
   } else {
-    // int4: 128 inputs per block; lane group g reads words 4g..4g+3 of the block
+    // int4: 128 inputs per step; lane group g reads words 4g..4g+3 of each 128-input block
     const uint32_t* wr[RT];
     const uint16_t* ar[RT];
     int seg_rows[RT];
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      const int s = sub_seg[i];
+      const int s = seg_of(a, sub_row[i]);
       const int sb = seg_begin(a, s);
       const int local = sub_row[i] - sb + r16;
-      wr[i] = reinterpret_cast<const uint32_t*>(a.w[s]) + (int64_t)local * (K >> 3) + 4 * g;
+      wr[i] = reinterpret_cast<const uint32_t*>(a.w[s]) + (int64_t)local * (K >> 3) + (kbeg >> 3) + 4 * g;
       seg_rows[i] = a.seg_end[s] - sb;
-      // scale/bias pairs of output rows 4*g .. 4*g+3 of the subtile
       ar[i] = reinterpret_cast<const uint16_t*>(a.aux[s]) + (int64_t)(sub_row[i] - sb + 4 * g) * 2;
     }
     const uint4 ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const bf16x8_t ones = as_frag(ones_u);
-    for (int k = k0; k < k0 + kw; k += 128 * UC) {
-      uint4 Wq[UC][RT];
+    for (int st = 0; st < total; ++st) {
+      if (st % spc == 0) stage_x(kbeg + (st / spc) * KC);
+      u32x4_t Wq[UC][RT];
       uint4 SB[UC][RT][2];
-      bf16x8_t Bv[UC][4][NB];
 #pragma unroll
       for (int u = 0; u < UC; ++u)
 #pragma unroll
-        for (int i = 0; i < RT; ++i) Wq[u][i] = *reinterpret_cast<const uint4*>(wr[i] + ((k + 128 * u) >> 3));
-#pragma unroll
-      for (int u = 0; u < UC; ++u)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int c = 0; c < NB; ++c)
-            Bv[u][j][c] = load_frag(xr[c] + k + 128 * u + 64 * (j >> 1) + 16 * g + 8 * (j & 1));
-#pragma unroll
-      for (int u = 0; u < UC; ++u)
-#pragma unroll
-        for (int i = 0; i < RT; ++i)
+        for (int i = 0; i < RT; ++i) {
+          Wq[u][i] = load_stream(wr[i] + (st * UC + u) * 16);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const int grp = ((k + 128 * u) >> 6) + h;
+            const int grp = ((kbeg + (st * UC + u) * 128) >> 6) + h;
             SB[u][i][h] = *reinterpret_cast<const uint4*>(ar[i] + (int64_t)grp * seg_rows[i] * 2);
           }
+        }
 #pragma unroll
-      for (int u = 0; u < UC; ++u)
+      for (int u = 0; u < UC; ++u) {
+        const int kb = ((st % spc) * UC + u) * 128;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          f32x4_t xs[NB];
+          bf16x8_t X[2][NB][2];
+          f32x4_t xsum[NB];
 #pragma unroll
           for (int c = 0; c < NB; ++c) {
-            xs[c] = mfma(ones, Bv[u][2 * h][c], f32x4_t{0.f, 0.f, 0.f, 0.f});
-            xs[c] = mfma(ones, Bv[u][2 * h + 1][c], xs[c]);
+            f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              const int off = kb + 64 * h + 16 * g + 8 * jj;
+              X[jj][c][0] = lds_frag(xs + (16 * c + r16) * XROW + off);
+              X[jj][c][1] = lds_frag(xs + (ROWS + 16 * c + r16) * XROW + off);
+              t = mfma(ones, X[jj][c][0], t);
+              t = mfma(ones, X[jj][c][1], t);
+            }
+            xsum[c] = t;
           }
 #pragma unroll
           for (int i = 0; i < RT; ++i) {
-            const uint32_t w0 = h ? Wq[u][i].z : Wq[u][i].x;
-            const uint32_t w1 = h ? Wq[u][i].w : Wq[u][i].y;
+            const uint32_t w0 = h ? Wq[u][i][2] : Wq[u][i][0];
+            const uint32_t w1 = h ? Wq[u][i][3] : Wq[u][i][1];
             const bf16x8_t A0 = widen_codes(w0), A1 = widen_codes(w1);
             const uint4 sb = SB[u][i][h];
             float sc[4], bc[4];
@@ -196,65 +278,117 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
             }
 #pragma unroll
             for (int c = 0; c < NB; ++c) {
-              f32x4_t t = mfma(A0, Bv[u][2 * h][c], f32x4_t{0.f, 0.f, 0.f, 0.f});
-              t = mfma(A1, Bv[u][2 * h + 1][c], t);
+              f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int e = 0; e < 4; ++e) acc[i][c][e] += sc[e] * t[e] + bc[e] * xs[c][e];
+              for (int p = 0; p < 2; ++p) {
+                t = mfma(A0, X[0][c][p], t);
+                t = mfma(A1, X[1][c][p], t);
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][c][e] += sc[e] * t[e] + bc[e] * xsum[c][e];
             }
           }
         }
+      }
     }
   }
 
-  // fixed-order reduction of the four K quarters through LDS
-  __shared__ float red[3][RT * NB * 4][64];
-  if (wave > 0) {
+  // -- split-K: partial tiles to the workspace; the last workgroup of the row block adds them.
+  // Partial tiles and the arrival counter are written and read with agent-scope
+  // atomic accesses, which the hardware performs at the level where all XCDs'
+  // L2 caches agree; each wave waits for its stores to be acknowledged
+  // (vmcnt 0) before the workgroup's arrival is counted. This avoids the full
+  // L2 write-back and invalidate that a device-wide fence costs per workgroup.
+  if (S > 1) {
+    float* base = a.part + (int64_t)blk * S * 4 * NACC * 64;
+    float* mine = base + ((int64_t)split * 4 + wave) * NACC * 64;
 #pragma unroll
     for (int i = 0; i < RT; ++i)
 #pragma unroll
       for (int c = 0; c < NB; ++c)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[wave - 1][(i * NB + c) * 4 + e][lane] = acc[i][c][e];
+        for (int e = 0; e < 4; ++e)
+          __hip_atomic_store(mine + ((i * NB + c) * 4 + e) * 64 + lane, acc[i][c][e], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(a.counters + blk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    __syncthreads();
+    if (!s_last) return;
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+      const float* src = base + ((int64_t)s * 4 + wave) * NACC * 64;
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int c = 0; c < NB; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][c][e] += __hip_atomic_load(src + ((i * NB + c) * 4 + e) * 64 + lane, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(a.counters + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  if (wave != 0) return;
+
+  float inv[NB];
 #pragma unroll
-  for (int w = 0; w < 3; ++w)
-#pragma unroll
-    for (int i = 0; i < RT; ++i)
-#pragma unroll
-      for (int c = 0; c < NB; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][c][e] += red[w][(i * NB + c) * 4 + e][lane];
+  for (int c = 0; c < NB; ++c) {
+    inv[c] = 1.f;
+    if (a.ss) {
+      float s = 0.f;
+      for (int grp = 0; grp < 16; ++grp) s += norm_part[grp * ROWS + 16 * c + r16];
+      inv[c] = 1.0f / sqrtf(s / a.norm_dim + a.eps);
+    }
+  }
 
   // epilogue: lane holds y[b = 16c + l%16][n = subtile + 4*(l/16) + e]
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
     const int b = 16 * c + r16;
-    if (b >= rows_valid) continue;
-    const int64_t orow = (int64_t)(xblk * 16 * NB + b) * a.ldo;
-    if (EPI == EPI_SWIGLU) {
-      const int half = RT / 2;
+    const bool valid = b < rows_valid;
+    const int64_t orow = (int64_t)(col0 + b) * a.ldo;
+    if constexpr (EPI == EPI_SWIGLU) {
+      static_assert(RT == 2, "gate and up subtiles");
+      const int n = sub_row[0] + 4 * g;
+      float m[4];
 #pragma unroll
-      for (int i = 0; i < half; ++i) {
-        const int n = tile * 16 * half + 16 * i + 4 * g;
-        const f32x4_t gt = acc[i][c], up = acc[i + half][c];
-        uint2 o;
-        o.x = pack_bf16x2(silu_f(gt[0]) * up[0], silu_f(gt[1]) * up[1]);
-        o.y = pack_bf16x2(silu_f(gt[2]) * up[2], silu_f(gt[3]) * up[3]);
-        *reinterpret_cast<uint2*>(a.out_bf16 + orow + n) = o;
+      for (int e = 0; e < 4; ++e) m[e] = silu_f(acc[0][c][e] * inv[c]) * (acc[1][c][e] * inv[c]);
+      if (valid) store_split4(a.out_x + orow + n, a.out_x + a.out_plane + orow + n, m[0], m[1], m[2], m[3]);
+    } else if constexpr (EPI == EPI_RESIDUAL) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const int n = sub_row[i] + 4 * g;
+        float4 hn = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) {
+          float4* p = reinterpret_cast<float4*>(a.out + orow + n);
+          const float4 h = *p;
+          hn = make_float4(h.x + acc[i][c][0], h.y + acc[i][c][1], h.z + acc[i][c][2], h.w + acc[i][c][3]);
+          *p = hn;
+          if (a.next_gain) {
+            const uint2 gg = *reinterpret_cast<const uint2*>(a.next_gain + n);
+            store_split4(a.out_x + orow + n, a.out_x + a.out_plane + orow + n, hn.x * bf16_to_f32(gg.x & 0xFFFFu),
+                         hn.y * bf16_to_f32(gg.x >> 16), hn.z * bf16_to_f32(gg.y & 0xFFFFu),
+                         hn.w * bf16_to_f32(gg.y >> 16));
+          }
+        }
+        if (a.ss_out) {
+          float s = hn.x * hn.x + hn.y * hn.y + hn.z * hn.z + hn.w * hn.w;
+          s += __shfl_xor(s, 16, 64);
+          s += __shfl_xor(s, 32, 64);
+          if (valid && g == 0) a.ss_out[(int64_t)(sub_row[i] >> 4) * a.ss_out_ld + col0 + b] = s;
+        }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < RT; ++i) {
         const int n = sub_row[i] + 4 * g;
-        float4* p = reinterpret_cast<float4*>(a.out + orow + n);
-        float4 v = make_float4(acc[i][c][0], acc[i][c][1], acc[i][c][2], acc[i][c][3]);
-        if (EPI == EPI_RESIDUAL) {
-          const float4 h = *p;
-          v.x += h.x; v.y += h.y; v.z += h.z; v.w += h.w;
-        }
-        *p = v;
+        if (valid)
+          *reinterpret_cast<float4*>(a.out + orow + n) =
+              make_float4(acc[i][c][0] * inv[c], acc[i][c][1] * inv[c], acc[i][c][2] * inv[c], acc[i][c][3] * inv[c]);
       }
     }
   }
@@ -262,37 +396,83 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
 
 // ----------------------------------------------------------------------------- launcher
 
+bool skinny_shape_ok(int fmt, int K) { return fmt == FMT_INT4 ? K % 512 == 0 : K % 256 == 0; }
+
 template <int RT, int EPI, int FMT, int UC>
 static hipError_t launch_nb(const SkinnyArgs& a, int nb, dim3 grid, hipStream_t st) {
+  const size_t lds = skinny_lds_bytes(nb, a.kc);
   switch (nb) {
-    case 1: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 3, EPI, FMT, UC>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 4, EPI, FMT, UC>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
+    case 2: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
+    case 3: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 3, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
+    default: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 4, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
   }
   return hipGetLastError();
 }
 
-template <int RT, int EPI>
-static hipError_t launch_fmt(const SkinnyArgs& a, int fmt, int nb, dim3 grid, hipStream_t st) {
-  if (fmt == FMT_INT4) return launch_nb<RT, EPI, FMT_INT4, 1>(a, nb, grid, st);
-  if ((a.K / 4) % 128 == 0) return launch_nb<RT, EPI, FMT_BF16, 4>(a, nb, grid, st);
-  return launch_nb<RT, EPI, FMT_BF16, 2>(a, nb, grid, st);
+// Plan of one launch: subtiles per wave, split of K, LDS chunk.
+SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int splits) {
+  SkinnyPlan p{};
+  const int per_block = x_blocks > 1 ? 64 : rows;
+  p.nb = (per_block + 15) / 16;
+  p.rt = (epi == EPI_SWIGLU || N % 128 == 0) ? 2 : 1;
+  p.row_blocks = epi == EPI_SWIGLU ? N / 64 : N / (64 * p.rt);
+  const int step = fmt == FMT_INT4 ? 128 : 32;
+  p.uc = fmt == FMT_INT4 ? 1 : (p.nb > 2 ? 2 : 4);
+  const int unit = step * p.uc;                    // one k-step of a wave
+  const int kc_max = (960 / p.nb) / unit * unit;   // activation chunk: LDS stays within 64 KB
+  if (splits > 0) {
+    p.splits = splits;
+  } else if (x_blocks > 1) {
+    p.splits = 1;
+  } else {
+    // smallest split giving ~3 workgroups per CU, keeping >= 2 k-steps per wave and <= 16 partials
+    p.splits = 1;
+    for (int s = 2; s <= 16 && (long)p.row_blocks * p.splits < 768; ++s) {
+      if (K % s || (K / s) % unit || K / s < 2 * unit) continue;
+      p.splits = s;
+    }
+  }
+  const int kr = K / p.splits;
+  p.kc = unit;
+  for (int kc = unit; kc <= std::min(kr, kc_max); kc += unit)
+    if (kr % kc == 0) p.kc = kc;
+  return p;
 }
 
-bool skinny_shape_ok(int fmt, int K) { return fmt == FMT_INT4 ? K % 512 == 0 : K % 256 == 0; }
-
-hipError_t launch_skinny_gemm(const SkinnyArgs& a, int epi, int fmt, int x_blocks, hipStream_t st) {
-  // rows per column block: 16*nb with nb = ceil(min(rows, 64) / 16)
-  const int per_block = x_blocks > 1 ? 64 : a.rows;
-  const int nb = (per_block + 15) / 16;
-  if (epi == EPI_SWIGLU) {
-    dim3 grid(a.N / 16, x_blocks);
-    return launch_fmt<2, EPI_SWIGLU>(a, fmt, nb, grid, st);
+hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st) {
+  if (p.splits < 1 || a.K % p.splits || (x_blocks > 1 && p.splits > 1)) return hipErrorInvalidValue;
+  const int kr = a.K / p.splits;
+  const int unit = (fmt == FMT_INT4 ? 128 : 32) * p.uc;
+  if (kr % p.kc || p.kc % unit) return hipErrorInvalidValue;
+  if (p.splits > 1 && (!a.part || !a.counters)) return hipErrorInvalidValue;
+  a.kc = p.kc;
+  const dim3 grid(p.row_blocks, p.splits, x_blocks);
+  if (fmt == FMT_INT4) {
+    if (epi == EPI_SWIGLU) return launch_nb<2, EPI_SWIGLU, FMT_INT4, 1>(a, p.nb, grid, st);
+    if (p.rt == 1) {
+      if (epi == EPI_RESIDUAL) return launch_nb<1, EPI_RESIDUAL, FMT_INT4, 1>(a, p.nb, grid, st);
+      return launch_nb<1, EPI_STORE, FMT_INT4, 1>(a, p.nb, grid, st);
+    }
+    if (epi == EPI_RESIDUAL) return launch_nb<2, EPI_RESIDUAL, FMT_INT4, 1>(a, p.nb, grid, st);
+    return launch_nb<2, EPI_STORE, FMT_INT4, 1>(a, p.nb, grid, st);
   }
-  dim3 grid(a.N / 16, x_blocks);
-  if (epi == EPI_RESIDUAL) return launch_fmt<1, EPI_RESIDUAL>(a, fmt, nb, grid, st);
-  return launch_fmt<1, EPI_STORE>(a, fmt, nb, grid, st);
+  if (p.uc == 4) {
+    if (epi == EPI_SWIGLU) return launch_nb<2, EPI_SWIGLU, FMT_BF16, 4>(a, p.nb, grid, st);
+    if (p.rt == 1) {
+      if (epi == EPI_RESIDUAL) return launch_nb<1, EPI_RESIDUAL, FMT_BF16, 4>(a, p.nb, grid, st);
+      return launch_nb<1, EPI_STORE, FMT_BF16, 4>(a, p.nb, grid, st);
+    }
+    if (epi == EPI_RESIDUAL) return launch_nb<2, EPI_RESIDUAL, FMT_BF16, 4>(a, p.nb, grid, st);
+    return launch_nb<2, EPI_STORE, FMT_BF16, 4>(a, p.nb, grid, st);
+  }
+  if (epi == EPI_SWIGLU) return launch_nb<2, EPI_SWIGLU, FMT_BF16, 2>(a, p.nb, grid, st);
+  if (p.rt == 1) {
+    if (epi == EPI_RESIDUAL) return launch_nb<1, EPI_RESIDUAL, FMT_BF16, 2>(a, p.nb, grid, st);
+    return launch_nb<1, EPI_STORE, FMT_BF16, 2>(a, p.nb, grid, st);
+  }
+  if (epi == EPI_RESIDUAL) return launch_nb<2, EPI_RESIDUAL, FMT_BF16, 2>(a, p.nb, grid, st);
+  return launch_nb<2, EPI_STORE, FMT_BF16, 2>(a, p.nb, grid, st);
 }
 
 }  // namespace cbd

@@ -11,41 +11,75 @@ enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2 };
 enum { FMT_BF16 = 0, FMT_INT4 = 1 };
 
 // y = W x over up to three weight matrices stacked along the output dim.
+// Activations come as two bf16 planes (hi, lo) x_plane elements apart.
 struct SkinnyArgs {
-  const uint16_t* x;   // bf16 activations, row stride ldx; rows padded to the column block
+  const uint16_t* x;       // plane 0 (hi); plane 1 (lo) at x + x_plane; row stride ldx
+  int64_t x_plane;
   int32_t ldx;
   int32_t K;
-  int32_t rows;        // valid activation rows (all column blocks together)
-  int32_t N;           // output features (SWIGLU: ffn width; gate = segment 0, up = segment 1)
-  const void* w[3];    // per segment: bf16 [n_s, K] or int4 packed words
-  const void* aux[3];  // int4: (scale, bias) pairs [K/64, n_s, 2]
-  int32_t seg_end[3];  // cumulative row ends of the segments
-  float* out;          // STORE / RESIDUAL: fp32 [rows, ldo] (RESIDUAL adds into it)
-  uint16_t* out_bf16;  // SWIGLU: bf16 [rows, ldo]
+  int32_t rows;            // valid output rows (all column blocks together)
+  int32_t N;               // output features (SWIGLU: ffn width; gate = segment 0, up = segment 1)
+  const int32_t* x_rows;   // optional: activation row feeding output row b (gather), else b
+  const void* w[3];        // per segment: bf16 [n_s, K] or int4 packed words
+  const void* aux[3];      // int4: (scale, bias) pairs [K/64, n_s, 2]
+  int32_t seg_end[3];      // cumulative row ends of the segments
+  // input normalisation: accumulators *= 1/sqrt(sum_t ss[t][row] / norm_dim + eps) (ss == null: none)
+  const float* ss;
+  int32_t ss_tiles;        // number of 16-feature partial sums per row (a multiple of 16)
+  int32_t ss_ld;
+  float norm_dim;
+  float eps;
+  // outputs
+  float* out;              // STORE: fp32 [rows, ldo]; RESIDUAL: the fp32 residual stream (in/out)
   int32_t ldo;
+  uint16_t* out_x;         // SWIGLU: product planes; RESIDUAL: planes of next_gain * h (row stride ldo)
+  int64_t out_plane;
+  const uint16_t* next_gain;  // RESIDUAL: gain of the norm that consumes h next (null: no planes)
+  float* ss_out;           // RESIDUAL: partial sums of squares of h, [N/16][ss_out_ld]
+  int32_t ss_out_ld;
+  // split-K workspace: partial tiles and per-row-block arrival counters (zero between launches)
+  float* part;
+  int32_t* counters;
+  int32_t kc;              // activation chunk staged in LDS (set from the plan)
+};
+
+// How one launch is cut: 4 waves x rt subtiles of 16 rows per workgroup, nb column tiles,
+// K split over `splits` workgroups, activation chunks of kc inputs.
+struct SkinnyPlan {
+  int nb, rt, uc, row_blocks, splits, kc;
 };
 
 bool skinny_shape_ok(int fmt, int K);
-// x_blocks > 1: activations come in blocks of 64 rows (prefill); else one block of `rows`.
-hipError_t launch_skinny_gemm(const SkinnyArgs& a, int epi, int fmt, int x_blocks, hipStream_t st);
+// x_blocks > 1: activation rows come in blocks of 64 (prefill); else one block of `rows`.
+// splits: 0 = chosen from the shape.
+SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int splits);
+size_t skinny_lds_bytes(int nb, int kc);
+// workspace bytes a plan needs for its partial tiles
+inline size_t skinny_part_bytes(const SkinnyPlan& p) {
+  return p.splits > 1 ? (size_t)p.row_blocks * p.splits * 4 * p.rt * p.nb * 4 * 64 * 4 : 0;
+}
+hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st);
 
-// embed + RMSNorm: h[r] = E[tok[r]] (fp32), xn[r] = bf16(rmsnorm(h[r]) * g)
-hipError_t launch_embed_norm(const int32_t* tokens, int rows, const uint16_t* embed, int vocab, int d,
-                             const uint16_t* gain, float eps, float* h, uint16_t* xn, hipStream_t st);
-// xn[r] = bf16(rmsnorm(h[src(r)]) * g); src = row_idx[r] if row_idx else r
-hipError_t launch_rmsnorm(const float* h, const int32_t* row_idx, int rows, int d, const uint16_t* gain, float eps,
-                          uint16_t* xn, hipStream_t st);
+// split fp32 rows into hi/lo bf16 planes: hi = bf16(x), lo = bf16(x - hi)
+hipError_t launch_split_planes(const float* x, int rows, int K, uint16_t* out, int64_t plane, hipStream_t st);
+
+// embedding gather: h[r] = E[tok[r]] (fp32); planes of gain * h; per-16-feature sums of squares
+// ss[t][r] (row stride ss_ld)
+hipError_t launch_embed(const int32_t* tokens, int rows, const uint16_t* embed, int vocab, int d,
+                        const uint16_t* gain, float* h, uint16_t* xplanes, int64_t plane, float* ss, int ss_ld,
+                        hipStream_t st);
 // RoPE q in place (fp32) and write rotated k, v (bf16) to each row's slab at its position
 hipError_t launch_rope_append(float* qkv, int ld_qkv, const RowMeta* meta, int rows, int n_heads, int n_kv_heads,
                               int head_dim, int layer, uint8_t* arena, const float* rope_cs, hipStream_t st);
-// attention of each item's query row over its key range; direct bf16 output or partials
+// attention of each item's query row over its key range; direct output (hi/lo planes) or partials
 hipError_t launch_attention(const float* qkv, int ld_qkv, const RowMeta* meta, const AttnItem* items, int n_items,
                             int n_heads, int n_kv_heads, int head_dim, int layer, const uint8_t* arena,
-                            uint16_t* out, int ld_out, float* part_o, float* part_ml, int max_parts,
+                            uint16_t* out, int64_t out_plane, int ld_out, float* part_o, float* part_ml,
                             hipStream_t st);
-// merge split partials of each (row, head) -> bf16 out
+// merge split partials of each (row, head) -> hi/lo planes
 hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const int32_t* row_parts, int rows,
-                               int n_heads, int head_dim, int max_parts, uint16_t* out, int ld_out, hipStream_t st);
+                               int n_heads, int head_dim, uint16_t* out, int64_t out_plane, int ld_out,
+                               hipStream_t st);
 // greedy argmax per row, lowest id on ties
 hipError_t launch_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st);
 // scatter canonical K/V [L, n, Hkv, Dh] into a slab at [pos, pos+n), or gather back

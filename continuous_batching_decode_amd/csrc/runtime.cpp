@@ -7,8 +7,8 @@
 //  - section "decode_step_batch - paint-by-numbers": t_s is the sequence's
 //    own length, captured once per step on the host and used for RoPE, the
 //    append slot and the attention range; after the step t_s += 1.
-// Failure containment (page "Batching", section 4): arguments are validated
-// before anything is enqueued, so a rejected call changes no slab.
+// Failure containment (page "Batching", section 4.5): arguments are
+// validated before anything is enqueued, so a rejected call changes no slab.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -107,11 +107,17 @@ struct cbd_ctx {
   bool host_only = true;
   int rows_pad = 0;  // activation rows available (multiple of 64)
   void* ws = nullptr;
-  float* h = nullptr;
-  uint16_t* xa = nullptr;
-  uint16_t* xo = nullptr;
-  uint16_t* xm = nullptr;
+  float* h = nullptr;       // residual stream fp32 [R, d]
+  uint16_t* xa = nullptr;   // planes of gain * h for the next norm's consumer [2][R, d]
+  uint16_t* xo = nullptr;   // planes of the attention output [2][R, q_dim]
+  uint16_t* xm = nullptr;   // planes of the SwiGLU product [2][R, max(F, d)]
+  float* ss = nullptr;      // per-16-feature sums of squares of h [d/16][R]
+  float* gemm_part = nullptr;   // split-K partial tiles
+  int32_t* gemm_counters = nullptr;  // split-K arrival counters, one per row block
+  size_t gemm_part_bytes = 0;
+  int gemm_counter_count = 0;
   float* qkv = nullptr;
+  int64_t xa_plane = 0, xo_plane = 0, xm_plane = 0;
   float* part_o = nullptr;
   float* part_ml = nullptr;
   float* rope_cs = nullptr;
@@ -120,6 +126,16 @@ struct cbd_ctx {
   uint8_t* staging = nullptr;   // pinned host, kStagingSlots slots
   hipEvent_t slot_ev[kStagingSlots] = {};
   int next_slot = 0;
+
+  // per-kernel event timing (cbd_profile_begin / cbd_profile_end)
+  uint32_t prof_mask = 0;
+  int prof_max = 0;
+  std::vector<hipEvent_t> prof_ev;  // 2 per recorded launch
+  struct ProfRec {
+    int kind;
+    double bytes, flops;
+  };
+  std::vector<ProfRec> prof_rec;
 };
 
 // ----------------------------------------------------------------------------- metadata staging
@@ -172,7 +188,7 @@ bool valid_model(const cbd_model_config* m, std::string* why) {
     snprintf(buf, sizeof buf, "d_model, ffn_dim and n_heads*head_dim must be multiples of %d", kmul);
     return bad(buf);
   }
-  if (m->vocab % 16 || (m->n_kv_heads * m->head_dim) % 16) return bad("vocab and kv width must be multiples of 16");
+  if (m->vocab % 64 || (m->n_kv_heads * m->head_dim) % 64) return bad("vocab and kv width must be multiples of 64");
   if (m->max_position < 1) return bad("max_position must be positive");
   if (!(m->rms_eps >= 0.f) || !(m->rope_theta > 0.f)) return bad("rms_eps >= 0 and rope_theta > 0 required");
   return true;
@@ -215,6 +231,22 @@ int plan_decode_items(const cbd_ctx* c, const std::vector<RowMeta>& rows, AttnIt
   }
   return n;
 }
+
+// Bracket one launch with events when its kind is being profiled.
+struct ProfScope {
+  cbd_ctx* c;
+  hipStream_t st;
+  bool on;
+  ProfScope(cbd_ctx* c_, int kind, double bytes, double flops, hipStream_t st_) : c(c_), st(st_), on(false) {
+    if (!(c->prof_mask & (1u << kind)) || (int)c->prof_rec.size() >= c->prof_max) return;
+    const size_t i = c->prof_rec.size();
+    c->prof_rec.push_back({kind, bytes, flops});
+    on = hipEventRecord(c->prof_ev[2 * i], st) == hipSuccess;
+  }
+  ~ProfScope() {
+    if (on) (void)hipEventRecord(c->prof_ev[2 * (c->prof_rec.size() - 1) + 1], st);
+  }
+};
 
 }  // namespace
 
@@ -270,10 +302,28 @@ static cbd_status setup_device(cbd_ctx* c) {
   const MetaLayout ml = meta_layout(c);
   c->slot_bytes = ml.total;
   size_t bytes = 0;
+  const size_t wm = std::max(m.ffn_dim, m.d_model);
+  // split-K workspace: the largest any decode-size launch plans (cbd_linear included)
+  {
+    const int shapes[][3] = {{EPI_STORE, c->qkv_dim, m.d_model},  {EPI_RESIDUAL, m.d_model, c->q_dim},
+                             {EPI_SWIGLU, m.ffn_dim, m.d_model},  {EPI_RESIDUAL, m.d_model, m.ffn_dim},
+                             {EPI_STORE, m.vocab, m.d_model}};
+    for (int rows = 1; rows <= 64; rows += 16)
+      for (const auto& sh : shapes) {
+        const SkinnyPlan pl = plan_skinny(sh[0], c->fmt, sh[1], sh[2], rows, 1, 0);
+        c->gemm_part_bytes = std::max(c->gemm_part_bytes, skinny_part_bytes(pl));
+        c->gemm_counter_count = std::max(c->gemm_counter_count, pl.row_blocks);
+      }
+    c->gemm_part_bytes = std::max<size_t>(c->gemm_part_bytes, 64u << 20);  // room for cbd_linear plans
+    c->gemm_counter_count = std::max(c->gemm_counter_count, 1 << 16);
+  }
+  bytes += c->gemm_part_bytes + 256;
+  bytes += (size_t)c->gemm_counter_count * 4 + 256;
   bytes += R * m.d_model * 4 + 256;                 // h
-  bytes += R * m.d_model * 2 + 256;                 // xa
-  bytes += R * c->q_dim * 2 + 256;                  // xo
-  bytes += R * std::max(m.ffn_dim, m.d_model) * 2 + 256;  // xm (also the standalone-linear input)
+  bytes += 2 * R * m.d_model * 2 + 256;             // xa planes
+  bytes += 2 * R * c->q_dim * 2 + 256;              // xo planes
+  bytes += 2 * R * wm * 2 + 256;                    // xm planes (also the standalone-linear input)
+  bytes += (size_t)(m.d_model / 16) * R * 4 + 256;  // ss
   bytes += R * c->qkv_dim * 4 + 256;                // qkv
   bytes += (size_t)kMaxParts * G * m.head_dim * 4 + 256;  // partial outputs
   bytes += (size_t)kMaxParts * G * 2 * 4 + 256;     // partial (max, sum)
@@ -283,10 +333,16 @@ static cbd_status setup_device(cbd_ctx* c) {
   HIP_TRY(hipMemset(c->ws, 0, bytes), "workspace clear");
   uint8_t* p = static_cast<uint8_t*>(c->ws);
   c->h = align_ptr<float>(p, R * m.d_model);
-  c->xa = align_ptr<uint16_t>(p, R * m.d_model);
-  c->xo = align_ptr<uint16_t>(p, R * c->q_dim);
-  c->xm = align_ptr<uint16_t>(p, R * std::max(m.ffn_dim, m.d_model));
+  c->xa = align_ptr<uint16_t>(p, 2 * R * m.d_model);
+  c->xo = align_ptr<uint16_t>(p, 2 * R * c->q_dim);
+  c->xm = align_ptr<uint16_t>(p, 2 * R * wm);
+  c->ss = align_ptr<float>(p, (size_t)(m.d_model / 16) * R);
+  c->gemm_part = align_ptr<float>(p, c->gemm_part_bytes / 4);
+  c->gemm_counters = align_ptr<int32_t>(p, c->gemm_counter_count);
   c->qkv = align_ptr<float>(p, R * c->qkv_dim);
+  c->xa_plane = (int64_t)R * m.d_model;
+  c->xo_plane = (int64_t)R * c->q_dim;
+  c->xm_plane = (int64_t)R * wm;
   c->part_o = align_ptr<float>(p, (size_t)kMaxParts * G * m.head_dim);
   c->part_ml = align_ptr<float>(p, (size_t)kMaxParts * G * 2);
   c->rope_cs = align_ptr<float>(p, (size_t)m.max_position * half * 2);
@@ -313,6 +369,7 @@ static void release(cbd_ctx* c) {
   if (!c) return;
   if (!c->host_only) {
     (void)hipDeviceSynchronize();
+    for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
     for (int i = 0; i < kStagingSlots; ++i)
       if (c->slot_ev[i]) (void)hipEventDestroy(c->slot_ev[i]);
     if (c->staging) (void)hipHostFree(c->staging);
@@ -501,10 +558,11 @@ extern "C" cbd_status kvslab_read(const cbd_ctx* c, int32_t seq_id, int32_t star
 
 namespace {
 
-SkinnyArgs gemm_args(const cbd_ctx* c, const uint16_t* x, int K, int rows, std::initializer_list<Mat> segs,
-                     std::initializer_list<int> seg_rows, int N) {
+SkinnyArgs gemm_args(const cbd_ctx* c, const uint16_t* x, int64_t x_plane, int K, int rows,
+                     std::initializer_list<Mat> segs, std::initializer_list<int> seg_rows, int N) {
   SkinnyArgs a{};
   a.x = x;
+  a.x_plane = x_plane;
   a.ldx = K;
   a.K = K;
   a.rows = rows;
@@ -523,56 +581,133 @@ SkinnyArgs gemm_args(const cbd_ctx* c, const uint16_t* x, int K, int rows, std::
   return a;
 }
 
+// Plan and launch one weight-streaming product; the plan's workspace is checked against the context's.
+hipError_t run_gemm(cbd_ctx* c, SkinnyArgs a, int epi, int x_blocks, int splits, hipStream_t st) {
+  const SkinnyPlan p = plan_skinny(epi, c->fmt, a.N, a.K, a.rows, x_blocks, splits);
+  if (skinny_part_bytes(p) > c->gemm_part_bytes || (p.splits > 1 && p.row_blocks > c->gemm_counter_count))
+    return hipErrorInvalidValue;
+  a.part = c->gemm_part;
+  a.counters = c->gemm_counters;
+  return launch_skinny_gemm(a, epi, c->fmt, x_blocks, p, st);
+}
+
+// The consumer of a norm: accumulators scaled by 1/rms of each activation row.
+void with_norm(const cbd_ctx* c, SkinnyArgs& a) {
+  a.ss = c->ss;
+  a.ss_tiles = c->cfg.d_model / 16;
+  a.ss_ld = c->rows_pad;
+  a.norm_dim = (float)c->cfg.d_model;
+  a.eps = c->cfg.rms_eps;
+}
+
+// A residual producer: h += y, then planes of next_gain * h and sums of squares for the next norm.
+void with_residual(cbd_ctx* c, SkinnyArgs& a, const uint16_t* next_gain) {
+  a.out = c->h;
+  a.ldo = c->cfg.d_model;
+  a.out_x = c->xa;
+  a.out_plane = c->xa_plane;
+  a.next_gain = next_gain;
+  a.ss_out = c->ss;
+  a.ss_out_ld = c->rows_pad;
+}
+
+// Algorithmic bytes of one weight-streaming launch: weights + activations read + outputs written.
+double gemm_bytes(const cbd_ctx* c, int rows, int n_total, int K, int epi) {
+  const double w = c->fmt == FMT_INT4 ? (double)n_total * K / 2 + (double)n_total * (K / 64) * 4
+                                      : (double)n_total * K * 2;
+  const int n_out = epi == EPI_SWIGLU ? n_total / 2 : n_total;
+  const double out = epi == EPI_SWIGLU ? (double)rows * n_out * 2
+                                       : (double)rows * n_out * 4 * (epi == EPI_RESIDUAL ? 2 : 1);
+  return w + (double)rows * K * 2 + out;
+}
+
+double gemm_flops(int rows, int n_total, int K) { return 2.0 * rows * n_total * K; }
+
 // Every layer for `rows` query rows whose metadata/items are already on the device.
+// kv_keys: total keys attended per KV head over all items (for byte accounting).
 cbd_status run_layers(cbd_ctx* c, int rows, int x_blocks, const RowMeta* meta_d, const AttnItem* items_d, int n_items,
-                      const int32_t* row_parts_d, bool any_split, hipStream_t st) {
+                      const int32_t* row_parts_d, int n_parts, double kv_keys, hipStream_t st) {
   const cbd_model_config& m = c->cfg;
   for (int l = 0; l < m.n_layers; ++l) {
     const LayerW& L = c->layers[l];
-    SkinnyArgs a = gemm_args(c, c->xa, m.d_model, rows, {L.wq, L.wk, L.wv}, {c->q_dim, c->kv_dim, c->kv_dim},
-                             c->qkv_dim);
+    SkinnyArgs a = gemm_args(c, c->xa, c->xa_plane, m.d_model, rows, {L.wq, L.wk, L.wv},
+                             {c->q_dim, c->kv_dim, c->kv_dim}, c->qkv_dim);
+    with_norm(c, a);
     a.out = c->qkv;
     a.ldo = c->qkv_dim;
-    HIP_TRY(launch_skinny_gemm(a, EPI_STORE, c->fmt, x_blocks, st), "qkv projection");
-    HIP_TRY(launch_rope_append(c->qkv, c->qkv_dim, meta_d, rows, m.n_heads, m.n_kv_heads, m.head_dim, l, c->arena,
-                               c->rope_cs, st),
-            "rope/append");
-    HIP_TRY(launch_attention(c->qkv, c->qkv_dim, meta_d, items_d, n_items, m.n_heads, m.n_kv_heads, m.head_dim, l,
-                             c->arena, c->xo, c->q_dim, c->part_o, c->part_ml, kMaxParts, st),
-            "attention");
-    if (any_split)
-      HIP_TRY(launch_attn_combine(c->part_o, c->part_ml, row_parts_d, rows, m.n_heads, m.head_dim, kMaxParts, c->xo,
+    {
+      ProfScope p(c, CBD_KERNEL_QKV, gemm_bytes(c, rows, c->qkv_dim, m.d_model, EPI_STORE),
+                  gemm_flops(rows, c->qkv_dim, m.d_model), st);
+      HIP_TRY(run_gemm(c, a, EPI_STORE, x_blocks, 0, st), "qkv projection");
+    }
+    {
+      ProfScope p(c, CBD_KERNEL_ROPE_APPEND, (double)rows * (c->qkv_dim * 4.0 + c->q_dim * 4.0 + c->kv_dim * 4.0), 0, st);
+      HIP_TRY(launch_rope_append(c->qkv, c->qkv_dim, meta_d, rows, m.n_heads, m.n_kv_heads, m.head_dim, l, c->arena,
+                                 c->rope_cs, st),
+              "rope/append");
+    }
+    {
+      const double kvb = kv_keys * c->kv_dim * 2.0 * 2.0;
+      ProfScope p(c, CBD_KERNEL_ATTENTION, kvb + (double)rows * c->q_dim * (4.0 + 4.0),
+                  kv_keys * m.n_heads * m.head_dim * 4.0, st);
+      HIP_TRY(launch_attention(c->qkv, c->qkv_dim, meta_d, items_d, n_items, m.n_heads, m.n_kv_heads, m.head_dim, l,
+                               c->arena, c->xo, c->xo_plane, c->q_dim, c->part_o, c->part_ml, st),
+              "attention");
+    }
+    if (n_parts > 0) {
+      ProfScope p(c, CBD_KERNEL_ATTN_COMBINE, (double)n_parts * m.n_heads * (m.head_dim + 2) * 4.0 +
+                  (double)rows * c->q_dim * 4.0, 0, st);
+      HIP_TRY(launch_attn_combine(c->part_o, c->part_ml, row_parts_d, rows, m.n_heads, m.head_dim, c->xo, c->xo_plane,
                                   c->q_dim, st),
               "attention combine");
-    a = gemm_args(c, c->xo, c->q_dim, rows, {L.wo}, {m.d_model}, m.d_model);
-    a.out = c->h;
-    a.ldo = m.d_model;
-    HIP_TRY(launch_skinny_gemm(a, EPI_RESIDUAL, c->fmt, x_blocks, st), "o projection");
-    HIP_TRY(launch_rmsnorm(c->h, nullptr, rows, m.d_model, L.ffn_norm, m.rms_eps, c->xa, st), "ffn norm");
-    a = gemm_args(c, c->xa, m.d_model, rows, {L.wg, L.wu}, {m.ffn_dim, m.ffn_dim}, m.ffn_dim);
-    a.out_bf16 = c->xm;
+    }
+    a = gemm_args(c, c->xo, c->xo_plane, c->q_dim, rows, {L.wo}, {m.d_model}, m.d_model);
+    with_residual(c, a, L.ffn_norm);
+    {
+      ProfScope p(c, CBD_KERNEL_O_PROJ, gemm_bytes(c, rows, m.d_model, c->q_dim, EPI_RESIDUAL),
+                  gemm_flops(rows, m.d_model, c->q_dim), st);
+      HIP_TRY(run_gemm(c, a, EPI_RESIDUAL, x_blocks, 0, st), "o projection");
+    }
+    a = gemm_args(c, c->xa, c->xa_plane, m.d_model, rows, {L.wg, L.wu}, {m.ffn_dim, m.ffn_dim}, m.ffn_dim);
+    with_norm(c, a);
+    a.out_x = c->xm;
+    a.out_plane = c->xm_plane;
     a.ldo = m.ffn_dim;
-    HIP_TRY(launch_skinny_gemm(a, EPI_SWIGLU, c->fmt, x_blocks, st), "gate/up projection");
-    a = gemm_args(c, c->xm, m.ffn_dim, rows, {L.wd}, {m.d_model}, m.d_model);
-    a.out = c->h;
-    a.ldo = m.d_model;
-    HIP_TRY(launch_skinny_gemm(a, EPI_RESIDUAL, c->fmt, x_blocks, st), "down projection");
-    const uint16_t* next_gain = (l + 1 < m.n_layers) ? c->layers[l + 1].attn_norm : nullptr;
-    if (next_gain)
-      HIP_TRY(launch_rmsnorm(c->h, nullptr, rows, m.d_model, next_gain, m.rms_eps, c->xa, st), "attn norm");
+    {
+      ProfScope p(c, CBD_KERNEL_GATE_UP, gemm_bytes(c, rows, 2 * m.ffn_dim, m.d_model, EPI_SWIGLU),
+                  gemm_flops(rows, 2 * m.ffn_dim, m.d_model), st);
+      HIP_TRY(run_gemm(c, a, EPI_SWIGLU, x_blocks, 0, st), "gate/up projection");
+    }
+    a = gemm_args(c, c->xm, c->xm_plane, m.ffn_dim, rows, {L.wd}, {m.d_model}, m.d_model);
+    with_residual(c, a, (l + 1 < m.n_layers) ? c->layers[l + 1].attn_norm : c->final_norm);
+    {
+      ProfScope p(c, CBD_KERNEL_DOWN, gemm_bytes(c, rows, m.d_model, m.ffn_dim, EPI_RESIDUAL),
+                  gemm_flops(rows, m.d_model, m.ffn_dim), st);
+      HIP_TRY(run_gemm(c, a, EPI_RESIDUAL, x_blocks, 0, st), "down projection");
+    }
   }
   return CBD_OK;
 }
 
+// Final norm (folded into the product) + lm_head for `rows` rows; row_idx_d gathers the
+// activation rows (prefill: each segment's last token).
 cbd_status run_head(cbd_ctx* c, const int32_t* row_idx_d, int rows, float* logits, int32_t* next_tokens,
                     hipStream_t st) {
   const cbd_model_config& m = c->cfg;
-  HIP_TRY(launch_rmsnorm(c->h, row_idx_d, rows, m.d_model, c->final_norm, m.rms_eps, c->xa, st), "final norm");
-  SkinnyArgs a = gemm_args(c, c->xa, m.d_model, rows, {c->lm_head}, {m.vocab}, m.vocab);
+  SkinnyArgs a = gemm_args(c, c->xa, c->xa_plane, m.d_model, rows, {c->lm_head}, {m.vocab}, m.vocab);
+  with_norm(c, a);
+  a.x_rows = row_idx_d;
   a.out = logits;
   a.ldo = m.vocab;
-  HIP_TRY(launch_skinny_gemm(a, EPI_STORE, c->fmt, 1, st), "lm_head");
-  if (next_tokens) HIP_TRY(launch_argmax(logits, rows, m.vocab, next_tokens, st), "argmax");
+  {
+    ProfScope p(c, CBD_KERNEL_LM_HEAD, gemm_bytes(c, rows, m.vocab, m.d_model, EPI_STORE),
+                gemm_flops(rows, m.vocab, m.d_model), st);
+    HIP_TRY(run_gemm(c, a, EPI_STORE, 1, 0, st), "lm_head");
+  }
+  if (next_tokens) {
+    ProfScope p(c, CBD_KERNEL_ARGMAX, rows * (double)m.vocab * 4.0, 0, st);
+    HIP_TRY(launch_argmax(logits, rows, m.vocab, next_tokens, st), "argmax");
+  }
   return CBD_OK;
 }
 
@@ -611,18 +746,23 @@ extern "C" cbd_status decode_step_batch(cbd_ctx* c, const int32_t* seq_ids, int3
   const int n_items = plan_decode_items(c, rows, items, row_parts.data());
   const size_t parts_off = round_up(items_off + (size_t)n_items * sizeof(AttnItem), 256);
   std::memcpy(host + parts_off, row_parts.data(), row_parts.size() * sizeof(int32_t));
-  bool any_split = false;
-  for (int i = 0; i < B; ++i) any_split |= row_parts[2 * i + 1] > 0;
+  int n_parts = 0;
+  for (int i = 0; i < B; ++i) n_parts += row_parts[2 * i + 1];
+  double kv_keys = 0;
+  for (int i = 0; i < B; ++i) kv_keys += rows[i].pos + 1;
   if (cbd_status s = upload(c, slot, parts_off + row_parts.size() * sizeof(int32_t), st)) return s;
   const RowMeta* meta_d = reinterpret_cast<const RowMeta*>(c->meta_dev);
   const AttnItem* items_d = reinterpret_cast<const AttnItem*>(c->meta_dev + items_off);
   const int32_t* parts_d = reinterpret_cast<const int32_t*>(c->meta_dev + parts_off);
 
   const cbd_model_config& m = c->cfg;
-  HIP_TRY(launch_embed_norm(last_tokens_dev, B, c->embed, m.vocab, m.d_model, c->layers[0].attn_norm, m.rms_eps,
-                            c->h, c->xa, st),
-          "embed");
-  if (cbd_status s = run_layers(c, B, 1, meta_d, items_d, n_items, parts_d, any_split, st)) return s;
+  {
+    ProfScope p(c, CBD_KERNEL_EMBED, B * (double)m.d_model * 12.0, 0, st);
+    HIP_TRY(launch_embed(last_tokens_dev, B, c->embed, m.vocab, m.d_model, c->layers[0].attn_norm, c->h, c->xa,
+                         c->xa_plane, c->ss, c->rows_pad, st),
+            "embed");
+  }
+  if (cbd_status s = run_layers(c, B, 1, meta_d, items_d, n_items, parts_d, n_parts, kv_keys, st)) return s;
   if (cbd_status s = run_head(c, nullptr, B, logits_dev, next_tokens_dev, st)) return s;
   for (int i = 0; i < B; ++i) c->slabs[seq_ids[i]].len += 1;
   c->stats.decode_steps += 1;
@@ -680,10 +820,15 @@ extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, cons
 
   const cbd_model_config& m = c->cfg;
   const int x_blocks = (int)((T + 63) / 64);
-  HIP_TRY(launch_embed_norm(tokens_dev, (int)T, c->embed, m.vocab, m.d_model, c->layers[0].attn_norm, m.rms_eps,
-                            c->h, c->xa, st),
-          "embed");
-  if (cbd_status s = run_layers(c, (int)T, x_blocks, meta_d, items_d, (int)T, nullptr, false, st)) return s;
+  double kv_keys = 0;
+  for (int i = 0; i < K; ++i) kv_keys += 0.5 * (double)seg_lens[i] * (seg_lens[i] + 1);
+  {
+    ProfScope p(c, CBD_KERNEL_EMBED, T * (double)m.d_model * 12.0, 0, st);
+    HIP_TRY(launch_embed(tokens_dev, (int)T, c->embed, m.vocab, m.d_model, c->layers[0].attn_norm, c->h, c->xa,
+                         c->xa_plane, c->ss, c->rows_pad, st),
+            "embed");
+  }
+  if (cbd_status s = run_layers(c, (int)T, x_blocks, meta_d, items_d, (int)T, nullptr, 0, kv_keys, st)) return s;
   if (cbd_status s = run_head(c, idx_d, K, last_logits_dev, next_tokens_dev, st)) return s;
   for (int i = 0; i < K; ++i) c->slabs[seq_ids[i]].len = seg_lens[i];
   c->stats.prefill_calls += 1;
@@ -702,25 +847,27 @@ extern "C" cbd_status greedy_argmax(cbd_ctx* c, const float* logits_dev, int32_t
   return CBD_OK;
 }
 
-extern "C" cbd_status cbd_linear(cbd_ctx* c, const cbd_matrix* w, int32_t N, int32_t K, const void* x_dev,
-                                 int32_t rows, float* y_dev, cbd_stream stream) {
+extern "C" cbd_status cbd_linear(cbd_ctx* c, const cbd_matrix* w, int32_t N, int32_t K, const float* x_dev,
+                                 int32_t rows, float* y_dev, int32_t splits, cbd_stream stream) {
   if (!c || !w || !x_dev || !y_dev) return fail(CBD_E_INVAL, "cbd_linear: null argument");
   if (rows < 1 || rows > 64) return fail(CBD_E_INVAL, "cbd_linear: rows must be in 1..64");
-  if (N < 16 || N % 16) return fail(CBD_E_INVAL, "cbd_linear: N must be a positive multiple of 16");
+  if (N < 64 || N % 64) return fail(CBD_E_INVAL, "cbd_linear: N must be a positive multiple of 64");
   if (K < 1 || !skinny_shape_ok(c->fmt, K))
     return fail(CBD_E_INVAL, "cbd_linear: K=%d not supported for this weight format", K);
   if (K > std::max(c->cfg.ffn_dim, c->cfg.d_model)) return fail(CBD_E_INVAL, "cbd_linear: K above the model width");
+  if (splits < 0 || splits > 64 || (splits > 0 && (K % splits || (K / splits) % 128)))
+    return fail(CBD_E_INVAL, "cbd_linear: splits must divide K into multiples of 128 inputs");
   if (!w->data || !aligned16(w->data) || (c->fmt == FMT_INT4 && (!w->aux || !aligned16(w->aux))) ||
       !aligned16(y_dev) || !aligned16(x_dev))
     return fail(CBD_E_INVAL, "cbd_linear: pointers must be 16-byte aligned");
   if (c->host_only) return fail(CBD_E_NODEVICE, "cbd_linear: host-only context");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // copy the rows into the padded workspace so the column tile never reads past the caller's buffer
-  HIP_TRY(hipMemcpyAsync(c->xm, x_dev, (size_t)rows * K * 2, hipMemcpyDeviceToDevice, st), "cbd_linear input copy");
-  SkinnyArgs a = gemm_args(c, c->xm, K, rows, {Mat{w->data, w->aux}}, {N}, N);
+  // split the rows into hi/lo planes in the padded workspace (the column tile never reads past it)
+  HIP_TRY(launch_split_planes(static_cast<const float*>(x_dev), rows, K, c->xm, c->xm_plane, st), "cbd_linear split");
+  SkinnyArgs a = gemm_args(c, c->xm, c->xm_plane, K, rows, {Mat{w->data, w->aux}}, {N}, N);
   a.out = y_dev;
   a.ldo = N;
-  HIP_TRY(launch_skinny_gemm(a, EPI_STORE, c->fmt, 1, st), "cbd_linear");
+  HIP_TRY(run_gemm(c, a, EPI_STORE, 1, splits, st), "cbd_linear");
   return CBD_OK;
 }
 
@@ -749,5 +896,39 @@ extern "C" cbd_status cbd_pack_int4(const uint8_t* codes, const uint16_t* scale,
       aux_out[(gi * N + n) * 2 + 1] = bias[n * G + gi];
     }
   }
+  return CBD_OK;
+}
+
+extern "C" cbd_status cbd_profile_begin(cbd_ctx* c, uint32_t kind_mask, int32_t max_launches) {
+  if (!c) return fail(CBD_E_INVAL, "cbd_profile_begin: null context");
+  if (max_launches < 0 || max_launches > (1 << 22)) return fail(CBD_E_INVAL, "cbd_profile_begin: bad max_launches");
+  if (c->host_only) return fail(CBD_E_NODEVICE, "cbd_profile_begin: host-only context");
+  while ((int)c->prof_ev.size() < 2 * max_launches) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreate(&e), "profile event create");
+    c->prof_ev.push_back(e);
+  }
+  c->prof_rec.clear();
+  c->prof_max = max_launches;
+  c->prof_mask = kind_mask;
+  return CBD_OK;
+}
+
+extern "C" cbd_status cbd_profile_end(cbd_ctx* c, cbd_kernel_time* out) {
+  if (!c || !out) return fail(CBD_E_INVAL, "cbd_profile_end: null argument");
+  for (int k = 0; k < CBD_KERNEL_KINDS; ++k) out[k] = cbd_kernel_time{0, 0.0, 0.0, 0.0};
+  c->prof_mask = 0;
+  if (c->prof_rec.empty()) return CBD_OK;
+  HIP_TRY(hipEventSynchronize(c->prof_ev[2 * c->prof_rec.size() - 1]), "profile wait");
+  for (size_t i = 0; i < c->prof_rec.size(); ++i) {
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, c->prof_ev[2 * i], c->prof_ev[2 * i + 1]), "profile elapsed");
+    cbd_kernel_time& t = out[c->prof_rec[i].kind];
+    t.launches += 1;
+    t.total_ms += ms;
+    t.bytes += c->prof_rec[i].bytes;
+    t.flops += c->prof_rec[i].flops;
+  }
+  c->prof_rec.clear();
   return CBD_OK;
 }

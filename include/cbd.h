@@ -79,7 +79,7 @@ typedef struct {
   int32_t n_kv_heads;   /* n_heads must be a multiple of n_kv_heads (GQA) */
   int32_t head_dim;     /* 64 or 128 */
   int32_t ffn_dim;
-  int32_t vocab;
+  int32_t vocab;        /* multiple of 64 */
   float rms_eps;
   float rope_theta;
   int32_t weight_format; /* CBD_WEIGHTS_BF16 or CBD_WEIGHTS_INT4 */
@@ -240,13 +240,16 @@ cbd_status greedy_argmax(cbd_ctx* ctx, const float* logits_dev, int32_t rows, in
  * The batched weight-streaming product alone (the page's batched matvec
  * that shares one weight read across all lanes):
  * y_dev[b, n] = sum_k W[n, k] * x_dev[b, k] for b < rows.
- *  x_dev  bf16 [rows, K] row-major;  y_dev fp32 [rows, N].
- * rows 1..64; N a multiple of 64; K a multiple of 128. Uses the context's
- * weight format. Exposed for kernel-level parity tests and bandwidth
- * measurements.
+ *  x_dev  fp32 [rows, K] row-major (carried internally as two bf16 planes,
+ *         hi = bf16(x) and lo = bf16(x - hi));  y_dev fp32 [rows, N].
+ * rows 1..64; N a multiple of 64; K a multiple of 256 (bf16 weights) or 512
+ * (int4) and at most max(d_model, ffn_dim). Uses the context's weight
+ * format. splits: number of workgroups the input dimension is divided over
+ * (0 = the library's choice; else it must divide K into multiples of 128).
+ * Exposed for kernel-level parity tests and bandwidth measurements.
  */
-cbd_status cbd_linear(cbd_ctx* ctx, const cbd_matrix* w, int32_t N, int32_t K, const void* x_dev,
-                      int32_t rows, float* y_dev, cbd_stream stream);
+cbd_status cbd_linear(cbd_ctx* ctx, const cbd_matrix* w, int32_t N, int32_t K, const float* x_dev, int32_t rows,
+                      float* y_dev, int32_t splits, cbd_stream stream);
 
 /*
  * Pack a 4-bit affine matrix into the int4 layout (host memory, any thread).
@@ -261,6 +264,43 @@ cbd_status cbd_linear(cbd_ctx* ctx, const cbd_matrix* w, int32_t N, int32_t K, c
  */
 cbd_status cbd_pack_int4(const uint8_t* codes, const uint16_t* scale, const uint16_t* bias, int64_t N,
                          int64_t K, uint32_t* packed_out, uint16_t* aux_out);
+
+/*
+ * Per-kernel timing with HIP events (a tracing aid, the counterpart of the
+ * per-step trace of page "Batching", section 4.4, "Housekeeping"). Between cbd_profile_begin and
+ * cbd_profile_end every launch of a selected kind is bracketed by two
+ * events recorded on the launch's own stream. cbd_profile_end waits for the
+ * last event and returns, per kind, the launch count, the summed
+ * event-to-event milliseconds, and the summed algorithmic bytes and flops
+ * of those launches (counted from shapes: weights + activations read +
+ * outputs written; K/V bytes read for attention). kind_mask is a bit mask
+ * of (1 << cbd_kernel_kind). max_launches bounds the launches recorded;
+ * later ones are not timed. Event handles are created in cbd_profile_begin.
+ */
+typedef enum {
+  CBD_KERNEL_EMBED = 0,
+  CBD_KERNEL_NORM = 1,
+  CBD_KERNEL_QKV = 2,
+  CBD_KERNEL_ROPE_APPEND = 3,
+  CBD_KERNEL_ATTENTION = 4,
+  CBD_KERNEL_ATTN_COMBINE = 5,
+  CBD_KERNEL_O_PROJ = 6,
+  CBD_KERNEL_GATE_UP = 7,
+  CBD_KERNEL_DOWN = 8,
+  CBD_KERNEL_LM_HEAD = 9,
+  CBD_KERNEL_ARGMAX = 10,
+  CBD_KERNEL_KINDS = 11
+} cbd_kernel_kind;
+
+typedef struct {
+  int64_t launches;
+  double total_ms;
+  double bytes;
+  double flops;
+} cbd_kernel_time;
+
+cbd_status cbd_profile_begin(cbd_ctx* ctx, uint32_t kind_mask, int32_t max_launches);
+cbd_status cbd_profile_end(cbd_ctx* ctx, cbd_kernel_time* out /* [CBD_KERNEL_KINDS] */);
 
 #ifdef __cplusplus
 }

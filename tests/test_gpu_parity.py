@@ -56,21 +56,49 @@ def linear_engines(torch, cbd):
         e.close()
 
 
+# Activations enter as fp32 and are carried as bf16 hi + lo planes (about 16
+# significant bits); weights are exact bf16 and products accumulate in fp32,
+# so the result is within a few 1e-6 of the float64 product of the same values.
+LINEAR_RTOL = 2e-5
+
+
 @pytest.mark.parametrize("N,K", [(6144, 4096), (4096, 14336), (1024, 256), (512, 1024)])
 @pytest.mark.parametrize("rows", [1, 7, 16, 33, 64])
 def test_linear_bf16(torch, cbd, linear_engines, N, K, rows):
     _say("linear bf16 N=%d K=%d rows=%d" % (N, K, rows))
     eng = linear_engines["bf16"]
     W = synth.normal_bf16(7, N + K, (N, K), 0.02)
-    X = synth.normal_bf16(8, rows, (rows, K), 1.0)
-    wd, xd = to_dev_bits(torch, W), to_dev_bits(torch, X)
+    X = synth.normal_f32(8, rows, (rows, K), 1.0)
+    wd, xd = to_dev_bits(torch, W), torch.from_numpy(X).cuda()
     y = torch.empty((rows, N), dtype=torch.float32, device="cuda")
     eng.linear(cbd.Matrix(wd.data_ptr(), None), N, K, xd, y)
     torch.cuda.synchronize()
-    ref = synth.bf16_bits_to_f32(X).astype(np.float64) @ synth.bf16_bits_to_f32(W).astype(np.float64).T
+    ref = X.astype(np.float64) @ synth.bf16_bits_to_f32(W).astype(np.float64).T
     got = y.cpu().numpy()
     err = np.max(np.abs(got - ref))
-    assert err <= 2e-5 * np.max(np.abs(ref)) + 1e-6, err
+    assert err <= LINEAR_RTOL * np.max(np.abs(ref)), err
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 16])
+@pytest.mark.parametrize("N,K,rows", [(4096, 14336, 8), (4096, 14336, 1), (1024, 14336, 33)])
+def test_linear_bf16_splits(torch, cbd, linear_engines, N, K, rows, splits):
+    """Every split of K over workgroups gives the product (fixed-order reduction of partial tiles)."""
+    _say("linear bf16 splits=%d N=%d K=%d rows=%d" % (splits, N, K, rows))
+    eng = linear_engines["bf16"]
+    W = synth.normal_bf16(17, N + K, (N, K), 0.02)
+    X = synth.normal_f32(18, rows, (rows, K), 1.0)
+    wd, xd = to_dev_bits(torch, W), torch.from_numpy(X).cuda()
+    y = torch.empty((rows, N), dtype=torch.float32, device="cuda")
+    eng.linear(cbd.Matrix(wd.data_ptr(), None), N, K, xd, y, splits=splits)
+    torch.cuda.synchronize()
+    y2 = torch.empty_like(y)
+    eng.linear(cbd.Matrix(wd.data_ptr(), None), N, K, xd, y2, splits=splits)  # counters were reset
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    torch.cuda.synchronize()
+    ref = X.astype(np.float64) @ synth.bf16_bits_to_f32(W).astype(np.float64).T
+    err = np.max(np.abs(y.cpu().numpy() - ref))
+    assert err <= LINEAR_RTOL * np.max(np.abs(ref)), err
 
 
 @pytest.mark.parametrize("N,K", [(6144, 4096), (4096, 14336), (512, 512)])
@@ -82,16 +110,16 @@ def test_linear_int4(torch, cbd, linear_engines, N, K, rows):
     packed, aux = cbd.pack_int4(m["codes"], m["scale"], m["bias"])
     pd = torch.from_numpy(packed.view(np.int32)).cuda()
     ad = to_dev_bits(torch, aux)
-    X = synth.normal_bf16(10, rows, (rows, K), 1.0)
-    xd = to_dev_bits(torch, X)
+    X = synth.normal_f32(10, rows, (rows, K), 1.0)
+    xd = torch.from_numpy(X).cuda()
     y = torch.empty((rows, N), dtype=torch.float32, device="cuda")
     eng.linear(cbd.Matrix(pd.data_ptr(), ad.data_ptr()), N, K, xd, y)
     torch.cuda.synchronize()
     from oracle import dequant_int4
     Wd = dequant_int4(m["codes"], m["scale"], m["bias"], 64)
-    ref = synth.bf16_bits_to_f32(X).astype(np.float64) @ Wd.T
+    ref = X.astype(np.float64) @ Wd.T
     err = np.max(np.abs(y.cpu().numpy() - ref))
-    assert err <= 2e-5 * np.max(np.abs(ref)) + 1e-6, err
+    assert err <= LINEAR_RTOL * np.max(np.abs(ref)), err
 
 
 # ----------------------------------------------------------------------------- slabs and argmax
