@@ -25,7 +25,7 @@ WEIGHTS_BF16, WEIGHTS_INT4 = 0, 1
 EXPORTS = ["cbd_kv_bytes_per_token", "cbd_slab_granule_tokens", "cbd_create", "cbd_destroy", "cbd_last_error",
            "cbd_stats", "kvslab_alloc", "kvslab_free", "kvslab_len", "kvslab_capacity", "kvslab_append",
            "kvslab_read", "decode_step_batch", "prefill_segmented", "greedy_argmax", "cbd_linear", "cbd_pack_int4",
-           "cbd_profile_begin", "cbd_profile_end"]
+           "cbd_profile_begin", "cbd_profile_end", "cbd_pack_bf16"]
 
 KERNEL_KINDS = ["embed", "norm", "qkv", "rope_append", "attention", "attn_combine", "o_proj", "gate_up", "down",
                 "lm_head", "argmax"]
@@ -99,6 +99,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "cbd_linear": (i32, [ctx_p, P(Matrix), i32, i32, vp, i32, vp, i32, vp]),
         "cbd_pack_int4": (i32, [vp, vp, vp, i64, i64, vp, vp]),
         "cbd_profile_begin": (i32, [ctx_p, ctypes.c_uint32, i32]),
+        "cbd_pack_bf16": (i32, [vp, i64, i64, vp, vp]),
         "cbd_profile_end": (i32, [ctx_p, P(KernelTime)]),
     }
     for name, (res, args) in sig.items():
@@ -141,11 +142,20 @@ def pack_int4(codes: np.ndarray, scale: np.ndarray, bias: np.ndarray):
     scale = np.ascontiguousarray(scale, dtype=np.uint16)
     bias = np.ascontiguousarray(bias, dtype=np.uint16)
     n, k = codes.shape
-    packed = np.empty((n, k // 8), dtype=np.uint32)
+    packed = np.empty((n * k // 8,), dtype=np.uint32)
     aux = np.empty((k // 64, n, 2), dtype=np.uint16)
     _check(lib().cbd_pack_int4(codes.ctypes.data, scale.ctypes.data, bias.ctypes.data, n, k,
                                packed.ctypes.data, aux.ctypes.data))
     return packed, aux
+
+
+def pack_bf16_device(w_rowmajor_dev, stream=None):
+    """Device-side repack of a row-major bf16 matrix (int16 tensor [N, K]) into the streaming layout."""
+    import torch
+    out = torch.empty_like(w_rowmajor_dev)
+    n, k = w_rowmajor_dev.shape
+    _check(lib().cbd_pack_bf16(w_rowmajor_dev.data_ptr(), int(n), int(k), out.data_ptr(), _stream_ptr(stream)))
+    return out
 
 
 def _stream_ptr(stream) -> Optional[int]:
@@ -202,7 +212,13 @@ class Engine:
         if isinstance(m, dict):
             packed, aux = pack_int4(m["codes"], m["scale"], m["bias"])
             return Matrix(self._dev(packed), self._dev(aux))
-        return Matrix(self._dev(m), None)
+        import torch
+        rowmajor = torch.from_numpy(np.ascontiguousarray(m).view(np.int16)).to(self.device)
+        packed = pack_bf16_device(rowmajor)
+        torch.cuda.synchronize()
+        del rowmajor
+        self._keep.append(packed)
+        return Matrix(packed.data_ptr(), None)
 
     def _upload_weights(self, w: Dict) -> Weights:
         layers = (LayerWeights * self.shape.n_layers)()

@@ -8,9 +8,12 @@
 // row of the batch rides on that single read.
 //
 // Mapping (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
-//  - A operand = 16 consecutive weight rows x 32 inputs, loaded straight from
-//    HBM (one 16-byte load per lane: lane l reads row l%16, inputs
-//    8*(l/16)..+7), double-buffered in registers.
+//  - A operand = 16 consecutive weight rows x 32 inputs (lane l holds row
+//    l%16, inputs 8*(l/16)..+7). Weights live in the library's streaming
+//    layout: each such 1 KB fragment is stored contiguously in lane order and
+//    fragments run along K, so every wave load instruction reads 1 KB of
+//    consecutive memory (DRAM-friendly, unlike 16 rows x 64 bytes of a
+//    row-major matrix). Loads are double-buffered in registers.
 //  - B operand = 16 activation rows x the same 32 inputs, read from LDS: the
 //    workgroup stages each chunk of the activations once and its 4 waves
 //    share it, so the vector-memory path carries (almost) only weights.
@@ -92,6 +95,26 @@ CBD_DEVICE void store_split4(uint16_t* hi, uint16_t* lo, float v0, float v1, flo
 }  // namespace
 
 // LDS bytes of one launch: activation chunk (2 planes) + norm partial sums.
+// Pack a row-major bf16 matrix [N, K] into the streaming layout (N % 16 == 0, K % 32 == 0).
+__global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t* src, int64_t N, int64_t K, uint16_t* dst) {
+  const int64_t chunks = N * K / 8;
+  const int64_t kfr = K / 32;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
+    const int64_t f = c >> 6;
+    const int l = (int)(c & 63);
+    const int64_t tr = f / kfr, tk = f - tr * kfr;
+    const int64_t row = 16 * tr + (l & 15), col = 32 * tk + 8 * (l >> 4);
+    *reinterpret_cast<uint4*>(dst + 8 * c) = *reinterpret_cast<const uint4*>(src + row * K + col);
+  }
+}
+
+hipError_t launch_pack_bf16(const uint16_t* src, int64_t N, int64_t K, uint16_t* dst, hipStream_t st) {
+  const int64_t chunks = N * K / 8;
+  const int blocks = (int)std::min<int64_t>((chunks + 255) / 256, 65536);
+  hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, st, src, N, K, dst);
+  return hipGetLastError();
+}
+
 size_t skinny_lds_bytes(int nb, int kc) { return (size_t)2 * 16 * nb * (kc + 8) * 2 + (size_t)16 * 16 * nb * 4; }
 
 template <int RT, int NB, int EPI, int FMT, int UC>
@@ -119,21 +142,6 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
   const int col0 = xblk * ROWS;
   const int rows_valid = min(ROWS, a.rows - col0);
 
-  // -- 1/rms partial sums for this block's activation rows: 16 fixed groups of tiles
-  if (a.ss) {
-    const int per = a.ss_tiles / 16;
-    for (int i = threadIdx.x; i < 16 * ROWS; i += 256) {
-      const int c = i % ROWS, grp = i / ROWS;
-      float s = 0.f;
-      if (c < rows_valid) {
-        const int row = a.x_rows ? a.x_rows[col0 + c] : col0 + c;
-        const float* p = a.ss + (int64_t)grp * per * a.ss_ld + row;
-        for (int t = 0; t < per; ++t) s += p[(int64_t)t * a.ss_ld];
-      }
-      norm_part[grp * ROWS + c] = s;
-    }
-  }
-
   // weight-row subtiles of this wave
   int sub_row[RT];
 #pragma unroll
@@ -156,12 +164,12 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
   auto stage_x = [&](int kc0) {
     __syncthreads();  // the previous chunk has been consumed
     const int per_row = KC / 8;
-    for (int idx = threadIdx.x; idx < 2 * ROWS * per_row; idx += 256) {
-      const int plane = idx / (ROWS * per_row);
-      const int rem = idx - plane * ROWS * per_row;
+    // only the valid rows: padding rows of the LDS tile feed padding outputs only
+    for (int idx = threadIdx.x; idx < 2 * rows_valid * per_row; idx += 256) {
+      const int plane = idx / (rows_valid * per_row);
+      const int rem = idx - plane * rows_valid * per_row;
       const int r = rem / per_row, c8 = rem - r * per_row;
-      const int b = min(col0 + r, a.rows - 1);
-      const int row = a.x_rows ? a.x_rows[b] : col0 + r;
+      const int row = a.x_rows ? a.x_rows[col0 + r] : col0 + r;
       const uint16_t* src = a.x + (int64_t)plane * a.x_plane + (int64_t)row * a.ldx + kc0 + 8 * c8;
       *reinterpret_cast<uint4*>(xs + (plane * ROWS + r) * XROW + 8 * c8) = *reinterpret_cast<const uint4*>(src);
     }
@@ -172,19 +180,20 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
   const int total = Kr / ((FMT == FMT_BF16 ? 32 : 128) * UC);
 
   if constexpr (FMT == FMT_BF16) {
+    // fragment (tile row tr, k-fragment tk) at ((tr * K/32) + tk) * 512 elements; lane l at 8*l
     const uint16_t* wr[RT];
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
       const int s = seg_of(a, sub_row[i]);
-      const int local = sub_row[i] - seg_begin(a, s) + r16;
-      wr[i] = reinterpret_cast<const uint16_t*>(a.w[s]) + (int64_t)local * K + kbeg + 8 * g;
+      const int tr = (sub_row[i] - seg_begin(a, s)) >> 4;
+      wr[i] = reinterpret_cast<const uint16_t*>(a.w[s]) + ((int64_t)tr * (K >> 5) + (kbeg >> 5)) * 512 + 8 * lane;
     }
     u32x4_t A0[UC][RT], A1[UC][RT];
     auto loadw = [&](u32x4_t (&A)[UC][RT], int st) {
 #pragma unroll
       for (int u = 0; u < UC; ++u)
 #pragma unroll
-        for (int i = 0; i < RT; ++i) A[u][i] = load_stream(wr[i] + (st * UC + u) * 32);
+        for (int i = 0; i < RT; ++i) A[u][i] = load_stream(wr[i] + (int64_t)(st * UC + u) * 512);
     };
     auto compute = [&](const u32x4_t (&A)[UC][RT], int st) {
       const int koff = ((st % spc) * UC) * 32 + 8 * g;
@@ -202,9 +211,10 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
         }
     };
     loadw(A0, 0);
+    if (total > 1) loadw(A1, 1);
     for (int st = 0; st < total; st += 2) {
       if (st % spc == 0) stage_x(kbeg + (st / spc) * KC);
-      if (st + 1 < total) loadw(A1, st + 1);
+      if (st > 0 && st + 1 < total) loadw(A1, st + 1);
       compute(A0, st);
       if (st + 1 < total) {
         if ((st + 1) % spc == 0) stage_x(kbeg + ((st + 1) / spc) * KC);
@@ -213,7 +223,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
       }
     }
   } else {
-    // int4: 128 inputs per step; lane group g reads words 4g..4g+3 of each 128-input block
+    // int4: 128 inputs per step; lane l (row l%16, group g = l/16) reads its 4 words of the block
     const uint32_t* wr[RT];
     const uint16_t* ar[RT];
     int seg_rows[RT];
@@ -221,8 +231,8 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
     for (int i = 0; i < RT; ++i) {
       const int s = seg_of(a, sub_row[i]);
       const int sb = seg_begin(a, s);
-      const int local = sub_row[i] - sb + r16;
-      wr[i] = reinterpret_cast<const uint32_t*>(a.w[s]) + (int64_t)local * (K >> 3) + (kbeg >> 3) + 4 * g;
+      const int tr = (sub_row[i] - sb) >> 4;
+      wr[i] = reinterpret_cast<const uint32_t*>(a.w[s]) + ((int64_t)tr * (K >> 7) + (kbeg >> 7)) * 256 + 4 * lane;
       seg_rows[i] = a.seg_end[s] - sb;
       ar[i] = reinterpret_cast<const uint16_t*>(a.aux[s]) + (int64_t)(sub_row[i] - sb + 4 * g) * 2;
     }
@@ -236,7 +246,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
       for (int u = 0; u < UC; ++u)
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
-          Wq[u][i] = load_stream(wr[i] + (st * UC + u) * 16);
+          Wq[u][i] = load_stream(wr[i] + (int64_t)(st * UC + u) * 256);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int grp = ((kbeg + (st * UC + u) * 128) >> 6) + h;
@@ -294,6 +304,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
   }
 
   // -- split-K: partial tiles to the workspace; the last workgroup of the row block adds them.
+  (void)rows_valid;
   // Partial tiles and the arrival counter are written and read with agent-scope
   // atomic accesses, which the hardware performs at the level where all XCDs'
   // L2 caches agree; each wave waits for its stores to be acknowledged
@@ -334,7 +345,24 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
+  // 1/rms of each activation row from the producer's per-16-feature sums of squares, added in
+  // 16 fixed groups (the same order in every workgroup and launch)
   float inv[NB];
+  if (a.ss) {
+    __syncthreads();  // LDS reuse: all waves are past their last activation read
+    const int per = a.ss_tiles / 16;
+    for (int i = threadIdx.x; i < 16 * ROWS; i += 256) {
+      const int c = i % ROWS, grp = i / ROWS;
+      float s = 0.f;
+      if (c < rows_valid) {
+        const int row = a.x_rows ? a.x_rows[col0 + c] : col0 + c;
+        const float* p = a.ss + (int64_t)grp * per * a.ss_ld + row;
+        for (int t = 0; t < per; ++t) s += p[(int64_t)t * a.ss_ld];
+      }
+      norm_part[grp * ROWS + c] = s;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
     inv[c] = 1.f;

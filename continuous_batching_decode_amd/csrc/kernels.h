@@ -59,6 +59,8 @@ inline size_t skinny_part_bytes(const SkinnyPlan& p) {
   return p.splits > 1 ? (size_t)p.row_blocks * p.splits * 4 * p.rt * p.nb * 4 * 64 * 4 : 0;
 }
 hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st);
+// row-major bf16 [N, K] -> streaming layout (fragments of 16 rows x 32 inputs, lane order, along K)
+hipError_t launch_pack_bf16(const uint16_t* src, int64_t N, int64_t K, uint16_t* dst, hipStream_t st);
 
 // split fp32 rows into hi/lo bf16 planes: hi = bf16(x), lo = bf16(x - hi)
 hipError_t launch_split_planes(const float* x, int rows, int K, uint16_t* out, int64_t plane, hipStream_t st);
@@ -71,15 +73,27 @@ hipError_t launch_embed(const int32_t* tokens, int rows, const uint16_t* embed, 
 // RoPE q in place (fp32) and write rotated k, v (bf16) to each row's slab at its position
 hipError_t launch_rope_append(float* qkv, int ld_qkv, const RowMeta* meta, int rows, int n_heads, int n_kv_heads,
                               int head_dim, int layer, uint8_t* arena, const float* rope_cs, hipStream_t st);
-// attention of each item's query row over its key range; direct output (hi/lo planes) or partials
-hipError_t launch_attention(const float* qkv, int ld_qkv, const RowMeta* meta, const AttnItem* items, int n_items,
-                            int n_heads, int n_kv_heads, int head_dim, int layer, const uint8_t* arena,
-                            uint16_t* out, int64_t out_plane, int ld_out, float* part_o, float* part_ml,
-                            hipStream_t st);
-// merge split partials of each (row, head) -> hi/lo planes
-hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const int32_t* row_parts, int rows,
-                               int n_heads, int head_dim, uint16_t* out, int64_t out_plane, int ld_out,
-                               hipStream_t st);
+// Attention of each item's query row over its key range of the row's slab.
+struct AttnArgs {
+  const float* qkv;          // projections [rows, ld_qkv]: q heads, then k heads, then v heads
+  int32_t ld_qkv;
+  const RowMeta* meta;
+  const AttnItem* items;
+  int32_t n_heads, n_kv_heads, layer;
+  uint8_t* arena;
+  const float2* rope_cs;     // [max_pos][head_dim/2] (cos, sin)
+  int32_t rope_q;            // 1: rotate q to the row's position here (decode)
+  int32_t append;            // 1: the item ending at pos+1 rotates k, writes K/V at pos (decode)
+  uint16_t* out;             // output planes (hi; lo at out + out_plane), row stride ld_out
+  int64_t out_plane;
+  int32_t ld_out;
+  float* part_o;             // split partials [slot][n_heads][head_dim]
+  float* part_ml;            // split (max, sum) [slot][n_heads][2]
+  const int2* row_parts;     // per row: (first slot, number of splits; 0 = not split)
+  int32_t* counters;         // per (row, KV head) arrival counters, zero between launches
+};
+hipError_t launch_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
+
 // greedy argmax per row, lowest id on ties
 hipError_t launch_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st);
 // scatter canonical K/V [L, n, Hkv, Dh] into a slab at [pos, pos+n), or gather back

@@ -114,6 +114,7 @@ struct cbd_ctx {
   float* ss = nullptr;      // per-16-feature sums of squares of h [d/16][R]
   float* gemm_part = nullptr;   // split-K partial tiles
   int32_t* gemm_counters = nullptr;  // split-K arrival counters, one per row block
+  int32_t* attn_counters = nullptr;  // split-attention arrival counters [64][n_kv_heads]
   size_t gemm_part_bytes = 0;
   int gemm_counter_count = 0;
   float* qkv = nullptr;
@@ -319,6 +320,7 @@ static cbd_status setup_device(cbd_ctx* c) {
   }
   bytes += c->gemm_part_bytes + 256;
   bytes += (size_t)c->gemm_counter_count * 4 + 256;
+  bytes += (size_t)64 * m.n_kv_heads * 4 + 256;
   bytes += R * m.d_model * 4 + 256;                 // h
   bytes += 2 * R * m.d_model * 2 + 256;             // xa planes
   bytes += 2 * R * c->q_dim * 2 + 256;              // xo planes
@@ -339,6 +341,7 @@ static cbd_status setup_device(cbd_ctx* c) {
   c->ss = align_ptr<float>(p, (size_t)(m.d_model / 16) * R);
   c->gemm_part = align_ptr<float>(p, c->gemm_part_bytes / 4);
   c->gemm_counters = align_ptr<int32_t>(p, c->gemm_counter_count);
+  c->attn_counters = align_ptr<int32_t>(p, (size_t)64 * m.n_kv_heads);
   c->qkv = align_ptr<float>(p, R * c->qkv_dim);
   c->xa_plane = (int64_t)R * m.d_model;
   c->xo_plane = (int64_t)R * c->q_dim;
@@ -640,26 +643,39 @@ cbd_status run_layers(cbd_ctx* c, int rows, int x_blocks, const RowMeta* meta_d,
                   gemm_flops(rows, c->qkv_dim, m.d_model), st);
       HIP_TRY(run_gemm(c, a, EPI_STORE, x_blocks, 0, st), "qkv projection");
     }
-    {
+    // decode rotates q and appends K/V inside the attention kernel; the prefill appends every
+    // token's K/V first (its queries read each other's keys)
+    const bool fused = row_parts_d != nullptr;
+    if (!fused) {
       ProfScope p(c, CBD_KERNEL_ROPE_APPEND, (double)rows * (c->qkv_dim * 4.0 + c->q_dim * 4.0 + c->kv_dim * 4.0), 0, st);
       HIP_TRY(launch_rope_append(c->qkv, c->qkv_dim, meta_d, rows, m.n_heads, m.n_kv_heads, m.head_dim, l, c->arena,
                                  c->rope_cs, st),
               "rope/append");
     }
     {
+      AttnArgs at{};
+      at.qkv = c->qkv;
+      at.ld_qkv = c->qkv_dim;
+      at.meta = meta_d;
+      at.items = items_d;
+      at.n_heads = m.n_heads;
+      at.n_kv_heads = m.n_kv_heads;
+      at.layer = l;
+      at.arena = c->arena;
+      at.rope_cs = reinterpret_cast<const float2*>(c->rope_cs);
+      at.rope_q = fused ? 1 : 0;
+      at.append = fused ? 1 : 0;
+      at.out = c->xo;
+      at.out_plane = c->xo_plane;
+      at.ld_out = c->q_dim;
+      at.part_o = c->part_o;
+      at.part_ml = c->part_ml;
+      at.row_parts = reinterpret_cast<const int2*>(row_parts_d);
+      at.counters = c->attn_counters;
       const double kvb = kv_keys * c->kv_dim * 2.0 * 2.0;
-      ProfScope p(c, CBD_KERNEL_ATTENTION, kvb + (double)rows * c->q_dim * (4.0 + 4.0),
+      ProfScope p(c, CBD_KERNEL_ATTENTION, kvb + (double)rows * c->q_dim * (4.0 + 4.0) + n_parts * 0.0,
                   kv_keys * m.n_heads * m.head_dim * 4.0, st);
-      HIP_TRY(launch_attention(c->qkv, c->qkv_dim, meta_d, items_d, n_items, m.n_heads, m.n_kv_heads, m.head_dim, l,
-                               c->arena, c->xo, c->xo_plane, c->q_dim, c->part_o, c->part_ml, st),
-              "attention");
-    }
-    if (n_parts > 0) {
-      ProfScope p(c, CBD_KERNEL_ATTN_COMBINE, (double)n_parts * m.n_heads * (m.head_dim + 2) * 4.0 +
-                  (double)rows * c->q_dim * 4.0, 0, st);
-      HIP_TRY(launch_attn_combine(c->part_o, c->part_ml, row_parts_d, rows, m.n_heads, m.head_dim, c->xo, c->xo_plane,
-                                  c->q_dim, st),
-              "attention combine");
+      HIP_TRY(launch_attention(at, n_items, m.head_dim, st), "attention");
     }
     a = gemm_args(c, c->xo, c->xo_plane, c->q_dim, rows, {L.wo}, {m.d_model}, m.d_model);
     with_residual(c, a, L.ffn_norm);
@@ -875,12 +891,13 @@ extern "C" cbd_status cbd_pack_int4(const uint8_t* codes, const uint16_t* scale,
                                     int64_t K, uint32_t* packed_out, uint16_t* aux_out) {
   if (!codes || !scale || !bias || !packed_out || !aux_out) return fail(CBD_E_INVAL, "cbd_pack_int4: null argument");
   if (N < 1 || K < 128 || K % 128 || N % 16) return fail(CBD_E_INVAL, "cbd_pack_int4: need K % 128 == 0 and N % 16 == 0");
-  const int64_t G = K / 64;
+  const int64_t G = K / 64, blocks = K / 128;
   for (int64_t n = 0; n < N; ++n) {
     const uint8_t* row = codes + n * K;
-    uint32_t* out = packed_out + n * (K / 8);
-    for (int64_t b = 0; b < K / 128; ++b)
-      for (int g = 0; g < 4; ++g)
+    const int64_t tr = n / 16, r = n % 16;
+    for (int64_t b = 0; b < blocks; ++b)
+      for (int g = 0; g < 4; ++g) {
+        uint32_t* lane_words = packed_out + ((tr * blocks + b) * 64 + (16 * g + r)) * 4;
         for (int j = 0; j < 4; ++j) {
           uint32_t word = 0;
           const int64_t base = b * 128 + 64 * (j / 2) + 16 * g + 8 * (j % 2);
@@ -889,13 +906,25 @@ extern "C" cbd_status cbd_pack_int4(const uint8_t* codes, const uint16_t* scale,
             if (q > 15) return fail(CBD_E_INVAL, "cbd_pack_int4: code %u out of range", q);
             word |= q << (4 * ((e >> 1) + 4 * (e & 1)));
           }
-          out[b * 16 + 4 * g + j] = word;
+          lane_words[j] = word;
         }
+      }
     for (int64_t gi = 0; gi < G; ++gi) {
       aux_out[(gi * N + n) * 2 + 0] = scale[n * G + gi];
       aux_out[(gi * N + n) * 2 + 1] = bias[n * G + gi];
     }
   }
+  return CBD_OK;
+}
+
+extern "C" cbd_status cbd_pack_bf16(const void* src_dev, int64_t N, int64_t K, void* dst_dev, cbd_stream stream) {
+  if (!src_dev || !dst_dev || !aligned16(src_dev) || !aligned16(dst_dev))
+    return fail(CBD_E_INVAL, "cbd_pack_bf16: pointers must be 16-byte aligned device pointers");
+  if (N < 16 || N % 16 || K < 32 || K % 32) return fail(CBD_E_INVAL, "cbd_pack_bf16: need N % 16 == 0 and K % 32 == 0");
+  if (src_dev == dst_dev) return fail(CBD_E_INVAL, "cbd_pack_bf16: source and destination must differ");
+  HIP_TRY(launch_pack_bf16(static_cast<const uint16_t*>(src_dev), N, K, static_cast<uint16_t*>(dst_dev),
+                           static_cast<hipStream_t>(stream)),
+          "cbd_pack_bf16 launch");
   return CBD_OK;
 }
 

@@ -87,12 +87,15 @@ typedef struct {
 } cbd_model_config;
 
 /*
- * One weight matrix W [N, K] (N outputs, K inputs; y = W x).
- *  bf16 format: data = bf16 [N, K] row-major; aux unused.
+ * One weight matrix W [N, K] (N outputs, K inputs; y = W x), in the
+ * library's streaming layout (each weight is read once per step, so the
+ * layout is chosen for sequential HBM reads):
+ *  bf16 format: data = bf16 as written by cbd_pack_bf16 from a row-major
+ *  [N, K] matrix; aux unused.
  *  int4 format (4-bit affine, groups of 64 consecutive inputs of one row,
  *  w = scale * code + bias with codes 0..15): data = packed codes and aux =
- *  bf16 (scale, bias) pairs, both in the layout cbd_pack_int4 writes.
- *  K must be a multiple of 128 for int4.
+ *  bf16 (scale, bias) pairs, both as written by cbd_pack_int4.
+ *  N must be a multiple of 16; K a multiple of 32 (bf16) or 128 (int4).
  */
 typedef struct {
   const void* data;
@@ -252,15 +255,26 @@ cbd_status cbd_linear(cbd_ctx* ctx, const cbd_matrix* w, int32_t N, int32_t K, c
                       float* y_dev, int32_t splits, cbd_stream stream);
 
 /*
- * Pack a 4-bit affine matrix into the int4 layout (host memory, any thread).
+ * Pack a row-major bf16 matrix [N, K] (device) into the streaming layout
+ * (device, a different buffer of the same size), enqueued on `stream`.
+ * Layout: fragments of 16 rows x 32 inputs, 1 KB each; fragment (t, f)
+ * (rows 16t.., inputs 32f..) is the (t * K/32 + f)-th; inside it, the 16
+ * bytes at offset 16*l hold row 16t + l%16, inputs 32f + 8*(l/16) .. +7.
+ * N % 16 == 0, K % 32 == 0.
+ */
+cbd_status cbd_pack_bf16(const void* src_dev, int64_t N, int64_t K, void* dst_dev, cbd_stream stream);
+
+/*
+ * Pack a 4-bit affine matrix into the int4 streaming layout (host memory).
  *  codes   uint8 [N, K], values 0..15 (w = scale * code + bias)
  *  scale, bias  bf16 bits [N, K/64]
- *  packed_out   uint32 [N, K/8]
+ *  packed_out   uint32 [N*K/8]
  *  aux_out      bf16 bits [K/64, N, 2]: (scale, bias) pairs, group-major
- * Packed layout: each row is split into blocks of 128 inputs held in 16
- * words. Word 4g+j of a block (g, j in 0..3) holds the 8 codes of inputs
- * 64*(j/2) + 16*g + 8*(j%2) + e, e = 0..7, with input e in nibble
- * (e/2) + 4*(e%2). K must be a multiple of 128 and N of 16.
+ * Packed layout: blocks of 16 rows x 128 inputs, 1 KB each; block (t, b)
+ * is the (t * K/128 + b)-th. Inside it, the 4 words at offset 16*l belong
+ * to row 16t + r with r = l%16 and g = l/16: word j (0..3) holds the 8
+ * codes of inputs 128b + 64*(j/2) + 16*g + 8*(j%2) + e, e = 0..7, with
+ * input e in nibble (e/2) + 4*(e%2). K % 128 == 0, N % 16 == 0.
  */
 cbd_status cbd_pack_int4(const uint8_t* codes, const uint16_t* scale, const uint16_t* bias, int64_t N,
                          int64_t K, uint32_t* packed_out, uint16_t* aux_out);
@@ -281,9 +295,9 @@ typedef enum {
   CBD_KERNEL_EMBED = 0,
   CBD_KERNEL_NORM = 1,
   CBD_KERNEL_QKV = 2,
-  CBD_KERNEL_ROPE_APPEND = 3,
+  CBD_KERNEL_ROPE_APPEND = 3,  /* prefill only: decode rotates and appends inside attention */
   CBD_KERNEL_ATTENTION = 4,
-  CBD_KERNEL_ATTN_COMBINE = 5,
+  CBD_KERNEL_ATTN_COMBINE = 5, /* reserved: splits are merged inside the attention kernel */
   CBD_KERNEL_O_PROJ = 6,
   CBD_KERNEL_GATE_UP = 7,
   CBD_KERNEL_DOWN = 8,

@@ -148,15 +148,17 @@ def test_create_rejects_bad_shapes(cbd):
 def unpack_int4_reference(packed, aux, n, k):
     """Decode the packed layout as the header documents it (independent of the packer's loops)."""
     codes = np.zeros((n, k), dtype=np.uint8)
-    words = packed.reshape(n, k // 128, 4, 4)  # [row, block, g, j]
-    for g in range(4):
+    words = packed.reshape(n // 16, k // 128, 64, 4)  # [row tile, block, lane, word]
+    for lane in range(64):
+        r, g = lane % 16, lane // 16
         for j in range(4):
-            w = words[:, :, g, j].astype(np.uint64)
+            w = words[:, :, lane, j].astype(np.uint64)  # [row tile, block]
             for e in range(8):
                 nib = (e // 2) + 4 * (e % 2)
                 vals = ((w >> np.uint64(4 * nib)) & np.uint64(15)).astype(np.uint8)
+                rows = np.arange(n // 16) * 16 + r
                 cols = np.arange(k // 128) * 128 + 64 * (j // 2) + 16 * g + 8 * (j % 2) + e
-                codes[:, cols] = vals
+                codes[np.ix_(rows, cols)] = vals
     scale = aux[:, :, 0].T.copy()
     bias = aux[:, :, 1].T.copy()
     return codes, scale, bias
@@ -165,7 +167,7 @@ def unpack_int4_reference(packed, aux, n, k):
 def test_int4_packing_layout(cbd):
     m = synth._int4_matrix(3, 5, (32, 256), 64, 0.02)
     packed, aux = cbd.pack_int4(m["codes"], m["scale"], m["bias"])
-    assert packed.shape == (32, 32) and aux.shape == (4, 32, 2)
+    assert packed.shape == (32 * 256 // 8,) and aux.shape == (4, 32, 2)
     codes, scale, bias = unpack_int4_reference(packed, aux, 32, 256)
     assert np.array_equal(codes, m["codes"])
     assert np.array_equal(scale, m["scale"]) and np.array_equal(bias, m["bias"])

@@ -69,7 +69,7 @@ def test_linear_bf16(torch, cbd, linear_engines, N, K, rows):
     eng = linear_engines["bf16"]
     W = synth.normal_bf16(7, N + K, (N, K), 0.02)
     X = synth.normal_f32(8, rows, (rows, K), 1.0)
-    wd, xd = to_dev_bits(torch, W), torch.from_numpy(X).cuda()
+    wd, xd = cbd.pack_bf16_device(to_dev_bits(torch, W)), torch.from_numpy(X).cuda()
     y = torch.empty((rows, N), dtype=torch.float32, device="cuda")
     eng.linear(cbd.Matrix(wd.data_ptr(), None), N, K, xd, y)
     torch.cuda.synchronize()
@@ -87,7 +87,7 @@ def test_linear_bf16_splits(torch, cbd, linear_engines, N, K, rows, splits):
     eng = linear_engines["bf16"]
     W = synth.normal_bf16(17, N + K, (N, K), 0.02)
     X = synth.normal_f32(18, rows, (rows, K), 1.0)
-    wd, xd = to_dev_bits(torch, W), torch.from_numpy(X).cuda()
+    wd, xd = cbd.pack_bf16_device(to_dev_bits(torch, W)), torch.from_numpy(X).cuda()
     y = torch.empty((rows, N), dtype=torch.float32, device="cuda")
     eng.linear(cbd.Matrix(wd.data_ptr(), None), N, K, xd, y, splits=splits)
     torch.cuda.synchronize()
@@ -123,6 +123,20 @@ def test_linear_int4(torch, cbd, linear_engines, N, K, rows):
 
 
 # ----------------------------------------------------------------------------- slabs and argmax
+
+def test_pack_bf16_layout(torch, cbd):
+    """The device packer writes exactly the documented streaming layout (checked on the host)."""
+    N, K = 48, 96
+    W = (np.arange(N * K, dtype=np.uint32) % 60000).astype(np.uint16).reshape(N, K)
+    got = cbd.pack_bf16_device(to_dev_bits(torch, W)).cpu().numpy().view(np.uint16).reshape(-1)
+    ref = np.empty(N * K, dtype=np.uint16)
+    for t in range(N // 16):
+        for f in range(K // 32):
+            for l in range(64):
+                off = ((t * (K // 32) + f) * 64 + l) * 8
+                ref[off:off + 8] = W[16 * t + l % 16, 32 * f + 8 * (l // 16): 32 * f + 8 * (l // 16) + 8]
+    assert np.array_equal(got, ref)
+
 
 def test_slab_append_read_roundtrip(torch, cbd):
     _say("slab append/read roundtrip")
