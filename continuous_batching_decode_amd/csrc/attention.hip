@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
       float acc = 0.f;
 #pragma unroll
       for (int g2 = 0; g2 < KGROUPS; ++g2) acc += red[g2][h][d];
-      const int64_t off = (int64_t)it.row * a.ld_out + (j * G + h) * DH + d;
+      const int64_t off = xfrag_off(it.row, (j * G + h) * DH + d, a.ld_out);
       store_split(a.out + off, a.out + a.out_plane + off, acc / ml_s[h][1]);
     }
     return;
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
       acc += w * __hip_atomic_load(a.part_o + slot * DH + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       l += w * __hip_atomic_load(a.part_ml + slot * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const int64_t off = (int64_t)it.row * a.ld_out + (j * G + h) * DH + d;
+    const int64_t off = xfrag_off(it.row, (j * G + h) * DH + d, a.ld_out);
     store_split(a.out + off, a.out + a.out_plane + off, acc / l);
   }
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

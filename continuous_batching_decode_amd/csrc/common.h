@@ -33,6 +33,15 @@ CBD_DEVICE float wave_max(float v) {
   return v;
 }
 
+// Activations fed to the weight-streaming products are stored fragment-major:
+// fragments of 16 rows x 32 inputs (1 KB of bf16), fragment (row/16, k/32)
+// at index (row/16) * (K/32) + k/32, and inside it lane l = 16*((k%32)/8) +
+// row%16 holds 8 consecutive inputs. A wave then loads an MFMA operand of 16
+// rows x 32 inputs as 1 KB of consecutive memory.
+CBD_DEVICE int64_t xfrag_off(int row, int k, int K) {
+  return ((int64_t)(row >> 4) * (K >> 5) + (k >> 5)) * 512 + ((((k & 31) >> 3) << 4) + (row & 15)) * 8 + (k & 7);
+}
+
 // Per-query-row metadata shared by the RoPE/append and attention kernels.
 struct RowMeta {
   int64_t slab_off;  // byte offset of the row's slab in the arena

@@ -31,7 +31,6 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, const
   tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);  // ids stay on the device: clamp out-of-range ids
   const uint16_t* e = embed + (int64_t)tok * d;
   float* hrow = h + (int64_t)r * d;
-  uint16_t* xr = xp + (int64_t)r * d;
   for (int t = threadIdx.x; t < d / 16; t += 256) {
     float s = 0.f;
 #pragma unroll
@@ -40,7 +39,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, const
       const float v = bf16_to_f32(e[f]);
       hrow[f] = v;
       s += v * v;
-      split_store(xr + f, xr + plane + f, v * bf16_to_f32(gain[f]));
+      const int64_t o = xfrag_off(r, f, d);
+      split_store(xp + o, xp + plane + o, v * bf16_to_f32(gain[f]));
     }
     ss[(int64_t)t * ss_ld + r] = s;
   }
@@ -49,9 +49,24 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, const
 __global__ __launch_bounds__(256) void split_planes_kernel(const float* x, int K, uint16_t* out, int64_t plane) {
   const int r = blockIdx.x;
   for (int i = threadIdx.x; i < K; i += 256) {
-    const int64_t o = (int64_t)r * K + i;
-    split_store(out + o, out + plane + o, x[o]);
+    const int64_t o = xfrag_off(r, i, K);
+    split_store(out + o, out + plane + o, x[(int64_t)r * K + i]);
   }
+}
+
+// Copy activation row row_idx[r] (fragment-major planes, width d) to row r of the output planes,
+// with its per-16-feature sums of squares.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* x, int64_t x_plane, const float* ss,
+                                                          int ss_ld, const int32_t* row_idx, int d, uint16_t* out,
+                                                          int64_t out_plane, float* ss_out, int ss_out_ld) {
+  const int r = blockIdx.x;
+  const int src = row_idx[r];
+  for (int f = threadIdx.x; f < d; f += 256) {
+    const int64_t i = xfrag_off(src, f, d), o = xfrag_off(r, f, d);
+    out[o] = x[i];
+    out[o + out_plane] = x[i + x_plane];
+  }
+  for (int t = threadIdx.x; t < d / 16; t += 256) ss_out[(int64_t)t * ss_out_ld + r] = ss[(int64_t)t * ss_ld + src];
 }
 
 // rope_cs: [max_pos][head_dim/2] (cos, sin) pairs, fp32 values of angles computed in fp64.
@@ -159,6 +174,14 @@ hipError_t launch_embed(const int32_t* tokens, int rows, const uint16_t* embed, 
 
 hipError_t launch_split_planes(const float* x, int rows, int K, uint16_t* out, int64_t plane, hipStream_t st) {
   hipLaunchKernelGGL(split_planes_kernel, dim3(rows), dim3(256), 0, st, x, K, out, plane);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const uint16_t* x, int64_t x_plane, const float* ss, int ss_ld, const int32_t* row_idx,
+                              int rows, int d, uint16_t* out, int64_t out_plane, float* ss_out, int ss_out_ld,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(rows), dim3(256), 0, st, x, x_plane, ss, ss_ld, row_idx, d, out,
+                     out_plane, ss_out, ss_out_ld);
   return hipGetLastError();
 }
 

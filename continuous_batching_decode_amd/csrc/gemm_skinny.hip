@@ -2,29 +2,31 @@
 //
 // y[b, n] = sum_k W[n, k] x[b, k] for up to 64 activation rows per column block.
 // The page "Continuous Decode Batching - the transformer capture" (section
-// "The throughput law") is the reason for the shape of this kernel: the
-// weight read w is paid once per launch whatever the number of rows, so the
-// kernel streams W from HBM exactly once with wide coalesced loads and every
-// row of the batch rides on that single read.
+// "The throughput law") is the reason for the shape of these kernels: the
+// weight read w is paid once per launch whatever the number of rows, so they
+// stream W from HBM exactly once with wide sequential loads and every row of
+// the batch rides on that single read.
 //
-// Mapping (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
-//  - A operand = 16 consecutive weight rows x 32 inputs (lane l holds row
-//    l%16, inputs 8*(l/16)..+7). Weights live in the library's streaming
-//    layout: each such 1 KB fragment is stored contiguously in lane order and
-//    fragments run along K, so every wave load instruction reads 1 KB of
-//    consecutive memory (DRAM-friendly, unlike 16 rows x 64 bytes of a
-//    row-major matrix). Loads are double-buffered in registers.
-//  - B operand = 16 activation rows x the same 32 inputs, read from LDS: the
-//    workgroup stages each chunk of the activations once and its 4 waves
-//    share it, so the vector-memory path carries (almost) only weights.
-//  - A workgroup = 4 waves x RT subtiles of 16 weight rows. The input dim is
-//    split over S workgroups when the matrix is too small to fill the chip;
-//    their partial tiles go to a workspace and the last workgroup to finish
-//    (an atomic arrival counter, reset by that workgroup) adds them in a
-//    fixed order and runs the epilogue, so results are deterministic.
+// Operands (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
+//  - A = 16 weight rows x 32 inputs (lane l: row l%16, inputs 8*(l/16)..+7).
+//    Weights live in the streaming layout: each such 1 KB fragment is stored
+//    contiguously in lane order and fragments run along K, so every wave load
+//    instruction reads 1 KB of consecutive memory.
+//  - B = 16 activation rows x the same 32 inputs, from activations stored
+//    fragment-major the same way (xfrag_off).
 //  - NB column tiles of 16 cover up to 16*NB activation rows; padding rows
 //    only affect padding outputs (an MFMA output column depends only on the
 //    same column of B), which are never stored.
+// Two ways to cut a launch:
+//  - k split (small matrices): one tile of 16*RT weight rows per workgroup;
+//    its waves each stream a contiguous slice of K (double-buffered loads,
+//    activations straight from L2) and add their partial sums through LDS in
+//    a fixed order. No workgroup waits on another.
+//  - row split (large matrices, and every prefill): 4 waves x RT subtiles of
+//    16 rows share activation chunks staged once in LDS. If K must also be
+//    split over workgroups, the partial tiles go to a workspace and the last
+//    workgroup to arrive (agent-scope atomic counter, reset by it) adds them
+//    in a fixed order. Results are deterministic either way.
 // Activations are carried as two bf16 planes, x = hi + lo with hi = bf16(x)
 // and lo = bf16(x - hi), so the product keeps about 16 significant bits of x
 // (two MFMAs per weight fragment; the products are exact in fp32).
@@ -48,7 +50,6 @@ namespace cbd {
 
 namespace {
 
-CBD_DEVICE bf16x8_t as_frag(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 CBD_DEVICE bf16x8_t as_frag(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // weights are read once per launch: non-temporal loads keep them from
@@ -57,15 +58,15 @@ CBD_DEVICE u32x4_t load_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
-CBD_DEVICE bf16x8_t lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+CBD_DEVICE bf16x8_t load_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
 // 8 int4 codes of one packed word -> bf16 (128 + q) in input order.
 CBD_DEVICE bf16x8_t widen_codes(uint32_t w) {
-  uint4 r;
-  r.x = (w & 0x000F000Fu) | 0x43004300u;
-  r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  u32x4_t r;
+  r[0] = (w & 0x000F000Fu) | 0x43004300u;
+  r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+  r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+  r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
   return as_frag(r);
 }
 
@@ -80,7 +81,7 @@ CBD_DEVICE int seg_of(const SkinnyArgs& a, int grow) {
 }
 CBD_DEVICE int seg_begin(const SkinnyArgs& a, int s) { return s == 0 ? 0 : a.seg_end[s - 1]; }
 
-// 4 consecutive values -> hi/lo bf16 planes (8 bytes each)
+// 4 consecutive inputs k..k+3 (k % 4 == 0) of one row -> hi/lo planes (8 bytes each)
 CBD_DEVICE void store_split4(uint16_t* hi, uint16_t* lo, float v0, float v1, float v2, float v3) {
   const uint32_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1), h2 = f32_to_bf16(v2), h3 = f32_to_bf16(v3);
   uint2 H, L;
@@ -92,67 +93,201 @@ CBD_DEVICE void store_split4(uint16_t* hi, uint16_t* lo, float v0, float v1, flo
   *reinterpret_cast<uint2*>(lo) = L;
 }
 
-}  // namespace
+// First row of weight subtile i of tile t (16*RT consecutive rows, or for SwiGLU the gate and up
+// rows of the same 16 features).
+template <int RT, int EPI>
+CBD_DEVICE int subtile_row(const SkinnyArgs& a, int t, int i) {
+  if constexpr (EPI == EPI_SWIGLU) return i == 0 ? 16 * t : a.seg_end[0] + 16 * t;
+  return 16 * RT * t + 16 * i;
+}
 
-// LDS bytes of one launch: activation chunk (2 planes) + norm partial sums.
-// Pack a row-major bf16 matrix [N, K] into the streaming layout (N % 16 == 0, K % 32 == 0).
-__global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t* src, int64_t N, int64_t K, uint16_t* dst) {
-  const int64_t chunks = N * K / 8;
-  const int64_t kfr = K / 32;
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
-    const int64_t f = c >> 6;
-    const int l = (int)(c & 63);
-    const int64_t tr = f / kfr, tk = f - tr * kfr;
-    const int64_t row = 16 * tr + (l & 15), col = 32 * tk + 8 * (l >> 4);
-    *reinterpret_cast<uint4*>(dst + 8 * c) = *reinterpret_cast<const uint4*>(src + row * K + col);
+// Weight pointers (lane offset included) of the RT subtiles at input k0.
+template <int RT, int FMT>
+CBD_DEVICE void weight_ptrs(const SkinnyArgs& a, const int (&sub_row)[RT], int K, int k0, int lane,
+                            const void* (&wr)[RT]) {
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const int s = seg_of(a, sub_row[i]);
+    const int tr = (sub_row[i] - seg_begin(a, s)) >> 4;
+    if constexpr (FMT == FMT_BF16)
+      wr[i] = reinterpret_cast<const uint16_t*>(a.w[s]) + ((int64_t)tr * (K >> 5) + (k0 >> 5)) * 512 + 8 * lane;
+    else
+      wr[i] = reinterpret_cast<const uint32_t*>(a.w[s]) + ((int64_t)tr * (K >> 7) + (k0 >> 7)) * 256 + 4 * lane;
   }
 }
 
-hipError_t launch_pack_bf16(const uint16_t* src, int64_t N, int64_t K, uint16_t* dst, hipStream_t st) {
-  const int64_t chunks = N * K / 8;
-  const int blocks = (int)std::min<int64_t>((chunks + 255) / 256, 65536);
-  hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, st, src, N, K, dst);
-  return hipGetLastError();
+// 1/rms of each activation row of the block from the producer's per-16-feature sums of squares,
+// added in 16 fixed groups (same order in every workgroup and launch). All threads take part;
+// norm_part is [16][ROWS] floats of LDS.
+template <int ROWS>
+CBD_DEVICE void norm_partials(const SkinnyArgs& a, int col0, int rows_valid, float* norm_part) {
+  const int per = a.ss_tiles / 16;
+  for (int i = threadIdx.x; i < 16 * ROWS; i += blockDim.x) {
+    const int c = i % ROWS, grp = i / ROWS;
+    float s = 0.f;
+    if (c < rows_valid) {
+      const float* p = a.ss + (int64_t)grp * per * a.ss_ld + col0 + c;
+      for (int t = 0; t < per; ++t) s += p[(int64_t)t * a.ss_ld];
+    }
+    norm_part[grp * ROWS + c] = s;
+  }
 }
 
-size_t skinny_lds_bytes(int nb, int kc) { return (size_t)2 * 16 * nb * (kc + 8) * 2 + (size_t)16 * 16 * nb * 4; }
+// norm_part may hold nq sets of [16][ROWS] partials (set-major), added set by set in each group.
+template <int ROWS>
+CBD_DEVICE float norm_inv(const SkinnyArgs& a, const float* norm_part, int col, int nq) {
+  float s = 0.f;
+  for (int grp = 0; grp < 16; ++grp)
+    for (int q = 0; q < nq; ++q) s += norm_part[(q * 16 + grp) * ROWS + col];
+  return 1.0f / sqrtf(s / a.norm_dim + a.eps);
+}
 
+// Epilogue of one wave: lane holds y[b = 16c + l%16][n = subtile + 4*(l/16) + e].
+template <int RT, int NB, int EPI>
+CBD_DEVICE void epilogue(const SkinnyArgs& a, f32x4_t (&acc)[RT][NB], const int (&sub_row)[RT], int col0,
+                         int rows_valid, const float (&inv)[NB], int lane, const float4 (*hpre)[RT][NB]) {
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    const int b = 16 * c + r16;
+    const bool valid = b < rows_valid;
+    const int row = col0 + b;
+    if constexpr (EPI == EPI_SWIGLU) {
+      static_assert(RT == 2, "gate and up subtiles");
+      const int n = sub_row[0] + 4 * g;
+      float m[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m[e] = silu_f(acc[0][c][e] * inv[c]) * (acc[1][c][e] * inv[c]);
+      if (valid) {
+        const int64_t o = xfrag_off(row, n, a.N);
+        store_split4(a.out_x + o, a.out_x + a.out_plane + o, m[0], m[1], m[2], m[3]);
+      }
+    } else if constexpr (EPI == EPI_RESIDUAL) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const int n = sub_row[i] + 4 * g;
+        float4 hn = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) {
+          float4* p = reinterpret_cast<float4*>(a.out + (int64_t)row * a.ldo + n);
+          const float4 h = hpre ? (*hpre)[i][c] : *p;
+          hn = make_float4(h.x + acc[i][c][0], h.y + acc[i][c][1], h.z + acc[i][c][2], h.w + acc[i][c][3]);
+          *p = hn;
+          if (a.next_gain) {
+            const uint2 gg = *reinterpret_cast<const uint2*>(a.next_gain + n);
+            const int64_t o = xfrag_off(row, n, a.N);
+            store_split4(a.out_x + o, a.out_x + a.out_plane + o, hn.x * bf16_to_f32(gg.x & 0xFFFFu),
+                         hn.y * bf16_to_f32(gg.x >> 16), hn.z * bf16_to_f32(gg.y & 0xFFFFu),
+                         hn.w * bf16_to_f32(gg.y >> 16));
+          }
+        }
+        if (a.ss_out) {
+          float s = hn.x * hn.x + hn.y * hn.y + hn.z * hn.z + hn.w * hn.w;
+          s += __shfl_xor(s, 16, 64);
+          s += __shfl_xor(s, 32, 64);
+          if (valid && g == 0) a.ss_out[(int64_t)(sub_row[i] >> 4) * a.ss_out_ld + row] = s;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const int n = sub_row[i] + 4 * g;
+        if (valid)
+          *reinterpret_cast<float4*>(a.out + (int64_t)row * a.ldo + n) =
+              make_float4(acc[i][c][0] * inv[c], acc[i][c][1] * inv[c], acc[i][c][2] * inv[c], acc[i][c][3] * inv[c]);
+      }
+    }
+  }
+}
+
+// int4 contribution of one 128-input block (4 k-fragments; fragments 0,1 form one group of 64,
+// fragments 2,3 the next). X[j][c][p] = activation fragment j of column tile c, plane p.
+template <int RT, int NB>
+CBD_DEVICE void int4_block(f32x4_t (&acc)[RT][NB], const u32x4_t (&Wq)[RT], const uint4 (&SB)[RT][2],
+                           const bf16x8_t (&X)[4][NB][2]) {
+  const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const bf16x8_t ones = as_frag(ones_u);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f32x4_t xsum[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        t = mfma(ones, X[2 * h + jj][c][0], t);
+        t = mfma(ones, X[2 * h + jj][c][1], t);
+      }
+      xsum[c] = t;
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const bf16x8_t A0 = widen_codes(Wq[i][2 * h]), A1 = widen_codes(Wq[i][2 * h + 1]);
+      const uint4 sb = SB[i][h];
+      float sc[4], bc[4];
+      const uint32_t pr[4] = {sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[e] = bf16_to_f32(pr[e] & 0xFFFFu);
+        bc[e] = bf16_to_f32(pr[e] >> 16) - 128.0f * sc[e];
+      }
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          t = mfma(A0, X[2 * h][c][p], t);
+          t = mfma(A1, X[2 * h + 1][c][p], t);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][c][e] += sc[e] * t[e] + bc[e] * xsum[c][e];
+      }
+    }
+  }
+}
+
+// scale/bias pairs of output rows 4g..4g+3 of each subtile for groups (k0/64, k0/64 + 1)
+template <int RT>
+CBD_DEVICE void load_scales(const SkinnyArgs& a, const int (&sub_row)[RT], int k0, int g, uint4 (&SB)[RT][2]) {
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const int s = seg_of(a, sub_row[i]);
+    const int sb = seg_begin(a, s), rows = a.seg_end[s] - sb;
+    const uint16_t* ar = reinterpret_cast<const uint16_t*>(a.aux[s]) + (int64_t)(sub_row[i] - sb + 4 * g) * 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      SB[i][h] = *reinterpret_cast<const uint4*>(ar + (int64_t)((k0 >> 6) + h) * rows * 2);
+  }
+}
+
+}  // namespace
+
+// ============================================================================ k split
+
+// Largest workgroup an instantiation is compiled for: 16 waves leave 128 registers per lane, enough
+// for one subtile and one column tile; the others get 8 waves (256 registers).
 template <int RT, int NB, int EPI, int FMT, int UC>
-__global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
+__global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_gemm_kernel(SkinnyArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int ROWS = 16 * NB;
   constexpr int NACC = RT * NB * 4;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
-  const int blk = blockIdx.x;
-  const int split = blockIdx.y;
-  const int S = gridDim.y;
-  const int xblk = blockIdx.z;
-  const int K = a.K;
-  const int Kr = K / S;
-  const int kbeg = split * Kr;
-  const int KC = a.kc;
-  const int XROW = KC + 8;  // padded LDS row (elements): consecutive rows start 16 bytes apart mod the bank width
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* norm_part = reinterpret_cast<float*>(smem + (size_t)2 * ROWS * XROW * 2);  // [16][ROWS]
-  __shared__ int s_last;
-
+  const int nw = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tile = blockIdx.x, xblk = blockIdx.y;
+  const int K = a.K, kw = K / nw, k0 = wave * kw;
   const int col0 = xblk * ROWS;
   const int rows_valid = min(ROWS, a.rows - col0);
+  float* red = reinterpret_cast<float*>(smem);              // [nw-1][NACC][64]
+  float* norm_part = red + (size_t)(nw - 1) * NACC * 64;    // [16][ROWS]
 
-  // weight-row subtiles of this wave
   int sub_row[RT];
 #pragma unroll
-  for (int i = 0; i < RT; ++i) {
-    if constexpr (EPI == EPI_SWIGLU) {  // RT == 2: the gate and up rows of the same 16 features
-      const int f0 = blk * 64 + 16 * wave;
-      sub_row[i] = i == 0 ? f0 : a.seg_end[0] + f0;
-    } else {
-      sub_row[i] = blk * 64 * RT + wave * 16 * RT + 16 * i;
-    }
-  }
+  for (int i = 0; i < RT; ++i) sub_row[i] = subtile_row<RT, EPI>(a, tile, i);
+  const void* wr[RT];
+  weight_ptrs<RT, FMT>(a, sub_row, K, k0, lane, wr);
+  // activation fragment pointers at k0 for each column tile
+  const uint16_t* xr[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) xr[c] = a.x + ((int64_t)((col0 >> 4) + c) * (K >> 5) + (k0 >> 5)) * 512 + 8 * lane;
 
   f32x4_t acc[RT][NB];
 #pragma unroll
@@ -160,49 +295,214 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // stage activation chunk [kc0, kc0 + KC) of this block's rows into LDS
+  // The epilogue's inputs that do not depend on the product are requested before the weights, so
+  // their latency hides behind the stream. First the norm's per-16-feature sums of squares: the 16
+  // groups x ROWS rows are split over nq thread sets, each adding ss_cnt consecutive partials in
+  // order (bf16 path only; the int4 path adds them all after its loop).
+  constexpr int SSMAX = 8;
+  const int ss_per = a.ss ? a.ss_tiles / 16 : 0;
+  int nq = 1;
+  while (2 * nq * 16 * ROWS <= (int)blockDim.x && ss_per % (2 * nq) == 0) nq *= 2;
+  const int ss_cnt = ss_per / nq;
+  const bool ss_early = FMT == FMT_BF16 && a.ss && ss_cnt <= SSMAX;
+  const int ss_item = threadIdx.x % (16 * ROWS), ss_q = threadIdx.x / (16 * ROWS);
+  const bool ss_mine = ss_early && ss_q < nq && (ss_item % ROWS) < rows_valid;
+  float ssv[SSMAX];
+  if (ss_mine) {
+    const float* p = a.ss + (int64_t)((ss_item / ROWS) * ss_per + ss_q * ss_cnt) * a.ss_ld + col0 + ss_item % ROWS;
+#pragma unroll
+    for (int t = 0; t < SSMAX; ++t)
+      if (t < ss_cnt) ssv[t] = p[(int64_t)t * a.ss_ld];
+  }
+  auto ss_store = [&]() {  // norm_part[q][grp][row]
+    if (ss_early && ss_q < nq) {
+      float s = 0.f;
+      if (ss_mine)
+#pragma unroll
+        for (int t = 0; t < SSMAX; ++t)
+          if (t < ss_cnt) s += ssv[t];
+      norm_part[(ss_q * 16 + ss_item / ROWS) * ROWS + ss_item % ROWS] = s;
+    }
+  };
+  // ... and the residual rows this wave's epilogue adds to
+  float4 hres[RT][NB];
+  if constexpr (EPI == EPI_RESIDUAL) {
+    if (wave == 0) {
+#pragma unroll
+      for (int c = 0; c < NB; ++c)
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+          if (16 * c + (lane & 15) < rows_valid)
+            hres[i][c] = *reinterpret_cast<const float4*>(a.out + (int64_t)(col0 + 16 * c + (lane & 15)) * a.ldo +
+                                                          sub_row[i] + 4 * (lane >> 4));
+    }
+  }
+
+  if constexpr (FMT == FMT_BF16) {
+    struct Buf {
+      u32x4_t A[UC][RT];
+      bf16x8_t X[UC][NB][2];
+    };
+    auto load = [&](Buf& f, int st) {
+#pragma unroll
+      for (int u = 0; u < UC; ++u)
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+          f.A[u][i] = load_stream(reinterpret_cast<const uint16_t*>(wr[i]) + (int64_t)(st * UC + u) * 512);
+#pragma unroll
+      for (int u = 0; u < UC; ++u)
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+          if (16 * c + (lane & 15) < rows_valid) {  // padding rows feed padding outputs only
+            f.X[u][c][0] = load_frag(xr[c] + (st * UC + u) * 512);
+            f.X[u][c][1] = load_frag(xr[c] + a.x_plane + (st * UC + u) * 512);
+          } else {
+            f.X[u][c][0] = f.X[u][c][1] = bf16x8_t{};
+          }
+        }
+    };
+    auto compute = [&](const Buf& f) {
+#pragma unroll
+      for (int u = 0; u < UC; ++u)
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+          for (int c = 0; c < NB; ++c) {
+            acc[i][c] = mfma(as_frag(f.A[u][i]), f.X[u][c][0], acc[i][c]);
+            acc[i][c] = mfma(as_frag(f.A[u][i]), f.X[u][c][1], acc[i][c]);
+          }
+    };
+    const int total = kw / (32 * UC);
+    Buf b0, b1;
+    load(b0, 0);
+    if (total > 1) load(b1, 1);
+    ss_store();  // waits for the sums only: they were requested before the weights
+    for (int st = 0; st < total; st += 2) {
+      compute(b0);
+      if (st + 2 < total) load(b0, st + 2);
+      if (st + 1 < total) {
+        compute(b1);
+        if (st + 3 < total) load(b1, st + 3);
+      }
+    }
+  } else {
+    const int total = kw / 128;
+    for (int st = 0; st < total; ++st) {
+      u32x4_t Wq[RT];
+      uint4 SB[RT][2];
+      bf16x8_t X[4][NB][2];
+#pragma unroll
+      for (int i = 0; i < RT; ++i) Wq[i] = load_stream(reinterpret_cast<const uint32_t*>(wr[i]) + (int64_t)st * 256);
+      load_scales<RT>(a, sub_row, k0 + st * 128, lane >> 4, SB);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+          if (16 * c + (lane & 15) < rows_valid) {
+            X[j][c][0] = load_frag(xr[c] + (4 * st + j) * 512);
+            X[j][c][1] = load_frag(xr[c] + a.x_plane + (4 * st + j) * 512);
+          } else {
+            X[j][c][0] = X[j][c][1] = bf16x8_t{};
+          }
+        }
+      int4_block<RT, NB>(acc, Wq, SB, X);
+    }
+  }
+
+  // fixed-order reduction of the K slices through LDS; the norm partials are gathered meanwhile
+  if (wave > 0) {
+    float* dst = red + (size_t)(wave - 1) * NACC * 64;
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int c = 0; c < NB; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[((i * NB + c) * 4 + e) * 64 + lane] = acc[i][c][e];
+  }
+  if (a.ss && !ss_early) norm_partials<ROWS>(a, col0, rows_valid, norm_part);
+  __syncthreads();
+  if (wave != 0) return;
+  for (int w = 1; w < nw; ++w) {
+    const float* src = red + (size_t)(w - 1) * NACC * 64;
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int c = 0; c < NB; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][c][e] += src[((i * NB + c) * 4 + e) * 64 + lane];
+  }
+  float inv[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c)
+    inv[c] = a.ss ? norm_inv<ROWS>(a, norm_part, 16 * c + (lane & 15), ss_early ? nq : 1) : 1.f;
+  epilogue<RT, NB, EPI>(a, acc, sub_row, col0, rows_valid, inv, lane, EPI == EPI_RESIDUAL ? &hres : nullptr);
+}
+
+// ============================================================================ row split
+
+template <int RT, int NB, int EPI, int FMT, int UC>
+__global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int ROWS = 16 * NB;
+  constexpr int NACC = RT * NB * 4;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int blk = blockIdx.x, split = blockIdx.y, S = gridDim.y, xblk = blockIdx.z;
+  const int K = a.K, Kr = K / S, kbeg = split * Kr, KC = a.kc;
+  const int col0 = xblk * ROWS;
+  const int rows_valid = min(ROWS, a.rows - col0);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [plane][NB][KC/32] fragments of 512 elements
+  float* norm_part = reinterpret_cast<float*>(smem + (size_t)2 * NB * KC * 16 * 2);  // [16][ROWS]
+  __shared__ int s_last;
+
+  // workgroup tile = 4 waves x RT subtiles (SwiGLU: 64 features, gate and up rows per wave)
+  int sub_row[RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) sub_row[i] = subtile_row<RT, EPI>(a, blk * 4 + wave, i);
+  const void* wr[RT];
+  weight_ptrs<RT, FMT>(a, sub_row, K, kbeg, lane, wr);
+
+  f32x4_t acc[RT][NB];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // stage activation chunk [kc0, kc0 + KC): whole fragments of the valid column tiles
+  const int kfc = KC >> 5;
+  const int valid_tiles = (rows_valid + 15) >> 4;
   auto stage_x = [&](int kc0) {
     __syncthreads();  // the previous chunk has been consumed
-    const int per_row = KC / 8;
-    // only the valid rows: padding rows of the LDS tile feed padding outputs only
-    for (int idx = threadIdx.x; idx < 2 * rows_valid * per_row; idx += 256) {
-      const int plane = idx / (rows_valid * per_row);
-      const int rem = idx - plane * rows_valid * per_row;
-      const int r = rem / per_row, c8 = rem - r * per_row;
-      const int row = a.x_rows ? a.x_rows[col0 + r] : col0 + r;
-      const uint16_t* src = a.x + (int64_t)plane * a.x_plane + (int64_t)row * a.ldx + kc0 + 8 * c8;
-      *reinterpret_cast<uint4*>(xs + (plane * ROWS + r) * XROW + 8 * c8) = *reinterpret_cast<const uint4*>(src);
+    const int per_tile = kfc * 64;  // 16-byte words of one plane of one column tile
+    for (int idx = threadIdx.x; idx < 2 * valid_tiles * per_tile; idx += 256) {
+      const int plane = idx / (valid_tiles * per_tile);
+      const int rem = idx - plane * valid_tiles * per_tile;
+      const int c = rem / per_tile, w = rem - c * per_tile;
+      if (16 * c + (w & 15) >= rows_valid) continue;  // word w holds row w%16 of its fragment
+      const uint16_t* src = a.x + (int64_t)plane * a.x_plane +
+                            ((int64_t)((col0 >> 4) + c) * (K >> 5) + (kc0 >> 5)) * 512 + 8 * w;
+      *reinterpret_cast<uint4*>(xs + ((plane * NB + c) * kfc) * 512 + 8 * w) = *reinterpret_cast<const uint4*>(src);
     }
     __syncthreads();
   };
-
-  const int spc = KC / ((FMT == FMT_BF16 ? 32 : 128) * UC);  // k-steps per chunk
-  const int total = Kr / ((FMT == FMT_BF16 ? 32 : 128) * UC);
+  auto xlds = [&](int plane, int c, int kf) { return load_frag(xs + ((plane * NB + c) * kfc + kf) * 512 + 8 * lane); };
 
   if constexpr (FMT == FMT_BF16) {
-    // fragment (tile row tr, k-fragment tk) at ((tr * K/32) + tk) * 512 elements; lane l at 8*l
-    const uint16_t* wr[RT];
-#pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      const int s = seg_of(a, sub_row[i]);
-      const int tr = (sub_row[i] - seg_begin(a, s)) >> 4;
-      wr[i] = reinterpret_cast<const uint16_t*>(a.w[s]) + ((int64_t)tr * (K >> 5) + (kbeg >> 5)) * 512 + 8 * lane;
-    }
+    const int spc = KC / (32 * UC), total = Kr / (32 * UC);
     u32x4_t A0[UC][RT], A1[UC][RT];
     auto loadw = [&](u32x4_t (&A)[UC][RT], int st) {
 #pragma unroll
       for (int u = 0; u < UC; ++u)
 #pragma unroll
-        for (int i = 0; i < RT; ++i) A[u][i] = load_stream(wr[i] + (int64_t)(st * UC + u) * 512);
+        for (int i = 0; i < RT; ++i)
+          A[u][i] = load_stream(reinterpret_cast<const uint16_t*>(wr[i]) + (int64_t)(st * UC + u) * 512);
     };
     auto compute = [&](const u32x4_t (&A)[UC][RT], int st) {
-      const int koff = ((st % spc) * UC) * 32 + 8 * g;
+      const int kf0 = (st % spc) * UC;
 #pragma unroll
       for (int u = 0; u < UC; ++u)
 #pragma unroll
         for (int c = 0; c < NB; ++c) {
-          const bf16x8_t xh = lds_frag(xs + (16 * c + r16) * XROW + koff + 32 * u);
-          const bf16x8_t xl = lds_frag(xs + (ROWS + 16 * c + r16) * XROW + koff + 32 * u);
+          const bf16x8_t xh = xlds(0, c, kf0 + u), xl = xlds(1, c, kf0 + u);
 #pragma unroll
           for (int i = 0; i < RT; ++i) {
             acc[i][c] = mfma(as_frag(A[u][i]), xh, acc[i][c]);
@@ -223,93 +523,31 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
       }
     }
   } else {
-    // int4: 128 inputs per step; lane l (row l%16, group g = l/16) reads its 4 words of the block
-    const uint32_t* wr[RT];
-    const uint16_t* ar[RT];
-    int seg_rows[RT];
-#pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      const int s = seg_of(a, sub_row[i]);
-      const int sb = seg_begin(a, s);
-      const int tr = (sub_row[i] - sb) >> 4;
-      wr[i] = reinterpret_cast<const uint32_t*>(a.w[s]) + ((int64_t)tr * (K >> 7) + (kbeg >> 7)) * 256 + 4 * lane;
-      seg_rows[i] = a.seg_end[s] - sb;
-      ar[i] = reinterpret_cast<const uint16_t*>(a.aux[s]) + (int64_t)(sub_row[i] - sb + 4 * g) * 2;
-    }
-    const uint4 ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-    const bf16x8_t ones = as_frag(ones_u);
+    const int spc = KC / 128, total = Kr / 128;
     for (int st = 0; st < total; ++st) {
       if (st % spc == 0) stage_x(kbeg + (st / spc) * KC);
-      u32x4_t Wq[UC][RT];
-      uint4 SB[UC][RT][2];
+      u32x4_t Wq[RT];
+      uint4 SB[RT][2];
+      bf16x8_t X[4][NB][2];
 #pragma unroll
-      for (int u = 0; u < UC; ++u)
+      for (int i = 0; i < RT; ++i) Wq[i] = load_stream(reinterpret_cast<const uint32_t*>(wr[i]) + (int64_t)st * 256);
+      load_scales<RT>(a, sub_row, kbeg + st * 128, lane >> 4, SB);
+      const int kf0 = (st % spc) * 4;
 #pragma unroll
-        for (int i = 0; i < RT; ++i) {
-          Wq[u][i] = load_stream(wr[i] + (int64_t)(st * UC + u) * 256);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int grp = ((kbeg + (st * UC + u) * 128) >> 6) + h;
-            SB[u][i][h] = *reinterpret_cast<const uint4*>(ar[i] + (int64_t)grp * seg_rows[i] * 2);
-          }
+        for (int c = 0; c < NB; ++c) {
+          X[j][c][0] = xlds(0, c, kf0 + j);
+          X[j][c][1] = xlds(1, c, kf0 + j);
         }
-#pragma unroll
-      for (int u = 0; u < UC; ++u) {
-        const int kb = ((st % spc) * UC + u) * 128;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          bf16x8_t X[2][NB][2];
-          f32x4_t xsum[NB];
-#pragma unroll
-          for (int c = 0; c < NB; ++c) {
-            f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-              const int off = kb + 64 * h + 16 * g + 8 * jj;
-              X[jj][c][0] = lds_frag(xs + (16 * c + r16) * XROW + off);
-              X[jj][c][1] = lds_frag(xs + (ROWS + 16 * c + r16) * XROW + off);
-              t = mfma(ones, X[jj][c][0], t);
-              t = mfma(ones, X[jj][c][1], t);
-            }
-            xsum[c] = t;
-          }
-#pragma unroll
-          for (int i = 0; i < RT; ++i) {
-            const uint32_t w0 = h ? Wq[u][i][2] : Wq[u][i][0];
-            const uint32_t w1 = h ? Wq[u][i][3] : Wq[u][i][1];
-            const bf16x8_t A0 = widen_codes(w0), A1 = widen_codes(w1);
-            const uint4 sb = SB[u][i][h];
-            float sc[4], bc[4];
-            const uint32_t pr[4] = {sb.x, sb.y, sb.z, sb.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              sc[e] = bf16_to_f32(pr[e] & 0xFFFFu);
-              bc[e] = bf16_to_f32(pr[e] >> 16) - 128.0f * sc[e];
-            }
-#pragma unroll
-            for (int c = 0; c < NB; ++c) {
-              f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int p = 0; p < 2; ++p) {
-                t = mfma(A0, X[0][c][p], t);
-                t = mfma(A1, X[1][c][p], t);
-              }
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[i][c][e] += sc[e] * t[e] + bc[e] * xsum[c][e];
-            }
-          }
-        }
-      }
+      int4_block<RT, NB>(acc, Wq, SB, X);
     }
   }
 
-  // -- split-K: partial tiles to the workspace; the last workgroup of the row block adds them.
-  (void)rows_valid;
-  // Partial tiles and the arrival counter are written and read with agent-scope
-  // atomic accesses, which the hardware performs at the level where all XCDs'
-  // L2 caches agree; each wave waits for its stores to be acknowledged
-  // (vmcnt 0) before the workgroup's arrival is counted. This avoids the full
-  // L2 write-back and invalidate that a device-wide fence costs per workgroup.
+  // split over workgroups: partial tiles to the workspace; the last workgroup of the row block adds
+  // them. Partials and the arrival counter use agent-scope atomic accesses (coherent across the XCDs'
+  // L2 caches); each wave waits for its stores to be acknowledged (vmcnt 0) before arrival is counted,
+  // which avoids the full L2 write-back and invalidate of a device-wide fence.
   if (S > 1) {
     float* base = a.part + (int64_t)blk * S * 4 * NACC * 64;
     float* mine = base + ((int64_t)split * 4 + wave) * NACC * 64;
@@ -345,112 +583,92 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // 1/rms of each activation row from the producer's per-16-feature sums of squares, added in
-  // 16 fixed groups (the same order in every workgroup and launch)
   float inv[NB];
   if (a.ss) {
-    __syncthreads();  // LDS reuse: all waves are past their last activation read
-    const int per = a.ss_tiles / 16;
-    for (int i = threadIdx.x; i < 16 * ROWS; i += 256) {
-      const int c = i % ROWS, grp = i / ROWS;
-      float s = 0.f;
-      if (c < rows_valid) {
-        const int row = a.x_rows ? a.x_rows[col0 + c] : col0 + c;
-        const float* p = a.ss + (int64_t)grp * per * a.ss_ld + row;
-        for (int t = 0; t < per; ++t) s += p[(int64_t)t * a.ss_ld];
-      }
-      norm_part[grp * ROWS + c] = s;
-    }
+    norm_partials<ROWS>(a, col0, rows_valid, norm_part);
     __syncthreads();
   }
 #pragma unroll
-  for (int c = 0; c < NB; ++c) {
-    inv[c] = 1.f;
-    if (a.ss) {
-      float s = 0.f;
-      for (int grp = 0; grp < 16; ++grp) s += norm_part[grp * ROWS + 16 * c + r16];
-      inv[c] = 1.0f / sqrtf(s / a.norm_dim + a.eps);
-    }
-  }
+  for (int c = 0; c < NB; ++c) inv[c] = a.ss ? norm_inv<ROWS>(a, norm_part, 16 * c + (lane & 15), 1) : 1.f;
+  epilogue<RT, NB, EPI>(a, acc, sub_row, col0, rows_valid, inv, lane, nullptr);
+}
 
-  // epilogue: lane holds y[b = 16c + l%16][n = subtile + 4*(l/16) + e]
-#pragma unroll
-  for (int c = 0; c < NB; ++c) {
-    const int b = 16 * c + r16;
-    const bool valid = b < rows_valid;
-    const int64_t orow = (int64_t)(col0 + b) * a.ldo;
-    if constexpr (EPI == EPI_SWIGLU) {
-      static_assert(RT == 2, "gate and up subtiles");
-      const int n = sub_row[0] + 4 * g;
-      float m[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) m[e] = silu_f(acc[0][c][e] * inv[c]) * (acc[1][c][e] * inv[c]);
-      if (valid) store_split4(a.out_x + orow + n, a.out_x + a.out_plane + orow + n, m[0], m[1], m[2], m[3]);
-    } else if constexpr (EPI == EPI_RESIDUAL) {
-#pragma unroll
-      for (int i = 0; i < RT; ++i) {
-        const int n = sub_row[i] + 4 * g;
-        float4 hn = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (valid) {
-          float4* p = reinterpret_cast<float4*>(a.out + orow + n);
-          const float4 h = *p;
-          hn = make_float4(h.x + acc[i][c][0], h.y + acc[i][c][1], h.z + acc[i][c][2], h.w + acc[i][c][3]);
-          *p = hn;
-          if (a.next_gain) {
-            const uint2 gg = *reinterpret_cast<const uint2*>(a.next_gain + n);
-            store_split4(a.out_x + orow + n, a.out_x + a.out_plane + orow + n, hn.x * bf16_to_f32(gg.x & 0xFFFFu),
-                         hn.y * bf16_to_f32(gg.x >> 16), hn.z * bf16_to_f32(gg.y & 0xFFFFu),
-                         hn.w * bf16_to_f32(gg.y >> 16));
-          }
-        }
-        if (a.ss_out) {
-          float s = hn.x * hn.x + hn.y * hn.y + hn.z * hn.z + hn.w * hn.w;
-          s += __shfl_xor(s, 16, 64);
-          s += __shfl_xor(s, 32, 64);
-          if (valid && g == 0) a.ss_out[(int64_t)(sub_row[i] >> 4) * a.ss_out_ld + col0 + b] = s;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < RT; ++i) {
-        const int n = sub_row[i] + 4 * g;
-        if (valid)
-          *reinterpret_cast<float4*>(a.out + orow + n) =
-              make_float4(acc[i][c][0] * inv[c], acc[i][c][1] * inv[c], acc[i][c][2] * inv[c], acc[i][c][3] * inv[c]);
-      }
-    }
+// ============================================================================ weight packing
+
+// row-major bf16 [N, K] -> streaming layout (N % 16 == 0, K % 32 == 0)
+__global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t* src, int64_t N, int64_t K, uint16_t* dst) {
+  const int64_t chunks = N * K / 8;
+  const int64_t kfr = K / 32;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
+    const int64_t f = c >> 6;
+    const int l = (int)(c & 63);
+    const int64_t tr = f / kfr, tk = f - tr * kfr;
+    const int64_t row = 16 * tr + (l & 15), col = 32 * tk + 8 * (l >> 4);
+    *reinterpret_cast<uint4*>(dst + 8 * c) = *reinterpret_cast<const uint4*>(src + row * K + col);
   }
 }
 
-// ----------------------------------------------------------------------------- launcher
-
-bool skinny_shape_ok(int fmt, int K) { return fmt == FMT_INT4 ? K % 512 == 0 : K % 256 == 0; }
-
-template <int RT, int EPI, int FMT, int UC>
-static hipError_t launch_nb(const SkinnyArgs& a, int nb, dim3 grid, hipStream_t st) {
-  const size_t lds = skinny_lds_bytes(nb, a.kc);
-  switch (nb) {
-    case 1: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
-    case 2: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
-    case 3: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 3, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
-    default: hipLaunchKernelGGL((skinny_gemm_kernel<RT, 4, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
-  }
+hipError_t launch_pack_bf16(const uint16_t* src, int64_t N, int64_t K, uint16_t* dst, hipStream_t st) {
+  const int64_t chunks = N * K / 8;
+  const int blocks = (int)std::min<int64_t>((chunks + 255) / 256, 65536);
+  hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, st, src, N, K, dst);
   return hipGetLastError();
 }
 
-// Plan of one launch: subtiles per wave, split of K, LDS chunk.
-SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int splits) {
+// ============================================================================ planning and launch
+
+bool skinny_shape_ok(int fmt, int K) { return fmt == FMT_INT4 ? K % 512 == 0 : K % 256 == 0; }
+
+static size_t rowsplit_lds(int nb, int kc) { return (size_t)2 * nb * kc * 16 * 2 + (size_t)16 * 16 * nb * 4; }
+static size_t ksplit_lds(int nw, int rt, int nb) {
+  // reduction slots, then up to max(threads, 16 * rows) norm partials
+  return (size_t)(nw - 1) * rt * nb * 4 * 64 * 4 + (size_t)std::max(64 * nw, 16 * 16 * nb) * 4;
+}
+
+SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int force) {
   SkinnyPlan p{};
   const int per_block = x_blocks > 1 ? 64 : rows;
   p.nb = (per_block + 15) / 16;
-  p.rt = (epi == EPI_SWIGLU || N % 128 == 0) ? 2 : 1;
-  p.row_blocks = epi == EPI_SWIGLU ? N / 64 : N / (64 * p.rt);
   const int step = fmt == FMT_INT4 ? 128 : 32;
+  // k split: one 16*rt-row tile per workgroup, enough waves to cover the chip
+  const int ks_rt = epi == EPI_SWIGLU ? 2 : 1;
+  const int ks_tiles = N / 16;
+  const int ks_uc = fmt == FMT_INT4 ? 1 : (K % (4 * 128) == 0 ? 4 : (K % (4 * 64) == 0 ? 2 : 1));
+  const int ks_unit = step * ks_uc;
+  const int ks_maxw = (ks_rt == 1 && p.nb == 1) ? 16 : 8;
+  const bool ks_ok = x_blocks == 1 && p.nb <= 2 && K % (4 * ks_unit) == 0;
+  // row split: 4 waves x rt subtiles
+  const int rs_rt = (epi == EPI_SWIGLU || N % 128 == 0) ? 2 : 1;
+  const int rs_blocks = epi == EPI_SWIGLU ? N / 64 : N / (64 * rs_rt);
+  bool use_ks = ks_ok && (long)rs_blocks < 600;
+  if (force < 0) use_ks = ks_ok;
+  if (force > 0) use_ks = false;
+  if (use_ks) {
+    p.kind = 1;
+    p.rt = ks_rt;
+    p.uc = ks_uc;
+    p.row_blocks = ks_tiles;
+    p.splits = 1;
+    p.kc = 0;
+    int nw = 4;
+    if (force < 0) {
+      nw = -force;
+    } else {
+      while (nw < ks_maxw && (long)ks_tiles * nw < 4096 && K % (2 * nw * ks_unit) == 0 && K / (2 * nw) >= 2 * ks_unit)
+        nw *= 2;
+    }
+    p.waves = nw;
+    return p;
+  }
+  p.kind = 0;
+  p.rt = rs_rt;
+  p.row_blocks = rs_blocks;
   p.uc = fmt == FMT_INT4 ? 1 : (p.nb > 2 ? 2 : 4);
-  const int unit = step * p.uc;                    // one k-step of a wave
-  const int kc_max = (960 / p.nb) / unit * unit;   // activation chunk: LDS stays within 64 KB
-  if (splits > 0) {
-    p.splits = splits;
+  p.waves = 4;
+  const int unit = step * p.uc;
+  const int kc_max = std::max(unit, (1024 / p.nb) / unit * unit);  // activation chunk: LDS <= 64 KB
+  if (force > 0) {
+    p.splits = force;
   } else if (x_blocks > 1) {
     p.splits = 1;
   } else {
@@ -468,39 +686,76 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
   return p;
 }
 
-hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st) {
-  if (p.splits < 1 || a.K % p.splits || (x_blocks > 1 && p.splits > 1)) return hipErrorInvalidValue;
-  const int kr = a.K / p.splits;
-  const int unit = (fmt == FMT_INT4 ? 128 : 32) * p.uc;
-  if (kr % p.kc || p.kc % unit) return hipErrorInvalidValue;
-  if (p.splits > 1 && (!a.part || !a.counters)) return hipErrorInvalidValue;
-  a.kc = p.kc;
+template <int RT, int EPI, int FMT, int UC>
+static hipError_t launch_rs(const SkinnyArgs& a, const SkinnyPlan& p, int x_blocks, hipStream_t st) {
   const dim3 grid(p.row_blocks, p.splits, x_blocks);
-  if (fmt == FMT_INT4) {
-    if (epi == EPI_SWIGLU) return launch_nb<2, EPI_SWIGLU, FMT_INT4, 1>(a, p.nb, grid, st);
+  const size_t lds = rowsplit_lds(p.nb, p.kc);
+  switch (p.nb) {
+    case 1: hipLaunchKernelGGL((rowsplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
+    case 2: hipLaunchKernelGGL((rowsplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
+    case 3:
+      hipLaunchKernelGGL((rowsplit_gemm_kernel<RT, 3, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(256), lds, st, a);
+      break;
+    default:
+      hipLaunchKernelGGL((rowsplit_gemm_kernel<RT, 4, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(256), lds, st, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <int RT, int EPI, int FMT, int UC>
+static hipError_t launch_ks(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t st) {
+  const dim3 grid(p.row_blocks, 1);
+  if (p.nb == 1)
+    hipLaunchKernelGGL((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
+                       st, a);
+  else
+    hipLaunchKernelGGL((ksplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 2),
+                       st, a);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t dispatch(const SkinnyArgs& a, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st) {
+  if (p.kind == 1) {
+    constexpr int KRT = EPI == EPI_SWIGLU ? 2 : 1;
+    if (fmt == FMT_INT4) return launch_ks<KRT, EPI, FMT_INT4, 1>(a, p, st);
+    if (p.uc == 4) return launch_ks<KRT, EPI, FMT_BF16, 4>(a, p, st);
+    if (p.uc == 2) return launch_ks<KRT, EPI, FMT_BF16, 2>(a, p, st);
+    return launch_ks<KRT, EPI, FMT_BF16, 1>(a, p, st);
+  }
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (fmt == FMT_INT4) return launch_rs<2, EPI, FMT_INT4, 1>(a, p, x_blocks, st);
+    if (p.uc == 4) return launch_rs<2, EPI, FMT_BF16, 4>(a, p, x_blocks, st);
+    return launch_rs<2, EPI, FMT_BF16, 2>(a, p, x_blocks, st);
+  } else {
     if (p.rt == 1) {
-      if (epi == EPI_RESIDUAL) return launch_nb<1, EPI_RESIDUAL, FMT_INT4, 1>(a, p.nb, grid, st);
-      return launch_nb<1, EPI_STORE, FMT_INT4, 1>(a, p.nb, grid, st);
+      if (fmt == FMT_INT4) return launch_rs<1, EPI, FMT_INT4, 1>(a, p, x_blocks, st);
+      if (p.uc == 4) return launch_rs<1, EPI, FMT_BF16, 4>(a, p, x_blocks, st);
+      return launch_rs<1, EPI, FMT_BF16, 2>(a, p, x_blocks, st);
     }
-    if (epi == EPI_RESIDUAL) return launch_nb<2, EPI_RESIDUAL, FMT_INT4, 1>(a, p.nb, grid, st);
-    return launch_nb<2, EPI_STORE, FMT_INT4, 1>(a, p.nb, grid, st);
+    if (fmt == FMT_INT4) return launch_rs<2, EPI, FMT_INT4, 1>(a, p, x_blocks, st);
+    if (p.uc == 4) return launch_rs<2, EPI, FMT_BF16, 4>(a, p, x_blocks, st);
+    return launch_rs<2, EPI, FMT_BF16, 2>(a, p, x_blocks, st);
   }
-  if (p.uc == 4) {
-    if (epi == EPI_SWIGLU) return launch_nb<2, EPI_SWIGLU, FMT_BF16, 4>(a, p.nb, grid, st);
-    if (p.rt == 1) {
-      if (epi == EPI_RESIDUAL) return launch_nb<1, EPI_RESIDUAL, FMT_BF16, 4>(a, p.nb, grid, st);
-      return launch_nb<1, EPI_STORE, FMT_BF16, 4>(a, p.nb, grid, st);
-    }
-    if (epi == EPI_RESIDUAL) return launch_nb<2, EPI_RESIDUAL, FMT_BF16, 4>(a, p.nb, grid, st);
-    return launch_nb<2, EPI_STORE, FMT_BF16, 4>(a, p.nb, grid, st);
+}
+
+hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st) {
+  const int step = fmt == FMT_INT4 ? 128 : 32;
+  if (p.kind == 1) {
+    if (x_blocks != 1 || p.nb > 2 || p.waves < 1 || p.waves > 16 || a.K % p.waves ||
+        (a.K / p.waves) % (step * p.uc) || (p.waves > 8 && (p.rt != 1 || p.nb != 1)))
+      return hipErrorInvalidValue;
+  } else {
+    if (p.splits < 1 || a.K % p.splits || (x_blocks > 1 && p.splits > 1)) return hipErrorInvalidValue;
+    const int kr = a.K / p.splits;
+    if (kr % p.kc || p.kc % (step * p.uc)) return hipErrorInvalidValue;
+    if (p.splits > 1 && (!a.part || !a.counters)) return hipErrorInvalidValue;
+    a.kc = p.kc;
   }
-  if (epi == EPI_SWIGLU) return launch_nb<2, EPI_SWIGLU, FMT_BF16, 2>(a, p.nb, grid, st);
-  if (p.rt == 1) {
-    if (epi == EPI_RESIDUAL) return launch_nb<1, EPI_RESIDUAL, FMT_BF16, 2>(a, p.nb, grid, st);
-    return launch_nb<1, EPI_STORE, FMT_BF16, 2>(a, p.nb, grid, st);
-  }
-  if (epi == EPI_RESIDUAL) return launch_nb<2, EPI_RESIDUAL, FMT_BF16, 2>(a, p.nb, grid, st);
-  return launch_nb<2, EPI_STORE, FMT_BF16, 2>(a, p.nb, grid, st);
+  if (epi == EPI_SWIGLU) return dispatch<EPI_SWIGLU>(a, fmt, x_blocks, p, st);
+  if (epi == EPI_RESIDUAL) return dispatch<EPI_RESIDUAL>(a, fmt, x_blocks, p, st);
+  return dispatch<EPI_STORE>(a, fmt, x_blocks, p, st);
 }
 
 }  // namespace cbd

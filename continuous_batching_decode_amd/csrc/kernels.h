@@ -11,16 +11,14 @@ enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2 };
 enum { FMT_BF16 = 0, FMT_INT4 = 1 };
 
 // y = W x over up to three weight matrices stacked along the output dim.
-// Activations come as two bf16 planes (hi, lo) x_plane elements apart.
+// Activations come as two bf16 planes (hi, lo) in the fragment-major layout (xfrag_off).
 struct SkinnyArgs {
-  const uint16_t* x;       // plane 0 (hi); plane 1 (lo) at x + x_plane; row stride ldx
+  const uint16_t* x;       // plane 0 (hi); plane 1 (lo) at x + x_plane
   int64_t x_plane;
-  int32_t ldx;
   int32_t K;
   int32_t rows;            // valid output rows (all column blocks together)
   int32_t N;               // output features (SWIGLU: ffn width; gate = segment 0, up = segment 1)
-  const int32_t* x_rows;   // optional: activation row feeding output row b (gather), else b
-  const void* w[3];        // per segment: bf16 [n_s, K] or int4 packed words
+  const void* w[3];        // per segment: streaming-layout bf16 or int4 words
   const void* aux[3];      // int4: (scale, bias) pairs [K/64, n_s, 2]
   int32_t seg_end[3];      // cumulative row ends of the segments
   // input normalisation: accumulators *= 1/sqrt(sum_t ss[t][row] / norm_dim + eps) (ss == null: none)
@@ -32,38 +30,45 @@ struct SkinnyArgs {
   // outputs
   float* out;              // STORE: fp32 [rows, ldo]; RESIDUAL: the fp32 residual stream (in/out)
   int32_t ldo;
-  uint16_t* out_x;         // SWIGLU: product planes; RESIDUAL: planes of next_gain * h (row stride ldo)
+  uint16_t* out_x;         // SWIGLU: product planes; RESIDUAL: planes of next_gain * h (fragment-major, K = N)
   int64_t out_plane;
   const uint16_t* next_gain;  // RESIDUAL: gain of the norm that consumes h next (null: no planes)
   float* ss_out;           // RESIDUAL: partial sums of squares of h, [N/16][ss_out_ld]
   int32_t ss_out_ld;
-  // split-K workspace: partial tiles and per-row-block arrival counters (zero between launches)
+  // split-K workspace of the row-split kernel: partial tiles and arrival counters (zero between launches)
   float* part;
   int32_t* counters;
   int32_t kc;              // activation chunk staged in LDS (set from the plan)
 };
 
-// How one launch is cut: 4 waves x rt subtiles of 16 rows per workgroup, nb column tiles,
-// K split over `splits` workgroups, activation chunks of kc inputs.
+// How one launch is cut.
+//  kind 0 (row split): 4 waves x rt subtiles of 16 rows per workgroup share activation
+//    chunks of kc inputs staged in LDS; K split over `splits` workgroups.
+//  kind 1 (k split): one tile of 16*rt rows per workgroup, its `waves` waves each stream a
+//    contiguous 1/waves of K with activations read from L2; partial sums added through LDS.
 struct SkinnyPlan {
-  int nb, rt, uc, row_blocks, splits, kc;
+  int kind, nb, rt, uc, row_blocks, splits, kc, waves;
 };
 
 bool skinny_shape_ok(int fmt, int K);
 // x_blocks > 1: activation rows come in blocks of 64 (prefill); else one block of `rows`.
-// splits: 0 = chosen from the shape.
-SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int splits);
-size_t skinny_lds_bytes(int nb, int kc);
+// force: 0 = chosen from the shape; > 0 = row split over `force` workgroups; < 0 = k split
+// over -force waves.
+SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int force);
 // workspace bytes a plan needs for its partial tiles
 inline size_t skinny_part_bytes(const SkinnyPlan& p) {
-  return p.splits > 1 ? (size_t)p.row_blocks * p.splits * 4 * p.rt * p.nb * 4 * 64 * 4 : 0;
+  return (p.kind == 0 && p.splits > 1) ? (size_t)p.row_blocks * p.splits * 4 * p.rt * p.nb * 4 * 64 * 4 : 0;
 }
 hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st);
 // row-major bf16 [N, K] -> streaming layout (fragments of 16 rows x 32 inputs, lane order, along K)
 hipError_t launch_pack_bf16(const uint16_t* src, int64_t N, int64_t K, uint16_t* dst, hipStream_t st);
 
-// split fp32 rows into hi/lo bf16 planes: hi = bf16(x), lo = bf16(x - hi)
+// split fp32 rows [rows, K] into fragment-major hi/lo bf16 planes: hi = bf16(x), lo = bf16(x - hi)
 hipError_t launch_split_planes(const float* x, int rows, int K, uint16_t* out, int64_t plane, hipStream_t st);
+// gather activation rows (fragment-major planes, K = d) and their sums of squares into compact rows
+hipError_t launch_gather_rows(const uint16_t* x, int64_t x_plane, const float* ss, int ss_ld, const int32_t* row_idx,
+                              int rows, int d, uint16_t* out, int64_t out_plane, float* ss_out, int ss_out_ld,
+                              hipStream_t st);
 
 // embedding gather: h[r] = E[tok[r]] (fp32); planes of gain * h; per-16-feature sums of squares
 // ss[t][r] (row stride ss_ld)
@@ -84,7 +89,7 @@ struct AttnArgs {
   const float2* rope_cs;     // [max_pos][head_dim/2] (cos, sin)
   int32_t rope_q;            // 1: rotate q to the row's position here (decode)
   int32_t append;            // 1: the item ending at pos+1 rotates k, writes K/V at pos (decode)
-  uint16_t* out;             // output planes (hi; lo at out + out_plane), row stride ld_out
+  uint16_t* out;             // output planes (hi; lo at out + out_plane), fragment-major with K = ld_out
   int64_t out_plane;
   int32_t ld_out;
   float* part_o;             // split partials [slot][n_heads][head_dim]

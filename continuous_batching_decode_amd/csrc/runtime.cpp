@@ -112,6 +112,7 @@ struct cbd_ctx {
   uint16_t* xo = nullptr;   // planes of the attention output [2][R, q_dim]
   uint16_t* xm = nullptr;   // planes of the SwiGLU product [2][R, max(F, d)]
   float* ss = nullptr;      // per-16-feature sums of squares of h [d/16][R]
+  float* ss_head = nullptr; // the same for the rows gathered for a prefill's lm_head [d/16][64]
   float* gemm_part = nullptr;   // split-K partial tiles
   int32_t* gemm_counters = nullptr;  // split-K arrival counters, one per row block
   int32_t* attn_counters = nullptr;  // split-attention arrival counters [64][n_kv_heads]
@@ -326,6 +327,7 @@ static cbd_status setup_device(cbd_ctx* c) {
   bytes += 2 * R * c->q_dim * 2 + 256;              // xo planes
   bytes += 2 * R * wm * 2 + 256;                    // xm planes (also the standalone-linear input)
   bytes += (size_t)(m.d_model / 16) * R * 4 + 256;  // ss
+  bytes += (size_t)(m.d_model / 16) * 64 * 4 + 256;  // ss_head
   bytes += R * c->qkv_dim * 4 + 256;                // qkv
   bytes += (size_t)kMaxParts * G * m.head_dim * 4 + 256;  // partial outputs
   bytes += (size_t)kMaxParts * G * 2 * 4 + 256;     // partial (max, sum)
@@ -339,6 +341,7 @@ static cbd_status setup_device(cbd_ctx* c) {
   c->xo = align_ptr<uint16_t>(p, 2 * R * c->q_dim);
   c->xm = align_ptr<uint16_t>(p, 2 * R * wm);
   c->ss = align_ptr<float>(p, (size_t)(m.d_model / 16) * R);
+  c->ss_head = align_ptr<float>(p, (size_t)(m.d_model / 16) * 64);
   c->gemm_part = align_ptr<float>(p, c->gemm_part_bytes / 4);
   c->gemm_counters = align_ptr<int32_t>(p, c->gemm_counter_count);
   c->attn_counters = align_ptr<int32_t>(p, (size_t)64 * m.n_kv_heads);
@@ -566,7 +569,6 @@ SkinnyArgs gemm_args(const cbd_ctx* c, const uint16_t* x, int64_t x_plane, int K
   SkinnyArgs a{};
   a.x = x;
   a.x_plane = x_plane;
-  a.ldx = K;
   a.K = K;
   a.rows = rows;
   a.N = N;
@@ -706,13 +708,26 @@ cbd_status run_layers(cbd_ctx* c, int rows, int x_blocks, const RowMeta* meta_d,
 }
 
 // Final norm (folded into the product) + lm_head for `rows` rows; row_idx_d gathers the
-// activation rows (prefill: each segment's last token).
+// activation rows (prefill: each segment's last token) into compact rows first.
 cbd_status run_head(cbd_ctx* c, const int32_t* row_idx_d, int rows, float* logits, int32_t* next_tokens,
                     hipStream_t st) {
   const cbd_model_config& m = c->cfg;
-  SkinnyArgs a = gemm_args(c, c->xa, c->xa_plane, m.d_model, rows, {c->lm_head}, {m.vocab}, m.vocab);
+  const uint16_t* x = c->xa;
+  int64_t x_plane = c->xa_plane;
+  if (row_idx_d) {
+    // the last layer's SwiGLU planes are consumed: reuse them for the gathered rows
+    HIP_TRY(launch_gather_rows(c->xa, c->xa_plane, c->ss, c->rows_pad, row_idx_d, rows, m.d_model, c->xm, c->xm_plane,
+                               c->ss_head, 64, st),
+            "head row gather");
+    x = c->xm;
+    x_plane = c->xm_plane;
+  }
+  SkinnyArgs a = gemm_args(c, x, x_plane, m.d_model, rows, {c->lm_head}, {m.vocab}, m.vocab);
   with_norm(c, a);
-  a.x_rows = row_idx_d;
+  if (row_idx_d) {
+    a.ss = c->ss_head;
+    a.ss_ld = 64;
+  }
   a.out = logits;
   a.ldo = m.vocab;
   {
@@ -871,8 +886,10 @@ extern "C" cbd_status cbd_linear(cbd_ctx* c, const cbd_matrix* w, int32_t N, int
   if (K < 1 || !skinny_shape_ok(c->fmt, K))
     return fail(CBD_E_INVAL, "cbd_linear: K=%d not supported for this weight format", K);
   if (K > std::max(c->cfg.ffn_dim, c->cfg.d_model)) return fail(CBD_E_INVAL, "cbd_linear: K above the model width");
-  if (splits < 0 || splits > 64 || (splits > 0 && (K % splits || (K / splits) % 128)))
+  if (splits > 64 || (splits > 0 && (K % splits || (K / splits) % 128)))
     return fail(CBD_E_INVAL, "cbd_linear: splits must divide K into multiples of 128 inputs");
+  if (splits < 0 && splits != -4 && splits != -8 && splits != -16)
+    return fail(CBD_E_INVAL, "cbd_linear: a k split takes 4, 8 or 16 waves");
   if (!w->data || !aligned16(w->data) || (c->fmt == FMT_INT4 && (!w->aux || !aligned16(w->aux))) ||
       !aligned16(y_dev) || !aligned16(x_dev))
     return fail(CBD_E_INVAL, "cbd_linear: pointers must be 16-byte aligned");
@@ -900,7 +917,7 @@ extern "C" cbd_status cbd_pack_int4(const uint8_t* codes, const uint16_t* scale,
         uint32_t* lane_words = packed_out + ((tr * blocks + b) * 64 + (16 * g + r)) * 4;
         for (int j = 0; j < 4; ++j) {
           uint32_t word = 0;
-          const int64_t base = b * 128 + 64 * (j / 2) + 16 * g + 8 * (j % 2);
+          const int64_t base = b * 128 + 32 * j + 8 * g;
           for (int e = 0; e < 8; ++e) {
             const uint32_t q = row[base + e];
             if (q > 15) return fail(CBD_E_INVAL, "cbd_pack_int4: code %u out of range", q);

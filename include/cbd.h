@@ -247,9 +247,12 @@ cbd_status greedy_argmax(cbd_ctx* ctx, const float* logits_dev, int32_t rows, in
  *         hi = bf16(x) and lo = bf16(x - hi));  y_dev fp32 [rows, N].
  * rows 1..64; N a multiple of 64; K a multiple of 256 (bf16 weights) or 512
  * (int4) and at most max(d_model, ffn_dim). Uses the context's weight
- * format. splits: number of workgroups the input dimension is divided over
- * (0 = the library's choice; else it must divide K into multiples of 128).
- * Exposed for kernel-level parity tests and bandwidth measurements.
+ * format. splits selects how the launch is cut (0 = the library's choice):
+ * splits > 0: 4-wave workgroups share staged activations and K is divided
+ * over `splits` workgroups (it must divide K into multiples of 128);
+ * splits = -4, -8 or -16: each workgroup owns 16 weight rows and divides K
+ * over that many waves (rows <= 32; -16 needs rows <= 16). Exposed for
+ * kernel-level parity tests and bandwidth measurements.
  */
 cbd_status cbd_linear(cbd_ctx* ctx, const cbd_matrix* w, int32_t N, int32_t K, const float* x_dev, int32_t rows,
                       float* y_dev, int32_t splits, cbd_stream stream);
@@ -273,8 +276,8 @@ cbd_status cbd_pack_bf16(const void* src_dev, int64_t N, int64_t K, void* dst_de
  * Packed layout: blocks of 16 rows x 128 inputs, 1 KB each; block (t, b)
  * is the (t * K/128 + b)-th. Inside it, the 4 words at offset 16*l belong
  * to row 16t + r with r = l%16 and g = l/16: word j (0..3) holds the 8
- * codes of inputs 128b + 64*(j/2) + 16*g + 8*(j%2) + e, e = 0..7, with
- * input e in nibble (e/2) + 4*(e%2). K % 128 == 0, N % 16 == 0.
+ * codes of inputs 128b + 32*j + 8*g + e, e = 0..7, with input e in nibble
+ * (e/2) + 4*(e%2). K % 128 == 0, N % 16 == 0.
  */
 cbd_status cbd_pack_int4(const uint8_t* codes, const uint16_t* scale, const uint16_t* bias, int64_t N,
                          int64_t K, uint32_t* packed_out, uint16_t* aux_out);

@@ -157,7 +157,7 @@ def unpack_int4_reference(packed, aux, n, k):
                 nib = (e // 2) + 4 * (e % 2)
                 vals = ((w >> np.uint64(4 * nib)) & np.uint64(15)).astype(np.uint8)
                 rows = np.arange(n // 16) * 16 + r
-                cols = np.arange(k // 128) * 128 + 64 * (j // 2) + 16 * g + 8 * (j % 2) + e
+                cols = np.arange(k // 128) * 128 + 32 * j + 8 * g + e
                 codes[np.ix_(rows, cols)] = vals
     scale = aux[:, :, 0].T.copy()
     bias = aux[:, :, 1].T.copy()
