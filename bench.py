@@ -74,6 +74,9 @@ def main():
     ap.add_argument("--shape", default="llama3-8b-shape")
     ap.add_argument("--ctx-lo", type=int, default=512)
     ap.add_argument("--ctx-hi", type=int, default=4096)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only copy a device buffer of this many MiB 5 times (a plain copy of known size, "
+                         "used to calibrate HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (each GPU would run its own "
@@ -83,6 +86,18 @@ def main():
     import torch
     import continuous_batching_decode_amd as cbd
     import synth
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)  # device-to-device copy: n bytes read, n bytes written
+        for _ in range(5):
+            torch.bitwise_not(src, out=dst)  # the same traffic through an elementwise kernel
+        torch.cuda.synchronize()
+        log("copy probe: 2 x 5 passes over %d MiB" % args.copy_probe_mib)
+        return
 
     shape = synth.SHAPES[args.shape]
     B = args.batch

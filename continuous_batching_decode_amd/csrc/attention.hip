@@ -4,34 +4,405 @@
 // "decode_step_batch - paint-by-numbers": each query row rotates q and k at
 // its own position t_s (delta 1), writes its new K/V into its own slab at
 // t_s (delta 2), and attends only to [0..=t_s] of that slab (delta 3). The
-// same kernel serves the segmented prefill (section "REVISED"), where a token
-// at segment-local position p attends to [0..=p] of its segment's slab, so
-// no query ever reads another sequence's keys (block-diagonal causal).
+// segmented prefill (section "REVISED") attends a token at segment-local
+// position p to [0..=p] of its own segment's slab, so no query ever reads
+// another sequence's keys (block-diagonal causal).
 //
-// One workgroup (4 waves) = one work item (query row, key range) x one KV
-// head; the G = Hq/Hkv query heads sharing that KV head are processed
-// together so every K/V tile is read once for all of them (GQA reuse). Keys
-// stream through LDS in tiles of 64 with the next tile already in flight in
-// registers; softmax is the running (max, sum) form in fp32. Long histories
-// are split over several items (flash-decoding style); the last item of a
-// (row, KV head) to finish merges the splits with the log-sum-exp rule.
+// Decode (decode_attention_kernel): one wave = one work item (query row, key
+// range) x one KV head, for the G = Hq/Hkv query heads sharing that KV head
+// (GQA: every K/V byte is read once for all of them). Keys stream straight
+// from HBM in blocks of 32 in the slab's MFMA fragment layout, the next block
+// in flight while the current one is used:
+//   S^T[32 keys x 16 cols] = K[32 x Dh] . Q^T[Dh x 16]   (cols = heads, G used)
+//   O^T[Dh x 16]          += V^T[Dh x 32] . P^T[32 x 16]
+// q and p enter the products as bf16 hi + lo pairs (about 16 significant
+// bits, as the activations of the weight-streaming products do); the running
+// (max, sum) softmax is fp32 and per column, so rescaling never leaves the
+// lane. The new token's key and value are rotated and rounded in registers,
+// taken as the first key, and stored to the slab. Long histories are split
+// over several items (flash-decoding); the last wave of a (row, KV head) to
+// finish merges the splits with the log-sum-exp rule in a fixed order.
+//
+// Prefill (prefill_attention_kernel): one workgroup per (query row, KV head),
+// key tiles of 64 staged through LDS; the row's K/V were appended beforehand.
 #include "common.h"
 #include "kernels.h"
 
 namespace cbd {
 
 namespace {
-constexpr int TILE = 64;
 
 CBD_DEVICE void store_split(uint16_t* hi, uint16_t* lo, float v) {
   const uint32_t h = f32_to_bf16(v);
   *hi = (uint16_t)h;
   *lo = (uint16_t)f32_to_bf16(v - bf16_to_f32(h));
 }
+
+// 8 fp32 values -> bf16 hi and lo operands (v ~ hi + lo)
+CBD_DEVICE void split8(const float (&v)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  u32x4_t h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
+    h[i] = h0 | (h1 << 16);
+    l[i] = f32_to_bf16(v[2 * i] - bf16_to_f32(h0)) | (f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1)) << 16);
+  }
+  hi = as_frag(h);
+  lo = as_frag(l);
+}
+
+// 4 fp32 -> 4 bf16 hi values and 4 lo values, as two 8-byte words
+CBD_DEVICE void split4(const float (&v)[4], uint2& hi, uint2& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = f32_to_bf16(v[e]);
+    l[e] = f32_to_bf16(v[e] - bf16_to_f32(h[e]));
+  }
+  hi = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  lo = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+}
+
+CBD_DEVICE float exp_or_zero(float x, float m) { return x == -INFINITY ? 0.f : __expf(x - m); }
+
 }  // namespace
 
+// ============================================================================ decode
+
 template <int DH, int G>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, int n_waves) {
+  constexpr int NU = DH / 32;  // dim chunks of 32 (K fragments per 16 keys)
+  constexpr int NT = DH / 16;  // dim tiles of 16 (V fragments per 32 keys)
+  constexpr int BLK = 32 * DH;
+  constexpr int PAIR = DH / 64;  // RoPE partner of chunk u is u ^ PAIR (dims d and d + Dh/2)
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (w >= n_waves) return;
+  const int j = w % a.n_kv_heads;
+  AttnItem it = a.items[w / a.n_kv_heads];
+  // the item is the same for the whole wave: keep it in scalar registers (uniform branches)
+  it.slab_off = ((int64_t)__builtin_amdgcn_readfirstlane((int32_t)(it.slab_off >> 32)) << 32) |
+                (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)it.slab_off);
+  it.stride = __builtin_amdgcn_readfirstlane(it.stride);
+  it.pos = __builtin_amdgcn_readfirstlane(it.pos);
+  it.row = __builtin_amdgcn_readfirstlane(it.row);
+  it.k_begin = __builtin_amdgcn_readfirstlane(it.k_begin);
+  it.k_end = __builtin_amdgcn_readfirstlane(it.k_end);
+  it.part = __builtin_amdgcn_readfirstlane(it.part);
+  const int pos = it.pos;
+  const int64_t region = (int64_t)it.stride * DH;
+  uint16_t* slab = reinterpret_cast<uint16_t*>(a.arena + it.slab_off);
+  uint16_t* kbase = slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * region;
+  uint16_t* vbase = slab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * region;
+  const bool appends = it.k_end == pos + 1;
+  const int kend = appends ? pos : it.k_end;  // keys read from the slab: [k_begin, kend)
+  const int b_first = it.k_begin >> 5, b_end = (kend + 31) >> 5;
+  const float scale = 1.0f / sqrtf((float)DH);
+
+  auto load_k = [&](u32x4_t (&K)[2 * NU], int b) {
+    const uint16_t* kb = kbase + (int64_t)b * BLK + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < 2 * NU; ++i) K[i] = load_stream(kb + 512 * i);
+  };
+  auto load_v = [&](u32x4_t (&V)[NT], int b) {
+    const uint16_t* vb = vbase + (int64_t)b * BLK + 8 * lane;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) V[t] = load_stream(vb + 512 * t);
+  };
+  // The first block's keys are requested before anything else, so their latency overlaps the
+  // set-up below (its values follow the set-up: they are needed only after the first scores).
+  // Loads of K/V blocks are never conditional: a branch around them would make the compiler's
+  // load-completion waits conservative (wait for everything). Block b_first is inside the slab
+  // even when the item reads no slab key (b_first = pos / 32 < stride / 32).
+  u32x4_t K0[2 * NU], V0[NT];
+  load_k(K0, b_first);
+
+  const float2* cs = a.rope_cs + (int64_t)pos * (DH / 2);
+  const float* qkv_row = a.qkv + (int64_t)it.row * a.ld_qkv;
+  // lane's dims in the score product: d(u, e) = 32u + 8g + e; rotate pairs (u, u ^ PAIR) in place
+  auto rotate = [&](float (&x)[NU][8]) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (u & PAIR) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 c = cs[32 * u + 8 * g + e];
+        const float x1 = x[u][e], x2 = x[u ^ PAIR][e];
+        x[u][e] = x1 * c.x - x2 * c.y;
+        x[u ^ PAIR][e] = x2 * c.x + x1 * c.y;
+      }
+    }
+  };
+  auto load8 = [&](const float* p, float (&x)[8]) {
+    const float4 x0 = *reinterpret_cast<const float4*>(p);
+    const float4 x1 = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+    x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+  };
+
+  // Q^T operand: column c16 = query head j*G + c16 (zero beyond G)
+  bf16x8_t qh[NU], ql[NU];
+  {
+    float qv[NU][8];
+    const float* q = qkv_row + (int64_t)(j * G + (c16 < G ? c16 : 0)) * DH;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) load8(q + 32 * u + 8 * g, qv[u]);
+    rotate(qv);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (c16 >= G)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[u][e] = 0.f;
+      split8(qv[u], qh[u], ql[u]);
+    }
+  }
+
+  f32x4_t o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // per column (head); equal in the column's 4 lanes
+
+  if (appends) {
+    // The new token goes first (the softmax sum does not depend on the order): k rotated to pos and
+    // rounded to bf16 on the lane's score dims, v rounded on its output dims; then stored at pos.
+    const float* kx = qkv_row + (int64_t)a.n_heads * DH + (int64_t)j * DH;
+    const float* vx = kx + (int64_t)a.n_kv_heads * DH;
+    float kv[NU][8];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) load8(kx + 32 * u + 8 * g, kv[u]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {  // v lands in the accumulator: O starts as 1 x v
+      const float4 x = *reinterpret_cast<const float4*>(vx + 16 * t + 4 * g);
+      o[t] = f32x4_t{x.x, x.y, x.z, x.w};
+    }
+    rotate(kv);
+    float dot = 0.f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const u32x4_t qhu = __builtin_bit_cast(u32x4_t, qh[u]), qlu = __builtin_bit_cast(u32x4_t, ql[u]);
+      uint32_t kb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t b0 = f32_to_bf16(kv[u][2 * i]), b1 = f32_to_bf16(kv[u][2 * i + 1]);
+        kb[i] = b0 | (b1 << 16);
+        const float q0 = bf16_to_f32(qhu[i] & 0xFFFFu) + bf16_to_f32(qlu[i] & 0xFFFFu);
+        const float q1 = bf16_to_f32(qhu[i] >> 16) + bf16_to_f32(qlu[i] >> 16);
+        dot += q0 * bf16_to_f32(b0) + q1 * bf16_to_f32(b1);
+      }
+      if (c16 == 0)  // lanes 0, 16, 32, 48 hold every dim once
+        *reinterpret_cast<uint4*>(kbase + kslab_off(pos, 32 * u + 8 * g, DH)) = uint4{kb[0], kb[1], kb[2], kb[3]};
+    }
+    dot += __shfl_xor(dot, 16, 64);
+    dot += __shfl_xor(dot, 32, 64);
+    m_run = dot * scale;  // p = exp(s - m) = 1
+    l_run = 1.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t vb = f32_to_bf16(o[t][e]);
+        o[t][e] = bf16_to_f32(vb);
+        if (c16 == 0) vbase[vslab_off(pos, 16 * t + 4 * g + e, DH)] = (uint16_t)vb;
+      }
+  }
+
+  // S^T of a block: lane holds keys 32b + 4g + e (s0) and 32b + 16 + 4g + e (s1) of its column
+  auto scores = [&](const u32x4_t (&K)[2 * NU], f32x4_t& s0, f32x4_t& s1) {
+    s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      s0 = mfma(as_frag(K[u]), qh[u], s0);
+      s0 = mfma(as_frag(K[u]), ql[u], s0);
+      s1 = mfma(as_frag(K[NU + u]), qh[u], s1);
+      s1 = mfma(as_frag(K[NU + u]), ql[u], s1);
+    }
+  };
+  // online softmax over the block, then O^T += V^T P^T
+  auto accumulate = [&](const u32x4_t (&V)[NT], const f32x4_t& s0, const f32x4_t& s1, int b) {
+    float sv[8];
+    const int k0 = 32 * b + 4 * g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = k0 + e < kend ? s0[e] * scale : -INFINITY;
+      sv[4 + e] = k0 + 16 + e < kend ? s1[e] * scale : -INFINITY;
+    }
+    float bm = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) bm = fmaxf(bm, sv[i]);
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float m_new = fmaxf(m_run, bm);
+    const float alpha = exp_or_zero(m_run, m_new);
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = exp_or_zero(sv[i], m_new);
+      ps += p[i];
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    // P^T operand: element i of lane group g is key kk = 8g + i of the block's V order
+    bf16x8_t ph, pl;
+    split8(p, ph, pl);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      o[t] = o[t] * alpha;
+      o[t] = mfma(as_frag(V[t]), ph, o[t]);
+      o[t] = mfma(as_frag(V[t]), pl, o[t]);
+    }
+  };
+
+  load_v(V0, b_first);
+  // one block in registers, staggered: the next K loads during the softmax and P.V of this block,
+  // the next V during the next block's scores; the last block is peeled off the loop
+  for (int b = b_first; b + 1 < b_end; ++b) {  // scheduling barriers keep the loads in this order
+    f32x4_t s0, s1;
+    scores(K0, s0, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(K0, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate(V0, s0, s1, b);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(V0, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (b_first < b_end) {
+    f32x4_t s0, s1;
+    scores(K0, s0, s1);
+    accumulate(V0, s0, s1, b_end - 1);
+  }
+
+  if (it.part < 0) {
+    // output: lane (c16 < G) holds dims 16t + 4g + e of head j*G + c16
+    if (c16 < G) {
+      const float inv = 1.0f / l_run;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float y[4] = {o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv};
+        uint2 hi, lo;
+        split4(y, hi, lo);
+        const int64_t off = xfrag_off(it.row, (j * G + c16) * DH + 16 * t + 4 * g, a.ld_out);
+        *reinterpret_cast<uint2*>(a.out + off) = hi;
+        *reinterpret_cast<uint2*>(a.out + a.out_plane + off) = lo;
+      }
+    }
+    return;
+  }
+  // split item: publish the unnormalised partial and (max, sum); the last wave of the (row, KV head)
+  // merges. Partials and the arrival counter use agent-scope accesses (coherent across the XCDs'
+  // L2 caches), partials 16 bytes at a time; the wave's stores are acknowledged (vmcnt 0) before its
+  // arrival is counted.
+  if (c16 < G) {
+    const int64_t slot = (int64_t)it.part * a.n_heads + j * G + c16;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) store_agent_x4(a.part_o, (int)((slot * DH + 16 * t + 4 * g) * 4), o[t]);
+    if (g == 0) store_agent_x2(a.part_ml, (int)(slot * 2 * 4), float2{m_run, l_run});
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  const int2 rp = a.row_parts[it.row];
+  int32_t* counter = a.counters + (int64_t)it.row * a.n_kv_heads + j;
+  int last = 0;
+  if (lane == 0) last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == rp.y - 1;
+  last = __shfl(last, 0, 64);
+  if (!last) return;
+
+  // Merge with the whole wave (at most 64 splits). Lane s loads split s's (max, sum) for every head
+  // in one round; the per-head maximum and weighted sum come from wave reductions. Lane l then
+  // combines output elements NE*l .. NE*l + NE - 1 of the G x Dh block over the splits in order,
+  // the loads of 8 splits in flight at a time.
+  constexpr int NE = G * DH / 64;  // 8, 4 or 2 floats per lane
+  const int ns = rp.y;
+  // lane s: (max, sum) of split s for the G heads, 2G consecutive floats
+  float mv[G], wv[G], Mh[G], Lh[G];
+  {
+    const int off = (int)((((int64_t)(rp.x + min(lane, ns - 1)) * a.n_heads + j * G) * 2) * 4);
+    float ml[2 * G];
+    if constexpr (G == 1) {
+      const float2 x = load_agent_x2(a.part_ml, off);
+      ml[0] = x.x;
+      ml[1] = x.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < G / 2; ++q) {
+        const f32x4_t x = load_agent_x4(a.part_ml, off + 16 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ml[4 * q + e] = x[e];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mv[h] = lane < ns ? ml[2 * h] : -INFINITY;  // lanes past the last split take no part
+      wv[h] = lane < ns ? ml[2 * h + 1] : 0.f;
+    }
+  }
+  const int e0 = lane * NE, hh = e0 / DH, d0 = e0 % DH;
+  const int64_t split_stride = (int64_t)a.n_heads * DH;
+  const int64_t o_base = (int64_t)rp.x * a.n_heads + j * G + hh;  // slot row of split 0, in DH units
+  constexpr int SB = 8;
+  float ov[SB][NE];
+  auto load_batch = [&](int s0) {  // splits past the last reload it (their weight is 0)
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int off = (int)(((o_base * DH + d0) + (int64_t)min(s0 + u, ns - 1) * split_stride) * 4);
+      if constexpr (NE == 2) {
+        const float2 x = load_agent_x2(a.part_o, off);
+        ov[u][0] = x.x;
+        ov[u][1] = x.y;
+      } else {
+#pragma unroll
+        for (int q = 0; q < NE / 4; ++q) {
+          const f32x4_t x = load_agent_x4(a.part_o, off + 16 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[u][4 * q + e] = x[e];
+        }
+      }
+    }
+  };
+  load_batch(0);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    Mh[h] = wave_max(mv[h]);
+    Lh[h] = wave_sum(exp_or_zero(mv[h], Mh[h]) * wv[h]);
+    wv[h] = exp_or_zero(mv[h], Mh[h]);  // lane s: weight of split s for head h
+  }
+  float acc[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += SB) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      float wgt = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float x = __shfl(wv[h], s0 + u, 64);
+        if (hh == h) wgt = x;
+      }
+#pragma unroll
+      for (int i = 0; i < NE; ++i) acc[i] += wgt * ov[u][i];
+    }
+    if (s0 + SB < ns) load_batch(s0 + SB);
+  }
+  float L = Lh[0];
+#pragma unroll
+  for (int h = 1; h < G; ++h)
+    if (hh == h) L = Lh[h];
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int64_t off = xfrag_off(it.row, (j * G + hh) * DH + d0 + i, a.ld_out);
+    store_split(a.out + off, a.out + a.out_plane + off, acc[i] * inv);
+  }
+  if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ============================================================================ prefill
+
+template <int DH, int G>
+__global__ __launch_bounds__(256) void prefill_attention_kernel(AttnArgs a) {
+  constexpr int TILE = 64;
   constexpr int KROW = DH + 8;           // padded LDS row (elements) against bank conflicts
   constexpr int CH = DH / 8;             // 16-byte chunks per key row
   constexpr int LOADS = TILE * CH / 256;  // 16-byte chunks per thread per tile (K and V each)
@@ -39,62 +410,29 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   constexpr int DPAIRS = DH / 2;         // threads per key group in the PV phase
   constexpr int KGROUPS = 256 / DPAIRS;   // key groups in the PV phase
   constexpr int KPER = TILE / KGROUPS;    // keys per thread per tile in the PV phase
+  constexpr int VCH = 4 * DH;            // 16-byte V chunks per block of 32 keys
   static_assert(LOADS >= 1, "tile too small");
   __shared__ float qs[G][DH];
   __shared__ __attribute__((aligned(16))) uint16_t Ks[TILE][KROW];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[TILE][KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t knew[DH], vnew[DH];
   __shared__ float S[G][TILE];
   __shared__ float alpha_s[G];
   __shared__ float red[KGROUPS][G][DH];
   __shared__ float ml_s[G][2];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const AttnItem it = a.items[blockIdx.x];
   const int j = blockIdx.y;
-  const RowMeta m = a.meta[it.row];
-  const int pos = m.pos;
   const float scale = 1.0f / sqrtf((float)DH);
-  const int half = DH / 2;
-  const float2* cs = a.rope_cs + (int64_t)pos * half;
 
-  // queries of this KV group, rotated to pos when the projection left them unrotated
+  // queries of this KV group (already rotated)
   const float* q = a.qkv + (int64_t)it.row * a.ld_qkv + (int64_t)j * G * DH;
-  for (int i = tid; i < G * DH; i += 256) {
-    const int h = i / DH, d = i % DH;
-    float v = q[i];
-    if (a.rope_q) {
-      const int p = d < half ? d : d - half;
-      const float2 c = cs[p];
-      const float o = d < half ? q[i + half] : q[i - half];
-      v = d < half ? v * c.x - o * c.y : v * c.x + o * c.y;
-    }
-    qs[h][d] = v;
-  }
+  for (int i = tid; i < G * DH; i += 256) qs[i / DH][i % DH] = q[i];
 
-  const int64_t head_stride = (int64_t)m.cap * DH;
-  uint16_t* slab = reinterpret_cast<uint16_t*>(a.arena + m.slab_off);
-  uint16_t* kbase = slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * head_stride;
-  uint16_t* vbase = slab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * head_stride;
-
-  // the item that ends at pos + 1 appends the new token's K/V (rotated, bf16) to the slab
-  const bool appends = a.append && it.k_end == pos + 1;
-  if (appends) {
-    const float* kx = a.qkv + (int64_t)it.row * a.ld_qkv + (int64_t)a.n_heads * DH + (int64_t)j * DH;
-    const float* vx = kx + (int64_t)a.n_kv_heads * DH;
-    for (int d = tid; d < DH; d += 256) {
-      const int p = d < half ? d : d - half;
-      const float2 c = cs[p];
-      const float o = d < half ? kx[d + half] : kx[d - half];
-      const float kr = d < half ? kx[d] * c.x - o * c.y : kx[d] * c.x + o * c.y;
-      const uint16_t kb = (uint16_t)f32_to_bf16(kr), vb = (uint16_t)f32_to_bf16(vx[d]);
-      knew[d] = kb;
-      vnew[d] = vb;
-      kbase[(int64_t)pos * DH + d] = kb;
-      vbase[(int64_t)pos * DH + d] = vb;
-    }
-  }
+  const int64_t region = (int64_t)it.stride * DH;
+  const uint16_t* slab = reinterpret_cast<const uint16_t*>(a.arena + it.slab_off);
+  const uint16_t* kbase = slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * region;
+  const uint16_t* vbase = slab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * region;
 
   float m_run = -INFINITY, l_run = 0.f;  // held by wave h for head h (h < G)
   float o[G][2];
@@ -102,35 +440,37 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = 0.f;
   const int dp = tid % DPAIRS, kg = tid / DPAIRS;
 
-  // tile prefetch: keys at pos come from LDS when this item appended them
-  const int key_lim = appends ? pos : it.k_end;  // keys read from the slab: [k_begin, key_lim)
+  // K chunk c: key c / CH, dims 8 (c % CH) .. +7. V chunk c: block c / VCH, fragment t, lane ln:
+  // dim 16 t + ln%16 of keys kk = 8 (ln/16) .. +7 in the block's V order.
   uint4 kreg[LOADS], vreg[LOADS];
   auto fetch = [&](int kb) {
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
       const int c = tid + 256 * l;
-      const int r = c / CH, col = (c % CH) * 8;
-      const int key = kb + r;
-      kreg[l] = vreg[l] = uint4{0u, 0u, 0u, 0u};
-      if (key < key_lim) {
-        kreg[l] = *reinterpret_cast<const uint4*>(kbase + (int64_t)key * DH + col);
-        vreg[l] = *reinterpret_cast<const uint4*>(vbase + (int64_t)key * DH + col);
-      }
+      const int key = kb + c / CH;
+      kreg[l] = key < it.k_end ? *reinterpret_cast<const uint4*>(kbase + kslab_off(key, (c % CH) * 8, DH))
+                               : uint4{0u, 0u, 0u, 0u};
+      const int blk = (kb >> 5) + c / VCH;
+      vreg[l] = 32 * blk < it.k_end ? *reinterpret_cast<const uint4*>(vbase + (int64_t)blk * 32 * DH + 8 * (c % VCH))
+                                    : uint4{0u, 0u, 0u, 0u};
     }
   };
   fetch(it.k_begin);
   for (int kb = it.k_begin; kb < it.k_end; kb += TILE) {
-    __syncthreads();  // previous tile consumed (and the prologue's LDS writes done)
+    __syncthreads();  // previous tile consumed (and the query staging done)
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
       const int c = tid + 256 * l;
-      const int r = c / CH, col = (c % CH) * 8;
-      if (appends && kb + r == pos) {
-        kreg[l] = *reinterpret_cast<const uint4*>(knew + col);
-        vreg[l] = *reinterpret_cast<const uint4*>(vnew + col);
+      *reinterpret_cast<uint4*>(&Ks[c / CH][(c % CH) * 8]) = kreg[l];
+      const int bl = c / VCH, rem = c % VCH, t = rem >> 6, ln = rem & 63;
+      const int d = 16 * t + (ln & 15), gg = ln >> 4;
+      const uint32_t vw[4] = {vreg[l].x, vreg[l].y, vreg[l].z, vreg[l].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = 32 * bl + 16 * (i >> 2) + 4 * gg + (i & 3);  // tile-local key of kk = 8 gg + i
+        const uint16_t v = (uint16_t)(vw[i >> 1] >> (16 * (i & 1)));
+        Vs[key][d] = kb + key < it.k_end ? v : (uint16_t)0;
       }
-      *reinterpret_cast<uint4*>(&Ks[r][col]) = kreg[l];
-      *reinterpret_cast<uint4*>(&Vs[r][col]) = vreg[l];
     }
     __syncthreads();
     if (kb + TILE < it.k_end) fetch(kb + TILE);  // next tile in flight during this one
@@ -165,8 +505,8 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
     if (wave < G) {
       const float s = S[wave][lane];
       const float m_new = fmaxf(m_run, wave_max(s));
-      const float p = (s == -INFINITY) ? 0.f : __expf(s - m_new);
-      const float alpha = __expf(m_run - m_new);
+      const float p = exp_or_zero(s, m_new);
+      const float alpha = exp_or_zero(m_run, m_new);
       l_run = l_run * alpha + wave_sum(p);
       m_run = m_new;
       S[wave][lane] = p;
@@ -204,72 +544,52 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
     ml_s[wave][1] = l_run;
   }
   __syncthreads();
-  if (it.part < 0) {
-    for (int i = tid; i < G * DH; i += 256) {
-      const int h = i / DH, d = i % DH;
-      float acc = 0.f;
-#pragma unroll
-      for (int g2 = 0; g2 < KGROUPS; ++g2) acc += red[g2][h][d];
-      const int64_t off = xfrag_off(it.row, (j * G + h) * DH + d, a.ld_out);
-      store_split(a.out + off, a.out + a.out_plane + off, acc / ml_s[h][1]);
-    }
-    return;
-  }
-  // split item: publish the unnormalised partial; the last split of (row, KV head) merges.
-  // Partials and the arrival counter use agent-scope atomic accesses (coherent across
-  // the XCDs' L2 caches); stores are acknowledged (vmcnt 0) before arrival is counted.
   for (int i = tid; i < G * DH; i += 256) {
     const int h = i / DH, d = i % DH;
     float acc = 0.f;
 #pragma unroll
     for (int g2 = 0; g2 < KGROUPS; ++g2) acc += red[g2][h][d];
-    const int64_t slot = (int64_t)it.part * a.n_heads + j * G + h;
-    __hip_atomic_store(a.part_o + slot * DH + d, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d < 2) __hip_atomic_store(a.part_ml + slot * 2 + d, ml_s[h][d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-  const int2 rp = a.row_parts[it.row];
-  int32_t* counter = a.counters + (int64_t)it.row * a.n_kv_heads + j;
-  if (tid == 0) s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == rp.y - 1;
-  __syncthreads();
-  if (!s_last) return;
-  for (int i = tid; i < G * DH; i += 256) {
-    const int h = i / DH, d = i % DH;
-    float M = -INFINITY;
-    for (int s = 0; s < rp.y; ++s) {
-      const int64_t slot = (int64_t)(rp.x + s) * a.n_heads + j * G + h;
-      M = fmaxf(M, __hip_atomic_load(a.part_ml + slot * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    }
-    float acc = 0.f, l = 0.f;
-    for (int s = 0; s < rp.y; ++s) {
-      const int64_t slot = (int64_t)(rp.x + s) * a.n_heads + j * G + h;
-      const float w = __expf(__hip_atomic_load(a.part_ml + slot * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
-      acc += w * __hip_atomic_load(a.part_o + slot * DH + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      l += w * __hip_atomic_load(a.part_ml + slot * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
     const int64_t off = xfrag_off(it.row, (j * G + h) * DH + d, a.ld_out);
-    store_split(a.out + off, a.out + a.out_plane + off, acc / l);
+    store_split(a.out + off, a.out + a.out_plane + off, acc / ml_s[h][1]);
   }
-  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int DH>
-static hipError_t launch_attn_dh(int G, dim3 grid, hipStream_t st, const AttnArgs& a) {
+static hipError_t launch_decode_dh(int G, dim3 grid, int n_waves, hipStream_t st, const AttnArgs& a) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((attention_kernel<DH, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((attention_kernel<DH, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((attention_kernel<DH, 4>), grid, dim3(256), 0, st, a); break;
+    case 1: launch_kernel((decode_attention_kernel<DH, 1>), grid, dim3(256), 0, st, a, n_waves); break;
+    case 2: launch_kernel((decode_attention_kernel<DH, 2>), grid, dim3(256), 0, st, a, n_waves); break;
+    case 4: launch_kernel((decode_attention_kernel<DH, 4>), grid, dim3(256), 0, st, a, n_waves); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st) {
+template <int DH>
+static hipError_t launch_prefill_dh(int G, dim3 grid, hipStream_t st, const AttnArgs& a) {
+  switch (G) {
+    case 1: launch_kernel((prefill_attention_kernel<DH, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: launch_kernel((prefill_attention_kernel<DH, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: launch_kernel((prefill_attention_kernel<DH, 4>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st) {
+  const int G = a.n_heads / a.n_kv_heads;
+  const int n_waves = n_items * a.n_kv_heads;
+  const dim3 grid((n_waves + 3) / 4);
+  if (head_dim == 128) return launch_decode_dh<128>(G, grid, n_waves, st, a);
+  if (head_dim == 64) return launch_decode_dh<64>(G, grid, n_waves, st, a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st) {
   const int G = a.n_heads / a.n_kv_heads;
   const dim3 grid(n_items, a.n_kv_heads);
-  if (head_dim == 128) return launch_attn_dh<128>(G, grid, st, a);
-  if (head_dim == 64) return launch_attn_dh<64>(G, grid, st, a);
+  if (head_dim == 128) return launch_prefill_dh<128>(G, grid, st, a);
+  if (head_dim == 64) return launch_prefill_dh<64>(G, grid, st, a);
   return hipErrorInvalidValue;
 }
 

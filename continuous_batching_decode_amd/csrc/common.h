@@ -21,6 +21,44 @@ CBD_DEVICE uint32_t f32_to_bf16(float f) {
 
 CBD_DEVICE uint32_t pack_bf16x2(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
 
+CBD_DEVICE bf16x8_t as_frag(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// Data read once per launch (weights, K/V histories): non-temporal loads keep it from evicting
+// what is reused from the caches (activations, partial tiles).
+CBD_DEVICE u32x4_t load_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+// D += A B on a 16 x 16 x 32 bf16 tile (fp32 accumulate). Lane l supplies A row l%16 and B column
+// l%16, each at k = 8*(l/16) .. 8*(l/16)+7; it receives D rows 4*(l/16) .. +3 of column l%16.
+CBD_DEVICE f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Agent-scope (device-coherent) loads of 16 or 8 bytes at base + byte_off, base uniform over the
+// wave: the sc1 policy makes them miss in caches that another XCD's writes do not reach, as
+// __hip_atomic_load at agent scope does for 4 bytes (one request instead of four).
+CBD_DEVICE f32x4_t load_agent_x4(const float* base, int byte_off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, 0x00020000);
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16));
+}
+CBD_DEVICE float2 load_agent_x2(const float* base, int byte_off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, 0x00020000);
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 16));
+}
+
+// Agent-scope 16- and 8-byte stores (sc1: written through to where every XCD's agent-scope loads
+// read), as __hip_atomic_store at agent scope does for 4 bytes.
+CBD_DEVICE void store_agent_x4(float* base, int byte_off, f32x4_t v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, byte_off, 0, 16);
+}
+CBD_DEVICE void store_agent_x2(float* base, int byte_off, float2 v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, 0x00020000);
+  typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, byte_off, 0, 16);
+}
+
 CBD_DEVICE float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -42,15 +80,41 @@ CBD_DEVICE int64_t xfrag_off(int row, int k, int K) {
   return ((int64_t)(row >> 4) * (K >> 5) + (k >> 5)) * 512 + ((((k & 31) >> 3) << 4) + (row & 15)) * 8 + (k & 7);
 }
 
+// Slab layout. A sequence's slab holds, for each layer l and KV head j, a K region and a V region
+// of stride * Dh bf16 elements at ((2 l + {0: K, 1: V}) * Hkv + j) * stride * Dh, where stride is
+// the slab's granule-rounded capacity (a multiple of 256 tokens). Inside a region keys come in
+// blocks of 32 (32 * Dh contiguous elements), each made of 1 KB MFMA operand fragments:
+//  K: fragment (key half h = (key%32)/16, dim chunk u = d/32) at index h * (Dh/32) + u; in it lane
+//     16 * ((d%32)/8) + key%16 holds dims d - d%8 .. +7. A fragment is the operand of a 16 x 16 x 32
+//     product with keys as its 16 rows and dims as its k.
+//  V: fragment t = d/16; in it lane 16 * (kk/8) + d%16 holds 8 consecutive kk, where
+//     kk = 8 * ((key%16)/4) + 4 * ((key%32)/16) + key%4 reorders the block's keys. A fragment is the
+//     operand with dims as rows and keys as k; the reordering matches the rows in which the score
+//     tiles of keys 0..15 and 16..31 come out of the product, so probabilities feed P.V in place.
+CBD_DEVICE int64_t kslab_off(int key, int d, int dh) {
+  return (int64_t)(key >> 5) * 32 * dh + ((((key >> 4) & 1) * (dh >> 5) + (d >> 5)) << 9) +
+         (((((d & 31) >> 3) << 4) + (key & 15)) << 3) + (d & 7);
+}
+CBD_DEVICE int vslab_kk(int key) { return (((key & 15) >> 2) << 3) + (((key >> 4) & 1) << 2) + (key & 3); }
+CBD_DEVICE int64_t vslab_off(int key, int d, int dh) {
+  const int kk = vslab_kk(key);
+  return (int64_t)(key >> 5) * 32 * dh + ((d >> 4) << 9) + ((((kk >> 3) << 4) + (d & 15)) << 3) + (kk & 7);
+}
+
 // Per-query-row metadata shared by the RoPE/append and attention kernels.
 struct RowMeta {
   int64_t slab_off;  // byte offset of the row's slab in the arena
-  int32_t cap;       // slab capacity (tokens)
+  int32_t stride;    // tokens per K or V region of the slab (granule-rounded capacity)
   int32_t pos;       // position of this query token (t_s for decode, p for prefill)
 };
 
-// One attention work item: query row `row` over keys [k_begin, k_end) of its slab.
+// One attention work item: query row `row` (at position pos of the slab at slab_off) over keys
+// [k_begin, k_end) of that slab. The slab fields repeat the row's metadata so a kernel needs one
+// load to start.
 struct AttnItem {
+  int64_t slab_off;
+  int32_t stride;
+  int32_t pos;
   int32_t row;
   int32_t k_begin;
   int32_t k_end;

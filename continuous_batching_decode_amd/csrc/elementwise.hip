@@ -91,21 +91,21 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float* qkv, int ld_qkv
   }
   // keys: rotate, round to bf16, write to the slab at pos; values: round and write
   uint16_t* slab = reinterpret_cast<uint16_t*>(arena + m.slab_off);
-  const int64_t head_stride = (int64_t)m.cap * head_dim;
-  uint16_t* kbase = slab + (int64_t)(layer * 2 + 0) * n_kv_heads * head_stride + (int64_t)m.pos * head_dim;
-  uint16_t* vbase = slab + (int64_t)(layer * 2 + 1) * n_kv_heads * head_stride + (int64_t)m.pos * head_dim;
+  const int64_t region = (int64_t)m.stride * head_dim;
+  uint16_t* kbase = slab + (int64_t)(layer * 2 + 0) * n_kv_heads * region;
+  uint16_t* vbase = slab + (int64_t)(layer * 2 + 1) * n_kv_heads * region;
   for (int idx = threadIdx.x; idx < n_kv_heads * half; idx += 256) {
     const int j = idx / half, i = idx - j * half;
     const float* x = k + j * head_dim;
     const float2 c = cs[i];
     const float x1 = x[i], x2 = x[i + half];
-    uint16_t* dst = kbase + j * head_stride;
-    dst[i] = (uint16_t)f32_to_bf16(x1 * c.x - x2 * c.y);
-    dst[i + half] = (uint16_t)f32_to_bf16(x2 * c.x + x1 * c.y);
+    uint16_t* dst = kbase + j * region;
+    dst[kslab_off(m.pos, i, head_dim)] = (uint16_t)f32_to_bf16(x1 * c.x - x2 * c.y);
+    dst[kslab_off(m.pos, i + half, head_dim)] = (uint16_t)f32_to_bf16(x2 * c.x + x1 * c.y);
   }
   for (int idx = threadIdx.x; idx < n_kv_heads * head_dim; idx += 256) {
     const int j = idx / head_dim, i = idx - j * head_dim;
-    vbase[j * head_stride + i] = (uint16_t)f32_to_bf16(v[idx]);
+    vbase[j * region + vslab_off(m.pos, i, head_dim)] = (uint16_t)f32_to_bf16(v[idx]);
   }
 }
 
@@ -142,24 +142,32 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int vo
 }
 
 // canonical [L, n, Hkv, Dh] <-> slab [L][2][Hkv][cap][Dh] at positions [pos, pos+n); 16-byte moves
-__global__ __launch_bounds__(256) void slab_copy_kernel(uint8_t* arena, int64_t slab_off, int cap, int pos, int n,
-                                                        int n_kv_heads, int head_dim, const uint16_t* k_in,
+__global__ __launch_bounds__(256) void slab_copy_kernel(uint8_t* arena, int64_t slab_off, int stride, int pos,
+                                                        int n, int n_kv_heads, int head_dim, const uint16_t* k_in,
                                                         const uint16_t* v_in, uint16_t* k_out, uint16_t* v_out) {
   const int t = blockIdx.x, l = blockIdx.y, kv = blockIdx.z;
   const int chunks = n_kv_heads * head_dim / 8;
   uint16_t* slab = reinterpret_cast<uint16_t*>(arena + slab_off);
-  const int64_t head_stride = (int64_t)cap * head_dim;
+  const int64_t region = (int64_t)stride * head_dim;
   const int64_t canon = ((int64_t)l * n + t) * n_kv_heads * head_dim;
+  const int key = pos + t;
   for (int c = threadIdx.x; c < chunks; c += 256) {
     const int j = (c * 8) / head_dim, i = (c * 8) - j * head_dim;
-    uint16_t* s = slab + (int64_t)(l * 2 + kv) * n_kv_heads * head_stride + j * head_stride +
-                  (int64_t)(pos + t) * head_dim + i;
-    if (k_in) {
-      const uint16_t* src = (kv ? v_in : k_in) + canon + c * 8;
-      *reinterpret_cast<uint4*>(s) = *reinterpret_cast<const uint4*>(src);
-    } else {
-      uint16_t* dst = (kv ? v_out : k_out) + canon + c * 8;
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(s);
+    uint16_t* base = slab + ((int64_t)(l * 2 + kv) * n_kv_heads + j) * region;
+    if (kv == 0) {  // 8 consecutive dims of a key are contiguous in a K fragment
+      uint16_t* s = base + kslab_off(key, i, head_dim);
+      if (k_in)
+        *reinterpret_cast<uint4*>(s) = *reinterpret_cast<const uint4*>(k_in + canon + c * 8);
+      else
+        *reinterpret_cast<uint4*>(k_out + canon + c * 8) = *reinterpret_cast<const uint4*>(s);
+    } else {  // ... but 16 bytes apart in a V fragment
+      for (int e = 0; e < 8; ++e) {
+        uint16_t* s = base + vslab_off(key, i + e, head_dim);
+        if (v_in)
+          *s = v_in[canon + c * 8 + e];
+        else
+          v_out[canon + c * 8 + e] = *s;
+      }
     }
   }
 }
@@ -167,40 +175,40 @@ __global__ __launch_bounds__(256) void slab_copy_kernel(uint8_t* arena, int64_t 
 hipError_t launch_embed(const int32_t* tokens, int rows, const uint16_t* embed, int vocab, int d,
                         const uint16_t* gain, float* h, uint16_t* xplanes, int64_t plane, float* ss, int ss_ld,
                         hipStream_t st) {
-  hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(256), 0, st, tokens, embed, vocab, d, gain, h, xplanes, plane, ss,
+  launch_kernel(embed_kernel, dim3(rows), dim3(256), 0, st, tokens, embed, vocab, d, gain, h, xplanes, plane, ss,
                      ss_ld);
   return hipGetLastError();
 }
 
 hipError_t launch_split_planes(const float* x, int rows, int K, uint16_t* out, int64_t plane, hipStream_t st) {
-  hipLaunchKernelGGL(split_planes_kernel, dim3(rows), dim3(256), 0, st, x, K, out, plane);
+  launch_kernel(split_planes_kernel, dim3(rows), dim3(256), 0, st, x, K, out, plane);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_rows(const uint16_t* x, int64_t x_plane, const float* ss, int ss_ld, const int32_t* row_idx,
                               int rows, int d, uint16_t* out, int64_t out_plane, float* ss_out, int ss_out_ld,
                               hipStream_t st) {
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(rows), dim3(256), 0, st, x, x_plane, ss, ss_ld, row_idx, d, out,
+  launch_kernel(gather_rows_kernel, dim3(rows), dim3(256), 0, st, x, x_plane, ss, ss_ld, row_idx, d, out,
                      out_plane, ss_out, ss_out_ld);
   return hipGetLastError();
 }
 
 hipError_t launch_rope_append(float* qkv, int ld_qkv, const RowMeta* meta, int rows, int n_heads, int n_kv_heads,
                               int head_dim, int layer, uint8_t* arena, const float* rope_cs, hipStream_t st) {
-  hipLaunchKernelGGL(rope_append_kernel, dim3(rows), dim3(256), 0, st, qkv, ld_qkv, meta, n_heads, n_kv_heads,
+  launch_kernel(rope_append_kernel, dim3(rows), dim3(256), 0, st, qkv, ld_qkv, meta, n_heads, n_kv_heads,
                      head_dim, layer, arena, reinterpret_cast<const float2*>(rope_cs));
   return hipGetLastError();
 }
 
 hipError_t launch_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(256), 0, st, logits, vocab, out);
+  launch_kernel(argmax_kernel, dim3(rows), dim3(256), 0, st, logits, vocab, out);
   return hipGetLastError();
 }
 
-hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int cap, int pos, int n, int n_layers, int n_kv_heads,
-                            int head_dim, const uint16_t* k_in, const uint16_t* v_in, uint16_t* k_out,
+hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_layers,
+                            int n_kv_heads, int head_dim, const uint16_t* k_in, const uint16_t* v_in, uint16_t* k_out,
                             uint16_t* v_out, hipStream_t st) {
-  hipLaunchKernelGGL(slab_copy_kernel, dim3(n, n_layers, 2), dim3(256), 0, st, arena, slab_off, cap, pos, n,
+  launch_kernel(slab_copy_kernel, dim3(n, n_layers, 2), dim3(256), 0, st, arena, slab_off, stride, pos, n,
                      n_kv_heads, head_dim, k_in, v_in, k_out, v_out);
   return hipGetLastError();
 }

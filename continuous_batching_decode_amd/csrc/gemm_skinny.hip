@@ -50,14 +50,6 @@ namespace cbd {
 
 namespace {
 
-CBD_DEVICE bf16x8_t as_frag(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
-
-// weights are read once per launch: non-temporal loads keep them from
-// evicting the activations, partial tiles and K/V held in the caches
-CBD_DEVICE u32x4_t load_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
-
 CBD_DEVICE bf16x8_t load_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
 // 8 int4 codes of one packed word -> bf16 (128 + q) in input order.
@@ -68,10 +60,6 @@ CBD_DEVICE bf16x8_t widen_codes(uint32_t w) {
   r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
   r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
   return as_frag(r);
-}
-
-CBD_DEVICE f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 CBD_DEVICE float silu_f(float g) { return g / (1.0f + __expf(-g)); }
@@ -304,7 +292,8 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
   int nq = 1;
   while (2 * nq * 16 * ROWS <= (int)blockDim.x && ss_per % (2 * nq) == 0) nq *= 2;
   const int ss_cnt = ss_per / nq;
-  const bool ss_early = FMT == FMT_BF16 && a.ss && ss_cnt <= SSMAX;
+  // (every one of the 16 x ROWS items needs a thread of its own)
+  const bool ss_early = FMT == FMT_BF16 && a.ss && ss_cnt <= SSMAX && (int)blockDim.x >= 16 * ROWS;
   const int ss_item = threadIdx.x % (16 * ROWS), ss_q = threadIdx.x / (16 * ROWS);
   const bool ss_mine = ss_early && ss_q < nq && (ss_item % ROWS) < rows_valid;
   float ssv[SSMAX];
@@ -349,16 +338,14 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
 #pragma unroll
         for (int i = 0; i < RT; ++i)
           f.A[u][i] = load_stream(reinterpret_cast<const uint16_t*>(wr[i]) + (int64_t)(st * UC + u) * 512);
+      // padding rows of a fragment share its cache lines with the valid rows and feed only padding
+      // outputs: they are loaded like the rest (no branch, so load completion counts stay static)
 #pragma unroll
       for (int u = 0; u < UC; ++u)
 #pragma unroll
         for (int c = 0; c < NB; ++c) {
-          if (16 * c + (lane & 15) < rows_valid) {  // padding rows feed padding outputs only
-            f.X[u][c][0] = load_frag(xr[c] + (st * UC + u) * 512);
-            f.X[u][c][1] = load_frag(xr[c] + a.x_plane + (st * UC + u) * 512);
-          } else {
-            f.X[u][c][0] = f.X[u][c][1] = bf16x8_t{};
-          }
+          f.X[u][c][0] = load_frag(xr[c] + (st * UC + u) * 512);
+          f.X[u][c][1] = load_frag(xr[c] + a.x_plane + (st * UC + u) * 512);
         }
     };
     auto compute = [&](const Buf& f) {
@@ -372,18 +359,38 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
             acc[i][c] = mfma(as_frag(f.A[u][i]), f.X[u][c][1], acc[i][c]);
           }
     };
+    // Every load in the prologue and the steady-state loop is unconditional, so the compiler's
+    // load-completion waits stay exact (wait for one buffer while the other is in flight); the
+    // last 2 or 3 stages are peeled. The plan guarantees total >= 2.
+    // Scheduling barriers keep each buffer's loads together and in program order, so waiting for
+    // one buffer never waits for the other's.
     const int total = kw / (32 * UC);
     Buf b0, b1;
     load(b0, 0);
-    if (total > 1) load(b1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b1, 1);
+    __builtin_amdgcn_sched_barrier(0);
     ss_store();  // waits for the sums only: they were requested before the weights
-    for (int st = 0; st < total; st += 2) {
+    int st = 0;
+    for (; st + 3 < total; st += 2) {
       compute(b0);
-      if (st + 2 < total) load(b0, st + 2);
-      if (st + 1 < total) {
-        compute(b1);
-        if (st + 3 < total) load(b1, st + 3);
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      load(b0, st + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(b1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(b1, st + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    compute(b0);
+    if (st + 2 < total) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(b0, st + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(b1);
+      compute(b0);
+    } else {
+      compute(b1);
     }
   } else {
     const int total = kw / 128;
@@ -398,12 +405,8 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int c = 0; c < NB; ++c) {
-          if (16 * c + (lane & 15) < rows_valid) {
-            X[j][c][0] = load_frag(xr[c] + (4 * st + j) * 512);
-            X[j][c][1] = load_frag(xr[c] + a.x_plane + (4 * st + j) * 512);
-          } else {
-            X[j][c][0] = X[j][c][1] = bf16x8_t{};
-          }
+          X[j][c][0] = load_frag(xr[c] + (4 * st + j) * 512);
+          X[j][c][1] = load_frag(xr[c] + a.x_plane + (4 * st + j) * 512);
         }
       int4_block<RT, NB>(acc, Wq, SB, X);
     }
@@ -549,16 +552,14 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
   // L2 caches); each wave waits for its stores to be acknowledged (vmcnt 0) before arrival is counted,
   // which avoids the full L2 write-back and invalidate of a device-wide fence.
   if (S > 1) {
-    float* base = a.part + (int64_t)blk * S * 4 * NACC * 64;
-    float* mine = base + ((int64_t)split * 4 + wave) * NACC * 64;
+    // partial tile of (split, wave): [i][c][lane] f32x4, 16 bytes per lane and subtile
+    const int64_t base = (int64_t)blk * S * 4 * NACC * 64;
+    const int64_t mine = base + ((int64_t)split * 4 + wave) * NACC * 64;
 #pragma unroll
     for (int i = 0; i < RT; ++i)
 #pragma unroll
       for (int c = 0; c < NB; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __hip_atomic_store(mine + ((i * NB + c) * 4 + e) * 64 + lane, acc[i][c][e], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        store_agent_x4(a.part, (int)((mine + ((i * NB + c) * 64 + lane) * 4) * 4), acc[i][c]);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
     __syncthreads();
     if (threadIdx.x == 0)
@@ -570,15 +571,12 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
       for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < S; ++s) {
-      const float* src = base + ((int64_t)s * 4 + wave) * NACC * 64;
+      const int64_t src = base + ((int64_t)s * 4 + wave) * NACC * 64;
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int c = 0; c < NB; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[i][c][e] += __hip_atomic_load(src + ((i * NB + c) * 4 + e) * 64 + lane, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+          acc[i][c] += load_agent_x4(a.part, (int)((src + ((i * NB + c) * 64 + lane) * 4) * 4));
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -611,7 +609,7 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t* src, int
 hipError_t launch_pack_bf16(const uint16_t* src, int64_t N, int64_t K, uint16_t* dst, hipStream_t st) {
   const int64_t chunks = N * K / 8;
   const int blocks = (int)std::min<int64_t>((chunks + 255) / 256, 65536);
-  hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, st, src, N, K, dst);
+  launch_kernel(pack_bf16_kernel, dim3(blocks), dim3(256), 0, st, src, N, K, dst);
   return hipGetLastError();
 }
 
@@ -650,13 +648,16 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
     p.row_blocks = ks_tiles;
     p.splits = 1;
     p.kc = 0;
+    // each wave needs >= 2 stages of its K slice (the loop keeps two in flight)
     int nw = 4;
     if (force < 0) {
       nw = -force;
     } else {
+      while (nw > 1 && K / nw < 2 * ks_unit) nw /= 2;
       while (nw < ks_maxw && (long)ks_tiles * nw < 4096 && K % (2 * nw * ks_unit) == 0 && K / (2 * nw) >= 2 * ks_unit)
         nw *= 2;
     }
+    while (fmt == FMT_BF16 && p.uc > 1 && K / nw < 2 * step * p.uc) p.uc /= 2;
     p.waves = nw;
     return p;
   }
@@ -691,13 +692,13 @@ static hipError_t launch_rs(const SkinnyArgs& a, const SkinnyPlan& p, int x_bloc
   const dim3 grid(p.row_blocks, p.splits, x_blocks);
   const size_t lds = rowsplit_lds(p.nb, p.kc);
   switch (p.nb) {
-    case 1: hipLaunchKernelGGL((rowsplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
-    case 2: hipLaunchKernelGGL((rowsplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
+    case 1: launch_kernel((rowsplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
+    case 2: launch_kernel((rowsplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
     case 3:
-      hipLaunchKernelGGL((rowsplit_gemm_kernel<RT, 3, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(256), lds, st, a);
+      launch_kernel((rowsplit_gemm_kernel<RT, 3, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(256), lds, st, a);
       break;
     default:
-      hipLaunchKernelGGL((rowsplit_gemm_kernel<RT, 4, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(256), lds, st, a);
+      launch_kernel((rowsplit_gemm_kernel<RT, 4, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(256), lds, st, a);
       break;
   }
   return hipGetLastError();
@@ -707,10 +708,10 @@ template <int RT, int EPI, int FMT, int UC>
 static hipError_t launch_ks(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t st) {
   const dim3 grid(p.row_blocks, 1);
   if (p.nb == 1)
-    hipLaunchKernelGGL((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
+    launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
                        st, a);
   else
-    hipLaunchKernelGGL((ksplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 2),
+    launch_kernel((ksplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 2),
                        st, a);
   return hipGetLastError();
 }
@@ -744,7 +745,8 @@ hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, cons
   const int step = fmt == FMT_INT4 ? 128 : 32;
   if (p.kind == 1) {
     if (x_blocks != 1 || p.nb > 2 || p.waves < 1 || p.waves > 16 || a.K % p.waves ||
-        (a.K / p.waves) % (step * p.uc) || (p.waves > 8 && (p.rt != 1 || p.nb != 1)))
+        (a.K / p.waves) % (step * p.uc) || (p.waves > 8 && (p.rt != 1 || p.nb != 1)) ||
+        (fmt == FMT_BF16 && a.K / p.waves < 2 * step * p.uc))
       return hipErrorInvalidValue;
   } else {
     if (p.splits < 1 || a.K % p.splits || (x_blocks > 1 && p.splits > 1)) return hipErrorInvalidValue;

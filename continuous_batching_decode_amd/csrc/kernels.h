@@ -1,11 +1,31 @@
 // Internal launch interface between the host runtime and the gfx950 kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "common.h"
 
 namespace cbd {
+
+// Profiling hook. When start is set, the next kernel launched from this thread goes through
+// hipExtLaunchKernelGGL, which stamps start/stop at that kernel's own begin and end (no dispatch
+// or event-packet overhead inside the interval), and the hook is cleared.
+struct LaunchEvents {
+  hipEvent_t start, stop;
+};
+LaunchEvents& launch_events();
+
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args... args) {
+  LaunchEvents& ev = launch_events();
+  if (ev.start) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev.start, ev.stop, 0, args...);
+    ev = LaunchEvents{nullptr, nullptr};
+  } else {
+    kernel<<<grid, block, lds, st>>>(args...);
+  }
+}
 
 enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2 };
 enum { FMT_BF16 = 0, FMT_INT4 = 1 };
@@ -87,8 +107,6 @@ struct AttnArgs {
   int32_t n_heads, n_kv_heads, layer;
   uint8_t* arena;
   const float2* rope_cs;     // [max_pos][head_dim/2] (cos, sin)
-  int32_t rope_q;            // 1: rotate q to the row's position here (decode)
-  int32_t append;            // 1: the item ending at pos+1 rotates k, writes K/V at pos (decode)
   uint16_t* out;             // output planes (hi; lo at out + out_plane), fragment-major with K = ld_out
   int64_t out_plane;
   int32_t ld_out;
@@ -97,12 +115,16 @@ struct AttnArgs {
   const int2* row_parts;     // per row: (first slot, number of splits; 0 = not split)
   int32_t* counters;         // per (row, KV head) arrival counters, zero between launches
 };
-hipError_t launch_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
+// decode: q unrotated; the item ending at pos + 1 rotates the new k, appends K/V at pos and uses it;
+// items cover key ranges that start at multiples of 32 (one wave per item and KV head)
+hipError_t launch_decode_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
+// prefill: q rotated and every token's K/V appended beforehand (one workgroup per item and KV head)
+hipError_t launch_prefill_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
 
 // greedy argmax per row, lowest id on ties
 hipError_t launch_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st);
 // scatter canonical K/V [L, n, Hkv, Dh] into a slab at [pos, pos+n), or gather back
-hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int cap, int pos, int n, int n_layers, int n_kv_heads,
+hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_layers, int n_kv_heads,
                             int head_dim, const uint16_t* k_in, const uint16_t* v_in, uint16_t* k_out,
                             uint16_t* v_out, hipStream_t st);
 

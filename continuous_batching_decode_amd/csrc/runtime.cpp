@@ -68,7 +68,8 @@ struct LayerW {
 
 struct Slab {
   int64_t off = 0;
-  int32_t cap = 0;
+  int32_t cap = 0;     // tokens the slab may hold (granule-rounded, clipped to the RoPE table)
+  int32_t stride = 0;  // tokens per K or V region in the slab layout (granule-rounded)
   int32_t len = 0;
   int64_t gran_begin = 0, gran_count = 0;
   bool live = false;
@@ -198,13 +199,27 @@ bool valid_model(const cbd_model_config* m, std::string* why) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Build the (row, key range) work items of one decode step: long histories
-// are split so that the grid covers the chip; each split gets a partial slot.
+// Build the (row, key range) work items of one decode step. The attention kernel runs one wave per
+// item and KV head and streams keys in blocks of 32, so ranges start at multiples of 32. Ranges are
+// sized so that about kDecodeWaves waves cover the step's keys (two per SIMD of the chip), at least
+// kMinChunk keys each; every split of a row gets a partial slot.
+#ifndef CBD_DECODE_WAVES
+#define CBD_DECODE_WAVES 2048
+#endif
+#ifndef CBD_DECODE_MIN_CHUNK
+#define CBD_DECODE_MIN_CHUNK 256
+#endif
+constexpr int64_t kDecodeWaves = CBD_DECODE_WAVES;
+constexpr int64_t kMinChunk = CBD_DECODE_MIN_CHUNK;
+constexpr int64_t kMaxSplits = 64;
 int plan_decode_items(const cbd_ctx* c, const std::vector<RowMeta>& rows, AttnItem* items, int32_t* row_parts) {
   int64_t total = 0;
   for (const RowMeta& r : rows) total += r.pos + 1;
-  const int target_items = std::max<int>((int)rows.size(), 512 / c->cfg.n_kv_heads);
-  int64_t chunk = std::max<int64_t>(256, round_up((total + target_items - 1) / target_items, 64));
+  const int64_t per_wave = (total * c->cfg.n_kv_heads + kDecodeWaves - 1) / kDecodeWaves;
+  int64_t longest = 0;
+  for (const RowMeta& r : rows) longest = std::max<int64_t>(longest, r.pos + 1);
+  // at most kMaxSplits splits per row: the merge reads one (max, sum) pair per lane
+  int64_t chunk = std::max({kMinChunk, round_up(per_wave, 32), round_up((longest + kMaxSplits - 1) / kMaxSplits, 32)});
   for (;;) {
     int64_t slots = 0;
     for (const RowMeta& r : rows) {
@@ -219,7 +234,7 @@ int plan_decode_items(const cbd_ctx* c, const std::vector<RowMeta>& rows, AttnIt
     const int nk = rows[i].pos + 1;
     const int splits = (int)((nk + chunk - 1) / chunk);
     if (splits <= 1) {
-      items[n++] = AttnItem{(int32_t)i, 0, nk, -1};
+      items[n++] = AttnItem{rows[i].slab_off, rows[i].stride, rows[i].pos, (int32_t)i, 0, nk, -1};
       row_parts[2 * i] = 0;
       row_parts[2 * i + 1] = 0;
     } else {
@@ -227,26 +242,48 @@ int plan_decode_items(const cbd_ctx* c, const std::vector<RowMeta>& rows, AttnIt
       row_parts[2 * i + 1] = splits;
       for (int s = 0; s < splits; ++s) {
         const int b = (int)(s * chunk), e = (int)std::min<int64_t>(nk, (s + 1) * chunk);
-        items[n++] = AttnItem{(int32_t)i, b, e, slot++};
+        items[n++] = AttnItem{rows[i].slab_off, rows[i].stride, rows[i].pos, (int32_t)i, b, e, slot++};
       }
     }
   }
   return n;
 }
 
-// Bracket one launch with events when its kind is being profiled.
+}  // namespace
+
+namespace cbd {
+LaunchEvents& launch_events() {
+  static thread_local LaunchEvents ev{nullptr, nullptr};
+  return ev;
+}
+}  // namespace cbd
+
+namespace {
+
+// Time the first kernel launched inside the scope when its kind is being profiled: the launch
+// helper stamps the pair of events at that kernel's own start and end.
 struct ProfScope {
   cbd_ctx* c;
   hipStream_t st;
   bool on;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
   ProfScope(cbd_ctx* c_, int kind, double bytes, double flops, hipStream_t st_) : c(c_), st(st_), on(false) {
     if (!(c->prof_mask & (1u << kind)) || (int)c->prof_rec.size() >= c->prof_max) return;
     const size_t i = c->prof_rec.size();
     c->prof_rec.push_back({kind, bytes, flops});
-    on = hipEventRecord(c->prof_ev[2 * i], st) == hipSuccess;
+    e0 = c->prof_ev[2 * i];
+    e1 = c->prof_ev[2 * i + 1];
+    cbd::launch_events() = cbd::LaunchEvents{e0, e1};
+    on = true;
   }
   ~ProfScope() {
-    if (on) (void)hipEventRecord(c->prof_ev[2 * (c->prof_rec.size() - 1) + 1], st);
+    if (!on) return;
+    cbd::LaunchEvents& ev = cbd::launch_events();
+    if (ev.start == e0) {  // nothing was launched (or the launch was refused): record an empty interval
+      ev = cbd::LaunchEvents{nullptr, nullptr};
+      (void)hipEventRecord(e0, st);
+      (void)hipEventRecord(e1, st);
+    }
   }
 };
 
@@ -412,8 +449,11 @@ extern "C" cbd_status cbd_create(const cbd_model_config* cfg, const cbd_weights*
   if (!c->host_only) {
     if (!kv_arena_dev || (reinterpret_cast<uintptr_t>(kv_arena_dev) & 255)) {
       s = fail(CBD_E_INVAL, "kv arena must be a 256-byte aligned device pointer");
-    } else if ((s = setup_weights(c, weights)) == CBD_OK) {
-      s = setup_device(c);
+    } else if ((s = setup_weights(c, weights)) == CBD_OK && (s = setup_device(c)) == CBD_OK) {
+      // masked keys get probability 0, and 0 x (finite V) = 0: the arena starts cleared so that the
+      // slab positions beyond a sequence's length never hold non-finite bit patterns
+      if (hipMemset(kv_arena_dev, 0, arena_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        s = fail(CBD_E_HIP, "kv arena clear failed");
     }
   }
   if (s != CBD_OK) {
@@ -469,6 +509,7 @@ extern "C" cbd_status kvslab_alloc(cbd_ctx* c, int32_t capacity_tokens, int32_t*
   s.live = true;
   s.len = 0;
   s.cap = (int32_t)std::min<int64_t>(need * kGranuleTokens, c->cfg.max_position);
+  s.stride = (int32_t)(need * kGranuleTokens);
   s.gran_begin = first;
   s.gran_count = need;
   s.off = first * c->granule_bytes;
@@ -533,7 +574,7 @@ extern "C" cbd_status kvslab_append(cbd_ctx* c, int32_t seq_id, int32_t n_tokens
   if (!k_dev || !v_dev || !aligned16(k_dev) || !aligned16(v_dev))
     return fail(CBD_E_INVAL, "kvslab_append: K/V must be 16-byte aligned device pointers");
   if (c->host_only) return fail(CBD_E_NODEVICE, "kvslab_append: host-only context");
-  HIP_TRY(launch_slab_copy(c->arena, s->off, s->cap, s->len, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
+  HIP_TRY(launch_slab_copy(c->arena, s->off, s->stride, s->len, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
                            c->cfg.head_dim, static_cast<const uint16_t*>(k_dev), static_cast<const uint16_t*>(v_dev),
                            nullptr, nullptr, static_cast<hipStream_t>(stream)),
           "kvslab_append launch");
@@ -553,7 +594,7 @@ extern "C" cbd_status kvslab_read(const cbd_ctx* c, int32_t seq_id, int32_t star
   if (!k_out_dev || !v_out_dev || !aligned16(k_out_dev) || !aligned16(v_out_dev))
     return fail(CBD_E_INVAL, "kvslab_read: outputs must be 16-byte aligned device pointers");
   if (c->host_only) return fail(CBD_E_NODEVICE, "kvslab_read: host-only context");
-  HIP_TRY(launch_slab_copy(c->arena, s->off, s->cap, start, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
+  HIP_TRY(launch_slab_copy(c->arena, s->off, s->stride, start, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
                            c->cfg.head_dim, nullptr, nullptr, static_cast<uint16_t*>(k_out_dev),
                            static_cast<uint16_t*>(v_out_dev), static_cast<hipStream_t>(stream)),
           "kvslab_read launch");
@@ -665,8 +706,6 @@ cbd_status run_layers(cbd_ctx* c, int rows, int x_blocks, const RowMeta* meta_d,
       at.layer = l;
       at.arena = c->arena;
       at.rope_cs = reinterpret_cast<const float2*>(c->rope_cs);
-      at.rope_q = fused ? 1 : 0;
-      at.append = fused ? 1 : 0;
       at.out = c->xo;
       at.out_plane = c->xo_plane;
       at.ld_out = c->q_dim;
@@ -677,7 +716,9 @@ cbd_status run_layers(cbd_ctx* c, int rows, int x_blocks, const RowMeta* meta_d,
       const double kvb = kv_keys * c->kv_dim * 2.0 * 2.0;
       ProfScope p(c, CBD_KERNEL_ATTENTION, kvb + (double)rows * c->q_dim * (4.0 + 4.0) + n_parts * 0.0,
                   kv_keys * m.n_heads * m.head_dim * 4.0, st);
-      HIP_TRY(launch_attention(at, n_items, m.head_dim, st), "attention");
+      HIP_TRY(fused ? launch_decode_attention(at, n_items, m.head_dim, st)
+                    : launch_prefill_attention(at, n_items, m.head_dim, st),
+              "attention");
     }
     a = gemm_args(c, c->xo, c->xo_plane, c->q_dim, rows, {L.wo}, {m.d_model}, m.d_model);
     with_residual(c, a, L.ffn_norm);
@@ -763,7 +804,7 @@ extern "C" cbd_status decode_step_batch(cbd_ctx* c, const int32_t* seq_ids, int3
       return fail(CBD_E_CAPACITY, "decode_step_batch: sequence %d is full (%d tokens)", seq_ids[i], s->cap);
     if (s->len + 1 > c->cfg.max_position)
       return fail(CBD_E_CAPACITY, "decode_step_batch: sequence %d reached max_position", seq_ids[i]);
-    rows[i] = RowMeta{s->off, s->cap, s->len};
+    rows[i] = RowMeta{s->off, s->stride, s->len};
   }
   if (c->host_only) return fail(CBD_E_NODEVICE, "decode_step_batch: host-only context");
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -839,8 +880,8 @@ extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, cons
   for (int i = 0; i < K; ++i) {
     const Slab& s = c->slabs[seq_ids[i]];
     for (int p = 0; p < seg_lens[i]; ++p, ++g) {
-      rows[g] = RowMeta{s.off, s.cap, p};
-      items[g] = AttnItem{g, 0, p + 1, -1};
+      rows[g] = RowMeta{s.off, s.stride, p};
+      items[g] = AttnItem{s.off, s.stride, p, g, 0, p + 1, -1};
     }
     last_idx[i] = g - 1;
   }

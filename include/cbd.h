@@ -149,7 +149,10 @@ int32_t cbd_slab_granule_tokens(void);
  * Create a context. Weights are referenced, not copied: they must stay
  * valid until cbd_destroy. kv_arena_dev (arena_bytes long, 256-byte
  * aligned) is caller-owned device memory that the library carves into
- * per-sequence slabs. Allocates the device workspace (sized by limits) and
+ * per-sequence slabs; it is cleared here and must not be written by the
+ * caller while the context lives (slab contents are read and written only
+ * through kvslab_append / kvslab_read and the step calls; their internal
+ * layout is private). Allocates the device workspace (sized by limits) and
  * the RoPE table (built on the host in double precision, stored as fp32).
  * Returns CBD_E_INVAL on inconsistent shapes, CBD_E_HIP if the workspace
  * cannot be allocated. With limits->host_only the weight and arena pointers
