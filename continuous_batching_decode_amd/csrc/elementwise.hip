@@ -109,36 +109,69 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float* qkv, int ld_qkv
   }
 }
 
-// Greedy argmax of one row per block: strict > keeps the first maximum a
-// thread sees; across threads equal values resolve to the lower index.
-__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int vocab, int32_t* out) {
-  __shared__ float sv[256];
-  __shared__ int si[256];
-  const int r = blockIdx.x;
-  const float* row = logits + (int64_t)r * vocab;
-  float best = -INFINITY;
-  int bi = 0x7FFFFFFF;
-  for (int v = threadIdx.x * 4; v < vocab; v += 256 * 4) {
-    const float4 x = *reinterpret_cast<const float4*>(row + v);
-    if (x.x > best || (bi == 0x7FFFFFFF && x.x == best)) { best = x.x; bi = v; }
-    if (x.y > best) { best = x.y; bi = v + 1; }
-    if (x.z > best) { best = x.z; bi = v + 2; }
-    if (x.w > best) { best = x.w; bi = v + 3; }
-  }
-  sv[threadIdx.x] = best;
+// Greedy argmax, lowest index on ties. Row r is cut into P segments, one block each: strict >
+// keeps the first maximum a thread sees, and across threads and blocks equal values resolve to
+// the lower index. Each block publishes (max, index) with agent-scope stores; the last block of the
+// row (arrival counter) reduces the P pairs in the same way and resets the counter.
+namespace {
+CBD_DEVICE void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+CBD_DEVICE void block_best(float& bv, int& bi, float* sv, int* si) {
+  sv[threadIdx.x] = bv;
   si[threadIdx.x] = bi;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
     if (threadIdx.x < s) {
-      const float ov = sv[threadIdx.x + s];
-      const int oi = si[threadIdx.x + s];
-      const float mv = sv[threadIdx.x];
-      const int mi = si[threadIdx.x];
-      if (ov > mv || (ov == mv && oi < mi)) { sv[threadIdx.x] = ov; si[threadIdx.x] = oi; }
+      float mv = sv[threadIdx.x];
+      int mi = si[threadIdx.x];
+      better(mv, mi, sv[threadIdx.x + s], si[threadIdx.x + s]);
+      sv[threadIdx.x] = mv;
+      si[threadIdx.x] = mi;
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[r] = si[0] == 0x7FFFFFFF ? 0 : si[0];
+  bv = sv[0];
+  bi = si[0];
+}
+}  // namespace
+
+__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int vocab, int seg, float* part,
+                                                     int32_t* counters, int32_t* out) {
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  __shared__ int s_last;
+  const int r = blockIdx.y, P = gridDim.x, b = blockIdx.x;
+  const float* row = logits + (int64_t)r * vocab;
+  const int v0 = b * seg, v1 = min(vocab, v0 + seg);
+  float best = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int v = v0 + threadIdx.x * 4; v < v1; v += 256 * 4) {
+    const float4 x = *reinterpret_cast<const float4*>(row + v);
+    better(best, bi, x.x, v);
+    better(best, bi, x.y, v + 1);
+    better(best, bi, x.z, v + 2);
+    better(best, bi, x.w, v + 3);
+  }
+  block_best(best, bi, sv, si);
+  if (threadIdx.x == 0) {
+    store_agent_x2(part, (int)(((int64_t)r * P + b) * 8), float2{best, __int_as_float(bi)});
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the pair is stored before arrival counts
+    s_last = __hip_atomic_fetch_add(counters + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  best = -INFINITY;
+  bi = 0x7FFFFFFF;
+  for (int q = threadIdx.x; q < P; q += 256) {
+    const float2 x = load_agent_x2(part, (int)(((int64_t)r * P + q) * 8));
+    better(best, bi, x.x, __float_as_int(x.y));
+  }
+  block_best(best, bi, sv, si);
+  if (threadIdx.x == 0) {
+    out[r] = bi == 0x7FFFFFFF ? 0 : bi;  // every logit NaN: token 0
+    __hip_atomic_store(counters + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // canonical [L, n, Hkv, Dh] <-> slab [L][2][Hkv][cap][Dh] at positions [pos, pos+n); 16-byte moves
@@ -200,8 +233,14 @@ hipError_t launch_rope_append(float* qkv, int ld_qkv, const RowMeta* meta, int r
   return hipGetLastError();
 }
 
-hipError_t launch_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st) {
-  launch_kernel(argmax_kernel, dim3(rows), dim3(256), 0, st, logits, vocab, out);
+hipError_t launch_argmax(const float* logits, int rows, int vocab, float* part, int32_t* counters, int32_t* out,
+                         hipStream_t st) {
+  // segments of a multiple of 4 logits, 4096 or more each, at most kArgmaxSegments per row
+  int P = (vocab + 4095) / 4096;
+  P = P < 1 ? 1 : (P > kArgmaxSegments ? kArgmaxSegments : P);
+  const int seg = ((vocab + P - 1) / P + 3) / 4 * 4;
+  P = (vocab + seg - 1) / seg;
+  launch_kernel(argmax_kernel, dim3(P, rows), dim3(256), 0, st, logits, vocab, seg, part, counters, out);
   return hipGetLastError();
 }
 

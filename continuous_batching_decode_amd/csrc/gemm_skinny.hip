@@ -623,6 +623,16 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
   return (size_t)(nw - 1) * rt * nb * 4 * 64 * 4 + (size_t)std::max(64 * nw, 16 * 16 * nb) * 4;
 }
 
+#ifndef CBD_KS_MAX_UC
+#define CBD_KS_MAX_UC 4
+#endif
+#ifndef CBD_KS_WAVE_TARGET
+#define CBD_KS_WAVE_TARGET 1024
+#endif
+#ifndef CBD_RS_MIN_BLOCKS
+#define CBD_RS_MIN_BLOCKS 600
+#endif
+
 SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int force) {
   SkinnyPlan p{};
   const int per_block = x_blocks > 1 ? 64 : rows;
@@ -631,14 +641,15 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
   // k split: one 16*rt-row tile per workgroup, enough waves to cover the chip
   const int ks_rt = epi == EPI_SWIGLU ? 2 : 1;
   const int ks_tiles = N / 16;
-  const int ks_uc = fmt == FMT_INT4 ? 1 : (K % (4 * 128) == 0 ? 4 : (K % (4 * 64) == 0 ? 2 : 1));
+  int ks_uc = fmt == FMT_INT4 ? 1 : (K % (4 * 128) == 0 ? 4 : (K % (4 * 64) == 0 ? 2 : 1));
+  ks_uc = std::min(ks_uc, CBD_KS_MAX_UC);
   const int ks_unit = step * ks_uc;
   const int ks_maxw = (ks_rt == 1 && p.nb == 1) ? 16 : 8;
   const bool ks_ok = x_blocks == 1 && p.nb <= 2 && K % (4 * ks_unit) == 0;
   // row split: 4 waves x rt subtiles
   const int rs_rt = (epi == EPI_SWIGLU || N % 128 == 0) ? 2 : 1;
   const int rs_blocks = epi == EPI_SWIGLU ? N / 64 : N / (64 * rs_rt);
-  bool use_ks = ks_ok && (long)rs_blocks < 600;
+  bool use_ks = ks_ok && (long)rs_blocks < CBD_RS_MIN_BLOCKS;
   if (force < 0) use_ks = ks_ok;
   if (force > 0) use_ks = false;
   if (use_ks) {
@@ -654,7 +665,8 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
       nw = -force;
     } else {
       while (nw > 1 && K / nw < 2 * ks_unit) nw /= 2;
-      while (nw < ks_maxw && (long)ks_tiles * nw < 4096 && K % (2 * nw * ks_unit) == 0 && K / (2 * nw) >= 2 * ks_unit)
+      while (nw < ks_maxw && (long)ks_tiles * nw < CBD_KS_WAVE_TARGET && K % (2 * nw * ks_unit) == 0 &&
+             K / (2 * nw) >= 2 * ks_unit)
         nw *= 2;
     }
     while (fmt == FMT_BF16 && p.uc > 1 && K / nw < 2 * step * p.uc) p.uc /= 2;

@@ -122,7 +122,10 @@ hipError_t launch_decode_attention(const AttnArgs& a, int n_items, int head_dim,
 hipError_t launch_prefill_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
 
 // greedy argmax per row, lowest id on ties
-hipError_t launch_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st);
+// part: kArgmaxSegments x 64 (max, index) pairs; counters: 64 ints, zero between launches
+constexpr int kArgmaxSegments = 64;
+hipError_t launch_argmax(const float* logits, int rows, int vocab, float* part, int32_t* counters, int32_t* out,
+                         hipStream_t st);
 // scatter canonical K/V [L, n, Hkv, Dh] into a slab at [pos, pos+n), or gather back
 hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_layers, int n_kv_heads,
                             int head_dim, const uint16_t* k_in, const uint16_t* v_in, uint16_t* k_out,

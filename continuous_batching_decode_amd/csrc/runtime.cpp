@@ -117,6 +117,8 @@ struct cbd_ctx {
   float* gemm_part = nullptr;   // split-K partial tiles
   int32_t* gemm_counters = nullptr;  // split-K arrival counters, one per row block
   int32_t* attn_counters = nullptr;  // split-attention arrival counters [64][n_kv_heads]
+  float* argmax_part = nullptr;      // argmax (max, index) pairs [64][kArgmaxSegments]
+  int32_t* argmax_counters = nullptr;  // argmax arrival counters [64]
   size_t gemm_part_bytes = 0;
   int gemm_counter_count = 0;
   float* qkv = nullptr;
@@ -359,6 +361,7 @@ static cbd_status setup_device(cbd_ctx* c) {
   bytes += c->gemm_part_bytes + 256;
   bytes += (size_t)c->gemm_counter_count * 4 + 256;
   bytes += (size_t)64 * m.n_kv_heads * 4 + 256;
+  bytes += (size_t)64 * kArgmaxSegments * 2 * 4 + 256 + 64 * 4 + 256;  // argmax pairs and counters
   bytes += R * m.d_model * 4 + 256;                 // h
   bytes += 2 * R * m.d_model * 2 + 256;             // xa planes
   bytes += 2 * R * c->q_dim * 2 + 256;              // xo planes
@@ -382,6 +385,8 @@ static cbd_status setup_device(cbd_ctx* c) {
   c->gemm_part = align_ptr<float>(p, c->gemm_part_bytes / 4);
   c->gemm_counters = align_ptr<int32_t>(p, c->gemm_counter_count);
   c->attn_counters = align_ptr<int32_t>(p, (size_t)64 * m.n_kv_heads);
+  c->argmax_part = align_ptr<float>(p, (size_t)64 * kArgmaxSegments * 2);
+  c->argmax_counters = align_ptr<int32_t>(p, 64);
   c->qkv = align_ptr<float>(p, R * c->qkv_dim);
   c->xa_plane = (int64_t)R * m.d_model;
   c->xo_plane = (int64_t)R * c->q_dim;
@@ -778,7 +783,7 @@ cbd_status run_head(cbd_ctx* c, const int32_t* row_idx_d, int rows, float* logit
   }
   if (next_tokens) {
     ProfScope p(c, CBD_KERNEL_ARGMAX, rows * (double)m.vocab * 4.0, 0, st);
-    HIP_TRY(launch_argmax(logits, rows, m.vocab, next_tokens, st), "argmax");
+    HIP_TRY(launch_argmax(logits, rows, m.vocab, c->argmax_part, c->argmax_counters, next_tokens, st), "argmax");
   }
   return CBD_OK;
 }
@@ -915,7 +920,8 @@ extern "C" cbd_status greedy_argmax(cbd_ctx* c, const float* logits_dev, int32_t
   if (rows == 0) return CBD_OK;
   if (!logits_dev || !tokens_dev || !aligned16(logits_dev)) return fail(CBD_E_INVAL, "greedy_argmax: bad pointer");
   if (c->host_only) return fail(CBD_E_NODEVICE, "greedy_argmax: host-only context");
-  HIP_TRY(launch_argmax(logits_dev, rows, c->cfg.vocab, tokens_dev, static_cast<hipStream_t>(stream)), "argmax");
+  HIP_TRY(launch_argmax(logits_dev, rows, c->cfg.vocab, c->argmax_part, c->argmax_counters, tokens_dev,
+                        static_cast<hipStream_t>(stream)), "argmax");
   return CBD_OK;
 }
 
