@@ -662,14 +662,15 @@ void with_residual(cbd_ctx* c, SkinnyArgs& a, const uint16_t* next_gain) {
   a.ss_out_ld = c->rows_pad;
 }
 
-// Algorithmic bytes of one weight-streaming launch: weights + activations read + outputs written.
+// Algorithmic bytes of one weight-streaming launch: weights, the activation pair read (hi + lo bf16
+// = 4 bytes per element), and what the epilogue writes: fp32 outputs (store), the residual read and
+// written plus the next activation pair (residual), or the SwiGLU activation pair (swiglu).
 double gemm_bytes(const cbd_ctx* c, int rows, int n_total, int K, int epi) {
   const double w = c->fmt == FMT_INT4 ? (double)n_total * K / 2 + (double)n_total * (K / 64) * 4
                                       : (double)n_total * K * 2;
-  const int n_out = epi == EPI_SWIGLU ? n_total / 2 : n_total;
-  const double out = epi == EPI_SWIGLU ? (double)rows * n_out * 2
-                                       : (double)rows * n_out * 4 * (epi == EPI_RESIDUAL ? 2 : 1);
-  return w + (double)rows * K * 2 + out;
+  const double out = epi == EPI_SWIGLU ? (double)rows * (n_total / 2) * 4
+                                       : (double)rows * n_total * (epi == EPI_RESIDUAL ? 12 : 4);
+  return w + (double)rows * K * 4 + out;
 }
 
 double gemm_flops(int rows, int n_total, int K) { return 2.0 * rows * n_total * K; }
