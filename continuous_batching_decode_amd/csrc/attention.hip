@@ -23,8 +23,10 @@
 // over several items (flash-decoding); the last wave of a (row, KV head) to
 // finish merges the splits with the log-sum-exp rule in a fixed order.
 //
-// Prefill (prefill_attention_kernel): one workgroup per (query row, KV head),
-// key tiles of 64 staged through LDS; the row's K/V were appended beforehand.
+// Prefill (prefill_attention_kernel): the same products with the 16 columns
+// holding 16 consecutive query tokens of one segment and one query head; each
+// column masks keys after its own position (causal) and reads only its own
+// segment's slab (block-diagonal). The tokens' K/V were appended beforehand.
 #include "common.h"
 #include "kernels.h"
 
@@ -65,22 +67,144 @@ CBD_DEVICE void split4(const float (&v)[4], uint2& hi, uint2& lo) {
 
 CBD_DEVICE float exp_or_zero(float x, float m) { return x == -INFINITY ? 0.f : __expf(x - m); }
 
-}  // namespace
+CBD_DEVICE void load8(const float* p, float (&x)[8]) {
+  const float4 x0 = *reinterpret_cast<const float4*>(p);
+  const float4 x1 = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+  x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+}
 
-// ============================================================================ decode
+// Keys of one (slab, layer, KV head) region, streamed in blocks of 32 (K then V fragments).
+template <int DH>
+struct KVStream {
+  static constexpr int NU = DH / 32;  // dim chunks of 32 (K fragments per 16 keys)
+  static constexpr int NT = DH / 16;  // dim tiles of 16 (V fragments per 32 keys)
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  int lane;
+  CBD_DEVICE void load_k(u32x4_t (&K)[2 * NU], int b) const {
+    const uint16_t* p = kbase + (int64_t)b * 32 * DH + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < 2 * NU; ++i) K[i] = load_stream(p + 512 * i);
+  }
+  CBD_DEVICE void load_v(u32x4_t (&V)[NT], int b) const {
+    const uint16_t* p = vbase + (int64_t)b * 32 * DH + 8 * lane;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) V[t] = load_stream(p + 512 * t);
+  }
+};
 
-template <int DH, int G>
-__global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, int n_waves) {
-  constexpr int NU = DH / 32;  // dim chunks of 32 (K fragments per 16 keys)
-  constexpr int NT = DH / 16;  // dim tiles of 16 (V fragments per 32 keys)
-  constexpr int BLK = 32 * DH;
-  constexpr int PAIR = DH / 64;  // RoPE partner of chunk u is u ^ PAIR (dims d and d + Dh/2)
-  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
-  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  if (w >= n_waves) return;
-  const int j = w % a.n_kv_heads;
-  AttnItem it = a.items[w / a.n_kv_heads];
-  // the item is the same for the whole wave: keep it in scalar registers (uniform branches)
+// Running softmax state of the lane's column (equal in the column's 4 lanes) and its O^T tiles.
+template <int DH>
+struct Online {
+  f32x4_t o[DH / 16];
+  float m, l;
+  CBD_DEVICE void clear() {
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
+  }
+};
+
+// S^T of one block: lane holds keys 32b + 4g + e (s0) and 32b + 16 + 4g + e (s1) of its column.
+template <int DH>
+CBD_DEVICE void block_scores(const u32x4_t (&K)[DH / 16], const bf16x8_t (&qh)[DH / 32],
+                             const bf16x8_t (&ql)[DH / 32], f32x4_t& s0, f32x4_t& s1) {
+  constexpr int NU = DH / 32;
+  s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    s0 = mfma(as_frag(K[u]), qh[u], s0);
+    s0 = mfma(as_frag(K[u]), ql[u], s0);
+    s1 = mfma(as_frag(K[NU + u]), qh[u], s1);
+    s1 = mfma(as_frag(K[NU + u]), ql[u], s1);
+  }
+}
+
+// Online softmax over block b (keys at or past lim, the limit of the lane's column, are masked),
+// then O^T += V^T P^T, where P^T element i of lane group g is key kk = 8g + i of the block's V order.
+template <int DH>
+CBD_DEVICE void block_accumulate(const u32x4_t (&V)[DH / 16], const f32x4_t& s0, const f32x4_t& s1, int b, int g,
+                                 int lim, float scale, Online<DH>& st) {
+  float sv[8];
+  const int k0 = 32 * b + 4 * g;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sv[e] = k0 + e < lim ? s0[e] * scale : -INFINITY;
+    sv[4 + e] = k0 + 16 + e < lim ? s1[e] * scale : -INFINITY;
+  }
+  float bm = sv[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) bm = fmaxf(bm, sv[i]);
+  bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+  bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+  const float m_new = fmaxf(st.m, bm);
+  const float alpha = exp_or_zero(st.m, m_new);
+  float p[8], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = exp_or_zero(sv[i], m_new);
+    ps += p[i];
+  }
+  ps += __shfl_xor(ps, 16, 64);
+  ps += __shfl_xor(ps, 32, 64);
+  st.l = st.l * alpha + ps;
+  st.m = m_new;
+  bf16x8_t ph, pl;
+  split8(p, ph, pl);
+#pragma unroll
+  for (int t = 0; t < DH / 16; ++t) {
+    st.o[t] = st.o[t] * alpha;
+    st.o[t] = mfma(as_frag(V[t]), ph, st.o[t]);
+    st.o[t] = mfma(as_frag(V[t]), pl, st.o[t]);
+  }
+}
+
+// Blocks [b_first, b_end), K0/V0 already holding block b_first. One block in registers,
+// staggered: the next K loads during the softmax and P.V of this block, the next V during the next
+// block's scores. The loads are unconditional (a branch around them makes the compiler's completion
+// waits cover everything) and scheduling barriers keep them in this order; the last block is peeled.
+template <int DH>
+CBD_DEVICE void stream_blocks(const KVStream<DH>& kv, u32x4_t (&K0)[DH / 16], u32x4_t (&V0)[DH / 16], int b_first,
+                              int b_end, int g, int lim, float scale, const bf16x8_t (&qh)[DH / 32],
+                              const bf16x8_t (&ql)[DH / 32], Online<DH>& st) {
+  for (int b = b_first; b + 1 < b_end; ++b) {
+    f32x4_t s0, s1;
+    block_scores<DH>(K0, qh, ql, s0, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    kv.load_k(K0, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    block_accumulate<DH>(V0, s0, s1, b, g, lim, scale, st);
+    __builtin_amdgcn_sched_barrier(0);
+    kv.load_v(V0, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (b_first < b_end) {
+    f32x4_t s0, s1;
+    block_scores<DH>(K0, qh, ql, s0, s1);
+    block_accumulate<DH>(V0, s0, s1, b_end - 1, g, lim, scale, st);
+  }
+}
+
+// The lane's O^T tiles (dims 16t + 4g + e of its column), times inv, to the hi/lo planes of `row`.
+template <int DH>
+CBD_DEVICE void store_out(const AttnArgs& a, int row, int head, int g, const f32x4_t (&o)[DH / 16], float inv) {
+#pragma unroll
+  for (int t = 0; t < DH / 16; ++t) {
+    const float y[4] = {o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv};
+    uint2 hi, lo;
+    split4(y, hi, lo);
+    const int64_t off = xfrag_off(row, head * DH + 16 * t + 4 * g, a.ld_out);
+    *reinterpret_cast<uint2*>(a.out + off) = hi;
+    *reinterpret_cast<uint2*>(a.out + a.out_plane + off) = lo;
+  }
+}
+
+// An item is the same for the whole wave: keep it in scalar registers (uniform branches).
+CBD_DEVICE AttnItem uniform_item(const AttnItem* items, int i) {
+  AttnItem it = items[i];
   it.slab_off = ((int64_t)__builtin_amdgcn_readfirstlane((int32_t)(it.slab_off >> 32)) << 32) |
                 (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)it.slab_off);
   it.stride = __builtin_amdgcn_readfirstlane(it.stride);
@@ -89,6 +213,23 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
   it.k_begin = __builtin_amdgcn_readfirstlane(it.k_begin);
   it.k_end = __builtin_amdgcn_readfirstlane(it.k_end);
   it.part = __builtin_amdgcn_readfirstlane(it.part);
+  return it;
+}
+
+}  // namespace
+
+// ============================================================================ decode
+
+template <int DH, int G>
+__global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, int n_waves) {
+  constexpr int NU = DH / 32;  // dim chunks of 32 (K fragments per 16 keys)
+  constexpr int NT = DH / 16;  // dim tiles of 16 (V fragments per 32 keys)
+  constexpr int PAIR = DH / 64;  // RoPE partner of chunk u is u ^ PAIR (dims d and d + Dh/2)
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (w >= n_waves) return;
+  const int j = w % a.n_kv_heads;
+  const AttnItem it = uniform_item(a.items, w / a.n_kv_heads);
   const int pos = it.pos;
   const int64_t region = (int64_t)it.stride * DH;
   uint16_t* slab = reinterpret_cast<uint16_t*>(a.arena + it.slab_off);
@@ -98,24 +239,13 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
   const int kend = appends ? pos : it.k_end;  // keys read from the slab: [k_begin, kend)
   const int b_first = it.k_begin >> 5, b_end = (kend + 31) >> 5;
   const float scale = 1.0f / sqrtf((float)DH);
+  const KVStream<DH> kv{kbase, vbase, lane};
 
-  auto load_k = [&](u32x4_t (&K)[2 * NU], int b) {
-    const uint16_t* kb = kbase + (int64_t)b * BLK + 8 * lane;
-#pragma unroll
-    for (int i = 0; i < 2 * NU; ++i) K[i] = load_stream(kb + 512 * i);
-  };
-  auto load_v = [&](u32x4_t (&V)[NT], int b) {
-    const uint16_t* vb = vbase + (int64_t)b * BLK + 8 * lane;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) V[t] = load_stream(vb + 512 * t);
-  };
   // The first block's keys are requested before anything else, so their latency overlaps the
   // set-up below (its values follow the set-up: they are needed only after the first scores).
-  // Loads of K/V blocks are never conditional: a branch around them would make the compiler's
-  // load-completion waits conservative (wait for everything). Block b_first is inside the slab
-  // even when the item reads no slab key (b_first = pos / 32 < stride / 32).
+  // Block b_first is inside the slab even when the item reads no slab key (b_first = pos / 32).
   u32x4_t K0[2 * NU], V0[NT];
-  load_k(K0, b_first);
+  kv.load_k(K0, b_first);
 
   const float2* cs = a.rope_cs + (int64_t)pos * (DH / 2);
   const float* qkv_row = a.qkv + (int64_t)it.row * a.ld_qkv;
@@ -132,12 +262,6 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
         x[u ^ PAIR][e] = x2 * c.x + x1 * c.y;
       }
     }
-  };
-  auto load8 = [&](const float* p, float (&x)[8]) {
-    const float4 x0 = *reinterpret_cast<const float4*>(p);
-    const float4 x1 = *reinterpret_cast<const float4*>(p + 4);
-    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-    x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
   };
 
   // Q^T operand: column c16 = query head j*G + c16 (zero beyond G)
@@ -157,25 +281,22 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
     }
   }
 
-  f32x4_t o[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;  // per column (head); equal in the column's 4 lanes
-
+  Online<DH> st;
+  st.clear();
   if (appends) {
     // The new token goes first (the softmax sum does not depend on the order): k rotated to pos and
     // rounded to bf16 on the lane's score dims, v rounded on its output dims; then stored at pos.
     const float* kx = qkv_row + (int64_t)a.n_heads * DH + (int64_t)j * DH;
     const float* vx = kx + (int64_t)a.n_kv_heads * DH;
-    float kv[NU][8];
+    float kvals[NU][8];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) load8(kx + 32 * u + 8 * g, kv[u]);
+    for (int u = 0; u < NU; ++u) load8(kx + 32 * u + 8 * g, kvals[u]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {  // v lands in the accumulator: O starts as 1 x v
       const float4 x = *reinterpret_cast<const float4*>(vx + 16 * t + 4 * g);
-      o[t] = f32x4_t{x.x, x.y, x.z, x.w};
+      st.o[t] = f32x4_t{x.x, x.y, x.z, x.w};
     }
-    rotate(kv);
+    rotate(kvals);
     float dot = 0.f;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -183,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
       uint32_t kb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t b0 = f32_to_bf16(kv[u][2 * i]), b1 = f32_to_bf16(kv[u][2 * i + 1]);
+        const uint32_t b0 = f32_to_bf16(kvals[u][2 * i]), b1 = f32_to_bf16(kvals[u][2 * i + 1]);
         kb[i] = b0 | (b1 << 16);
         const float q0 = bf16_to_f32(qhu[i] & 0xFFFFu) + bf16_to_f32(qlu[i] & 0xFFFFu);
         const float q1 = bf16_to_f32(qhu[i] >> 16) + bf16_to_f32(qlu[i] >> 16);
@@ -194,101 +315,25 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
     }
     dot += __shfl_xor(dot, 16, 64);
     dot += __shfl_xor(dot, 32, 64);
-    m_run = dot * scale;  // p = exp(s - m) = 1
-    l_run = 1.f;
+    st.m = dot * scale;  // p = exp(s - m) = 1
+    st.l = 1.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t vb = f32_to_bf16(o[t][e]);
-        o[t][e] = bf16_to_f32(vb);
+        const uint32_t vb = f32_to_bf16(st.o[t][e]);
+        st.o[t][e] = bf16_to_f32(vb);
         if (c16 == 0) vbase[vslab_off(pos, 16 * t + 4 * g + e, DH)] = (uint16_t)vb;
       }
   }
 
-  // S^T of a block: lane holds keys 32b + 4g + e (s0) and 32b + 16 + 4g + e (s1) of its column
-  auto scores = [&](const u32x4_t (&K)[2 * NU], f32x4_t& s0, f32x4_t& s1) {
-    s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      s0 = mfma(as_frag(K[u]), qh[u], s0);
-      s0 = mfma(as_frag(K[u]), ql[u], s0);
-      s1 = mfma(as_frag(K[NU + u]), qh[u], s1);
-      s1 = mfma(as_frag(K[NU + u]), ql[u], s1);
-    }
-  };
-  // online softmax over the block, then O^T += V^T P^T
-  auto accumulate = [&](const u32x4_t (&V)[NT], const f32x4_t& s0, const f32x4_t& s1, int b) {
-    float sv[8];
-    const int k0 = 32 * b + 4 * g;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sv[e] = k0 + e < kend ? s0[e] * scale : -INFINITY;
-      sv[4 + e] = k0 + 16 + e < kend ? s1[e] * scale : -INFINITY;
-    }
-    float bm = sv[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) bm = fmaxf(bm, sv[i]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-    const float m_new = fmaxf(m_run, bm);
-    const float alpha = exp_or_zero(m_run, m_new);
-    float p[8], ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = exp_or_zero(sv[i], m_new);
-      ps += p[i];
-    }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-    // P^T operand: element i of lane group g is key kk = 8g + i of the block's V order
-    bf16x8_t ph, pl;
-    split8(p, ph, pl);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      o[t] = o[t] * alpha;
-      o[t] = mfma(as_frag(V[t]), ph, o[t]);
-      o[t] = mfma(as_frag(V[t]), pl, o[t]);
-    }
-  };
+  kv.load_v(V0, b_first);
+  stream_blocks<DH>(kv, K0, V0, b_first, b_end, g, kend, scale, qh, ql, st);
+  const f32x4_t(&o)[NT] = st.o;
+  const float m_run = st.m, l_run = st.l;
 
-  load_v(V0, b_first);
-  // one block in registers, staggered: the next K loads during the softmax and P.V of this block,
-  // the next V during the next block's scores; the last block is peeled off the loop
-  for (int b = b_first; b + 1 < b_end; ++b) {  // scheduling barriers keep the loads in this order
-    f32x4_t s0, s1;
-    scores(K0, s0, s1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_k(K0, b + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    accumulate(V0, s0, s1, b);
-    __builtin_amdgcn_sched_barrier(0);
-    load_v(V0, b + 1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (b_first < b_end) {
-    f32x4_t s0, s1;
-    scores(K0, s0, s1);
-    accumulate(V0, s0, s1, b_end - 1);
-  }
-
-  if (it.part < 0) {
-    // output: lane (c16 < G) holds dims 16t + 4g + e of head j*G + c16
-    if (c16 < G) {
-      const float inv = 1.0f / l_run;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float y[4] = {o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv};
-        uint2 hi, lo;
-        split4(y, hi, lo);
-        const int64_t off = xfrag_off(it.row, (j * G + c16) * DH + 16 * t + 4 * g, a.ld_out);
-        *reinterpret_cast<uint2*>(a.out + off) = hi;
-        *reinterpret_cast<uint2*>(a.out + a.out_plane + off) = lo;
-      }
-    }
+  if (it.part < 0) {  // output: lane (c16 < G) holds dims 16t + 4g + e of head j*G + c16
+    if (c16 < G) store_out<DH>(a, it.row, j * G + c16, g, o, 1.0f / l_run);
     return;
   }
   // split item: publish the unnormalised partial and (max, sum); the last wave of the (row, KV head)
@@ -400,158 +445,46 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
 
 // ============================================================================ prefill
 
-template <int DH, int G>
-__global__ __launch_bounds__(256) void prefill_attention_kernel(AttnArgs a) {
-  constexpr int TILE = 64;
-  constexpr int KROW = DH + 8;           // padded LDS row (elements) against bank conflicts
-  constexpr int CH = DH / 8;             // 16-byte chunks per key row
-  constexpr int LOADS = TILE * CH / 256;  // 16-byte chunks per thread per tile (K and V each)
-  constexpr int QD = DH / 4;             // dims per thread in the score phase
-  constexpr int DPAIRS = DH / 2;         // threads per key group in the PV phase
-  constexpr int KGROUPS = 256 / DPAIRS;   // key groups in the PV phase
-  constexpr int KPER = TILE / KGROUPS;    // keys per thread per tile in the PV phase
-  constexpr int VCH = 4 * DH;            // 16-byte V chunks per block of 32 keys
-  static_assert(LOADS >= 1, "tile too small");
-  __shared__ float qs[G][DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[TILE][KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[TILE][KROW];
-  __shared__ float S[G][TILE];
-  __shared__ float alpha_s[G];
-  __shared__ float red[KGROUPS][G][DH];
-  __shared__ float ml_s[G][2];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const AttnItem it = a.items[blockIdx.x];
-  const int j = blockIdx.y;
-  const float scale = 1.0f / sqrtf((float)DH);
-
-  // queries of this KV group (already rotated)
-  const float* q = a.qkv + (int64_t)it.row * a.ld_qkv + (int64_t)j * G * DH;
-  for (int i = tid; i < G * DH; i += 256) qs[i / DH][i % DH] = q[i];
-
+template <int DH>
+__global__ __launch_bounds__(256, 2) void prefill_attention_kernel(AttnArgs a, int n_waves) {
+  constexpr int NU = DH / 32;
+  constexpr int NT = DH / 16;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (w >= n_waves) return;
+  // A tile of up to 16 queries p = pos .. k_end - 1 of one segment (global rows row, row + 1, ...);
+  // the waves of a workgroup take consecutive query heads of the same tile, so the G heads of a
+  // KV head read its blocks together.
+  const AttnItem it = uniform_item(a.items, w / a.n_heads);
+  const int h = w % a.n_heads, j = h / (a.n_heads / a.n_kv_heads);
+  const int n_q = it.k_end - it.pos;
   const int64_t region = (int64_t)it.stride * DH;
   const uint16_t* slab = reinterpret_cast<const uint16_t*>(a.arena + it.slab_off);
-  const uint16_t* kbase = slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * region;
-  const uint16_t* vbase = slab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * region;
-
-  float m_run = -INFINITY, l_run = 0.f;  // held by wave h for head h (h < G)
-  float o[G][2];
+  const KVStream<DH> kv{slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * region,
+                        slab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * region, lane};
+  u32x4_t K0[2 * NU], V0[NT];
+  kv.load_k(K0, 0);
+  // Q^T operand: column c16 = query pos + c16 (zero past the tile), already rotated
+  bf16x8_t qh[NU], ql[NU];
+  {
+    const float* q = a.qkv + (int64_t)(it.row + min(c16, n_q - 1)) * a.ld_qkv + (int64_t)h * DH;
 #pragma unroll
-  for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = 0.f;
-  const int dp = tid % DPAIRS, kg = tid / DPAIRS;
-
-  // K chunk c: key c / CH, dims 8 (c % CH) .. +7. V chunk c: block c / VCH, fragment t, lane ln:
-  // dim 16 t + ln%16 of keys kk = 8 (ln/16) .. +7 in the block's V order.
-  uint4 kreg[LOADS], vreg[LOADS];
-  auto fetch = [&](int kb) {
+    for (int u = 0; u < NU; ++u) {
+      float qv[8];
+      load8(q + 32 * u + 8 * g, qv);
+      if (c16 >= n_q)
 #pragma unroll
-    for (int l = 0; l < LOADS; ++l) {
-      const int c = tid + 256 * l;
-      const int key = kb + c / CH;
-      kreg[l] = key < it.k_end ? *reinterpret_cast<const uint4*>(kbase + kslab_off(key, (c % CH) * 8, DH))
-                               : uint4{0u, 0u, 0u, 0u};
-      const int blk = (kb >> 5) + c / VCH;
-      vreg[l] = 32 * blk < it.k_end ? *reinterpret_cast<const uint4*>(vbase + (int64_t)blk * 32 * DH + 8 * (c % VCH))
-                                    : uint4{0u, 0u, 0u, 0u};
-    }
-  };
-  fetch(it.k_begin);
-  for (int kb = it.k_begin; kb < it.k_end; kb += TILE) {
-    __syncthreads();  // previous tile consumed (and the query staging done)
-#pragma unroll
-    for (int l = 0; l < LOADS; ++l) {
-      const int c = tid + 256 * l;
-      *reinterpret_cast<uint4*>(&Ks[c / CH][(c % CH) * 8]) = kreg[l];
-      const int bl = c / VCH, rem = c % VCH, t = rem >> 6, ln = rem & 63;
-      const int d = 16 * t + (ln & 15), gg = ln >> 4;
-      const uint32_t vw[4] = {vreg[l].x, vreg[l].y, vreg[l].z, vreg[l].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int key = 32 * bl + 16 * (i >> 2) + 4 * gg + (i & 3);  // tile-local key of kk = 8 gg + i
-        const uint16_t v = (uint16_t)(vw[i >> 1] >> (16 * (i & 1)));
-        Vs[key][d] = kb + key < it.k_end ? v : (uint16_t)0;
-      }
-    }
-    __syncthreads();
-    if (kb + TILE < it.k_end) fetch(kb + TILE);  // next tile in flight during this one
-    // scores: 4 threads per key, QD dims each
-    {
-      const int r = tid >> 2, qd = tid & 3;
-      float part[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) part[h] = 0.f;
-#pragma unroll
-      for (int d8 = 0; d8 < QD; d8 += 8) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(&Ks[r][qd * QD + d8]);
-        const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float k0 = bf16_to_f32(kw[e] & 0xFFFFu), k1 = bf16_to_f32(kw[e] >> 16);
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-            part[h] += qs[h][qd * QD + d8 + 2 * e] * k0 + qs[h][qd * QD + d8 + 2 * e + 1] * k1;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float s = part[h];
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        if (qd == 0) S[h][r] = (kb + r < it.k_end) ? s * scale : -INFINITY;
-      }
-    }
-    __syncthreads();
-    // online softmax: wave h owns head h
-    if (wave < G) {
-      const float s = S[wave][lane];
-      const float m_new = fmaxf(m_run, wave_max(s));
-      const float p = exp_or_zero(s, m_new);
-      const float alpha = exp_or_zero(m_run, m_new);
-      l_run = l_run * alpha + wave_sum(p);
-      m_run = m_new;
-      S[wave][lane] = p;
-      if (lane == 0) alpha_s[wave] = alpha;
-    }
-    __syncthreads();
-    // P.V: thread owns dims (2dp, 2dp+1) of all G heads over KPER keys
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float al = alpha_s[h];
-      o[h][0] *= al;
-      o[h][1] *= al;
-    }
-#pragma unroll 4
-    for (int kk = 0; kk < KPER; ++kk) {
-      const int r = kg * KPER + kk;
-      const uint32_t v2 = *reinterpret_cast<const uint32_t*>(&Vs[r][2 * dp]);
-      const float v0 = bf16_to_f32(v2 & 0xFFFFu), v1 = bf16_to_f32(v2 >> 16);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = S[h][r];
-        o[h][0] += p * v0;
-        o[h][1] += p * v1;
-      }
+        for (int e = 0; e < 8; ++e) qv[e] = 0.f;
+      split8(qv, qh[u], ql[u]);
     }
   }
-  // combine the key groups in a fixed order
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    red[kg][h][2 * dp] = o[h][0];
-    red[kg][h][2 * dp + 1] = o[h][1];
-  }
-  if (wave < G && lane == 0) {
-    ml_s[wave][0] = m_run;
-    ml_s[wave][1] = l_run;
-  }
-  __syncthreads();
-  for (int i = tid; i < G * DH; i += 256) {
-    const int h = i / DH, d = i % DH;
-    float acc = 0.f;
-#pragma unroll
-    for (int g2 = 0; g2 < KGROUPS; ++g2) acc += red[g2][h][d];
-    const int64_t off = xfrag_off(it.row, (j * G + h) * DH + d, a.ld_out);
-    store_split(a.out + off, a.out + a.out_plane + off, acc / ml_s[h][1]);
-  }
+  kv.load_v(V0, 0);
+  Online<DH> st;
+  st.clear();
+  // causal: column c16 sees keys 0 .. pos + c16 of its own segment (columns past the tile see none)
+  const int lim = c16 < n_q ? it.pos + c16 + 1 : 0;
+  stream_blocks<DH>(kv, K0, V0, 0, (it.k_end + 31) >> 5, g, lim, 1.0f / sqrtf((float)DH), qh, ql, st);
+  if (c16 < n_q) store_out<DH>(a, it.row + c16, h, g, st.o, 1.0f / st.l);
 }
 
 template <int DH>
@@ -560,17 +493,6 @@ static hipError_t launch_decode_dh(int G, dim3 grid, int n_waves, hipStream_t st
     case 1: launch_kernel((decode_attention_kernel<DH, 1>), grid, dim3(256), 0, st, a, n_waves); break;
     case 2: launch_kernel((decode_attention_kernel<DH, 2>), grid, dim3(256), 0, st, a, n_waves); break;
     case 4: launch_kernel((decode_attention_kernel<DH, 4>), grid, dim3(256), 0, st, a, n_waves); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <int DH>
-static hipError_t launch_prefill_dh(int G, dim3 grid, hipStream_t st, const AttnArgs& a) {
-  switch (G) {
-    case 1: launch_kernel((prefill_attention_kernel<DH, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: launch_kernel((prefill_attention_kernel<DH, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: launch_kernel((prefill_attention_kernel<DH, 4>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -586,11 +508,12 @@ hipError_t launch_decode_attention(const AttnArgs& a, int n_items, int head_dim,
 }
 
 hipError_t launch_prefill_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st) {
-  const int G = a.n_heads / a.n_kv_heads;
-  const dim3 grid(n_items, a.n_kv_heads);
-  if (head_dim == 128) return launch_prefill_dh<128>(G, grid, st, a);
-  if (head_dim == 64) return launch_prefill_dh<64>(G, grid, st, a);
-  return hipErrorInvalidValue;
+  const int n_waves = n_items * a.n_heads;
+  const dim3 grid((n_waves + 3) / 4);
+  if (head_dim == 128) launch_kernel((prefill_attention_kernel<128>), grid, dim3(256), 0, st, a, n_waves);
+  else if (head_dim == 64) launch_kernel((prefill_attention_kernel<64>), grid, dim3(256), 0, st, a, n_waves);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace cbd

@@ -882,15 +882,18 @@ extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, cons
   RowMeta* rows = reinterpret_cast<RowMeta*>(host);
   AttnItem* items = reinterpret_cast<AttnItem*>(host + items_off);
   int32_t* last_idx = reinterpret_cast<int32_t*>(host + idx_off);
-  int g = 0;
+  // attention items: tiles of up to 16 consecutive queries of one segment (keys 0 .. end of tile),
+  // the longest first so the grid's tail is short
+  int g = 0, n_items = 0;
   for (int i = 0; i < K; ++i) {
     const Slab& s = c->slabs[seq_ids[i]];
-    for (int p = 0; p < seg_lens[i]; ++p, ++g) {
-      rows[g] = RowMeta{s.off, s.stride, p};
-      items[g] = AttnItem{s.off, s.stride, p, g, 0, p + 1, -1};
-    }
+    for (int p = 0; p < seg_lens[i]; ++p) rows[g + p] = RowMeta{s.off, s.stride, p};
+    for (int p0 = 0; p0 < seg_lens[i]; p0 += 16)
+      items[n_items++] = AttnItem{s.off, s.stride, p0, g + p0, 0, std::min(p0 + 16, seg_lens[i]), -1};
+    g += seg_lens[i];
     last_idx[i] = g - 1;
   }
+  std::stable_sort(items, items + n_items, [](const AttnItem& x, const AttnItem& y) { return x.k_end > y.k_end; });
   if (cbd_status s = upload(c, slot, idx_off + K * sizeof(int32_t), st)) return s;
   const RowMeta* meta_d = reinterpret_cast<const RowMeta*>(c->meta_dev);
   const AttnItem* items_d = reinterpret_cast<const AttnItem*>(c->meta_dev + items_off);
@@ -906,7 +909,7 @@ extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, cons
                          c->xa_plane, c->ss, c->rows_pad, st),
             "embed");
   }
-  if (cbd_status s = run_layers(c, (int)T, x_blocks, meta_d, items_d, (int)T, nullptr, 0, kv_keys, st)) return s;
+  if (cbd_status s = run_layers(c, (int)T, x_blocks, meta_d, items_d, n_items, nullptr, 0, kv_keys, st)) return s;
   if (cbd_status s = run_head(c, idx_d, K, last_logits_dev, next_tokens_dev, st)) return s;
   for (int i = 0; i < K; ++i) c->slabs[seq_ids[i]].len = seg_lens[i];
   c->stats.prefill_calls += 1;
