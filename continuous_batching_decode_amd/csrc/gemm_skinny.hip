@@ -141,14 +141,17 @@ CBD_DEVICE void epilogue(const SkinnyArgs& a, f32x4_t (&acc)[RT][NB], const int 
     const bool valid = b < rows_valid;
     const int row = col0 + b;
     if constexpr (EPI == EPI_SWIGLU) {
-      static_assert(RT == 2, "gate and up subtiles");
-      const int n = sub_row[0] + 4 * g;
-      float m[4];
+      static_assert(RT % 2 == 0, "gate subtiles then their up subtiles");
 #pragma unroll
-      for (int e = 0; e < 4; ++e) m[e] = silu_f(acc[0][c][e] * inv[c]) * (acc[1][c][e] * inv[c]);
-      if (valid) {
-        const int64_t o = xfrag_off(row, n, a.N);
-        store_split4(a.out_x + o, a.out_x + a.out_plane + o, m[0], m[1], m[2], m[3]);
+      for (int i = 0; i < RT / 2; ++i) {
+        const int n = sub_row[i] + 4 * g;
+        float m[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m[e] = silu_f(acc[i][c][e] * inv[c]) * (acc[i + RT / 2][c][e] * inv[c]);
+        if (valid) {
+          const int64_t o = xfrag_off(row, n, a.N);
+          store_split4(a.out_x + o, a.out_x + a.out_plane + o, m[0], m[1], m[2], m[3]);
+        }
       }
     } else if constexpr (EPI == EPI_RESIDUAL) {
 #pragma unroll
@@ -591,6 +594,154 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
   epilogue<RT, NB, EPI>(a, acc, sub_row, col0, rows_valid, inv, lane, nullptr);
 }
 
+// ============================================================================ dense tiles
+
+// Many activation rows (prefill): 128 weight rows x 128 activation rows per workgroup, 2 x 2 waves of
+// 64 x 64. Each stage stages one 32-input fragment column of both operands in LDS (the fragments are
+// already MFMA operands: a copy), double-buffered with one barrier per stage. SwiGLU tiles hold 64
+// gate rows and the matching 64 up rows. bf16 weights only.
+namespace {
+constexpr int kDenseTileN = 128, kDenseTileM = 128;
+constexpr int kDenseStageElems = (8 + 16) * 512;  // 8 weight fragments + 8 row tiles x 2 planes
+
+// weight row of subtile f (0..7) of the workgroup's tile
+template <int EPI>
+CBD_DEVICE int dense_row(const SkinnyArgs& a, int n0, int f) {
+  if constexpr (EPI == EPI_SWIGLU) return f < 4 ? n0 + 16 * f : a.seg_end[0] + n0 + 16 * (f - 4);
+  return n0 + 16 * f;
+}
+}  // namespace
+
+template <int EPI>
+__global__ __launch_bounds__(256) void dense_gemm_kernel(SkinnyArgs a, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int RT = 4, NB = 4;
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);  // 2 stages of kDenseStageElems
+  float* inv_s = reinterpret_cast<float*>(smem + 2 * kDenseStageElems * 2);  // [128]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wn = wave & 1, wm = wave >> 1;
+  // XCD-aware tile order: workgroups go to the 8 XCDs round-robin, so the ones an XCD runs together
+  // (ids x, x + 8, x + 16, ...) get one 8 x 8 block of tiles and reuse its weight and activation
+  // fragments from that XCD's L2. Ids that fall outside the tile grid return.
+  const int tiles_m = (a.rows + kDenseTileM - 1) / kDenseTileM;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int super = (j >> 6) * 8 + xcd, r = j & 63;
+  const int super_n = (tiles_n + 7) >> 3;
+  const int tn = (super % super_n) * 8 + (r & 7), tm = (super / super_n) * 8 + (r >> 3);
+  if (tn >= tiles_n || tm >= tiles_m) return;
+  const int n0 = tn * (EPI == EPI_SWIGLU ? kDenseTileN / 2 : kDenseTileN);
+  const int m0 = tm * kDenseTileM;
+  const int K = a.K, nk = K >> 5;
+
+  // this thread's 6 fragment copies per stage: fragment f = wave + 4 i (0..7 weights, 8..23 activations)
+  const uint16_t* src[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const int f = wave + 4 * i;
+    if (f < 8) {
+      const int grow = dense_row<EPI>(a, n0, f);
+      const int sg = seg_of(a, grow);
+      const int tr = (grow - seg_begin(a, sg)) >> 4;
+      src[i] = reinterpret_cast<const uint16_t*>(a.w[sg]) + (int64_t)tr * nk * 512 + 8 * lane;
+    } else {
+      const int plane = (f - 8) >> 3, c = (f - 8) & 7;
+      src[i] = a.x + plane * a.x_plane + (int64_t)((m0 >> 4) + c) * nk * 512 + 8 * lane;
+    }
+  }
+  // global -> registers -> LDS; two register sets keep the loads of the next two stages in flight
+  auto fetch = [&](u32x4_t (&r)[6], int kf) {  // cached loads: other tiles of the block reuse them
+#pragma unroll
+    for (int i = 0; i < 6; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(src[i] + (int64_t)kf * 512);
+  };
+  auto put = [&](const u32x4_t (&r)[6], int buf) {  // a fragment is a 1 KB copy
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+      *reinterpret_cast<u32x4_t*>(lds + buf * kDenseStageElems + (wave + 4 * i) * 512 + 8 * lane) = r[i];
+  };
+  u32x4_t r0[6], r1[6];
+
+  // 1/rms of the tile's rows, added in the same fixed order as the other kernels (16 groups)
+  fetch(r0, 0);
+  if (a.ss) {
+    float* part = reinterpret_cast<float*>(lds + kDenseStageElems);  // [16][128], stage 1 is free here
+    const int per = a.ss_tiles / 16;
+    for (int i = tid; i < 16 * kDenseTileM; i += 256) {
+      const int r = i % kDenseTileM, grp = i / kDenseTileM;
+      float sum = 0.f;
+      if (m0 + r < a.rows) {
+        const float* q = a.ss + (int64_t)grp * per * a.ss_ld + m0 + r;
+        for (int t = 0; t < per; ++t) sum += q[(int64_t)t * a.ss_ld];
+      }
+      part[grp * kDenseTileM + r] = sum;
+    }
+    __syncthreads();
+    if (tid < kDenseTileM) {
+      float sum = 0.f;
+      for (int grp = 0; grp < 16; ++grp) sum += part[grp * kDenseTileM + tid];
+      inv_s[tid] = 1.0f / sqrtf(sum / a.norm_dim + a.eps);
+    }
+  }
+  put(r0, 0);
+  __syncthreads();
+  // stages past the last refetch the last one (unused): loads stay unconditional
+  fetch(r0, min(1, nk - 1));
+  fetch(r1, min(2, nk - 1));
+
+  f32x4_t acc[RT][NB];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // LDS fragments of this wave: weights (4 subtiles), activations (4 row tiles x 2 planes)
+  int fa[RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    if constexpr (EPI == EPI_SWIGLU) fa[i] = i < 2 ? 2 * wn + i : 4 + 2 * wn + (i - 2);
+    else fa[i] = 4 * wn + i;
+  }
+  auto compute = [&](int buf) {
+    const uint16_t* st = lds + buf * kDenseStageElems;
+    bf16x8_t A[RT], X[NB][2];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) A[i] = *reinterpret_cast<const bf16x8_t*>(st + fa[i] * 512 + 8 * lane);
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+        X[c][pl] = *reinterpret_cast<const bf16x8_t*>(st + (8 + pl * 8 + 4 * wm + c) * 512 + 8 * lane);
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        acc[i][c] = mfma(A[i], X[c][0], acc[i][c]);
+        acc[i][c] = mfma(A[i], X[c][1], acc[i][c]);
+      }
+  };
+  // stage kf is in LDS buffer kf & 1; the register set of stage kf + 1 is put after computing kf.
+  // nk is even (K % 64 == 0), so the loop body has no branch and the load waits stay exact.
+  for (int kf = 0; kf < nk; kf += 2) {
+    compute(0);
+    put(r0, 1);
+    __syncthreads();
+    fetch(r0, min(kf + 3, nk - 1));
+    compute(1);
+    put(r1, 0);
+    __syncthreads();
+    fetch(r1, min(kf + 4, nk - 1));
+  }
+
+  int sub_row[RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) sub_row[i] = dense_row<EPI>(a, n0, fa[i]);
+  const int col0 = m0 + 64 * wm;
+  const int rows_valid = min(64, a.rows - col0);
+  if (rows_valid <= 0) return;
+  float inv[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) inv[c] = a.ss ? inv_s[64 * wm + 16 * c + (lane & 15)] : 1.f;
+  epilogue<RT, NB, EPI>(a, acc, sub_row, col0, rows_valid, inv, lane, nullptr);
+}
+
 // ============================================================================ weight packing
 
 // row-major bf16 [N, K] -> streaming layout (N % 16 == 0, K % 32 == 0)
@@ -635,6 +786,18 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
 
 SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int force) {
   SkinnyPlan p{};
+  // dense tiles for many activation rows (bf16 weights; N in whole tiles)
+  if (force == 0 && x_blocks > 1 && fmt == FMT_BF16 && K % 64 == 0 &&
+      (epi == EPI_SWIGLU ? N % (kDenseTileN / 2) == 0 : N % kDenseTileN == 0)) {
+    p.kind = 2;
+    p.rt = 4;
+    p.nb = 4;
+    p.uc = 1;
+    p.splits = 1;
+    p.waves = 4;
+    p.row_blocks = epi == EPI_SWIGLU ? N / (kDenseTileN / 2) : N / kDenseTileN;
+    return p;
+  }
   const int per_block = x_blocks > 1 ? 64 : rows;
   p.nb = (per_block + 15) / 16;
   const int step = fmt == FMT_INT4 ? 128 : 32;
@@ -755,6 +918,19 @@ static hipError_t dispatch(const SkinnyArgs& a, int fmt, int x_blocks, const Ski
 
 hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st) {
   const int step = fmt == FMT_INT4 ? 128 : 32;
+  if (p.kind == 2) {
+    if (fmt != FMT_BF16 || a.K % 64 || a.rows < 1 || p.row_blocks < 1) return hipErrorInvalidValue;
+    // linear ids over 8 x 8 blocks of (N tile, M tile), a whole number of blocks per XCD
+    const int tiles_m = (a.rows + kDenseTileM - 1) / kDenseTileM;
+    const int supers = ((p.row_blocks + 7) / 8) * ((tiles_m + 7) / 8);
+    const dim3 grid(((supers + 7) / 8) * 8 * 64);
+    const size_t lds = (size_t)2 * kDenseStageElems * 2 + kDenseTileM * 4;
+    const int tn = p.row_blocks;
+    if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU>), grid, dim3(256), lds, st, a, tn);
+    else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL>), grid, dim3(256), lds, st, a, tn);
+    else launch_kernel((dense_gemm_kernel<EPI_STORE>), grid, dim3(256), lds, st, a, tn);
+    return hipGetLastError();
+  }
   if (p.kind == 1) {
     if (x_blocks != 1 || p.nb > 2 || p.waves < 1 || p.waves > 16 || a.K % p.waves ||
         (a.K / p.waves) % (step * p.uc) || (p.waves > 8 && (p.rt != 1 || p.nb != 1)) ||

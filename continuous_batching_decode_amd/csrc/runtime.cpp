@@ -106,7 +106,7 @@ struct cbd_ctx {
   cbd_stats_t stats{};
 
   bool host_only = true;
-  int rows_pad = 0;  // activation rows available (multiple of 64)
+  int rows_pad = 0;  // activation rows available (multiple of 128)
   void* ws = nullptr;
   float* h = nullptr;       // residual stream fp32 [R, d]
   uint16_t* xa = nullptr;   // planes of gain * h for the next norm's consumer [2][R, d]
@@ -336,7 +336,7 @@ static cbd_status setup_weights(cbd_ctx* c, const cbd_weights* w) {
 static cbd_status setup_device(cbd_ctx* c) {
   const cbd_model_config& m = c->cfg;
   const int rows = std::max(c->lim.max_batch, c->lim.max_prefill_tokens);
-  c->rows_pad = (int)round_up(std::max(rows, 64), 64);
+  c->rows_pad = (int)round_up(std::max(rows, 128), 128);  // whole 128-row tiles of the dense product
   const size_t R = (size_t)c->rows_pad;
   const size_t G = (size_t)m.n_heads;
   const size_t half = (size_t)m.head_dim / 2;
