@@ -17,6 +17,13 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   timed region, against the 8 TB/s HBM peak
 - cpu_baseline: the CPU oracle timed on one decode step of the same rows
 - sweep: tok/s at B = 1..64 on the same model (scaling check)
+
+Other workloads (``--workload``), each printing its own JSON line:
+- mistral7b-int4: Mistral-7B-shaped model with 4-bit affine weights (group 64),
+  B = 8 (sweep 1, 4, 8, 16), contexts uniform in [1024, 8192]; roofline on the
+  fused-dequant gate/up product.
+- llama8b-long: the 8B-shape bf16 model with B = 8 rows at 32768-token contexts,
+  128 steps; roofline on decode attention (the K/V stream dominates the step).
 """
 import argparse
 import hashlib
@@ -33,6 +40,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "aggregate decode tok/s at B=1..64, 8B-shape bf16; achieved HBM GB/s"
+WORKLOADS = {
+    "llama8b-b8": {"shape": "llama3-8b-shape", "steps": 256, "batch": 8, "sweep": "1,2,4,8,16,32,64", "ctx_lo": 512,
+                   "ctx_hi": 4096, "roofline": "gate_up", "hist_seed": 1},
+    "mistral7b-int4": {"shape": "mistral7b-shape-int4", "steps": 128, "batch": 8, "sweep": "1,4,8,16",
+                       "ctx_lo": 1024, "ctx_hi": 8192, "roofline": "gate_up", "hist_seed": 4},
+    "llama8b-long": {"shape": "llama3-8b-shape", "steps": 128, "batch": 8, "sweep": "", "ctx_lo": 32768,
+                     "ctx_hi": 32768, "roofline": "attention", "hist_seed": 5},
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_llama8b_b8.md")
 KERNEL_SRC = os.path.join(ROOT, "continuous_batching_decode_amd", "csrc", "gemm_skinny.hip")
 
@@ -64,20 +79,24 @@ def committed_traffic():
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--batch", type=int, default=8)
-    ap.add_argument("--sweep", default="1,2,4,8,16,32,64", help="batch sizes for the scaling sweep ('' = none)")
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--sweep", default=None, help="batch sizes for the scaling sweep ('' = none)")
     ap.add_argument("--sweep-steps", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
-    ap.add_argument("--shape", default="llama3-8b-shape")
-    ap.add_argument("--ctx-lo", type=int, default=512)
-    ap.add_argument("--ctx-hi", type=int, default=4096)
+    ap.add_argument("--ctx-lo", type=int, default=None)
+    ap.add_argument("--ctx-hi", type=int, default=None)
+    ap.add_argument("--workload", default="llama8b-b8", choices=sorted(WORKLOADS))
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a device buffer of this many MiB 5 times (a plain copy of known size, "
                          "used to calibrate HBM byte counters), then exit")
     args = ap.parse_args()
+    wl = WORKLOADS[args.workload]
+    for k in ("steps", "batch", "sweep", "ctx_lo", "ctx_hi"):
+        if getattr(args, k) is None:
+            setattr(args, k, wl[k])
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (each GPU would run its own "
               "independent engine; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
@@ -99,11 +118,11 @@ def main():
         log("copy probe: 2 x 5 passes over %d MiB" % args.copy_probe_mib)
         return
 
-    shape = synth.SHAPES[args.shape]
+    shape = synth.SHAPES[wl["shape"]]
     B = args.batch
     sweep = [int(x) for x in args.sweep.split(",") if x.strip()]
     n_rows = max([B] + sweep)
-    ctx = synth.uniform_lengths(1, B, args.ctx_lo, args.ctx_hi).astype(int)
+    ctx = synth.uniform_lengths(wl["hist_seed"], B, args.ctx_lo, args.ctx_hi).astype(int)
     ctx_main = ctx.copy()
     # sweep-only rows (beyond B) reuse the main rows' histories
     ctx = np.array([ctx[r % B] for r in range(n_rows)], dtype=int)
@@ -114,7 +133,8 @@ def main():
     kv_tok = shape.kv_bytes_per_token()
     max_pos = int(max(caps)) + gran
 
-    log("generating %s weights (%.2f GB streamed per step)" % (shape.name, shape.streamed_params() * 2 / 1e9))
+    w_bytes = shape.streamed_params() * (2 if shape.weight_format == "bf16" else 0.5625)
+    log("%s: generating %s weights (%.2f GB streamed per step)" % (args.workload, shape.name, w_bytes / 1e9))
     weights = synth.make_weights(shape, seed=0)
     log("uploading weights; arena %.1f GB" % (arena_tokens * kv_tok / 1e9))
     eng = cbd.Engine(weights, arena_bytes=arena_tokens * kv_tok, max_batch=64, max_prefill_tokens=64,
@@ -122,10 +142,25 @@ def main():
     dev = torch.device("cuda:0")
     ids = [eng.alloc(c) for c in caps]
     hist = []
+    keep = not args.no_cpu_baseline and args.workload != "llama8b-long"  # the oracle needs the histories
     for r in range(B):
-        k, v = synth.kv_history(shape, 1, r, int(ctx[r]))
-        hist.append((k, v))
-        eng.append(ids[r], torch.from_numpy(k.view(np.int16)).to(dev), torch.from_numpy(v.view(np.int16)).to(dev))
+        # seeded K/V, appended in chunks of tokens (the same values as synth.kv_history of the whole row)
+        n = int(ctx[r])
+        std = shape.weight_std * float(np.sqrt(shape.d_model))
+        per_layer = n * shape.kv_dim
+        ks, vs = [], []
+        for t0 in range(0, n, 4096):
+            cn = min(4096, n - t0)
+            kc = np.stack([synth.normal_bf16(wl["hist_seed"], 10_000_000 + 2 * r, (cn, shape.n_kv_heads, shape.head_dim),
+                                             std, offset=l * per_layer + t0 * shape.kv_dim) for l in range(shape.n_layers)])
+            vc = np.stack([synth.normal_bf16(wl["hist_seed"], 10_000_001 + 2 * r, (cn, shape.n_kv_heads, shape.head_dim),
+                                             std, offset=l * per_layer + t0 * shape.kv_dim) for l in range(shape.n_layers)])
+            eng.append(ids[r], torch.from_numpy(kc.view(np.int16)).to(dev), torch.from_numpy(vc.view(np.int16)).to(dev))
+            if keep:
+                ks.append(kc)
+                vs.append(vc)
+        if keep:
+            hist.append((np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)))
     for r in range(B, n_rows):
         # sweep-only rows reuse the histories of the main rows (device copies)
         src = r % B
@@ -152,7 +187,8 @@ def main():
     torch.cuda.synchronize()
 
     log("timing %d steps at B=%d" % (args.steps, B))
-    eng.profile_begin(["gate_up"], max_launches=shape.n_layers * args.steps + 64)
+    rk = wl["roofline"]
+    eng.profile_begin([rk], max_launches=shape.n_layers * args.steps + 64)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -166,22 +202,27 @@ def main():
     tokps = B * args.steps / secs
 
     # algorithmic bytes per step, averaged over the timed steps
-    w_bytes = shape.streamed_params() * (2 if shape.weight_format == "bf16" else 0.5625)
     mean_t = float(np.mean(ctx_main)) + args.warmup + (args.steps - 1) / 2.0
     step_bytes = w_bytes + B * (mean_t + 1) * kv_tok + B * kv_tok + B * V * 4
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
-    gu = prof["gate_up"]
+    gu = prof[rk]
     per_launch_bytes = gu["bytes"] / gu["launches"]
     avg_ms = gu["total_ms"] / gu["launches"]
     achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
+    kernel_desc = {
+        "gate_up": "ksplit_gemm_kernel: gate/up weight stream with fused SwiGLU (%s weights), %s, B=%d" % (
+            shape.weight_format, shape.name, B),
+        "attention": "decode_attention_kernel: RoPE + K/V append + ragged GQA attention, %s, B=%d at %d-token "
+                     "contexts" % (shape.name, B, args.ctx_lo),
+    }[rk]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": committed_traffic(),
-                "kernel": "skinny_gemm_kernel (gate/up weight stream, fused SwiGLU), 8B shape, B=%d" % B,
-                "bytes_per_launch": per_launch_bytes, "avg_launch_us": round(avg_ms * 1e3, 2),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": committed_traffic() if args.workload == "llama8b-b8" else None,
+                "kernel": kernel_desc, "bytes_per_launch": per_launch_bytes, "avg_launch_us": round(avg_ms * 1e3, 2),
                 "launches": gu["launches"], "kernel_source_sha256_16": source_hash()}
-    log("B=%d: %.1f tok/s, %.3f ms/step, step %.0f GB/s; gate/up %.1f us -> %.0f GB/s" % (
-        B, tokps, ms_step, step_gbps, avg_ms * 1e3, achieved))
+    log("B=%d: %.1f tok/s, %.3f ms/step, step %.0f GB/s; %s %.1f us -> %.0f GB/s" % (
+        B, tokps, ms_step, step_gbps, rk, avg_ms * 1e3, achieved))
 
     breakdown = None
     if not args.no_breakdown:
@@ -219,7 +260,7 @@ def main():
 
     cpu = None
     parity = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload != "llama8b-long":
         from oracle import OracleModel, greedy
         try:
             from threadpoolctl import threadpool_info
@@ -248,8 +289,8 @@ def main():
            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16" if shape.weight_format == "bf16" else "int4-affine/bf16",
            "data": "synthetic",
-           "config": {"workload": "%s decode_step_batch, B=%d, contexts U[%d,%d], greedy, %d layers" % (
-               shape.name, B, args.ctx_lo, args.ctx_hi, shape.n_layers),
+           "config": {"workload": "%s: %s decode_step_batch, B=%d, contexts U[%d,%d], greedy, %d layers" % (
+               args.workload, shape.name, B, args.ctx_lo, args.ctx_hi, shape.n_layers),
                "batch": B, "contexts": [int(c) for c in ctx_main], "parallelism": "single GPU"},
            "achieved_hbm_GBps": round(step_gbps, 1), "step_bytes": step_bytes,
            "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),
