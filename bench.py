@@ -24,6 +24,11 @@ Other workloads (``--workload``), each printing its own JSON line:
   fused-dequant gate/up product.
 - llama8b-long: the 8B-shape bf16 model with B = 8 rows at 32768-token contexts,
   128 steps; roofline on decode attention (the K/V stream dominates the step).
+- continuous: the 8B-shape bf16 model under continuous batching with the batch cap
+  swept over 1..64: Poisson arrivals (in decode ticks, offered concurrency about
+  1.25 x cap), prompts uniform in [256, 2048] sharing a 1024-token prefix,
+  generation lengths uniform in [64, 512]. Joiners are admitted between steps
+  with one segmented prefill, rows retire when their length is reached.
 """
 import argparse
 import hashlib
@@ -47,6 +52,8 @@ WORKLOADS = {
                        "ctx_lo": 1024, "ctx_hi": 8192, "roofline": "gate_up", "hist_seed": 4},
     "llama8b-long": {"shape": "llama3-8b-shape", "steps": 128, "batch": 8, "sweep": "", "ctx_lo": 32768,
                      "ctx_hi": 32768, "roofline": "attention", "hist_seed": 5},
+    "continuous": {"shape": "llama3-8b-shape", "steps": 0, "batch": 64, "sweep": "1,2,4,8,16,32,64", "ctx_lo": 256,
+                   "ctx_hi": 2048, "roofline": "gate_up", "hist_seed": 2},
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_llama8b_b8.md")
 KERNEL_SRC = os.path.join(ROOT, "continuous_batching_decode_amd", "csrc", "gemm_skinny.hip")
@@ -118,6 +125,8 @@ def main():
         log("copy probe: 2 x 5 passes over %d MiB" % args.copy_probe_mib)
         return
 
+    if args.workload == "continuous":
+        return run_continuous(args, wl, torch, cbd, synth)
     shape = synth.SHAPES[wl["shape"]]
     B = args.batch
     sweep = [int(x) for x in args.sweep.split(",") if x.strip()]
@@ -296,6 +305,121 @@ def main():
            "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),
            "roofline": roofline, "cpu_baseline": cpu, "parity_first_step": parity, "sweep": sweep_out,
            "kernel_breakdown": breakdown}
+    eng.close()
+    print(json.dumps(out), flush=True)
+
+
+def run_continuous(args, wl, torch, cbd, synth):
+    """Continuous batching over the C ABI: admission with a segmented prefill, one batched decode step
+    per tick over every live row, retirement between steps (no host synchronisation in the loop)."""
+    shape = synth.SHAPES[wl["shape"]]
+    caps = [int(x) for x in args.sweep.split(",") if x.strip()]
+    V, kv_tok = shape.vocab, shape.kv_bytes_per_token()
+    w_bytes = shape.streamed_params() * 2
+    log("continuous: generating %s weights" % shape.name)
+    weights = synth.make_weights(shape, seed=0)
+    gran = 256
+    max_ctx = args.ctx_hi + 512
+    cap_tokens = (max_ctx + gran - 1) // gran * gran
+    max_cap = max(caps)
+    eng = cbd.Engine(weights, arena_bytes=(max_cap + 16) * cap_tokens * kv_tok, max_batch=64,
+                     max_prefill_tokens=16384, max_segments=16, max_position=cap_tokens)
+    dev = torch.device("cuda:0")
+    logits = torch.empty((64, V), dtype=torch.float32, device=dev)
+    pf_logits = torch.empty((16, V), dtype=torch.float32, device=dev)
+    next_b = torch.empty(64, dtype=torch.int32, device=dev)
+    pf_next = torch.empty(16, dtype=torch.int32, device=dev)
+    tok_by_sid = torch.zeros(4096, dtype=torch.int32, device=dev)
+    results = {}
+    for cap in caps:
+        n_req = 4 * cap + 8
+        rng = np.random.Generator(np.random.PCG64(1000 + cap))
+        plens = synth.uniform_lengths(2000 + cap, n_req, args.ctx_lo, args.ctx_hi).astype(int)
+        glens = synth.uniform_lengths(3000 + cap, n_req, 64, 512).astype(int)
+        prompts = synth.shared_prefix_prompts(4000 + cap, plens, V, prefix_len=1024)
+        # arrivals in decode ticks: exponential gaps with mean E[gen] / (1.25 cap)
+        arrive = np.cumsum(rng.exponential(288.0 / (1.25 * cap), size=n_req))
+        arrive -= arrive[0]
+        waiting, live = 0, []  # live: [sid, generated, target, context]
+        dec_ev, pf_ev = [], []
+        dec_rows = pf_tokens = done = 0
+        step_bytes = 0.0
+        tick = 0
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        while done < n_req:
+            joiners = []
+            tot = 0
+            while (waiting < n_req and arrive[waiting] <= tick and len(live) + len(joiners) < cap
+                   and len(joiners) < 16 and tot + plens[waiting] <= 16384):
+                try:
+                    sid = eng.alloc(int(plens[waiting] + glens[waiting]))
+                except cbd.CbdError:
+                    break  # arena full: the request waits
+                joiners.append((sid, waiting))
+                tot += int(plens[waiting])
+                waiting += 1
+            if joiners:
+                toks = torch.from_numpy(np.concatenate([prompts[i] for _, i in joiners]).astype(np.int32)).to(dev)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                eng.prefill_segmented([sd for sd, _ in joiners], [int(plens[i]) for _, i in joiners], toks,
+                                      pf_logits[:len(joiners)], pf_next[:len(joiners)])
+                e1.record()
+                pf_ev.append((e0, e1))
+                sids = torch.tensor([sd for sd, _ in joiners], dtype=torch.int64, device=dev)
+                tok_by_sid.index_copy_(0, sids, pf_next[:len(joiners)])
+                pf_tokens += tot
+                for sd, i in joiners:
+                    live.append([sd, 1, int(glens[i]), int(plens[i])])  # the prefill gave token 1
+            if live:
+                ids = [r[0] for r in live]
+                idx = torch.tensor(ids, dtype=torch.int64, device=dev)
+                last = tok_by_sid.index_select(0, idx)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                eng.decode_step_batch(ids, last, logits[:len(ids)], next_b[:len(ids)])
+                e1.record()
+                dec_ev.append((e0, e1))
+                tok_by_sid.index_copy_(0, idx, next_b[:len(ids)])
+                dec_rows += len(ids)
+                step_bytes += w_bytes + sum(r[3] + r[1] for r in live) * kv_tok + len(ids) * kv_tok
+                for r in live:
+                    r[1] += 1
+                keep = []
+                for r in live:
+                    if r[1] >= r[2]:
+                        eng.free(r[0])
+                        done += 1
+                    else:
+                        keep.append(r)
+                live = keep
+                tick += 1
+            elif waiting < n_req and not joiners:
+                tick = max(tick + 1, int(np.ceil(arrive[waiting])))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        dec_ms = sum(a.elapsed_time(b) for a, b in dec_ev)
+        pf_ms = sum(a.elapsed_time(b) for a, b in pf_ev)
+        gen = int(glens.sum())
+        results[str(cap)] = {
+            "requests": n_req, "decode_steps": len(dec_ev), "mean_live_rows": round(dec_rows / max(1, len(dec_ev)), 2),
+            "decode_tok_s": round(dec_rows / (dec_ms * 1e-3), 1), "decode_ms": round(dec_ms, 1),
+            "prefill_calls": len(pf_ev), "prefill_tokens": pf_tokens, "prefill_ms": round(pf_ms, 1),
+            "prefill_tok_s": round(pf_tokens / (pf_ms * 1e-3), 1) if pf_ms else None,
+            "wall_tok_s": round(gen / wall, 1), "wall_s": round(wall, 2),
+            "decode_GBps": round(step_bytes / (dec_ms * 1e-3) / 1e9, 1)}
+        log("cap %d: %s" % (cap, json.dumps(results[str(cap)])))
+    top = results[str(max(caps))]
+    out = {"metric": "continuous batching: decode-only aggregate tok/s at batch cap %d, 8B-shape bf16" % max(caps),
+           "value": top["decode_tok_s"], "unit": "tok/s", "n_gpus": 1, "steps": top["decode_steps"], "warmup": 0,
+           "ms_per_step": round(top["decode_ms"] / max(1, top["decode_steps"]), 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "continuous: %s, caps %s, Poisson arrivals (offered 1.25 x cap), prompts U[%d,%d] "
+                                  "with a 1024-token shared prefix, generation U[64,512], %d requests per cap = 4 cap + 8"
+                                  % (shape.name, caps, args.ctx_lo, args.ctx_hi, 4 * max(caps) + 8),
+                      "parallelism": "single GPU"},
+           "caps": results}
     eng.close()
     print(json.dumps(out), flush=True)
 

@@ -85,7 +85,10 @@ CBD_DEVICE void store_split4(uint16_t* hi, uint16_t* lo, float v0, float v1, flo
 // rows of the same 16 features).
 template <int RT, int EPI>
 CBD_DEVICE int subtile_row(const SkinnyArgs& a, int t, int i) {
-  if constexpr (EPI == EPI_SWIGLU) return i == 0 ? 16 * t : a.seg_end[0] + 16 * t;
+  if constexpr (EPI == EPI_SWIGLU) {  // RT/2 gate subtiles, then the up subtiles of the same features
+    constexpr int H = RT / 2;
+    return i < H ? 16 * H * t + 16 * i : a.seg_end[0] + 16 * H * t + 16 * (i - H);
+  }
   return 16 * RT * t + 16 * i;
 }
 
@@ -289,14 +292,14 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
   // The epilogue's inputs that do not depend on the product are requested before the weights, so
   // their latency hides behind the stream. First the norm's per-16-feature sums of squares: the 16
   // groups x ROWS rows are split over nq thread sets, each adding ss_cnt consecutive partials in
-  // order (bf16 path only; the int4 path adds them all after its loop).
+  // order.
   constexpr int SSMAX = 8;
   const int ss_per = a.ss ? a.ss_tiles / 16 : 0;
   int nq = 1;
   while (2 * nq * 16 * ROWS <= (int)blockDim.x && ss_per % (2 * nq) == 0) nq *= 2;
   const int ss_cnt = ss_per / nq;
   // (every one of the 16 x ROWS items needs a thread of its own)
-  const bool ss_early = FMT == FMT_BF16 && a.ss && ss_cnt <= SSMAX && (int)blockDim.x >= 16 * ROWS;
+  const bool ss_early = a.ss && ss_cnt <= SSMAX && (int)blockDim.x >= 16 * ROWS;
   const int ss_item = threadIdx.x % (16 * ROWS), ss_q = threadIdx.x / (16 * ROWS);
   const bool ss_mine = ss_early && ss_q < nq && (ss_item % ROWS) < rows_valid;
   float ssv[SSMAX];
@@ -396,22 +399,51 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
       compute(b1);
     }
   } else {
-    const int total = kw / 128;
-    for (int st = 0; st < total; ++st) {
+    // int4: 128 inputs per stage; the same two-buffer pipeline as the bf16 path
+    struct QBuf {
       u32x4_t Wq[RT];
       uint4 SB[RT][2];
       bf16x8_t X[4][NB][2];
+    };
+    auto qload = [&](QBuf& f, int st) {
 #pragma unroll
-      for (int i = 0; i < RT; ++i) Wq[i] = load_stream(reinterpret_cast<const uint32_t*>(wr[i]) + (int64_t)st * 256);
-      load_scales<RT>(a, sub_row, k0 + st * 128, lane >> 4, SB);
+      for (int i = 0; i < RT; ++i) f.Wq[i] = load_stream(reinterpret_cast<const uint32_t*>(wr[i]) + (int64_t)st * 256);
+      load_scales<RT>(a, sub_row, k0 + st * 128, lane >> 4, f.SB);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int c = 0; c < NB; ++c) {
-          X[j][c][0] = load_frag(xr[c] + (4 * st + j) * 512);
-          X[j][c][1] = load_frag(xr[c] + a.x_plane + (4 * st + j) * 512);
+          f.X[j][c][0] = load_frag(xr[c] + (4 * st + j) * 512);
+          f.X[j][c][1] = load_frag(xr[c] + a.x_plane + (4 * st + j) * 512);
         }
-      int4_block<RT, NB>(acc, Wq, SB, X);
+    };
+    const int total = kw / 128;  // >= 2 (plan)
+    QBuf b0, b1;
+    qload(b0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    qload(b1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    ss_store();
+    int st = 0;
+    for (; st + 3 < total; st += 2) {
+      int4_block<RT, NB>(acc, b0.Wq, b0.SB, b0.X);
+      __builtin_amdgcn_sched_barrier(0);
+      qload(b0, st + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      int4_block<RT, NB>(acc, b1.Wq, b1.SB, b1.X);
+      __builtin_amdgcn_sched_barrier(0);
+      qload(b1, st + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    int4_block<RT, NB>(acc, b0.Wq, b0.SB, b0.X);
+    if (st + 2 < total) {
+      __builtin_amdgcn_sched_barrier(0);
+      qload(b0, st + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      int4_block<RT, NB>(acc, b1.Wq, b1.SB, b1.X);
+      int4_block<RT, NB>(acc, b0.Wq, b0.SB, b0.X);
+    } else {
+      int4_block<RT, NB>(acc, b1.Wq, b1.SB, b1.X);
     }
   }
 
@@ -802,13 +834,16 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
   p.nb = (per_block + 15) / 16;
   const int step = fmt == FMT_INT4 ? 128 : 32;
   // k split: one 16*rt-row tile per workgroup, enough waves to cover the chip
-  const int ks_rt = epi == EPI_SWIGLU ? 2 : 1;
-  const int ks_tiles = N / 16;
+  // int4 stages carry 8x more activation bytes than weight bytes per subtile: a wave takes two
+  // subtiles per activation load (for SwiGLU, as for bf16: one gate, one up)
+  const int ks_rt = (epi == EPI_SWIGLU || fmt == FMT_INT4) ? 2 : 1;
+  const int ks_tiles = epi == EPI_SWIGLU ? N / (8 * ks_rt) : N / (16 * ks_rt);
   int ks_uc = fmt == FMT_INT4 ? 1 : (K % (4 * 128) == 0 ? 4 : (K % (4 * 64) == 0 ? 2 : 1));
   ks_uc = std::min(ks_uc, CBD_KS_MAX_UC);
   const int ks_unit = step * ks_uc;
   const int ks_maxw = (ks_rt == 1 && p.nb == 1) ? 16 : 8;
-  const bool ks_ok = x_blocks == 1 && p.nb <= 2 && K % (4 * ks_unit) == 0;
+  const bool ks_ok = x_blocks == 1 && p.nb <= (fmt == FMT_INT4 ? 1 : 2) && K % (4 * ks_unit) == 0 &&
+                     (epi == EPI_SWIGLU ? N % (8 * ks_rt) == 0 : N % (16 * ks_rt) == 0);
   // row split: 4 waves x rt subtiles
   const int rs_rt = (epi == EPI_SWIGLU || N % 128 == 0) ? 2 : 1;
   const int rs_blocks = epi == EPI_SWIGLU ? N / 64 : N / (64 * rs_rt);
@@ -882,12 +917,17 @@ static hipError_t launch_rs(const SkinnyArgs& a, const SkinnyPlan& p, int x_bloc
 template <int RT, int EPI, int FMT, int UC>
 static hipError_t launch_ks(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t st) {
   const dim3 grid(p.row_blocks, 1);
-  if (p.nb == 1)
+  if constexpr (FMT == FMT_INT4) {  // one column tile only (the plan never asks for more)
+    if (p.nb != 1) return hipErrorInvalidValue;
     launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
-                       st, a);
-  else
+                  st, a);
+  } else if (p.nb == 1) {
+    launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
+                  st, a);
+  } else {
     launch_kernel((ksplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 2),
-                       st, a);
+                  st, a);
+  }
   return hipGetLastError();
 }
 
@@ -895,7 +935,7 @@ template <int EPI>
 static hipError_t dispatch(const SkinnyArgs& a, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st) {
   if (p.kind == 1) {
     constexpr int KRT = EPI == EPI_SWIGLU ? 2 : 1;
-    if (fmt == FMT_INT4) return launch_ks<KRT, EPI, FMT_INT4, 1>(a, p, st);
+    if (fmt == FMT_INT4) return launch_ks<2, EPI, FMT_INT4, 1>(a, p, st);
     if (p.uc == 4) return launch_ks<KRT, EPI, FMT_BF16, 4>(a, p, st);
     if (p.uc == 2) return launch_ks<KRT, EPI, FMT_BF16, 2>(a, p, st);
     return launch_ks<KRT, EPI, FMT_BF16, 1>(a, p, st);
@@ -934,7 +974,7 @@ hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, cons
   if (p.kind == 1) {
     if (x_blocks != 1 || p.nb > 2 || p.waves < 1 || p.waves > 16 || a.K % p.waves ||
         (a.K / p.waves) % (step * p.uc) || (p.waves > 8 && (p.rt != 1 || p.nb != 1)) ||
-        (fmt == FMT_BF16 && a.K / p.waves < 2 * step * p.uc))
+        a.K / p.waves < 2 * step * p.uc)
       return hipErrorInvalidValue;
   } else {
     if (p.splits < 1 || a.K % p.splits || (x_blocks > 1 && p.splits > 1)) return hipErrorInvalidValue;
