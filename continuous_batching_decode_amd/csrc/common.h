@@ -71,13 +71,14 @@ CBD_DEVICE float wave_max(float v) {
   return v;
 }
 
-// Activations fed to the weight-streaming products are stored fragment-major:
-// fragments of 16 rows x 32 inputs (1 KB of bf16), fragment (row/16, k/32)
-// at index (row/16) * (K/32) + k/32, and inside it lane l = 16*((k%32)/8) +
-// row%16 holds 8 consecutive inputs. A wave then loads an MFMA operand of 16
-// rows x 32 inputs as 1 KB of consecutive memory.
+// Activations fed to the products are bf16 pairs (hi, lo) stored as MFMA operand fragments of
+// 8 rows x 32 inputs: fragment (row/8, k/32) at index (row/8) * (K/32) + k/32, and inside it lane
+// l = 16*((k%32)/8) + 8*plane + row%8 holds 8 consecutive inputs of (row, plane). One 1 KB wave
+// load is a B operand whose 16 columns are the hi and lo values of 8 rows; the lo value of an
+// element sits kXLo elements after its hi value.
+constexpr int kXLo = 64;
 CBD_DEVICE int64_t xfrag_off(int row, int k, int K) {
-  return ((int64_t)(row >> 4) * (K >> 5) + (k >> 5)) * 512 + ((((k & 31) >> 3) << 4) + (row & 15)) * 8 + (k & 7);
+  return ((int64_t)(row >> 3) * (K >> 5) + (k >> 5)) * 512 + ((((k & 31) >> 3) << 4) + (row & 7)) * 8 + (k & 7);
 }
 
 // Slab layout. A sequence's slab holds, for each layer l and KV head j, a K region and a V region

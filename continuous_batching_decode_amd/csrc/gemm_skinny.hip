@@ -133,15 +133,23 @@ CBD_DEVICE float norm_inv(const SkinnyArgs& a, const float* norm_part, int col, 
   return 1.0f / sqrtf(s / a.norm_dim + a.eps);
 }
 
-// Epilogue of one wave: lane holds y[b = 16c + l%16][n = subtile + 4*(l/16) + e].
+// Epilogue of one wave. Lane l holds the products of column l%16 of each 8-row group c, rows
+// n = subtile + 4*(l/16) + e: columns 0..7 are the hi parts of rows 8c + 0..7, columns 8..15 the lo
+// parts. Adding lanes l and l^8 gives y[b = 8c + l%8][n] in both; lanes with l & 8 clear store it.
 template <int RT, int NB, int EPI>
 CBD_DEVICE void epilogue(const SkinnyArgs& a, f32x4_t (&acc)[RT][NB], const int (&sub_row)[RT], int col0,
                          int rows_valid, const float (&inv)[NB], int lane, const float4 (*hpre)[RT][NB]) {
-  const int r16 = lane & 15, g = lane >> 4;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][c][e] += __shfl_xor(acc[i][c][e], 8, 64);
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
-    const int b = 16 * c + r16;
-    const bool valid = b < rows_valid;
+    const int b = 8 * c + (lane & 7);
+    const bool valid = (lane & 8) == 0 && b < rows_valid;
     const int row = col0 + b;
     if constexpr (EPI == EPI_SWIGLU) {
       static_assert(RT % 2 == 0, "gate subtiles then their up subtiles");
@@ -194,10 +202,10 @@ CBD_DEVICE void epilogue(const SkinnyArgs& a, f32x4_t (&acc)[RT][NB], const int 
 }
 
 // int4 contribution of one 128-input block (4 k-fragments; fragments 0,1 form one group of 64,
-// fragments 2,3 the next). X[j][c][p] = activation fragment j of column tile c, plane p.
+// fragments 2,3 the next). X[j][c] = activation fragment j of 8-row group c (hi and lo columns).
 template <int RT, int NB>
 CBD_DEVICE void int4_block(f32x4_t (&acc)[RT][NB], const u32x4_t (&Wq)[RT], const uint4 (&SB)[RT][2],
-                           const bf16x8_t (&X)[4][NB][2]) {
+                           const bf16x8_t (&X)[4][NB]) {
   const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const bf16x8_t ones = as_frag(ones_u);
 #pragma unroll
@@ -207,10 +215,7 @@ CBD_DEVICE void int4_block(f32x4_t (&acc)[RT][NB], const u32x4_t (&Wq)[RT], cons
     for (int c = 0; c < NB; ++c) {
       f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        t = mfma(ones, X[2 * h + jj][c][0], t);
-        t = mfma(ones, X[2 * h + jj][c][1], t);
-      }
+      for (int jj = 0; jj < 2; ++jj) t = mfma(ones, X[2 * h + jj][c], t);
       xsum[c] = t;
     }
 #pragma unroll
@@ -227,11 +232,8 @@ CBD_DEVICE void int4_block(f32x4_t (&acc)[RT][NB], const u32x4_t (&Wq)[RT], cons
 #pragma unroll
       for (int c = 0; c < NB; ++c) {
         f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          t = mfma(A0, X[2 * h][c][p], t);
-          t = mfma(A1, X[2 * h + 1][c][p], t);
-        }
+        t = mfma(A0, X[2 * h][c], t);
+        t = mfma(A1, X[2 * h + 1][c], t);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][c][e] += sc[e] * t[e] + bc[e] * xsum[c][e];
       }
@@ -262,7 +264,7 @@ CBD_DEVICE void load_scales(const SkinnyArgs& a, const int (&sub_row)[RT], int k
 template <int RT, int NB, int EPI, int FMT, int UC>
 __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_gemm_kernel(SkinnyArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int ROWS = 16 * NB;
+  constexpr int ROWS = 8 * NB;  // activation rows: NB groups of 8
   constexpr int NACC = RT * NB * 4;
   const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -278,10 +280,10 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
   for (int i = 0; i < RT; ++i) sub_row[i] = subtile_row<RT, EPI>(a, tile, i);
   const void* wr[RT];
   weight_ptrs<RT, FMT>(a, sub_row, K, k0, lane, wr);
-  // activation fragment pointers at k0 for each column tile
+  // activation fragment pointers at k0 for each 8-row group
   const uint16_t* xr[NB];
 #pragma unroll
-  for (int c = 0; c < NB; ++c) xr[c] = a.x + ((int64_t)((col0 >> 4) + c) * (K >> 5) + (k0 >> 5)) * 512 + 8 * lane;
+  for (int c = 0; c < NB; ++c) xr[c] = a.x + ((int64_t)((col0 >> 3) + c) * (K >> 5) + (k0 >> 5)) * 512 + 8 * lane;
 
   f32x4_t acc[RT][NB];
 #pragma unroll
@@ -327,8 +329,8 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
       for (int c = 0; c < NB; ++c)
 #pragma unroll
         for (int i = 0; i < RT; ++i)
-          if (16 * c + (lane & 15) < rows_valid)
-            hres[i][c] = *reinterpret_cast<const float4*>(a.out + (int64_t)(col0 + 16 * c + (lane & 15)) * a.ldo +
+          if (8 * c + (lane & 7) < rows_valid)
+            hres[i][c] = *reinterpret_cast<const float4*>(a.out + (int64_t)(col0 + 8 * c + (lane & 7)) * a.ldo +
                                                           sub_row[i] + 4 * (lane >> 4));
     }
   }
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
   if constexpr (FMT == FMT_BF16) {
     struct Buf {
       u32x4_t A[UC][RT];
-      bf16x8_t X[UC][NB][2];
+      bf16x8_t X[UC][NB];
     };
     auto load = [&](Buf& f, int st) {
 #pragma unroll
@@ -349,10 +351,7 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
 #pragma unroll
       for (int u = 0; u < UC; ++u)
 #pragma unroll
-        for (int c = 0; c < NB; ++c) {
-          f.X[u][c][0] = load_frag(xr[c] + (st * UC + u) * 512);
-          f.X[u][c][1] = load_frag(xr[c] + a.x_plane + (st * UC + u) * 512);
-        }
+        for (int c = 0; c < NB; ++c) f.X[u][c] = load_frag(xr[c] + (st * UC + u) * 512);
     };
     auto compute = [&](const Buf& f) {
 #pragma unroll
@@ -360,10 +359,7 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
 #pragma unroll
         for (int i = 0; i < RT; ++i)
 #pragma unroll
-          for (int c = 0; c < NB; ++c) {
-            acc[i][c] = mfma(as_frag(f.A[u][i]), f.X[u][c][0], acc[i][c]);
-            acc[i][c] = mfma(as_frag(f.A[u][i]), f.X[u][c][1], acc[i][c]);
-          }
+          for (int c = 0; c < NB; ++c) acc[i][c] = mfma(as_frag(f.A[u][i]), f.X[u][c], acc[i][c]);
     };
     // Every load in the prologue and the steady-state loop is unconditional, so the compiler's
     // load-completion waits stay exact (wait for one buffer while the other is in flight); the
@@ -403,7 +399,7 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
     struct QBuf {
       u32x4_t Wq[RT];
       uint4 SB[RT][2];
-      bf16x8_t X[4][NB][2];
+      bf16x8_t X[4][NB];
     };
     auto qload = [&](QBuf& f, int st) {
 #pragma unroll
@@ -412,10 +408,7 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int c = 0; c < NB; ++c) {
-          f.X[j][c][0] = load_frag(xr[c] + (4 * st + j) * 512);
-          f.X[j][c][1] = load_frag(xr[c] + a.x_plane + (4 * st + j) * 512);
-        }
+        for (int c = 0; c < NB; ++c) f.X[j][c] = load_frag(xr[c] + (4 * st + j) * 512);
     };
     const int total = kw / 128;  // >= 2 (plan)
     QBuf b0, b1;
@@ -472,7 +465,7 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
   float inv[NB];
 #pragma unroll
   for (int c = 0; c < NB; ++c)
-    inv[c] = a.ss ? norm_inv<ROWS>(a, norm_part, 16 * c + (lane & 15), ss_early ? nq : 1) : 1.f;
+    inv[c] = a.ss ? norm_inv<ROWS>(a, norm_part, 8 * c + (lane & 7), ss_early ? nq : 1) : 1.f;
   epilogue<RT, NB, EPI>(a, acc, sub_row, col0, rows_valid, inv, lane, EPI == EPI_RESIDUAL ? &hres : nullptr);
 }
 
@@ -481,15 +474,15 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
 template <int RT, int NB, int EPI, int FMT, int UC>
 __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int ROWS = 16 * NB;
+  constexpr int ROWS = 8 * NB;  // activation rows: NB groups of 8
   constexpr int NACC = RT * NB * 4;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int blk = blockIdx.x, split = blockIdx.y, S = gridDim.y, xblk = blockIdx.z;
   const int K = a.K, Kr = K / S, kbeg = split * Kr, KC = a.kc;
   const int col0 = xblk * ROWS;
   const int rows_valid = min(ROWS, a.rows - col0);
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [plane][NB][KC/32] fragments of 512 elements
-  float* norm_part = reinterpret_cast<float*>(smem + (size_t)2 * NB * KC * 16 * 2);  // [16][ROWS]
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [NB][KC/32] fragments of 512 elements
+  float* norm_part = reinterpret_cast<float*>(smem + (size_t)NB * KC * 32);  // [16][ROWS]
   __shared__ int s_last;
 
   // workgroup tile = 4 waves x RT subtiles (SwiGLU: 64 features, gate and up rows per wave)
@@ -505,24 +498,21 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // stage activation chunk [kc0, kc0 + KC): whole fragments of the valid column tiles
+  // stage activation chunk [kc0, kc0 + KC): whole fragments of the valid 8-row groups
   const int kfc = KC >> 5;
-  const int valid_tiles = (rows_valid + 15) >> 4;
+  const int valid_groups = (rows_valid + 7) >> 3;
   auto stage_x = [&](int kc0) {
     __syncthreads();  // the previous chunk has been consumed
-    const int per_tile = kfc * 64;  // 16-byte words of one plane of one column tile
-    for (int idx = threadIdx.x; idx < 2 * valid_tiles * per_tile; idx += 256) {
-      const int plane = idx / (valid_tiles * per_tile);
-      const int rem = idx - plane * valid_tiles * per_tile;
-      const int c = rem / per_tile, w = rem - c * per_tile;
-      if (16 * c + (w & 15) >= rows_valid) continue;  // word w holds row w%16 of its fragment
-      const uint16_t* src = a.x + (int64_t)plane * a.x_plane +
-                            ((int64_t)((col0 >> 4) + c) * (K >> 5) + (kc0 >> 5)) * 512 + 8 * w;
-      *reinterpret_cast<uint4*>(xs + ((plane * NB + c) * kfc) * 512 + 8 * w) = *reinterpret_cast<const uint4*>(src);
+    const int per_group = kfc * 64;  // 16-byte words of one group's chunk
+    for (int idx = threadIdx.x; idx < valid_groups * per_group; idx += 256) {
+      const int c = idx / per_group, w = idx - c * per_group;
+      if (8 * c + (w & 7) >= rows_valid) continue;  // word w holds row w%8 of its fragment
+      const uint16_t* src = a.x + ((int64_t)((col0 >> 3) + c) * (K >> 5) + (kc0 >> 5)) * 512 + 8 * w;
+      *reinterpret_cast<uint4*>(xs + (c * kfc) * 512 + 8 * w) = *reinterpret_cast<const uint4*>(src);
     }
     __syncthreads();
   };
-  auto xlds = [&](int plane, int c, int kf) { return load_frag(xs + ((plane * NB + c) * kfc + kf) * 512 + 8 * lane); };
+  auto xlds = [&](int c, int kf) { return load_frag(xs + (c * kfc + kf) * 512 + 8 * lane); };
 
   if constexpr (FMT == FMT_BF16) {
     const int spc = KC / (32 * UC), total = Kr / (32 * UC);
@@ -540,12 +530,9 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
       for (int u = 0; u < UC; ++u)
 #pragma unroll
         for (int c = 0; c < NB; ++c) {
-          const bf16x8_t xh = xlds(0, c, kf0 + u), xl = xlds(1, c, kf0 + u);
+          const bf16x8_t x = xlds(c, kf0 + u);
 #pragma unroll
-          for (int i = 0; i < RT; ++i) {
-            acc[i][c] = mfma(as_frag(A[u][i]), xh, acc[i][c]);
-            acc[i][c] = mfma(as_frag(A[u][i]), xl, acc[i][c]);
-          }
+          for (int i = 0; i < RT; ++i) acc[i][c] = mfma(as_frag(A[u][i]), x, acc[i][c]);
         }
     };
     loadw(A0, 0);
@@ -566,7 +553,7 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
       if (st % spc == 0) stage_x(kbeg + (st / spc) * KC);
       u32x4_t Wq[RT];
       uint4 SB[RT][2];
-      bf16x8_t X[4][NB][2];
+      bf16x8_t X[4][NB];
 #pragma unroll
       for (int i = 0; i < RT; ++i) Wq[i] = load_stream(reinterpret_cast<const uint32_t*>(wr[i]) + (int64_t)st * 256);
       load_scales<RT>(a, sub_row, kbeg + st * 128, lane >> 4, SB);
@@ -574,10 +561,7 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int c = 0; c < NB; ++c) {
-          X[j][c][0] = xlds(0, c, kf0 + j);
-          X[j][c][1] = xlds(1, c, kf0 + j);
-        }
+        for (int c = 0; c < NB; ++c) X[j][c] = xlds(c, kf0 + j);
       int4_block<RT, NB>(acc, Wq, SB, X);
     }
   }
@@ -622,19 +606,19 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
     __syncthreads();
   }
 #pragma unroll
-  for (int c = 0; c < NB; ++c) inv[c] = a.ss ? norm_inv<ROWS>(a, norm_part, 16 * c + (lane & 15), 1) : 1.f;
+  for (int c = 0; c < NB; ++c) inv[c] = a.ss ? norm_inv<ROWS>(a, norm_part, 8 * c + (lane & 7), 1) : 1.f;
   epilogue<RT, NB, EPI>(a, acc, sub_row, col0, rows_valid, inv, lane, nullptr);
 }
 
 // ============================================================================ dense tiles
 
-// Many activation rows (prefill): 128 weight rows x 128 activation rows per workgroup, 2 x 2 waves of
-// 64 x 64. Each stage stages one 32-input fragment column of both operands in LDS (the fragments are
+// Many activation rows (prefill): 128 weight rows x 128 activation rows per workgroup, 2 x 4 waves of
+// 64 x 32. Each stage stages one 32-input fragment column of both operands in LDS (the fragments are
 // already MFMA operands: a copy), double-buffered with one barrier per stage. SwiGLU tiles hold 64
 // gate rows and the matching 64 up rows. bf16 weights only.
 namespace {
 constexpr int kDenseTileN = 128, kDenseTileM = 128;
-constexpr int kDenseStageElems = (8 + 16) * 512;  // 8 weight fragments + 8 row tiles x 2 planes
+constexpr int kDenseStageElems = (8 + 16) * 512;  // 8 weight fragments + 16 activation groups
 
 // weight row of subtile f (0..7) of the workgroup's tile
 template <int EPI>
@@ -645,13 +629,13 @@ CBD_DEVICE int dense_row(const SkinnyArgs& a, int n0, int f) {
 }  // namespace
 
 template <int EPI>
-__global__ __launch_bounds__(256) void dense_gemm_kernel(SkinnyArgs a, int tiles_n) {
+__global__ __launch_bounds__(512) void dense_gemm_kernel(SkinnyArgs a, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int RT = 4, NB = 4;
+  constexpr int RT = 4, NB = 4;  // a wave: 4 weight subtiles x 4 activation groups (64 x 32)
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);  // 2 stages of kDenseStageElems
   float* inv_s = reinterpret_cast<float*>(smem + 2 * kDenseStageElems * 2);  // [128]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave & 1, wm = wave >> 1;  // 2 x 4 waves
   // XCD-aware tile order: workgroups go to the 8 XCDs round-robin, so the ones an XCD runs together
   // (ids x, x + 8, x + 16, ...) get one 8 x 8 block of tiles and reuse its weight and activation
   // fragments from that XCD's L2. Ids that fall outside the tile grid return.
@@ -665,39 +649,39 @@ __global__ __launch_bounds__(256) void dense_gemm_kernel(SkinnyArgs a, int tiles
   const int m0 = tm * kDenseTileM;
   const int K = a.K, nk = K >> 5;
 
-  // this thread's 6 fragment copies per stage: fragment f = wave + 4 i (0..7 weights, 8..23 activations)
-  const uint16_t* src[6];
+  // this thread's 3 fragment copies per stage: fragment f = wave + 8 i (0..7 weights, 8..23 the
+  // 16 activation groups of the tile)
+  const uint16_t* src[3];
 #pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const int f = wave + 4 * i;
+  for (int i = 0; i < 3; ++i) {
+    const int f = wave + 8 * i;
     if (f < 8) {
       const int grow = dense_row<EPI>(a, n0, f);
       const int sg = seg_of(a, grow);
       const int tr = (grow - seg_begin(a, sg)) >> 4;
       src[i] = reinterpret_cast<const uint16_t*>(a.w[sg]) + (int64_t)tr * nk * 512 + 8 * lane;
     } else {
-      const int plane = (f - 8) >> 3, c = (f - 8) & 7;
-      src[i] = a.x + plane * a.x_plane + (int64_t)((m0 >> 4) + c) * nk * 512 + 8 * lane;
+      src[i] = a.x + (int64_t)((m0 >> 3) + (f - 8)) * nk * 512 + 8 * lane;
     }
   }
   // global -> registers -> LDS; two register sets keep the loads of the next two stages in flight
-  auto fetch = [&](u32x4_t (&r)[6], int kf) {  // cached loads: other tiles of the block reuse them
+  auto fetch = [&](u32x4_t (&r)[3], int kf) {  // cached loads: other tiles of the block reuse them
 #pragma unroll
-    for (int i = 0; i < 6; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(src[i] + (int64_t)kf * 512);
+    for (int i = 0; i < 3; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(src[i] + (int64_t)kf * 512);
   };
-  auto put = [&](const u32x4_t (&r)[6], int buf) {  // a fragment is a 1 KB copy
+  auto put = [&](const u32x4_t (&r)[3], int buf) {  // a fragment is a 1 KB copy
 #pragma unroll
-    for (int i = 0; i < 6; ++i)
-      *reinterpret_cast<u32x4_t*>(lds + buf * kDenseStageElems + (wave + 4 * i) * 512 + 8 * lane) = r[i];
+    for (int i = 0; i < 3; ++i)
+      *reinterpret_cast<u32x4_t*>(lds + buf * kDenseStageElems + (wave + 8 * i) * 512 + 8 * lane) = r[i];
   };
-  u32x4_t r0[6], r1[6];
+  u32x4_t r0[3], r1[3];
 
   // 1/rms of the tile's rows, added in the same fixed order as the other kernels (16 groups)
   fetch(r0, 0);
   if (a.ss) {
     float* part = reinterpret_cast<float*>(lds + kDenseStageElems);  // [16][128], stage 1 is free here
     const int per = a.ss_tiles / 16;
-    for (int i = tid; i < 16 * kDenseTileM; i += 256) {
+    for (int i = tid; i < 16 * kDenseTileM; i += 512) {
       const int r = i % kDenseTileM, grp = i / kDenseTileM;
       float sum = 0.f;
       if (m0 + r < a.rows) {
@@ -724,7 +708,7 @@ __global__ __launch_bounds__(256) void dense_gemm_kernel(SkinnyArgs a, int tiles
   for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // LDS fragments of this wave: weights (4 subtiles), activations (4 row tiles x 2 planes)
+  // LDS fragments of this wave: weights (4 subtiles), activations (4 groups of 8 rows)
   int fa[RT];
 #pragma unroll
   for (int i = 0; i < RT; ++i) {
@@ -733,21 +717,15 @@ __global__ __launch_bounds__(256) void dense_gemm_kernel(SkinnyArgs a, int tiles
   }
   auto compute = [&](int buf) {
     const uint16_t* st = lds + buf * kDenseStageElems;
-    bf16x8_t A[RT], X[NB][2];
+    bf16x8_t A[RT], X[NB];
 #pragma unroll
     for (int i = 0; i < RT; ++i) A[i] = *reinterpret_cast<const bf16x8_t*>(st + fa[i] * 512 + 8 * lane);
 #pragma unroll
-    for (int c = 0; c < NB; ++c)
-#pragma unroll
-      for (int pl = 0; pl < 2; ++pl)
-        X[c][pl] = *reinterpret_cast<const bf16x8_t*>(st + (8 + pl * 8 + 4 * wm + c) * 512 + 8 * lane);
+    for (int c = 0; c < NB; ++c) X[c] = *reinterpret_cast<const bf16x8_t*>(st + (8 + 4 * wm + c) * 512 + 8 * lane);
 #pragma unroll
     for (int i = 0; i < RT; ++i)
 #pragma unroll
-      for (int c = 0; c < NB; ++c) {
-        acc[i][c] = mfma(A[i], X[c][0], acc[i][c]);
-        acc[i][c] = mfma(A[i], X[c][1], acc[i][c]);
-      }
+      for (int c = 0; c < NB; ++c) acc[i][c] = mfma(A[i], X[c], acc[i][c]);
   };
   // stage kf is in LDS buffer kf & 1; the register set of stage kf + 1 is put after computing kf.
   // nk is even (K % 64 == 0), so the loop body has no branch and the load waits stay exact.
@@ -765,12 +743,12 @@ __global__ __launch_bounds__(256) void dense_gemm_kernel(SkinnyArgs a, int tiles
   int sub_row[RT];
 #pragma unroll
   for (int i = 0; i < RT; ++i) sub_row[i] = dense_row<EPI>(a, n0, fa[i]);
-  const int col0 = m0 + 64 * wm;
-  const int rows_valid = min(64, a.rows - col0);
+  const int col0 = m0 + 32 * wm;
+  const int rows_valid = min(32, a.rows - col0);
   if (rows_valid <= 0) return;
   float inv[NB];
 #pragma unroll
-  for (int c = 0; c < NB; ++c) inv[c] = a.ss ? inv_s[64 * wm + 16 * c + (lane & 15)] : 1.f;
+  for (int c = 0; c < NB; ++c) inv[c] = a.ss ? inv_s[32 * wm + 8 * c + (lane & 7)] : 1.f;
   epilogue<RT, NB, EPI>(a, acc, sub_row, col0, rows_valid, inv, lane, nullptr);
 }
 
@@ -800,10 +778,10 @@ hipError_t launch_pack_bf16(const uint16_t* src, int64_t N, int64_t K, uint16_t*
 
 bool skinny_shape_ok(int fmt, int K) { return fmt == FMT_INT4 ? K % 512 == 0 : K % 256 == 0; }
 
-static size_t rowsplit_lds(int nb, int kc) { return (size_t)2 * nb * kc * 16 * 2 + (size_t)16 * 16 * nb * 4; }
+static size_t rowsplit_lds(int nb, int kc) { return (size_t)nb * kc * 32 + (size_t)16 * 8 * nb * 4; }
 static size_t ksplit_lds(int nw, int rt, int nb) {
   // reduction slots, then up to max(threads, 16 * rows) norm partials
-  return (size_t)(nw - 1) * rt * nb * 4 * 64 * 4 + (size_t)std::max(64 * nw, 16 * 16 * nb) * 4;
+  return (size_t)(nw - 1) * rt * nb * 4 * 64 * 4 + (size_t)std::max(64 * nw, 16 * 8 * nb) * 4;
 }
 
 #ifndef CBD_KS_MAX_UC
@@ -831,7 +809,8 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
     return p;
   }
   const int per_block = x_blocks > 1 ? 64 : rows;
-  p.nb = (per_block + 15) / 16;
+  const int groups = (per_block + 7) / 8;  // 8-row groups, rounded up to 1, 2, 4 or 8
+  p.nb = groups <= 1 ? 1 : groups <= 2 ? 2 : groups <= 4 ? 4 : 8;
   const int step = fmt == FMT_INT4 ? 128 : 32;
   // k split: one 16*rt-row tile per workgroup, enough waves to cover the chip
   // int4 stages carry 8x more activation bytes than weight bytes per subtile: a wave takes two
@@ -839,10 +818,10 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
   const int ks_rt = (epi == EPI_SWIGLU || fmt == FMT_INT4) ? 2 : 1;
   const int ks_tiles = epi == EPI_SWIGLU ? N / (8 * ks_rt) : N / (16 * ks_rt);
   int ks_uc = fmt == FMT_INT4 ? 1 : (K % (4 * 128) == 0 ? 4 : (K % (4 * 64) == 0 ? 2 : 1));
-  ks_uc = std::min(ks_uc, CBD_KS_MAX_UC);
+  ks_uc = std::min(ks_uc, p.nb >= 4 ? 2 : CBD_KS_MAX_UC);  // four groups: two stages' worth of registers
   const int ks_unit = step * ks_uc;
   const int ks_maxw = (ks_rt == 1 && p.nb == 1) ? 16 : 8;
-  const bool ks_ok = x_blocks == 1 && p.nb <= (fmt == FMT_INT4 ? 1 : 2) && K % (4 * ks_unit) == 0 &&
+  const bool ks_ok = x_blocks == 1 && p.nb <= (fmt == FMT_INT4 ? 1 : 4) && K % (4 * ks_unit) == 0 &&
                      (epi == EPI_SWIGLU ? N % (8 * ks_rt) == 0 : N % (16 * ks_rt) == 0);
   // row split: 4 waves x rt subtiles
   const int rs_rt = (epi == EPI_SWIGLU || N % 128 == 0) ? 2 : 1;
@@ -877,7 +856,7 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
   p.uc = fmt == FMT_INT4 ? 1 : (p.nb > 2 ? 2 : 4);
   p.waves = 4;
   const int unit = step * p.uc;
-  const int kc_max = std::max(unit, (1024 / p.nb) / unit * unit);  // activation chunk: LDS <= 64 KB
+  const int kc_max = std::max(unit, (2048 / p.nb) / unit * unit);  // activation chunk: LDS <= 64 KB
   if (force > 0) {
     p.splits = force;
   } else if (x_blocks > 1) {
@@ -901,15 +880,16 @@ template <int RT, int EPI, int FMT, int UC>
 static hipError_t launch_rs(const SkinnyArgs& a, const SkinnyPlan& p, int x_blocks, hipStream_t st) {
   const dim3 grid(p.row_blocks, p.splits, x_blocks);
   const size_t lds = rowsplit_lds(p.nb, p.kc);
-  switch (p.nb) {
+  switch (p.nb) {  // 8-row groups: 1, 2, 4 or 8 (the plan rounds up)
     case 1: launch_kernel((rowsplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
     case 2: launch_kernel((rowsplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(256), lds, st, a); break;
-    case 3:
-      launch_kernel((rowsplit_gemm_kernel<RT, 3, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(256), lds, st, a);
-      break;
-    default:
+    case 4:
       launch_kernel((rowsplit_gemm_kernel<RT, 4, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(256), lds, st, a);
       break;
+    case 8:
+      launch_kernel((rowsplit_gemm_kernel<RT, 8, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(256), lds, st, a);
+      break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -917,16 +897,21 @@ static hipError_t launch_rs(const SkinnyArgs& a, const SkinnyPlan& p, int x_bloc
 template <int RT, int EPI, int FMT, int UC>
 static hipError_t launch_ks(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t st) {
   const dim3 grid(p.row_blocks, 1);
-  if constexpr (FMT == FMT_INT4) {  // one column tile only (the plan never asks for more)
+  if constexpr (FMT == FMT_INT4) {  // one 8-row group (the plan never asks for more)
     if (p.nb != 1) return hipErrorInvalidValue;
     launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
                   st, a);
   } else if (p.nb == 1) {
     launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
                   st, a);
-  } else {
+  } else if (p.nb == 2) {
     launch_kernel((ksplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 2),
                   st, a);
+  } else if (p.nb == 4) {
+    launch_kernel((ksplit_gemm_kernel<RT, 4, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(64 * p.waves),
+                  ksplit_lds(p.waves, RT, 4), st, a);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -966,13 +951,13 @@ hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, cons
     const dim3 grid(((supers + 7) / 8) * 8 * 64);
     const size_t lds = (size_t)2 * kDenseStageElems * 2 + kDenseTileM * 4;
     const int tn = p.row_blocks;
-    if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU>), grid, dim3(256), lds, st, a, tn);
-    else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL>), grid, dim3(256), lds, st, a, tn);
-    else launch_kernel((dense_gemm_kernel<EPI_STORE>), grid, dim3(256), lds, st, a, tn);
+    if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU>), grid, dim3(512), lds, st, a, tn);
+    else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL>), grid, dim3(512), lds, st, a, tn);
+    else launch_kernel((dense_gemm_kernel<EPI_STORE>), grid, dim3(512), lds, st, a, tn);
     return hipGetLastError();
   }
   if (p.kind == 1) {
-    if (x_blocks != 1 || p.nb > 2 || p.waves < 1 || p.waves > 16 || a.K % p.waves ||
+    if (x_blocks != 1 || p.nb > 4 || p.waves < 1 || p.waves > 16 || a.K % p.waves ||
         (a.K / p.waves) % (step * p.uc) || (p.waves > 8 && (p.rt != 1 || p.nb != 1)) ||
         a.K / p.waves < 2 * step * p.uc)
       return hipErrorInvalidValue;

@@ -388,9 +388,10 @@ static cbd_status setup_device(cbd_ctx* c) {
   c->argmax_part = align_ptr<float>(p, (size_t)64 * kArgmaxSegments * 2);
   c->argmax_counters = align_ptr<int32_t>(p, 64);
   c->qkv = align_ptr<float>(p, R * c->qkv_dim);
-  c->xa_plane = (int64_t)R * m.d_model;
-  c->xo_plane = (int64_t)R * c->q_dim;
-  c->xm_plane = (int64_t)R * wm;
+  // the lo value of an activation pair sits kXLo elements after its hi value (common.h)
+  c->xa_plane = kXLo;
+  c->xo_plane = kXLo;
+  c->xm_plane = kXLo;
   c->part_o = align_ptr<float>(p, (size_t)kMaxParts * G * m.head_dim);
   c->part_ml = align_ptr<float>(p, (size_t)kMaxParts * G * 2);
   c->rope_cs = align_ptr<float>(p, (size_t)m.max_position * half * 2);
