@@ -612,13 +612,18 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
 
 // ============================================================================ dense tiles
 
-// Many activation rows (prefill): 128 weight rows x 128 activation rows per workgroup, 2 x 4 waves of
-// 64 x 32. Each stage stages one 32-input fragment column of both operands in LDS (the fragments are
-// already MFMA operands: a copy), double-buffered with one barrier per stage. SwiGLU tiles hold 64
-// gate rows and the matching 64 up rows. bf16 weights only.
+
+// Many activation rows: 128 weight rows x 32*WM activation rows per workgroup, 2 x WM waves of
+// 64 x 32 (WM = 4 for prefill, 2 for decode steps of 33..64 rows). Each stage copies one 32-input
+// fragment column of both operands to LDS (the fragments are already MFMA operands), double-buffered
+// with one barrier per stage and two stages of loads in flight. SwiGLU tiles hold 64 gate rows and
+// the matching 64 up rows. bf16 weights only. With splits > 1 (one row tile), workgroup (tile, s)
+// adds the inputs [s K/splits, (s + 1) K/splits); the last workgroup of a tile to arrive adds the
+// partial tiles in order (agent-scope 16-byte accesses and an arrival counter, as the row split).
 namespace {
-constexpr int kDenseTileN = 128, kDenseTileM = 128;
-constexpr int kDenseStageElems = (8 + 16) * 512;  // 8 weight fragments + 16 activation groups
+constexpr int kDenseTileN = 128;
+// LDS of a dense workgroup with 2 x wm waves: two stages of (8 + 4 wm) fragments, 1/rms per row
+inline size_t dense_lds(int wm) { return (size_t)2 * (8 + 4 * wm) * 512 * 2 + 32 * wm * 4; }
 
 // weight row of subtile f (0..7) of the workgroup's tile
 template <int EPI>
@@ -628,80 +633,99 @@ CBD_DEVICE int dense_row(const SkinnyArgs& a, int n0, int f) {
 }
 }  // namespace
 
-template <int EPI>
-__global__ __launch_bounds__(512) void dense_gemm_kernel(SkinnyArgs a, int tiles_n) {
+template <int EPI, int WM, int D>
+__global__ __launch_bounds__(128 * WM, WM == 2 ? 3 : 1) void dense_gemm_kernel(SkinnyArgs a, int tiles_n,
+                                                                                           int splits) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int RT = 4, NB = 4;  // a wave: 4 weight subtiles x 4 activation groups (64 x 32)
-  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);  // 2 stages of kDenseStageElems
-  float* inv_s = reinterpret_cast<float*>(smem + 2 * kDenseStageElems * 2);  // [128]
+  constexpr int RT = 4, NB = 4;            // a wave: 4 weight subtiles x 4 activation groups (64 x 32)
+  constexpr int TM = 32 * WM;              // activation rows of the tile
+  constexpr int FR = 8 + TM / 8;           // fragments per stage: 8 weight subtiles + TM/8 groups
+  constexpr int NTH = 128 * WM, PER = FR / (2 * WM);  // threads; fragment copies per thread and stage
+  static_assert(FR % (2 * WM) == 0, "fragments per stage split evenly over the waves");
+  constexpr int STAGE = FR * 512;          // elements of one LDS stage
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);  // 2 stages
+  float* inv_s = reinterpret_cast<float*>(smem + 2 * STAGE * 2);  // [TM]
+  __shared__ int s_last;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wn = wave & 1, wm = wave >> 1;  // 2 x 4 waves
-  // XCD-aware tile order: workgroups go to the 8 XCDs round-robin, so the ones an XCD runs together
-  // (ids x, x + 8, x + 16, ...) get one 8 x 8 block of tiles and reuse its weight and activation
-  // fragments from that XCD's L2. Ids that fall outside the tile grid return.
-  const int tiles_m = (a.rows + kDenseTileM - 1) / kDenseTileM;
-  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int super = (j >> 6) * 8 + xcd, r = j & 63;
-  const int super_n = (tiles_n + 7) >> 3;
-  const int tn = (super % super_n) * 8 + (r & 7), tm = (super / super_n) * 8 + (r >> 3);
-  if (tn >= tiles_n || tm >= tiles_m) return;
+  const int wn = wave & 1, wm = wave >> 1;  // 2 x WM waves
+  const int tiles_m = (a.rows + TM - 1) / TM;
+  int tn, tm, split = 0;
+  if (splits == 1) {
+    // XCD-aware tile order: workgroups go to the 8 XCDs round-robin, so the ones an XCD runs together
+    // (ids x, x + 8, x + 16, ...) get one 8 x 8 block of tiles and reuse its weight and activation
+    // fragments from that XCD's L2. Ids that fall outside the tile grid return.
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int super = (j >> 6) * 8 + xcd, r = j & 63;
+    const int super_n = (tiles_n + 7) >> 3;
+    tn = (super % super_n) * 8 + (r & 7);
+    tm = (super / super_n) * 8 + (r >> 3);
+    if (tn >= tiles_n || tm >= tiles_m) return;
+  } else {
+    tn = blockIdx.x / splits;
+    split = blockIdx.x - tn * splits;
+    tm = 0;
+  }
   const int n0 = tn * (EPI == EPI_SWIGLU ? kDenseTileN / 2 : kDenseTileN);
-  const int m0 = tm * kDenseTileM;
-  const int K = a.K, nk = K >> 5;
+  const int m0 = tm * TM;
+  const int K = a.K, nk_all = K >> 5, nk = nk_all / splits, kf0 = split * nk;
 
-  // this thread's 3 fragment copies per stage: fragment f = wave + 8 i (0..7 weights, 8..23 the
-  // 16 activation groups of the tile)
-  const uint16_t* src[3];
+  // this thread's fragment copies per stage: f = wave + 2 WM i (0..7 weights, then activation groups)
+  const uint16_t* src[PER];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int f = wave + 8 * i;
+  for (int i = 0; i < PER; ++i) {
+    const int f = wave + 2 * WM * i;
     if (f < 8) {
       const int grow = dense_row<EPI>(a, n0, f);
       const int sg = seg_of(a, grow);
       const int tr = (grow - seg_begin(a, sg)) >> 4;
-      src[i] = reinterpret_cast<const uint16_t*>(a.w[sg]) + (int64_t)tr * nk * 512 + 8 * lane;
+      src[i] = reinterpret_cast<const uint16_t*>(a.w[sg]) + ((int64_t)tr * nk_all + kf0) * 512 + 8 * lane;
     } else {
-      src[i] = a.x + (int64_t)((m0 >> 3) + (f - 8)) * nk * 512 + 8 * lane;
+      src[i] = a.x + ((int64_t)((m0 >> 3) + (f - 8)) * nk_all + kf0) * 512 + 8 * lane;
     }
   }
-  // global -> registers -> LDS; two register sets keep the loads of the next two stages in flight
-  auto fetch = [&](u32x4_t (&r)[3], int kf) {  // cached loads: other tiles of the block reuse them
+  // global -> registers -> LDS; D register sets keep the loads of the next D stages in flight
+  auto fetch = [&](u32x4_t (&r)[PER], int kf) {  // cached loads: other tiles reuse them
 #pragma unroll
-    for (int i = 0; i < 3; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(src[i] + (int64_t)kf * 512);
+    for (int i = 0; i < PER; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(src[i] + (int64_t)kf * 512);
   };
-  auto put = [&](const u32x4_t (&r)[3], int buf) {  // a fragment is a 1 KB copy
+  auto put = [&](const u32x4_t (&r)[PER], int buf) {  // a fragment is a 1 KB copy
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
-      *reinterpret_cast<u32x4_t*>(lds + buf * kDenseStageElems + (wave + 8 * i) * 512 + 8 * lane) = r[i];
+    for (int i = 0; i < PER; ++i)
+      *reinterpret_cast<u32x4_t*>(lds + buf * STAGE + (wave + 2 * WM * i) * 512 + 8 * lane) = r[i];
   };
-  u32x4_t r0[3], r1[3];
+  u32x4_t rr[D][PER];
 
   // 1/rms of the tile's rows, added in the same fixed order as the other kernels (16 groups)
-  fetch(r0, 0);
+  fetch(rr[0], 0);
   if (a.ss) {
-    float* part = reinterpret_cast<float*>(lds + kDenseStageElems);  // [16][128], stage 1 is free here
+    float* part = reinterpret_cast<float*>(lds + STAGE);  // [16][TM], stage 1 is free here
     const int per = a.ss_tiles / 16;
-    for (int i = tid; i < 16 * kDenseTileM; i += 512) {
-      const int r = i % kDenseTileM, grp = i / kDenseTileM;
+    for (int i = tid; i < 16 * TM; i += NTH) {
+      const int r = i % TM, grp = i / TM;
       float sum = 0.f;
       if (m0 + r < a.rows) {
         const float* q = a.ss + (int64_t)grp * per * a.ss_ld + m0 + r;
         for (int t = 0; t < per; ++t) sum += q[(int64_t)t * a.ss_ld];
       }
-      part[grp * kDenseTileM + r] = sum;
+      part[grp * TM + r] = sum;
     }
     __syncthreads();
-    if (tid < kDenseTileM) {
+    if (tid < TM) {
       float sum = 0.f;
-      for (int grp = 0; grp < 16; ++grp) sum += part[grp * kDenseTileM + tid];
+      for (int grp = 0; grp < 16; ++grp) sum += part[grp * TM + tid];
       inv_s[tid] = 1.0f / sqrtf(sum / a.norm_dim + a.eps);
     }
   }
-  put(r0, 0);
+  put(rr[0], 0);
   __syncthreads();
   // stages past the last refetch the last one (unused): loads stay unconditional
-  fetch(r0, min(1, nk - 1));
-  fetch(r1, min(2, nk - 1));
+  // (scheduling barriers keep the loads in register-set order here and in the loop, so that the
+  // waits at the loop head count the same outstanding loads on entry and on the back edge)
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    fetch(rr[j], min(1 + j, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   f32x4_t acc[RT][NB];
 #pragma unroll
@@ -716,7 +740,7 @@ __global__ __launch_bounds__(512) void dense_gemm_kernel(SkinnyArgs a, int tiles
     else fa[i] = 4 * wn + i;
   }
   auto compute = [&](int buf) {
-    const uint16_t* st = lds + buf * kDenseStageElems;
+    const uint16_t* st = lds + buf * STAGE;
     bf16x8_t A[RT], X[NB];
 #pragma unroll
     for (int i = 0; i < RT; ++i) A[i] = *reinterpret_cast<const bf16x8_t*>(st + fa[i] * 512 + 8 * lane);
@@ -727,17 +751,58 @@ __global__ __launch_bounds__(512) void dense_gemm_kernel(SkinnyArgs a, int tiles
 #pragma unroll
       for (int c = 0; c < NB; ++c) acc[i][c] = mfma(A[i], X[c], acc[i][c]);
   };
-  // stage kf is in LDS buffer kf & 1; the register set of stage kf + 1 is put after computing kf.
-  // nk is even (K % 64 == 0), so the loop body has no branch and the load waits stay exact.
-  for (int kf = 0; kf < nk; kf += 2) {
-    compute(0);
-    put(r0, 1);
+  // stage s is in LDS buffer s & 1; register set s % D holds stage s + 1 and is put after computing
+  // s, then refilled with stage s + 1 + D. nk is a multiple of D (and even), so the loop body has no
+  // branch and the load waits stay exact.
+  for (int kf = 0; kf < nk; kf += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      compute(j & 1);
+      put(rr[j], (j + 1) & 1);
+      __syncthreads();
+      fetch(rr[j], min(kf + j + 1 + D, nk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  if (splits > 1) {
+    // partial tile of (tile, split, wave): hi and lo products added first, then [i][c][32 lanes]
+    // f32x4 from the lanes that hold a low half (16 bytes per lane and subtile); the merged sums go
+    // back to those lanes, zero to the others, so the epilogue's hi + lo addition leaves them as is
+    constexpr int TILE_F = 2 * WM * RT * NB * 32 * 4;  // floats of one workgroup's partial
+    const int64_t base = (int64_t)tn * splits * TILE_F;
+    const int l32 = ((lane >> 4) << 3) | (lane & 7);
+    const bool holder = (lane & 8) == 0;
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        f32x4_t v = acc[i][c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], 8, 64);
+        if (holder)
+          store_agent_x4(a.part, (int)((base + (int64_t)split * TILE_F + ((wave * RT + i) * NB + c) * 128 + l32 * 4) * 4),
+                         v);
+      }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
     __syncthreads();
-    fetch(r0, min(kf + 3, nk - 1));
-    compute(1);
-    put(r1, 0);
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(a.counters + tn, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
     __syncthreads();
-    fetch(r1, min(kf + 4, nk - 1));
+    if (!s_last) return;
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (holder)
+      for (int sp = 0; sp < splits; ++sp)
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+          for (int c = 0; c < NB; ++c)
+            acc[i][c] += load_agent_x4(
+                a.part, (int)((base + (int64_t)sp * TILE_F + ((wave * RT + i) * NB + c) * 128 + l32 * 4) * 4));
+    if (tid == 0) __hip_atomic_store(a.counters + tn, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   int sub_row[RT];
@@ -793,19 +858,45 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
 #ifndef CBD_RS_MIN_BLOCKS
 #define CBD_RS_MIN_BLOCKS 600
 #endif
+#ifndef CBD_KS_MAX_NB
+#define CBD_KS_MAX_NB 4
+#endif
+#ifndef CBD_DENSE_MIN_ROWS
+#define CBD_DENSE_MIN_ROWS 32
+#endif
+#ifndef CBD_DENSE_WG_TARGET
+#define CBD_DENSE_WG_TARGET 768
+#endif
+#ifndef CBD_DENSE_MAX_SPLITS
+#define CBD_DENSE_MAX_SPLITS 8
+#endif
+#ifndef CBD_DENSE_MIN_SPLIT_K
+#define CBD_DENSE_MIN_SPLIT_K 1024
+#endif
 
 SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int force) {
   SkinnyPlan p{};
-  // dense tiles for many activation rows (bf16 weights; N in whole tiles)
-  if (force == 0 && x_blocks > 1 && fmt == FMT_BF16 && K % 64 == 0 &&
+  // dense tiles for many activation rows (bf16 weights; N in whole tiles): 128-row activation
+  // tiles for prefill; one 64-row tile, K split over workgroups to fill the chip, for decode steps
+  // of more than CBD_DENSE_MIN_ROWS rows
+  if (force == 0 && fmt == FMT_BF16 && K % 64 == 0 && (x_blocks > 1 || rows > CBD_DENSE_MIN_ROWS) &&
       (epi == EPI_SWIGLU ? N % (kDenseTileN / 2) == 0 : N % kDenseTileN == 0)) {
     p.kind = 2;
     p.rt = 4;
     p.nb = 4;
     p.uc = 1;
-    p.splits = 1;
-    p.waves = 4;
     p.row_blocks = epi == EPI_SWIGLU ? N / (kDenseTileN / 2) : N / kDenseTileN;
+    p.splits = 1;
+    if (x_blocks > 1) {
+      p.waves = 8;
+    } else {
+      p.waves = 4;
+      // most splits keeping at most CBD_DENSE_WG_TARGET workgroups and CBD_DENSE_MIN_SPLIT_K inputs
+      // per split: every split adds a 32 KB partial tile that one workgroup reads back at the end
+      for (int s = 2; s <= CBD_DENSE_MAX_SPLITS; ++s)
+        if (K % (64 * s) == 0 && K / s >= CBD_DENSE_MIN_SPLIT_K && (long)p.row_blocks * s <= CBD_DENSE_WG_TARGET)
+          p.splits = s;
+    }
     return p;
   }
   const int per_block = x_blocks > 1 ? 64 : rows;
@@ -818,10 +909,10 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
   const int ks_rt = (epi == EPI_SWIGLU || fmt == FMT_INT4) ? 2 : 1;
   const int ks_tiles = epi == EPI_SWIGLU ? N / (8 * ks_rt) : N / (16 * ks_rt);
   int ks_uc = fmt == FMT_INT4 ? 1 : (K % (4 * 128) == 0 ? 4 : (K % (4 * 64) == 0 ? 2 : 1));
-  ks_uc = std::min(ks_uc, p.nb >= 4 ? 2 : CBD_KS_MAX_UC);  // four groups: two stages' worth of registers
+  ks_uc = std::min(ks_uc, p.nb >= 8 ? 1 : p.nb >= 4 ? 2 : CBD_KS_MAX_UC);  // registers for the stages
   const int ks_unit = step * ks_uc;
   const int ks_maxw = (ks_rt == 1 && p.nb == 1) ? 16 : 8;
-  const bool ks_ok = x_blocks == 1 && p.nb <= (fmt == FMT_INT4 ? 1 : 4) && K % (4 * ks_unit) == 0 &&
+  const bool ks_ok = x_blocks == 1 && p.nb <= (fmt == FMT_INT4 ? 1 : CBD_KS_MAX_NB) && K % (4 * ks_unit) == 0 &&
                      (epi == EPI_SWIGLU ? N % (8 * ks_rt) == 0 : N % (16 * ks_rt) == 0);
   // row split: 4 waves x rt subtiles
   const int rs_rt = (epi == EPI_SWIGLU || N % 128 == 0) ? 2 : 1;
@@ -910,6 +1001,9 @@ static hipError_t launch_ks(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_
   } else if (p.nb == 4) {
     launch_kernel((ksplit_gemm_kernel<RT, 4, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(64 * p.waves),
                   ksplit_lds(p.waves, RT, 4), st, a);
+  } else if (p.nb == 8) {
+    launch_kernel((ksplit_gemm_kernel<RT, 8, EPI, FMT, 1>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 8),
+                  st, a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -944,20 +1038,36 @@ static hipError_t dispatch(const SkinnyArgs& a, int fmt, int x_blocks, const Ski
 hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st) {
   const int step = fmt == FMT_INT4 ? 128 : 32;
   if (p.kind == 2) {
-    if (fmt != FMT_BF16 || a.K % 64 || a.rows < 1 || p.row_blocks < 1) return hipErrorInvalidValue;
-    // linear ids over 8 x 8 blocks of (N tile, M tile), a whole number of blocks per XCD
-    const int tiles_m = (a.rows + kDenseTileM - 1) / kDenseTileM;
-    const int supers = ((p.row_blocks + 7) / 8) * ((tiles_m + 7) / 8);
-    const dim3 grid(((supers + 7) / 8) * 8 * 64);
-    const size_t lds = (size_t)2 * kDenseStageElems * 2 + kDenseTileM * 4;
-    const int tn = p.row_blocks;
-    if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU>), grid, dim3(512), lds, st, a, tn);
-    else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL>), grid, dim3(512), lds, st, a, tn);
-    else launch_kernel((dense_gemm_kernel<EPI_STORE>), grid, dim3(512), lds, st, a, tn);
+    // 2 x WM waves; 128 weight rows x 32 WM activation rows per tile
+    const int wm = p.waves / 2, tm_rows = 32 * wm;
+    if (fmt != FMT_BF16 || a.rows < 1 || p.row_blocks < 1 || (wm != 2 && wm != 4) || p.splits < 1 ||
+        a.K % (64 * p.splits) ||
+        (p.splits > 1 && (x_blocks > 1 || a.rows > tm_rows || !a.part || !a.counters)))
+      return hipErrorInvalidValue;
+    const int tiles_m = (a.rows + tm_rows - 1) / tm_rows;
+    dim3 grid;
+    if (p.splits > 1) {
+      grid = dim3(p.row_blocks * p.splits);  // (tile, split) = (id / splits, id % splits)
+    } else {
+      // linear ids over 8 x 8 blocks of (N tile, M tile), a whole number of blocks per XCD
+      const int supers = ((p.row_blocks + 7) / 8) * ((tiles_m + 7) / 8);
+      grid = dim3(((supers + 7) / 8) * 8 * 64);
+    }
+    const size_t lds = dense_lds(wm);
+    const int tn = p.row_blocks, sp = p.splits;
+    if (wm == 4) {
+      if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU, 4, 2>), grid, dim3(512), lds, st, a, tn, sp);
+      else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL, 4, 2>), grid, dim3(512), lds, st, a, tn, sp);
+      else launch_kernel((dense_gemm_kernel<EPI_STORE, 4, 2>), grid, dim3(512), lds, st, a, tn, sp);
+    } else {
+      if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU, 2, 2>), grid, dim3(256), lds, st, a, tn, sp);
+      else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL, 2, 2>), grid, dim3(256), lds, st, a, tn, sp);
+      else launch_kernel((dense_gemm_kernel<EPI_STORE, 2, 2>), grid, dim3(256), lds, st, a, tn, sp);
+    }
     return hipGetLastError();
   }
   if (p.kind == 1) {
-    if (x_blocks != 1 || p.nb > 4 || p.waves < 1 || p.waves > 16 || a.K % p.waves ||
+    if (x_blocks != 1 || p.nb > 8 || p.waves < 1 || p.waves > 16 || a.K % p.waves ||
         (a.K / p.waves) % (step * p.uc) || (p.waves > 8 && (p.rt != 1 || p.nb != 1)) ||
         a.K / p.waves < 2 * step * p.uc)
       return hipErrorInvalidValue;

@@ -349,7 +349,7 @@ static cbd_status setup_device(cbd_ctx* c) {
     const int shapes[][3] = {{EPI_STORE, c->qkv_dim, m.d_model},  {EPI_RESIDUAL, m.d_model, c->q_dim},
                              {EPI_SWIGLU, m.ffn_dim, m.d_model},  {EPI_RESIDUAL, m.d_model, m.ffn_dim},
                              {EPI_STORE, m.vocab, m.d_model}};
-    for (int rows = 1; rows <= 64; rows += 16)
+    for (int rows = 1; rows <= 64; ++rows)
       for (const auto& sh : shapes) {
         const SkinnyPlan pl = plan_skinny(sh[0], c->fmt, sh[1], sh[2], rows, 1, 0);
         c->gemm_part_bytes = std::max(c->gemm_part_bytes, skinny_part_bytes(pl));

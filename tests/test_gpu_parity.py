@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_common import MID, MID_INT4, assert_logits_close, check_greedy, compare_slab_bits
+from gpu_common import MID, MID_INT4, WIDE, assert_logits_close, check_greedy, compare_slab_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -311,6 +311,47 @@ def test_ragged_long_history_decode(torch, cbd):
     assert_logits_close(solo.cpu().numpy(), logits.cpu().numpy()[5:6], "batched vs solo")
     eng.close()
     eng2.close()
+
+
+@pytest.mark.parametrize("B,shape", [(40, MID), (64, MID), (64, WIDE)], ids=["mid-40", "mid-64", "wide-64"])
+def test_wide_batch_decode(torch, cbd, B, shape):
+    """Decode steps of 33..64 rows (dense projection tiles; K split over workgroups for the wide
+    shape): ragged seeded histories, 2 teacher-forced steps, logits, greedy ids and appended K/V
+    against the oracle."""
+    _say("wide batch decode B=%d %s" % (B, shape.name))
+    from oracle import OracleModel, greedy
+    w = synth.make_weights(shape, seed=21, gain_std=0.1)
+    ctx = [int(n) for n in synth.uniform_lengths(22 + B, B, 0, 700)]
+    gran = cbd.lib().cbd_slab_granule_tokens()
+    arena = sum((n + 4 + gran - 1) // gran * gran for n in ctx) * shape.kv_bytes_per_token()
+    eng = cbd.Engine(w, arena_bytes=arena, max_batch=64, max_prefill_tokens=64, max_position=1024)
+    orc = OracleModel(w)
+    ids, oids = [], []
+    for r, n in enumerate(ctx):
+        i = eng.alloc(n + 4)
+        o = orc.new_sequence()
+        if n:
+            k, v = synth.kv_history(shape, 23, r, n)
+            eng.append(i, to_dev_bits(torch, k), to_dev_bits(torch, v))
+            orc.append_history(o, k, v)
+        ids.append(i)
+        oids.append(o)
+    tok = synth.prompts(24, [B], shape.vocab)[0].astype(np.int64)
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    for step in range(2):
+        eng.decode_step_batch(ids, torch.from_numpy(tok.astype(np.int32)).cuda(), logits, nxt)
+        ref = orc.decode_step_batch(oids, tok)
+        torch.cuda.synchronize()
+        errs = assert_logits_close(logits.cpu().numpy(), ref, "B=%d step %d" % (B, step))
+        check_greedy(nxt.cpu().numpy(), ref, errs, "B=%d step %d" % (B, step))
+        tok = greedy(ref)
+    for r in (0, B // 2, B - 1):
+        k, v = eng.read(ids[r], ctx[r], 2)
+        torch.cuda.synchronize()
+        compare_slab_bits(k.cpu().numpy(), np.stack(orc.seqs[oids[r]].k)[:, ctx[r]:ctx[r] + 2], "K")
+        compare_slab_bits(v.cpu().numpy(), np.stack(orc.seqs[oids[r]].v)[:, ctx[r]:ctx[r] + 2], "V")
+    eng.close()
 
 
 def test_segmented_prefill_no_leakage_gpu(torch, cbd):
