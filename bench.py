@@ -93,6 +93,8 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--roofline-every", type=int, default=31,
+                    help="time one roofline-kernel launch in this many inside the timed region")
     ap.add_argument("--ctx-lo", type=int, default=None)
     ap.add_argument("--ctx-hi", type=int, default=None)
     ap.add_argument("--workload", default="llama8b-b8", choices=sorted(WORKLOADS))
@@ -197,7 +199,9 @@ def main():
 
     log("timing %d steps at B=%d" % (args.steps, B))
     rk = wl["roofline"]
-    eng.profile_begin([rk], max_launches=shape.n_layers * args.steps + 64)
+    # one launch in `every` of the roofline kernel carries timing events (each costs the stream a few
+    # microseconds); a stride co-prime to the layer count cycles the sample through the layers
+    eng.profile_begin([rk], max_launches=shape.n_layers * args.steps + 64, every=args.roofline_every)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):

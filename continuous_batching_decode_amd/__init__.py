@@ -98,7 +98,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "greedy_argmax": (i32, [ctx_p, vp, i32, vp, vp]),
         "cbd_linear": (i32, [ctx_p, P(Matrix), i32, i32, vp, i32, vp, i32, vp]),
         "cbd_pack_int4": (i32, [vp, vp, vp, i64, i64, vp, vp]),
-        "cbd_profile_begin": (i32, [ctx_p, ctypes.c_uint32, i32]),
+        "cbd_profile_begin": (i32, [ctx_p, ctypes.c_uint32, i32, i32]),
         "cbd_pack_bf16": (i32, [vp, i64, i64, vp, vp]),
         "cbd_profile_end": (i32, [ctx_p, P(KernelTime)]),
     }
@@ -305,11 +305,11 @@ class Engine:
                                    int(x_dev.shape[0]), y_dev.data_ptr(), int(splits), _stream_ptr(stream)))
 
     # -- per-kernel event timing
-    def profile_begin(self, kinds: Sequence[str], max_launches: int = 1 << 16) -> None:
+    def profile_begin(self, kinds: Sequence[str], max_launches: int = 1 << 16, every: int = 1) -> None:
         mask = 0
         for k in kinds:
             mask |= 1 << KERNEL_KINDS.index(k)
-        _check(self.lib.cbd_profile_begin(self.ctx, mask, int(max_launches)))
+        _check(self.lib.cbd_profile_begin(self.ctx, mask, int(max_launches), int(every)))
 
     def profile_end(self) -> Dict[str, Dict[str, float]]:
         out = (KernelTime * len(KERNEL_KINDS))()

@@ -135,6 +135,8 @@ struct cbd_ctx {
   // per-kernel event timing (cbd_profile_begin / cbd_profile_end)
   uint32_t prof_mask = 0;
   int prof_max = 0;
+  int prof_every = 1;      // time one selected launch in prof_every
+  int64_t prof_seen = 0;   // selected launches so far
   std::vector<hipEvent_t> prof_ev;  // 2 per recorded launch
   struct ProfRec {
     int kind;
@@ -271,6 +273,7 @@ struct ProfScope {
   hipEvent_t e0 = nullptr, e1 = nullptr;
   ProfScope(cbd_ctx* c_, int kind, double bytes, double flops, hipStream_t st_) : c(c_), st(st_), on(false) {
     if (!(c->prof_mask & (1u << kind)) || (int)c->prof_rec.size() >= c->prof_max) return;
+    if (c->prof_seen++ % c->prof_every) return;
     const size_t i = c->prof_rec.size();
     c->prof_rec.push_back({kind, bytes, flops});
     e0 = c->prof_ev[2 * i];
@@ -997,9 +1000,10 @@ extern "C" cbd_status cbd_pack_bf16(const void* src_dev, int64_t N, int64_t K, v
   return CBD_OK;
 }
 
-extern "C" cbd_status cbd_profile_begin(cbd_ctx* c, uint32_t kind_mask, int32_t max_launches) {
+extern "C" cbd_status cbd_profile_begin(cbd_ctx* c, uint32_t kind_mask, int32_t max_launches, int32_t every) {
   if (!c) return fail(CBD_E_INVAL, "cbd_profile_begin: null context");
   if (max_launches < 0 || max_launches > (1 << 22)) return fail(CBD_E_INVAL, "cbd_profile_begin: bad max_launches");
+  if (every < 1) return fail(CBD_E_INVAL, "cbd_profile_begin: every must be >= 1");
   if (c->host_only) return fail(CBD_E_NODEVICE, "cbd_profile_begin: host-only context");
   while ((int)c->prof_ev.size() < 2 * max_launches) {
     hipEvent_t e;
@@ -1008,6 +1012,8 @@ extern "C" cbd_status cbd_profile_begin(cbd_ctx* c, uint32_t kind_mask, int32_t 
   }
   c->prof_rec.clear();
   c->prof_max = max_launches;
+  c->prof_every = every;
+  c->prof_seen = 0;
   c->prof_mask = kind_mask;
   return CBD_OK;
 }

@@ -294,8 +294,13 @@ cbd_status cbd_pack_int4(const uint8_t* codes, const uint16_t* scale, const uint
  * event-to-event milliseconds, and the summed algorithmic bytes and flops
  * of those launches (counted from shapes: weights + activations read +
  * outputs written; K/V bytes read for attention). kind_mask is a bit mask
- * of (1 << cbd_kernel_kind). max_launches bounds the launches recorded;
- * later ones are not timed. Event handles are created in cbd_profile_begin.
+ * of (1 << cbd_kernel_kind). every >= 1 times one selected launch in
+ * `every` (counted over all selected kinds in launch order; 1 = all of
+ * them): each timed launch costs the stream a few microseconds of event
+ * handling, so sampling keeps a timed run close to an untimed one.
+ * max_launches bounds the launches recorded; later ones are not timed.
+ * Event handles are created in cbd_profile_begin. CBD_E_INVAL: null
+ * context, max_launches outside 0..2^22 or every < 1.
  */
 typedef enum {
   CBD_KERNEL_EMBED = 0,
@@ -319,7 +324,7 @@ typedef struct {
   double flops;
 } cbd_kernel_time;
 
-cbd_status cbd_profile_begin(cbd_ctx* ctx, uint32_t kind_mask, int32_t max_launches);
+cbd_status cbd_profile_begin(cbd_ctx* ctx, uint32_t kind_mask, int32_t max_launches, int32_t every);
 cbd_status cbd_profile_end(cbd_ctx* ctx, cbd_kernel_time* out /* [CBD_KERNEL_KINDS] */);
 
 #ifdef __cplusplus
