@@ -124,12 +124,24 @@ CBD_DEVICE void norm_partials(const SkinnyArgs& a, int col0, int rows_valid, flo
   }
 }
 
-// norm_part may hold nq sets of [16][ROWS] partials (set-major), added set by set in each group.
+// norm_part may hold nq sets of [16][ROWS] partials (set-major): each group adds its sets in
+// order, then the 16 group sums are added in order. The 16 reads of a set are issued together (one
+// LDS wait per set, not one per partial).
 template <int ROWS>
 CBD_DEVICE float norm_inv(const SkinnyArgs& a, const float* norm_part, int col, int nq) {
+  float gs[16];
+#pragma unroll
+  for (int grp = 0; grp < 16; ++grp) gs[grp] = 0.f;
+  for (int q = 0; q < nq; ++q) {
+    float v[16];
+#pragma unroll
+    for (int grp = 0; grp < 16; ++grp) v[grp] = norm_part[(q * 16 + grp) * ROWS + col];
+#pragma unroll
+    for (int grp = 0; grp < 16; ++grp) gs[grp] += v[grp];
+  }
   float s = 0.f;
-  for (int grp = 0; grp < 16; ++grp)
-    for (int q = 0; q < nq; ++q) s += norm_part[(q * 16 + grp) * ROWS + col];
+#pragma unroll
+  for (int grp = 0; grp < 16; ++grp) s += gs[grp];
   return 1.0f / sqrtf(s / a.norm_dim + a.eps);
 }
 
@@ -295,7 +307,7 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
   // their latency hides behind the stream. First the norm's per-16-feature sums of squares: the 16
   // groups x ROWS rows are split over nq thread sets, each adding ss_cnt consecutive partials in
   // order.
-  constexpr int SSMAX = 8;
+  constexpr int SSMAX = NB >= 2 ? 16 : 8;  // partials per thread (8: two thread sets per item at NB = 1)
   const int ss_per = a.ss ? a.ss_tiles / 16 : 0;
   int nq = 1;
   while (2 * nq * 16 * ROWS <= (int)blockDim.x && ss_per % (2 * nq) == 0) nq *= 2;
@@ -304,16 +316,21 @@ __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_ge
   const bool ss_early = a.ss && ss_cnt <= SSMAX && (int)blockDim.x >= 16 * ROWS;
   const int ss_item = threadIdx.x % (16 * ROWS), ss_q = threadIdx.x / (16 * ROWS);
   const bool ss_mine = ss_early && ss_q < nq && (ss_item % ROWS) < rows_valid;
+  // The loads are unconditional inside the (uniform) norm branch: threads without an item, and
+  // partials past ss_cnt, reread valid ones that the sum skips. (The compiler would otherwise start
+  // the sum next to the loads, waiting for them before any weight is requested.)
   float ssv[SSMAX];
-  if (ss_mine) {
-    const float* p = a.ss + (int64_t)((ss_item / ROWS) * ss_per + ss_q * ss_cnt) * a.ss_ld + col0 + ss_item % ROWS;
+  if (ss_early) {
+    const float* p = a.ss + (ss_mine ? (int64_t)((ss_item / ROWS) * ss_per + ss_q * ss_cnt) * a.ss_ld + col0 +
+                                           ss_item % ROWS
+                                     : 0);
 #pragma unroll
-    for (int t = 0; t < SSMAX; ++t)
-      if (t < ss_cnt) ssv[t] = p[(int64_t)t * a.ss_ld];
+    for (int t = 0; t < SSMAX; ++t) ssv[t] = p[(int64_t)min(t, ss_cnt - 1) * a.ss_ld];
   }
   auto ss_store = [&]() {  // norm_part[q][grp][row]
     if (ss_early && ss_q < nq) {
       float s = 0.f;
+      asm volatile("" : "+v"(s));  // the sum starts here, not next to the loads (no early wait)
       if (ss_mine)
 #pragma unroll
         for (int t = 0; t < SSMAX; ++t)
@@ -695,27 +712,7 @@ __global__ __launch_bounds__(128 * WM, WM == 2 ? 3 : 1) void dense_gemm_kernel(S
   };
   u32x4_t rr[D][PER];
 
-  // 1/rms of the tile's rows, added in the same fixed order as the other kernels (16 groups)
   fetch(rr[0], 0);
-  if (a.ss) {
-    float* part = reinterpret_cast<float*>(lds + STAGE);  // [16][TM], stage 1 is free here
-    const int per = a.ss_tiles / 16;
-    for (int i = tid; i < 16 * TM; i += NTH) {
-      const int r = i % TM, grp = i / TM;
-      float sum = 0.f;
-      if (m0 + r < a.rows) {
-        const float* q = a.ss + (int64_t)grp * per * a.ss_ld + m0 + r;
-        for (int t = 0; t < per; ++t) sum += q[(int64_t)t * a.ss_ld];
-      }
-      part[grp * TM + r] = sum;
-    }
-    __syncthreads();
-    if (tid < TM) {
-      float sum = 0.f;
-      for (int grp = 0; grp < 16; ++grp) sum += part[grp * TM + tid];
-      inv_s[tid] = 1.0f / sqrtf(sum / a.norm_dim + a.eps);
-    }
-  }
   put(rr[0], 0);
   __syncthreads();
   // stages past the last refetch the last one (unused): loads stay unconditional
@@ -803,6 +800,50 @@ __global__ __launch_bounds__(128 * WM, WM == 2 ? 3 : 1) void dense_gemm_kernel(S
             acc[i][c] += load_agent_x4(
                 a.part, (int)((base + (int64_t)sp * TILE_F + ((wave * RT + i) * NB + c) * 128 + l32 * 4) * 4));
     if (tid == 0) __hip_atomic_store(a.counters + tn, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // 1/rms of the tile's rows, added in the same fixed order as the other kernels (per group of 16
+  // partials in order, then the 16 groups in order). Computed after the product, by the workgroups
+  // that run the epilogue only, with each thread's loads for 8 partials of its 4 items in flight
+  // together; the stage buffers hold the per-group sums.
+  if (a.ss) {
+    constexpr int IPT = 16 * TM / NTH;  // (row, group) items per thread
+    static_assert(16 * TM % NTH == 0, "items split evenly");
+    __syncthreads();  // every wave is past its last read of the stage buffers
+    float* part = reinterpret_cast<float*>(lds);  // [16][TM]
+    const int per = a.ss_tiles / 16;
+    const float* q[IPT];
+    float sum[IPT];
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int i = tid + NTH * j, r = i % TM, grp = i / TM;
+      q[j] = a.ss + (int64_t)grp * per * a.ss_ld + min(m0 + r, a.rows - 1);  // rows past the last: unused
+      sum[j] = 0.f;
+    }
+    for (int t0 = 0; t0 < per; t0 += 8) {
+      float v[IPT][8];
+#pragma unroll
+      for (int j = 0; j < IPT; ++j)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[j][u] = q[j][(int64_t)min(t0 + u, per - 1) * a.ss_ld];
+#pragma unroll
+      for (int j = 0; j < IPT; ++j)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (t0 + u < per) sum[j] += v[j][u];
+    }
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int i = tid + NTH * j;
+      part[(i / TM) * TM + i % TM] = sum[j];
+    }
+    __syncthreads();
+    if (tid < TM) {
+      float s2 = 0.f;
+      for (int grp = 0; grp < 16; ++grp) s2 += part[grp * TM + tid];
+      inv_s[tid] = 1.0f / sqrtf(s2 / a.norm_dim + a.eps);
+    }
+    __syncthreads();
   }
 
   int sub_row[RT];
