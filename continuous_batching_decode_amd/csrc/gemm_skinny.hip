@@ -631,7 +631,7 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
 
 
 // Many activation rows: 128 weight rows x 32*WM activation rows per workgroup, 2 x WM waves of
-// 64 x 32 (WM = 4 for prefill, 2 for decode steps of 33..64 rows). Each stage copies one 32-input
+// 64 x 32 (WM = 4 for prefill; 2 or 1 for decode steps of 33..64 or 17..32 rows). Each stage copies one 32-input
 // fragment column of both operands to LDS (the fragments are already MFMA operands), double-buffered
 // with one barrier per stage and two stages of loads in flight. SwiGLU tiles hold 64 gate rows and
 // the matching 64 up rows. bf16 weights only. With splits > 1 (one row tile), workgroup (tile, s)
@@ -651,7 +651,7 @@ CBD_DEVICE int dense_row(const SkinnyArgs& a, int n0, int f) {
 }  // namespace
 
 template <int EPI, int WM, int D>
-__global__ __launch_bounds__(128 * WM, WM == 2 ? 3 : 1) void dense_gemm_kernel(SkinnyArgs a, int tiles_n,
+__global__ __launch_bounds__(128 * WM, WM == 4 ? 1 : 3) void dense_gemm_kernel(SkinnyArgs a, int tiles_n,
                                                                                            int splits) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int RT = 4, NB = 4;            // a wave: 4 weight subtiles x 4 activation groups (64 x 32)
@@ -900,7 +900,7 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
 #define CBD_RS_MIN_BLOCKS 600
 #endif
 #ifndef CBD_KS_MAX_NB
-#define CBD_KS_MAX_NB 4
+#define CBD_KS_MAX_NB 8
 #endif
 #ifndef CBD_DENSE_MIN_ROWS
 #define CBD_DENSE_MIN_ROWS 32
@@ -914,13 +914,31 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
 #ifndef CBD_DENSE_MIN_SPLIT_K
 #define CBD_DENSE_MIN_SPLIT_K 1024
 #endif
+#ifndef CBD_DENSE1_MIN_ROWS
+#define CBD_DENSE1_MIN_ROWS 16
+#endif
+#ifndef CBD_DENSE1_WG_TARGET
+#define CBD_DENSE1_WG_TARGET 768
+#endif
+#ifndef CBD_DENSE_MIN_TILES
+#define CBD_DENSE_MIN_TILES 40
+#endif
+#ifndef CBD_DENSE1_MIN_SPLIT_K
+#define CBD_DENSE1_MIN_SPLIT_K 512
+#endif
 
 SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int force) {
   SkinnyPlan p{};
   // dense tiles for many activation rows (bf16 weights; N in whole tiles): 128-row activation
-  // tiles for prefill; one 64-row tile, K split over workgroups to fill the chip, for decode steps
-  // of more than CBD_DENSE_MIN_ROWS rows
-  if (force == 0 && fmt == FMT_BF16 && K % 64 == 0 && (x_blocks > 1 || rows > CBD_DENSE_MIN_ROWS) &&
+  // tiles for prefill; for decode steps one activation tile, K split over workgroups to fill the
+  // chip: 64 rows above CBD_DENSE_MIN_ROWS rows, 32 rows above CBD_DENSE1_MIN_ROWS
+  // (decode: only products with enough weight tiles, or long K, to fill the chip without many
+  // splits; the others measured faster on the k-split kernel)
+  const int dense_tiles = epi == EPI_SWIGLU ? N / (kDenseTileN / 2) : N / kDenseTileN;
+  const bool dense_decode =
+      rows > CBD_DENSE_MIN_ROWS ? (dense_tiles >= CBD_DENSE_MIN_TILES || K >= 8192)
+                                : (rows > CBD_DENSE1_MIN_ROWS && dense_tiles >= CBD_DENSE_MIN_TILES && dense_tiles <= 512);
+  if (force == 0 && fmt == FMT_BF16 && K % 64 == 0 && (x_blocks > 1 || dense_decode) &&
       (epi == EPI_SWIGLU ? N % (kDenseTileN / 2) == 0 : N % kDenseTileN == 0)) {
     p.kind = 2;
     p.rt = 4;
@@ -931,12 +949,14 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
     if (x_blocks > 1) {
       p.waves = 8;
     } else {
-      p.waves = 4;
-      // most splits keeping at most CBD_DENSE_WG_TARGET workgroups and CBD_DENSE_MIN_SPLIT_K inputs
-      // per split: every split adds a 32 KB partial tile that one workgroup reads back at the end
+      const bool wide = rows > CBD_DENSE_MIN_ROWS;
+      p.waves = wide ? 4 : 2;
+      const long wg_target = wide ? CBD_DENSE_WG_TARGET : CBD_DENSE1_WG_TARGET;
+      const int min_k = wide ? CBD_DENSE_MIN_SPLIT_K : CBD_DENSE1_MIN_SPLIT_K;
+      // most splits keeping at most wg_target workgroups and min_k inputs per split: every split
+      // adds a partial tile (32 KB, or 16 KB for 32 rows) that one workgroup reads back at the end
       for (int s = 2; s <= CBD_DENSE_MAX_SPLITS; ++s)
-        if (K % (64 * s) == 0 && K / s >= CBD_DENSE_MIN_SPLIT_K && (long)p.row_blocks * s <= CBD_DENSE_WG_TARGET)
-          p.splits = s;
+        if (K % (64 * s) == 0 && K / s >= min_k && (long)p.row_blocks * s <= wg_target) p.splits = s;
     }
     return p;
   }
@@ -1079,9 +1099,9 @@ static hipError_t dispatch(const SkinnyArgs& a, int fmt, int x_blocks, const Ski
 hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st) {
   const int step = fmt == FMT_INT4 ? 128 : 32;
   if (p.kind == 2) {
-    // 2 x WM waves; 128 weight rows x 32 WM activation rows per tile
+    // 2 x WM waves; 128 weight rows x 32 WM activation rows per tile (WM = 1, 2: decode; 4: prefill)
     const int wm = p.waves / 2, tm_rows = 32 * wm;
-    if (fmt != FMT_BF16 || a.rows < 1 || p.row_blocks < 1 || (wm != 2 && wm != 4) || p.splits < 1 ||
+    if (fmt != FMT_BF16 || a.rows < 1 || p.row_blocks < 1 || (wm != 1 && wm != 2 && wm != 4) || p.splits < 1 ||
         a.K % (64 * p.splits) ||
         (p.splits > 1 && (x_blocks > 1 || a.rows > tm_rows || !a.part || !a.counters)))
       return hipErrorInvalidValue;
@@ -1100,10 +1120,14 @@ hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, cons
       if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU, 4, 2>), grid, dim3(512), lds, st, a, tn, sp);
       else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL, 4, 2>), grid, dim3(512), lds, st, a, tn, sp);
       else launch_kernel((dense_gemm_kernel<EPI_STORE, 4, 2>), grid, dim3(512), lds, st, a, tn, sp);
-    } else {
+    } else if (wm == 2) {
       if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU, 2, 2>), grid, dim3(256), lds, st, a, tn, sp);
       else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL, 2, 2>), grid, dim3(256), lds, st, a, tn, sp);
       else launch_kernel((dense_gemm_kernel<EPI_STORE, 2, 2>), grid, dim3(256), lds, st, a, tn, sp);
+    } else {
+      if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU, 1, 2>), grid, dim3(128), lds, st, a, tn, sp);
+      else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL, 1, 2>), grid, dim3(128), lds, st, a, tn, sp);
+      else launch_kernel((dense_gemm_kernel<EPI_STORE, 1, 2>), grid, dim3(128), lds, st, a, tn, sp);
     }
     return hipGetLastError();
   }

@@ -75,5 +75,6 @@ def compare_slab_bits(gpu_bits, ref_bits, what=""):
 # shapes used only by the parity tests (random-init, small enough for the oracle)
 MID = synth.ModelShape("mid-dh128-g4", 2, 512, 4, 1, 128, 1536, 2048, 500000.0)
 MID_INT4 = synth.ModelShape("mid-int4", 2, 512, 4, 1, 128, 1024, 2048, 1000000.0, weight_format="int4")
-# inputs of 2048 and more features: decode steps of over 32 rows split K over workgroups
-WIDE = synth.ModelShape("wide-d2048", 2, 2048, 16, 4, 128, 5632, 4096, 500000.0)
+# inputs of 2048 and more features: decode steps of over 32 rows split K over workgroups (gate/up;
+# down with 8192 inputs, residual epilogue)
+WIDE = synth.ModelShape("wide-d2048", 2, 2048, 16, 4, 128, 8192, 4096, 500000.0)

@@ -63,7 +63,7 @@ LINEAR_RTOL = 2e-5
 
 
 @pytest.mark.parametrize("N,K", [(6144, 4096), (4096, 14336), (1024, 256), (512, 1024)])
-@pytest.mark.parametrize("rows", [1, 7, 16, 33, 64])
+@pytest.mark.parametrize("rows", [1, 7, 16, 24, 33, 64])
 def test_linear_bf16(torch, cbd, linear_engines, N, K, rows):
     _say("linear bf16 N=%d K=%d rows=%d" % (N, K, rows))
     eng = linear_engines["bf16"]
@@ -313,11 +313,12 @@ def test_ragged_long_history_decode(torch, cbd):
     eng2.close()
 
 
-@pytest.mark.parametrize("B,shape", [(40, MID), (64, MID), (64, WIDE)], ids=["mid-40", "mid-64", "wide-64"])
+@pytest.mark.parametrize("B,shape", [(24, WIDE), (32, MID), (40, MID), (64, MID), (64, WIDE)],
+                         ids=["wide-24", "mid-32", "mid-40", "mid-64", "wide-64"])
 def test_wide_batch_decode(torch, cbd, B, shape):
-    """Decode steps of 33..64 rows (dense projection tiles; K split over workgroups for the wide
-    shape): ragged seeded histories, 2 teacher-forced steps, logits, greedy ids and appended K/V
-    against the oracle."""
+    """Decode steps of 17..64 rows (dense projection tiles of 32 or 64 rows; K split over workgroups
+    for the wide shape): ragged seeded histories, 2 teacher-forced steps, logits, greedy ids and
+    appended K/V against the oracle."""
     _say("wide batch decode B=%d %s" % (B, shape.name))
     from oracle import OracleModel, greedy
     w = synth.make_weights(shape, seed=21, gain_std=0.1)
