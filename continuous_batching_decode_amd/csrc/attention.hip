@@ -45,9 +45,8 @@ CBD_DEVICE void split8(const float (&v)[8], bf16x8_t& hi, bf16x8_t& lo) {
   u32x4_t h, l;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
-    h[i] = h0 | (h1 << 16);
-    l[i] = f32_to_bf16(v[2 * i] - bf16_to_f32(h0)) | (f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1)) << 16);
+    h[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    l[i] = pack_bf16x2(v[2 * i] - bf16_to_f32(h[i] & 0xFFFFu), v[2 * i + 1] - bf16_to_f32(h[i] >> 16));
   }
   hi = as_frag(h);
   lo = as_frag(l);
@@ -55,14 +54,9 @@ CBD_DEVICE void split8(const float (&v)[8], bf16x8_t& hi, bf16x8_t& lo) {
 
 // 4 fp32 -> 4 bf16 hi values and 4 lo values, as two 8-byte words
 CBD_DEVICE void split4(const float (&v)[4], uint2& hi, uint2& lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = f32_to_bf16(v[e]);
-    l[e] = f32_to_bf16(v[e] - bf16_to_f32(h[e]));
-  }
-  hi = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-  lo = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+  hi = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  lo = uint2{pack_bf16x2(v[0] - bf16_to_f32(hi.x & 0xFFFFu), v[1] - bf16_to_f32(hi.x >> 16)),
+             pack_bf16x2(v[2] - bf16_to_f32(hi.y & 0xFFFFu), v[3] - bf16_to_f32(hi.y >> 16))};
 }
 
 CBD_DEVICE float exp_or_zero(float x, float m) { return x == -INFINITY ? 0.f : __expf(x - m); }
@@ -241,14 +235,33 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
   const float scale = 1.0f / sqrtf((float)DH);
   const KVStream<DH> kv{kbase, vbase, lane};
 
-  // The first block's keys are requested before anything else, so their latency overlaps the
-  // set-up below (its values follow the set-up: they are needed only after the first scores).
+  // Everything the wave reads before its stream depends on the item only, so it is requested up
+  // front (one memory latency before the first scores): the first block's keys, q, the new token's
+  // k and v (every item of the row reads them; only the appending one uses them), the RoPE pairs and
+  // the row's split map for the merge; the first block's values follow as soon as q is in registers.
   // Block b_first is inside the slab even when the item reads no slab key (b_first = pos / 32).
   u32x4_t K0[2 * NU], V0[NT];
   kv.load_k(K0, b_first);
+  const float* qkv_row = a.qkv + (int64_t)it.row * a.ld_qkv;
+  float qv[NU][8], kvals[NU][8];
+  Online<DH> st;  // the new token's v lands in the accumulator: O starts as 1 x v
+  {
+    const float* q = qkv_row + (int64_t)(j * G + (c16 < G ? c16 : 0)) * DH;
+    const float* kx = qkv_row + (int64_t)a.n_heads * DH + (int64_t)j * DH;
+    const float* vx = kx + (int64_t)a.n_kv_heads * DH;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) load8(q + 32 * u + 8 * g, qv[u]);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) load8(kx + 32 * u + 8 * g, kvals[u]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float4 x = *reinterpret_cast<const float4*>(vx + 16 * t + 4 * g);
+      st.o[t] = f32x4_t{x.x, x.y, x.z, x.w};
+    }
+  }
+  const int2 rp = a.row_parts[it.row];
 
   const float2* cs = a.rope_cs + (int64_t)pos * (DH / 2);
-  const float* qkv_row = a.qkv + (int64_t)it.row * a.ld_qkv;
   // lane's dims in the score product: d(u, e) = 32u + 8g + e; rotate pairs (u, u ^ PAIR) in place
   auto rotate = [&](float (&x)[NU][8]) {
 #pragma unroll
@@ -266,36 +279,21 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
 
   // Q^T operand: column c16 = query head j*G + c16 (zero beyond G)
   bf16x8_t qh[NU], ql[NU];
-  {
-    float qv[NU][8];
-    const float* q = qkv_row + (int64_t)(j * G + (c16 < G ? c16 : 0)) * DH;
+  rotate(qv);
 #pragma unroll
-    for (int u = 0; u < NU; ++u) load8(q + 32 * u + 8 * g, qv[u]);
-    rotate(qv);
+  for (int u = 0; u < NU; ++u) {
+    if (c16 >= G)
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if (c16 >= G)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[u][e] = 0.f;
-      split8(qv[u], qh[u], ql[u]);
-    }
+      for (int e = 0; e < 8; ++e) qv[u][e] = 0.f;
+    split8(qv[u], qh[u], ql[u]);
   }
+  kv.load_v(V0, b_first);  // (after q: its registers are free by now)
 
-  Online<DH> st;
-  st.clear();
-  if (appends) {
+  if (!appends) {
+    st.clear();
+  } else {
     // The new token goes first (the softmax sum does not depend on the order): k rotated to pos and
     // rounded to bf16 on the lane's score dims, v rounded on its output dims; then stored at pos.
-    const float* kx = qkv_row + (int64_t)a.n_heads * DH + (int64_t)j * DH;
-    const float* vx = kx + (int64_t)a.n_kv_heads * DH;
-    float kvals[NU][8];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) load8(kx + 32 * u + 8 * g, kvals[u]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {  // v lands in the accumulator: O starts as 1 x v
-      const float4 x = *reinterpret_cast<const float4*>(vx + 16 * t + 4 * g);
-      st.o[t] = f32x4_t{x.x, x.y, x.z, x.w};
-    }
     rotate(kvals);
     float dot = 0.f;
 #pragma unroll
@@ -327,7 +325,6 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
       }
   }
 
-  kv.load_v(V0, b_first);
   stream_blocks<DH>(kv, K0, V0, b_first, b_end, g, kend, scale, qh, ql, st);
   const f32x4_t(&o)[NT] = st.o;
   const float m_run = st.m, l_run = st.l;
@@ -347,7 +344,6 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
     if (g == 0) store_agent_x2(a.part_ml, (int)(slot * 2 * 4), float2{m_run, l_run});
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  const int2 rp = a.row_parts[it.row];
   int32_t* counter = a.counters + (int64_t)it.row * a.n_kv_heads + j;
   int last = 0;
   if (lane == 0) last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == rp.y - 1;

@@ -12,14 +12,14 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 // bf16 <-> fp32 on raw bit patterns. fp32 -> bf16 rounds to nearest even.
 CBD_DEVICE float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-CBD_DEVICE uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// fp32 -> bf16, round to nearest even, with gfx950's packed conversion (one instruction per pair;
+// non-finite inputs stay non-finite).
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+CBD_DEVICE uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{lo, hi}, bf16x2_v));
 }
-
-CBD_DEVICE uint32_t pack_bf16x2(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
+CBD_DEVICE uint32_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 CBD_DEVICE bf16x8_t as_frag(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
 

@@ -71,12 +71,11 @@ CBD_DEVICE int seg_begin(const SkinnyArgs& a, int s) { return s == 0 ? 0 : a.seg
 
 // 4 consecutive inputs k..k+3 (k % 4 == 0) of one row -> hi/lo planes (8 bytes each)
 CBD_DEVICE void store_split4(uint16_t* hi, uint16_t* lo, float v0, float v1, float v2, float v3) {
-  const uint32_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1), h2 = f32_to_bf16(v2), h3 = f32_to_bf16(v3);
   uint2 H, L;
-  H.x = h0 | (h1 << 16);
-  H.y = h2 | (h3 << 16);
-  L.x = f32_to_bf16(v0 - bf16_to_f32(h0)) | (f32_to_bf16(v1 - bf16_to_f32(h1)) << 16);
-  L.y = f32_to_bf16(v2 - bf16_to_f32(h2)) | (f32_to_bf16(v3 - bf16_to_f32(h3)) << 16);
+  H.x = pack_bf16x2(v0, v1);
+  H.y = pack_bf16x2(v2, v3);
+  L.x = pack_bf16x2(v0 - bf16_to_f32(H.x & 0xFFFFu), v1 - bf16_to_f32(H.x >> 16));
+  L.y = pack_bf16x2(v2 - bf16_to_f32(H.y & 0xFFFFu), v3 - bf16_to_f32(H.y >> 16));
   *reinterpret_cast<uint2*>(hi) = H;
   *reinterpret_cast<uint2*>(lo) = L;
 }
