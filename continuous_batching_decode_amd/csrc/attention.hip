@@ -214,13 +214,20 @@ CBD_DEVICE AttnItem uniform_item(const AttnItem* items, int i) {
 
 // ============================================================================ decode
 
+// Workgroups of CBD_ATTN_WG_WAVES waves (the waves share nothing): single-wave workgroups let the
+// dispatcher spread a step's waves evenly over the compute units.
+#ifndef CBD_ATTN_WG_WAVES
+#define CBD_ATTN_WG_WAVES 1
+#endif
+constexpr int kAttnWgWaves = CBD_ATTN_WG_WAVES;
+
 template <int DH, int G>
-__global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, int n_waves) {
+__global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_kernel(AttnArgs a, int n_waves) {
   constexpr int NU = DH / 32;  // dim chunks of 32 (K fragments per 16 keys)
   constexpr int NT = DH / 16;  // dim tiles of 16 (V fragments per 32 keys)
   constexpr int PAIR = DH / 64;  // RoPE partner of chunk u is u ^ PAIR (dims d and d + Dh/2)
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
-  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kAttnWgWaves + (threadIdx.x >> 6));
   if (w >= n_waves) return;
   const int j = w % a.n_kv_heads;
   const AttnItem it = uniform_item(a.items, w / a.n_kv_heads);
@@ -350,17 +357,18 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
   last = __shfl(last, 0, 64);
   if (!last) return;
 
-  // Merge with the whole wave (at most 64 splits). Lane s loads split s's (max, sum) for every head
-  // in one round; the per-head maximum and weighted sum come from wave reductions. Lane l then
-  // combines output elements NE*l .. NE*l + NE - 1 of the G x Dh block over the splits in order,
-  // the loads of 8 splits in flight at a time.
+  // Merge with the whole wave (at most 64 splits). Lane s loads split s's (max, sum) for every head;
+  // the per-head maximum and weighted sum come from wave reductions. Lane l combines output
+  // elements NE*l .. NE*l + NE - 1 of the G x Dh block over the splits in order, the loads of SB
+  // splits in flight at a time; the first SB are requested with the (max, sum) pairs, so up to SB
+  // splits cost one memory latency.
   constexpr int NE = G * DH / 64;  // 8, 4 or 2 floats per lane
   const int ns = rp.y;
   // lane s: (max, sum) of split s for the G heads, 2G consecutive floats
   float mv[G], wv[G], Mh[G], Lh[G];
+  float ml[2 * G];
   {
     const int off = (int)((((int64_t)(rp.x + min(lane, ns - 1)) * a.n_heads + j * G) * 2) * 4);
-    float ml[2 * G];
     if constexpr (G == 1) {
       const float2 x = load_agent_x2(a.part_ml, off);
       ml[0] = x.x;
@@ -373,16 +381,11 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
         for (int e = 0; e < 4; ++e) ml[4 * q + e] = x[e];
       }
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      mv[h] = lane < ns ? ml[2 * h] : -INFINITY;  // lanes past the last split take no part
-      wv[h] = lane < ns ? ml[2 * h + 1] : 0.f;
-    }
   }
   const int e0 = lane * NE, hh = e0 / DH, d0 = e0 % DH;
   const int64_t split_stride = (int64_t)a.n_heads * DH;
   const int64_t o_base = (int64_t)rp.x * a.n_heads + j * G + hh;  // slot row of split 0, in DH units
-  constexpr int SB = 8;
+  constexpr int SB = NE >= 4 ? 8 : 16;  // registers: SB x NE floats
   float ov[SB][NE];
   auto load_batch = [&](int s0) {  // splits past the last reload it (their weight is 0)
 #pragma unroll
@@ -403,6 +406,11 @@ __global__ __launch_bounds__(256, 2) void decode_attention_kernel(AttnArgs a, in
     }
   };
   load_batch(0);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mv[h] = lane < ns ? ml[2 * h] : -INFINITY;  // lanes past the last split take no part
+    wv[h] = lane < ns ? ml[2 * h + 1] : 0.f;
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     Mh[h] = wave_max(mv[h]);
@@ -486,9 +494,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(AttnArgs a, i
 template <int DH>
 static hipError_t launch_decode_dh(int G, dim3 grid, int n_waves, hipStream_t st, const AttnArgs& a) {
   switch (G) {
-    case 1: launch_kernel((decode_attention_kernel<DH, 1>), grid, dim3(256), 0, st, a, n_waves); break;
-    case 2: launch_kernel((decode_attention_kernel<DH, 2>), grid, dim3(256), 0, st, a, n_waves); break;
-    case 4: launch_kernel((decode_attention_kernel<DH, 4>), grid, dim3(256), 0, st, a, n_waves); break;
+    case 1: launch_kernel((decode_attention_kernel<DH, 1>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
+    case 2: launch_kernel((decode_attention_kernel<DH, 2>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
+    case 4: launch_kernel((decode_attention_kernel<DH, 4>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -497,7 +505,7 @@ static hipError_t launch_decode_dh(int G, dim3 grid, int n_waves, hipStream_t st
 hipError_t launch_decode_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st) {
   const int G = a.n_heads / a.n_kv_heads;
   const int n_waves = n_items * a.n_kv_heads;
-  const dim3 grid((n_waves + 3) / 4);
+  const dim3 grid((n_waves + kAttnWgWaves - 1) / kAttnWgWaves);
   if (head_dim == 128) return launch_decode_dh<128>(G, grid, n_waves, st, a);
   if (head_dim == 64) return launch_decode_dh<64>(G, grid, n_waves, st, a);
   return hipErrorInvalidValue;
