@@ -271,9 +271,11 @@ CBD_DEVICE void load_scales(const SkinnyArgs& a, const int (&sub_row)[RT], int k
 // ============================================================================ k split
 
 // Largest workgroup an instantiation is compiled for: 16 waves leave 128 registers per lane, enough
-// for one subtile and one column tile; the others get 8 waves (256 registers).
+// for one subtile and one column tile; int4 with two row groups gets 4 waves (its stages hold the
+// codes, their scales and 8 activation fragments); the others get 8 waves (256 registers).
 template <int RT, int NB, int EPI, int FMT, int UC>
-__global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : 512)) void ksplit_gemm_kernel(SkinnyArgs a) {
+__global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : (FMT == FMT_INT4 && NB > 1) ? 256 : 512)) void
+ksplit_gemm_kernel(SkinnyArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int ROWS = 8 * NB;  // activation rows: NB groups of 8
   constexpr int NACC = RT * NB * 4;
@@ -898,6 +900,9 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
 #ifndef CBD_RS_MIN_BLOCKS
 #define CBD_RS_MIN_BLOCKS 600
 #endif
+#ifndef CBD_KS_INT4_MAX_NB
+#define CBD_KS_INT4_MAX_NB 2
+#endif
 #ifndef CBD_KS_MAX_NB
 #define CBD_KS_MAX_NB 8
 #endif
@@ -971,8 +976,9 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
   int ks_uc = fmt == FMT_INT4 ? 1 : (K % (4 * 128) == 0 ? 4 : (K % (4 * 64) == 0 ? 2 : 1));
   ks_uc = std::min(ks_uc, p.nb >= 8 ? 1 : p.nb >= 4 ? 2 : CBD_KS_MAX_UC);  // registers for the stages
   const int ks_unit = step * ks_uc;
-  const int ks_maxw = (ks_rt == 1 && p.nb == 1) ? 16 : 8;
-  const bool ks_ok = x_blocks == 1 && p.nb <= (fmt == FMT_INT4 ? 1 : CBD_KS_MAX_NB) && K % (4 * ks_unit) == 0 &&
+  const int ks_maxw = (ks_rt == 1 && p.nb == 1) ? 16 : (fmt == FMT_INT4 && p.nb > 1) ? 4 : 8;
+  const bool ks_ok = x_blocks == 1 && p.nb <= (fmt == FMT_INT4 ? CBD_KS_INT4_MAX_NB : CBD_KS_MAX_NB) &&
+                     K % (4 * ks_unit) == 0 &&
                      (epi == EPI_SWIGLU ? N % (8 * ks_rt) == 0 : N % (16 * ks_rt) == 0);
   // row split: 4 waves x rt subtiles
   const int rs_rt = (epi == EPI_SWIGLU || N % 128 == 0) ? 2 : 1;
@@ -1048,10 +1054,15 @@ static hipError_t launch_rs(const SkinnyArgs& a, const SkinnyPlan& p, int x_bloc
 template <int RT, int EPI, int FMT, int UC>
 static hipError_t launch_ks(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t st) {
   const dim3 grid(p.row_blocks, 1);
-  if constexpr (FMT == FMT_INT4) {  // one 8-row group (the plan never asks for more)
-    if (p.nb != 1) return hipErrorInvalidValue;
-    launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
-                  st, a);
+  if constexpr (FMT == FMT_INT4) {  // one or two 8-row groups (the plan never asks for more)
+    if (p.nb == 1)
+      launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
+                    st, a);
+    else if (p.nb == 2)
+      launch_kernel((ksplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 2),
+                    st, a);
+    else
+      return hipErrorInvalidValue;
   } else if (p.nb == 1) {
     launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
                   st, a);
@@ -1132,7 +1143,7 @@ hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, cons
   }
   if (p.kind == 1) {
     if (x_blocks != 1 || p.nb > 8 || p.waves < 1 || p.waves > 16 || a.K % p.waves ||
-        (a.K / p.waves) % (step * p.uc) || (p.waves > 8 && (p.rt != 1 || p.nb != 1)) ||
+        (a.K / p.waves) % (step * p.uc) || (p.waves > 8 && (p.rt != 1 || p.nb != 1)) || (fmt == FMT_INT4 && p.nb > 1 && p.waves > 4) ||
         a.K / p.waves < 2 * step * p.uc)
       return hipErrorInvalidValue;
   } else {
