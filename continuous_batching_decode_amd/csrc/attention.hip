@@ -182,6 +182,88 @@ CBD_DEVICE void stream_blocks(const KVStream<DH>& kv, u32x4_t (&K0)[DH / 16], u3
   }
 }
 
+// Online softmax over the 64 keys of blocks b and b + 1 at once (one max, one rescale), then
+// O^T += V0^T P0^T + V1^T P1^T. Same element order as block_accumulate, block by block.
+template <int DH>
+CBD_DEVICE void pair_accumulate(const u32x4_t (&V0)[DH / 16], const u32x4_t (&V1)[DH / 16], const f32x4_t (&s)[4],
+                                int b, int g, int lim, float scale, Online<DH>& st) {
+  float sv[16];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k0 = 32 * (b + h) + 4 * g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[8 * h + e] = k0 + e < lim ? s[2 * h][e] * scale : -INFINITY;
+      sv[8 * h + 4 + e] = k0 + 16 + e < lim ? s[2 * h + 1][e] * scale : -INFINITY;
+    }
+  }
+  float bm = sv[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) bm = fmaxf(bm, sv[i]);
+  bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+  bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+  const float m_new = fmaxf(st.m, bm);
+  const float alpha = exp_or_zero(st.m, m_new);
+  float p0[8], p1[8], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p0[i] = exp_or_zero(sv[i], m_new);
+    p1[i] = exp_or_zero(sv[8 + i], m_new);
+    ps += p0[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ps += p1[i];
+  ps += __shfl_xor(ps, 16, 64);
+  ps += __shfl_xor(ps, 32, 64);
+  st.l = st.l * alpha + ps;
+  st.m = m_new;
+  bf16x8_t ph0, pl0, ph1, pl1;
+  split8(p0, ph0, pl0);
+  split8(p1, ph1, pl1);
+#pragma unroll
+  for (int t = 0; t < DH / 16; ++t) {
+    st.o[t] = st.o[t] * alpha;
+    st.o[t] = mfma(as_frag(V0[t]), ph0, st.o[t]);
+    st.o[t] = mfma(as_frag(V0[t]), pl0, st.o[t]);
+    st.o[t] = mfma(as_frag(V1[t]), ph1, st.o[t]);
+    st.o[t] = mfma(as_frag(V1[t]), pl1, st.o[t]);
+  }
+}
+
+// Blocks [b_first, b_end) two at a time with two blocks in flight: (K0, V0) and (K1, V1) hold
+// blocks b and b + 1 on entry (indices past the last clamp to it, so every load stays
+// unconditional) and are refilled with b + 2 and b + 3 as soon as they have been used.
+template <int DH>
+CBD_DEVICE void stream_pairs(const KVStream<DH>& kv, u32x4_t (&K0)[DH / 16], u32x4_t (&V0)[DH / 16],
+                             u32x4_t (&K1)[DH / 16], u32x4_t (&V1)[DH / 16], int b_first, int b_end, int g, int lim,
+                             float scale, const bf16x8_t (&qh)[DH / 32], const bf16x8_t (&ql)[DH / 32],
+                             Online<DH>& st) {
+  const int last = b_end - 1;
+  int b = b_first;
+  f32x4_t s[4];
+  for (; b + 2 < b_end; b += 2) {
+    block_scores<DH>(K0, qh, ql, s[0], s[1]);
+    block_scores<DH>(K1, qh, ql, s[2], s[3]);
+    __builtin_amdgcn_sched_barrier(0);
+    kv.load_k(K0, b + 2);
+    kv.load_k(K1, min(b + 3, last));
+    __builtin_amdgcn_sched_barrier(0);
+    pair_accumulate<DH>(V0, V1, s, b, g, lim, scale, st);
+    __builtin_amdgcn_sched_barrier(0);
+    kv.load_v(V0, b + 2);
+    kv.load_v(V1, min(b + 3, last));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (b + 1 < b_end) {  // a last pair
+    block_scores<DH>(K0, qh, ql, s[0], s[1]);
+    block_scores<DH>(K1, qh, ql, s[2], s[3]);
+    pair_accumulate<DH>(V0, V1, s, b, g, lim, scale, st);
+  } else if (b < b_end) {  // a last single block
+    block_scores<DH>(K0, qh, ql, s[0], s[1]);
+    block_accumulate<DH>(V0, s[0], s[1], b, g, lim, scale, st);
+  }
+}
+
 // The lane's O^T tiles (dims 16t + 4g + e of its column), times inv, to the hi/lo planes of `row`.
 template <int DH>
 CBD_DEVICE void store_out(const AttnArgs& a, int row, int head, int g, const f32x4_t (&o)[DH / 16], float inv) {
@@ -220,8 +302,11 @@ CBD_DEVICE AttnItem uniform_item(const AttnItem* items, int i) {
 #define CBD_ATTN_WG_WAVES 1
 #endif
 constexpr int kAttnWgWaves = CBD_ATTN_WG_WAVES;
+#ifndef CBD_ATTN_PD
+#define CBD_ATTN_PD 2
+#endif
 
-template <int DH, int G>
+template <int DH, int G, int PD>
 __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_kernel(AttnArgs a, int n_waves) {
   constexpr int NU = DH / 32;  // dim chunks of 32 (K fragments per 16 keys)
   constexpr int NT = DH / 16;  // dim tiles of 16 (V fragments per 32 keys)
@@ -332,7 +417,15 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_kernel(
       }
   }
 
-  stream_blocks<DH>(kv, K0, V0, b_first, b_end, g, kend, scale, qh, ql, st);
+  if constexpr (PD == 1) {
+    stream_blocks<DH>(kv, K0, V0, b_first, b_end, g, kend, scale, qh, ql, st);
+  } else {
+    u32x4_t K1[2 * NU], V1[NT];
+    const int b1 = min(b_first + 1, max(b_end - 1, b_first));
+    kv.load_k(K1, b1);
+    kv.load_v(V1, b1);
+    stream_pairs<DH>(kv, K0, V0, K1, V1, b_first, b_end, g, kend, scale, qh, ql, st);
+  }
   const f32x4_t(&o)[NT] = st.o;
   const float m_run = st.m, l_run = st.l;
 
@@ -494,9 +587,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(AttnArgs a, i
 template <int DH>
 static hipError_t launch_decode_dh(int G, dim3 grid, int n_waves, hipStream_t st, const AttnArgs& a) {
   switch (G) {
-    case 1: launch_kernel((decode_attention_kernel<DH, 1>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
-    case 2: launch_kernel((decode_attention_kernel<DH, 2>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
-    case 4: launch_kernel((decode_attention_kernel<DH, 4>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
+    case 1: launch_kernel((decode_attention_kernel<DH, 1, CBD_ATTN_PD>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
+    case 2: launch_kernel((decode_attention_kernel<DH, 2, CBD_ATTN_PD>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
+    case 4: launch_kernel((decode_attention_kernel<DH, 4, CBD_ATTN_PD>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
