@@ -994,7 +994,9 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
     p.splits = 1;
     p.kc = 0;
     // each wave needs >= 2 stages of its K slice (the loop keeps two in flight)
-    int nw = 4;
+    // (int4 at one row group: two waves per tile to start with, so wide products stay within one
+    // round of resident waves; their stages carry the dequantization and are fewer per wave)
+    int nw = (fmt == FMT_INT4 && p.nb == 1) ? 2 : 4;
     if (force < 0) {
       nw = -force;
     } else {
