@@ -630,42 +630,47 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
 
 // ============================================================================ dense tiles
 
-
-// Many activation rows: 128 weight rows x 32*WM activation rows per workgroup, 2 x WM waves of
-// 64 x 32 (WM = 4 for prefill; 2 or 1 for decode steps of 33..64 or 17..32 rows). Each stage copies one 32-input
-// fragment column of both operands to LDS (the fragments are already MFMA operands), double-buffered
-// with one barrier per stage and two stages of loads in flight. SwiGLU tiles hold 64 gate rows and
-// the matching 64 up rows. bf16 weights only. With splits > 1 (one row tile), workgroup (tile, s)
-// adds the inputs [s K/splits, (s + 1) K/splits); the last workgroup of a tile to arrive adds the
-// partial tiles in order (agent-scope 16-byte accesses and an arrival counter, as the row split).
+// Many activation rows: WN x WM waves of 64 weight rows x 8*NBW activation rows each, so a
+// workgroup covers TN = 64 WN weight rows x TM = 8 NBW WM activation rows (prefill: 256 x 128 with
+// 64 x 64 waves; decode steps: 128 x 64 or 128 x 32 with 64 x 32 waves). Each stage copies one
+// 32-input fragment column of both operands to LDS (the fragments are already MFMA operands),
+// double-buffered with one barrier per stage and two stages of loads in flight. SwiGLU tiles hold
+// TN/2 gate rows and the matching up rows. bf16 weights only. With splits > 1 (one row tile),
+// workgroup (tile, s) adds the inputs [s K/splits, (s + 1) K/splits); the last workgroup of a tile
+// to arrive adds the partial tiles in order (agent-scope 16-byte accesses and an arrival counter, as
+// the row split).
 namespace {
-constexpr int kDenseTileN = 128;
-// LDS of a dense workgroup with 2 x wm waves: two stages of (8 + 4 wm) fragments, 1/rms per row
-inline size_t dense_lds(int wm) { return (size_t)2 * (8 + 4 * wm) * 512 * 2 + 32 * wm * 4; }
+// LDS of a dense workgroup: two stages of (4 wn + nbw wm) fragments, 1/rms per activation row
+inline size_t dense_lds(int wn, int wm, int nbw) {
+  return (size_t)2 * (4 * wn + nbw * wm) * 512 * 2 + 8 * nbw * wm * 4;
+}
 
-// weight row of subtile f (0..7) of the workgroup's tile
-template <int EPI>
+// weight row of subtile f (0 .. NWF-1) of the workgroup's tile
+template <int EPI, int NWF>
 CBD_DEVICE int dense_row(const SkinnyArgs& a, int n0, int f) {
-  if constexpr (EPI == EPI_SWIGLU) return f < 4 ? n0 + 16 * f : a.seg_end[0] + n0 + 16 * (f - 4);
+  if constexpr (EPI == EPI_SWIGLU)
+    return f < NWF / 2 ? n0 + 16 * f : a.seg_end[0] + n0 + 16 * (f - NWF / 2);
   return n0 + 16 * f;
 }
 }  // namespace
 
-template <int EPI, int WM, int D>
-__global__ __launch_bounds__(128 * WM, WM == 4 ? 1 : 3) void dense_gemm_kernel(SkinnyArgs a, int tiles_n,
-                                                                                           int splits) {
+template <int EPI, int WN, int WM, int NBW>
+__global__ __launch_bounds__(64 * WN * WM, 2) void dense_gemm_kernel(SkinnyArgs a, int tiles_n, int splits) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int RT = 4, NB = 4;            // a wave: 4 weight subtiles x 4 activation groups (64 x 32)
-  constexpr int TM = 32 * WM;              // activation rows of the tile
-  constexpr int FR = 8 + TM / 8;           // fragments per stage: 8 weight subtiles + TM/8 groups
-  constexpr int NTH = 128 * WM, PER = FR / (2 * WM);  // threads; fragment copies per thread and stage
-  static_assert(FR % (2 * WM) == 0, "fragments per stage split evenly over the waves");
+  constexpr int RT = 4, NB = NBW;          // a wave: 4 weight subtiles x NBW activation groups
+  static_assert(NBW % 4 == 0, "activation groups come 4 at a time");
+  constexpr int D = 2;                     // register stages in flight
+  constexpr int NW = WN * WM, NTH = 64 * NW;
+  constexpr int TN = 64 * WN, TM = 8 * NBW * WM;  // weight rows and activation rows of the tile
+  constexpr int NWF = 4 * WN, FR = NWF + NBW * WM;  // fragments per stage: weight subtiles, then groups
+  constexpr int PER = FR / NW;             // fragment copies per thread and stage
+  static_assert(FR % NW == 0, "fragments per stage split evenly over the waves");
   constexpr int STAGE = FR * 512;          // elements of one LDS stage
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);  // 2 stages
   float* inv_s = reinterpret_cast<float*>(smem + 2 * STAGE * 2);  // [TM]
   __shared__ int s_last;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wn = wave & 1, wm = wave >> 1;  // 2 x WM waves
+  const int wn = wave % WN, wm = wave / WN;
   const int tiles_m = (a.rows + TM - 1) / TM;
   int tn, tm, split = 0;
   if (splits == 1) {
@@ -683,22 +688,22 @@ __global__ __launch_bounds__(128 * WM, WM == 4 ? 1 : 3) void dense_gemm_kernel(S
     split = blockIdx.x - tn * splits;
     tm = 0;
   }
-  const int n0 = tn * (EPI == EPI_SWIGLU ? kDenseTileN / 2 : kDenseTileN);
+  const int n0 = tn * (EPI == EPI_SWIGLU ? TN / 2 : TN);
   const int m0 = tm * TM;
   const int K = a.K, nk_all = K >> 5, nk = nk_all / splits, kf0 = split * nk;
 
-  // this thread's fragment copies per stage: f = wave + 2 WM i (0..7 weights, then activation groups)
+  // this thread's fragment copies per stage: f = wave + NW i (weights first, then activation groups)
   const uint16_t* src[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int f = wave + 2 * WM * i;
-    if (f < 8) {
-      const int grow = dense_row<EPI>(a, n0, f);
+    const int f = wave + NW * i;
+    if (f < NWF) {
+      const int grow = dense_row<EPI, NWF>(a, n0, f);
       const int sg = seg_of(a, grow);
       const int tr = (grow - seg_begin(a, sg)) >> 4;
       src[i] = reinterpret_cast<const uint16_t*>(a.w[sg]) + ((int64_t)tr * nk_all + kf0) * 512 + 8 * lane;
     } else {
-      src[i] = a.x + ((int64_t)((m0 >> 3) + (f - 8)) * nk_all + kf0) * 512 + 8 * lane;
+      src[i] = a.x + ((int64_t)((m0 >> 3) + (f - NWF)) * nk_all + kf0) * 512 + 8 * lane;
     }
   }
   // global -> registers -> LDS; D register sets keep the loads of the next D stages in flight
@@ -709,7 +714,7 @@ __global__ __launch_bounds__(128 * WM, WM == 4 ? 1 : 3) void dense_gemm_kernel(S
   auto put = [&](const u32x4_t (&r)[PER], int buf) {  // a fragment is a 1 KB copy
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      *reinterpret_cast<u32x4_t*>(lds + buf * STAGE + (wave + 2 * WM * i) * 512 + 8 * lane) = r[i];
+      *reinterpret_cast<u32x4_t*>(lds + buf * STAGE + (wave + NW * i) * 512 + 8 * lane) = r[i];
   };
   u32x4_t rr[D][PER];
 
@@ -730,24 +735,29 @@ __global__ __launch_bounds__(128 * WM, WM == 4 ? 1 : 3) void dense_gemm_kernel(S
   for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // LDS fragments of this wave: weights (4 subtiles), activations (4 groups of 8 rows)
+  // LDS fragments of this wave: weights (4 subtiles; SwiGLU: 2 gate, then their 2 up), activations
   int fa[RT];
 #pragma unroll
   for (int i = 0; i < RT; ++i) {
-    if constexpr (EPI == EPI_SWIGLU) fa[i] = i < 2 ? 2 * wn + i : 4 + 2 * wn + (i - 2);
+    if constexpr (EPI == EPI_SWIGLU) fa[i] = i < 2 ? 2 * wn + i : NWF / 2 + 2 * wn + (i - 2);
     else fa[i] = 4 * wn + i;
   }
-  auto compute = [&](int buf) {
+  auto compute = [&](int buf) {  // activation groups 4 at a time (registers)
     const uint16_t* st = lds + buf * STAGE;
-    bf16x8_t A[RT], X[NB];
+    bf16x8_t A[RT];
 #pragma unroll
     for (int i = 0; i < RT; ++i) A[i] = *reinterpret_cast<const bf16x8_t*>(st + fa[i] * 512 + 8 * lane);
 #pragma unroll
-    for (int c = 0; c < NB; ++c) X[c] = *reinterpret_cast<const bf16x8_t*>(st + (8 + 4 * wm + c) * 512 + 8 * lane);
+    for (int c0 = 0; c0 < NB; c0 += 4) {
+      bf16x8_t X[4];
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
+      for (int c = 0; c < 4; ++c)
+        X[c] = *reinterpret_cast<const bf16x8_t*>(st + (NWF + NBW * wm + c0 + c) * 512 + 8 * lane);
 #pragma unroll
-      for (int c = 0; c < NB; ++c) acc[i][c] = mfma(A[i], X[c], acc[i][c]);
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[i][c0 + c] = mfma(A[i], X[c], acc[i][c0 + c]);
+    }
   };
   // stage s is in LDS buffer s & 1; register set s % D holds stage s + 1 and is put after computing
   // s, then refilled with stage s + 1 + D. nk is a multiple of D (and even), so the loop body has no
@@ -767,7 +777,7 @@ __global__ __launch_bounds__(128 * WM, WM == 4 ? 1 : 3) void dense_gemm_kernel(S
     // partial tile of (tile, split, wave): hi and lo products added first, then [i][c][32 lanes]
     // f32x4 from the lanes that hold a low half (16 bytes per lane and subtile); the merged sums go
     // back to those lanes, zero to the others, so the epilogue's hi + lo addition leaves them as is
-    constexpr int TILE_F = 2 * WM * RT * NB * 32 * 4;  // floats of one workgroup's partial
+    constexpr int TILE_F = NW * RT * NB * 32 * 4;  // floats of one workgroup's partial
     const int64_t base = (int64_t)tn * splits * TILE_F;
     const int l32 = ((lane >> 4) << 3) | (lane & 7);
     const bool holder = (lane & 8) == 0;
@@ -849,14 +859,23 @@ __global__ __launch_bounds__(128 * WM, WM == 4 ? 1 : 3) void dense_gemm_kernel(S
 
   int sub_row[RT];
 #pragma unroll
-  for (int i = 0; i < RT; ++i) sub_row[i] = dense_row<EPI>(a, n0, fa[i]);
-  const int col0 = m0 + 32 * wm;
-  const int rows_valid = min(32, a.rows - col0);
+  for (int i = 0; i < RT; ++i) sub_row[i] = dense_row<EPI, NWF>(a, n0, fa[i]);
+  const int col0 = m0 + 8 * NBW * wm;
+  const int rows_valid = min(8 * NBW, a.rows - col0);
   if (rows_valid <= 0) return;
-  float inv[NB];
+  // the epilogue takes the activation groups 4 at a time (registers)
 #pragma unroll
-  for (int c = 0; c < NB; ++c) inv[c] = a.ss ? inv_s[32 * wm + 8 * c + (lane & 7)] : 1.f;
-  epilogue<RT, NB, EPI>(a, acc, sub_row, col0, rows_valid, inv, lane, nullptr);
+  for (int c0 = 0; c0 < NB; c0 += 4) {
+    f32x4_t part[RT][4];
+    float inv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      inv[c] = a.ss ? inv_s[8 * NBW * wm + 8 * (c0 + c) + (lane & 7)] : 1.f;
+#pragma unroll
+      for (int i = 0; i < RT; ++i) part[i][c] = acc[i][c0 + c];
+    }
+    epilogue<RT, 4, EPI>(a, part, sub_row, col0 + 8 * c0, rows_valid - 8 * c0, inv, lane, nullptr);
+  }
 }
 
 // ============================================================================ weight packing
@@ -924,6 +943,9 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
 #ifndef CBD_DENSE1_WG_TARGET
 #define CBD_DENSE1_WG_TARGET 768
 #endif
+#ifndef CBD_DENSE_WIDE_PREFILL
+#define CBD_DENSE_WIDE_PREFILL 1
+#endif
 #ifndef CBD_DENSE_MIN_TILES
 #define CBD_DENSE_MIN_TILES 40
 #endif
@@ -933,28 +955,34 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
 
 SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int force) {
   SkinnyPlan p{};
-  // dense tiles for many activation rows (bf16 weights; N in whole tiles): 128-row activation
-  // tiles for prefill; for decode steps one activation tile, K split over workgroups to fill the
-  // chip: 64 rows above CBD_DENSE_MIN_ROWS rows, 32 rows above CBD_DENSE1_MIN_ROWS
-  // (decode: only products with enough weight tiles, or long K, to fill the chip without many
-  // splits; the others measured faster on the k-split kernel)
-  const int dense_tiles = epi == EPI_SWIGLU ? N / (kDenseTileN / 2) : N / kDenseTileN;
+  // dense tiles for many activation rows (bf16 weights; N in whole tiles). Prefill: 256 x 128
+  // tiles of 64 x 64 waves (CBD_DENSE_WIDE_PREFILL; 128 x 128 tiles of 64 x 32 waves where N does
+  // not divide). Decode steps: one activation tile of 64 rows above CBD_DENSE_MIN_ROWS rows, 32 rows
+  // above CBD_DENSE1_MIN_ROWS, 128 weight rows, K split over workgroups to fill the chip; only for
+  // products with enough weight tiles, or long K, to fill the chip without many splits (the others
+  // measured faster on the k-split kernel). The plan fields: rt = waves along N, nb = activation
+  // groups per wave, waves = all waves of the workgroup.
+  auto ntiles = [&](int tn_rows) { return epi == EPI_SWIGLU ? N / (tn_rows / 2) : N / tn_rows; };
+  auto divides = [&](int tn_rows) { return epi == EPI_SWIGLU ? N % (tn_rows / 2) == 0 : N % tn_rows == 0; };
   const bool dense_decode =
-      rows > CBD_DENSE_MIN_ROWS ? (dense_tiles >= CBD_DENSE_MIN_TILES || K >= 8192)
-                                : (rows > CBD_DENSE1_MIN_ROWS && dense_tiles >= CBD_DENSE_MIN_TILES && dense_tiles <= 512);
-  if (force == 0 && fmt == FMT_BF16 && K % 64 == 0 && (x_blocks > 1 || dense_decode) &&
-      (epi == EPI_SWIGLU ? N % (kDenseTileN / 2) == 0 : N % kDenseTileN == 0)) {
+      rows > CBD_DENSE_MIN_ROWS ? (ntiles(128) >= CBD_DENSE_MIN_TILES || K >= 8192)
+                                : (rows > CBD_DENSE1_MIN_ROWS && ntiles(128) >= CBD_DENSE_MIN_TILES && ntiles(128) <= 512);
+  if (force == 0 && fmt == FMT_BF16 && K % 64 == 0 && (x_blocks > 1 || dense_decode) && divides(128)) {
     p.kind = 2;
-    p.rt = 4;
-    p.nb = 4;
     p.uc = 1;
-    p.row_blocks = epi == EPI_SWIGLU ? N / (kDenseTileN / 2) : N / kDenseTileN;
     p.splits = 1;
     if (x_blocks > 1) {
+      const bool wide_tile = CBD_DENSE_WIDE_PREFILL && divides(256);
+      p.rt = wide_tile ? 4 : 2;
+      p.nb = wide_tile ? 8 : 4;
       p.waves = 8;
+      p.row_blocks = ntiles(64 * p.rt);
     } else {
       const bool wide = rows > CBD_DENSE_MIN_ROWS;
+      p.rt = 2;
+      p.nb = 4;
       p.waves = wide ? 4 : 2;
+      p.row_blocks = ntiles(128);
       const long wg_target = wide ? CBD_DENSE_WG_TARGET : CBD_DENSE1_WG_TARGET;
       const int min_k = wide ? CBD_DENSE_MIN_SPLIT_K : CBD_DENSE1_MIN_SPLIT_K;
       // most splits keeping at most wg_target workgroups and min_k inputs per split: every split
@@ -1111,11 +1139,13 @@ static hipError_t dispatch(const SkinnyArgs& a, int fmt, int x_blocks, const Ski
 hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st) {
   const int step = fmt == FMT_INT4 ? 128 : 32;
   if (p.kind == 2) {
-    // 2 x WM waves; 128 weight rows x 32 WM activation rows per tile (WM = 1, 2: decode; 4: prefill)
-    const int wm = p.waves / 2, tm_rows = 32 * wm;
-    if (fmt != FMT_BF16 || a.rows < 1 || p.row_blocks < 1 || (wm != 1 && wm != 2 && wm != 4) || p.splits < 1 ||
-        a.K % (64 * p.splits) ||
-        (p.splits > 1 && (x_blocks > 1 || a.rows > tm_rows || !a.part || !a.counters)))
+    // p.rt x (waves / p.rt) waves of 64 weight rows x 8 p.nb activation rows (see plan_skinny)
+    const int wn = p.rt, wm = p.waves / std::max(1, p.rt), nbw = p.nb;
+    const int tm_rows = 8 * nbw * wm;
+    const bool known = (wn == 4 && wm == 2 && nbw == 8) || (wn == 2 && wm == 4 && nbw == 4) ||
+                       (wn == 2 && wm == 2 && nbw == 4) || (wn == 2 && wm == 1 && nbw == 4);
+    if (fmt != FMT_BF16 || a.rows < 1 || p.row_blocks < 1 || !known || p.waves != wn * wm || p.splits < 1 ||
+        a.K % (64 * p.splits) || (p.splits > 1 && (x_blocks > 1 || a.rows > tm_rows || !a.part || !a.counters)))
       return hipErrorInvalidValue;
     const int tiles_m = (a.rows + tm_rows - 1) / tm_rows;
     dim3 grid;
@@ -1126,20 +1156,26 @@ hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, cons
       const int supers = ((p.row_blocks + 7) / 8) * ((tiles_m + 7) / 8);
       grid = dim3(((supers + 7) / 8) * 8 * 64);
     }
-    const size_t lds = dense_lds(wm);
+    const size_t lds = dense_lds(wn, wm, nbw);
     const int tn = p.row_blocks, sp = p.splits;
-    if (wm == 4) {
-      if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU, 4, 2>), grid, dim3(512), lds, st, a, tn, sp);
-      else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL, 4, 2>), grid, dim3(512), lds, st, a, tn, sp);
-      else launch_kernel((dense_gemm_kernel<EPI_STORE, 4, 2>), grid, dim3(512), lds, st, a, tn, sp);
+    const dim3 block(64 * p.waves);
+    auto go = [&](auto kernel) { launch_kernel(kernel, grid, block, lds, st, a, tn, sp); };
+    if (wn == 4) {
+      if (epi == EPI_SWIGLU) go(dense_gemm_kernel<EPI_SWIGLU, 4, 2, 8>);
+      else if (epi == EPI_RESIDUAL) go(dense_gemm_kernel<EPI_RESIDUAL, 4, 2, 8>);
+      else go(dense_gemm_kernel<EPI_STORE, 4, 2, 8>);
+    } else if (wm == 4) {
+      if (epi == EPI_SWIGLU) go(dense_gemm_kernel<EPI_SWIGLU, 2, 4, 4>);
+      else if (epi == EPI_RESIDUAL) go(dense_gemm_kernel<EPI_RESIDUAL, 2, 4, 4>);
+      else go(dense_gemm_kernel<EPI_STORE, 2, 4, 4>);
     } else if (wm == 2) {
-      if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU, 2, 2>), grid, dim3(256), lds, st, a, tn, sp);
-      else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL, 2, 2>), grid, dim3(256), lds, st, a, tn, sp);
-      else launch_kernel((dense_gemm_kernel<EPI_STORE, 2, 2>), grid, dim3(256), lds, st, a, tn, sp);
+      if (epi == EPI_SWIGLU) go(dense_gemm_kernel<EPI_SWIGLU, 2, 2, 4>);
+      else if (epi == EPI_RESIDUAL) go(dense_gemm_kernel<EPI_RESIDUAL, 2, 2, 4>);
+      else go(dense_gemm_kernel<EPI_STORE, 2, 2, 4>);
     } else {
-      if (epi == EPI_SWIGLU) launch_kernel((dense_gemm_kernel<EPI_SWIGLU, 1, 2>), grid, dim3(128), lds, st, a, tn, sp);
-      else if (epi == EPI_RESIDUAL) launch_kernel((dense_gemm_kernel<EPI_RESIDUAL, 1, 2>), grid, dim3(128), lds, st, a, tn, sp);
-      else launch_kernel((dense_gemm_kernel<EPI_STORE, 1, 2>), grid, dim3(128), lds, st, a, tn, sp);
+      if (epi == EPI_SWIGLU) go(dense_gemm_kernel<EPI_SWIGLU, 2, 1, 4>);
+      else if (epi == EPI_RESIDUAL) go(dense_gemm_kernel<EPI_RESIDUAL, 2, 1, 4>);
+      else go(dense_gemm_kernel<EPI_STORE, 2, 1, 4>);
     }
     return hipGetLastError();
   }

@@ -66,8 +66,9 @@ struct SkinnyArgs {
 //    chunks of kc inputs staged in LDS; K split over `splits` workgroups.
 //  kind 1 (k split): one tile of 16*rt rows per workgroup, its `waves` waves each stream a
 //    contiguous 1/waves of K with activations read from L2; partial sums added through LDS.
-//  kind 2 (dense): 128 weight rows x 16*waves activation rows per workgroup, both staged in LDS;
-//    K split over `splits` workgroups (one activation tile only).
+//  kind 2 (dense): rt x (waves / rt) waves of 64 weight rows x 8*nb activation rows per
+//    workgroup, both operands staged in LDS; K split over `splits` workgroups (one activation
+//    tile only).
 struct SkinnyPlan {
   int kind, nb, rt, uc, row_blocks, splits, kc, waves;
 };
@@ -80,7 +81,7 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
 // workspace bytes a plan needs for its partial tiles
 inline size_t skinny_part_bytes(const SkinnyPlan& p) {
   if (p.splits <= 1) return 0;
-  if (p.kind == 2) return (size_t)p.row_blocks * p.splits * p.waves * 4 * 4 * 32 * 4 * 4;  // hi + lo added
+  if (p.kind == 2) return (size_t)p.row_blocks * p.splits * p.waves * 4 * p.nb * 32 * 4 * 4;  // hi + lo added
   return p.kind == 0 ? (size_t)p.row_blocks * p.splits * 4 * p.rt * p.nb * 4 * 64 * 4 : 0;
 }
 hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st);
