@@ -21,8 +21,10 @@ CBD_DEVICE void split_store(uint16_t* hi, uint16_t* lo, float v) {
 
 }  // namespace
 
-// One block per row. Thread i handles features [16i, 16i+16): it writes h,
-// the planes of gain * h and the partial sum of squares of its 16 features.
+// One block per row. Each thread takes 8 consecutive features at a time (one 16-byte load of the
+// embedding row and of the gain): it writes them to h, the 8 hi and 8 lo values of gain * h (16
+// contiguous bytes each in the fragment layout), and with its neighbour lane (the other half of a
+// 16-feature group) the group's sum of squares. d % 16 == 0.
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, const uint16_t* embed, int vocab, int d,
                                                     const uint16_t* gain, float* h, uint16_t* xp, int64_t plane,
                                                     float* ss, int ss_ld) {
@@ -31,18 +33,44 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, const
   tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);  // ids stay on the device: clamp out-of-range ids
   const uint16_t* e = embed + (int64_t)tok * d;
   float* hrow = h + (int64_t)r * d;
-  for (int t = threadIdx.x; t < d / 16; t += 256) {
+  // chunks of 8 features; whole waves take part in every round (the sum pairs lanes t, t ^ 1)
+  const int chunks = d / 8, rounds = (chunks + 255) / 256;
+  for (int k = 0; k < rounds; ++k) {
+    const int t = threadIdx.x + 256 * k;
+    const bool on = t < chunks;
+    const int tc = on ? t : 0;
+    const uint4 ev = *reinterpret_cast<const uint4*>(e + 8 * tc);
+    const uint4 gv = *reinterpret_cast<const uint4*>(gain + 8 * tc);
+    const uint32_t ew[4] = {ev.x, ev.y, ev.z, ev.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    float v[8], y[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(ew[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_to_f32(ew[i] >> 16);
+      y[2 * i] = v[2 * i] * bf16_to_f32(gw[i] & 0xFFFFu);
+      y[2 * i + 1] = v[2 * i + 1] * bf16_to_f32(gw[i] >> 16);
+    }
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int f = 16 * t + i;
-      const float v = bf16_to_f32(e[f]);
-      hrow[f] = v;
-      s += v * v;
-      const int64_t o = xfrag_off(r, f, d);
-      split_store(xp + o, xp + plane + o, v * bf16_to_f32(gain[f]));
+    for (int i = 0; i < 8; ++i) s += v[i] * v[i];
+    s += __shfl_xor(s, 1, 64);  // the 16-feature group: chunks 2u and 2u + 1
+    if (on) {
+      *reinterpret_cast<float4*>(hrow + 8 * t) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(hrow + 8 * t + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      uint4 hi, lo;
+      hi.x = pack_bf16x2(y[0], y[1]);
+      hi.y = pack_bf16x2(y[2], y[3]);
+      hi.z = pack_bf16x2(y[4], y[5]);
+      hi.w = pack_bf16x2(y[6], y[7]);
+      lo.x = pack_bf16x2(y[0] - bf16_to_f32(hi.x & 0xFFFFu), y[1] - bf16_to_f32(hi.x >> 16));
+      lo.y = pack_bf16x2(y[2] - bf16_to_f32(hi.y & 0xFFFFu), y[3] - bf16_to_f32(hi.y >> 16));
+      lo.z = pack_bf16x2(y[4] - bf16_to_f32(hi.z & 0xFFFFu), y[5] - bf16_to_f32(hi.z >> 16));
+      lo.w = pack_bf16x2(y[6] - bf16_to_f32(hi.w & 0xFFFFu), y[7] - bf16_to_f32(hi.w >> 16));
+      const int64_t o = xfrag_off(r, 8 * t, d);  // features 8t .. 8t + 7 are contiguous there
+      *reinterpret_cast<uint4*>(xp + o) = hi;
+      *reinterpret_cast<uint4*>(xp + plane + o) = lo;
+      if ((t & 1) == 0) ss[(int64_t)(t >> 1) * ss_ld + r] = s;
     }
-    ss[(int64_t)t * ss_ld + r] = s;
   }
 }
 

@@ -314,7 +314,7 @@ static cbd_status setup_weights(cbd_ctx* c, const cbd_weights* w) {
     return CBD_OK;
   };
   auto vec = [&](const void* p, const char* name, const uint16_t** out) -> cbd_status {
-    if (!p || (reinterpret_cast<uintptr_t>(p) & 7)) return fail(CBD_E_INVAL, "%s: null or not 8-byte aligned", name);
+    if (!p || !aligned16(p)) return fail(CBD_E_INVAL, "%s: null or not 16-byte aligned", name);
     *out = static_cast<const uint16_t*>(p);
     return CBD_OK;
   };

@@ -147,7 +147,8 @@ int32_t cbd_slab_granule_tokens(void);
 
 /*
  * Create a context. Weights are referenced, not copied: they must stay
- * valid until cbd_destroy. kv_arena_dev (arena_bytes long, 256-byte
+ * valid until cbd_destroy; every weight pointer (matrices, int4 scale/bias
+ * pairs, norm gains, embedding) must be 16-byte aligned (CBD_E_INVAL). kv_arena_dev (arena_bytes long, 256-byte
  * aligned) is caller-owned device memory that the library carves into
  * per-sequence slabs; it is cleared here and must not be written by the
  * caller while the context lives (slab contents are read and written only
