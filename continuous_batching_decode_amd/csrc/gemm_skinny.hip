@@ -943,6 +943,9 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
 #ifndef CBD_DENSE1_WG_TARGET
 #define CBD_DENSE1_WG_TARGET 768
 #endif
+#ifndef CBD_DENSE_WIDE_DECODE
+#define CBD_DENSE_WIDE_DECODE 1
+#endif
 #ifndef CBD_DENSE_WIDE_PREFILL
 #define CBD_DENSE_WIDE_PREFILL 1
 #endif
@@ -979,10 +982,12 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
       p.row_blocks = ntiles(64 * p.rt);
     } else {
       const bool wide = rows > CBD_DENSE_MIN_ROWS;
-      p.rt = 2;
-      p.nb = 4;
-      p.waves = wide ? 4 : 2;
-      p.row_blocks = ntiles(128);
+      // 256-row tiles only where they need no K split (their partial tiles are twice as large)
+      const bool wide_tile = wide && CBD_DENSE_WIDE_DECODE && divides(256) && ntiles(256) >= 384;
+      p.rt = wide_tile ? 4 : 2;
+      p.nb = wide_tile ? 8 : 4;
+      p.waves = wide_tile ? 4 : wide ? 4 : 2;
+      p.row_blocks = ntiles(64 * p.rt);
       const long wg_target = wide ? CBD_DENSE_WG_TARGET : CBD_DENSE1_WG_TARGET;
       const int min_k = wide ? CBD_DENSE_MIN_SPLIT_K : CBD_DENSE1_MIN_SPLIT_K;
       // most splits keeping at most wg_target workgroups and min_k inputs per split: every split
@@ -1142,7 +1147,8 @@ hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, cons
     // p.rt x (waves / p.rt) waves of 64 weight rows x 8 p.nb activation rows (see plan_skinny)
     const int wn = p.rt, wm = p.waves / std::max(1, p.rt), nbw = p.nb;
     const int tm_rows = 8 * nbw * wm;
-    const bool known = (wn == 4 && wm == 2 && nbw == 8) || (wn == 2 && wm == 4 && nbw == 4) ||
+    const bool known = (wn == 4 && wm == 2 && nbw == 8) || (wn == 4 && wm == 1 && nbw == 8) ||
+                       (wn == 2 && wm == 4 && nbw == 4) ||
                        (wn == 2 && wm == 2 && nbw == 4) || (wn == 2 && wm == 1 && nbw == 4);
     if (fmt != FMT_BF16 || a.rows < 1 || p.row_blocks < 1 || !known || p.waves != wn * wm || p.splits < 1 ||
         a.K % (64 * p.splits) || (p.splits > 1 && (x_blocks > 1 || a.rows > tm_rows || !a.part || !a.counters)))
@@ -1160,10 +1166,14 @@ hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, cons
     const int tn = p.row_blocks, sp = p.splits;
     const dim3 block(64 * p.waves);
     auto go = [&](auto kernel) { launch_kernel(kernel, grid, block, lds, st, a, tn, sp); };
-    if (wn == 4) {
+    if (wn == 4 && wm == 2) {
       if (epi == EPI_SWIGLU) go(dense_gemm_kernel<EPI_SWIGLU, 4, 2, 8>);
       else if (epi == EPI_RESIDUAL) go(dense_gemm_kernel<EPI_RESIDUAL, 4, 2, 8>);
       else go(dense_gemm_kernel<EPI_STORE, 4, 2, 8>);
+    } else if (wn == 4) {
+      if (epi == EPI_SWIGLU) go(dense_gemm_kernel<EPI_SWIGLU, 4, 1, 8>);
+      else if (epi == EPI_RESIDUAL) go(dense_gemm_kernel<EPI_RESIDUAL, 4, 1, 8>);
+      else go(dense_gemm_kernel<EPI_STORE, 4, 1, 8>);
     } else if (wm == 4) {
       if (epi == EPI_SWIGLU) go(dense_gemm_kernel<EPI_SWIGLU, 2, 4, 4>);
       else if (epi == EPI_RESIDUAL) go(dense_gemm_kernel<EPI_RESIDUAL, 2, 4, 4>);

@@ -79,6 +79,23 @@ def test_linear_bf16(torch, cbd, linear_engines, N, K, rows):
     assert err <= LINEAR_RTOL * np.max(np.abs(ref)), err
 
 
+@pytest.mark.parametrize("rows", [40, 64])
+def test_linear_bf16_wide_n(torch, cbd, linear_engines, rows):
+    """A product with enough weight rows (98304) for 256-row dense tiles without a K split."""
+    N, K = 98304, 256
+    _say("linear bf16 N=%d K=%d rows=%d" % (N, K, rows))
+    eng = linear_engines["bf16"]
+    W = synth.normal_bf16(17, N + K, (N, K), 0.02)
+    X = synth.normal_f32(18, rows, (rows, K), 1.0)
+    wd, xd = cbd.pack_bf16_device(to_dev_bits(torch, W)), torch.from_numpy(X).cuda()
+    y = torch.empty((rows, N), dtype=torch.float32, device="cuda")
+    eng.linear(cbd.Matrix(wd.data_ptr(), None), N, K, xd, y)
+    torch.cuda.synchronize()
+    ref = X.astype(np.float64) @ synth.bf16_bits_to_f32(W).astype(np.float64).T
+    err = np.max(np.abs(y.cpu().numpy() - ref))
+    assert err <= LINEAR_RTOL * np.max(np.abs(ref)), err
+
+
 @pytest.mark.parametrize("splits", [1, 2, 7, 16])
 @pytest.mark.parametrize("N,K,rows", [(4096, 14336, 8), (4096, 14336, 1), (1024, 14336, 33)])
 def test_linear_bf16_splits(torch, cbd, linear_engines, N, K, rows, splits):
