@@ -137,7 +137,8 @@ def main():
     ctx_main = ctx.copy()
     # sweep-only rows (beyond B) reuse the main rows' histories
     ctx = np.array([ctx[r % B] for r in range(n_rows)], dtype=int)
-    grow = args.warmup + args.steps + 1 + (len(sweep) * (args.sweep_steps + 4))
+    grow = args.warmup + args.steps + 1 + (0 if args.no_breakdown else min(16, args.steps)) + \
+           len(sweep) * (args.sweep_steps + 4)
     caps = [int(c) + grow + 8 for c in ctx]
     gran = 256
     arena_tokens = sum((c + gran - 1) // gran * gran for c in caps)

@@ -42,6 +42,7 @@
 //   sum_k x_k (s q_k + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * sum_k x_k,
 // where sum_k x_k over the group comes from one more MFMA with an all-ones A.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -878,6 +879,187 @@ __global__ __launch_bounds__(64 * WN * WM, 2) void dense_gemm_kernel(SkinnyArgs 
   }
 }
 
+// ============================================================================ wide k split
+
+// 9..64 activation rows (decode steps of wide batches): a workgroup of 4 waves takes one tile of
+// 64 weight rows (4 subtiles; SwiGLU: 32 gate rows and the 32 up rows of the same features) over one
+// of `splits` K ranges; each wave streams a contiguous quarter of that range with all NB activation
+// groups, so every activation fragment read from L2 feeds 4 weight fragments (the k-split kernel
+// feeds one). The waves' sums are added through LDS in wave order; wave w then owns the groups
+// c = w (mod 4): with splits > 1 it stores their partial tiles (agent scope) and the last workgroup
+// of a tile to arrive adds the splits in order, computes 1/rms of the rows if the input is normed,
+// and runs the epilogue of the groups its waves own.
+namespace {
+constexpr int kWideWaves = 4;
+inline size_t wide_lds(int nb) { return (size_t)kWideWaves * nb * 4 * 32 * 16 + 16 * 8 * nb * 4 + 8 * nb * 4; }
+}  // namespace
+
+template <int EPI, int NB, int UC>
+__global__ __launch_bounds__(64 * kWideWaves, NB == 8 ? 1 : 2) void wide_ksplit_kernel(SkinnyArgs a, int splits) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int RT = 4, NW = kWideWaves, NTH = 64 * NW, ROWS = 8 * NB;
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);                          // [NW][NB][RT][32]
+  float* npart = reinterpret_cast<float*>(smem + NW * NB * RT * 32 * 16);  // [16][ROWS]
+  float* inv_s = npart + 16 * ROWS;                                        // [ROWS]
+  __shared__ int s_last;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tile = blockIdx.x / splits, split = blockIdx.x - tile * splits;
+  const int K = a.K, kr = K / splits, kw = kr / NW, k0 = split * kr + wave * kw;
+
+  int sub_row[RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) sub_row[i] = subtile_row<RT, EPI>(a, tile, i);
+  const void* wr[RT];
+  weight_ptrs<RT, FMT_BF16>(a, sub_row, K, k0, lane, wr);
+  const uint16_t* xr = a.x + (int64_t)(k0 >> 5) * 512 + 8 * lane;  // group c at + c (K/32) 512
+  const int64_t xg = (int64_t)(K >> 5) * 512;
+
+  f32x4_t acc[RT][NB];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  struct Buf {
+    u32x4_t A[UC][RT];
+    bf16x8_t X[UC][NB];
+  };
+  auto load = [&](Buf& f, int st) {
+#pragma unroll
+    for (int u = 0; u < UC; ++u)
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+        f.A[u][i] = load_stream(reinterpret_cast<const uint16_t*>(wr[i]) + (int64_t)(st * UC + u) * 512);
+    // padding rows of the last groups are loaded like the rest (the workspace holds whole groups)
+#pragma unroll
+    for (int u = 0; u < UC; ++u)
+#pragma unroll
+      for (int c = 0; c < NB; ++c) f.X[u][c] = load_frag(xr + c * xg + (st * UC + u) * 512);
+  };
+  auto compute = [&](const Buf& f) {
+#pragma unroll
+    for (int u = 0; u < UC; ++u)
+#pragma unroll
+      for (int c = 0; c < NB; ++c)
+#pragma unroll
+        for (int i = 0; i < RT; ++i) acc[i][c] = mfma(as_frag(f.A[u][i]), f.X[u][c], acc[i][c]);
+  };
+  // the k-split kernel's two-buffer pipeline: unconditional loads, each buffer's loads kept together
+  // by scheduling barriers, the last 2 or 3 stages peeled (the plan guarantees total >= 2)
+  const int total = kw / (32 * UC);
+  Buf b0, b1;
+  load(b0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(b1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  int st = 0;
+  for (; st + 3 < total; st += 2) {
+    compute(b0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b0, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b1, st + 3);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  compute(b0);
+  if (st + 2 < total) {
+    __builtin_amdgcn_sched_barrier(0);
+    load(b0, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b1);
+    compute(b0);
+  } else {
+    compute(b1);
+  }
+
+  // hi + lo, then the waves' sums through LDS: lanes with l & 8 clear hold (row l%8, outputs 4 g..)
+  const int l32 = ((lane >> 4) << 3) | (lane & 7);
+  const bool holder = (lane & 8) == 0;
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][c][e] += __shfl_xor(acc[i][c][e], 8, 64);
+      if (holder) red[((wave * NB + c) * RT + i) * 32 + l32] = acc[i][c];
+    }
+  __syncthreads();
+  // wave w adds the groups c = w (mod NW) over the waves in order; the sums go to the holder lanes,
+  // zero to the others (the epilogue's hi + lo addition then leaves them as they are)
+#pragma unroll
+  for (int c = 0; c < NB; ++c)
+    if (c % NW == wave) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        f32x4_t v = red[(c * RT + i) * 32 + l32];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[((w * NB + c) * RT + i) * 32 + l32];
+        acc[i][c] = holder ? v : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+
+  if (splits > 1) {
+    constexpr int TILE_F = NB * RT * 32 * 4;  // floats of one workgroup's partial tile
+    const int64_t base = (int64_t)tile * splits * TILE_F;
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+      if (c % NW == wave && holder)
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+          store_agent_x4(a.part, (int)((base + (int64_t)split * TILE_F + ((c * RT + i) * 32 + l32) * 4) * 4), acc[i][c]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(a.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
+    __syncthreads();
+    if (!s_last) return;
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+      if (c % NW == wave) {
+#pragma unroll
+        for (int i = 0; i < RT; ++i) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (holder)
+          for (int sp = 0; sp < splits; ++sp)
+#pragma unroll
+            for (int i = 0; i < RT; ++i)
+              acc[i][c] += load_agent_x4(a.part, (int)((base + (int64_t)sp * TILE_F + ((c * RT + i) * 32 + l32) * 4) * 4));
+      }
+    if (tid == 0) __hip_atomic_store(a.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // 1/rms of the rows (the same fixed order as the other kernels: per group of 16 partials in order,
+  // then the 16 groups in order), by the workgroups that run the epilogue only
+  if (a.ss) {
+    const int per = a.ss_tiles / 16;
+    for (int it = tid; it < 16 * ROWS; it += NTH) {
+      const int r = it % ROWS, grp = it / ROWS;
+      const float* q = a.ss + (int64_t)grp * per * a.ss_ld + min(r, a.rows - 1);  // rows past the last: unused
+      float sum = 0.f;
+      for (int t = 0; t < per; ++t) sum += q[(int64_t)t * a.ss_ld];
+      npart[grp * ROWS + r] = sum;
+    }
+    __syncthreads();
+    if (tid < ROWS) {
+      float s2 = 0.f;
+      for (int grp = 0; grp < 16; ++grp) s2 += npart[grp * ROWS + tid];
+      inv_s[tid] = 1.0f / sqrtf(s2 / a.norm_dim + a.eps);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int c = 0; c < NB; ++c)
+    if (c % NW == wave && 8 * c < a.rows) {
+      f32x4_t one[RT][1];
+#pragma unroll
+      for (int i = 0; i < RT; ++i) one[i][0] = acc[i][c];
+      const float inv[1] = {a.ss ? inv_s[8 * c + (lane & 7)] : 1.f};
+      epilogue<RT, 1, EPI>(a, one, sub_row, 8 * c, a.rows - 8 * c, inv, lane, nullptr);
+    }
+}
+
 // ============================================================================ weight packing
 
 // row-major bf16 [N, K] -> streaming layout (N % 16 == 0, K % 32 == 0)
@@ -956,8 +1138,65 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
 #define CBD_DENSE1_MIN_SPLIT_K 512
 #endif
 
+#ifndef CBD_WIDE_KS
+#define CBD_WIDE_KS 1
+#endif
+#ifndef CBD_WIDE_MIN_ROWS
+#define CBD_WIDE_MIN_ROWS 8
+#endif
+#ifndef CBD_WIDE_WG_TARGET
+#define CBD_WIDE_WG_TARGET 256
+#endif
+#ifndef CBD_WIDE_MAX_SPLITS
+#define CBD_WIDE_MAX_SPLITS 16
+#endif
+#ifndef CBD_WIDE_MIN_SPLIT_K
+#define CBD_WIDE_MIN_SPLIT_K 512
+#endif
+#ifndef CBD_WIDE_ALL
+#define CBD_WIDE_ALL 0
+#endif
+#ifndef CBD_WIDE_UC8
+#define CBD_WIDE_UC8 1
+#endif
+#ifndef CBD_DENSE_WIDE_MIN_TILES
+#define CBD_DENSE_WIDE_MIN_TILES 384
+#endif
+#ifndef CBD_WIDE_UC
+#define CBD_WIDE_UC 2
+#endif
+
 SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int force) {
   SkinnyPlan p{};
+  // wide k split for decode steps of more than CBD_WIDE_MIN_ROWS rows (bf16 weights): 64-row tiles
+  // of 4 waves, K split over workgroups up to CBD_WIDE_WG_TARGET workgroups with at least
+  // CBD_WIDE_MIN_SPLIT_K inputs per split. The plan fields: rt = 4 subtiles per wave, nb = activation
+  // groups (2, 4 or 8), uc = 32-input fragments per pipeline stage, waves = 4.
+  const int wide_groups = (rows + 7) / 8;
+  const int wide_nb = wide_groups <= 2 ? 2 : wide_groups <= 4 ? 4 : 8;
+  const long n_all = epi == EPI_SWIGLU ? 2L * N : (long)N;  // weight rows
+  // measured at the 8B shape: at 17..32 rows it beats the k-split and dense kernels on long-K and
+  // wide products (down, gate/up, lm_head), at 33..64 rows on the 4096-row products (O, down)
+  const bool wide_pick = CBD_WIDE_ALL ? wide_nb >= 2
+                                      : wide_nb == 4 ? (K >= 8192 || n_all >= 16384) : wide_nb == 8 && n_all <= 4096;
+  if (force == 0 && CBD_WIDE_KS && fmt == FMT_BF16 && x_blocks == 1 && rows > CBD_WIDE_MIN_ROWS && rows <= 64 &&
+      wide_pick && (epi == EPI_SWIGLU ? N % 32 == 0 : N % 64 == 0)) {
+    p.kind = 3;
+    p.rt = 4;
+    p.waves = 4;
+    p.nb = wide_nb;
+    p.uc = p.nb == 8 ? CBD_WIDE_UC8 : CBD_WIDE_UC;
+    p.row_blocks = epi == EPI_SWIGLU ? N / 32 : N / 64;
+    p.splits = 1;
+    const int unit = 4 * 32 * p.uc;  // inputs of one stage of the 4 waves
+    if (K % (2 * unit) == 0) {
+      for (int s = 2; s <= CBD_WIDE_MAX_SPLITS; ++s)
+        if (K % (s * 2 * unit) == 0 && K / s >= CBD_WIDE_MIN_SPLIT_K && (long)p.row_blocks * s <= CBD_WIDE_WG_TARGET)
+          p.splits = s;
+      return p;
+    }
+    p = SkinnyPlan{};
+  }
   // dense tiles for many activation rows (bf16 weights; N in whole tiles). Prefill: 256 x 128
   // tiles of 64 x 64 waves (CBD_DENSE_WIDE_PREFILL; 128 x 128 tiles of 64 x 32 waves where N does
   // not divide). Decode steps: one activation tile of 64 rows above CBD_DENSE_MIN_ROWS rows, 32 rows
@@ -983,7 +1222,7 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
     } else {
       const bool wide = rows > CBD_DENSE_MIN_ROWS;
       // 256-row tiles only where they need no K split (their partial tiles are twice as large)
-      const bool wide_tile = wide && CBD_DENSE_WIDE_DECODE && divides(256) && ntiles(256) >= 384;
+      const bool wide_tile = wide && CBD_DENSE_WIDE_DECODE && divides(256) && ntiles(256) >= CBD_DENSE_WIDE_MIN_TILES;
       p.rt = wide_tile ? 4 : 2;
       p.nb = wide_tile ? 8 : 4;
       p.waves = wide_tile ? 4 : wide ? 4 : 2;
@@ -1187,6 +1426,27 @@ hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, cons
       else if (epi == EPI_RESIDUAL) go(dense_gemm_kernel<EPI_RESIDUAL, 2, 1, 4>);
       else go(dense_gemm_kernel<EPI_STORE, 2, 1, 4>);
     }
+    return hipGetLastError();
+  }
+  if (p.kind == 3) {
+    const int unit = 4 * 32 * p.uc;
+    const bool known = (p.nb == 2 && p.uc == CBD_WIDE_UC) || (p.nb == 4 && p.uc == CBD_WIDE_UC) || (p.nb == 8 && p.uc == CBD_WIDE_UC8);
+    if (fmt != FMT_BF16 || x_blocks != 1 || !known || p.rt != 4 || p.waves != 4 || a.rows < 1 || a.rows > 8 * p.nb ||
+        p.splits < 1 || a.K % (p.splits * unit) || a.K / p.splits < 2 * unit || p.row_blocks < 1 ||
+        p.row_blocks != (epi == EPI_SWIGLU ? a.N / 32 : a.N / 64) || (p.splits > 1 && (!a.part || !a.counters)))
+      return hipErrorInvalidValue;
+    const dim3 grid(p.row_blocks * p.splits), block(64 * kWideWaves);
+    const size_t lds = wide_lds(p.nb);
+    auto go = [&](auto kernel) { launch_kernel(kernel, grid, block, lds, st, a, p.splits); };
+    auto by_nb = [&](auto epi_c) {
+      constexpr int E = decltype(epi_c)::value;
+      if (p.nb == 2) go(wide_ksplit_kernel<E, 2, CBD_WIDE_UC>);
+      else if (p.nb == 4) go(wide_ksplit_kernel<E, 4, CBD_WIDE_UC>);
+      else go(wide_ksplit_kernel<E, 8, CBD_WIDE_UC8>);
+    };
+    if (epi == EPI_SWIGLU) by_nb(std::integral_constant<int, EPI_SWIGLU>{});
+    else if (epi == EPI_RESIDUAL) by_nb(std::integral_constant<int, EPI_RESIDUAL>{});
+    else by_nb(std::integral_constant<int, EPI_STORE>{});
     return hipGetLastError();
   }
   if (p.kind == 1) {

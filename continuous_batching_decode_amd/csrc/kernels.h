@@ -69,6 +69,9 @@ struct SkinnyArgs {
 //  kind 2 (dense): rt x (waves / rt) waves of 64 weight rows x 8*nb activation rows per
 //    workgroup, both operands staged in LDS; K split over `splits` workgroups (one activation
 //    tile only).
+//  kind 3 (wide k split): 4 waves x 4 subtiles of 16 rows (64 weight rows) per workgroup, each wave
+//    a quarter of the workgroup's K range with all nb activation groups (activations read from
+//    L2); K split over `splits` workgroups; decode steps of 9..64 rows.
 struct SkinnyPlan {
   int kind, nb, rt, uc, row_blocks, splits, kc, waves;
 };
@@ -82,6 +85,7 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
 inline size_t skinny_part_bytes(const SkinnyPlan& p) {
   if (p.splits <= 1) return 0;
   if (p.kind == 2) return (size_t)p.row_blocks * p.splits * p.waves * 4 * p.nb * 32 * 4 * 4;  // hi + lo added
+  if (p.kind == 3) return (size_t)p.row_blocks * p.splits * p.nb * 4 * 32 * 4 * 4;  // hi + lo added
   return p.kind == 0 ? (size_t)p.row_blocks * p.splits * 4 * p.rt * p.nb * 4 * 64 * 4 : 0;
 }
 hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st);
