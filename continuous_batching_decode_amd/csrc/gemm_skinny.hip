@@ -1175,10 +1175,13 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
   const int wide_groups = (rows + 7) / 8;
   const int wide_nb = wide_groups <= 2 ? 2 : wide_groups <= 4 ? 4 : 8;
   const long n_all = epi == EPI_SWIGLU ? 2L * N : (long)N;  // weight rows
-  // measured at the 8B shape: at 17..32 rows it beats the k-split and dense kernels on long-K and
-  // wide products (down, gate/up, lm_head), at 33..64 rows on the 4096-row products (O, down)
+  // measured at the 8B shape: at 9..16 rows it beats the k-split kernel on long K (down), at 17..32
+  // rows the k-split and dense kernels on long-K and wide products (down, gate/up, lm_head), at
+  // 33..64 rows on the 4096-row products (O, down)
   const bool wide_pick = CBD_WIDE_ALL ? wide_nb >= 2
-                                      : wide_nb == 4 ? (K >= 8192 || n_all >= 16384) : wide_nb == 8 && n_all <= 4096;
+                         : wide_nb == 2 ? K >= 8192
+                         : wide_nb == 4 ? (K >= 8192 || n_all >= 16384)
+                                        : n_all <= 4096;
   if (force == 0 && CBD_WIDE_KS && fmt == FMT_BF16 && x_blocks == 1 && rows > CBD_WIDE_MIN_ROWS && rows <= 64 &&
       wide_pick && (epi == EPI_SWIGLU ? N % 32 == 0 : N % 64 == 0)) {
     p.kind = 3;
