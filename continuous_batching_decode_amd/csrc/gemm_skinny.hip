@@ -276,14 +276,16 @@ CBD_DEVICE void load_scales(const SkinnyArgs& a, const int (&sub_row)[RT], int k
 // codes, their scales and 8 activation fragments); the others get 8 waves (256 registers).
 template <int RT, int NB, int EPI, int FMT, int UC>
 __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : (FMT == FMT_INT4 && NB > 1) ? 256 : 512)) void
-ksplit_gemm_kernel(SkinnyArgs a) {
+ksplit_gemm_kernel(SkinnyArgs a, int splits) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int ROWS = 8 * NB;  // activation rows: NB groups of 8
   constexpr int NACC = RT * NB * 4;
   const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tile = blockIdx.x, xblk = blockIdx.y;
-  const int K = a.K, kw = K / nw, k0 = wave * kw;
+  // workgroup (tile, split) takes inputs [split K/splits, (split + 1) K/splits), its waves a
+  // contiguous 1/nw of that range each
+  const int tile = blockIdx.x / splits, split = blockIdx.x - tile * splits, xblk = blockIdx.y;
+  const int K = a.K, kw = K / (nw * splits), k0 = split * (K / splits) + wave * kw;
   const int col0 = xblk * ROWS;
   const int rows_valid = min(ROWS, a.rows - col0);
   float* red = reinterpret_cast<float*>(smem);              // [nw-1][NACC][64]
@@ -480,6 +482,33 @@ ksplit_gemm_kernel(SkinnyArgs a) {
       for (int c = 0; c < NB; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][c][e] += src[((i * NB + c) * 4 + e) * 64 + lane];
+  }
+  if (splits > 1) {
+    // K split over workgroups (to even out the work per compute unit): wave 0 of each stores its
+    // sums (agent scope); the last to arrive adds the splits in order
+    constexpr int TILE_F = NACC * 64;
+    const int64_t base = (int64_t)tile * splits * TILE_F;
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int c = 0; c < NB; ++c)
+        store_agent_x4(a.part, (int)((base + (int64_t)split * TILE_F + ((i * NB + c) * 64 + lane) * 4) * 4), acc[i][c]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial stores are done
+    int last = 0;
+    if (lane == 0)
+      last = __hip_atomic_fetch_add(a.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
+    if (!__shfl(last, 0, 64)) return;
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < splits; ++sp)
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int c = 0; c < NB; ++c)
+          acc[i][c] += load_agent_x4(a.part, (int)((base + (int64_t)sp * TILE_F + ((i * NB + c) * 64 + lane) * 4) * 4));
+    if (lane == 0) __hip_atomic_store(a.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   float inv[NB];
 #pragma unroll
@@ -1141,6 +1170,17 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
 #ifndef CBD_WIDE_KS
 #define CBD_WIDE_KS 1
 #endif
+#ifndef CBD_KS_MAX_SPLITS
+#define CBD_KS_MAX_SPLITS 4
+#endif
+
+namespace {
+int g_plan_units = 256;  // compute units of the device the plans are for (set by the context)
+}
+void set_plan_compute_units(int units) {
+  if (units > 0) g_plan_units = units;
+}
+int plan_compute_units() { return g_plan_units; }
 #ifndef CBD_WIDE_MIN_ROWS
 #define CBD_WIDE_MIN_ROWS 8
 #endif
@@ -1280,7 +1320,16 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
              K / (2 * nw) >= 2 * ks_unit)
         nw *= 2;
     }
-    while (fmt == FMT_BF16 && p.uc > 1 && K / nw < 2 * step * p.uc) p.uc /= 2;
+    // Fewer tiles than compute units leave units idle: K is then split over s workgroups per tile
+    // (the same waves each, over 1/s of K), doubling s while the workgroups still fit one per unit.
+    // (Splits that only even out 1.5 or 3.5 tiles per unit measured slower: the merge costs more.)
+    if (force == 0) {
+      const int units = plan_compute_units();
+      while ((long)ks_tiles * p.splits * 2 <= units && p.splits * 2 <= CBD_KS_MAX_SPLITS &&
+             K % (p.splits * 2 * nw * ks_unit) == 0 && K / (p.splits * 2 * nw) >= 2 * ks_unit)
+        p.splits *= 2;
+    }
+    while (fmt == FMT_BF16 && p.uc > 1 && K / (nw * p.splits) < 2 * step * p.uc) p.uc /= 2;
     p.waves = nw;
     return p;
   }
@@ -1330,28 +1379,28 @@ static hipError_t launch_rs(const SkinnyArgs& a, const SkinnyPlan& p, int x_bloc
 
 template <int RT, int EPI, int FMT, int UC>
 static hipError_t launch_ks(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t st) {
-  const dim3 grid(p.row_blocks, 1);
+  const dim3 grid(p.row_blocks * p.splits, 1);
   if constexpr (FMT == FMT_INT4) {  // one or two 8-row groups (the plan never asks for more)
     if (p.nb == 1)
       launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
-                    st, a);
+                    st, a, p.splits);
     else if (p.nb == 2)
       launch_kernel((ksplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 2),
-                    st, a);
+                    st, a, p.splits);
     else
       return hipErrorInvalidValue;
   } else if (p.nb == 1) {
     launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
-                  st, a);
+                  st, a, p.splits);
   } else if (p.nb == 2) {
     launch_kernel((ksplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 2),
-                  st, a);
+                  st, a, p.splits);
   } else if (p.nb == 4) {
     launch_kernel((ksplit_gemm_kernel<RT, 4, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(64 * p.waves),
-                  ksplit_lds(p.waves, RT, 4), st, a);
+                  ksplit_lds(p.waves, RT, 4), st, a, p.splits);
   } else if (p.nb == 8) {
     launch_kernel((ksplit_gemm_kernel<RT, 8, EPI, FMT, 1>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 8),
-                  st, a);
+                  st, a, p.splits);
   } else {
     return hipErrorInvalidValue;
   }
@@ -1453,9 +1502,10 @@ hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, cons
     return hipGetLastError();
   }
   if (p.kind == 1) {
-    if (x_blocks != 1 || p.nb > 8 || p.waves < 1 || p.waves > 16 || a.K % p.waves ||
-        (a.K / p.waves) % (step * p.uc) || (p.waves > 8 && (p.rt != 1 || p.nb != 1)) || (fmt == FMT_INT4 && p.nb > 1 && p.waves > 4) ||
-        a.K / p.waves < 2 * step * p.uc)
+    if (x_blocks != 1 || p.nb > 8 || p.waves < 1 || p.waves > 16 || p.splits < 1 || a.K % (p.waves * p.splits) ||
+        (a.K / (p.waves * p.splits)) % (step * p.uc) || (p.waves > 8 && (p.rt != 1 || p.nb != 1)) ||
+        (fmt == FMT_INT4 && p.nb > 1 && p.waves > 4) || a.K / (p.waves * p.splits) < 2 * step * p.uc ||
+        (p.splits > 1 && (!a.part || !a.counters)))
       return hipErrorInvalidValue;
   } else {
     if (p.splits < 1 || a.K % p.splits || (x_blocks > 1 && p.splits > 1)) return hipErrorInvalidValue;

@@ -65,7 +65,8 @@ struct SkinnyArgs {
 //  kind 0 (row split): 4 waves x rt subtiles of 16 rows per workgroup share activation
 //    chunks of kc inputs staged in LDS; K split over `splits` workgroups.
 //  kind 1 (k split): one tile of 16*rt rows per workgroup, its `waves` waves each stream a
-//    contiguous 1/waves of K with activations read from L2; partial sums added through LDS.
+//    contiguous 1/waves of K with activations read from L2; partial sums added through LDS; K split
+//    over `splits` workgroups where that evens out the work per compute unit.
 //  kind 2 (dense): rt x (waves / rt) waves of 64 weight rows x 8*nb activation rows per
 //    workgroup, both operands staged in LDS; K split over `splits` workgroups (one activation
 //    tile only).
@@ -81,11 +82,15 @@ bool skinny_shape_ok(int fmt, int K);
 // force: 0 = chosen from the shape; > 0 = row split over `force` workgroups; < 0 = k split
 // over -force waves.
 SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, int force);
+// compute units the plans even the work over (the device's count; 256 until set)
+void set_plan_compute_units(int units);
+int plan_compute_units();
 // workspace bytes a plan needs for its partial tiles
 inline size_t skinny_part_bytes(const SkinnyPlan& p) {
   if (p.splits <= 1) return 0;
   if (p.kind == 2) return (size_t)p.row_blocks * p.splits * p.waves * 4 * p.nb * 32 * 4 * 4;  // hi + lo added
   if (p.kind == 3) return (size_t)p.row_blocks * p.splits * p.nb * 4 * 32 * 4 * 4;  // hi + lo added
+  if (p.kind == 1) return (size_t)p.row_blocks * p.splits * p.rt * p.nb * 4 * 64 * 4;  // raw sums
   return p.kind == 0 ? (size_t)p.row_blocks * p.splits * 4 * p.rt * p.nb * 4 * 64 * 4 : 0;
 }
 hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, const SkinnyPlan& p, hipStream_t st);

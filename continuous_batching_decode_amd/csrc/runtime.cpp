@@ -338,6 +338,12 @@ static cbd_status setup_weights(cbd_ctx* c, const cbd_weights* w) {
 
 static cbd_status setup_device(cbd_ctx* c) {
   const cbd_model_config& m = c->cfg;
+  {  // the products even their work out over the device's compute units
+    int dev = 0, units = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&units, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      set_plan_compute_units(units);
+  }
   const int rows = std::max(c->lim.max_batch, c->lim.max_prefill_tokens);
   c->rows_pad = (int)round_up(std::max(rows, 128), 128);  // whole 128-row tiles of the dense product
   const size_t R = (size_t)c->rows_pad;
