@@ -669,6 +669,9 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
 // workgroup (tile, s) adds the inputs [s K/splits, (s + 1) K/splits); the last workgroup of a tile
 // to arrive adds the partial tiles in order (agent-scope 16-byte accesses and an arrival counter, as
 // the row split).
+#ifndef CBD_DENSE_DEPTH
+#define CBD_DENSE_DEPTH 2
+#endif
 namespace {
 // LDS of a dense workgroup: two stages of (4 wn + nbw wm) fragments, 1/rms per activation row
 inline size_t dense_lds(int wn, int wm, int nbw) {
@@ -689,7 +692,7 @@ __global__ __launch_bounds__(64 * WN * WM, 2) void dense_gemm_kernel(SkinnyArgs 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int RT = 4, NB = NBW;          // a wave: 4 weight subtiles x NBW activation groups
   static_assert(NBW % 4 == 0, "activation groups come 4 at a time");
-  constexpr int D = 2;                     // register stages in flight
+  constexpr int D = CBD_DENSE_DEPTH;       // register stages in flight (even)
   constexpr int NW = WN * WM, NTH = 64 * NW;
   constexpr int TN = 64 * WN, TM = 8 * NBW * WM;  // weight rows and activation rows of the tile
   constexpr int NWF = 4 * WN, FR = NWF + NBW * WM;  // fragments per stage: weight subtiles, then groups
@@ -920,13 +923,13 @@ __global__ __launch_bounds__(64 * WN * WM, 2) void dense_gemm_kernel(SkinnyArgs 
 // and runs the epilogue of the groups its waves own.
 namespace {
 constexpr int kWideWaves = 4;
-inline size_t wide_lds(int nb) { return (size_t)kWideWaves * nb * 4 * 32 * 16 + 16 * 8 * nb * 4 + 8 * nb * 4; }
+inline size_t wide_lds(int nb, int rt) { return (size_t)kWideWaves * nb * rt * 32 * 16 + 16 * 8 * nb * 4 + 8 * nb * 4; }
 }  // namespace
 
-template <int EPI, int NB, int UC>
-__global__ __launch_bounds__(64 * kWideWaves, NB == 8 ? 1 : 2) void wide_ksplit_kernel(SkinnyArgs a, int splits) {
+template <int EPI, int NB, int UC, int RT>
+__global__ __launch_bounds__(64 * kWideWaves, (NB == 8 && RT == 4) ? 1 : 2) void wide_ksplit_kernel(SkinnyArgs a, int splits) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int RT = 4, NW = kWideWaves, NTH = 64 * NW, ROWS = 8 * NB;
+  constexpr int NW = kWideWaves, NTH = 64 * NW, ROWS = 8 * NB;
   f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);                          // [NW][NB][RT][32]
   float* npart = reinterpret_cast<float*>(smem + NW * NB * RT * 32 * 16);  // [16][ROWS]
   float* inv_s = npart + 16 * ROWS;                                        // [ROWS]
@@ -1223,13 +1226,15 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
                          : wide_nb == 4 ? (K >= 8192 || n_all >= 16384)
                                         : n_all <= 4096;
   if (force == 0 && CBD_WIDE_KS && fmt == FMT_BF16 && x_blocks == 1 && rows > CBD_WIDE_MIN_ROWS && rows <= 64 &&
-      wide_pick && (epi == EPI_SWIGLU ? N % 32 == 0 : N % 64 == 0)) {
+      wide_pick && (epi == EPI_SWIGLU ? N % 32 == 0 : N % 64 == 0)) {  // (whole tiles at 4 subtiles, so at 2)
     p.kind = 3;
-    p.rt = 4;
+    // 33..64 rows: 2 subtiles per wave on short K (O: 22.1 -> 18.4 us per layer at B = 64; two waves
+    // per SIMD instead of one), 4 on long K (down: 41.8 against 45.1 us with 2)
+    p.rt = (wide_nb == 8 && K < 8192) ? 2 : 4;
     p.waves = 4;
     p.nb = wide_nb;
     p.uc = p.nb == 8 ? CBD_WIDE_UC8 : CBD_WIDE_UC;
-    p.row_blocks = epi == EPI_SWIGLU ? N / 32 : N / 64;
+    p.row_blocks = epi == EPI_SWIGLU ? N / (8 * p.rt) : N / (16 * p.rt);
     p.splits = 1;
     const int unit = 4 * 32 * p.uc;  // inputs of one stage of the 4 waves
     if (K % (2 * unit) == 0) {
@@ -1482,19 +1487,21 @@ hipError_t launch_skinny_gemm(SkinnyArgs a, int epi, int fmt, int x_blocks, cons
   }
   if (p.kind == 3) {
     const int unit = 4 * 32 * p.uc;
-    const bool known = (p.nb == 2 && p.uc == CBD_WIDE_UC) || (p.nb == 4 && p.uc == CBD_WIDE_UC) || (p.nb == 8 && p.uc == CBD_WIDE_UC8);
-    if (fmt != FMT_BF16 || x_blocks != 1 || !known || p.rt != 4 || p.waves != 4 || a.rows < 1 || a.rows > 8 * p.nb ||
+    const bool known = (p.nb == 2 && p.uc == CBD_WIDE_UC && p.rt == 4) || (p.nb == 4 && p.uc == CBD_WIDE_UC && p.rt == 4) ||
+                       (p.nb == 8 && p.uc == CBD_WIDE_UC8 && (p.rt == 2 || p.rt == 4));
+    if (fmt != FMT_BF16 || x_blocks != 1 || !known || p.waves != 4 || a.rows < 1 || a.rows > 8 * p.nb ||
         p.splits < 1 || a.K % (p.splits * unit) || a.K / p.splits < 2 * unit || p.row_blocks < 1 ||
-        p.row_blocks != (epi == EPI_SWIGLU ? a.N / 32 : a.N / 64) || (p.splits > 1 && (!a.part || !a.counters)))
+        p.row_blocks != (epi == EPI_SWIGLU ? a.N / (8 * p.rt) : a.N / (16 * p.rt)) || (p.splits > 1 && (!a.part || !a.counters)))
       return hipErrorInvalidValue;
     const dim3 grid(p.row_blocks * p.splits), block(64 * kWideWaves);
-    const size_t lds = wide_lds(p.nb);
+    const size_t lds = wide_lds(p.nb, p.rt);
     auto go = [&](auto kernel) { launch_kernel(kernel, grid, block, lds, st, a, p.splits); };
     auto by_nb = [&](auto epi_c) {
       constexpr int E = decltype(epi_c)::value;
-      if (p.nb == 2) go(wide_ksplit_kernel<E, 2, CBD_WIDE_UC>);
-      else if (p.nb == 4) go(wide_ksplit_kernel<E, 4, CBD_WIDE_UC>);
-      else go(wide_ksplit_kernel<E, 8, CBD_WIDE_UC8>);
+      if (p.nb == 2) go(wide_ksplit_kernel<E, 2, CBD_WIDE_UC, 4>);
+      else if (p.nb == 4) go(wide_ksplit_kernel<E, 4, CBD_WIDE_UC, 4>);
+      else if (p.rt == 2) go(wide_ksplit_kernel<E, 8, CBD_WIDE_UC8, 2>);
+      else go(wide_ksplit_kernel<E, 8, CBD_WIDE_UC8, 4>);
     };
     if (epi == EPI_SWIGLU) by_nb(std::integral_constant<int, EPI_SWIGLU>{});
     else if (epi == EPI_RESIDUAL) by_nb(std::integral_constant<int, EPI_RESIDUAL>{});

@@ -70,7 +70,7 @@ struct SkinnyArgs {
 //  kind 2 (dense): rt x (waves / rt) waves of 64 weight rows x 8*nb activation rows per
 //    workgroup, both operands staged in LDS; K split over `splits` workgroups (one activation
 //    tile only).
-//  kind 3 (wide k split): 4 waves x 4 subtiles of 16 rows (64 weight rows) per workgroup, each wave
+//  kind 3 (wide k split): 4 waves x rt subtiles of 16 rows (16 rt weight rows) per workgroup, each wave
 //    a quarter of the workgroup's K range with all nb activation groups (activations read from
 //    L2); K split over `splits` workgroups; decode steps of 9..64 rows.
 struct SkinnyPlan {
@@ -89,7 +89,7 @@ int plan_compute_units();
 inline size_t skinny_part_bytes(const SkinnyPlan& p) {
   if (p.splits <= 1) return 0;
   if (p.kind == 2) return (size_t)p.row_blocks * p.splits * p.waves * 4 * p.nb * 32 * 4 * 4;  // hi + lo added
-  if (p.kind == 3) return (size_t)p.row_blocks * p.splits * p.nb * 4 * 32 * 4 * 4;  // hi + lo added
+  if (p.kind == 3) return (size_t)p.row_blocks * p.splits * p.nb * p.rt * 32 * 4 * 4;  // hi + lo added
   if (p.kind == 1) return (size_t)p.row_blocks * p.splits * p.rt * p.nb * 4 * 64 * 4;  // raw sums
   return p.kind == 0 ? (size_t)p.row_blocks * p.splits * 4 * p.rt * p.nb * 4 * 64 * 4 : 0;
 }
