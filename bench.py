@@ -106,6 +106,9 @@ def main():
     ap.add_argument("--ctx-lo", type=int, default=None)
     ap.add_argument("--ctx-hi", type=int, default=None)
     ap.add_argument("--workload", default="llama8b-b8", choices=sorted(WORKLOADS))
+    ap.add_argument("--prefill-chunk", type=int, default=2048,
+                    help="continuous workload: prefill tokens per tick (joiner prompts continue over ticks); "
+                         "0 = whole prompts per call")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a device buffer of this many MiB 5 times (a plain copy of known size, "
                          "used to calibrate HBM byte counters), then exit")
@@ -460,37 +463,52 @@ def run_continuous(args, wl, torch, cbd, synth):
         arrive = np.cumsum(rng.exponential(288.0 / (1.25 * cap), size=n_req))
         arrive -= arrive[0]
         waiting, live = 0, []  # live: [sid, generated, target, context]
+        pending = []  # admitted, prompt not yet fully prefilled: [sid, request, tokens done]
         dec_ev, pf_ev = [], []
         dec_rows = pf_tokens = done = 0
+        max_stall_ms = 0.0
         step_bytes = 0.0
         tick = 0
+        chunk = args.prefill_chunk if args.prefill_chunk > 0 else 16384
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         while done < n_req:
-            joiners = []
-            tot = 0
-            while (waiting < n_req and arrive[waiting] <= tick and len(live) + len(joiners) < cap
-                   and len(joiners) < 16 and tot + plens[waiting] <= 16384):
+            while waiting < n_req and arrive[waiting] <= tick and len(live) + len(pending) < cap:
                 try:
                     sid = eng.alloc(int(plens[waiting] + glens[waiting]))
                 except cbd.CbdError:
                     break  # arena full: the request waits
-                joiners.append((sid, waiting))
-                tot += int(plens[waiting])
+                pending.append([sid, waiting, 0])
                 waiting += 1
-            if joiners:
-                toks = torch.from_numpy(np.concatenate([prompts[i] for _, i in joiners]).astype(np.int32)).to(dev)
+            # one prefill call per tick: the pending prompts in arrival order, at most `chunk` tokens in
+            # all (a prompt may continue over several ticks; --prefill-chunk 0: whole prompts)
+            segs, budget = [], chunk
+            for q in pending:
+                if len(segs) == 16 or budget == 0:
+                    break
+                rest = int(plens[q[1]]) - q[2]
+                if args.prefill_chunk <= 0 and rest > budget:
+                    break
+                take = min(rest, budget)
+                segs.append((q, take))
+                budget -= take
+            if segs:
+                toks = torch.from_numpy(np.concatenate([prompts[q[1]][q[2]:q[2] + n] for q, n in segs])
+                                        .astype(np.int32)).to(dev)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                eng.prefill_segmented([sd for sd, _ in joiners], [int(plens[i]) for _, i in joiners], toks,
-                                      pf_logits[:len(joiners)], pf_next[:len(joiners)])
+                eng.prefill_segmented([q[0] for q, _ in segs], [n for _, n in segs], toks,
+                                      pf_logits[:len(segs)], pf_next[:len(segs)])
                 e1.record()
                 pf_ev.append((e0, e1))
-                sids = torch.tensor([sd for sd, _ in joiners], dtype=torch.int64, device=dev)
-                tok_by_sid.index_copy_(0, sids, pf_next[:len(joiners)])
-                pf_tokens += tot
-                for sd, i in joiners:
-                    live.append([sd, 1, int(glens[i]), int(plens[i])])  # the prefill gave token 1
+                sids = torch.tensor([q[0] for q, _ in segs], dtype=torch.int64, device=dev)
+                tok_by_sid.index_copy_(0, sids, pf_next[:len(segs)])
+                for q, n in segs:
+                    q[2] += n
+                    pf_tokens += n
+                    if q[2] == int(plens[q[1]]):  # prompt complete: the last chunk's argmax is token 1
+                        live.append([q[0], 1, int(glens[q[1]]), int(plens[q[1]])])
+                pending = [q for q in pending if q[2] < int(plens[q[1]])]
             if live:
                 ids = [r[0] for r in live]
                 idx = torch.tensor(ids, dtype=torch.int64, device=dev)
@@ -514,17 +532,19 @@ def run_continuous(args, wl, torch, cbd, synth):
                         keep.append(r)
                 live = keep
                 tick += 1
-            elif waiting < n_req and not joiners:
+            elif waiting < n_req and not segs and not pending:
                 tick = max(tick + 1, int(np.ceil(arrive[waiting])))
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
         dec_ms = sum(a.elapsed_time(b) for a, b in dec_ev)
         pf_ms = sum(a.elapsed_time(b) for a, b in pf_ev)
+        max_stall_ms = max([a.elapsed_time(b) for a, b in pf_ev] + [0.0])
         gen = int(glens.sum())
         results[str(cap)] = {
             "requests": n_req, "decode_steps": len(dec_ev), "mean_live_rows": round(dec_rows / max(1, len(dec_ev)), 2),
             "decode_tok_s": round(dec_rows / (dec_ms * 1e-3), 1), "decode_ms": round(dec_ms, 1),
             "prefill_calls": len(pf_ev), "prefill_tokens": pf_tokens, "prefill_ms": round(pf_ms, 1),
+            "longest_prefill_call_ms": round(max_stall_ms, 1),
             "prefill_tok_s": round(pf_tokens / (pf_ms * 1e-3), 1) if pf_ms else None,
             "wall_tok_s": round(gen / wall, 1), "wall_s": round(wall, 2),
             "decode_GBps": round(step_bytes / (dec_ms * 1e-3) / 1e9, 1)}
@@ -535,8 +555,10 @@ def run_continuous(args, wl, torch, cbd, synth):
            "ms_per_step": round(top["decode_ms"] / max(1, top["decode_steps"]), 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "continuous: %s, caps %s, Poisson arrivals (offered 1.25 x cap), prompts U[%d,%d] "
-                                  "with a 1024-token shared prefix, generation U[64,512], %d requests per cap = 4 cap + 8"
-                                  % (shape.name, caps, args.ctx_lo, args.ctx_hi, 4 * max(caps) + 8),
+                                  "with a 1024-token shared prefix, generation U[64,512], %d requests per cap = 4 cap + 8; "
+                                  "admission %s" % (shape.name, caps, args.ctx_lo, args.ctx_hi, 4 * max(caps) + 8,
+                                                    "in chunks of at most %d tokens per tick" % args.prefill_chunk
+                                                    if args.prefill_chunk > 0 else "of whole prompts"),
                       "parallelism": "single GPU"},
            "caps": results}
     eng.close()

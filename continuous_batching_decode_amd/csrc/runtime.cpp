@@ -874,9 +874,10 @@ extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, cons
     for (int j = 0; j < i; ++j)
       if (seq_ids[j] == seq_ids[i]) return fail(CBD_E_INVAL, "prefill_segmented: duplicate sequence id %d", seq_ids[i]);
     if (seg_lens[i] < 1) return fail(CBD_E_INVAL, "prefill_segmented: segment %d has length %d", i, seg_lens[i]);
-    if (s->len != 0) return fail(CBD_E_INVAL, "prefill_segmented: sequence %d is not empty", seq_ids[i]);
-    if (seg_lens[i] > s->cap || seg_lens[i] > c->cfg.max_position)
-      return fail(CBD_E_CAPACITY, "prefill_segmented: segment of %d tokens exceeds slab %d", seg_lens[i], seq_ids[i]);
+    // a segment continues its sequence: positions len .. len + L - 1 (len = 0 for a fresh slab)
+    if ((int64_t)s->len + seg_lens[i] > s->cap || (int64_t)s->len + seg_lens[i] > c->cfg.max_position)
+      return fail(CBD_E_CAPACITY, "prefill_segmented: %d tokens after %d exceed slab %d (capacity %d)", seg_lens[i],
+                  s->len, seq_ids[i], s->cap);
     T += seg_lens[i];
   }
   if (T > c->lim.max_prefill_tokens)
@@ -892,14 +893,16 @@ extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, cons
   RowMeta* rows = reinterpret_cast<RowMeta*>(host);
   AttnItem* items = reinterpret_cast<AttnItem*>(host + items_off);
   int32_t* last_idx = reinterpret_cast<int32_t*>(host + idx_off);
-  // attention items: tiles of up to 16 consecutive queries of one segment (keys 0 .. end of tile),
-  // the longest first so the grid's tail is short
+  // attention items: tiles of up to 16 consecutive queries of one segment (keys 0 .. end of tile:
+  // the sequence's earlier keys, then the segment's own up to each query), the longest first so the
+  // grid's tail is short
   int g = 0, n_items = 0;
   for (int i = 0; i < K; ++i) {
     const Slab& s = c->slabs[seq_ids[i]];
-    for (int p = 0; p < seg_lens[i]; ++p) rows[g + p] = RowMeta{s.off, s.stride, p};
+    const int t0 = s.len;
+    for (int p = 0; p < seg_lens[i]; ++p) rows[g + p] = RowMeta{s.off, s.stride, t0 + p};
     for (int p0 = 0; p0 < seg_lens[i]; p0 += 16)
-      items[n_items++] = AttnItem{s.off, s.stride, p0, g + p0, 0, std::min(p0 + 16, seg_lens[i]), -1};
+      items[n_items++] = AttnItem{s.off, s.stride, t0 + p0, g + p0, 0, t0 + std::min(p0 + 16, seg_lens[i]), -1};
     g += seg_lens[i];
     last_idx[i] = g - 1;
   }
@@ -912,7 +915,8 @@ extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, cons
   const cbd_model_config& m = c->cfg;
   const int x_blocks = (int)((T + 63) / 64);
   double kv_keys = 0;
-  for (int i = 0; i < K; ++i) kv_keys += 0.5 * (double)seg_lens[i] * (seg_lens[i] + 1);
+  for (int i = 0; i < K; ++i)
+    kv_keys += (double)seg_lens[i] * c->slabs[seq_ids[i]].len + 0.5 * (double)seg_lens[i] * (seg_lens[i] + 1);
   {
     ProfScope p(c, CBD_KERNEL_EMBED, T * (double)m.d_model * 12.0, 0, st);
     HIP_TRY(launch_embed(tokens_dev, (int)T, c->embed, m.vocab, m.d_model, c->layers[0].attn_norm, c->h, c->xa,
@@ -921,7 +925,7 @@ extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, cons
   }
   if (cbd_status s = run_layers(c, (int)T, x_blocks, meta_d, items_d, n_items, nullptr, 0, kv_keys, st)) return s;
   if (cbd_status s = run_head(c, idx_d, K, last_logits_dev, next_tokens_dev, st)) return s;
-  for (int i = 0; i < K; ++i) c->slabs[seq_ids[i]].len = seg_lens[i];
+  for (int i = 0; i < K; ++i) c->slabs[seq_ids[i]].len += seg_lens[i];
   c->stats.prefill_calls += 1;
   c->stats.prefill_tokens += T;
   return CBD_OK;

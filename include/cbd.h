@@ -220,16 +220,22 @@ cbd_status decode_step_batch(cbd_ctx* ctx, const int32_t* seq_ids, int32_t B, co
                              float* logits_dev, int32_t* next_tokens_dev, cbd_stream stream);
 
 /*
- * Segmented prefill of K distinct live sequences with empty slabs.
+ * Segmented prefill of K distinct live sequences.
  *  seq_ids     host int32 [K]
  *  seg_lens    host int32 [K], each >= 1
  *  tokens_dev  device int32 [sum(seg_lens)]: the segments back to back
  *  last_logits_dev  device fp32 [K, vocab]: logits of each segment's last token
  *  next_tokens_dev  device int32 [K] or NULL: their greedy argmax
- * Segment s is written to its slab at positions 0..len_s-1 and its length
- * becomes len_s. K = 0 is a no-op. CBD_E_INVAL: zero-length segment,
- * duplicate id, a non-empty slab, K > max_segments, or the total above
- * max_prefill_tokens; CBD_E_CAPACITY: a segment longer than its slab.
+ * Segment s continues its sequence: with t = kvslab_len(seq_ids[s]) before the
+ * call (0 for a fresh slab), its tokens take positions t..t+len_s-1, attend to
+ * the sequence's keys 0..own position (earlier chunks and decoded tokens
+ * included, never another sequence's), are written to the slab there, and the
+ * length becomes t + len_s. A long prompt can so be admitted in chunks with
+ * decode steps in between (page "Batching", section 4.2: joiner prefill one
+ * chunk of at most 2048 tokens per loop iteration, one decode step between
+ * chunks). K = 0 is a no-op. CBD_E_INVAL: zero-length segment, duplicate id,
+ * K > max_segments, or the total above max_prefill_tokens; CBD_E_CAPACITY:
+ * t + len_s above the slab's capacity or max_position.
  */
 cbd_status prefill_segmented(cbd_ctx* ctx, const int32_t* seq_ids, const int32_t* seg_lens, int32_t K,
                              const int32_t* tokens_dev, float* last_logits_dev, int32_t* next_tokens_dev,

@@ -408,6 +408,64 @@ def test_segmented_prefill_no_leakage_gpu(torch, cbd):
         compare_slab_bits(s1[j][0], np.stack(orc.seqs[o].k), "K")
 
 
+def test_chunked_prefill_continuation(torch, cbd):
+    """Prefill segments that continue their sequences (chunked admission with decode steps between):
+    sequence 0's prompt in chunks of 64, 50 and 36 tokens (starts at 0, 64, 114); sequence 1 prefilled,
+    decoded two steps, then continued with 17 more prompt tokens (start 42); sequence 2 fresh in the
+    second call. Every call's last logits, every decode step and the final slabs against the oracle."""
+    _say("chunked prefill continuation")
+    from oracle import OracleModel, greedy
+    shape = MID
+    w = synth.make_weights(shape, seed=6)
+    p0, p1, p1b, p2 = synth.prompts(21, [150, 40, 17, 20], shape.vocab)
+    eng = cbd.Engine(w, arena_bytes=16 * 256 * shape.kv_bytes_per_token(), max_batch=8, max_prefill_tokens=256,
+                     max_position=1024)
+    orc = OracleModel(w, cache_all_layers=True)
+    ids = [eng.alloc(256) for _ in range(3)]
+    oids = [orc.new_sequence() for _ in range(3)]
+
+    def prefill(rows, segs, what):
+        toks = torch.from_numpy(np.concatenate(segs).astype(np.int32)).cuda()
+        lg = torch.empty((len(rows), shape.vocab), dtype=torch.float32, device="cuda")
+        nx = torch.empty(len(rows), dtype=torch.int32, device="cuda")
+        eng.prefill_segmented([ids[r] for r in rows], [len(x) for x in segs], toks, lg, nx)
+        ref = orc.prefill_segmented([oids[r] for r in rows], segs)
+        torch.cuda.synchronize()
+        errs = assert_logits_close(lg.cpu().numpy(), ref, what)
+        check_greedy(nx.cpu().numpy(), ref, errs, what)
+        return greedy(ref)
+
+    def decode(rows, toks, what):
+        lg = torch.empty((len(rows), shape.vocab), dtype=torch.float32, device="cuda")
+        nx = torch.empty(len(rows), dtype=torch.int32, device="cuda")
+        eng.decode_step_batch([ids[r] for r in rows], torch.from_numpy(np.asarray(toks, dtype=np.int32)).cuda(), lg, nx)
+        ref = orc.decode_step_batch([oids[r] for r in rows], np.asarray(toks, dtype=np.int64))
+        torch.cuda.synchronize()
+        errs = assert_logits_close(lg.cpu().numpy(), ref, what)
+        check_greedy(nx.cpu().numpy(), ref, errs, what)
+        return greedy(ref)
+
+    t = prefill([0, 1], [p0[:64], p1], "call 1")
+    t1 = decode([1], [t[1]], "decode 1")
+    t = prefill([0, 2], [p0[64:114], p2], "call 2 (sequence 0 from 64, sequence 2 fresh)")
+    t12 = decode([1, 2], [t1[0], t[1]], "decode 2")
+    t = prefill([0, 1], [p0[114:], p1b], "call 3 (sequence 0 from 114, sequence 1 from 42)")
+    decode([0, 1, 2], [t[0], t[1], t12[1]], "decode 3")
+    for i, o, n in zip(ids, oids, [151, 60, 22]):
+        assert eng.length(i) == n == orc.seqs[o].length
+        k, v = eng.read(i, 0, n)
+        torch.cuda.synchronize()
+        compare_slab_bits(k.cpu().numpy(), np.stack(orc.seqs[o].k), "K slab %d" % i)
+        compare_slab_bits(v.cpu().numpy(), np.stack(orc.seqs[o].v), "V slab %d" % i)
+    # a continuation that would pass the slab's capacity is rejected without changing it
+    big = torch.zeros(256, dtype=torch.int32, device="cuda")
+    lg = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
+    with pytest.raises(cbd.CbdError) as e:
+        eng.prefill_segmented([ids[0]], [106], big, lg)
+    assert e.value.status == cbd.CBD_E_CAPACITY and eng.length(ids[0]) == 151
+    eng.close()
+
+
 def test_int4_model_decode(torch, cbd):
     """int4-affine weights through prefill and 3 teacher-forced steps."""
     _say("int4 model")

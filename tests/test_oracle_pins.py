@@ -253,6 +253,32 @@ def test_prefill_equals_sequential_decode():
         assert (diff == 0).mean() >= 0.999 and diff.max() <= 1
 
 
+def test_chunked_prefill_equals_whole():
+    """A prompt prefilled in chunks (each continuing from the sequence's length, as a joiner admitted
+    one chunk per iteration) gives the whole prompt's last logits and slab: a token's computation
+    depends only on the keys at positions up to its own."""
+    w = synth.make_weights(synth.TINY, seed=5, gain_std=0.1)
+    pr = synth.prompts(9, [23], synth.TINY.vocab)[0]
+    a = OracleModel(w, cache_all_layers=True)
+    sa = a.new_sequence()
+    la = a.prefill(sa, pr)
+    b = OracleModel(w, cache_all_layers=True)
+    sb = b.new_sequence()
+    for lo, hi in ((0, 7), (7, 16), (16, 23)):
+        lb = b.prefill_segmented([sb], [pr[lo:hi]])[0]
+        assert b.seqs[sb].length == hi
+    assert np.allclose(la, lb, rtol=1e-9, atol=1e-9)
+    for l in range(synth.TINY.n_layers):
+        for x, y in ((a.seqs[sa].k[l], b.seqs[sb].k[l]), (a.seqs[sa].v[l], b.seqs[sb].v[l])):
+            assert x.shape == y.shape == (23, 2, 64)
+            diff = np.abs(x.astype(np.int32) - y.astype(np.int32))
+            assert (diff == 0).mean() >= 0.999 and diff.max() <= 1
+    # a chunk's first token sees the earlier chunks: the same chunk alone on a fresh sequence differs
+    c = OracleModel(w, cache_all_layers=True)
+    sc = c.new_sequence()
+    assert not np.allclose(c.prefill(sc, pr[16:23]), lb)
+
+
 def test_no_cross_segment_leakage():
     """Changing one segment's tokens leaves every other segment's logits and slab bitwise unchanged."""
     w = synth.make_weights(synth.TINY, seed=2, gain_std=0.1)
