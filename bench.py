@@ -265,6 +265,31 @@ def main():
                          "launches_per_step": v["launches"] // nb} for k, v in p.items()}
         log("breakdown (event-timed, %d steps): %s" % (nb, json.dumps(breakdown)))
 
+    # seeded top-p sampling of the step's logits rows (temperature 0.8, top_p 0.95), beside greedy argmax
+    sampling = None
+    if not args.no_breakdown:
+        s_t, s_p, s_seed = [0.8] * B, [0.95] * B, list(range(1, B + 1))
+        s_out = torch.empty(B, dtype=torch.int32, device=dev)
+        g_out = torch.empty(B, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            eng.sample_top_p(logits[:B], s_t, s_p, s_seed, [0] * B, s_out)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        for i in range(50):
+            eng.sample_top_p(logits[:B], s_t, s_p, s_seed, [i] * B, s_out)
+        ev[1].record()
+        for i in range(50):
+            eng.greedy_argmax(logits[:B], g_out)
+        ev[2].record()
+        torch.cuda.synchronize()
+        samp_logits = logits[:B].cpu().numpy().astype(np.float64)
+        sampling = {"rows": B, "vocab": V, "temperature": 0.8, "top_p": 0.95,
+                    "sample_us_per_call": round(ev[0].elapsed_time(ev[1]) * 1e3 / 50, 2),
+                    "argmax_us_per_call": round(ev[1].elapsed_time(ev[2]) * 1e3 / 50, 2),
+                    "sample_index": 49, "tokens": [int(x) for x in s_out.cpu().numpy()]}
+        log("sampling: %s" % json.dumps({k: v for k, v in sampling.items() if k != "tokens"}))
+
     sweep_out = {}
     for b in sweep:
         sids = ids[:b]
@@ -311,6 +336,11 @@ def main():
         parity = {"max_rel_err": float(np.max(errs)), "tol": 1e-2,
                   "greedy_match": int(np.sum(greedy(first_logits) == greedy(ref))), "rows": B}
         log("cpu baseline %.2f s/step; parity %s" % (csecs, parity))
+        if sampling is not None:
+            # the sampled tokens against the oracle's selection on the same (GPU) logits rows
+            from oracle import sample_rows
+            want = sample_rows(samp_logits, [0.8] * B, [0.95] * B, list(range(1, B + 1)), [49] * B)
+            sampling["oracle_match"] = int(np.sum(want == np.array(sampling["tokens"])))
 
     out = {"metric": METRIC, "value": round(tokps, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -322,7 +352,7 @@ def main():
            "achieved_hbm_GBps": round(step_gbps, 1), "step_bytes": step_bytes,
            "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),
            "roofline": roofline, "cpu_baseline": cpu, "parity_first_step": parity, "sweep": sweep_out,
-           "kernel_breakdown": breakdown}
+           "kernel_breakdown": breakdown, "sampling": sampling}
     eng.close()
     print(json.dumps(out), flush=True)
 

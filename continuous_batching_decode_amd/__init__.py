@@ -25,10 +25,10 @@ WEIGHTS_BF16, WEIGHTS_INT4 = 0, 1
 EXPORTS = ["cbd_kv_bytes_per_token", "cbd_slab_granule_tokens", "cbd_create", "cbd_destroy", "cbd_last_error",
            "cbd_stats", "kvslab_alloc", "kvslab_free", "kvslab_len", "kvslab_capacity", "kvslab_append",
            "kvslab_read", "decode_step_batch", "prefill_segmented", "greedy_argmax", "cbd_linear", "cbd_pack_int4",
-           "cbd_profile_begin", "cbd_profile_end", "cbd_pack_bf16"]
+           "cbd_profile_begin", "cbd_profile_end", "cbd_pack_bf16", "sample_top_p"]
 
 KERNEL_KINDS = ["embed", "norm", "qkv", "rope_append", "attention", "attn_combine", "o_proj", "gate_up", "down",
-                "lm_head", "argmax"]
+                "lm_head", "argmax", "sample"]
 
 
 class CbdError(RuntimeError):
@@ -96,6 +96,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "decode_step_batch": (i32, [ctx_p, P(i32), i32, vp, vp, vp, vp]),
         "prefill_segmented": (i32, [ctx_p, P(i32), P(i32), i32, vp, vp, vp, vp]),
         "greedy_argmax": (i32, [ctx_p, vp, i32, vp, vp]),
+        "sample_top_p": (i32, [ctx_p, vp, i32, P(ctypes.c_float), P(ctypes.c_float), P(ctypes.c_uint64),
+                               P(ctypes.c_uint64), vp, vp]),
         "cbd_linear": (i32, [ctx_p, P(Matrix), i32, i32, vp, i32, vp, i32, vp]),
         "cbd_pack_int4": (i32, [vp, vp, vp, i64, i64, vp, vp]),
         "cbd_profile_begin": (i32, [ctx_p, ctypes.c_uint32, i32, i32]),
@@ -298,6 +300,15 @@ class Engine:
     def greedy_argmax(self, logits_dev, tokens_dev, stream=None) -> None:
         _check(self.lib.greedy_argmax(self.ctx, logits_dev.data_ptr(), int(logits_dev.shape[0]),
                                       tokens_dev.data_ptr(), _stream_ptr(stream)))
+
+    def sample_top_p(self, logits_dev, temperature, top_p, seeds, sample_index, tokens_dev, stream=None) -> None:
+        """Seeded temperature / top-p sampling of each logits row (host lists of per-row parameters)."""
+        rows = int(logits_dev.shape[0])
+        F = ctypes.c_float * max(rows, 1)
+        U = ctypes.c_uint64 * max(rows, 1)
+        _check(self.lib.sample_top_p(self.ctx, logits_dev.data_ptr(), rows, F(*[float(x) for x in temperature]),
+                                     F(*[float(x) for x in top_p]), U(*[int(x) for x in seeds]),
+                                     U(*[int(x) for x in sample_index]), tokens_dev.data_ptr(), _stream_ptr(stream)))
 
     def linear(self, w_ptrs: Matrix, N: int, K: int, x_dev, y_dev, splits: int = 0, stream=None) -> None:
         """y_dev[b] = W x_dev[b]; x_dev fp32 [rows, K] device tensor, y_dev fp32 [rows, N]."""

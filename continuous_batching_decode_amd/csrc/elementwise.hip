@@ -280,4 +280,305 @@ hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int po
   return hipGetLastError();
 }
 
+
+// ============================================================================ seeded top-p sampling
+// Row r (one workgroup of 1024 threads): temperature T_r, nucleus mass p_r, draw from Philox4x64-10
+// with key (seed_r, 0) and counter (index_r, 0, 0, 0). T_r = 0 is greedy (lowest id among maxima).
+// Otherwise e_i = exp(z_i - max z) with z = logit / T, in fixed point w_i = floor(e_i 2^40) (integer
+// masses: every comparison below is exact and order-free). The nucleus is the shortest prefix of the
+// ids ordered by e descending (ties: lower id first) whose mass reaches floor(p_r W), W = sum w; the
+// token is the first of that order whose running mass exceeds floor(u M), M = nucleus mass, u the
+// 24-bit draw. Both searches descend the bit patterns of e (order-preserving for positive floats) in
+// three radix levels of 11, 11 and 10 bits with mass and count histograms in LDS; the ties at the
+// final pattern are resolved in id order with a scan of per-thread counts over contiguous chunks.
+namespace {
+constexpr int kSampleThreads = 1024;
+constexpr uint64_t kFix = 1ull << 40;
+
+CBD_DEVICE uint64_t mulhi64(uint64_t a, uint64_t b) { return __umul64hi(a, b); }
+
+// Philox4x64-10 word 0 for counter (ctr, 0, 0, 0) and key (k0, 0)
+CBD_DEVICE uint64_t philox_word0(uint64_t ctr, uint64_t k0) {
+  uint64_t c0 = ctr, c1 = 0, c2 = 0, c3 = 0, k1 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t h0 = mulhi64(c0, 0xD2E7470EE14C6C93ull), l0 = c0 * 0xD2E7470EE14C6C93ull;
+    const uint64_t h1 = mulhi64(c2, 0xCA5A826395121157ull), l1 = c2 * 0xCA5A826395121157ull;
+    const uint64_t n0 = h1 ^ c1 ^ k0, n2 = h0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = l1;
+    c2 = n2;
+    c3 = l0;
+    k0 += 0x9E3779B97F4A7C15ull;
+    k1 += 0xBB67AE8584CAA73Bull;
+  }
+  return c0;
+}
+
+template <typename T>
+CBD_DEVICE T block_sum(T v, T* red) {  // fixed order: lanes by xor tree, then the 16 waves in order
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  T s = 0;
+  for (int i = 0; i < kSampleThreads / 64; ++i) s += red[i];
+  return s;
+}
+
+CBD_DEVICE float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float m = red[0];
+  for (int i = 1; i < kSampleThreads / 64; ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+}  // namespace
+
+__global__ __launch_bounds__(kSampleThreads) void sample_top_p_kernel(const float* logits, int vocab, SampleArgs p,
+                                                                      int32_t* out) {
+  __shared__ uint64_t hmass[2048];
+  __shared__ uint32_t hcount[1024];
+  __shared__ uint64_t red64[kSampleThreads / 64];
+  __shared__ float redf[kSampleThreads / 64];
+  __shared__ uint32_t red32[kSampleThreads / 64];
+  __shared__ uint32_t s_bin;
+  __shared__ uint64_t s_above;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* row = logits + (int64_t)r * vocab;
+  const float4* row4 = reinterpret_cast<const float4*>(row);
+  const float temp = p.temperature[r];
+  const int n4 = vocab >> 2;  // vocab % 4 == 0 (checked by the host)
+  // Every pass visits the thread's float4s q = tid + 1024 i in increasing order, 8 loads in flight
+  // (clamped indices, so the loads are unconditional).
+  constexpr int UNR = 8;
+  auto pass = [&](auto&& visit) {
+    for (int q0 = tid; q0 < n4; q0 += UNR * kSampleThreads) {
+      float4 xb[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) xb[u] = row4[min(q0 + u * kSampleThreads, n4 - 1)];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+        if (q0 + u * kSampleThreads < n4) {
+          const int v = 4 * (q0 + u * kSampleThreads);
+          visit(xb[u].x, v);
+          visit(xb[u].y, v + 1);
+          visit(xb[u].z, v + 2);
+          visit(xb[u].w, v + 3);
+        }
+    }
+  };
+
+  if (temp == 0.f) {  // greedy: strict > in id order per thread, then (max, lowest id) over the block
+    float best = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    pass([&](float x, int v) {
+      if (x > best || (x == best && v < bi)) {
+        best = x;
+        bi = v;
+      }
+    });
+    const float m = block_max(best, redf);
+    uint32_t cand = (best == m) ? (uint32_t)bi : 0x7FFFFFFFu;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cand = min(cand, (uint32_t)__shfl_xor((int)cand, o, 64));
+    __syncthreads();
+    if ((tid & 63) == 0) red32[tid >> 6] = cand;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t bb = red32[0];
+      for (int i = 1; i < kSampleThreads / 64; ++i) bb = min(bb, red32[i]);
+      out[r] = bb == 0x7FFFFFFFu ? 0 : (int32_t)bb;  // every logit NaN: token 0
+    }
+    return;
+  }
+
+  const float inv_t = 1.0f / temp;
+  // max of z (NaN logits are skipped: they never win and weigh nothing)
+  float mz = -INFINITY;
+  pass([&](float x, int) { mz = fmaxf(mz, x * inv_t); });
+  mz = block_max(mz, redf);
+  // bit pattern of e = exp(z - max z) (0 for NaN) and its fixed-point mass floor(e 2^40): the
+  // mantissa shifted by the exponent (exact; 0 below 2^-40)
+  auto weight = [&](float x, uint32_t& bits) -> uint64_t {
+    const float e = __expf(x * inv_t - mz);
+    bits = (e == e) ? __float_as_uint(e) : 0u;
+    const int ex = (int)(bits >> 23);  // biased exponent; e <= 1 so ex <= 127
+    const uint64_t man = (uint64_t)((bits & 0x7FFFFFu) | 0x800000u);
+    const int sh = ex - 110;  // e 2^40 = man 2^(ex - 127 - 23 + 40)
+    return ex == 0 ? 0ull : sh >= 0 ? man << sh : (sh > -24 ? man >> (-sh) : 0ull);
+  };
+  uint64_t tw = 0;
+  pass([&](float x, int) {
+    uint32_t bb;
+    tw += weight(x, bb);
+  });
+  const uint64_t W = block_sum<uint64_t>(tw, red64);
+
+  // One radix descent over the patterns of positive weights: the largest pattern P such that the
+  // mass of the patterns above P (the ties at `cap_bits` counted as `cap_excess` lighter) plus the
+  // mass at P crosses `target` (>= when ge, else >). Returns P, the mass strictly above it and the
+  // number of tokens at it.
+  auto descend = [&](uint64_t target, bool ge, uint32_t cap_bits, uint64_t cap_excess, uint32_t& pat,
+                     uint64_t& above, uint32_t& cnt) {
+    uint32_t prefix = 0;
+    above = 0;
+    const int widths[3] = {11, 11, 10};
+    int shift = 32;
+    for (int lv = 0; lv < 3; ++lv) {
+      const int wb = widths[lv];
+      shift -= wb;
+      const int nb = 1 << wb;
+      for (int i = tid; i < nb; i += kSampleThreads) {
+        hmass[i] = 0;
+        if (lv == 2) hcount[i] = 0;
+      }
+      __syncthreads();
+      pass([&](float x, int) {
+        uint32_t bb;
+        const uint64_t w = weight(x, bb);
+        if (w != 0 && (shift + wb == 32 || (bb >> (shift + wb)) == prefix)) {
+          const int bin = (bb >> shift) & (nb - 1);
+          atomicAdd(reinterpret_cast<unsigned long long*>(&hmass[bin]), (unsigned long long)w);
+          if (lv == 2) atomicAdd(&hcount[bin], 1u);
+        }
+      });
+      __syncthreads();
+      if (tid == 0 && cap_excess && (shift + wb == 32 || (cap_bits >> (shift + wb)) == prefix))
+        hmass[(cap_bits >> shift) & (nb - 1)] -= cap_excess;
+      __syncthreads();
+      // running mass from the top bin down: thread t holds bins nb-1-2t and nb-2-2t; a scan over the
+      // threads gives each pair the mass above it, and the one pair where the running mass crosses
+      // the target names the bin
+      const int bh = nb - 1 - 2 * tid, bl = bh - 1;
+      const uint64_t mh = bh >= 0 ? hmass[bh] : 0ull, ml = bl >= 0 ? hmass[bl] : 0ull;
+      const uint64_t pr = mh + ml;
+      uint64_t incl = pr;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(incl, o, 64);
+        if ((tid & 63) >= o) incl += y;
+      }
+      if ((tid & 63) == 63) red64[tid >> 6] = incl;
+      if (tid == 0) {
+        s_bin = 0;  // (unreachable fallback: the lowest bin)
+        s_above = above;
+      }
+      __syncthreads();
+      uint64_t a0 = above + incl - pr;
+      for (int i = 0; i < (tid >> 6); ++i) a0 += red64[i];
+      auto crossed = [&](uint64_t m) { return ge ? m >= target : m > target; };
+      if (bh >= 0 && !crossed(a0)) {
+        if (crossed(a0 + mh)) {
+          s_bin = (uint32_t)bh;
+          s_above = a0;
+        } else if (bl >= 0 && crossed(a0 + pr)) {
+          s_bin = (uint32_t)bl;
+          s_above = a0 + mh;
+        }
+      }
+      __syncthreads();
+      prefix = (prefix << wb) | s_bin;
+      above = s_above;
+      if (lv == 2) cnt = hcount[s_bin];
+      __syncthreads();
+    }
+    pat = prefix;
+  };
+  auto fixed_of = [&](uint32_t bits) -> uint64_t {  // the weight of a pattern (as in weight())
+    const int ex = (int)(bits >> 23);
+    const uint64_t man = (uint64_t)((bits & 0x7FFFFFu) | 0x800000u);
+    const int sh = ex - 110;
+    return ex == 0 ? 0ull : sh >= 0 ? man << sh : (sh > -24 ? man >> (-sh) : 0ull);
+  };
+
+  // nucleus boundary: pattern theta, the mass above it, its tie count and how many ties it keeps
+  const uint64_t target = (uint64_t)((double)p.top_p[r] * (double)W);
+  uint32_t th, nt;
+  uint64_t above_th;
+  descend(target > 0 ? target : 1, true, 0u, 0ull, th, above_th, nt);
+  const uint64_t wth = fixed_of(th);
+  uint64_t keep = wth ? (target > above_th ? (target - above_th + wth - 1) / wth : 1) : nt;
+  keep = keep < 1 ? 1 : (keep > nt ? nt : keep);
+  const uint64_t M = above_th + keep * wth;
+  // the draw and its point t = floor(u M) in the nucleus mass (exact: u has 24 bits)
+  const uint64_t u24 = philox_word0(p.index[r], p.seed[r]) >> 40;
+  const uint64_t t = u24 * (M >> 24) + ((u24 * (M & 0xFFFFFFull)) >> 24);
+  uint32_t ph, nph;
+  uint64_t above_ph;
+  descend(t, false, th, (uint64_t)(nt - keep) * wth, ph, above_ph, nph);
+  const uint64_t wph = fixed_of(ph);
+  uint64_t j = wph ? (t - above_ph) / wph : 0;
+  const uint64_t avail = ph == th ? keep : nph;
+  if (j >= avail) j = avail ? avail - 1 : 0;
+  // the j-th id (ascending) among the tokens with pattern ph: per-thread counts over contiguous
+  // chunks of CH float4s, an exclusive scan, then the owner picks (token 0 stands if no weight is
+  // positive)
+  if (tid == 0) out[r] = 0;
+  const int CH = (n4 + kSampleThreads - 1) / kSampleThreads;
+  const int c0 = tid * CH, c1 = min(n4, c0 + CH);
+  uint32_t mine = 0;
+  for (int q0 = c0; q0 < c1; q0 += UNR) {
+    float4 xb[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) xb[u] = row4[min(q0 + u, n4 - 1)];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      if (q0 + u < c1) {
+        const float xs[4] = {xb[u].x, xb[u].y, xb[u].z, xb[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t bb;
+          if (weight(xs[e], bb) != 0 && bb == ph) ++mine;
+        }
+      }
+  }
+  uint32_t incl = mine;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) red32[tid >> 6] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int i = 0; i < (tid >> 6); ++i) base += red32[i];
+  const uint32_t excl = base + incl - mine;
+  if (mine && j >= excl && j < excl + mine) {
+    int k = (int)(j - excl), pick = -1;
+    for (int q0 = c0; q0 < c1 && pick < 0; q0 += UNR) {
+      float4 xb[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) xb[u] = row4[min(q0 + u, n4 - 1)];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+        if (q0 + u < c1) {
+          const float xs[4] = {xb[u].x, xb[u].y, xb[u].z, xb[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint32_t bb;
+            if (weight(xs[e], bb) != 0 && bb == ph) {
+              if (k == 0 && pick < 0) pick = 4 * (q0 + u) + e;
+              --k;
+            }
+          }
+        }
+    }
+    out[r] = pick < 0 ? 0 : pick;
+  }
+}
+
+hipError_t launch_sample_top_p(const float* logits, int rows, int vocab, const SampleArgs& p, int32_t* out,
+                               hipStream_t st) {
+  launch_kernel(sample_top_p_kernel, dim3(rows), dim3(kSampleThreads), 0, st, logits, vocab, p, out);
+  return hipGetLastError();
+}
+
 }  // namespace cbd

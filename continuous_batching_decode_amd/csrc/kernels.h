@@ -138,6 +138,15 @@ hipError_t launch_prefill_attention(const AttnArgs& a, int n_items, int head_dim
 // greedy argmax per row, lowest id on ties
 // part: kArgmaxSegments x 64 (max, index) pairs; counters: 64 ints, zero between launches
 constexpr int kArgmaxSegments = 64;
+// seeded top-p sampling: per-row parameters passed by value (rows <= 64)
+struct SampleArgs {
+  float temperature[64];  // 0: greedy
+  float top_p[64];        // in (0, 1]
+  uint64_t seed[64];      // Philox4x64-10 key word 0
+  uint64_t index[64];     // counter word 0
+};
+hipError_t launch_sample_top_p(const float* logits, int rows, int vocab, const SampleArgs& p, int32_t* out,
+                               hipStream_t st);
 hipError_t launch_argmax(const float* logits, int rows, int vocab, float* part, int32_t* counters, int32_t* out,
                          hipStream_t st);
 // scatter canonical K/V [L, n, Hkv, Dh] into a slab at [pos, pos+n), or gather back

@@ -943,6 +943,32 @@ extern "C" cbd_status greedy_argmax(cbd_ctx* c, const float* logits_dev, int32_t
   return CBD_OK;
 }
 
+extern "C" cbd_status sample_top_p(cbd_ctx* c, const float* logits_dev, int32_t rows, const float* temperature,
+                                   const float* top_p, const uint64_t* seeds, const uint64_t* sample_index,
+                                   int32_t* tokens_dev, cbd_stream stream) {
+  if (!c) return fail(CBD_E_INVAL, "sample_top_p: null context");
+  if (rows < 0 || rows > 64) return fail(CBD_E_INVAL, "sample_top_p: rows must be in 0..64");
+  if (rows == 0) return CBD_OK;
+  if (!logits_dev || !tokens_dev || !temperature || !top_p || !seeds || !sample_index || !aligned16(logits_dev))
+    return fail(CBD_E_INVAL, "sample_top_p: null or unaligned pointer");
+  if (c->cfg.vocab % 4) return fail(CBD_E_INVAL, "sample_top_p: vocab %d is not a multiple of 4", c->cfg.vocab);
+  SampleArgs a{};
+  for (int r = 0; r < rows; ++r) {
+    if (!(temperature[r] >= 0.f) || !std::isfinite(temperature[r]))
+      return fail(CBD_E_INVAL, "sample_top_p: row %d temperature %g", r, (double)temperature[r]);
+    if (!(top_p[r] > 0.f && top_p[r] <= 1.f)) return fail(CBD_E_INVAL, "sample_top_p: row %d top_p %g", r, (double)top_p[r]);
+    a.temperature[r] = temperature[r];
+    a.top_p[r] = top_p[r];
+    a.seed[r] = seeds[r];
+    a.index[r] = sample_index[r];
+  }
+  if (c->host_only) return fail(CBD_E_NODEVICE, "sample_top_p: host-only context");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  ProfScope p(c, CBD_KERNEL_SAMPLE, (double)rows * c->cfg.vocab * 4.0, 0, st);
+  HIP_TRY(launch_sample_top_p(logits_dev, rows, c->cfg.vocab, a, tokens_dev, st), "sample_top_p");
+  return CBD_OK;
+}
+
 extern "C" cbd_status cbd_linear(cbd_ctx* c, const cbd_matrix* w, int32_t N, int32_t K, const float* x_dev,
                                  int32_t rows, float* y_dev, int32_t splits, cbd_stream stream) {
   if (!c || !w || !x_dev || !y_dev) return fail(CBD_E_INVAL, "cbd_linear: null argument");

@@ -250,6 +250,34 @@ cbd_status greedy_argmax(cbd_ctx* ctx, const float* logits_dev, int32_t rows, in
                          cbd_stream stream);
 
 /*
+ * Seeded per-row sampling over rows of logits (page "Batching", later
+ * revision, section 4.4 "The decode step": a row's random draw is selected by
+ * its request's seed and local sample index, independently of the other rows;
+ * temperature 0 is greedy selection with the greedy tie rule).
+ *  logits_dev    device fp32 [rows, vocab] (the context's vocab, a multiple of
+ *                4; 16-byte aligned). NaN logits weigh nothing.
+ *  temperature   host fp32 [rows]: 0 = greedy (lowest id among maxima); > 0
+ *                divides the logits before the softmax
+ *  top_p         host fp32 [rows] in (0, 1]: the nucleus is the shortest prefix
+ *                of the tokens ordered by probability (highest first, equal
+ *                probabilities by lower id) whose mass reaches top_p
+ *  seeds, sample_index  host uint64 [rows]: the draw u in [0, 1) is the 24
+ *                high bits of word 0 of Philox4x64-10 (Salmon et al., SC 2011)
+ *                with key (seed, 0) and counter (sample_index, 0, 0, 0), over 2^24
+ *  tokens_dev    device int32 [rows], written: the first token of the nucleus
+ *                order whose running mass exceeds u times the nucleus mass
+ * Probabilities are taken in fixed point, e^(z - max z) in units of 2^-40 with
+ * z = logit / temperature; every selection after that is integer arithmetic,
+ * so the result does not depend on summation order. One workgroup per row.
+ * rows = 0 is a no-op. CBD_E_INVAL: rows outside 0..64, null or unaligned
+ * pointers, a temperature negative or not finite, top_p outside (0, 1], a
+ * vocab that is not a multiple of 4.
+ */
+cbd_status sample_top_p(cbd_ctx* ctx, const float* logits_dev, int32_t rows, const float* temperature,
+                        const float* top_p, const uint64_t* seeds, const uint64_t* sample_index,
+                        int32_t* tokens_dev, cbd_stream stream);
+
+/*
  * The batched weight-streaming product alone (the page's batched matvec
  * that shares one weight read across all lanes):
  * y_dev[b, n] = sum_k W[n, k] * x_dev[b, k] for b < rows.
@@ -321,7 +349,8 @@ typedef enum {
   CBD_KERNEL_DOWN = 8,
   CBD_KERNEL_LM_HEAD = 9,
   CBD_KERNEL_ARGMAX = 10,
-  CBD_KERNEL_KINDS = 11
+  CBD_KERNEL_SAMPLE = 11,
+  CBD_KERNEL_KINDS = 12
 } cbd_kernel_kind;
 
 typedef struct {

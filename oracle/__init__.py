@@ -14,12 +14,14 @@ lm_head logits; then its position advances by one. The segmented prefill of
 the same page (section "REVISED ... forward_batch_segmented") is each
 segment's causal forward with segment-local positions from 0, with no
 attention across segments. Arithmetic is float64 throughout; storage
-precision follows the model (bf16 weights, bf16 K/V slabs).
+precision follows the model (bf16 weights, bf16 K/V slabs). ``sampling`` holds
+the seeded temperature / top-p selection of a row's token.
 """
 from .model import (OracleModel, SeqState, bf16_bits_to_f64, round_to_bf16, f64_to_bf16_bits,
                     rmsnorm, rope_angles, apply_rope, attend_one_head, silu, dequant_int4,
                     greedy)
+from .sampling import philox4x64_10, uniform_draw, nucleus_order, sample_row, sample_rows
 
 __all__ = ["OracleModel", "SeqState", "bf16_bits_to_f64", "round_to_bf16", "f64_to_bf16_bits",
            "rmsnorm", "rope_angles", "apply_rope", "attend_one_head", "silu", "dequant_int4",
-           "greedy"]
+           "greedy", "philox4x64_10", "uniform_draw", "nucleus_order", "sample_row", "sample_rows"]

@@ -491,3 +491,114 @@ def test_int4_model_decode(torch, cbd):
         check_greedy(nxt.cpu().numpy(), ref, errs, "int4 step %d" % step)
         tok = greedy(ref)
     eng.close()
+
+
+# ----------------------------------------------------------------------------- seeded top-p sampling
+
+SAMPLE_SHAPE = synth.ModelShape("sample-v128256", 1, 256, 4, 1, 64, 512, 128256, 10000.0)
+
+
+def _sample_ok(logits, temp, top_p, seed, index, got, tol=2e-6):
+    """The GPU token against the oracle's selection on the same logits: equal, unless the draw or the
+    nucleus edge lies within `tol` (probability mass; the kernel's exp and fixed point put its masses
+    within about 1e-6 of the oracle's) of a boundary, where a neighbour in the oracle's order is
+    accepted too. Returns whether the token differs from the oracle's (an accepted neighbour)."""
+    from oracle import nucleus_order, sample_row, uniform_draw
+    want = sample_row(logits, temp, top_p, seed, index)
+    if temp == 0:
+        assert got == want, "greedy row: got %d, want %d" % (got, want)
+        return False
+    order, p, cum, n = nucleus_order(logits, temp, top_p)
+    ambiguous = set()
+    if abs(cum[n - 1] - top_p) < tol or (n >= 2 and abs(cum[n - 2] - top_p) < tol):
+        for nn in (n - 1, n, n + 1):  # the nucleus one token shorter or longer
+            if 1 <= nn <= len(order):
+                t = uniform_draw(seed, index) * cum[nn - 1]
+                j = min(int(np.searchsorted(cum[:nn], t, side="right")), nn - 1)
+                ambiguous.update(int(order[k]) for k in range(max(0, j - 1), min(nn, j + 2)))
+    t = uniform_draw(seed, index) * cum[n - 1]
+    j = min(int(np.searchsorted(cum[:n], t, side="right")), n - 1)
+    if (j > 0 and abs(t - cum[j - 1]) < tol) or abs(cum[j] - t) < tol:
+        ambiguous.update(int(order[k]) for k in range(max(0, j - 1), min(n, j + 2)))
+    if got == want:
+        return False
+    assert got in ambiguous, "got %d, want %d (order position %d of nucleus %d)" % (
+        got, want, int(np.where(order == got)[0][0]) if got in order else -1, n)
+    return True
+
+
+def test_sample_top_p_matches_oracle(torch, cbd):
+    """sample_top_p over 128256-token rows: temperatures 0 (greedy), 0.5, 1, 2; top_p 1e-6 .. 1;
+    random, peaked, heavily tied (logits on a 0.5 grid) and all-equal rows; every token against the
+    oracle's selection on the same logits."""
+    _say("sample_top_p vs oracle")
+    eng = cbd.Engine(synth.make_weights(SAMPLE_SHAPE, seed=1), arena_bytes=1 << 20, max_batch=64,
+                     max_prefill_tokens=64, max_position=256)
+    V = SAMPLE_SHAPE.vocab
+    rng = np.random.Generator(np.random.PCG64(77))
+    rows = []
+    for kind in range(16):
+        if kind < 6:
+            x = rng.normal(0.0, 2.0, V)
+        elif kind < 9:
+            x = rng.normal(0.0, 1.0, V)
+            x[rng.integers(0, V, 5)] += 12.0  # a few dominant tokens
+        elif kind < 13:
+            x = np.round(rng.normal(0.0, 2.0, V) * 2.0) / 2.0  # many exact ties
+        elif kind < 15:
+            x = np.zeros(V)  # all tokens tied
+        else:
+            x = rng.normal(0.0, 4.0, V)
+        rows.append(x.astype(np.float32))
+    temps = [0.0, 0.5, 1.0, 2.0]
+    tops = [1.0, 0.95, 0.5, 1e-6, 0.999]
+    cases = []
+    for i, x in enumerate(rows):
+        for k in range(4):
+            cases.append((x, temps[(i + k) % 4], tops[(i + 2 * k) % 5], 1000 + 7 * i + k, 3 * i + k))
+    amb = 0
+    for c0 in range(0, len(cases), 64):
+        chunk = cases[c0:c0 + 64]
+        L = torch.from_numpy(np.stack([c[0] for c in chunk])).cuda()
+        out = torch.full((len(chunk),), -1, dtype=torch.int32, device="cuda")
+        eng.sample_top_p(L, [c[1] for c in chunk], [c[2] for c in chunk], [c[3] for c in chunk],
+                         [c[4] for c in chunk], out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for c, g in zip(chunk, got):
+            amb += _sample_ok(c[0].astype(np.float64), c[1], c[2], c[3], c[4], int(g))
+    _say("sample_top_p: %d cases, %d neighbours of the oracle's token at a rounding-close boundary" % (
+        len(cases), amb))
+    assert amb <= len(cases) // 10
+    eng.close()
+
+
+def test_sample_top_p_frequencies_and_draws(torch, cbd):
+    """Small vocabulary (1024, a few tokens carry the mass): 4096 draws of one row with sample indices
+    0..4095, each token against the oracle, and the frequencies against the probabilities."""
+    _say("sample_top_p frequencies")
+    shape = synth.TINY
+    eng = cbd.Engine(synth.make_weights(shape, seed=2), arena_bytes=1 << 20, max_batch=64, max_prefill_tokens=64,
+                     max_position=256)
+    x = np.full(shape.vocab, -30.0, dtype=np.float32)
+    x[[3, 17, 500, 1023]] = [1.0, 0.0, -0.5, 0.7]
+    L = torch.from_numpy(np.tile(x, (64, 1))).cuda()
+    got = []
+    for c0 in range(0, 4096, 64):
+        out = torch.empty(64, dtype=torch.int32, device="cuda")
+        eng.sample_top_p(L, [1.0] * 64, [1.0] * 64, [42] * 64, list(range(c0, c0 + 64)), out)
+        torch.cuda.synchronize()
+        got.extend(int(v) for v in out.cpu().numpy())
+    amb = sum(_sample_ok(x.astype(np.float64), 1.0, 1.0, 42, i, g) for i, g in enumerate(got))
+    assert amb <= 8
+    from oracle import nucleus_order
+    _, p, _, _ = nucleus_order(x.astype(np.float64), 1.0, 1.0)
+    freq = np.bincount(np.array(got), minlength=shape.vocab) / 4096.0
+    for tok in (3, 17, 500, 1023):
+        assert abs(freq[tok] - p[tok]) < 4.0 * np.sqrt(p[tok] * (1 - p[tok]) / 4096.0) + 1e-3
+    # rows = 0 is a no-op; bad parameters are rejected
+    eng.sample_top_p(L[:0], [], [], [], [], torch.empty(0, dtype=torch.int32, device="cuda"))
+    for t, tp in ((-1.0, 0.9), (1.0, 0.0), (1.0, 1.5), (float("nan"), 0.9)):
+        with pytest.raises(cbd.CbdError):
+            eng.sample_top_p(L[:1], [t], [tp], [1], [0], torch.empty(1, dtype=torch.int32, device="cuda"))
+    eng.close()

@@ -316,3 +316,69 @@ def test_decode_uses_own_position_and_history():
     assert np.allclose(solo.decode_step_batch([t], [5])[0], lg[1], rtol=1e-12, atol=1e-12)
     with pytest.raises(ValueError):
         o.decode_step_batch([s0, s0], [1, 2])
+
+
+# --------------------------------------------------------------------------- seeded sampling
+
+def test_philox4x64_matches_numpy_bit_generator():
+    """The oracle's Philox4x64-10 block against NumPy's Philox bit generator (which increments its
+    counter before producing a block, so its block n is the function at counter n + 1)."""
+    from oracle import philox4x64_10
+    for key, ctr in (([0, 0], [1, 0, 0, 0]), ([0x0123456789ABCDEF, 0x1111], [7, 0, 0, 0]),
+                     ([2 ** 64 - 1, 5], [2 ** 40 + 3, 9, 1, 2]), ([42, 0], [123456789, 0, 0, 0])):
+        prev = list(ctr)
+        prev[0] -= 1
+        bg = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=np.array(prev, dtype=np.uint64))
+        assert [int(x) for x in bg.random_raw(4)] == philox4x64_10(ctr, key)
+
+
+def test_uniform_draw_range_bits_and_moments():
+    from oracle import uniform_draw
+    u = np.array([uniform_draw(9, i) for i in range(20000)])
+    assert u.min() >= 0.0 and u.max() < 1.0
+    assert np.array_equal(u * 2 ** 24, np.floor(u * 2 ** 24))  # 24 bits, exact in float32
+    assert abs(u.mean() - 0.5) < 0.01 and abs(u.var() - 1.0 / 12.0) < 0.005
+    # distinct seeds and indices give distinct streams
+    assert uniform_draw(1, 0) != uniform_draw(2, 0) and uniform_draw(1, 0) != uniform_draw(1, 1)
+
+
+def test_nucleus_closed_forms():
+    """Probabilities 1/2, 1/4, 1/8, 1/8 (ids 0, 1, 2, 3; the tie ordered by id): nucleus sizes for
+    several p away from the cumulative steps, and temperature 2 giving p proportional to sqrt(p)."""
+    from oracle import nucleus_order
+    x = np.log(np.array([0.5, 0.25, 0.125, 0.125]))
+    for top_p, n_want in ((1e-9, 1), (0.45, 1), (0.6, 2), (0.8, 3), (0.9, 4), (1.0, 4)):
+        order, p, cum, n = nucleus_order(x, 1.0, top_p)
+        assert list(order) == [0, 1, 2, 3] and n == n_want
+        assert np.allclose(p, [0.5, 0.25, 0.125, 0.125], rtol=1e-12)
+    _, p2, _, _ = nucleus_order(x, 2.0, 1.0)
+    q = np.sqrt([0.5, 0.25, 0.125, 0.125])
+    assert np.allclose(p2, q / q.sum(), rtol=1e-12)
+    # ties ordered by id whatever their position in the row
+    order, _, _, _ = nucleus_order(np.log(np.array([0.125, 0.25, 0.125, 0.5])), 1.0, 1.0)
+    assert list(order) == [3, 1, 0, 2]
+
+
+def test_sample_row_inverse_cdf_thresholds():
+    """With probabilities 1/2, 1/4, 1/8, 1/8 and the whole vocabulary: token 0 for u < 1/2, 1 for
+    u < 3/4, 2 for u < 7/8, else 3; with top_p = 0.6 (nucleus {0, 1}, mass 3/4): token 0 for
+    u < 2/3, else 1; greedy at temperature 0 and a vanishing top_p give the lowest-id maximum."""
+    from oracle import sample_row, uniform_draw
+    x = np.log(np.array([0.5, 0.25, 0.125, 0.125]))
+    for i in range(400):
+        u = uniform_draw(5, i)
+        assert sample_row(x, 1.0, 1.0, 5, i) == (0 if u < 0.5 else 1 if u < 0.75 else 2 if u < 0.875 else 3)
+        assert sample_row(x, 1.0, 0.6, 5, i) == (0 if u < 2.0 / 3.0 else 1)
+    y = np.array([1.0, 3.0, -2.0, 3.0])
+    assert sample_row(y, 0.0, 1.0, 1, 1) == 1
+    assert all(sample_row(y, 1.0, 1e-9, s, 0) == 1 for s in range(20))
+
+
+def test_sampling_frequencies_follow_the_softmax():
+    from oracle import nucleus_order, sample_row
+    x = np.array([0.3, -1.0, 2.0, 0.0, 1.2])
+    n = 20000
+    got = np.bincount([sample_row(x, 0.7, 1.0, 11, i) for i in range(n)], minlength=5) / n
+    _, p, _, _ = nucleus_order(x, 0.7, 1.0)
+    assert np.allclose(p, np.exp(x / 0.7) / np.exp(x / 0.7).sum(), rtol=1e-12)
+    assert np.all(np.abs(got - p) < 4 * np.sqrt(p * (1 - p) / n) + 1e-3)
