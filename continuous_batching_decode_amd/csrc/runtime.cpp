@@ -981,6 +981,13 @@ extern "C" cbd_status cbd_linear(cbd_ctx* c, const cbd_matrix* w, int32_t N, int
     return fail(CBD_E_INVAL, "cbd_linear: splits must divide K into multiples of 128 inputs");
   if (splits < 0 && splits != -4 && splits != -8 && splits != -16)
     return fail(CBD_E_INVAL, "cbd_linear: a k split takes 4, 8 or 16 waves");
+  if (splits < 0) {  // the k-split kernel's limits: row groups per wave, and two stages per wave
+    const bool int4 = c->fmt == FMT_INT4;
+    const int step = int4 ? 128 : 32;
+    if ((int4 && rows > 16) || (splits == -16 && rows > 8) || (int4 && splits < -4 && rows > 8) ||
+        K / (-splits) < 2 * step || K % (-splits * step))
+      return fail(CBD_E_INVAL, "cbd_linear: a %d-wave k split does not fit rows=%d, K=%d", -splits, rows, K);
+  }
   if (!w->data || !aligned16(w->data) || (c->fmt == FMT_INT4 && (!w->aux || !aligned16(w->aux))) ||
       !aligned16(y_dev) || !aligned16(x_dev))
     return fail(CBD_E_INVAL, "cbd_linear: pointers must be 16-byte aligned");

@@ -288,9 +288,11 @@ cbd_status sample_top_p(cbd_ctx* ctx, const float* logits_dev, int32_t rows, con
  * format. splits selects how the launch is cut (0 = the library's choice):
  * splits > 0: 4-wave workgroups share staged activations and K is divided
  * over `splits` workgroups (it must divide K into multiples of 128);
- * splits = -4, -8 or -16: each workgroup owns 16 weight rows and divides K
- * over that many waves (rows <= 32; -16 needs rows <= 16). Exposed for
- * kernel-level parity tests and bandwidth measurements.
+ * splits = -4, -8 or -16: each workgroup owns 16 weight rows (bf16; 32 for
+ * int4) and divides K over that many waves, each wave taking at least two
+ * stages of 32 (int4: 128) inputs; bf16 rows <= 64 (<= 8 with -16), int4
+ * rows <= 16 (<= 8 with more than 4 waves); CBD_E_INVAL otherwise. Exposed
+ * for kernel-level parity tests and bandwidth measurements.
  */
 cbd_status cbd_linear(cbd_ctx* ctx, const cbd_matrix* w, int32_t N, int32_t K, const float* x_dev, int32_t rows,
                       float* y_dev, int32_t splits, cbd_stream stream);

@@ -96,6 +96,28 @@ def test_linear_bf16_wide_n(torch, cbd, linear_engines, rows):
     assert err <= LINEAR_RTOL * np.max(np.abs(ref)), err
 
 
+@pytest.mark.parametrize("waves,rows", [(4, 1), (8, 8), (16, 8), (4, 33), (8, 64)])
+def test_linear_bf16_forced_k_split(torch, cbd, linear_engines, waves, rows):
+    """The k-split kernel with 4, 8 or 16 waves per tile forced through cbd_linear."""
+    N, K = 4096, 4096
+    _say("linear bf16 forced k split waves=%d rows=%d" % (waves, rows))
+    eng = linear_engines["bf16"]
+    W = synth.normal_bf16(27, N + K, (N, K), 0.02)
+    X = synth.normal_f32(28, rows, (rows, K), 1.0)
+    wd, xd = cbd.pack_bf16_device(to_dev_bits(torch, W)), torch.from_numpy(X).cuda()
+    y = torch.empty((rows, N), dtype=torch.float32, device="cuda")
+    eng.linear(cbd.Matrix(wd.data_ptr(), None), N, K, xd, y, splits=-waves)
+    torch.cuda.synchronize()
+    ref = X.astype(np.float64) @ synth.bf16_bits_to_f32(W).astype(np.float64).T
+    err = np.max(np.abs(y.cpu().numpy() - ref))
+    assert err <= LINEAR_RTOL * np.max(np.abs(ref)), err
+    # 16 waves take one row group only: 9 rows are rejected before any launch
+    with pytest.raises(cbd.CbdError) as e:
+        eng.linear(cbd.Matrix(wd.data_ptr(), None), N, K, torch.from_numpy(np.tile(X[:1], (9, 1))).cuda(),
+                   torch.empty((9, N), dtype=torch.float32, device="cuda"), splits=-16)
+    assert e.value.status == cbd.CBD_E_INVAL
+
+
 @pytest.mark.parametrize("splits", [1, 2, 7, 16])
 @pytest.mark.parametrize("N,K,rows", [(4096, 14336, 8), (4096, 14336, 1), (1024, 14336, 33)])
 def test_linear_bf16_splits(torch, cbd, linear_engines, N, K, rows, splits):
