@@ -78,17 +78,22 @@ def source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def committed_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter summary,
-    or None when absent or taken on a different kernel source."""
+def committed_profile(field):
+    """A figure of the dominant kernel from the committed profile summary (HBM bytes per launch from
+    the counters, or its average duration in the kernel trace), or None when absent or taken on a
+    different kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    t = re.search(field + r":\s*([0-9.eE+]+)", text)
     if not h or not t or h.group(1) != source_hash():
         return None
     return float(t.group(1))
+
+
+def committed_traffic():
+    return committed_profile("traffic_bytes_per_launch")
 
 
 def main():
@@ -248,6 +253,13 @@ def main():
                 "traffic": committed_traffic() if args.workload == "llama8b-b8" else None,
                 "kernel": kernel_desc, "bytes_per_launch": per_launch_bytes, "avg_launch_us": round(avg_ms * 1e3, 2),
                 "launches": gu["launches"], "kernel_source_sha256_16": source_hash()}
+    if args.workload == "llama8b-b8":
+        # the same kernel's average in the committed rocprofv3 trace of this command: the live events
+        # run a few microseconds longer on the launches they bracket (their completion signalling)
+        tr = committed_profile("kernel_trace_avg_us")
+        if tr:
+            roofline["trace_avg_launch_us"] = tr
+            roofline["frac_at_trace_avg"] = round(per_launch_bytes / (tr * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
     log("B=%d: %.1f tok/s, %.3f ms/step, step %.0f GB/s; %s %.1f us -> %.0f GB/s" % (
         B, tokps, ms_step, step_gbps, rk, avg_ms * 1e3, achieved))
 
