@@ -282,28 +282,33 @@ hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int po
 
 
 // ============================================================================ seeded top-p sampling
-// Row r (one workgroup of 1024 threads): temperature T_r, nucleus mass p_r, draw from Philox4x64-10
-// with key (seed_r, 0) and counter (index_r, 0, 0, 0). T_r = 0 is greedy (lowest id among maxima).
-// Otherwise e_i = exp(z_i - max z) with z = logit / T, in fixed point w_i = floor(e_i 2^40) (integer
-// masses: every comparison below is exact and order-free). The nucleus is the shortest prefix of the
-// ids ordered by e descending (ties: lower id first) whose mass reaches floor(p_r W), W = sum w; the
-// token is the first of that order whose running mass exceeds floor(u M), M = nucleus mass, u the
-// 24-bit draw. Both searches descend the bit patterns of e (order-preserving for positive floats) in
-// three radix levels of 11, 11 and 10 bits with mass and count histograms in LDS; the ties at the
-// final pattern are resolved in id order with a scan of per-thread counts over contiguous chunks.
+// Row r: temperature T_r, nucleus mass p_r, draw from Philox4x64-10 with key (seed_r, 0) and counter
+// (index_r, 0, 0, 0). T_r = 0 is greedy (lowest id among maxima). Otherwise e_i = exp(z_i - max z)
+// with z = logit / T, in fixed point w_i = floor(e_i 2^40) (integer masses: every comparison below
+// is exact and order-free). The nucleus is the shortest prefix of the ids ordered by e descending
+// (ties: lower id first) whose mass reaches floor(p_r W), W = sum w; the token is the first of that
+// order whose running mass exceeds floor(u M), M = nucleus mass, u the 24-bit draw. Both searches
+// descend the bit patterns of e (order-preserving for positive floats) byte by byte. A row is cut
+// into kSampleChunks chunks of consecutive ids, one workgroup each, over nine launches: chunk maxima;
+// then the weights (kept as bit patterns in the workspace) with the chunk's mass and its histogram of
+// top bytes; then each level: every workgroup adds the chunks' histograms of the level decided last
+// (the same integer sums in every workgroup), picks the byte where the running mass from the top
+// crosses the target, and histograms its own chunk's next byte inside that prefix. The last launch
+// resolves the ties at the final pattern in id order over the chunks' counts.
+#ifndef CBD_SAMPLE_UNR
+#define CBD_SAMPLE_UNR 8
+#endif
 namespace {
-constexpr int kSampleThreads = 1024;
-constexpr uint64_t kFix = 1ull << 40;
-
-CBD_DEVICE uint64_t mulhi64(uint64_t a, uint64_t b) { return __umul64hi(a, b); }
+constexpr int kSampleThreads = 256;
+constexpr int kSampleWaves = kSampleThreads / 64;
 
 // Philox4x64-10 word 0 for counter (ctr, 0, 0, 0) and key (k0, 0)
 CBD_DEVICE uint64_t philox_word0(uint64_t ctr, uint64_t k0) {
   uint64_t c0 = ctr, c1 = 0, c2 = 0, c3 = 0, k1 = 0;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t h0 = mulhi64(c0, 0xD2E7470EE14C6C93ull), l0 = c0 * 0xD2E7470EE14C6C93ull;
-    const uint64_t h1 = mulhi64(c2, 0xCA5A826395121157ull), l1 = c2 * 0xCA5A826395121157ull;
+    const uint64_t h0 = __umul64hi(c0, 0xD2E7470EE14C6C93ull), l0 = c0 * 0xD2E7470EE14C6C93ull;
+    const uint64_t h1 = __umul64hi(c2, 0xCA5A826395121157ull), l1 = c2 * 0xCA5A826395121157ull;
     const uint64_t n0 = h1 ^ c1 ^ k0, n2 = h0 ^ c3 ^ k1;
     c0 = n0;
     c1 = l1;
@@ -315,231 +320,348 @@ CBD_DEVICE uint64_t philox_word0(uint64_t ctr, uint64_t k0) {
   return c0;
 }
 
+// fixed-point weight floor(e 2^40) of a bit pattern of e in [0, 1]: the mantissa shifted by the
+// exponent (exact; 0 below 2^-40 and for the zero pattern)
+CBD_DEVICE uint64_t fixed_of(uint32_t bits) {
+  const int ex = (int)(bits >> 23);
+  const uint64_t man = (uint64_t)((bits & 0x7FFFFFu) | 0x800000u);
+  const int sh = ex - 110;  // e 2^40 = man 2^(ex - 127 - 23 + 40)
+  return (ex == 0 || ex > 127) ? 0ull : sh >= 0 ? man << sh : (sh > -24 ? man >> (-sh) : 0ull);
+}
+
 template <typename T>
-CBD_DEVICE T block_sum(T v, T* red) {  // fixed order: lanes by xor tree, then the 16 waves in order
+CBD_DEVICE T wg_sum(T v, T* red) {  // fixed order: lanes by xor tree, then the waves in order
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  const int w = threadIdx.x >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   T s = 0;
-  for (int i = 0; i < kSampleThreads / 64; ++i) s += red[i];
+  for (int i = 0; i < kSampleWaves; ++i) s += red[i];
   return s;
 }
 
-CBD_DEVICE float block_max(float v, float* red) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float m = red[0];
-  for (int i = 1; i < kSampleThreads / 64; ++i) m = fmaxf(m, red[i]);
-  return m;
-}
+// per-row state carried between the launches (written by the row's first workgroup)
+struct SampleState {
+  uint64_t W, target, above_th, keep, wth, t, excess;
+  uint32_t pre;   // bytes of the nucleus pattern decided so far
+  uint32_t th, nt;
+  uint32_t pre2;  // bytes of the sampled pattern decided so far
+  uint64_t above, above2;
+};
 }  // namespace
 
-__global__ __launch_bounds__(kSampleThreads) void sample_top_p_kernel(const float* logits, int vocab, SampleArgs p,
-                                                                      int32_t* out) {
-  __shared__ uint64_t hmass[2048];
-  __shared__ uint32_t hcount[1024];
-  __shared__ uint64_t red64[kSampleThreads / 64];
-  __shared__ float redf[kSampleThreads / 64];
-  __shared__ uint32_t red32[kSampleThreads / 64];
+SampleWs sample_ws_layout(uint8_t* base, int vocab) {
+  SampleWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    uint8_t* q = base ? base + o : nullptr;
+    o += (bytes + 255) / 256 * 256;
+    return q;
+  };
+  w.bits = reinterpret_cast<uint32_t*>(take((size_t)64 * vocab * 4));
+  w.pmax = reinterpret_cast<float*>(take((size_t)64 * kSampleChunks * 4));
+  w.pidx = reinterpret_cast<int32_t*>(take((size_t)64 * kSampleChunks * 4));
+  w.pw = reinterpret_cast<uint64_t*>(take((size_t)64 * kSampleChunks * 8));
+  w.hist = reinterpret_cast<uint64_t*>(take((size_t)7 * 64 * kSampleChunks * 256 * 8));
+  w.cnt = reinterpret_cast<uint32_t*>(take((size_t)2 * 64 * kSampleChunks * 256 * 4));
+  w.state = take((size_t)64 * sizeof(SampleState));
+  w.bytes = o;
+  return w;
+}
+
+__global__ __launch_bounds__(kSampleThreads) void sample_phase_kernel(const float* logits, int vocab, SampleArgs p,
+                                                                      SampleWs ws, int phase, int32_t* out) {
+  __shared__ uint64_t hm[256];
+  __shared__ uint32_t hc[256];
+  __shared__ uint64_t red64[kSampleWaves];
+  __shared__ float redf[kSampleWaves];
+  __shared__ uint32_t red32[kSampleWaves];
   __shared__ uint32_t s_bin;
   __shared__ uint64_t s_above;
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const float* row = logits + (int64_t)r * vocab;
-  const float4* row4 = reinterpret_cast<const float4*>(row);
-  const float temp = p.temperature[r];
+  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  constexpr int C = kSampleChunks;   // chunks of a row (gridDim.x)
+  constexpr int CS = kSampleChunks;  // slots per row in the workspace
+  const float4* row4 = reinterpret_cast<const float4*>(logits + (int64_t)r * vocab);
   const int n4 = vocab >> 2;  // vocab % 4 == 0 (checked by the host)
-  // Every pass visits the thread's float4s q = tid + 1024 i in increasing order, 8 loads in flight
-  // (clamped indices, so the loads are unconditional).
-  constexpr int UNR = 8;
-  auto pass = [&](auto&& visit) {
-    for (int q0 = tid; q0 < n4; q0 += UNR * kSampleThreads) {
-      float4 xb[UNR];
+  const int cs4 = (n4 + C - 1) / C;
+  const int q0 = c * cs4, q1 = min(n4, q0 + cs4);  // this chunk's float4s
+  uint32_t* bits = ws.bits + (int64_t)r * vocab;
+  SampleState* stp = reinterpret_cast<SampleState*>(ws.state) + r;
+  const float temp = p.temperature[r];
+  const bool greedy = temp == 0.f;
+  auto H = [&](int lv) { return ws.hist + ((int64_t)lv * 64 + r) * CS * 256; };  // [chunk][256]
+  auto N = [&](int k) { return ws.cnt + ((int64_t)k * 64 + r) * CS * 256; };
+  // the chunk's float4s q0 + tid + 256 i in increasing order, 8 loads in flight (clamped indices)
+  constexpr int UNR = CBD_SAMPLE_UNR;
+  auto each4 = [&](const uint4* src, auto&& visit) {
+    for (int qa = q0 + tid; qa < q1; qa += UNR * kSampleThreads) {
+      uint4 v[UNR];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) xb[u] = row4[min(q0 + u * kSampleThreads, n4 - 1)];
+      for (int u = 0; u < UNR; ++u) v[u] = src[min(qa + u * kSampleThreads, q1 - 1)];
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
-        if (q0 + u * kSampleThreads < n4) {
-          const int v = 4 * (q0 + u * kSampleThreads);
-          visit(xb[u].x, v);
-          visit(xb[u].y, v + 1);
-          visit(xb[u].z, v + 2);
-          visit(xb[u].w, v + 3);
-        }
+        if (qa + u * kSampleThreads < q1) visit(qa + u * kSampleThreads, v[u]);
     }
   };
 
-  if (temp == 0.f) {  // greedy: strict > in id order per thread, then (max, lowest id) over the block
+  // Add the chunks' histograms of one byte level (region `pre` of the `lv` bytes above), take off
+  // the nucleus ties beyond `keep` where the boundary pattern lies in the region, and find the byte
+  // where the running mass from the top, starting at `above`, crosses `target` (>= when ge, else >).
+  auto decide = [&](const uint64_t* h, int lv, uint32_t pre, uint64_t above, uint64_t target, bool ge,
+                    uint32_t cap_bits, uint64_t cap_excess, uint32_t& bin, uint64_t& above_out) {
+    const int b = 255 - tid;  // thread t holds byte 255 - t: the scan runs from the top
+    uint64_t m = 0;
+#pragma unroll
+    for (int k = 0; k < CS; ++k) {  // all loads in flight together (clamped: chunks beyond C add 0)
+      const uint64_t v = h[min(k, C - 1) * 256 + b];
+      m += k < C ? v : 0ull;
+    }
+    if (cap_excess && (lv == 0 || (cap_bits >> (32 - 8 * lv)) == pre) && ((cap_bits >> (24 - 8 * lv)) & 255) == (uint32_t)b)
+      m -= cap_excess;
+    uint64_t incl = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    __syncthreads();
+    if (lane == 63) red64[tid >> 6] = incl;
+    if (tid == 0) {
+      s_bin = 0;  // (unreachable fallback: the lowest byte)
+      s_above = above;
+    }
+    __syncthreads();
+    for (int i = 0; i < (tid >> 6); ++i) incl += red64[i];
+    const uint64_t a0 = above + incl - m, a1 = above + incl;
+    const bool before = ge ? a0 >= target : a0 > target, after = ge ? a1 >= target : a1 > target;
+    if (!before && after) {
+      s_bin = (uint32_t)b;
+      s_above = a0;
+    }
+    __syncthreads();
+    bin = s_bin;
+    above_out = s_above;
+    __syncthreads();
+  };
+  // histogram of this chunk's byte at level lv over the patterns in region `pre` (weights > 0)
+  auto build = [&](int lv, uint32_t pre, uint64_t* h_out, uint32_t* n_out) {
+    for (int i = tid; i < 256; i += kSampleThreads) {
+      hm[i] = 0;
+      hc[i] = 0;
+    }
+    __syncthreads();
+    const int sh = 24 - 8 * lv;
+    each4(reinterpret_cast<const uint4*>(bits), [&](int, uint4 bb) {
+      const uint32_t bs[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (bs[e] && (lv == 0 || (bs[e] >> (sh + 8)) == pre)) {
+          const int bin = (bs[e] >> sh) & 255;
+          atomicAdd(reinterpret_cast<unsigned long long*>(&hm[bin]), (unsigned long long)fixed_of(bs[e]));
+          if (n_out) atomicAdd(&hc[bin], 1u);
+        }
+    });
+    __syncthreads();
+    for (int i = tid; i < 256; i += kSampleThreads) {
+      h_out[c * 256 + i] = hm[i];
+      if (n_out) n_out[c * 256 + i] = hc[i];
+    }
+  };
+
+  if (phase == 0) {  // chunk maxima (greedy: the chunk's maximum and its lowest id)
+    if (c == 0 && tid == 0) out[r] = 0;  // stands if no weight is positive
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
-    pass([&](float x, int v) {
-      if (x > best || (x == best && v < bi)) {
-        best = x;
-        bi = v;
+    const float inv_t = greedy ? 1.f : 1.f / temp;
+    each4(reinterpret_cast<const uint4*>(row4), [&](int q, uint4 xb) {
+      const float xs[4] = {__uint_as_float(xb.x), __uint_as_float(xb.y), __uint_as_float(xb.z), __uint_as_float(xb.w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float z = greedy ? xs[e] : xs[e] * inv_t;
+        if (z > best || (z == best && 4 * q + e < bi)) {
+          best = z;
+          bi = 4 * q + e;
+        }
       }
     });
-    const float m = block_max(best, redf);
-    uint32_t cand = (best == m) ? (uint32_t)bi : 0x7FFFFFFFu;
+    const float m = wave_max(best);
+    __syncthreads();
+    if (lane == 0) redf[tid >> 6] = m;
+    __syncthreads();
+    float mm = redf[0];
+    for (int i = 1; i < kSampleWaves; ++i) mm = fmaxf(mm, redf[i]);
+    uint32_t cand = (best == mm) ? (uint32_t)bi : 0x7FFFFFFFu;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) cand = min(cand, (uint32_t)__shfl_xor((int)cand, o, 64));
     __syncthreads();
-    if ((tid & 63) == 0) red32[tid >> 6] = cand;
+    if (lane == 0) red32[tid >> 6] = cand;
     __syncthreads();
     if (tid == 0) {
       uint32_t bb = red32[0];
-      for (int i = 1; i < kSampleThreads / 64; ++i) bb = min(bb, red32[i]);
-      out[r] = bb == 0x7FFFFFFFu ? 0 : (int32_t)bb;  // every logit NaN: token 0
+      for (int i = 1; i < kSampleWaves; ++i) bb = min(bb, red32[i]);
+      ws.pmax[r * CS + c] = mm;
+      ws.pidx[r * CS + c] = (int32_t)bb;
+    }
+    return;
+  }
+  if (greedy) {  // the lowest id among the chunks' maxima, in chunk order
+    if (phase == 1 && c == 0 && tid == 0) {
+      float best = -INFINITY;
+      int bi = 0x7FFFFFFF;
+      for (int k = 0; k < C; ++k) {
+        const float v = ws.pmax[r * CS + k];
+        const int i = ws.pidx[r * CS + k];
+        if (i != 0x7FFFFFFF && (v > best || (v == best && i < bi))) {
+          best = v;
+          bi = i;
+        }
+      }
+      out[r] = bi == 0x7FFFFFFF ? 0 : bi;  // every logit NaN: token 0
     }
     return;
   }
 
-  const float inv_t = 1.0f / temp;
-  // max of z (NaN logits are skipped: they never win and weigh nothing)
-  float mz = -INFINITY;
-  pass([&](float x, int) { mz = fmaxf(mz, x * inv_t); });
-  mz = block_max(mz, redf);
-  // bit pattern of e = exp(z - max z) (0 for NaN) and its fixed-point mass floor(e 2^40): the
-  // mantissa shifted by the exponent (exact; 0 below 2^-40)
-  auto weight = [&](float x, uint32_t& bits) -> uint64_t {
-    const float e = __expf(x * inv_t - mz);
-    bits = (e == e) ? __float_as_uint(e) : 0u;
-    const int ex = (int)(bits >> 23);  // biased exponent; e <= 1 so ex <= 127
-    const uint64_t man = (uint64_t)((bits & 0x7FFFFFu) | 0x800000u);
-    const int sh = ex - 110;  // e 2^40 = man 2^(ex - 127 - 23 + 40)
-    return ex == 0 ? 0ull : sh >= 0 ? man << sh : (sh > -24 ? man >> (-sh) : 0ull);
-  };
-  uint64_t tw = 0;
-  pass([&](float x, int) {
-    uint32_t bb;
-    tw += weight(x, bb);
-  });
-  const uint64_t W = block_sum<uint64_t>(tw, red64);
-
-  // One radix descent over the patterns of positive weights: the largest pattern P such that the
-  // mass of the patterns above P (the ties at `cap_bits` counted as `cap_excess` lighter) plus the
-  // mass at P crosses `target` (>= when ge, else >). Returns P, the mass strictly above it and the
-  // number of tokens at it.
-  auto descend = [&](uint64_t target, bool ge, uint32_t cap_bits, uint64_t cap_excess, uint32_t& pat,
-                     uint64_t& above, uint32_t& cnt) {
-    uint32_t prefix = 0;
-    above = 0;
-    const int widths[3] = {11, 11, 10};
-    int shift = 32;
-    for (int lv = 0; lv < 3; ++lv) {
-      const int wb = widths[lv];
-      shift -= wb;
-      const int nb = 1 << wb;
-      for (int i = tid; i < nb; i += kSampleThreads) {
-        hmass[i] = 0;
-        if (lv == 2) hcount[i] = 0;
-      }
-      __syncthreads();
-      pass([&](float x, int) {
-        uint32_t bb;
-        const uint64_t w = weight(x, bb);
-        if (w != 0 && (shift + wb == 32 || (bb >> (shift + wb)) == prefix)) {
-          const int bin = (bb >> shift) & (nb - 1);
-          atomicAdd(reinterpret_cast<unsigned long long*>(&hmass[bin]), (unsigned long long)w);
-          if (lv == 2) atomicAdd(&hcount[bin], 1u);
-        }
-      });
-      __syncthreads();
-      if (tid == 0 && cap_excess && (shift + wb == 32 || (cap_bits >> (shift + wb)) == prefix))
-        hmass[(cap_bits >> shift) & (nb - 1)] -= cap_excess;
-      __syncthreads();
-      // running mass from the top bin down: thread t holds bins nb-1-2t and nb-2-2t; a scan over the
-      // threads gives each pair the mass above it, and the one pair where the running mass crosses
-      // the target names the bin
-      const int bh = nb - 1 - 2 * tid, bl = bh - 1;
-      const uint64_t mh = bh >= 0 ? hmass[bh] : 0ull, ml = bl >= 0 ? hmass[bl] : 0ull;
-      const uint64_t pr = mh + ml;
-      uint64_t incl = pr;
+  if (phase == 1) {  // weights of the chunk, its mass and its top-byte histogram
+    float mz = -INFINITY;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint64_t y = __shfl_up(incl, o, 64);
-        if ((tid & 63) >= o) incl += y;
+    for (int k = 0; k < CS; ++k) mz = fmaxf(mz, ws.pmax[r * CS + min(k, C - 1)]);
+    const float inv_t = 1.f / temp;
+    uint64_t tw = 0;
+    each4(reinterpret_cast<const uint4*>(row4), [&](int q, uint4 xb) {
+      const float xs[4] = {__uint_as_float(xb.x), __uint_as_float(xb.y), __uint_as_float(xb.z), __uint_as_float(xb.w)};
+      uint32_t bs[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ev = __expf(xs[e] * inv_t - mz);
+        const uint32_t b = (ev == ev) ? __float_as_uint(ev) : 0u;  // NaN: weight 0
+        const uint64_t w = fixed_of(b);
+        bs[e] = w ? b : 0u;
+        tw += w;
       }
-      if ((tid & 63) == 63) red64[tid >> 6] = incl;
-      if (tid == 0) {
-        s_bin = 0;  // (unreachable fallback: the lowest bin)
-        s_above = above;
-      }
-      __syncthreads();
-      uint64_t a0 = above + incl - pr;
-      for (int i = 0; i < (tid >> 6); ++i) a0 += red64[i];
-      auto crossed = [&](uint64_t m) { return ge ? m >= target : m > target; };
-      if (bh >= 0 && !crossed(a0)) {
-        if (crossed(a0 + mh)) {
-          s_bin = (uint32_t)bh;
-          s_above = a0;
-        } else if (bl >= 0 && crossed(a0 + pr)) {
-          s_bin = (uint32_t)bl;
-          s_above = a0 + mh;
-        }
-      }
-      __syncthreads();
-      prefix = (prefix << wb) | s_bin;
-      above = s_above;
-      if (lv == 2) cnt = hcount[s_bin];
-      __syncthreads();
+      reinterpret_cast<uint4*>(bits)[q] = make_uint4(bs[0], bs[1], bs[2], bs[3]);
+    });
+    const uint64_t cw = wg_sum<uint64_t>(tw, red64);
+    if (tid == 0) ws.pw[r * CS + c] = cw;
+    __syncthreads();
+    build(0, 0u, H(0), nullptr);
+    return;
+  }
+
+  SampleState s = *stp;  // the decisions of the earlier launches
+  if (phase == 2) {
+    uint64_t W = 0;
+#pragma unroll
+    for (int k = 0; k < CS; ++k) {
+      const uint64_t v = ws.pw[r * CS + min(k, C - 1)];
+      W += k < C ? v : 0ull;
     }
-    pat = prefix;
-  };
-  auto fixed_of = [&](uint32_t bits) -> uint64_t {  // the weight of a pattern (as in weight())
-    const int ex = (int)(bits >> 23);
-    const uint64_t man = (uint64_t)((bits & 0x7FFFFFu) | 0x800000u);
-    const int sh = ex - 110;
-    return ex == 0 ? 0ull : sh >= 0 ? man << sh : (sh > -24 ? man >> (-sh) : 0ull);
-  };
-
-  // nucleus boundary: pattern theta, the mass above it, its tie count and how many ties it keeps
-  const uint64_t target = (uint64_t)((double)p.top_p[r] * (double)W);
-  uint32_t th, nt;
-  uint64_t above_th;
-  descend(target > 0 ? target : 1, true, 0u, 0ull, th, above_th, nt);
-  const uint64_t wth = fixed_of(th);
-  uint64_t keep = wth ? (target > above_th ? (target - above_th + wth - 1) / wth : 1) : nt;
-  keep = keep < 1 ? 1 : (keep > nt ? nt : keep);
-  const uint64_t M = above_th + keep * wth;
-  // the draw and its point t = floor(u M) in the nucleus mass (exact: u has 24 bits)
-  const uint64_t u24 = philox_word0(p.index[r], p.seed[r]) >> 40;
-  const uint64_t t = u24 * (M >> 24) + ((u24 * (M & 0xFFFFFFull)) >> 24);
-  uint32_t ph, nph;
-  uint64_t above_ph;
-  descend(t, false, th, (uint64_t)(nt - keep) * wth, ph, above_ph, nph);
+    uint64_t target = (uint64_t)((double)p.top_p[r] * (double)W);
+    if (target == 0) target = 1;
+    uint32_t b0;
+    uint64_t a0;
+    decide(H(0), 0, 0u, 0ull, target, true, 0u, 0ull, b0, a0);
+    build(1, b0, H(1), nullptr);
+    if (c == 0 && tid == 0) {
+      s.W = W;
+      s.target = target;
+      s.pre = b0;
+      s.above = a0;
+      *stp = s;
+    }
+    return;
+  }
+  if (phase == 3 || phase == 4) {  // nucleus pattern, bytes 1 and 2
+    const int lv = phase - 2;
+    uint32_t b;
+    uint64_t a;
+    decide(H(lv), lv, s.pre, s.above, s.target, true, 0u, 0ull, b, a);
+    const uint32_t pre = (s.pre << 8) | b;
+    build(lv + 1, pre, H(lv + 1), lv + 1 == 3 ? N(0) : nullptr);
+    if (c == 0 && tid == 0) {
+      s.pre = pre;
+      s.above = a;
+      *stp = s;
+    }
+    return;
+  }
+  if (phase == 5) {  // nucleus pattern byte 3: the boundary, the nucleus mass, the draw; sampled byte 0
+    uint32_t b;
+    uint64_t a;
+    decide(H(3), 3, s.pre, s.above, s.target, true, 0u, 0ull, b, a);
+    const uint32_t th = (s.pre << 8) | b;
+    uint32_t nt = 0;
+#pragma unroll
+    for (int k = 0; k < CS; ++k) {
+      const uint32_t v = N(0)[min(k, C - 1) * 256 + b];
+      nt += k < C ? v : 0u;
+    }
+    const uint64_t wth = fixed_of(th);
+    uint64_t keep = wth ? (s.target > a ? (s.target - a + wth - 1) / wth : 1) : nt;
+    keep = keep < 1 ? 1 : (keep > nt ? nt : keep);
+    const uint64_t M = a + keep * wth;
+    const uint64_t u24 = philox_word0(p.index[r], p.seed[r]) >> 40;
+    const uint64_t t = u24 * (M >> 24) + ((u24 * (M & 0xFFFFFFull)) >> 24);  // floor(u M), exact
+    const uint64_t excess = (uint64_t)(nt - keep) * wth;
+    uint32_t b2;
+    uint64_t a2;
+    decide(H(0), 0, 0u, 0ull, t, false, th, excess, b2, a2);
+    build(1, b2, H(4), nullptr);  // byte 1 of the sampled pattern, kept as histogram 4
+    if (c == 0 && tid == 0) {
+      s.th = th;
+      s.nt = nt;
+      s.above_th = a;
+      s.keep = keep;
+      s.wth = wth;
+      s.t = t;
+      s.excess = excess;
+      s.pre2 = b2;
+      s.above2 = a2;
+      *stp = s;
+    }
+    return;
+  }
+  if (phase == 6 || phase == 7) {  // sampled pattern, bytes 1 and 2
+    const int lv = phase - 5;
+    uint32_t b;
+    uint64_t a;
+    decide(H(3 + lv), lv, s.pre2, s.above2, s.t, false, s.th, s.excess, b, a);
+    const uint32_t pre = (s.pre2 << 8) | b;
+    build(lv + 1, pre, H(4 + lv), lv + 1 == 3 ? N(1) : nullptr);
+    if (c == 0 && tid == 0) {
+      s.pre2 = pre;
+      s.above2 = a;
+      *stp = s;
+    }
+    return;
+  }
+  // phase 8: sampled pattern byte 3, then the j-th id (ascending) among the tokens with it
+  uint32_t b;
+  uint64_t a;
+  decide(H(6), 3, s.pre2, s.above2, s.t, false, s.th, s.excess, b, a);
+  const uint32_t ph = (s.pre2 << 8) | b;
   const uint64_t wph = fixed_of(ph);
-  uint64_t j = wph ? (t - above_ph) / wph : 0;
-  const uint64_t avail = ph == th ? keep : nph;
+  uint32_t nph = 0, before = 0, here = 0;
+#pragma unroll
+  for (int k = 0; k < CS; ++k) {
+    const uint32_t n = k < C ? N(1)[min(k, C - 1) * 256 + b] : 0u;
+    nph += n;
+    if (k < c) before += n;
+    if (k == c) here = n;
+  }
+  uint64_t j = wph ? (s.t - a) / wph : 0;
+  const uint64_t avail = ph == s.th ? s.keep : nph;
   if (j >= avail) j = avail ? avail - 1 : 0;
-  // the j-th id (ascending) among the tokens with pattern ph: per-thread counts over contiguous
-  // chunks of CH float4s, an exclusive scan, then the owner picks (token 0 stands if no weight is
-  // positive)
-  if (tid == 0) out[r] = 0;
-  const int CH = (n4 + kSampleThreads - 1) / kSampleThreads;
-  const int c0 = tid * CH, c1 = min(n4, c0 + CH);
+  if (here == 0 || j < before || j >= (uint64_t)before + here) return;  // (uniform over the workgroup)
+  // this chunk holds it: per-thread counts over contiguous runs of float4s, an exclusive scan, the pick
+  const int per = (q1 - q0 + kSampleThreads - 1) / kSampleThreads;
+  const int t0 = q0 + tid * per, t1 = min(q1, t0 + per);
   uint32_t mine = 0;
-  for (int q0 = c0; q0 < c1; q0 += UNR) {
-    float4 xb[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) xb[u] = row4[min(q0 + u, n4 - 1)];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u)
-      if (q0 + u < c1) {
-        const float xs[4] = {xb[u].x, xb[u].y, xb[u].z, xb[u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t bb;
-          if (weight(xs[e], bb) != 0 && bb == ph) ++mine;
-        }
-      }
+  for (int q = t0; q < t1; ++q) {
+    const uint4 bb = reinterpret_cast<const uint4*>(bits)[q];
+    mine += (bb.x == ph) + (bb.y == ph) + (bb.z == ph) + (bb.w == ph);
   }
   uint32_t incl = mine;
-  const int lane = tid & 63;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
@@ -548,37 +670,34 @@ __global__ __launch_bounds__(kSampleThreads) void sample_top_p_kernel(const floa
   __syncthreads();
   if (lane == 63) red32[tid >> 6] = incl;
   __syncthreads();
-  uint32_t base = 0;
-  for (int i = 0; i < (tid >> 6); ++i) base += red32[i];
-  const uint32_t excl = base + incl - mine;
-  if (mine && j >= excl && j < excl + mine) {
-    int k = (int)(j - excl), pick = -1;
-    for (int q0 = c0; q0 < c1 && pick < 0; q0 += UNR) {
-      float4 xb[UNR];
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) xb[u] = row4[min(q0 + u, n4 - 1)];
-#pragma unroll
-      for (int u = 0; u < UNR; ++u)
-        if (q0 + u < c1) {
-          const float xs[4] = {xb[u].x, xb[u].y, xb[u].z, xb[u].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            uint32_t bb;
-            if (weight(xs[e], bb) != 0 && bb == ph) {
-              if (k == 0 && pick < 0) pick = 4 * (q0 + u) + e;
-              --k;
-            }
+  for (int i = 0; i < (tid >> 6); ++i) incl += red32[i];
+  const uint32_t excl = incl - mine;
+  const uint64_t k = j - before;
+  if (mine && k >= excl && k < (uint64_t)excl + mine) {
+    int left = (int)(k - excl);
+    for (int q = t0; q < t1; ++q) {
+      const uint4 bb = reinterpret_cast<const uint4*>(bits)[q];
+      const uint32_t bs[4] = {bb.x, bb.y, bb.z, bb.w};
+      for (int e = 0; e < 4; ++e)
+        if (bs[e] == ph) {
+          if (left == 0) {
+            out[r] = 4 * q + e;
+            return;
           }
+          --left;
         }
     }
-    out[r] = pick < 0 ? 0 : pick;
   }
 }
 
-hipError_t launch_sample_top_p(const float* logits, int rows, int vocab, const SampleArgs& p, int32_t* out,
-                               hipStream_t st) {
-  launch_kernel(sample_top_p_kernel, dim3(rows), dim3(kSampleThreads), 0, st, logits, vocab, p, out);
-  return hipGetLastError();
+hipError_t launch_sample_top_p(const float* logits, int rows, int vocab, const SampleArgs& p, const SampleWs& ws,
+                               int32_t* out, hipStream_t st) {
+  for (int phase = 0; phase <= 8; ++phase) {
+    launch_kernel(sample_phase_kernel, dim3(kSampleChunks, rows), dim3(kSampleThreads), 0, st, logits, vocab, p, ws,
+                  phase, out);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace cbd

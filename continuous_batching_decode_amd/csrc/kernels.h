@@ -145,8 +145,22 @@ struct SampleArgs {
   uint64_t seed[64];      // Philox4x64-10 key word 0
   uint64_t index[64];     // counter word 0
 };
-hipError_t launch_sample_top_p(const float* logits, int rows, int vocab, const SampleArgs& p, int32_t* out,
-                               hipStream_t st);
+// its workspace: per-row weights (bit patterns), chunk maxima and masses, byte histograms of the
+// chunks for the seven levels of the two searches, tie counts, and the per-row state between launches
+constexpr int kSampleChunks = 32;
+struct SampleWs {
+  uint32_t* bits;  // [64][vocab]
+  float* pmax;     // [64][chunks]
+  int32_t* pidx;   // [64][chunks]
+  uint64_t* pw;    // [64][chunks]
+  uint64_t* hist;  // [7][64][chunks][256]
+  uint32_t* cnt;   // [2][64][chunks][256]
+  uint8_t* state;  // [64] per-row records
+  size_t bytes;
+};
+SampleWs sample_ws_layout(uint8_t* base, int vocab);  // base == nullptr: sizes only
+hipError_t launch_sample_top_p(const float* logits, int rows, int vocab, const SampleArgs& p, const SampleWs& ws,
+                               int32_t* out, hipStream_t st);
 hipError_t launch_argmax(const float* logits, int rows, int vocab, float* part, int32_t* counters, int32_t* out,
                          hipStream_t st);
 // scatter canonical K/V [L, n, Hkv, Dh] into a slab at [pos, pos+n), or gather back

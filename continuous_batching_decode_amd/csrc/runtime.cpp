@@ -119,6 +119,7 @@ struct cbd_ctx {
   int32_t* attn_counters = nullptr;  // split-attention arrival counters [64][n_kv_heads]
   float* argmax_part = nullptr;      // argmax (max, index) pairs [64][kArgmaxSegments]
   int32_t* argmax_counters = nullptr;  // argmax arrival counters [64]
+  SampleWs sample_ws{};                // sampling workspace (weights, chunk histograms, row state)
   size_t gemm_part_bytes = 0;
   int gemm_counter_count = 0;
   float* qkv = nullptr;
@@ -382,6 +383,8 @@ static cbd_status setup_device(cbd_ctx* c) {
   bytes += (size_t)kMaxParts * G * 2 * 4 + 256;     // partial (max, sum)
   bytes += (size_t)m.max_position * half * 2 * 4 + 256;  // rope table
   bytes += ml.total + 256;                          // metadata
+  const size_t sample_bytes = sample_ws_layout(nullptr, m.vocab).bytes;
+  bytes += sample_bytes + 256;                      // sampling workspace
   HIP_TRY(hipMalloc(&c->ws, bytes), "workspace allocation");
   HIP_TRY(hipMemset(c->ws, 0, bytes), "workspace clear");
   uint8_t* p = static_cast<uint8_t*>(c->ws);
@@ -405,6 +408,7 @@ static cbd_status setup_device(cbd_ctx* c) {
   c->part_ml = align_ptr<float>(p, (size_t)kMaxParts * G * 2);
   c->rope_cs = align_ptr<float>(p, (size_t)m.max_position * half * 2);
   c->meta_dev = align_ptr<uint8_t>(p, ml.total);
+  c->sample_ws = sample_ws_layout(align_ptr<uint8_t>(p, sample_bytes), m.vocab);
 
   // RoPE table: angles in double precision, stored as fp32 (cos, sin) pairs
   std::vector<float> cs((size_t)m.max_position * half * 2);
@@ -965,7 +969,7 @@ extern "C" cbd_status sample_top_p(cbd_ctx* c, const float* logits_dev, int32_t 
   if (c->host_only) return fail(CBD_E_NODEVICE, "sample_top_p: host-only context");
   hipStream_t st = static_cast<hipStream_t>(stream);
   ProfScope p(c, CBD_KERNEL_SAMPLE, (double)rows * c->cfg.vocab * 4.0, 0, st);
-  HIP_TRY(launch_sample_top_p(logits_dev, rows, c->cfg.vocab, a, tokens_dev, st), "sample_top_p");
+  HIP_TRY(launch_sample_top_p(logits_dev, rows, c->cfg.vocab, a, c->sample_ws, tokens_dev, st), "sample_top_p");
   return CBD_OK;
 }
 

@@ -268,7 +268,9 @@ cbd_status greedy_argmax(cbd_ctx* ctx, const float* logits_dev, int32_t rows, in
  *                order whose running mass exceeds u times the nucleus mass
  * Probabilities are taken in fixed point, e^(z - max z) in units of 2^-40 with
  * z = logit / temperature; every selection after that is integer arithmetic,
- * so the result does not depend on summation order. One workgroup per row.
+ * so the result does not depend on summation order. Each row is cut into 32
+ * chunks of consecutive ids, one workgroup each, over nine launches; the
+ * context's workspace holds the weights and the chunks' histograms.
  * rows = 0 is a no-op. CBD_E_INVAL: rows outside 0..64, null or unaligned
  * pointers, a temperature negative or not finite, top_p outside (0, 1], a
  * vocab that is not a multiple of 4.
