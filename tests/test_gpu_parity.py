@@ -488,6 +488,82 @@ def test_chunked_prefill_continuation(torch, cbd):
     eng.close()
 
 
+def test_continuous_schedule_join_leave(torch, cbd):
+    """A continuous-batching schedule through the C ABI, every call against the oracle: rows join by
+    prefill (one a single token, one in two chunks while the others decode), leave between steps (a
+    freed slab is handed to the next joiner with the old K/V still in it), and the batch order changes
+    from step to step. Logits and greedy ids at every call, slabs bit for bit at the end."""
+    _say("continuous schedule")
+    from oracle import OracleModel, greedy
+    shape = synth.TINY
+    w = synth.make_weights(shape, seed=8, gain_std=0.1)
+    eng = cbd.Engine(w, arena_bytes=4 * 256 * shape.kv_bytes_per_token(), max_batch=8, max_prefill_tokens=64,
+                     max_position=1024)
+    orc = OracleModel(w, cache_all_layers=True)
+    pr = dict(zip("ABCDE", synth.prompts(31, [20, 7, 33, 1, 50], shape.vocab)))
+    gid, oid, nxt = {}, {}, {}  # name -> GPU slab id, oracle id, next token (teacher-forced)
+    done = {}
+
+    def prefill(items, what):
+        names = [n for n, _ in items]
+        segs = [pr[n][lo:hi] for n, (lo, hi) in items]
+        for n, (lo, hi) in items:
+            if lo == 0:
+                gid[n] = eng.alloc(256)
+                oid[n] = orc.new_sequence()
+        toks = torch.from_numpy(np.concatenate(segs).astype(np.int32)).cuda()
+        lg = torch.empty((len(items), shape.vocab), dtype=torch.float32, device="cuda")
+        nx = torch.empty(len(items), dtype=torch.int32, device="cuda")
+        eng.prefill_segmented([gid[n] for n in names], [len(x) for x in segs], toks, lg, nx)
+        ref = orc.prefill_segmented([oid[n] for n in names], segs)
+        torch.cuda.synchronize()
+        errs = assert_logits_close(lg.cpu().numpy(), ref, what)
+        check_greedy(nx.cpu().numpy(), ref, errs, what)
+        for n, t in zip(names, greedy(ref)):
+            nxt[n] = int(t)
+
+    def step(names, what):
+        toks = np.array([nxt[n] for n in names])
+        lg = torch.empty((len(names), shape.vocab), dtype=torch.float32, device="cuda")
+        nx = torch.empty(len(names), dtype=torch.int32, device="cuda")
+        eng.decode_step_batch([gid[n] for n in names], torch.from_numpy(toks.astype(np.int32)).cuda(), lg, nx)
+        ref = orc.decode_step_batch([oid[n] for n in names], toks)
+        torch.cuda.synchronize()
+        errs = assert_logits_close(lg.cpu().numpy(), ref, what)
+        check_greedy(nx.cpu().numpy(), ref, errs, what)
+        for n, t in zip(names, greedy(ref)):
+            nxt[n] = int(t)
+
+    def leave(n):
+        k, v = eng.read(gid[n], 0, eng.length(gid[n]))
+        torch.cuda.synchronize()
+        compare_slab_bits(k.cpu().numpy(), np.stack(orc.seqs[oid[n]].k), "K %s" % n)
+        compare_slab_bits(v.cpu().numpy(), np.stack(orc.seqs[oid[n]].v), "V %s" % n)
+        done[n] = eng.length(gid[n])
+        eng.free(gid[n])
+        orc.free_sequence(oid[n])
+
+    prefill([("A", (0, 20)), ("B", (0, 7))], "t0 prefill A, B")
+    step(["A", "B"], "t1")
+    step(["B", "A"], "t2")
+    leave("B")  # B's granules hold its K/V when C takes them
+    prefill([("C", (0, 33))], "t3 prefill C")
+    step(["C", "A"], "t3")
+    prefill([("D", (0, 1))], "t4 prefill D (one token)")
+    step(["A", "D", "C"], "t4")
+    step(["D", "C", "A"], "t5")
+    leave("A")
+    prefill([("E", (0, 26))], "t6 prefill E, first chunk")
+    step(["C", "D"], "t6")
+    prefill([("E", (26, 50))], "t7 prefill E, second chunk")
+    step(["E", "C", "D"], "t7")
+    step(["D", "E", "C"], "t8")
+    for n in ("C", "D", "E"):
+        leave(n)
+    assert done == {"A": 25, "B": 9, "C": 39, "D": 6, "E": 52}
+    eng.close()
+
+
 def test_int4_model_decode(torch, cbd):
     """int4-affine weights through prefill and 3 teacher-forced steps."""
     _say("int4 model")
