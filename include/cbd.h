@@ -15,12 +15,17 @@
  *  - prefill_segmented: section "REVISED ... forward_batch_segmented". K
  *    prompts packed into one pass; every projection runs once over all
  *    tokens; attention is block-diagonal causal (a token attends only to
- *    earlier tokens of its own segment); positions are segment-local from 0.
- *    Returns the logits of each segment's last token only.
+ *    earlier tokens of its own sequence); positions continue from the
+ *    sequence's length (0 for a fresh slab), so a prompt can be admitted in
+ *    chunks between decode steps (page "Batching", section 4.2). Returns the
+ *    logits of each segment's last token only.
  *  - kvslab_alloc / kvslab_free: section "1. Native station": an N-slot KV
  *    arena keyed by sequence id; admission = fresh slab at length 0, EOS =
  *    drop the slab; capacity is bounded and the caller queues what does
  *    not fit (section "2. JS scheduler", "Backpressure").
+ *  - greedy_argmax / sample_top_p: the token of each logits row, greedy or
+ *    seeded temperature / top-p (page "Batching", later revision, section
+ *    4.4 and section 8).
  *
  * Model body (the pages do not spell it out; plainest Llama/Mistral reading):
  * RMSNorm (y = x / sqrt(mean(x^2) + eps) * g), GQA attention with rotate-half
@@ -28,8 +33,10 @@
  * (W_down(silu(W_gate x) * W_up x)), final RMSNorm, untied lm_head.
  *
  * Numerics: residual stream, softmax and every accumulation in fp32; weight
- * and activation operands of matrix products in bf16; K/V stored in the
- * slabs as bf16 (round to nearest even); logits fp32.
+ * operands of matrix products in bf16 (or int4-affine dequantized to bf16
+ * in registers), activation operands as a bf16 pair hi = bf16(x),
+ * lo = bf16(x - hi) (about 16 significant bits); K/V stored in the slabs as
+ * bf16 (round to nearest even); logits fp32.
  *
  * Memory ownership: the caller owns every device buffer it passes (weights,
  * KV arena, token and logit buffers) and every stream. The library
