@@ -131,6 +131,29 @@ def test_prefill_validation(cbd):
     assert e.length(a) == 0 and e.length(b) == 0
 
 
+def test_sample_validation(cbd):
+    """sample_top_p checks rows and every row's parameters before anything is enqueued."""
+    import ctypes
+    e = make(cbd)
+    P = 4096  # stands in for 16-byte aligned device pointers
+    F, U = ctypes.c_float, ctypes.c_uint64
+
+    def call(rows, temps, tops, logits=P, out=P):
+        n = max(1, len(temps))
+        return e.lib.sample_top_p(e.ctx, logits, rows, (F * n)(*temps), (F * n)(*tops), (U * n)(*([1] * n)),
+                                  (U * n)(*([0] * n)), out, None)
+    assert call(0, [], []) == cbd.CBD_OK
+    assert call(65, [1.0] * 65, [0.9] * 65) == cbd.CBD_E_INVAL  # more than 64 rows
+    assert call(2, [1.0, -0.5], [0.9, 0.9]) == cbd.CBD_E_INVAL  # negative temperature
+    assert call(1, [float("inf")], [0.9]) == cbd.CBD_E_INVAL
+    assert call(1, [float("nan")], [0.9]) == cbd.CBD_E_INVAL
+    assert call(2, [1.0, 1.0], [0.9, 0.0]) == cbd.CBD_E_INVAL  # top_p outside (0, 1]
+    assert call(1, [1.0], [1.5]) == cbd.CBD_E_INVAL
+    assert call(1, [1.0], [0.9], logits=P + 4) == cbd.CBD_E_INVAL  # unaligned logits
+    assert call(1, [1.0], [0.9], out=None) == cbd.CBD_E_INVAL
+    assert call(2, [0.0, 0.7], [1.0, 0.5]) == cbd.CBD_E_NODEVICE  # valid, but no device here
+
+
 def test_create_rejects_bad_shapes(cbd):
     from dataclasses import replace
     for bad in (replace(synth.TINY, head_dim=96), replace(synth.TINY, n_heads=3),
