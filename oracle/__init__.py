@@ -14,14 +14,17 @@ lm_head logits; then its position advances by one. The segmented prefill of
 the same page (section "REVISED ... forward_batch_segmented") is each
 segment's causal forward with segment-local positions from 0, with no
 attention across segments. Arithmetic is float64 throughout; storage
-precision follows the model (bf16 weights, bf16 K/V slabs). ``sampling`` holds
-the seeded temperature / top-p selection of a row's token.
+precision follows the model (bf16 weights, bf16 K/V slabs, or affine 8-bit K/V
+slabs from ``kvquant``). ``sampling`` holds the seeded temperature / top-p
+selection of a row's token.
 """
 from .model import (OracleModel, SeqState, bf16_bits_to_f64, round_to_bf16, f64_to_bf16_bits,
                     rmsnorm, rope_angles, apply_rope, attend_one_head, silu, dequant_int4,
                     greedy)
 from .sampling import philox4x64_10, uniform_draw, nucleus_order, sample_row, sample_rows
+from .kvquant import quantize_affine8, dequantize_affine8
 
 __all__ = ["OracleModel", "SeqState", "bf16_bits_to_f64", "round_to_bf16", "f64_to_bf16_bits",
            "rmsnorm", "rope_angles", "apply_rope", "attend_one_head", "silu", "dequant_int4",
-           "greedy", "philox4x64_10", "uniform_draw", "nucleus_order", "sample_row", "sample_rows"]
+           "greedy", "philox4x64_10", "uniform_draw", "nucleus_order", "sample_row", "sample_rows",
+           "quantize_affine8", "dequantize_affine8"]

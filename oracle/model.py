@@ -24,6 +24,9 @@ body; the plainest Llama/Mistral reading is taken):
   fed one at a time through decode attend to identical keys.
 - int4 affine weights: w = scale * code + bias per group of consecutive
   input-dimension elements.
+- Quantized K/V (``kv_format="affine8"``, module ``kvquant``): the slab keeps
+  the affine 8-bit form of the bf16 value above, written when the token is
+  appended; attention reads its dequantized value.
 """
 from __future__ import annotations
 
@@ -31,6 +34,8 @@ from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence
 
 import numpy as np
+
+from .kvquant import dequantize_affine8, quantize_affine8
 
 
 # --------------------------------------------------------------------------- number formats
@@ -131,9 +136,12 @@ def greedy(logits) -> np.ndarray:
 
 @dataclass
 class SeqState:
-    """One sequence's persistent slab: per-layer K and V (bf16 bits, [len, Hkv, Dh])."""
+    """One sequence's persistent slab: per-layer K and V, [len, Hkv, Dh] bf16 bits, or for affine8
+    storage uint8 codes with (scale, bias) pairs in k_sb / v_sb ([len, Hkv, Dh/group, 2] float32)."""
     k: List[np.ndarray]
     v: List[np.ndarray]
+    k_sb: Optional[List[np.ndarray]] = None
+    v_sb: Optional[List[np.ndarray]] = None
 
     @property
     def length(self) -> int:
@@ -148,9 +156,14 @@ class OracleModel:
     ``weights`` is the dict produced by ``synth.make_weights`` (bf16 bit
     patterns, or int4 dicts with ``codes``/``scale``/``bias``)."""
 
-    def __init__(self, weights: Dict, cache_all_layers: bool = False):
+    def __init__(self, weights: Dict, cache_all_layers: bool = False, kv_format: str = "bf16",
+                 kv_group: int = 64):
+        if kv_format not in ("bf16", "affine8"):
+            raise ValueError("kv_format must be 'bf16' or 'affine8'")
         self.w = weights
         self.cfg = weights["shape"]
+        self.kv_format = kv_format
+        self.kv_group = kv_group
         self.seqs: Dict[int, SeqState] = {}
         self._next_id = 0
         self._cache: Dict = {}
@@ -180,8 +193,14 @@ class OracleModel:
         c = self.cfg
         sid = self._next_id
         self._next_id += 1
-        empty = lambda: np.zeros((0, c.n_kv_heads, c.head_dim), dtype=np.uint16)
-        self.seqs[sid] = SeqState([empty() for _ in range(c.n_layers)], [empty() for _ in range(c.n_layers)])
+        if self.kv_format == "bf16":
+            empty = lambda: np.zeros((0, c.n_kv_heads, c.head_dim), dtype=np.uint16)
+            self.seqs[sid] = SeqState([empty() for _ in range(c.n_layers)], [empty() for _ in range(c.n_layers)])
+        else:
+            ec = lambda: np.zeros((0, c.n_kv_heads, c.head_dim), dtype=np.uint8)
+            es = lambda: np.zeros((0, c.n_kv_heads, c.head_dim // self.kv_group, 2), dtype=np.float32)
+            L = range(c.n_layers)
+            self.seqs[sid] = SeqState([ec() for _ in L], [ec() for _ in L], [es() for _ in L], [es() for _ in L])
         return sid
 
     def free_sequence(self, sid: int) -> None:
@@ -189,13 +208,31 @@ class OracleModel:
 
     def append_history(self, sid: int, k_bits, v_bits) -> None:
         """Append given K/V (bf16 bits, [L, n, Hkv, Dh]) to a slab."""
-        s = self.seqs[sid]
         for l in range(self.cfg.n_layers):
-            s.k[l] = np.concatenate([s.k[l], np.asarray(k_bits[l], dtype=np.uint16)])
-            s.v[l] = np.concatenate([s.v[l], np.asarray(v_bits[l], dtype=np.uint16)])
+            self._store(self.seqs[sid], l, np.asarray(k_bits[l], dtype=np.uint16), np.asarray(v_bits[l], dtype=np.uint16))
+
+    def _store(self, s: SeqState, l: int, kb: np.ndarray, vb: np.ndarray) -> None:
+        """Append bf16 K/V bits [n, Hkv, Dh] to layer l of a slab, in the slab's storage format."""
+        if self.kv_format == "bf16":
+            s.k[l] = np.concatenate([s.k[l], kb])
+            s.v[l] = np.concatenate([s.v[l], vb])
+            return
+        for codes, sbs, x in ((s.k, s.k_sb, kb), (s.v, s.v_sb, vb)):
+            c, sb = quantize_affine8(x, self.kv_group)
+            codes[l] = np.concatenate([codes[l], c])
+            sbs[l] = np.concatenate([sbs[l], sb])
+
+    def kv_values(self, sid: int, l: int):
+        """Values attention reads from layer l of a slab: (K, V) float64 [len, Hkv, Dh]."""
+        s = self.seqs[sid]
+        if self.kv_format == "bf16":
+            return bf16_bits_to_f64(s.k[l]), bf16_bits_to_f64(s.v[l])
+        return (dequantize_affine8(s.k[l], s.k_sb[l], self.kv_group),
+                dequantize_affine8(s.v[l], s.v_sb[l], self.kv_group))
 
     def copy_state(self) -> Dict[int, SeqState]:
-        return {sid: SeqState([a.copy() for a in s.k], [a.copy() for a in s.v]) for sid, s in self.seqs.items()}
+        cp = lambda xs: None if xs is None else [a.copy() for a in xs]
+        return {sid: SeqState(cp(s.k), cp(s.v), cp(s.k_sb), cp(s.v_sb)) for sid, s in self.seqs.items()}
 
     # -- one layer for a set of (row, position) queries
     def _layer(self, l: int, h: np.ndarray, rows: Sequence[int], positions: Sequence[int]) -> np.ndarray:
@@ -218,13 +255,12 @@ class OracleModel:
                 raise ValueError("slab length %d != position %d" % (s.k[l].shape[0], t))
             kb = f64_to_bf16_bits(apply_rope(k[i], t, c.rope_theta))[None]
             vb = f64_to_bf16_bits(v[i])[None]
-            s.k[l] = np.concatenate([s.k[l], kb])
-            s.v[l] = np.concatenate([s.v[l], vb])
+            self._store(s, l, kb, vb)
         o = np.zeros((len(rows), c.n_heads, c.head_dim))
         kv_f64 = {}
         for i, (sid, t) in enumerate(zip(rows, positions)):
             if sid not in kv_f64:
-                kv_f64[sid] = (bf16_bits_to_f64(self.seqs[sid].k[l]), bf16_bits_to_f64(self.seqs[sid].v[l]))
+                kv_f64[sid] = self.kv_values(sid, l)
             K, V = kv_f64[sid]
             qr = apply_rope(q[i], t, c.rope_theta)
             for hh in range(c.n_heads):

@@ -76,8 +76,32 @@ def rope(x, t, theta):
     return out
 
 
+def f32_round(x):
+    """Nearest float32 value of a Python float."""
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def affine8_nearest(xs, group):
+    """Affine 8-bit storage by direct search: per group, bias = min, scale = float32((max - min) / 255),
+    and each element takes the code 0..255 whose grid value bias + scale * code is nearest to it
+    (the lower code on an exact tie is never needed for random inputs). Returns dequantized values."""
+    out = []
+    for g0 in range(0, len(xs), group):
+        grp = xs[g0:g0 + group]
+        lo, hi = min(grp), max(grp)
+        s = f32_round((hi - lo) / 255.0)
+        for x in grp:
+            if s == 0.0:
+                out.append(lo)
+                continue
+            best = min(range(256), key=lambda c: abs(lo + s * c - x))
+            out.append(lo + s * best)
+    return out
+
+
 class BruteModel:
-    def __init__(self, weights):
+    def __init__(self, weights, kv_group=None):
+        self.kv_group = kv_group  # None: bf16 slabs; else affine 8-bit slabs with this group
         self.cfg = cfg = weights["shape"]
         if cfg.weight_format == "int4":
             conv = lambda m: int4_mat(m, cfg.group_size)
@@ -106,6 +130,9 @@ class BruteModel:
             v = matvec(L["wv"], a)
             ks = [[bf16_round(z) for z in rope(k[j * dh:(j + 1) * dh], pos, c.rope_theta)] for j in range(hkv)]
             vs = [[bf16_round(z) for z in v[j * dh:(j + 1) * dh]] for j in range(hkv)]
+            if self.kv_group:
+                ks = [affine8_nearest(x, self.kv_group) for x in ks]
+                vs = [affine8_nearest(x, self.kv_group) for x in vs]
             slab = self.kv[sid][l]
             assert len(slab) == pos
             slab.append((ks, vs))

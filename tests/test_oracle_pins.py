@@ -12,7 +12,8 @@ import pytest
 
 import synth
 from oracle import (OracleModel, apply_rope, attend_one_head, bf16_bits_to_f64, dequant_int4,
-                    f64_to_bf16_bits, greedy, rmsnorm, round_to_bf16, rope_angles, silu)
+                    dequantize_affine8, f64_to_bf16_bits, greedy, quantize_affine8, rmsnorm, round_to_bf16,
+                    rope_angles, silu)
 from bruteforce import BruteModel
 
 # micro shapes: small enough for the scalar brute force, big enough to have
@@ -157,12 +158,16 @@ def test_dequant_closed_form_and_group_index():
 
 # --------------------------------------------------------------------------- whole model vs brute force
 
-def _run_trajectory(weights, prompts, steps):
-    """Oracle: prefill each prompt, then greedy decode; brute: same tokens, one at a time."""
-    orc = OracleModel(weights, cache_all_layers=True)
+def _run_trajectory(weights, prompts, steps, kv_group=None, rtol=1e-10):
+    """Oracle: prefill each prompt, then greedy decode; brute: same tokens, one at a time.
+    kv_group: affine 8-bit slabs with that group (None: bf16 slabs)."""
+    if kv_group:
+        orc = OracleModel(weights, cache_all_layers=True, kv_format="affine8", kv_group=kv_group)
+    else:
+        orc = OracleModel(weights, cache_all_layers=True)
     ids = [orc.new_sequence() for _ in prompts]
     lg0 = orc.prefill_segmented(ids, prompts)
-    bf = BruteModel(weights)
+    bf = BruteModel(weights, kv_group=kv_group)
     for i in ids:
         bf.add_seq(i)
     brute0 = []
@@ -170,18 +175,23 @@ def _run_trajectory(weights, prompts, steps):
         for pos, tok in enumerate(p):
             out = bf.forward_token(i, int(tok), pos)
         brute0.append(out)
-    assert np.allclose(lg0, np.array(brute0), rtol=1e-10, atol=1e-12)
+    assert np.allclose(lg0, np.array(brute0), rtol=rtol, atol=1e-12)
     toks = greedy(lg0)
     for step in range(steps):
         lg = orc.decode_step_batch(ids, toks)
         ref = [bf.forward_token(i, int(t), len(p) + step) for i, t, p in zip(ids, toks, prompts)]
-        assert np.allclose(lg, np.array(ref), rtol=1e-10, atol=1e-12)
+        assert np.allclose(lg, np.array(ref), rtol=rtol, atol=1e-12)
         toks = greedy(lg)
-    # slabs: every stored K/V entry equal to the brute force's bf16 values
+    # slabs: every stored K/V entry equal to the brute force's stored values
     for i in ids:
         for l in range(weights["shape"].n_layers):
-            Kb = np.array([[kk for kk in ent[0]] for ent in bf.kv[i][l]])
-            assert np.array_equal(bf16_bits_to_f64(orc.seqs[i].k[l]), Kb)
+            for which in (0, 1):
+                Kb = np.array([[kk for kk in ent[which]] for ent in bf.kv[i][l]])
+                Ko = orc.kv_values(i, l)[which]
+                if kv_group:
+                    assert np.allclose(Ko, Kb, rtol=1e-12, atol=1e-12)
+                else:
+                    assert np.array_equal(Ko, Kb)
 
 
 @pytest.mark.parametrize("gain_std", [0.0, 0.3])
@@ -195,6 +205,113 @@ def test_oracle_matches_scalar_brute_force_int4():
     w = synth.make_weights(MICRO_INT4, seed=6)
     pr = synth.prompts(41, [4, 2], MICRO_INT4.vocab)
     _run_trajectory(w, pr, steps=2)
+
+
+def test_oracle_matches_scalar_brute_force_kv8():
+    """Affine 8-bit slabs: the oracle (float32 rint formula) against the brute force (nearest grid
+    value by search over all 256 codes), groups of 2 dims (two groups per 4-dim head)."""
+    w = synth.make_weights(MICRO, seed=8, gain_std=0.2)
+    pr = synth.prompts(42, [4, 6], MICRO.vocab)
+    _run_trajectory(w, pr, steps=3, kv_group=2, rtol=1e-9)
+
+
+# --------------------------------------------------------------------------- affine 8-bit K/V
+
+def _bf16_bits_of(values):
+    bits = f64_to_bf16_bits(np.asarray(values, dtype=np.float64))
+    assert np.array_equal(bf16_bits_to_f64(bits), values)  # the test values are bf16 values
+    return bits
+
+
+def test_affine8_exact_grid_roundtrip():
+    """Values on a grid b + s*c that bf16 holds exactly come back with their codes, s and b exactly."""
+    rng = np.random.default_rng(3)
+    c0 = np.concatenate([[0, 255], rng.integers(0, 256, 62)])
+    c1 = np.concatenate([[255, 0], rng.integers(0, 256, 62)])
+    v0 = -8.0 + c0 / 16.0            # s = 1/16, b = -8
+    v1 = -1.0 + c1 * 2.0 ** -7       # s = 2^-7, b = -1 (multiples of 2^-7 below 1 in magnitude)
+    bits = _bf16_bits_of(np.concatenate([v0, v1]))
+    codes, sb = quantize_affine8(bits)
+    assert np.array_equal(codes, np.concatenate([c0, c1]).astype(np.uint8))
+    assert np.array_equal(sb, np.array([[1 / 16, -8.0], [2.0 ** -7, -1.0]], dtype=np.float32))
+    assert np.array_equal(dequantize_affine8(codes, sb), np.concatenate([v0, v1]))
+
+
+def test_affine8_codes_are_nearest_grid_points():
+    """Every code is the nearest of the 256 grid values (searched exhaustively in float64), the bias
+    is the group minimum, the scale (max - min)/255 in float32, and the error at most half a step."""
+    rng = np.random.default_rng(11)
+    x = rng.normal(0, 1.5, (6, 2, 128)) * np.exp(rng.normal(0, 1, (6, 2, 1)))
+    bits = f64_to_bf16_bits(x)
+    xv = bf16_bits_to_f64(bits).reshape(6, 2, 2, 64)
+    codes, sb = quantize_affine8(bits)
+    s = sb[..., 0].astype(np.float64)
+    b = sb[..., 1].astype(np.float64)
+    assert np.array_equal(b, xv.min(axis=-1))
+    assert np.array_equal(sb[..., 0], ((xv.max(axis=-1) - xv.min(axis=-1)) / 255.0).astype(np.float32))
+    grid = b[..., None, None] + s[..., None, None] * np.arange(256)  # [6, 2, 2, 1, 256]
+    nearest = np.argmin(np.abs(grid - xv[..., None]), axis=-1)
+    # where (x - b)/s lies within float32 rounding of a half-way point (bf16 inputs make exact
+    # halves common before s is rounded), the float32 decision may take either neighbour
+    quo = (xv - b[..., None]) / s[..., None]
+    near_half = np.abs(quo - np.floor(quo) - 0.5) < 1e-5
+    cc = codes.reshape(6, 2, 2, 64).astype(np.int64)
+    assert np.array_equal(cc[~near_half], nearest[~near_half])
+    assert np.all(np.abs(cc - nearest)[near_half] <= 1) and near_half.sum() < 20
+    err = np.abs(dequantize_affine8(codes, sb).reshape(6, 2, 2, 64) - xv)
+    assert np.all(err <= s[..., None] * (0.5 + 1e-4))
+    assert np.all(codes.reshape(6, 2, 2, 64).min(axis=-1) == 0)
+    assert np.all(codes.reshape(6, 2, 2, 64).max(axis=-1) == 255)
+
+
+def test_affine8_constant_group_and_group_independence():
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([np.full(64, 0.375), rng.normal(0, 1, 64)])
+    bits = f64_to_bf16_bits(vals)
+    codes, sb = quantize_affine8(bits)
+    assert np.all(codes[:64] == 0) and sb[0, 0] == 0.0 and sb[0, 1] == np.float32(0.375)
+    assert np.array_equal(dequantize_affine8(codes, sb)[:64], bf16_bits_to_f64(bits[:64]))
+    # changing the second group leaves the first group's codes and pair alone, and vice versa
+    bits2 = bits.copy()
+    bits2[64:] = f64_to_bf16_bits(rng.normal(0, 3, 64))
+    codes2, sb2 = quantize_affine8(bits2)
+    assert np.array_equal(codes2[:64], codes[:64]) and np.array_equal(sb2[0], sb[0])
+    assert not np.array_equal(codes2[64:], codes[64:])
+    bits3 = bits.copy()
+    bits3[:64] = f64_to_bf16_bits(rng.normal(0, 1, 64))
+    codes3, sb3 = quantize_affine8(bits3)
+    assert np.array_equal(codes3[64:], codes[64:]) and np.array_equal(sb3[1], sb[1])
+
+
+def test_affine8_model_stores_quantized_history():
+    """An affine8 oracle's slab holds quantize(bits) of appended bf16 history, and its attention reads
+    the dequantized values: a history already on each group's grid behaves like the bf16 slab."""
+    w = synth.make_weights(synth.TINY, seed=2, gain_std=0.1)
+    c = synth.TINY
+    rng = np.random.default_rng(9)
+    n = 40
+    # history on a grid: per (layer, token, head, group) b + s*c with s = 2^-7, b = -1, codes 0..255
+    codes = rng.integers(0, 256, (c.n_layers, n, c.n_kv_heads, c.head_dim))
+    codes[..., 0] = 0
+    codes[..., 1] = 255
+    vals = -1.0 + codes * 2.0 ** -7
+    kb = _bf16_bits_of(vals)
+    vb = _bf16_bits_of(vals[:, ::-1])
+    a = OracleModel(w, cache_all_layers=True)
+    q8 = OracleModel(w, cache_all_layers=True, kv_format="affine8")
+    sa, sq = a.new_sequence(), q8.new_sequence()
+    a.append_history(sa, kb, vb)
+    q8.append_history(sq, kb, vb)
+    for l in range(c.n_layers):
+        assert np.array_equal(q8.seqs[sq].k[l], codes[l].astype(np.uint8))
+        assert np.array_equal(q8.kv_values(sq, l)[0], a.kv_values(sa, l)[0])
+        assert np.array_equal(q8.kv_values(sq, l)[1], a.kv_values(sa, l)[1])
+    # one step: identical up to the new token's quantization (a small, nonzero difference)
+    la = a.decode_step_batch([sa], [5])[0]
+    lq = q8.decode_step_batch([sq], [5])[0]
+    d = np.max(np.abs(la - lq))
+    assert 0 < d < 2e-2 * np.max(np.abs(la))
+    assert q8.seqs[sq].length == n + 1 and q8.seqs[sq].k_sb[0].shape == (n + 1, c.n_kv_heads, 1, 2)
 
 
 # --------------------------------------------------------------------------- the pages' invariants
