@@ -24,6 +24,8 @@ Other workloads (``--workload``), each printing its own JSON line:
   fused-dequant gate/up product.
 - llama8b-long: the 8B-shape bf16 model with B = 8 rows at 32768-token contexts,
   128 steps; roofline on decode attention (the K/V stream dominates the step).
+- llama8b-long-kv8: the same with affine 8-bit K/V slabs (codes + float32 scale and bias per
+  64 dims): the K/V stream shrinks to 144 of 256 bytes per token, layer and KV head.
 - continuous: the 8B-shape bf16 model under continuous batching with the batch cap
   swept over 1..64: Poisson arrivals (in decode ticks, offered concurrency about
   1.25 x cap), prompts uniform in [256, 2048] sharing a 1024-token prefix,
@@ -57,6 +59,8 @@ WORKLOADS = {
                        "ctx_lo": 1024, "ctx_hi": 8192, "roofline": "gate_up", "hist_seed": 4},
     "llama8b-long": {"shape": "llama3-8b-shape", "steps": 128, "batch": 8, "sweep": "", "ctx_lo": 32768,
                      "ctx_hi": 32768, "roofline": "attention", "hist_seed": 5},
+    "llama8b-long-kv8": {"shape": "llama3-8b-shape", "steps": 128, "batch": 8, "sweep": "", "ctx_lo": 32768,
+                         "ctx_hi": 32768, "roofline": "attention", "hist_seed": 5, "kv_format": "affine8"},
     "continuous": {"shape": "llama3-8b-shape", "steps": 0, "batch": 64, "sweep": "1,2,4,8,16,32,64", "ctx_lo": 256,
                    "ctx_hi": 2048, "roofline": "gate_up", "hist_seed": 2},
     "prefill": {"shape": "llama3-8b-shape", "steps": 8, "batch": 16, "sweep": "", "ctx_lo": 64, "ctx_hi": 1024,
@@ -160,7 +164,8 @@ def main():
     caps = [int(c) + grow + 8 for c in ctx]
     gran = 256
     arena_tokens = sum((c + gran - 1) // gran * gran for c in caps)
-    kv_tok = shape.kv_bytes_per_token()
+    kv_format = wl.get("kv_format", "bf16")
+    kv_tok = cbd.kv_bytes_per_token(shape, kv_format)
     max_pos = int(max(caps)) + gran
 
     w_bytes = shape.streamed_params() * (2 if shape.weight_format == "bf16" else 0.5625)
@@ -168,11 +173,12 @@ def main():
     weights = synth.make_weights(shape, seed=0)
     log("uploading weights; arena %.1f GB" % (arena_tokens * kv_tok / 1e9))
     eng = cbd.Engine(weights, arena_bytes=arena_tokens * kv_tok, max_batch=64, max_prefill_tokens=64,
-                     max_position=max_pos)
+                     max_position=max_pos, kv_format=kv_format)
     dev = torch.device("cuda:0")
     ids = [eng.alloc(c) for c in caps]
     hist = []
-    keep = not args.no_cpu_baseline and args.workload != "llama8b-long"  # the oracle needs the histories
+    long_ctx = args.workload.startswith("llama8b-long")
+    keep = not args.no_cpu_baseline and not long_ctx  # the oracle needs the histories
     for r in range(B):
         # seeded K/V, appended in chunks of tokens (the same values as synth.kv_history of the whole row)
         n = int(ctx[r])
@@ -191,6 +197,8 @@ def main():
                 vs.append(vc)
         if keep:
             hist.append((np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)))
+    if n_rows > B and kv_format != "bf16":
+        raise SystemExit("a sweep beyond B copies bf16 slabs; not available with %s K/V" % kv_format)
     for r in range(B, n_rows):
         # sweep-only rows reuse the histories of the main rows (device copies)
         src = r % B
@@ -245,8 +253,9 @@ def main():
     kernel_desc = {
         "gate_up": "ksplit_gemm_kernel: gate/up weight stream with fused SwiGLU (%s weights), %s, B=%d" % (
             shape.weight_format, shape.name, B),
-        "attention": "decode_attention_kernel: RoPE + K/V append + ragged GQA attention, %s, B=%d at %d-token "
-                     "contexts" % (shape.name, B, args.ctx_lo),
+        "attention": "%s: RoPE + K/V append + ragged GQA attention, %s K/V, %s, B=%d at %d-token contexts" % (
+            "decode_attention_q8_kernel" if kv_format == "affine8" else "decode_attention_kernel", kv_format,
+            shape.name, B, args.ctx_lo),
     }[rk]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -324,7 +333,7 @@ def main():
 
     cpu = None
     parity = None
-    if not args.no_cpu_baseline and args.workload != "llama8b-long":
+    if not args.no_cpu_baseline and not long_ctx:
         from oracle import OracleModel, greedy
         try:
             from threadpoolctl import threadpool_info
@@ -360,7 +369,8 @@ def main():
            "data": "synthetic",
            "config": {"workload": "%s: %s decode_step_batch, B=%d, contexts U[%d,%d], greedy, %d layers" % (
                args.workload, shape.name, B, args.ctx_lo, args.ctx_hi, shape.n_layers),
-               "batch": B, "contexts": [int(c) for c in ctx_main], "parallelism": "single GPU"},
+               "batch": B, "contexts": [int(c) for c in ctx_main], "kv_format": kv_format,
+               "parallelism": "single GPU"},
            "achieved_hbm_GBps": round(step_gbps, 1), "step_bytes": step_bytes,
            "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),
            "roofline": roofline, "cpu_baseline": cpu, "parity_first_step": parity, "sweep": sweep_out,

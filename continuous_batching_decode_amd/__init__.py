@@ -17,15 +17,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcbd.so")
 
 CBD_OK, CBD_E_INVAL, CBD_E_NOSPACE, CBD_E_CAPACITY, CBD_E_BADSEQ, CBD_E_HIP, CBD_E_NODEVICE = 0, -1, -2, -3, -4, -5, -6
+CBD_E_UNSUPPORTED = -7
 STATUS_NAMES = {0: "CBD_OK", -1: "CBD_E_INVAL", -2: "CBD_E_NOSPACE", -3: "CBD_E_CAPACITY", -4: "CBD_E_BADSEQ",
-                -5: "CBD_E_HIP", -6: "CBD_E_NODEVICE"}
+                -5: "CBD_E_HIP", -6: "CBD_E_NODEVICE", -7: "CBD_E_UNSUPPORTED"}
 WEIGHTS_BF16, WEIGHTS_INT4 = 0, 1
+KV_BF16, KV_AFFINE8 = 0, 1
+KV_FORMATS = {"bf16": KV_BF16, "affine8": KV_AFFINE8}
 
 # every symbol include/cbd.h declares
 EXPORTS = ["cbd_kv_bytes_per_token", "cbd_slab_granule_tokens", "cbd_create", "cbd_destroy", "cbd_last_error",
            "cbd_stats", "kvslab_alloc", "kvslab_free", "kvslab_len", "kvslab_capacity", "kvslab_append",
            "kvslab_read", "decode_step_batch", "prefill_segmented", "greedy_argmax", "cbd_linear", "cbd_pack_int4",
-           "cbd_profile_begin", "cbd_profile_end", "cbd_pack_bf16", "sample_top_p"]
+           "cbd_profile_begin", "cbd_profile_end", "cbd_pack_bf16", "sample_top_p", "kvslab_read_q8"]
 
 KERNEL_KINDS = ["embed", "norm", "qkv", "rope_append", "attention", "attn_combine", "o_proj", "gate_up", "down",
                 "lm_head", "argmax", "sample"]
@@ -41,7 +44,8 @@ class ModelConfig(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn_dim", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                ("weight_format", ctypes.c_int32), ("max_position", ctypes.c_int32)]
+                ("weight_format", ctypes.c_int32), ("max_position", ctypes.c_int32),
+                ("kv_format", ctypes.c_int32)]
 
 
 class Matrix(ctypes.Structure):
@@ -93,6 +97,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvslab_capacity": (i32, [ctx_p, i32, P(i32)]),
         "kvslab_append": (i32, [ctx_p, i32, i32, vp, vp, vp]),
         "kvslab_read": (i32, [ctx_p, i32, i32, i32, vp, vp, vp]),
+        "kvslab_read_q8": (i32, [ctx_p, i32, i32, i32, vp, vp, vp]),
         "decode_step_batch": (i32, [ctx_p, P(i32), i32, vp, vp, vp, vp]),
         "prefill_segmented": (i32, [ctx_p, P(i32), P(i32), i32, vp, vp, vp, vp]),
         "greedy_argmax": (i32, [ctx_p, vp, i32, vp, vp]),
@@ -131,11 +136,18 @@ def _ids(seq: Sequence[int]):
     return arr
 
 
-def model_config(shape, max_position: int) -> ModelConfig:
-    """C config from a shape object (attributes as in synth.ModelShape)."""
+def kv_bytes_per_token(shape, kv_format: str = "bf16") -> int:
+    """Slab bytes per token over all layers, as the library counts them."""
+    cfg = model_config(shape, 1, kv_format)
+    return int(lib().cbd_kv_bytes_per_token(ctypes.byref(cfg)))
+
+
+def model_config(shape, max_position: int, kv_format: str = "bf16") -> ModelConfig:
+    """C config from a shape object (attributes as in synth.ModelShape); kv_format "bf16" or "affine8"."""
     return ModelConfig(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim,
                        shape.ffn_dim, shape.vocab, float(shape.rms_eps), float(shape.rope_theta),
-                       WEIGHTS_INT4 if shape.weight_format == "int4" else WEIGHTS_BF16, int(max_position))
+                       WEIGHTS_INT4 if shape.weight_format == "int4" else WEIGHTS_BF16, int(max_position),
+                       KV_FORMATS[kv_format])
 
 
 def pack_int4(codes: np.ndarray, scale: np.ndarray, bias: np.ndarray):
@@ -176,12 +188,13 @@ class Engine:
 
     def __init__(self, weights: Dict, arena_bytes: int, max_batch: int = 64, max_prefill_tokens: int = 1024,
                  max_segments: int = 64, max_position: Optional[int] = None, host_only: bool = False,
-                 device: str = "cuda"):
+                 device: str = "cuda", kv_format: str = "bf16"):
         self.shape = shape = weights["shape"]
         self.lib = lib()
         if max_position is None:
             max_position = 8192
-        self.cfg = model_config(shape, max_position)
+        self.kv_format = kv_format
+        self.cfg = model_config(shape, max_position, kv_format)
         self.limits = Limits(max_batch, max_prefill_tokens, max_segments, 1 if host_only else 0)
         self._keep: List = []
         self.arena = None
@@ -276,6 +289,18 @@ class Engine:
         _check(self.lib.kvslab_read(self.ctx, int(seq_id), int(start), int(n), k.data_ptr(), v.data_ptr(),
                                     _stream_ptr(stream)))
         return k, v
+
+    def kvslab_read_q8(self, seq_id: int, start: int, n: int, stream=None):
+        """Stored form of an affine 8-bit slab: codes uint8 [L, n, 2, Hkv, Dh] and (scale, bias)
+        float32 [L, n, 2, Hkv, Dh/64, 2] (device tensors)."""
+        import torch
+        s = self.shape
+        codes = torch.empty((s.n_layers, n, 2, s.n_kv_heads, s.head_dim), dtype=torch.uint8, device=self.device)
+        sb = torch.empty((s.n_layers, n, 2, s.n_kv_heads, s.head_dim // 64, 2), dtype=torch.float32,
+                         device=self.device)
+        _check(self.lib.kvslab_read_q8(self.ctx, int(seq_id), int(start), int(n), codes.data_ptr(), sb.data_ptr(),
+                                       _stream_ptr(stream)))
+        return codes, sb
 
     def stats(self) -> Dict[str, int]:
         st = Stats()

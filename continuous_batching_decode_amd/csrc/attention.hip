@@ -294,6 +294,126 @@ CBD_DEVICE AttnItem uniform_item(const AttnItem* items, int i) {
 
 }  // namespace
 
+// The end of a decode item: an unsplit item writes its rows; a split item publishes its unnormalised
+// partial and (max, sum), and the last wave of the (row, KV head) to arrive merges the splits.
+template <int DH, int G>
+CBD_DEVICE void decode_finish(const AttnArgs& a, const AttnItem& it, int j, int2 rp, int lane, const Online<DH>& st) {
+  constexpr int NT = DH / 16;
+  const int g = lane >> 4, c16 = lane & 15;
+  const f32x4_t(&o)[NT] = st.o;
+  const float m_run = st.m, l_run = st.l;
+
+  if (it.part < 0) {  // output: lane (c16 < G) holds dims 16t + 4g + e of head j*G + c16
+    if (c16 < G) store_out<DH>(a, it.row, j * G + c16, g, o, 1.0f / l_run);
+    return;
+  }
+  // split item: publish the unnormalised partial and (max, sum); the last wave of the (row, KV head)
+  // merges. Partials and the arrival counter use agent-scope accesses (coherent across the XCDs'
+  // L2 caches), partials 16 bytes at a time; the wave's stores are acknowledged (vmcnt 0) before its
+  // arrival is counted.
+  if (c16 < G) {
+    const int64_t slot = (int64_t)it.part * a.n_heads + j * G + c16;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) store_agent_x4(a.part_o, (int)((slot * DH + 16 * t + 4 * g) * 4), o[t]);
+    if (g == 0) store_agent_x2(a.part_ml, (int)(slot * 2 * 4), float2{m_run, l_run});
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  int32_t* counter = a.counters + (int64_t)it.row * a.n_kv_heads + j;
+  int last = 0;
+  if (lane == 0) last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == rp.y - 1;
+  last = __shfl(last, 0, 64);
+  if (!last) return;
+
+  // Merge with the whole wave (at most 64 splits). Lane s loads split s's (max, sum) for every head;
+  // the per-head maximum and weighted sum come from wave reductions. Lane l combines output
+  // elements NE*l .. NE*l + NE - 1 of the G x Dh block over the splits in order, the loads of SB
+  // splits in flight at a time; the first SB are requested with the (max, sum) pairs, so up to SB
+  // splits cost one memory latency.
+  constexpr int NE = G * DH / 64;  // 8, 4 or 2 floats per lane
+  const int ns = rp.y;
+  // lane s: (max, sum) of split s for the G heads, 2G consecutive floats
+  float mv[G], wv[G], Mh[G], Lh[G];
+  float ml[2 * G];
+  {
+    const int off = (int)((((int64_t)(rp.x + min(lane, ns - 1)) * a.n_heads + j * G) * 2) * 4);
+    if constexpr (G == 1) {
+      const float2 x = load_agent_x2(a.part_ml, off);
+      ml[0] = x.x;
+      ml[1] = x.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < G / 2; ++q) {
+        const f32x4_t x = load_agent_x4(a.part_ml, off + 16 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ml[4 * q + e] = x[e];
+      }
+    }
+  }
+  const int e0 = lane * NE, hh = e0 / DH, d0 = e0 % DH;
+  const int64_t split_stride = (int64_t)a.n_heads * DH;
+  const int64_t o_base = (int64_t)rp.x * a.n_heads + j * G + hh;  // slot row of split 0, in DH units
+  constexpr int SB = NE >= 4 ? 8 : 16;  // registers: SB x NE floats
+  float ov[SB][NE];
+  auto load_batch = [&](int s0) {  // splits past the last reload it (their weight is 0)
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int off = (int)(((o_base * DH + d0) + (int64_t)min(s0 + u, ns - 1) * split_stride) * 4);
+      if constexpr (NE == 2) {
+        const float2 x = load_agent_x2(a.part_o, off);
+        ov[u][0] = x.x;
+        ov[u][1] = x.y;
+      } else {
+#pragma unroll
+        for (int q = 0; q < NE / 4; ++q) {
+          const f32x4_t x = load_agent_x4(a.part_o, off + 16 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[u][4 * q + e] = x[e];
+        }
+      }
+    }
+  };
+  load_batch(0);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mv[h] = lane < ns ? ml[2 * h] : -INFINITY;  // lanes past the last split take no part
+    wv[h] = lane < ns ? ml[2 * h + 1] : 0.f;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    Mh[h] = wave_max(mv[h]);
+    Lh[h] = wave_sum(exp_or_zero(mv[h], Mh[h]) * wv[h]);
+    wv[h] = exp_or_zero(mv[h], Mh[h]);  // lane s: weight of split s for head h
+  }
+  float acc[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += SB) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      float wgt = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float x = __shfl(wv[h], s0 + u, 64);
+        if (hh == h) wgt = x;
+      }
+#pragma unroll
+      for (int i = 0; i < NE; ++i) acc[i] += wgt * ov[u][i];
+    }
+    if (s0 + SB < ns) load_batch(s0 + SB);
+  }
+  float L = Lh[0];
+#pragma unroll
+  for (int h = 1; h < G; ++h)
+    if (hh == h) L = Lh[h];
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int64_t off = xfrag_off(it.row, (j * G + hh) * DH + d0 + i, a.ld_out);
+    store_split(a.out + off, a.out + a.out_plane + off, acc[i] * inv);
+  }
+  if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ============================================================================ decode
 
 // Workgroups of CBD_ATTN_WG_WAVES waves (the waves share nothing): single-wave workgroups let the
@@ -426,118 +546,346 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_kernel(
     kv.load_v(V1, b1);
     stream_pairs<DH>(kv, K0, V0, K1, V1, b_first, b_end, g, kend, scale, qh, ql, st);
   }
-  const f32x4_t(&o)[NT] = st.o;
-  const float m_run = st.m, l_run = st.l;
+  decode_finish<DH, G>(a, it, j, rp, lane, st);
+}
 
-  if (it.part < 0) {  // output: lane (c16 < G) holds dims 16t + 4g + e of head j*G + c16
-    if (c16 < G) store_out<DH>(a, it.row, j * G + c16, g, o, 1.0f / l_run);
-    return;
-  }
-  // split item: publish the unnormalised partial and (max, sum); the last wave of the (row, KV head)
-  // merges. Partials and the arrival counter use agent-scope accesses (coherent across the XCDs'
-  // L2 caches), partials 16 bytes at a time; the wave's stores are acknowledged (vmcnt 0) before its
-  // arrival is counted.
-  if (c16 < G) {
-    const int64_t slot = (int64_t)it.part * a.n_heads + j * G + c16;
+// ============================================================================ decode, affine 8-bit slabs
+// Keys and values are stored as codes c with a (scale s, bias b) pair per key and group of 64 dims
+// (value = s c + b). Codes 0..255 are exact in bf16, so the products run on the codes themselves and
+// the pairs are applied around them:
+//   score(key, col) = sum_g [ s_g(key) (C_g(key) . q_g(col)) + b_g(key) sum(q_g(col)) ]
+//   O(d, col)       = sum_key (p s_g(d))(key) c(key, d) + sum_key p(key) b_g(d)(key)
+// with C_g . q_g the product over the group's dims (one accumulator per group) and p s_g a bf16
+// pair per group in place of p; the bias sums are per lane (its 8 keys) until the end. A lane's 8
+// keys are those of its score rows, and the records are stored in that order, so every lane reads
+// the 8 records of its lane group with plain 16-byte loads.
+
+namespace {
+
+template <int DH>
+struct Q8Block {
+  static constexpr int NW = DH / 32;       // 16-byte code words per lane (two fragments each)
+  static constexpr int NG = DH / kQGroup;  // groups per head vector
+  static constexpr int NR = 4 * NG;        // 16-byte record loads per lane: 8 keys x NG pairs
+  u32x4_t c[NW];
+  f32x4_t r[NR];
+  // scale and bias of group gi for V-order key 8 * (lane / 16) + i
+  CBD_DEVICE float s(int i, int gi) const { return NG == 2 ? r[i][2 * gi] : r[i >> 1][2 * (i & 1)]; }
+  CBD_DEVICE float b(int i, int gi) const { return NG == 2 ? r[i][2 * gi + 1] : r[i >> 1][2 * (i & 1) + 1]; }
+};
+
+template <int DH>
+struct Q8Stream {
+  const uint8_t* kbase;
+  const uint8_t* vbase;
+  int lane;
+  CBD_DEVICE void load(Q8Block<DH>& x, const uint8_t* base, int b) const {
+    const uint8_t* p = base + (int64_t)b * q8_block_bytes(DH);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) store_agent_x4(a.part_o, (int)((slot * DH + 16 * t + 4 * g) * 4), o[t]);
-    if (g == 0) store_agent_x2(a.part_ml, (int)(slot * 2 * 4), float2{m_run, l_run});
+    for (int i = 0; i < Q8Block<DH>::NW; ++i) x.c[i] = load_stream(p + 1024 * i + 16 * lane);
+    const uint8_t* q = p + 32 * DH + (lane >> 4) * 64 * Q8Block<DH>::NG;
+#pragma unroll
+    for (int i = 0; i < Q8Block<DH>::NR; ++i) x.r[i] = *reinterpret_cast<const f32x4_t*>(q + 16 * i);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  int32_t* counter = a.counters + (int64_t)it.row * a.n_kv_heads + j;
-  int last = 0;
-  if (lane == 0) last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == rp.y - 1;
-  last = __shfl(last, 0, 64);
-  if (!last) return;
+  CBD_DEVICE void load_k(Q8Block<DH>& x, int b) const { load(x, kbase, b); }
+  CBD_DEVICE void load_v(Q8Block<DH>& x, int b) const { load(x, vbase, b); }
+};
 
-  // Merge with the whole wave (at most 64 splits). Lane s loads split s's (max, sum) for every head;
-  // the per-head maximum and weighted sum come from wave reductions. Lane l combines output
-  // elements NE*l .. NE*l + NE - 1 of the G x Dh block over the splits in order, the loads of SB
-  // splits in flight at a time; the first SB are requested with the (max, sum) pairs, so up to SB
-  // splits cost one memory latency.
-  constexpr int NE = G * DH / 64;  // 8, 4 or 2 floats per lane
-  const int ns = rp.y;
-  // lane s: (max, sum) of split s for the G heads, 2G consecutive floats
-  float mv[G], wv[G], Mh[G], Lh[G];
-  float ml[2 * G];
+// fragment `half` (0: bytes 0..7, 1: bytes 8..15) of a code word as 8 bf16 operands (exact)
+CBD_DEVICE bf16x8_t code_frag(const u32x4_t& w, int half) {
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t x = w[2 * half + i];
+    r[2 * i] = pack_bf16x2((float)(x & 255u), (float)((x >> 8) & 255u));
+    r[2 * i + 1] = pack_bf16x2((float)((x >> 16) & 255u), (float)(x >> 24));
+  }
+  return as_frag(r);
+}
+
+// Raw scores of block K for the lane's 8 keys in V order (i < 4: key 4g + i, else 16 + 4g + i - 4).
+template <int DH>
+CBD_DEVICE void q8_scores(const Q8Block<DH>& K, const bf16x8_t (&qh)[DH / 32], const bf16x8_t (&ql)[DH / 32],
+                          const float (&qs)[DH / kQGroup], float (&sv)[8]) {
+  constexpr int NU = DH / 32, NG = DH / kQGroup;
+  f32x4_t acc[2][NG];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) acc[h][gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int f = h * NU + u, gi = u / 2;
+      const bf16x8_t kf = code_frag(K.c[f >> 1], f & 1);
+      acc[h][gi] = mfma(kf, qh[u], acc[h][gi]);
+      acc[h][gi] = mfma(kf, ql[u], acc[h][gi]);
+    }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * h + e;
+      float x = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) x += K.s(i, gi) * acc[h][gi][e] + K.b(i, gi) * qs[gi];
+      sv[i] = x;
+    }
+}
+
+// Online softmax over block b's scores (keys at or past lim masked), then the code product with
+// p s_g as the probability operand of group g's dims and the bias sums.
+template <int DH>
+CBD_DEVICE void q8_accumulate(const Q8Block<DH>& V, float (&sv)[8], int b, int g, int lim, float scale,
+                              Online<DH>& st, float (&bacc)[DH / kQGroup]) {
+  constexpr int NG = DH / kQGroup, NT = DH / 16;
+  const int k0 = 32 * b + 4 * g;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sv[e] = k0 + e < lim ? sv[e] * scale : -INFINITY;
+    sv[4 + e] = k0 + 16 + e < lim ? sv[4 + e] * scale : -INFINITY;
+  }
+  float bm = sv[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) bm = fmaxf(bm, sv[i]);
+  bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+  bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+  const float m_new = fmaxf(st.m, bm);
+  const float alpha = exp_or_zero(st.m, m_new);
+  float p[8], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = exp_or_zero(sv[i], m_new);
+    ps += p[i];
+  }
+  ps += __shfl_xor(ps, 16, 64);
+  ps += __shfl_xor(ps, 32, 64);
+  st.l = st.l * alpha + ps;
+  st.m = m_new;
+  bf16x8_t ph[NG], pl[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    float pg[8], bs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pg[i] = p[i] * V.s(i, gi);
+      bs += p[i] * V.b(i, gi);
+    }
+    bacc[gi] = bacc[gi] * alpha + bs;
+    split8(pg, ph[gi], pl[gi]);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int gi = t / 4;
+    const bf16x8_t vf = code_frag(V.c[t >> 1], t & 1);
+    st.o[t] = st.o[t] * alpha;
+    st.o[t] = mfma(vf, ph[gi], st.o[t]);
+    st.o[t] = mfma(vf, pl[gi], st.o[t]);
+  }
+}
+
+}  // namespace
+
+template <int DH, int G>
+__global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kernel(AttnArgs a, int n_waves) {
+  constexpr int NU = DH / 32;
+  constexpr int NT = DH / 16;
+  constexpr int NG = DH / kQGroup;
+  constexpr int PAIR = DH / 64;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kAttnWgWaves + (threadIdx.x >> 6));
+  if (w >= n_waves) return;
+  const int j = w % a.n_kv_heads;
+  const AttnItem it = uniform_item(a.items, w / a.n_kv_heads);
+  const int pos = it.pos;
+  const int64_t region = (int64_t)(it.stride / 32) * q8_block_bytes(DH);
+  uint8_t* slab = a.arena + it.slab_off;
+  uint8_t* kbase = slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * region;
+  uint8_t* vbase = slab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * region;
+  const bool appends = it.k_end == pos + 1;
+  const int kend = appends ? pos : it.k_end;
+  const int b_first = it.k_begin >> 5, b_end = (kend + 31) >> 5;
+  const float scale = 1.0f / sqrtf((float)DH);
+  const Q8Stream<DH> kv{kbase, vbase, lane};
+
+  Q8Block<DH> K0, V0;
+  kv.load_k(K0, b_first);
+  const float* qkv_row = a.qkv + (int64_t)it.row * a.ld_qkv;
+  float qv[NU][8], kvals[NU][8];
+  Online<DH> st;
   {
-    const int off = (int)((((int64_t)(rp.x + min(lane, ns - 1)) * a.n_heads + j * G) * 2) * 4);
-    if constexpr (G == 1) {
-      const float2 x = load_agent_x2(a.part_ml, off);
-      ml[0] = x.x;
-      ml[1] = x.y;
-    } else {
+    const float* q = qkv_row + (int64_t)(j * G + (c16 < G ? c16 : 0)) * DH;
+    const float* kx = qkv_row + (int64_t)a.n_heads * DH + (int64_t)j * DH;
+    const float* vx = kx + (int64_t)a.n_kv_heads * DH;
 #pragma unroll
-      for (int q = 0; q < G / 2; ++q) {
-        const f32x4_t x = load_agent_x4(a.part_ml, off + 16 * q);
+    for (int u = 0; u < NU; ++u) load8(q + 32 * u + 8 * g, qv[u]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ml[4 * q + e] = x[e];
-      }
+    for (int u = 0; u < NU; ++u) load8(kx + 32 * u + 8 * g, kvals[u]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float4 x = *reinterpret_cast<const float4*>(vx + 16 * t + 4 * g);
+      st.o[t] = f32x4_t{x.x, x.y, x.z, x.w};
     }
   }
-  const int e0 = lane * NE, hh = e0 / DH, d0 = e0 % DH;
-  const int64_t split_stride = (int64_t)a.n_heads * DH;
-  const int64_t o_base = (int64_t)rp.x * a.n_heads + j * G + hh;  // slot row of split 0, in DH units
-  constexpr int SB = NE >= 4 ? 8 : 16;  // registers: SB x NE floats
-  float ov[SB][NE];
-  auto load_batch = [&](int s0) {  // splits past the last reload it (their weight is 0)
+  const int2 rp = a.row_parts[it.row];
+  const float2* cs = a.rope_cs + (int64_t)pos * (DH / 2);
+  auto rotate = [&](float (&x)[NU][8]) {
 #pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      const int off = (int)(((o_base * DH + d0) + (int64_t)min(s0 + u, ns - 1) * split_stride) * 4);
-      if constexpr (NE == 2) {
-        const float2 x = load_agent_x2(a.part_o, off);
-        ov[u][0] = x.x;
-        ov[u][1] = x.y;
-      } else {
+    for (int u = 0; u < NU; ++u) {
+      if (u & PAIR) continue;
 #pragma unroll
-        for (int q = 0; q < NE / 4; ++q) {
-          const f32x4_t x = load_agent_x4(a.part_o, off + 16 * q);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[u][4 * q + e] = x[e];
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float2 c = cs[32 * u + 8 * g + e];
+        const float x1 = x[u][e], x2 = x[u ^ PAIR][e];
+        x[u][e] = x1 * c.x - x2 * c.y;
+        x[u ^ PAIR][e] = x2 * c.x + x1 * c.y;
       }
     }
   };
-  load_batch(0);
+
+  bf16x8_t qh[NU], ql[NU];
+  float qs[NG];
+  rotate(qv);
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    mv[h] = lane < ns ? ml[2 * h] : -INFINITY;  // lanes past the last split take no part
-    wv[h] = lane < ns ? ml[2 * h + 1] : 0.f;
+  for (int gi = 0; gi < NG; ++gi) qs[gi] = 0.f;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (c16 >= G)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[u][e] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qs[u / 2] += qv[u][e];
+    split8(qv[u], qh[u], ql[u]);
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    Mh[h] = wave_max(mv[h]);
-    Lh[h] = wave_sum(exp_or_zero(mv[h], Mh[h]) * wv[h]);
-    wv[h] = exp_or_zero(mv[h], Mh[h]);  // lane s: weight of split s for head h
+  for (int gi = 0; gi < NG; ++gi) {
+    qs[gi] += __shfl_xor(qs[gi], 16, 64);
+    qs[gi] += __shfl_xor(qs[gi], 32, 64);
   }
-  float acc[NE];
+  kv.load_v(V0, b_first);
+
+  float bacc[NG];
 #pragma unroll
-  for (int i = 0; i < NE; ++i) acc[i] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += SB) {
+  for (int gi = 0; gi < NG; ++gi) bacc[gi] = 0.f;
+  if (!appends) {
+    st.clear();
+  } else {
+    // the new token: k rotated and rounded to bf16, quantized per group (the 16 dims of each lane
+    // group, reduced over the four lane groups), attended first with its dequantized value, stored
+    rotate(kvals);
+    float klo[NG], khi[NG];
 #pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      float wgt = 0.f;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float x = __shfl(wv[h], s0 + u, 64);
-        if (hh == h) wgt = x;
-      }
-#pragma unroll
-      for (int i = 0; i < NE; ++i) acc[i] += wgt * ov[u][i];
+    for (int gi = 0; gi < NG; ++gi) {
+      klo[gi] = INFINITY;
+      khi[gi] = -INFINITY;
     }
-    if (s0 + SB < ns) load_batch(s0 + SB);
-  }
-  float L = Lh[0];
 #pragma unroll
-  for (int h = 1; h < G; ++h)
-    if (hh == h) L = Lh[h];
-  const float inv = 1.0f / L;
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    const int64_t off = xfrag_off(it.row, (j * G + hh) * DH + d0 + i, a.ld_out);
-    store_split(a.out + off, a.out + a.out_plane + off, acc[i] * inv);
+      for (int e = 0; e < 8; ++e) {
+        kvals[u][e] = bf16_to_f32(f32_to_bf16(kvals[u][e]));
+        klo[u / 2] = fminf(klo[u / 2], kvals[u][e]);
+        khi[u / 2] = fmaxf(khi[u / 2], kvals[u][e]);
+      }
+    float ks[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      klo[gi] = fminf(klo[gi], __shfl_xor(klo[gi], 16, 64));
+      klo[gi] = fminf(klo[gi], __shfl_xor(klo[gi], 32, 64));
+      khi[gi] = fmaxf(khi[gi], __shfl_xor(khi[gi], 16, 64));
+      khi[gi] = fmaxf(khi[gi], __shfl_xor(khi[gi], 32, 64));
+      ks[gi] = q8_scale(klo[gi], khi[gi]);
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int gi = u / 2;
+      const u32x4_t qhu = __builtin_bit_cast(u32x4_t, qh[u]), qlu = __builtin_bit_cast(u32x4_t, ql[u]);
+      uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t code = q8_code(kvals[u][e], klo[gi], ks[gi]);
+        cw[e >> 2] |= code << (8 * (e & 3));
+        const uint32_t qb = e & 1 ? qhu[e >> 1] >> 16 : qhu[e >> 1] & 0xFFFFu;
+        const uint32_t lb = e & 1 ? qlu[e >> 1] >> 16 : qlu[e >> 1] & 0xFFFFu;
+        dot += (bf16_to_f32(qb) + bf16_to_f32(lb)) * fmaf(ks[gi], (float)code, klo[gi]);
+      }
+      if (c16 == 0) *reinterpret_cast<uint2*>(kbase + kq_off(pos, 32 * u + 8 * g, DH)) = uint2{cw[0], cw[1]};
+    }
+    dot += __shfl_xor(dot, 16, 64);
+    dot += __shfl_xor(dot, 32, 64);
+    st.m = dot * scale;
+    st.l = 1.f;
+    // v: the lane's dims 16t + 4g + e, group t / 4
+    float vlo[NG], vhi[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      vlo[gi] = INFINITY;
+      vhi[gi] = -INFINITY;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        st.o[t][e] = bf16_to_f32(f32_to_bf16(st.o[t][e]));
+        vlo[t / 4] = fminf(vlo[t / 4], st.o[t][e]);
+        vhi[t / 4] = fmaxf(vhi[t / 4], st.o[t][e]);
+      }
+    float vs[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      vlo[gi] = fminf(vlo[gi], __shfl_xor(vlo[gi], 16, 64));
+      vlo[gi] = fminf(vlo[gi], __shfl_xor(vlo[gi], 32, 64));
+      vhi[gi] = fmaxf(vhi[gi], __shfl_xor(vhi[gi], 16, 64));
+      vhi[gi] = fmaxf(vhi[gi], __shfl_xor(vhi[gi], 32, 64));
+      vs[gi] = q8_scale(vlo[gi], vhi[gi]);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gi = t / 4;
+        const uint32_t code = q8_code(st.o[t][e], vlo[gi], vs[gi]);
+        st.o[t][e] = fmaf(vs[gi], (float)code, vlo[gi]);
+        if (c16 == 0) vbase[vq_off(pos, 16 * t + 4 * g + e, DH)] = (uint8_t)code;
+      }
+    if (lane == 0)
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        *reinterpret_cast<float2*>(kbase + sbq_off(pos, gi, DH)) = float2{ks[gi], klo[gi]};
+        *reinterpret_cast<float2*>(vbase + sbq_off(pos, gi, DH)) = float2{vs[gi], vlo[gi]};
+      }
   }
-  if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // blocks [b_first, b_end): the next block's codes and records load while this one is used
+  for (int b = b_first; b + 1 < b_end; ++b) {
+    float sv[8];
+    q8_scores<DH>(K0, qh, ql, qs, sv);
+    __builtin_amdgcn_sched_barrier(0);
+    kv.load_k(K0, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    q8_accumulate<DH>(V0, sv, b, g, kend, scale, st, bacc);
+    __builtin_amdgcn_sched_barrier(0);
+    kv.load_v(V0, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (b_first < b_end) {
+    float sv[8];
+    q8_scores<DH>(K0, qh, ql, qs, sv);
+    q8_accumulate<DH>(V0, sv, b_end - 1, g, kend, scale, st, bacc);
+  }
+  // bias sums over the column's keys (all four lane groups), added to every dim of their group
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    bacc[gi] += __shfl_xor(bacc[gi], 16, 64);
+    bacc[gi] += __shfl_xor(bacc[gi], 32, 64);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.o[t][e] += bacc[t / 4];
+  decode_finish<DH, G>(a, it, j, rp, lane, st);
 }
 
 // ============================================================================ prefill
@@ -601,6 +949,26 @@ hipError_t launch_decode_attention(const AttnArgs& a, int n_items, int head_dim,
   const dim3 grid((n_waves + kAttnWgWaves - 1) / kAttnWgWaves);
   if (head_dim == 128) return launch_decode_dh<128>(G, grid, n_waves, st, a);
   if (head_dim == 64) return launch_decode_dh<64>(G, grid, n_waves, st, a);
+  return hipErrorInvalidValue;
+}
+
+template <int DH>
+static hipError_t launch_decode_q8_dh(int G, dim3 grid, int n_waves, hipStream_t st, const AttnArgs& a) {
+  switch (G) {
+    case 1: launch_kernel((decode_attention_q8_kernel<DH, 1>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
+    case 2: launch_kernel((decode_attention_q8_kernel<DH, 2>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
+    case 4: launch_kernel((decode_attention_q8_kernel<DH, 4>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_attention_q8(const AttnArgs& a, int n_items, int head_dim, hipStream_t st) {
+  const int G = a.n_heads / a.n_kv_heads;
+  const int n_waves = n_items * a.n_kv_heads;
+  const dim3 grid((n_waves + kAttnWgWaves - 1) / kAttnWgWaves);
+  if (head_dim == 128) return launch_decode_q8_dh<128>(G, grid, n_waves, st, a);
+  if (head_dim == 64) return launch_decode_q8_dh<64>(G, grid, n_waves, st, a);
   return hipErrorInvalidValue;
 }
 

@@ -102,6 +102,39 @@ CBD_DEVICE int64_t vslab_off(int key, int d, int dh) {
   return (int64_t)(key >> 5) * 32 * dh + ((d >> 4) << 9) + ((((kk >> 3) << 4) + (d & 15)) << 3) + (kk & 7);
 }
 
+// Affine 8-bit slab layout (K/V stored as codes with a float32 (scale, bias) pair per group of 64
+// dims of one head vector; value = scale * code + bias). A region holds stride tokens in blocks of
+// 32 keys of q8_block_bytes(Dh) bytes: 32 * Dh codes, then 32 records of Dh/64 (scale, bias) pairs.
+//  codes: the fragments of the bf16 layout above with one byte per element (K: fragment
+//     h * (Dh/32) + u, V: fragment t = d/16, lanes as there); 16-byte word i of lane l sits at
+//     byte 1024 i + 16 l and holds fragment 2i in bytes 0..7 and fragment 2i + 1 in bytes 8..15.
+//  records: key kk of the V order (vslab_kk) at byte 32 * Dh + kk * (Dh/64) * 8, group after group.
+//     Lane group g = l/16 owns keys kk = 8g .. 8g + 7: exactly the keys whose scores it holds.
+constexpr int kQGroup = 64;
+CBD_DEVICE constexpr int q8_block_bytes(int dh) { return 32 * dh + 32 * (dh / kQGroup) * 8; }
+CBD_DEVICE int64_t kq_off(int key, int d, int dh) {
+  const int f = ((key >> 4) & 1) * (dh >> 5) + (d >> 5);
+  const int lane = (((d & 31) >> 3) << 4) + (key & 15);
+  return (int64_t)(key >> 5) * q8_block_bytes(dh) + ((f >> 1) << 10) + (lane << 4) + ((f & 1) << 3) + (d & 7);
+}
+CBD_DEVICE int64_t vq_off(int key, int d, int dh) {
+  const int kk = vslab_kk(key), t = d >> 4;
+  const int lane = ((kk >> 3) << 4) + (d & 15);
+  return (int64_t)(key >> 5) * q8_block_bytes(dh) + ((t >> 1) << 10) + (lane << 4) + ((t & 1) << 3) + (kk & 7);
+}
+CBD_DEVICE int64_t sbq_off(int key, int gi, int dh) {
+  return (int64_t)(key >> 5) * q8_block_bytes(dh) + 32 * dh + ((int64_t)vslab_kk(key) * (dh / kQGroup) + gi) * 8;
+}
+
+// Affine 8-bit code of x in a group with minimum lo and scale s = (max - lo) / 255 (q8_scale): the
+// nearest grid point, decided in float32 ((x - lo) / s rounded half to even, clamped to 0..255);
+// a constant group (s = 0) takes code 0.
+CBD_DEVICE float q8_scale(float lo, float hi) { return (hi - lo) / 255.f; }
+CBD_DEVICE uint32_t q8_code(float x, float lo, float s) {
+  if (!(s > 0.f)) return 0u;
+  return (uint32_t)fminf(fmaxf(rintf((x - lo) / s), 0.f), 255.f);
+}
+
 // Per-query-row metadata shared by the RoPE/append and attention kernels.
 struct RowMeta {
   int64_t slab_off;  // byte offset of the row's slab in the arena

@@ -233,6 +233,34 @@ __global__ __launch_bounds__(256) void slab_copy_kernel(uint8_t* arena, int64_t 
   }
 }
 
+// Affine 8-bit slabs: one wave per (token, layer, K or V, KV head, group of 64 dims), lane = dim.
+__global__ __launch_bounds__(256) void slab_q8_kernel(uint8_t* arena, int64_t slab_off, int stride, int pos, int n,
+                                                      int n_kv_heads, int head_dim, const uint16_t* k_in,
+                                                      const uint16_t* v_in, uint8_t* codes_out, float* sb_out) {
+  const int t = blockIdx.x, l = blockIdx.y, kv = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ng = head_dim / kQGroup, units = n_kv_heads * ng;
+  const int64_t region = (int64_t)(stride / 32) * q8_block_bytes(head_dim);
+  const int key = pos + t;
+  for (int u = wave; u < units; u += 4) {
+    const int j = u / ng, gi = u - j * ng, d = gi * kQGroup + lane;
+    uint8_t* base = arena + slab_off + ((int64_t)(l * 2 + kv) * n_kv_heads + j) * region;
+    uint8_t* cp = base + (kv == 0 ? kq_off(key, d, head_dim) : vq_off(key, d, head_dim));
+    float2* sbp = reinterpret_cast<float2*>(base + sbq_off(key, gi, head_dim));
+    if (k_in) {
+      const uint16_t* in = kv == 0 ? k_in : v_in;
+      const float x = bf16_to_f32(in[(((int64_t)l * n + t) * n_kv_heads + j) * head_dim + d]);
+      const float lo = -wave_max(-x), s = q8_scale(lo, wave_max(x));
+      *cp = (uint8_t)q8_code(x, lo, s);
+      if (lane == 0) *sbp = float2{s, lo};
+    } else {
+      const int64_t o = (((int64_t)l * n + t) * 2 + kv) * n_kv_heads + j;
+      codes_out[o * head_dim + d] = *cp;
+      if (lane == 0) reinterpret_cast<float2*>(sb_out)[o * ng + gi] = *sbp;
+    }
+  }
+}
+
 hipError_t launch_embed(const int32_t* tokens, int rows, const uint16_t* embed, int vocab, int d,
                         const uint16_t* gain, float* h, uint16_t* xplanes, int64_t plane, float* ss, int ss_ld,
                         hipStream_t st) {
@@ -277,6 +305,15 @@ hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int po
                             uint16_t* v_out, hipStream_t st) {
   launch_kernel(slab_copy_kernel, dim3(n, n_layers, 2), dim3(256), 0, st, arena, slab_off, stride, pos, n,
                      n_kv_heads, head_dim, k_in, v_in, k_out, v_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_slab_q8(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_layers, int n_kv_heads,
+                          int head_dim, const uint16_t* k_in, const uint16_t* v_in, uint8_t* codes_out, float* sb_out,
+                          hipStream_t st) {
+  if (head_dim % kQGroup || stride % 32) return hipErrorInvalidValue;
+  launch_kernel(slab_q8_kernel, dim3(n, n_layers, 2), dim3(256), 0, st, arena, slab_off, stride, pos, n, n_kv_heads,
+                head_dim, k_in, v_in, codes_out, sb_out);
   return hipGetLastError();
 }
 

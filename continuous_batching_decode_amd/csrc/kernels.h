@@ -134,6 +134,9 @@ struct AttnArgs {
 hipError_t launch_decode_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
 // prefill: q rotated and every token's K/V appended beforehand (one workgroup per item and KV head)
 hipError_t launch_prefill_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
+// decode over affine 8-bit slabs (same items, splits and outputs as launch_decode_attention; the
+// appending item quantizes the new token's K/V into the slab)
+hipError_t launch_decode_attention_q8(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
 
 // greedy argmax per row, lowest id on ties
 // part: kArgmaxSegments x 64 (max, index) pairs; counters: 64 ints, zero between launches
@@ -167,5 +170,10 @@ hipError_t launch_argmax(const float* logits, int rows, int vocab, float* part, 
 hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_layers, int n_kv_heads,
                             int head_dim, const uint16_t* k_in, const uint16_t* v_in, uint16_t* k_out,
                             uint16_t* v_out, hipStream_t st);
+// affine 8-bit slabs: quantize canonical bf16 K/V [L, n, Hkv, Dh] into [pos, pos+n) (k_in, v_in), or
+// gather codes [L, n, 2, Hkv, Dh] and (scale, bias) pairs [L, n, 2, Hkv, Dh/64, 2] back (codes_out, sb_out)
+hipError_t launch_slab_q8(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_layers, int n_kv_heads,
+                          int head_dim, const uint16_t* k_in, const uint16_t* v_in, uint8_t* codes_out, float* sb_out,
+                          hipStream_t st);
 
 }  // namespace cbd

@@ -91,6 +91,7 @@ struct cbd_ctx {
   cbd_model_config cfg{};
   cbd_limits lim{};
   int fmt = FMT_BF16;
+  bool kv8 = false;  // affine 8-bit slabs
   int q_dim = 0, kv_dim = 0, qkv_dim = 0;
   const uint16_t* embed = nullptr;
   const uint16_t* final_norm = nullptr;
@@ -198,6 +199,7 @@ bool valid_model(const cbd_model_config* m, std::string* why) {
   }
   if (m->vocab % 64 || (m->n_kv_heads * m->head_dim) % 64) return bad("vocab and kv width must be multiples of 64");
   if (m->max_position < 1) return bad("max_position must be positive");
+  if (m->kv_format != CBD_KV_BF16 && m->kv_format != CBD_KV_AFFINE8) return bad("unknown kv_format");
   if (!(m->rms_eps >= 0.f) || !(m->rope_theta > 0.f)) return bad("rms_eps >= 0 and rope_theta > 0 required");
   return true;
 }
@@ -299,6 +301,8 @@ struct ProfScope {
 
 extern "C" size_t cbd_kv_bytes_per_token(const cbd_model_config* cfg) {
   if (!cfg) return 0;
+  if (cfg->kv_format == CBD_KV_AFFINE8)
+    return (size_t)cfg->n_layers * 2 * cfg->n_kv_heads * (cfg->head_dim + cfg->head_dim / kQGroup * 8);
   return (size_t)cfg->n_layers * 2 * cfg->n_kv_heads * cfg->head_dim * 2;
 }
 
@@ -455,6 +459,7 @@ extern "C" cbd_status cbd_create(const cbd_model_config* cfg, const cbd_weights*
   c->lim = *limits;
   c->host_only = limits->host_only != 0;
   c->fmt = cfg->weight_format == CBD_WEIGHTS_INT4 ? FMT_INT4 : FMT_BF16;
+  c->kv8 = cfg->kv_format == CBD_KV_AFFINE8;
   c->q_dim = cfg->n_heads * cfg->head_dim;
   c->kv_dim = cfg->n_kv_heads * cfg->head_dim;
   c->qkv_dim = c->q_dim + 2 * c->kv_dim;
@@ -593,10 +598,16 @@ extern "C" cbd_status kvslab_append(cbd_ctx* c, int32_t seq_id, int32_t n_tokens
   if (!k_dev || !v_dev || !aligned16(k_dev) || !aligned16(v_dev))
     return fail(CBD_E_INVAL, "kvslab_append: K/V must be 16-byte aligned device pointers");
   if (c->host_only) return fail(CBD_E_NODEVICE, "kvslab_append: host-only context");
-  HIP_TRY(launch_slab_copy(c->arena, s->off, s->stride, s->len, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
+  if (c->kv8)
+    HIP_TRY(launch_slab_q8(c->arena, s->off, s->stride, s->len, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
                            c->cfg.head_dim, static_cast<const uint16_t*>(k_dev), static_cast<const uint16_t*>(v_dev),
                            nullptr, nullptr, static_cast<hipStream_t>(stream)),
-          "kvslab_append launch");
+            "kvslab_append launch");
+  else
+    HIP_TRY(launch_slab_copy(c->arena, s->off, s->stride, s->len, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
+                             c->cfg.head_dim, static_cast<const uint16_t*>(k_dev), static_cast<const uint16_t*>(v_dev),
+                             nullptr, nullptr, static_cast<hipStream_t>(stream)),
+            "kvslab_append launch");
   c->slabs[seq_id].len += n_tokens;
   return CBD_OK;
 }
@@ -604,6 +615,7 @@ extern "C" cbd_status kvslab_append(cbd_ctx* c, int32_t seq_id, int32_t n_tokens
 extern "C" cbd_status kvslab_read(const cbd_ctx* c, int32_t seq_id, int32_t start, int32_t n_tokens, void* k_out_dev,
                                   void* v_out_dev, cbd_stream stream) {
   if (!c) return fail(CBD_E_INVAL, "kvslab_read: null context");
+  if (c->kv8) return fail(CBD_E_UNSUPPORTED, "kvslab_read: affine 8-bit slabs are read with kvslab_read_q8");
   const Slab* s;
   if (cbd_status st = live_slab(c, seq_id, &s)) return st;
   if (start < 0 || n_tokens < 0) return fail(CBD_E_INVAL, "kvslab_read: negative range");
@@ -617,6 +629,26 @@ extern "C" cbd_status kvslab_read(const cbd_ctx* c, int32_t seq_id, int32_t star
                            c->cfg.head_dim, nullptr, nullptr, static_cast<uint16_t*>(k_out_dev),
                            static_cast<uint16_t*>(v_out_dev), static_cast<hipStream_t>(stream)),
           "kvslab_read launch");
+  return CBD_OK;
+}
+
+extern "C" cbd_status kvslab_read_q8(const cbd_ctx* c, int32_t seq_id, int32_t start, int32_t n_tokens,
+                                     void* codes_out_dev, void* sb_out_dev, cbd_stream stream) {
+  if (!c) return fail(CBD_E_INVAL, "kvslab_read_q8: null context");
+  if (!c->kv8) return fail(CBD_E_UNSUPPORTED, "kvslab_read_q8: the context stores bf16 slabs");
+  const Slab* s;
+  if (cbd_status st = live_slab(c, seq_id, &s)) return st;
+  if (start < 0 || n_tokens < 0) return fail(CBD_E_INVAL, "kvslab_read_q8: negative range");
+  if ((int64_t)start + n_tokens > s->len)
+    return fail(CBD_E_CAPACITY, "kvslab_read_q8: [%d, %d) beyond length %d", start, start + n_tokens, s->len);
+  if (n_tokens == 0) return CBD_OK;
+  if (!codes_out_dev || !sb_out_dev || !aligned16(codes_out_dev) || !aligned16(sb_out_dev))
+    return fail(CBD_E_INVAL, "kvslab_read_q8: outputs must be 16-byte aligned device pointers");
+  if (c->host_only) return fail(CBD_E_NODEVICE, "kvslab_read_q8: host-only context");
+  HIP_TRY(launch_slab_q8(c->arena, s->off, s->stride, start, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
+                         c->cfg.head_dim, nullptr, nullptr, static_cast<uint8_t*>(codes_out_dev),
+                         static_cast<float*>(sb_out_dev), static_cast<hipStream_t>(stream)),
+          "kvslab_read_q8 launch");
   return CBD_OK;
 }
 
@@ -733,10 +765,12 @@ cbd_status run_layers(cbd_ctx* c, int rows, int x_blocks, const RowMeta* meta_d,
       at.part_ml = c->part_ml;
       at.row_parts = reinterpret_cast<const int2*>(row_parts_d);
       at.counters = c->attn_counters;
-      const double kvb = kv_keys * c->kv_dim * 2.0 * 2.0;
+      const double kvb = kv_keys * (c->kv8 ? m.n_kv_heads * (m.head_dim + m.head_dim / kQGroup * 8.0) * 2.0
+                                           : c->kv_dim * 2.0 * 2.0);
       ProfScope p(c, CBD_KERNEL_ATTENTION, kvb + (double)rows * c->q_dim * (4.0 + 4.0) + n_parts * 0.0,
                   kv_keys * m.n_heads * m.head_dim * 4.0, st);
-      HIP_TRY(fused ? launch_decode_attention(at, n_items, m.head_dim, st)
+      HIP_TRY(fused ? (c->kv8 ? launch_decode_attention_q8(at, n_items, m.head_dim, st)
+                              : launch_decode_attention(at, n_items, m.head_dim, st))
                     : launch_prefill_attention(at, n_items, m.head_dim, st),
               "attention");
     }
@@ -871,6 +905,7 @@ extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, cons
   if (K == 0) return CBD_OK;
   if (!seq_ids || !seg_lens || !tokens_dev || !last_logits_dev) return fail(CBD_E_INVAL, "prefill_segmented: null pointer");
   if (!aligned16(last_logits_dev)) return fail(CBD_E_INVAL, "prefill_segmented: logits must be 16-byte aligned");
+  if (c->kv8) return fail(CBD_E_UNSUPPORTED, "prefill_segmented: not available for affine 8-bit slabs");
   int64_t T = 0;
   for (int i = 0; i < K; ++i) {
     const Slab* s;

@@ -74,10 +74,27 @@ typedef enum {
   CBD_E_CAPACITY = -3, /* the slab's capacity (or the RoPE table) would be exceeded */
   CBD_E_BADSEQ = -4,   /* unknown or freed sequence id */
   CBD_E_HIP = -5,      /* a HIP runtime call failed */
-  CBD_E_NODEVICE = -6  /* context was created host-only: bookkeeping works, device work does not */
+  CBD_E_NODEVICE = -6, /* context was created host-only: bookkeeping works, device work does not */
+  CBD_E_UNSUPPORTED = -7 /* the call is not available for this context's K/V storage format */
 } cbd_status;
 
 enum { CBD_WEIGHTS_BF16 = 0, CBD_WEIGHTS_INT4 = 1 };
+
+/*
+ * K/V storage of the slabs (mlx-bun "Batching" design note, section 4.3: a quantized cache is held
+ * as (packed values, scales, biases); section 6 "KV memory model": quantized K/V multiplies the
+ * arena's capacity).
+ *  CBD_KV_BF16:    every K/V element is stored as bf16 (rounded to nearest even).
+ *  CBD_KV_AFFINE8: each group of 64 consecutive dims of one head vector is stored as 8-bit codes
+ *                  with a float32 (scale, bias) pair: bias = the group's minimum, scale = (maximum -
+ *                  bias) / 255, code = (x - bias) / scale rounded half to even and clamped to 0..255
+ *                  (decided in float32; code 0 when scale = 0), where x is the element's bf16 value;
+ *                  attention reads scale * code + bias. 144 bytes per token, layer and KV head at
+ *                  head_dim 128 (bf16: 256). decode_step_batch and kvslab_append support it;
+ *                  prefill_segmented and kvslab_read return CBD_E_UNSUPPORTED (kvslab_read_q8 reads
+ *                  the stored form).
+ */
+enum { CBD_KV_BF16 = 0, CBD_KV_AFFINE8 = 1 };
 
 typedef struct {
   int32_t n_layers;
@@ -91,6 +108,7 @@ typedef struct {
   float rope_theta;
   int32_t weight_format; /* CBD_WEIGHTS_BF16 or CBD_WEIGHTS_INT4 */
   int32_t max_position;  /* length of the RoPE table: no slab may grow beyond it */
+  int32_t kv_format;     /* CBD_KV_BF16 (0) or CBD_KV_AFFINE8 (1) */
 } cbd_model_config;
 
 /*
@@ -145,8 +163,9 @@ typedef struct {
   int64_t prefill_tokens;
 } cbd_stats_t;
 
-/* Bytes of K and V (bf16) one token occupies in a slab, over all layers:
- * n_layers * 2 * n_kv_heads * head_dim * 2. */
+/* Bytes of K and V one token occupies in a slab, over all layers: n_layers * 2 * n_kv_heads *
+ * head_dim * 2 for bf16 slabs, n_layers * 2 * n_kv_heads * (head_dim + head_dim / 64 * 8) for
+ * affine 8-bit slabs. */
 size_t cbd_kv_bytes_per_token(const cbd_model_config* cfg);
 
 /* Tokens per arena granule: slab capacities are rounded up to a multiple. */
@@ -197,7 +216,9 @@ cbd_status kvslab_capacity(const cbd_ctx* ctx, int32_t seq_id, int32_t* cap_out)
  * Append n_tokens of given K and V to a slab at positions [len, len+n):
  * k_dev, v_dev are bf16 [n_layers, n_tokens, n_kv_heads, head_dim]
  * (K already rotated to its position). Used to seed long histories and to
- * re-inject saved state. CBD_E_CAPACITY if len + n_tokens > capacity.
+ * re-inject saved state. An affine 8-bit slab stores them quantized (per
+ * token, head and group of 64 dims, as CBD_KV_AFFINE8 states). CBD_E_CAPACITY
+ * if len + n_tokens > capacity.
  */
 cbd_status kvslab_append(cbd_ctx* ctx, int32_t seq_id, int32_t n_tokens, const void* k_dev,
                          const void* v_dev, cbd_stream stream);
@@ -208,6 +229,16 @@ cbd_status kvslab_append(cbd_ctx* ctx, int32_t seq_id, int32_t n_tokens, const v
  */
 cbd_status kvslab_read(const cbd_ctx* ctx, int32_t seq_id, int32_t start, int32_t n_tokens,
                        void* k_out_dev, void* v_out_dev, cbd_stream stream);
+
+/*
+ * Read tokens [start, start + n) of an affine 8-bit slab in its stored form:
+ *  codes_out_dev  device uint8 [L, n, 2, n_kv_heads, head_dim] (index 2: 0 = K, 1 = V)
+ *  sb_out_dev     device float32 [L, n, 2, n_kv_heads, head_dim / 64, 2] (scale, bias)
+ * Both 16-byte aligned, caller-owned. CBD_E_UNSUPPORTED on a bf16 context, CBD_E_CAPACITY if
+ * start + n > len. For tests and for moving a quantized history out of the arena.
+ */
+cbd_status kvslab_read_q8(const cbd_ctx* ctx, int32_t seq_id, int32_t start, int32_t n_tokens, void* codes_out_dev,
+                          void* sb_out_dev, cbd_stream stream);
 
 /*
  * One batched decode step over B distinct live sequences.

@@ -196,3 +196,38 @@ def test_int4_packing_layout(cbd):
     assert np.array_equal(scale, m["scale"]) and np.array_equal(bias, m["bias"])
     with pytest.raises(cbd.CbdError):
         cbd.pack_int4(np.full((16, 256), 16, np.uint8), m["scale"][:16], m["bias"][:16])
+
+
+def test_affine8_kv_format_host(cbd):
+    """Affine 8-bit slabs: bytes per token, arena accounting and the calls that reject the format."""
+    assert cbd.kv_bytes_per_token(synth.LLAMA8B, "affine8") == 32 * 2 * 8 * (128 + 2 * 8)
+    assert cbd.kv_bytes_per_token(synth.TINY, "affine8") == 2 * 2 * 2 * (64 + 8)
+    assert cbd.kv_bytes_per_token(synth.LLAMA8B, "bf16") == synth.LLAMA8B.kv_bytes_per_token()
+    g = cbd.lib().cbd_slab_granule_tokens()
+    per_tok = cbd.kv_bytes_per_token(synth.TINY, "affine8")
+    e = cbd.Engine({"shape": synth.TINY}, arena_bytes=4 * g * per_tok, host_only=True, max_position=4096,
+                   kv_format="affine8")
+    a = e.alloc(2 * g)
+    assert e.stats()["arena_bytes_used"] == 2 * g * per_tok
+    b = e.alloc(2 * g)
+    with pytest.raises(cbd.CbdError) as ei:
+        e.alloc(1)
+    assert ei.value.status == cbd.CBD_E_NOSPACE
+    lib = cbd.lib()
+    ids = (ctypes.c_int32 * 1)(a)
+    lens = (ctypes.c_int32 * 1)(4)
+    assert lib.prefill_segmented(e.ctx, ids, lens, 1, 256, 256, None, None) == cbd.CBD_E_UNSUPPORTED
+    assert lib.kvslab_read(e.ctx, a, 0, 0, 256, 256, None) == cbd.CBD_E_UNSUPPORTED
+    assert lib.kvslab_read_q8(e.ctx, a, 0, 0, 256, 256, None) == cbd.CBD_OK
+    assert lib.kvslab_read_q8(e.ctx, a, 0, 1, 256, 256, None) == cbd.CBD_E_CAPACITY
+    assert lib.kvslab_read_q8(e.ctx, b + 5, 0, 0, 256, 256, None) == cbd.CBD_E_BADSEQ
+    e.free(a)
+    e.free(b)
+    bf = make(cbd)
+    s = bf.alloc(10)
+    assert lib.kvslab_read_q8(bf.ctx, s, 0, 0, 256, 256, None) == cbd.CBD_E_UNSUPPORTED
+    cfg = cbd.model_config(synth.TINY, 4096)
+    cfg.kv_format = 5
+    lim = cbd.Limits(8, 64, 8, 1)
+    ctx = ctypes.c_void_p()
+    assert lib.cbd_create(ctypes.byref(cfg), None, ctypes.byref(lim), None, 1 << 20, ctypes.byref(ctx)) == cbd.CBD_E_INVAL
