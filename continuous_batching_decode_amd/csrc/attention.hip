@@ -562,33 +562,50 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_kernel(
 
 namespace {
 
+// Codes of one block in registers; records of a block are staged through the wave's LDS slot (each
+// lane loads 16 bytes of the block's K and V records and writes them there), and each lane reads the
+// records of its lane group's 8 keys from LDS right before they are used. This keeps two blocks in
+// flight within two waves per SIMD.
 template <int DH>
-struct Q8Block {
-  static constexpr int NW = DH / 32;       // 16-byte code words per lane (two fragments each)
-  static constexpr int NG = DH / kQGroup;  // groups per head vector
-  static constexpr int NR = 4 * NG;        // 16-byte record loads per lane: 8 keys x NG pairs
+struct Q8Codes {
+  static constexpr int NW = DH / 32;  // 16-byte code words per lane (two fragments each)
   u32x4_t c[NW];
+};
+
+template <int DH>
+struct Q8Recs {
+  static constexpr int NG = DH / kQGroup;  // groups per head vector
+  static constexpr int NR = 4 * NG;        // 16-byte records per lane group: 8 keys x NG pairs
+  static constexpr int U = 16 * NG;        // 16-byte record units per block, K or V
   f32x4_t r[NR];
   // scale and bias of group gi for V-order key 8 * (lane / 16) + i
   CBD_DEVICE float s(int i, int gi) const { return NG == 2 ? r[i][2 * gi] : r[i >> 1][2 * (i & 1)]; }
   CBD_DEVICE float b(int i, int gi) const { return NG == 2 ? r[i][2 * gi + 1] : r[i >> 1][2 * (i & 1) + 1]; }
+  // slot: 64 units, K records first (U units), then V records (U units)
+  CBD_DEVICE void read(const f32x4_t* slot, int kv, int g) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) r[i] = slot[kv * U + NR * g + i];
+  }
 };
 
 template <int DH>
 struct Q8Stream {
   const uint8_t* kbase;
   const uint8_t* vbase;
+  const uint8_t* rbase;  // this lane's 16 record bytes of block 0
   int lane;
-  CBD_DEVICE void load(Q8Block<DH>& x, const uint8_t* base, int b) const {
-    const uint8_t* p = base + (int64_t)b * q8_block_bytes(DH);
-#pragma unroll
-    for (int i = 0; i < Q8Block<DH>::NW; ++i) x.c[i] = load_stream(p + 1024 * i + 16 * lane);
-    const uint8_t* q = p + 32 * DH + (lane >> 4) * 64 * Q8Block<DH>::NG;
-#pragma unroll
-    for (int i = 0; i < Q8Block<DH>::NR; ++i) x.r[i] = *reinterpret_cast<const f32x4_t*>(q + 16 * i);
+  CBD_DEVICE Q8Stream(const uint8_t* k, const uint8_t* v, int l) : kbase(k), vbase(v), lane(l) {
+    constexpr int U = Q8Recs<DH>::U;
+    rbase = (l < U ? k + 16 * l : v + 16 * (l < 2 * U ? l - U : 0)) + 32 * DH;
   }
-  CBD_DEVICE void load_k(Q8Block<DH>& x, int b) const { load(x, kbase, b); }
-  CBD_DEVICE void load_v(Q8Block<DH>& x, int b) const { load(x, vbase, b); }
+  CBD_DEVICE void load(Q8Codes<DH>& x, const uint8_t* base, int b) const {
+    const uint8_t* p = base + (int64_t)b * q8_block_bytes(DH) + 16 * lane;
+#pragma unroll
+    for (int i = 0; i < Q8Codes<DH>::NW; ++i) x.c[i] = load_stream(p + 1024 * i);
+  }
+  CBD_DEVICE void load_k(Q8Codes<DH>& x, int b) const { load(x, kbase, b); }
+  CBD_DEVICE void load_v(Q8Codes<DH>& x, int b) const { load(x, vbase, b); }
+  CBD_DEVICE void load_r(u32x4_t& r, int b) const { r = load_stream(rbase + (int64_t)b * q8_block_bytes(DH)); }
 };
 
 // fragment `half` (0: bytes 0..7, 1: bytes 8..15) of a code word as 8 bf16 operands (exact)
@@ -603,10 +620,10 @@ CBD_DEVICE bf16x8_t code_frag(const u32x4_t& w, int half) {
   return as_frag(r);
 }
 
-// Raw scores of block K for the lane's 8 keys in V order (i < 4: key 4g + i, else 16 + 4g + i - 4).
+// Raw scores of a block for the lane's 8 keys in V order (i < 4: key 4g + i, else 16 + 4g + i - 4).
 template <int DH>
-CBD_DEVICE void q8_scores(const Q8Block<DH>& K, const bf16x8_t (&qh)[DH / 32], const bf16x8_t (&ql)[DH / 32],
-                          const float (&qs)[DH / kQGroup], float (&sv)[8]) {
+CBD_DEVICE void q8_scores(const Q8Codes<DH>& K, const f32x4_t* slot, int g, const bf16x8_t (&qh)[DH / 32],
+                          const bf16x8_t (&ql)[DH / 32], const float (&qs)[DH / kQGroup], float (&sv)[8]) {
   constexpr int NU = DH / 32, NG = DH / kQGroup;
   f32x4_t acc[2][NG];
 #pragma unroll
@@ -622,6 +639,8 @@ CBD_DEVICE void q8_scores(const Q8Block<DH>& K, const bf16x8_t (&qh)[DH / 32], c
       acc[h][gi] = mfma(kf, qh[u], acc[h][gi]);
       acc[h][gi] = mfma(kf, ql[u], acc[h][gi]);
     }
+  Q8Recs<DH> R;
+  R.read(slot, 0, g);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -629,57 +648,73 @@ CBD_DEVICE void q8_scores(const Q8Block<DH>& K, const bf16x8_t (&qh)[DH / 32], c
       const int i = 4 * h + e;
       float x = 0.f;
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi) x += K.s(i, gi) * acc[h][gi][e] + K.b(i, gi) * qs[gi];
+      for (int gi = 0; gi < NG; ++gi) x += R.s(i, gi) * acc[h][gi][e] + R.b(i, gi) * qs[gi];
       sv[i] = x;
     }
 }
 
-// Online softmax over block b's scores (keys at or past lim masked), then the code product with
-// p s_g as the probability operand of group g's dims and the bias sums.
-template <int DH>
-CBD_DEVICE void q8_accumulate(const Q8Block<DH>& V, float (&sv)[8], int b, int g, int lim, float scale,
-                              Online<DH>& st, float (&bacc)[DH / kQGroup]) {
-  constexpr int NG = DH / kQGroup, NT = DH / 16;
-  const int k0 = 32 * b + 4 * g;
+// Online softmax over NB consecutive blocks from b (keys at or past lim masked): p for their keys,
+// and the running state, O and the bias sums rescaled.
+template <int DH, int NB>
+CBD_DEVICE void q8_softmax(float (&sv)[NB][8], float (&p)[NB][8], int b, int g, int lim, float scale,
+                           Online<DH>& st, float (&bacc)[DH / kQGroup]) {
+  float bm = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    sv[e] = k0 + e < lim ? sv[e] * scale : -INFINITY;
-    sv[4 + e] = k0 + 16 + e < lim ? sv[4 + e] * scale : -INFINITY;
+  for (int k = 0; k < NB; ++k) {
+    const int k0 = 32 * (b + k) + 4 * g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[k][e] = k0 + e < lim ? sv[k][e] * scale : -INFINITY;
+      sv[k][4 + e] = k0 + 16 + e < lim ? sv[k][4 + e] * scale : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bm = fmaxf(bm, sv[k][i]);
   }
-  float bm = sv[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) bm = fmaxf(bm, sv[i]);
   bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
   bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
   const float m_new = fmaxf(st.m, bm);
   const float alpha = exp_or_zero(st.m, m_new);
-  float p[8], ps = 0.f;
+  float ps = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    p[i] = exp_or_zero(sv[i], m_new);
-    ps += p[i];
-  }
+  for (int k = 0; k < NB; ++k)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[k][i] = exp_or_zero(sv[k][i], m_new);
+      ps += p[k][i];
+    }
   ps += __shfl_xor(ps, 16, 64);
   ps += __shfl_xor(ps, 32, 64);
   st.l = st.l * alpha + ps;
   st.m = m_new;
+#pragma unroll
+  for (int t = 0; t < DH / 16; ++t) st.o[t] = st.o[t] * alpha;
+#pragma unroll
+  for (int gi = 0; gi < DH / kQGroup; ++gi) bacc[gi] *= alpha;
+}
+
+// O^T += codes^T (p s_g)^T per group of dims, and the bias sums, for one block.
+template <int DH>
+CBD_DEVICE void q8_block_pv(const Q8Codes<DH>& V, const f32x4_t* slot, int g, const float (&p)[8], Online<DH>& st,
+                            float (&bacc)[DH / kQGroup]) {
+  constexpr int NG = DH / kQGroup, NT = DH / 16;
+  Q8Recs<DH> R;
+  R.read(slot, 1, g);
   bf16x8_t ph[NG], pl[NG];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     float pg[8], bs = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pg[i] = p[i] * V.s(i, gi);
-      bs += p[i] * V.b(i, gi);
+      pg[i] = p[i] * R.s(i, gi);
+      bs += p[i] * R.b(i, gi);
     }
-    bacc[gi] = bacc[gi] * alpha + bs;
+    bacc[gi] += bs;
     split8(pg, ph[gi], pl[gi]);
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int gi = t / 4;
     const bf16x8_t vf = code_frag(V.c[t >> 1], t & 1);
-    st.o[t] = st.o[t] * alpha;
     st.o[t] = mfma(vf, ph[gi], st.o[t]);
     st.o[t] = mfma(vf, pl[gi], st.o[t]);
   }
@@ -707,10 +742,20 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
   const int kend = appends ? pos : it.k_end;
   const int b_first = it.k_begin >> 5, b_end = (kend + 31) >> 5;
   const float scale = 1.0f / sqrtf((float)DH);
-  const Q8Stream<DH> kv{kbase, vbase, lane};
+  const Q8Stream<DH> kv(kbase, vbase, lane);
+  __shared__ f32x4_t q8_lds[kAttnWgWaves][2][64];
+  f32x4_t* slot0 = q8_lds[threadIdx.x >> 6][0];
+  f32x4_t* slot1 = q8_lds[threadIdx.x >> 6][1];
 
-  Q8Block<DH> K0, V0;
+  // blocks b_first and b1 in flight from the start (records first: they are staged first)
+  const int last = max(b_end - 1, b_first);
+  const int b1 = min(b_first + 1, last);
+  Q8Codes<DH> K0, V0, K1, V1;
+  u32x4_t R0, R1;
+  kv.load_r(R0, b_first);
+  kv.load_r(R1, b1);
   kv.load_k(K0, b_first);
+  kv.load_k(K1, b1);
   const float* qkv_row = a.qkv + (int64_t)it.row * a.ld_qkv;
   float qv[NU][8], kvals[NU][8];
   Online<DH> st;
@@ -764,6 +809,7 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
     qs[gi] += __shfl_xor(qs[gi], 32, 64);
   }
   kv.load_v(V0, b_first);
+  kv.load_v(V1, b1);
 
   float bacc[NG];
 #pragma unroll
@@ -858,22 +904,45 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
       }
   }
 
-  // blocks [b_first, b_end): the next block's codes and records load while this one is used
-  for (int b = b_first; b + 1 < b_end; ++b) {
-    float sv[8];
-    q8_scores<DH>(K0, qh, ql, qs, sv);
+  // blocks [b_first, b_end) two at a time, the next two loading while these are used (indices past
+  // the last clamp to it, so every load stays unconditional)
+  int b = b_first;
+  for (; b + 2 < b_end; b += 2) {
+    slot0[lane] = __builtin_bit_cast(f32x4_t, R0);
+    slot1[lane] = __builtin_bit_cast(f32x4_t, R1);
     __builtin_amdgcn_sched_barrier(0);
-    kv.load_k(K0, b + 1);
+    kv.load_r(R0, b + 2);
+    kv.load_r(R1, min(b + 3, last));
     __builtin_amdgcn_sched_barrier(0);
-    q8_accumulate<DH>(V0, sv, b, g, kend, scale, st, bacc);
+    float sv[2][8], p[2][8];
+    q8_scores<DH>(K0, slot0, g, qh, ql, qs, sv[0]);
+    q8_scores<DH>(K1, slot1, g, qh, ql, qs, sv[1]);
     __builtin_amdgcn_sched_barrier(0);
-    kv.load_v(V0, b + 1);
+    kv.load_k(K0, b + 2);
+    kv.load_k(K1, min(b + 3, last));
+    __builtin_amdgcn_sched_barrier(0);
+    q8_softmax<DH, 2>(sv, p, b, g, kend, scale, st, bacc);
+    q8_block_pv<DH>(V0, slot0, g, p[0], st, bacc);
+    q8_block_pv<DH>(V1, slot1, g, p[1], st, bacc);
+    __builtin_amdgcn_sched_barrier(0);
+    kv.load_v(V0, b + 2);
+    kv.load_v(V1, min(b + 3, last));
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (b_first < b_end) {
-    float sv[8];
-    q8_scores<DH>(K0, qh, ql, qs, sv);
-    q8_accumulate<DH>(V0, sv, b_end - 1, g, kend, scale, st, bacc);
+  slot0[lane] = __builtin_bit_cast(f32x4_t, R0);
+  slot1[lane] = __builtin_bit_cast(f32x4_t, R1);
+  if (b + 1 < b_end) {  // a last pair
+    float sv[2][8], p[2][8];
+    q8_scores<DH>(K0, slot0, g, qh, ql, qs, sv[0]);
+    q8_scores<DH>(K1, slot1, g, qh, ql, qs, sv[1]);
+    q8_softmax<DH, 2>(sv, p, b, g, kend, scale, st, bacc);
+    q8_block_pv<DH>(V0, slot0, g, p[0], st, bacc);
+    q8_block_pv<DH>(V1, slot1, g, p[1], st, bacc);
+  } else if (b < b_end) {  // a last single block
+    float sv[1][8], p[1][8];
+    q8_scores<DH>(K0, slot0, g, qh, ql, qs, sv[0]);
+    q8_softmax<DH, 1>(sv, p, b, g, kend, scale, st, bacc);
+    q8_block_pv<DH>(V0, slot0, g, p[0], st, bacc);
   }
   // bias sums over the column's keys (all four lane groups), added to every dim of their group
 #pragma unroll
