@@ -1001,6 +1001,82 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(AttnArgs a, i
   if (c16 < n_q) store_out<DH>(a, it.row + c16, h, g, st.o, 1.0f / st.l);
 }
 
+// Prefill over affine 8-bit slabs: the tile and column layout of prefill_attention_kernel, blocks
+// streamed one at a time through the code products of the decode kernel.
+template <int DH>
+__global__ __launch_bounds__(256, 2) void prefill_attention_q8_kernel(AttnArgs a, int n_waves) {
+  constexpr int NU = DH / 32;
+  constexpr int NT = DH / 16;
+  constexpr int NG = DH / kQGroup;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  __shared__ f32x4_t q8_lds[4][64];
+  f32x4_t* slot = q8_lds[threadIdx.x >> 6];
+  if (w >= n_waves) return;
+  const AttnItem it = uniform_item(a.items, w / a.n_heads);
+  const int h = w % a.n_heads, j = h / (a.n_heads / a.n_kv_heads);
+  const int n_q = it.k_end - it.pos;
+  const int64_t region = (int64_t)(it.stride / 32) * q8_block_bytes(DH);
+  const uint8_t* slab = a.arena + it.slab_off;
+  const Q8Stream<DH> kv(slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * region,
+                        slab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * region, lane);
+  Q8Codes<DH> K0, V0;
+  u32x4_t R0;
+  kv.load_r(R0, 0);
+  kv.load_k(K0, 0);
+  bf16x8_t qh[NU], ql[NU];
+  float qs[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) qs[gi] = 0.f;
+  {
+    const float* q = a.qkv + (int64_t)(it.row + min(c16, n_q - 1)) * a.ld_qkv + (int64_t)h * DH;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      float qv[8];
+      load8(q + 32 * u + 8 * g, qv);
+      if (c16 >= n_q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qs[u / 2] += qv[e];
+      split8(qv, qh[u], ql[u]);
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    qs[gi] += __shfl_xor(qs[gi], 16, 64);
+    qs[gi] += __shfl_xor(qs[gi], 32, 64);
+  }
+  kv.load_v(V0, 0);
+  Online<DH> st;
+  st.clear();
+  float bacc[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) bacc[gi] = 0.f;
+  const int lim = c16 < n_q ? it.pos + c16 + 1 : 0;
+  const int b_end = (it.k_end + 31) >> 5;
+  for (int b = 0; b < b_end; ++b) {
+    slot[lane] = __builtin_bit_cast(f32x4_t, R0);
+    kv.load_r(R0, min(b + 1, b_end - 1));
+    float sv[1][8], p[1][8];
+    q8_scores<DH>(K0, slot, g, qh, ql, qs, sv[0]);
+    kv.load_k(K0, min(b + 1, b_end - 1));
+    q8_softmax<DH, 1>(sv, p, b, g, lim, 1.0f / sqrtf((float)DH), st, bacc);
+    q8_block_pv<DH>(V0, slot, g, p[0], st, bacc);
+    kv.load_v(V0, min(b + 1, b_end - 1));
+  }
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    bacc[gi] += __shfl_xor(bacc[gi], 16, 64);
+    bacc[gi] += __shfl_xor(bacc[gi], 32, 64);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.o[t][e] += bacc[t / 4];
+  if (c16 < n_q) store_out<DH>(a, it.row + c16, h, g, st.o, 1.0f / st.l);
+}
+
 template <int DH>
 static hipError_t launch_decode_dh(int G, dim3 grid, int n_waves, hipStream_t st, const AttnArgs& a) {
   switch (G) {
@@ -1039,6 +1115,15 @@ hipError_t launch_decode_attention_q8(const AttnArgs& a, int n_items, int head_d
   if (head_dim == 128) return launch_decode_q8_dh<128>(G, grid, n_waves, st, a);
   if (head_dim == 64) return launch_decode_q8_dh<64>(G, grid, n_waves, st, a);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_attention_q8(const AttnArgs& a, int n_items, int head_dim, hipStream_t st) {
+  const int n_waves = n_items * a.n_heads;
+  const dim3 grid((n_waves + 3) / 4);
+  if (head_dim == 128) launch_kernel((prefill_attention_q8_kernel<128>), grid, dim3(256), 0, st, a, n_waves);
+  else if (head_dim == 64) launch_kernel((prefill_attention_q8_kernel<64>), grid, dim3(256), 0, st, a, n_waves);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st) {

@@ -137,6 +137,52 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float* qkv, int ld_qkv
   }
 }
 
+// The same for affine 8-bit slabs: queries rotate in place; each (KV head, group of 64 dims) of the
+// row's k (rotated) and v is rounded to bf16 and quantized by one wave (lane = dim), as the
+// quantizing append does.
+__global__ __launch_bounds__(256) void rope_append_q8_kernel(float* qkv, int ld_qkv, const RowMeta* meta, int n_heads,
+                                                             int n_kv_heads, int head_dim, int layer, uint8_t* arena,
+                                                             const float2* rope_cs) {
+  const int r = blockIdx.x;
+  const RowMeta m = meta[r];
+  const int half = head_dim >> 1;
+  const float2* cs = rope_cs + (int64_t)m.pos * half;
+  float* q = qkv + (int64_t)r * ld_qkv;
+  const float* k = q + n_heads * head_dim;
+  const float* v = k + n_kv_heads * head_dim;
+  for (int idx = threadIdx.x; idx < n_heads * half; idx += 256) {
+    const int hh = idx / half, i = idx - hh * half;
+    float* x = q + hh * head_dim;
+    const float2 c = cs[i];
+    const float x1 = x[i], x2 = x[i + half];
+    x[i] = x1 * c.x - x2 * c.y;
+    x[i + half] = x2 * c.x + x1 * c.y;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ng = head_dim / kQGroup, units = 2 * n_kv_heads * ng;
+  const int64_t region = (int64_t)(m.stride / 32) * q8_block_bytes(head_dim);
+  uint8_t* slab = arena + m.slab_off;
+  for (int u = wave; u < units; u += 4) {
+    const int kv = u / (n_kv_heads * ng), rem = u - kv * n_kv_heads * ng;
+    const int j = rem / ng, gi = rem - j * ng, d = gi * kQGroup + lane;
+    uint8_t* base = slab + ((int64_t)(layer * 2 + kv) * n_kv_heads + j) * region;
+    float x;
+    if (kv == 0) {
+      const float* kx = k + j * head_dim;
+      const int i = d < half ? d : d - half;
+      const float2 c = cs[i];
+      const float x1 = kx[i], x2 = kx[i + half];
+      x = d < half ? x1 * c.x - x2 * c.y : x2 * c.x + x1 * c.y;
+    } else {
+      x = v[j * head_dim + d];
+    }
+    x = bf16_to_f32(f32_to_bf16(x));
+    const float lo = -wave_max(-x), sc = q8_scale(lo, wave_max(x));
+    base[kv == 0 ? kq_off(m.pos, d, head_dim) : vq_off(m.pos, d, head_dim)] = (uint8_t)q8_code(x, lo, sc);
+    if (lane == 0) *reinterpret_cast<float2*>(base + sbq_off(m.pos, gi, head_dim)) = float2{sc, lo};
+  }
+}
+
 // Greedy argmax, lowest index on ties. Row r is cut into P segments, one block each: strict >
 // keeps the first maximum a thread sees, and across threads and blocks equal values resolve to
 // the lower index. Each block publishes (max, index) with agent-scope stores; the last block of the
@@ -286,6 +332,14 @@ hipError_t launch_rope_append(float* qkv, int ld_qkv, const RowMeta* meta, int r
                               int head_dim, int layer, uint8_t* arena, const float* rope_cs, hipStream_t st) {
   launch_kernel(rope_append_kernel, dim3(rows), dim3(256), 0, st, qkv, ld_qkv, meta, n_heads, n_kv_heads,
                      head_dim, layer, arena, reinterpret_cast<const float2*>(rope_cs));
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_append_q8(float* qkv, int ld_qkv, const RowMeta* meta, int rows, int n_heads, int n_kv_heads,
+                                 int head_dim, int layer, uint8_t* arena, const float* rope_cs, hipStream_t st) {
+  if (head_dim % kQGroup) return hipErrorInvalidValue;
+  launch_kernel(rope_append_q8_kernel, dim3(rows), dim3(256), 0, st, qkv, ld_qkv, meta, n_heads, n_kv_heads,
+                head_dim, layer, arena, reinterpret_cast<const float2*>(rope_cs));
   return hipGetLastError();
 }
 

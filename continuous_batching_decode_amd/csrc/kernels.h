@@ -112,6 +112,9 @@ hipError_t launch_embed(const int32_t* tokens, int rows, const uint16_t* embed, 
 // RoPE q in place (fp32) and write rotated k, v (bf16) to each row's slab at its position
 hipError_t launch_rope_append(float* qkv, int ld_qkv, const RowMeta* meta, int rows, int n_heads, int n_kv_heads,
                               int head_dim, int layer, uint8_t* arena, const float* rope_cs, hipStream_t st);
+// the same for affine 8-bit slabs (k and v quantized per KV head and group of 64 dims)
+hipError_t launch_rope_append_q8(float* qkv, int ld_qkv, const RowMeta* meta, int rows, int n_heads, int n_kv_heads,
+                                 int head_dim, int layer, uint8_t* arena, const float* rope_cs, hipStream_t st);
 // Attention of each item's query row over its key range of the row's slab.
 struct AttnArgs {
   const float* qkv;          // projections [rows, ld_qkv]: q heads, then k heads, then v heads
@@ -137,6 +140,7 @@ hipError_t launch_prefill_attention(const AttnArgs& a, int n_items, int head_dim
 // decode over affine 8-bit slabs (same items, splits and outputs as launch_decode_attention; the
 // appending item quantizes the new token's K/V into the slab)
 hipError_t launch_decode_attention_q8(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
+hipError_t launch_prefill_attention_q8(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
 
 // greedy argmax per row, lowest id on ties
 // part: kArgmaxSegments x 64 (max, index) pairs; counters: 64 ints, zero between launches

@@ -743,8 +743,9 @@ cbd_status run_layers(cbd_ctx* c, int rows, int x_blocks, const RowMeta* meta_d,
     const bool fused = row_parts_d != nullptr;
     if (!fused) {
       ProfScope p(c, CBD_KERNEL_ROPE_APPEND, (double)rows * (c->qkv_dim * 4.0 + c->q_dim * 4.0 + c->kv_dim * 4.0), 0, st);
-      HIP_TRY(launch_rope_append(c->qkv, c->qkv_dim, meta_d, rows, m.n_heads, m.n_kv_heads, m.head_dim, l, c->arena,
-                                 c->rope_cs, st),
+      HIP_TRY((c->kv8 ? launch_rope_append_q8 : launch_rope_append)(c->qkv, c->qkv_dim, meta_d, rows, m.n_heads,
+                                                                      m.n_kv_heads, m.head_dim, l, c->arena,
+                                                                      c->rope_cs, st),
               "rope/append");
     }
     {
@@ -771,7 +772,8 @@ cbd_status run_layers(cbd_ctx* c, int rows, int x_blocks, const RowMeta* meta_d,
                   kv_keys * m.n_heads * m.head_dim * 4.0, st);
       HIP_TRY(fused ? (c->kv8 ? launch_decode_attention_q8(at, n_items, m.head_dim, st)
                               : launch_decode_attention(at, n_items, m.head_dim, st))
-                    : launch_prefill_attention(at, n_items, m.head_dim, st),
+                    : (c->kv8 ? launch_prefill_attention_q8(at, n_items, m.head_dim, st)
+                              : launch_prefill_attention(at, n_items, m.head_dim, st)),
               "attention");
     }
     a = gemm_args(c, c->xo, c->xo_plane, c->q_dim, rows, {L.wo}, {m.d_model}, m.d_model);
@@ -905,7 +907,6 @@ extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, cons
   if (K == 0) return CBD_OK;
   if (!seq_ids || !seg_lens || !tokens_dev || !last_logits_dev) return fail(CBD_E_INVAL, "prefill_segmented: null pointer");
   if (!aligned16(last_logits_dev)) return fail(CBD_E_INVAL, "prefill_segmented: logits must be 16-byte aligned");
-  if (c->kv8) return fail(CBD_E_UNSUPPORTED, "prefill_segmented: not available for affine 8-bit slabs");
   int64_t T = 0;
   for (int i = 0; i < K; ++i) {
     const Slab* s;

@@ -90,8 +90,9 @@ enum { CBD_WEIGHTS_BF16 = 0, CBD_WEIGHTS_INT4 = 1 };
  *                  bias) / 255, code = (x - bias) / scale rounded half to even and clamped to 0..255
  *                  (decided in float32; code 0 when scale = 0), where x is the element's bf16 value;
  *                  attention reads scale * code + bias. 144 bytes per token, layer and KV head at
- *                  head_dim 128 (bf16: 256). decode_step_batch and kvslab_append support it;
- *                  prefill_segmented and kvslab_read return CBD_E_UNSUPPORTED (kvslab_read_q8 reads
+ *                  head_dim 128 (bf16: 256). decode_step_batch, prefill_segmented (whose tokens
+ *                  attend to the stored, quantized keys of their own segment) and kvslab_append
+ *                  quantize on append; kvslab_read returns CBD_E_UNSUPPORTED (kvslab_read_q8 reads
  *                  the stored form).
  */
 enum { CBD_KV_BF16 = 0, CBD_KV_AFFINE8 = 1 };

@@ -216,7 +216,7 @@ def test_affine8_kv_format_host(cbd):
     lib = cbd.lib()
     ids = (ctypes.c_int32 * 1)(a)
     lens = (ctypes.c_int32 * 1)(4)
-    assert lib.prefill_segmented(e.ctx, ids, lens, 1, 256, 256, None, None) == cbd.CBD_E_UNSUPPORTED
+    assert lib.prefill_segmented(e.ctx, ids, lens, 1, 256, 256, None, None) == cbd.CBD_E_NODEVICE
     assert lib.kvslab_read(e.ctx, a, 0, 0, 256, 256, None) == cbd.CBD_E_UNSUPPORTED
     assert lib.kvslab_read_q8(e.ctx, a, 0, 0, 256, 256, None) == cbd.CBD_OK
     assert lib.kvslab_read_q8(e.ctx, a, 0, 1, 256, 256, None) == cbd.CBD_E_CAPACITY

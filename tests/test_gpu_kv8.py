@@ -170,3 +170,54 @@ def test_kv8_long_context_sampled_rows(torch, cbd):
     torch.cuda.synchronize()
     assert_logits_close(logits.cpu().numpy(), ref, "kv8 long")
     eng.close()
+
+
+@pytest.mark.parametrize("shape", [MID, synth.TINY], ids=["dh128-g4", "dh64-g2"])
+def test_kv8_prefill_continuation_and_decode(torch, cbd, shape):
+    """Segmented prefill into affine 8-bit slabs (mixed lengths, one segment continuing its sequence in a
+    second call after decode steps), every call's logits and the stored K/V against the oracle."""
+    from oracle import OracleModel, dequantize_affine8, greedy
+    _say("kv8 prefill", shape.name)
+    w = synth.make_weights(shape, seed=7, gain_std=0.1)
+    lens = [1, 31, 32, 33, 100, 115]
+    prompts = synth.prompts(23, lens + [45], shape.vocab)
+    eng = _engine(cbd, w, shape, 16 * 256, max_batch=8, max_prefill_tokens=512, max_position=1024)
+    orc = OracleModel(w, cache_all_layers=True, kv_format="affine8")
+    ids = [eng.alloc(256) for _ in lens]
+    oids = [orc.new_sequence() for _ in lens]
+
+    def prefill(rows, segs, what):
+        toks = torch.from_numpy(np.concatenate(segs).astype(np.int32)).cuda()
+        lg = torch.empty((len(rows), shape.vocab), dtype=torch.float32, device="cuda")
+        nx = torch.empty(len(rows), dtype=torch.int32, device="cuda")
+        eng.prefill_segmented([ids[r] for r in rows], [len(x) for x in segs], toks, lg, nx)
+        ref = orc.prefill_segmented([oids[r] for r in rows], segs)
+        torch.cuda.synchronize()
+        errs = assert_logits_close(lg.cpu().numpy(), ref, what)
+        check_greedy(nx.cpu().numpy(), ref, errs, what)
+        return greedy(ref)
+
+    rows = list(range(len(lens)))
+    tok = prefill(rows, prompts[:len(lens)], "prefill")
+    lg = torch.empty((len(rows), shape.vocab), dtype=torch.float32, device="cuda")
+    for step in range(2):
+        eng.decode_step_batch([ids[r] for r in rows], torch.from_numpy(tok.astype(np.int32)).cuda(), lg)
+        ref = orc.decode_step_batch([oids[r] for r in rows], tok)
+        torch.cuda.synchronize()
+        assert_logits_close(lg.cpu().numpy(), ref, "decode %d" % step)
+        tok = greedy(ref)
+    prefill([4], [prompts[-1]], "continuation")  # 100 + 2 decoded + 45 more prompt tokens
+    for r in rows:
+        n = orc.seqs[oids[r]].length
+        assert eng.length(ids[r]) == n
+        codes, sb = eng.kvslab_read_q8(ids[r], 0, n)
+        torch.cuda.synchronize()
+        codes, sb = codes.cpu().numpy(), sb.cpu().numpy()
+        s = orc.seqs[oids[r]]
+        for which, oc, osb in ((0, s.k, s.k_sb), (1, s.v, s.v_sb)):
+            got = dequantize_affine8(codes[:, :, which], sb[:, :, which])
+            want = dequantize_affine8(np.stack(oc), np.stack(osb))
+            for l in range(shape.n_layers):
+                err = np.max(np.abs(got[l] - want[l]))
+                assert err <= LOGIT_RTOL * np.max(np.abs(want[l])), "row %d layer %d kv %d: %.4g" % (r, l, which, err)
+    eng.close()
