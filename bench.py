@@ -78,26 +78,35 @@ def log(*a):
 T0 = time.time()
 
 
-def source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+# per workload: the committed counter summary of its roofline kernel and that kernel's source file
+COMMITTED = {
+    "llama8b-b8": (TRAFFIC_FILE, KERNEL_SRC),
+    "llama8b-long-kv8": (os.path.join(ROOT, "profiles", "traffic_attention_q8_llama8b_long.md"),
+                         os.path.join(ROOT, "continuous_batching_decode_amd", "csrc", "attention.hip")),
+}
 
 
-def committed_profile(field):
-    """A figure of the dominant kernel from the committed profile summary (HBM bytes per launch from
-    the counters, or its average duration in the kernel trace), or None when absent or taken on a
-    different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def source_hash(path=KERNEL_SRC) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def committed_profile(field, workload="llama8b-b8"):
+    """A figure of the workload's roofline kernel from its committed profile summary (HBM bytes per
+    launch from the counters, or its average duration in the kernel trace), or None when absent or
+    taken on a different kernel source."""
+    if workload not in COMMITTED or not os.path.exists(COMMITTED[workload][0]):
         return None
-    text = open(TRAFFIC_FILE).read()
+    summary, src = COMMITTED[workload]
+    text = open(summary).read()
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(field + r":\s*([0-9.eE+]+)", text)
-    if not h or not t or h.group(1) != source_hash():
+    if not h or not t or h.group(1) != source_hash(src):
         return None
     return float(t.group(1))
 
 
-def committed_traffic():
-    return committed_profile("traffic_bytes_per_launch")
+def committed_traffic(workload="llama8b-b8"):
+    return committed_profile("traffic_bytes_per_launch", workload)
 
 
 def main():
@@ -259,13 +268,14 @@ def main():
     }[rk]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": committed_traffic() if args.workload == "llama8b-b8" else None,
+                "traffic": committed_traffic(args.workload),
                 "kernel": kernel_desc, "bytes_per_launch": per_launch_bytes, "avg_launch_us": round(avg_ms * 1e3, 2),
-                "launches": gu["launches"], "kernel_source_sha256_16": source_hash()}
-    if args.workload == "llama8b-b8":
+                "launches": gu["launches"],
+                "kernel_source_sha256_16": source_hash(COMMITTED.get(args.workload, (None, KERNEL_SRC))[1])}
+    if args.workload in COMMITTED:
         # the same kernel's average in the committed rocprofv3 trace of this command: the live events
         # run a few microseconds longer on the launches they bracket (their completion signalling)
-        tr = committed_profile("kernel_trace_avg_us")
+        tr = committed_profile("kernel_trace_avg_us", args.workload)
         if tr:
             roofline["trace_avg_launch_us"] = tr
             roofline["frac_at_trace_avg"] = round(per_launch_bytes / (tr * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
