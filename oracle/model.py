@@ -206,6 +206,24 @@ class OracleModel:
     def free_sequence(self, sid: int) -> None:
         del self.seqs[sid]
 
+    def fork(self, parent: int, prefix_len: int) -> int:
+        """A new sequence whose first prefix_len positions hold the parent's K/V (mlx-bun "Batching"
+        design note, section 6 "KV memory model", item 3: block-level copy-on-write sharing of a prefix).
+        Earlier positions never change once written (a slab only grows), so sharing them and copying
+        them give the same values; the new sequence continues from position prefix_len."""
+        p = self.seqs[parent]
+        if not 0 <= prefix_len <= p.length:
+            raise ValueError("prefix of %d tokens outside the parent's %d" % (prefix_len, p.length))
+        sid = self.new_sequence()
+        s = self.seqs[sid]
+        for l in range(self.cfg.n_layers):
+            s.k[l] = p.k[l][:prefix_len].copy()
+            s.v[l] = p.v[l][:prefix_len].copy()
+            if s.k_sb is not None:
+                s.k_sb[l] = p.k_sb[l][:prefix_len].copy()
+                s.v_sb[l] = p.v_sb[l][:prefix_len].copy()
+        return sid
+
     def append_history(self, sid: int, k_bits, v_bits) -> None:
         """Append given K/V (bf16 bits, [L, n, Hkv, Dh]) to a slab."""
         for l in range(self.cfg.n_layers):

@@ -215,6 +215,38 @@ def test_oracle_matches_scalar_brute_force_kv8():
     _run_trajectory(w, pr, steps=3, kv_group=2, rtol=1e-9)
 
 
+# --------------------------------------------------------------------------- shared prefixes
+
+@pytest.mark.parametrize("kv_format", ["bf16", "affine8"])
+def test_fork_equals_whole_prompt(kv_format):
+    """A sequence forked from a parent's first P tokens, then given the rest of its prompt and decoded,
+    gives exactly what a sequence that prefilled the whole prompt gives (causal attention: the prefix
+    positions never see the tokens after them), and leaves the parent untouched."""
+    w = synth.make_weights(synth.TINY, seed=3, gain_std=0.1)
+    shared, tail_a, tail_b = synth.prompts(51, [37, 11, 5], synth.TINY.vocab)
+    for P in (37, 32, 20):
+        orc = OracleModel(w, cache_all_layers=True, kv_format=kv_format)
+        par = orc.new_sequence()
+        orc.prefill(par, shared)
+        snap = orc.copy_state()[par]
+        kid = orc.fork(par, P)
+        lg_fork = orc.prefill(kid, np.concatenate([shared[P:], tail_a]))
+        whole = orc.new_sequence()
+        lg_whole = orc.prefill(whole, np.concatenate([shared, tail_a]))
+        assert np.allclose(lg_fork, lg_whole, rtol=1e-12, atol=1e-12)
+        nxt = greedy(lg_whole[None])
+        both = orc.decode_step_batch([kid, whole], [nxt[0], nxt[0]])
+        assert np.allclose(both[0], both[1], rtol=1e-12, atol=1e-12)
+        for l in range(w["shape"].n_layers):
+            assert np.array_equal(orc.seqs[par].k[l], snap.k[l])
+        # a second fork of the same parent decodes independently of the first
+        kid2 = orc.fork(par, P)
+        lg2 = orc.prefill(kid2, np.concatenate([shared[P:], tail_b]))
+        ref = OracleModel(w, cache_all_layers=True, kv_format=kv_format)
+        r = ref.new_sequence()
+        assert np.allclose(lg2, ref.prefill(r, np.concatenate([shared, tail_b])), rtol=1e-12, atol=1e-12)
+
+
 # --------------------------------------------------------------------------- affine 8-bit K/V
 
 def _bf16_bits_of(values):
