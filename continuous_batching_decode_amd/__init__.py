@@ -28,7 +28,7 @@ KV_FORMATS = {"bf16": KV_BF16, "affine8": KV_AFFINE8}
 EXPORTS = ["cbd_kv_bytes_per_token", "cbd_slab_granule_tokens", "cbd_create", "cbd_destroy", "cbd_last_error",
            "cbd_stats", "kvslab_alloc", "kvslab_free", "kvslab_len", "kvslab_capacity", "kvslab_append",
            "kvslab_read", "decode_step_batch", "prefill_segmented", "greedy_argmax", "cbd_linear", "cbd_pack_int4",
-           "cbd_profile_begin", "cbd_profile_end", "cbd_pack_bf16", "sample_top_p", "kvslab_read_q8"]
+           "cbd_profile_begin", "cbd_profile_end", "cbd_pack_bf16", "sample_top_p", "kvslab_read_q8", "kvslab_fork"]
 
 KERNEL_KINDS = ["embed", "norm", "qkv", "rope_append", "attention", "attn_combine", "o_proj", "gate_up", "down",
                 "lm_head", "argmax", "sample"]
@@ -98,6 +98,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvslab_append": (i32, [ctx_p, i32, i32, vp, vp, vp]),
         "kvslab_read": (i32, [ctx_p, i32, i32, i32, vp, vp, vp]),
         "kvslab_read_q8": (i32, [ctx_p, i32, i32, i32, vp, vp, vp]),
+        "kvslab_fork": (i32, [ctx_p, i32, i32, i32, P(i32), vp]),
         "decode_step_batch": (i32, [ctx_p, P(i32), i32, vp, vp, vp, vp]),
         "prefill_segmented": (i32, [ctx_p, P(i32), P(i32), i32, vp, vp, vp, vp]),
         "greedy_argmax": (i32, [ctx_p, vp, i32, vp, vp]),
@@ -272,6 +273,14 @@ class Engine:
     def capacity(self, seq_id: int) -> int:
         out = ctypes.c_int32()
         _check(self.lib.kvslab_capacity(self.ctx, int(seq_id), ctypes.byref(out)))
+        return out.value
+
+    def fork(self, parent: int, prefix_len: int, capacity_tokens: int, stream=None) -> int:
+        """A new sequence that shares the parent's first prefix_len positions."""
+        out = ctypes.c_int32()
+        st = None if self.arena is None else _stream_ptr(stream)  # a host-only context copies nothing
+        _check(self.lib.kvslab_fork(self.ctx, int(parent), int(prefix_len), int(capacity_tokens), ctypes.byref(out),
+                                    st))
         return out.value
 
     def append(self, seq_id: int, k_dev, v_dev, stream=None) -> None:

@@ -289,6 +289,10 @@ CBD_DEVICE AttnItem uniform_item(const AttnItem* items, int i) {
   it.k_begin = __builtin_amdgcn_readfirstlane(it.k_begin);
   it.k_end = __builtin_amdgcn_readfirstlane(it.k_end);
   it.part = __builtin_amdgcn_readfirstlane(it.part);
+  it.pre_off = ((int64_t)__builtin_amdgcn_readfirstlane((int32_t)(it.pre_off >> 32)) << 32) |
+               (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)it.pre_off);
+  it.pre_stride = __builtin_amdgcn_readfirstlane(it.pre_stride);
+  it.pre_end = __builtin_amdgcn_readfirstlane(it.pre_end);
   return it;
 }
 
@@ -976,8 +980,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(AttnArgs a, i
   const uint16_t* slab = reinterpret_cast<const uint16_t*>(a.arena + it.slab_off);
   const KVStream<DH> kv{slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * region,
                         slab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * region, lane};
+  // a forked sequence: blocks [0, pb) from the parent's slab, the rest from its own
+  const int pb = it.pre_end >> 5;
+  const int64_t pregion = (int64_t)it.pre_stride * DH;
+  const uint16_t* pslab = reinterpret_cast<const uint16_t*>(a.arena + it.pre_off);
+  const KVStream<DH> kp{pslab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * pregion,
+                        pslab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * pregion, lane};
   u32x4_t K0[2 * NU], V0[NT];
-  kv.load_k(K0, 0);
+  if (pb > 0) kp.load_k(K0, 0);
+  else kv.load_k(K0, 0);
   // Q^T operand: column c16 = query pos + c16 (zero past the tile), already rotated
   bf16x8_t qh[NU], ql[NU];
   {
@@ -992,12 +1003,19 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(AttnArgs a, i
       split8(qv, qh[u], ql[u]);
     }
   }
-  kv.load_v(V0, 0);
+  if (pb > 0) kp.load_v(V0, 0);
+  else kv.load_v(V0, 0);
   Online<DH> st;
   st.clear();
   // causal: column c16 sees keys 0 .. pos + c16 of its own segment (columns past the tile see none)
   const int lim = c16 < n_q ? it.pos + c16 + 1 : 0;
-  stream_blocks<DH>(kv, K0, V0, 0, (it.k_end + 31) >> 5, g, lim, 1.0f / sqrtf((float)DH), qh, ql, st);
+  const float scale = 1.0f / sqrtf((float)DH);
+  if (pb > 0) {
+    stream_blocks<DH>(kp, K0, V0, 0, pb, g, lim, scale, qh, ql, st);
+    kv.load_k(K0, pb);
+    kv.load_v(V0, pb);
+  }
+  stream_blocks<DH>(kv, K0, V0, pb, (it.k_end + 31) >> 5, g, lim, scale, qh, ql, st);
   if (c16 < n_q) store_out<DH>(a, it.row + c16, h, g, st.o, 1.0f / st.l);
 }
 
@@ -1020,10 +1038,16 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_q8_kernel(AttnArgs a
   const uint8_t* slab = a.arena + it.slab_off;
   const Q8Stream<DH> kv(slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * region,
                         slab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * region, lane);
+  // a forked sequence: blocks [0, pb) from the parent's slab, the rest from its own
+  const int pb = it.pre_end >> 5;
+  const int64_t pregion = (int64_t)(it.pre_stride / 32) * q8_block_bytes(DH);
+  const uint8_t* pslab = a.arena + it.pre_off;
+  const Q8Stream<DH> kp(pslab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * pregion,
+                        pslab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * pregion, lane);
   Q8Codes<DH> K0, V0;
   u32x4_t R0;
-  kv.load_r(R0, 0);
-  kv.load_k(K0, 0);
+  (pb > 0 ? kp : kv).load_r(R0, 0);
+  (pb > 0 ? kp : kv).load_k(K0, 0);
   bf16x8_t qh[NU], ql[NU];
   float qs[NG];
 #pragma unroll
@@ -1047,7 +1071,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_q8_kernel(AttnArgs a
     qs[gi] += __shfl_xor(qs[gi], 16, 64);
     qs[gi] += __shfl_xor(qs[gi], 32, 64);
   }
-  kv.load_v(V0, 0);
+  (pb > 0 ? kp : kv).load_v(V0, 0);
   Online<DH> st;
   st.clear();
   float bacc[NG];
@@ -1056,14 +1080,16 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_q8_kernel(AttnArgs a
   const int lim = c16 < n_q ? it.pos + c16 + 1 : 0;
   const int b_end = (it.k_end + 31) >> 5;
   for (int b = 0; b < b_end; ++b) {
+    const int nb = min(b + 1, b_end - 1);
+    const Q8Stream<DH>& nx = nb < pb ? kp : kv;  // the slab that holds the next block
     slot[lane] = __builtin_bit_cast(f32x4_t, R0);
-    kv.load_r(R0, min(b + 1, b_end - 1));
+    nx.load_r(R0, nb);
     float sv[1][8], p[1][8];
     q8_scores<DH>(K0, slot, g, qh, ql, qs, sv[0]);
-    kv.load_k(K0, min(b + 1, b_end - 1));
+    nx.load_k(K0, nb);
     q8_softmax<DH, 1>(sv, p, b, g, lim, 1.0f / sqrtf((float)DH), st, bacc);
     q8_block_pv<DH>(V0, slot, g, p[0], st, bacc);
-    kv.load_v(V0, min(b + 1, b_end - 1));
+    nx.load_v(V0, nb);
   }
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {

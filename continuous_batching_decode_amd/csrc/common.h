@@ -111,7 +111,7 @@ CBD_DEVICE int64_t vslab_off(int key, int d, int dh) {
 //  records: key kk of the V order (vslab_kk) at byte 32 * Dh + kk * (Dh/64) * 8, group after group.
 //     Lane group g = l/16 owns keys kk = 8g .. 8g + 7: exactly the keys whose scores it holds.
 constexpr int kQGroup = 64;
-CBD_DEVICE constexpr int q8_block_bytes(int dh) { return 32 * dh + 32 * (dh / kQGroup) * 8; }
+__host__ __device__ constexpr int q8_block_bytes(int dh) { return 32 * dh + 32 * (dh / kQGroup) * 8; }
 CBD_DEVICE int64_t kq_off(int key, int d, int dh) {
   const int f = ((key >> 4) & 1) * (dh >> 5) + (d >> 5);
   const int lane = (((d & 31) >> 3) << 4) + (key & 15);
@@ -136,10 +136,17 @@ CBD_DEVICE uint32_t q8_code(float x, float lo, float s) {
 }
 
 // Per-query-row metadata shared by the RoPE/append and attention kernels.
+// A sequence forked from another one's first positions reads keys [0, pre_end) (whole blocks of 32)
+// from the parent's slab (pre_off, pre_stride) and keeps the rest in its own: its slab_off is then
+// shifted back by pre_end / 32 blocks, so that key k of its own part sits where the layout functions
+// put key k (k >= pre_end only).
 struct RowMeta {
-  int64_t slab_off;  // byte offset of the row's slab in the arena
+  int64_t slab_off;  // byte offset of the row's slab in the arena (shifted as above for a fork)
   int32_t stride;    // tokens per K or V region of the slab (granule-rounded capacity)
   int32_t pos;       // position of this query token (t_s for decode, p for prefill)
+  int64_t pre_off;   // the parent's slab (pre_end > 0 only)
+  int32_t pre_stride;
+  int32_t pre_end;   // keys below it live in the parent's slab (a multiple of 32; 0 = none)
 };
 
 // One attention work item: query row `row` (at position pos of the slab at slab_off) over keys
@@ -153,4 +160,9 @@ struct AttnItem {
   int32_t k_begin;
   int32_t k_end;
   int32_t part;  // partial-result slot, or -1 when the item covers all keys [0, pos]
+  // prefill only: keys [0, pre_end) come from the parent's slab (decode items never straddle pre_end:
+  // their slab fields already name the slab that holds their range)
+  int64_t pre_off;
+  int32_t pre_stride;
+  int32_t pre_end;
 };

@@ -250,13 +250,14 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int vo
 
 // canonical [L, n, Hkv, Dh] <-> slab [L][2][Hkv][cap][Dh] at positions [pos, pos+n); 16-byte moves
 __global__ __launch_bounds__(256) void slab_copy_kernel(uint8_t* arena, int64_t slab_off, int stride, int pos,
-                                                        int n, int n_kv_heads, int head_dim, const uint16_t* k_in,
+                                                        int n_all, int t_off, int n_kv_heads, int head_dim,
+                                                        const uint16_t* k_in,
                                                         const uint16_t* v_in, uint16_t* k_out, uint16_t* v_out) {
   const int t = blockIdx.x, l = blockIdx.y, kv = blockIdx.z;
   const int chunks = n_kv_heads * head_dim / 8;
   uint16_t* slab = reinterpret_cast<uint16_t*>(arena + slab_off);
   const int64_t region = (int64_t)stride * head_dim;
-  const int64_t canon = ((int64_t)l * n + t) * n_kv_heads * head_dim;
+  const int64_t canon = ((int64_t)l * n_all + t_off + t) * n_kv_heads * head_dim;
   const int key = pos + t;
   for (int c = threadIdx.x; c < chunks; c += 256) {
     const int j = (c * 8) / head_dim, i = (c * 8) - j * head_dim;
@@ -280,8 +281,8 @@ __global__ __launch_bounds__(256) void slab_copy_kernel(uint8_t* arena, int64_t 
 }
 
 // Affine 8-bit slabs: one wave per (token, layer, K or V, KV head, group of 64 dims), lane = dim.
-__global__ __launch_bounds__(256) void slab_q8_kernel(uint8_t* arena, int64_t slab_off, int stride, int pos, int n,
-                                                      int n_kv_heads, int head_dim, const uint16_t* k_in,
+__global__ __launch_bounds__(256) void slab_q8_kernel(uint8_t* arena, int64_t slab_off, int stride, int pos, int n_all,
+                                                      int t_off, int n_kv_heads, int head_dim, const uint16_t* k_in,
                                                       const uint16_t* v_in, uint8_t* codes_out, float* sb_out) {
   const int t = blockIdx.x, l = blockIdx.y, kv = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -295,12 +296,12 @@ __global__ __launch_bounds__(256) void slab_q8_kernel(uint8_t* arena, int64_t sl
     float2* sbp = reinterpret_cast<float2*>(base + sbq_off(key, gi, head_dim));
     if (k_in) {
       const uint16_t* in = kv == 0 ? k_in : v_in;
-      const float x = bf16_to_f32(in[(((int64_t)l * n + t) * n_kv_heads + j) * head_dim + d]);
+      const float x = bf16_to_f32(in[(((int64_t)l * n_all + t_off + t) * n_kv_heads + j) * head_dim + d]);
       const float lo = -wave_max(-x), s = q8_scale(lo, wave_max(x));
       *cp = (uint8_t)q8_code(x, lo, s);
       if (lane == 0) *sbp = float2{s, lo};
     } else {
-      const int64_t o = (((int64_t)l * n + t) * 2 + kv) * n_kv_heads + j;
+      const int64_t o = (((int64_t)l * n_all + t_off + t) * 2 + kv) * n_kv_heads + j;
       codes_out[o * head_dim + d] = *cp;
       if (lane == 0) reinterpret_cast<float2*>(sb_out)[o * ng + gi] = *sbp;
     }
@@ -354,20 +355,20 @@ hipError_t launch_argmax(const float* logits, int rows, int vocab, float* part, 
   return hipGetLastError();
 }
 
-hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_layers,
-                            int n_kv_heads, int head_dim, const uint16_t* k_in, const uint16_t* v_in, uint16_t* k_out,
-                            uint16_t* v_out, hipStream_t st) {
-  launch_kernel(slab_copy_kernel, dim3(n, n_layers, 2), dim3(256), 0, st, arena, slab_off, stride, pos, n,
-                     n_kv_heads, head_dim, k_in, v_in, k_out, v_out);
+hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_all, int t_off,
+                            int n_layers, int n_kv_heads, int head_dim, const uint16_t* k_in, const uint16_t* v_in,
+                            uint16_t* k_out, uint16_t* v_out, hipStream_t st) {
+  launch_kernel(slab_copy_kernel, dim3(n, n_layers, 2), dim3(256), 0, st, arena, slab_off, stride, pos, n_all, t_off,
+                n_kv_heads, head_dim, k_in, v_in, k_out, v_out);
   return hipGetLastError();
 }
 
-hipError_t launch_slab_q8(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_layers, int n_kv_heads,
-                          int head_dim, const uint16_t* k_in, const uint16_t* v_in, uint8_t* codes_out, float* sb_out,
-                          hipStream_t st) {
+hipError_t launch_slab_q8(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_all, int t_off,
+                          int n_layers, int n_kv_heads, int head_dim, const uint16_t* k_in, const uint16_t* v_in,
+                          uint8_t* codes_out, float* sb_out, hipStream_t st) {
   if (head_dim % kQGroup || stride % 32) return hipErrorInvalidValue;
-  launch_kernel(slab_q8_kernel, dim3(n, n_layers, 2), dim3(256), 0, st, arena, slab_off, stride, pos, n, n_kv_heads,
-                head_dim, k_in, v_in, codes_out, sb_out);
+  launch_kernel(slab_q8_kernel, dim3(n, n_layers, 2), dim3(256), 0, st, arena, slab_off, stride, pos, n_all, t_off,
+                n_kv_heads, head_dim, k_in, v_in, codes_out, sb_out);
   return hipGetLastError();
 }
 

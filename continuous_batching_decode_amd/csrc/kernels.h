@@ -170,14 +170,16 @@ hipError_t launch_sample_top_p(const float* logits, int rows, int vocab, const S
                                int32_t* out, hipStream_t st);
 hipError_t launch_argmax(const float* logits, int rows, int vocab, float* part, int32_t* counters, int32_t* out,
                          hipStream_t st);
-// scatter canonical K/V [L, n, Hkv, Dh] into a slab at [pos, pos+n), or gather back
-hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_layers, int n_kv_heads,
-                            int head_dim, const uint16_t* k_in, const uint16_t* v_in, uint16_t* k_out,
-                            uint16_t* v_out, hipStream_t st);
-// affine 8-bit slabs: quantize canonical bf16 K/V [L, n, Hkv, Dh] into [pos, pos+n) (k_in, v_in), or
-// gather codes [L, n, 2, Hkv, Dh] and (scale, bias) pairs [L, n, 2, Hkv, Dh/64, 2] back (codes_out, sb_out)
-hipError_t launch_slab_q8(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_layers, int n_kv_heads,
-                          int head_dim, const uint16_t* k_in, const uint16_t* v_in, uint8_t* codes_out, float* sb_out,
-                          hipStream_t st);
+// scatter canonical K/V [L, n_all, Hkv, Dh] tokens [t_off, t_off + n) into a slab at [pos, pos+n), or
+// gather them back
+hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_all, int t_off,
+                            int n_layers, int n_kv_heads, int head_dim, const uint16_t* k_in, const uint16_t* v_in,
+                            uint16_t* k_out, uint16_t* v_out, hipStream_t st);
+// affine 8-bit slabs: quantize canonical bf16 K/V [L, n_all, Hkv, Dh] tokens [t_off, t_off + n) into
+// [pos, pos+n) (k_in, v_in), or gather codes [L, n_all, 2, Hkv, Dh] and (scale, bias) pairs
+// [L, n_all, 2, Hkv, Dh/64, 2] back (codes_out, sb_out)
+hipError_t launch_slab_q8(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_all, int t_off,
+                          int n_layers, int n_kv_heads, int head_dim, const uint16_t* k_in, const uint16_t* v_in,
+                          uint8_t* codes_out, float* sb_out, hipStream_t st);
 
 }  // namespace cbd

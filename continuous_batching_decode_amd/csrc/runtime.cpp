@@ -73,6 +73,12 @@ struct Slab {
   int32_t len = 0;
   int64_t gran_begin = 0, gran_count = 0;
   bool live = false;
+  // shared prefix: keys [0, base) are read from slab `parent` (base a multiple of 32); a slab with
+  // live forks that is freed stays allocated (zombie) until its last fork is freed
+  int32_t base = 0;
+  int32_t parent = -1;
+  int32_t children = 0;
+  bool zombie = false;
 };
 
 template <class T>
@@ -224,13 +230,19 @@ int plan_decode_items(const cbd_ctx* c, const std::vector<RowMeta>& rows, AttnIt
   for (const RowMeta& r : rows) total += r.pos + 1;
   const int64_t per_wave = (total * c->cfg.n_kv_heads + kDecodeWaves - 1) / kDecodeWaves;
   int64_t longest = 0;
-  for (const RowMeta& r : rows) longest = std::max<int64_t>(longest, r.pos + 1);
-  // at most kMaxSplits splits per row: the merge reads one (max, sum) pair per lane
-  int64_t chunk = std::max({kMinChunk, round_up(per_wave, 32), round_up((longest + kMaxSplits - 1) / kMaxSplits, 32)});
+  bool forked = false;
+  for (const RowMeta& r : rows) {
+    longest = std::max<int64_t>(longest, r.pos + 1);
+    forked |= r.pre_end > 0;
+  }
+  // at most kMaxSplits splits per row: the merge reads one (max, sum) pair per lane (a fork's range
+  // is cut at its prefix boundary too, which can add one split)
+  const int64_t max_splits = forked ? kMaxSplits - 1 : kMaxSplits;
+  int64_t chunk = std::max({kMinChunk, round_up(per_wave, 32), round_up((longest + max_splits - 1) / max_splits, 32)});
   for (;;) {
     int64_t slots = 0;
     for (const RowMeta& r : rows) {
-      const int64_t s = (r.pos + 1 + chunk - 1) / chunk;
+      const int64_t s = (r.pre_end + chunk - 1) / chunk + (r.pos + 1 - r.pre_end + chunk - 1) / chunk;
       if (s > 1) slots += s;
     }
     if (slots <= kMaxParts) break;
@@ -238,18 +250,26 @@ int plan_decode_items(const cbd_ctx* c, const std::vector<RowMeta>& rows, AttnIt
   }
   int n = 0, slot = 0;
   for (size_t i = 0; i < rows.size(); ++i) {
-    const int nk = rows[i].pos + 1;
-    const int splits = (int)((nk + chunk - 1) / chunk);
+    const RowMeta& r = rows[i];
+    const int nk = r.pos + 1;
+    // a fork's keys below pre_end are items over the parent's slab, the rest over its own
+    const int pre = r.pre_end;
+    const int pre_splits = (int)((pre + chunk - 1) / chunk);
+    const int splits = pre_splits + (int)((nk - pre + chunk - 1) / chunk);
     if (splits <= 1) {
-      items[n++] = AttnItem{rows[i].slab_off, rows[i].stride, rows[i].pos, (int32_t)i, 0, nk, -1};
+      items[n++] = AttnItem{r.slab_off, r.stride, r.pos, (int32_t)i, 0, nk, -1, 0, 0, 0};
       row_parts[2 * i] = 0;
       row_parts[2 * i + 1] = 0;
     } else {
       row_parts[2 * i] = slot;
       row_parts[2 * i + 1] = splits;
-      for (int s = 0; s < splits; ++s) {
-        const int b = (int)(s * chunk), e = (int)std::min<int64_t>(nk, (s + 1) * chunk);
-        items[n++] = AttnItem{rows[i].slab_off, rows[i].stride, rows[i].pos, (int32_t)i, b, e, slot++};
+      for (int s = 0; s < pre_splits; ++s) {
+        const int b = (int)(s * chunk), e = (int)std::min<int64_t>(pre, (s + 1) * chunk);
+        items[n++] = AttnItem{r.pre_off, r.pre_stride, r.pos, (int32_t)i, b, e, slot++, 0, 0, 0};
+      }
+      for (int s = 0; s < splits - pre_splits; ++s) {
+        const int b = pre + (int)(s * chunk), e = (int)std::min<int64_t>(nk, pre + (s + 1) * chunk);
+        items[n++] = AttnItem{r.slab_off, r.stride, r.pos, (int32_t)i, b, e, slot++, 0, 0, 0};
       }
     }
   }
@@ -509,46 +529,25 @@ static cbd_status live_slab(const cbd_ctx* c, int32_t id, const Slab** out) {
   return CBD_OK;
 }
 
-extern "C" cbd_status kvslab_alloc(cbd_ctx* c, int32_t capacity_tokens, int32_t* seq_id_out) {
-  if (!c || !seq_id_out) return fail(CBD_E_INVAL, "kvslab_alloc: null argument");
-  if (capacity_tokens < 1) return fail(CBD_E_INVAL, "kvslab_alloc: capacity must be >= 1");
-  if (capacity_tokens > c->cfg.max_position)
-    return fail(CBD_E_CAPACITY, "kvslab_alloc: capacity %d exceeds max_position %d", capacity_tokens,
-                c->cfg.max_position);
-  const int64_t need = (capacity_tokens + kGranuleTokens - 1) / kGranuleTokens;
+// Take a first-fit run of `need` granules (CBD_E_NOSPACE when none is free).
+static cbd_status take_granules(cbd_ctx* c, int64_t need, int64_t* first_out, const char* who) {
   if (need > c->n_granules)
-    return fail(CBD_E_CAPACITY, "kvslab_alloc: %lld granules exceed the whole arena (%lld)", (long long)need,
+    return fail(CBD_E_CAPACITY, "%s: %lld granules exceed the whole arena (%lld)", who, (long long)need,
                 (long long)c->n_granules);
   auto it = c->free_runs.begin();
   for (; it != c->free_runs.end(); ++it)
     if (it->second >= need) break;
-  if (it == c->free_runs.end()) return fail(CBD_E_NOSPACE, "kvslab_alloc: no free run of %lld granules", (long long)need);
+  if (it == c->free_runs.end()) return fail(CBD_E_NOSPACE, "%s: no free run of %lld granules", who, (long long)need);
   const int64_t first = it->first, run = it->second;
   c->free_runs.erase(it);
   if (run > need) c->free_runs[first + need] = run - need;
-  int32_t id = 0;
-  while ((size_t)id < c->slabs.size() && c->slabs[id].live) ++id;
-  if ((size_t)id == c->slabs.size()) c->slabs.emplace_back();
-  Slab& s = c->slabs[id];
-  s.live = true;
-  s.len = 0;
-  s.cap = (int32_t)std::min<int64_t>(need * kGranuleTokens, c->cfg.max_position);
-  s.stride = (int32_t)(need * kGranuleTokens);
-  s.gran_begin = first;
-  s.gran_count = need;
-  s.off = first * c->granule_bytes;
-  c->stats.live_seqs += 1;
   c->stats.arena_bytes_used += need * c->granule_bytes;
-  *seq_id_out = id;
+  *first_out = first;
   return CBD_OK;
 }
 
-extern "C" cbd_status kvslab_free(cbd_ctx* c, int32_t seq_id) {
-  if (!c) return fail(CBD_E_INVAL, "kvslab_free: null context");
-  const Slab* sp;
-  if (cbd_status st = live_slab(c, seq_id, &sp)) return st;
-  Slab& s = c->slabs[seq_id];
-  int64_t first = s.gran_begin, count = s.gran_count;
+static void give_granules(cbd_ctx* c, int64_t first, int64_t count) {
+  c->stats.arena_bytes_used -= count * c->granule_bytes;
   auto next = c->free_runs.lower_bound(first);
   if (next != c->free_runs.end() && next->first == first + count) {
     count += next->second;
@@ -564,9 +563,116 @@ extern "C" cbd_status kvslab_free(cbd_ctx* c, int32_t seq_id) {
     }
   }
   c->free_runs[first] = count;
-  c->stats.live_seqs -= 1;
-  c->stats.arena_bytes_used -= s.gran_count * c->granule_bytes;
+}
+
+// A new live slab record over granules [first, first + need), its own keys starting at base.
+static int32_t new_slab(cbd_ctx* c, int64_t first, int64_t need, int32_t base) {
+  int32_t id = 0;
+  while ((size_t)id < c->slabs.size() && (c->slabs[id].live || c->slabs[id].zombie)) ++id;
+  if ((size_t)id == c->slabs.size()) c->slabs.emplace_back();
+  Slab& s = c->slabs[id];
   s = Slab{};
+  s.live = true;
+  s.base = base;
+  s.cap = (int32_t)std::min<int64_t>(base + need * kGranuleTokens, c->cfg.max_position);
+  s.stride = (int32_t)(need * kGranuleTokens);
+  s.gran_begin = first;
+  s.gran_count = need;
+  s.off = first * c->granule_bytes;
+  c->stats.live_seqs += 1;
+  return id;
+}
+
+extern "C" cbd_status kvslab_alloc(cbd_ctx* c, int32_t capacity_tokens, int32_t* seq_id_out) {
+  if (!c || !seq_id_out) return fail(CBD_E_INVAL, "kvslab_alloc: null argument");
+  if (capacity_tokens < 1) return fail(CBD_E_INVAL, "kvslab_alloc: capacity must be >= 1");
+  if (capacity_tokens > c->cfg.max_position)
+    return fail(CBD_E_CAPACITY, "kvslab_alloc: capacity %d exceeds max_position %d", capacity_tokens,
+                c->cfg.max_position);
+  const int64_t need = (capacity_tokens + kGranuleTokens - 1) / kGranuleTokens;
+  int64_t first;
+  if (cbd_status st = take_granules(c, need, &first, "kvslab_alloc")) return st;
+  *seq_id_out = new_slab(c, first, need, 0);
+  return CBD_OK;
+}
+
+// Bytes of one block of 32 keys in one (layer, K or V, KV head) region, and of a whole region.
+static int64_t kv_block_bytes(const cbd_ctx* c) {
+  return c->kv8 ? q8_block_bytes(c->cfg.head_dim) : (int64_t)32 * c->cfg.head_dim * 2;
+}
+static int64_t kv_region_bytes(const cbd_ctx* c, int32_t stride) { return (int64_t)(stride / 32) * kv_block_bytes(c); }
+
+// The kernels' view of a slab at position pos: own keys addressed from a slab_off shifted back by
+// base / 32 blocks, keys below base in the parent's slab.
+static RowMeta row_meta(const cbd_ctx* c, const Slab& s, int32_t pos) {
+  RowMeta m{s.off - (int64_t)(s.base / 32) * kv_block_bytes(c), s.stride, pos, 0, 0, 0};
+  if (s.parent >= 0) {
+    const Slab& p = c->slabs[s.parent];
+    m.pre_off = p.off;
+    m.pre_stride = p.stride;
+    m.pre_end = s.base;
+  }
+  return m;
+}
+
+extern "C" cbd_status kvslab_fork(cbd_ctx* c, int32_t parent_id, int32_t prefix_len, int32_t capacity_tokens,
+                                  int32_t* seq_id_out, cbd_stream stream) {
+  if (!c || !seq_id_out) return fail(CBD_E_INVAL, "kvslab_fork: null argument");
+  const Slab* pp;
+  if (cbd_status st = live_slab(c, parent_id, &pp)) return st;
+  if (pp->parent >= 0) return fail(CBD_E_INVAL, "kvslab_fork: sequence %d is itself a fork", parent_id);
+  if (prefix_len < 0 || prefix_len > pp->len)
+    return fail(CBD_E_INVAL, "kvslab_fork: prefix %d outside the parent's %d tokens", prefix_len, pp->len);
+  if (capacity_tokens <= prefix_len)
+    return fail(CBD_E_INVAL, "kvslab_fork: capacity %d leaves no room after the prefix %d", capacity_tokens, prefix_len);
+  if (capacity_tokens > c->cfg.max_position)
+    return fail(CBD_E_CAPACITY, "kvslab_fork: capacity %d exceeds max_position %d", capacity_tokens,
+                c->cfg.max_position);
+  const int32_t base = prefix_len / 32 * 32;  // whole blocks stay shared
+  const int64_t need = (capacity_tokens - base + kGranuleTokens - 1) / kGranuleTokens;
+  int64_t first;
+  if (cbd_status st = take_granules(c, need, &first, "kvslab_fork")) return st;
+  const int32_t id = new_slab(c, first, need, base);
+  Slab& s = c->slabs[id];
+  Slab& p = c->slabs[parent_id];
+  s.parent = parent_id;
+  s.len = prefix_len;
+  p.children += 1;
+  if (prefix_len > base && !c->host_only) {
+    // the block holding the prefix's last keys is copied (its later keys are the fork's own)
+    const int64_t bb = kv_block_bytes(c);
+    const int64_t rows = (int64_t)c->cfg.n_layers * 2 * c->cfg.n_kv_heads;
+    HIP_TRY(hipMemcpy2DAsync(c->arena + s.off, (size_t)kv_region_bytes(c, s.stride),
+                             c->arena + p.off + (int64_t)(base / 32) * bb, (size_t)kv_region_bytes(c, p.stride),
+                             (size_t)bb, (size_t)rows, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)),
+            "kvslab_fork boundary block copy");
+  }
+  *seq_id_out = id;
+  return CBD_OK;
+}
+
+extern "C" cbd_status kvslab_free(cbd_ctx* c, int32_t seq_id) {
+  if (!c) return fail(CBD_E_INVAL, "kvslab_free: null context");
+  const Slab* sp;
+  if (cbd_status st = live_slab(c, seq_id, &sp)) return st;
+  Slab& s = c->slabs[seq_id];
+  c->stats.live_seqs -= 1;
+  if (s.children > 0) {  // forks still read its prefix: keep the granules until the last one goes
+    s.live = false;
+    s.zombie = true;
+    return CBD_OK;
+  }
+  give_granules(c, s.gran_begin, s.gran_count);
+  const int32_t parent = s.parent;
+  s = Slab{};
+  if (parent >= 0) {
+    Slab& p = c->slabs[parent];
+    p.children -= 1;
+    if (p.zombie && p.children == 0) {
+      give_granules(c, p.gran_begin, p.gran_count);
+      p = Slab{};
+    }
+  }
   return CBD_OK;
 }
 
@@ -598,15 +704,16 @@ extern "C" cbd_status kvslab_append(cbd_ctx* c, int32_t seq_id, int32_t n_tokens
   if (!k_dev || !v_dev || !aligned16(k_dev) || !aligned16(v_dev))
     return fail(CBD_E_INVAL, "kvslab_append: K/V must be 16-byte aligned device pointers");
   if (c->host_only) return fail(CBD_E_NODEVICE, "kvslab_append: host-only context");
+  const int64_t off = row_meta(c, *s, s->len).slab_off;  // positions >= len >= base: the own part
   if (c->kv8)
-    HIP_TRY(launch_slab_q8(c->arena, s->off, s->stride, s->len, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
-                           c->cfg.head_dim, static_cast<const uint16_t*>(k_dev), static_cast<const uint16_t*>(v_dev),
-                           nullptr, nullptr, static_cast<hipStream_t>(stream)),
+    HIP_TRY(launch_slab_q8(c->arena, off, s->stride, s->len, n_tokens, n_tokens, 0, c->cfg.n_layers,
+                           c->cfg.n_kv_heads, c->cfg.head_dim, static_cast<const uint16_t*>(k_dev),
+                           static_cast<const uint16_t*>(v_dev), nullptr, nullptr, static_cast<hipStream_t>(stream)),
             "kvslab_append launch");
   else
-    HIP_TRY(launch_slab_copy(c->arena, s->off, s->stride, s->len, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
-                             c->cfg.head_dim, static_cast<const uint16_t*>(k_dev), static_cast<const uint16_t*>(v_dev),
-                             nullptr, nullptr, static_cast<hipStream_t>(stream)),
+    HIP_TRY(launch_slab_copy(c->arena, off, s->stride, s->len, n_tokens, n_tokens, 0, c->cfg.n_layers,
+                             c->cfg.n_kv_heads, c->cfg.head_dim, static_cast<const uint16_t*>(k_dev),
+                             static_cast<const uint16_t*>(v_dev), nullptr, nullptr, static_cast<hipStream_t>(stream)),
             "kvslab_append launch");
   c->slabs[seq_id].len += n_tokens;
   return CBD_OK;
@@ -625,10 +732,19 @@ extern "C" cbd_status kvslab_read(const cbd_ctx* c, int32_t seq_id, int32_t star
   if (!k_out_dev || !v_out_dev || !aligned16(k_out_dev) || !aligned16(v_out_dev))
     return fail(CBD_E_INVAL, "kvslab_read: outputs must be 16-byte aligned device pointers");
   if (c->host_only) return fail(CBD_E_NODEVICE, "kvslab_read: host-only context");
-  HIP_TRY(launch_slab_copy(c->arena, s->off, s->stride, start, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
-                           c->cfg.head_dim, nullptr, nullptr, static_cast<uint16_t*>(k_out_dev),
-                           static_cast<uint16_t*>(v_out_dev), static_cast<hipStream_t>(stream)),
-          "kvslab_read launch");
+  // a fork's positions below its base are read from the parent's slab
+  const RowMeta m = row_meta(c, *s, start);
+  const int32_t end = start + n_tokens, cut = std::min(std::max(start, m.pre_end), end);
+  if (cut > start)
+    HIP_TRY(launch_slab_copy(c->arena, m.pre_off, m.pre_stride, start, cut - start, n_tokens, 0, c->cfg.n_layers,
+                             c->cfg.n_kv_heads, c->cfg.head_dim, nullptr, nullptr, static_cast<uint16_t*>(k_out_dev),
+                             static_cast<uint16_t*>(v_out_dev), static_cast<hipStream_t>(stream)),
+            "kvslab_read launch");
+  if (end > cut)
+    HIP_TRY(launch_slab_copy(c->arena, m.slab_off, s->stride, cut, end - cut, n_tokens, cut - start, c->cfg.n_layers,
+                             c->cfg.n_kv_heads, c->cfg.head_dim, nullptr, nullptr, static_cast<uint16_t*>(k_out_dev),
+                             static_cast<uint16_t*>(v_out_dev), static_cast<hipStream_t>(stream)),
+            "kvslab_read launch");
   return CBD_OK;
 }
 
@@ -645,10 +761,18 @@ extern "C" cbd_status kvslab_read_q8(const cbd_ctx* c, int32_t seq_id, int32_t s
   if (!codes_out_dev || !sb_out_dev || !aligned16(codes_out_dev) || !aligned16(sb_out_dev))
     return fail(CBD_E_INVAL, "kvslab_read_q8: outputs must be 16-byte aligned device pointers");
   if (c->host_only) return fail(CBD_E_NODEVICE, "kvslab_read_q8: host-only context");
-  HIP_TRY(launch_slab_q8(c->arena, s->off, s->stride, start, n_tokens, c->cfg.n_layers, c->cfg.n_kv_heads,
-                         c->cfg.head_dim, nullptr, nullptr, static_cast<uint8_t*>(codes_out_dev),
-                         static_cast<float*>(sb_out_dev), static_cast<hipStream_t>(stream)),
-          "kvslab_read_q8 launch");
+  const RowMeta m = row_meta(c, *s, start);
+  const int32_t end = start + n_tokens, cut = std::min(std::max(start, m.pre_end), end);
+  if (cut > start)
+    HIP_TRY(launch_slab_q8(c->arena, m.pre_off, m.pre_stride, start, cut - start, n_tokens, 0, c->cfg.n_layers,
+                           c->cfg.n_kv_heads, c->cfg.head_dim, nullptr, nullptr, static_cast<uint8_t*>(codes_out_dev),
+                           static_cast<float*>(sb_out_dev), static_cast<hipStream_t>(stream)),
+            "kvslab_read_q8 launch");
+  if (end > cut)
+    HIP_TRY(launch_slab_q8(c->arena, m.slab_off, s->stride, cut, end - cut, n_tokens, cut - start, c->cfg.n_layers,
+                           c->cfg.n_kv_heads, c->cfg.head_dim, nullptr, nullptr, static_cast<uint8_t*>(codes_out_dev),
+                           static_cast<float*>(sb_out_dev), static_cast<hipStream_t>(stream)),
+            "kvslab_read_q8 launch");
   return CBD_OK;
 }
 
@@ -860,7 +984,7 @@ extern "C" cbd_status decode_step_batch(cbd_ctx* c, const int32_t* seq_ids, int3
       return fail(CBD_E_CAPACITY, "decode_step_batch: sequence %d is full (%d tokens)", seq_ids[i], s->cap);
     if (s->len + 1 > c->cfg.max_position)
       return fail(CBD_E_CAPACITY, "decode_step_batch: sequence %d reached max_position", seq_ids[i]);
-    rows[i] = RowMeta{s->off, s->stride, s->len};
+    rows[i] = row_meta(c, *s, s->len);
   }
   if (c->host_only) return fail(CBD_E_NODEVICE, "decode_step_batch: host-only context");
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -940,9 +1064,11 @@ extern "C" cbd_status prefill_segmented(cbd_ctx* c, const int32_t* seq_ids, cons
   for (int i = 0; i < K; ++i) {
     const Slab& s = c->slabs[seq_ids[i]];
     const int t0 = s.len;
-    for (int p = 0; p < seg_lens[i]; ++p) rows[g + p] = RowMeta{s.off, s.stride, t0 + p};
+    for (int p = 0; p < seg_lens[i]; ++p) rows[g + p] = row_meta(c, s, t0 + p);
+    const RowMeta& m = rows[g];
     for (int p0 = 0; p0 < seg_lens[i]; p0 += 16)
-      items[n_items++] = AttnItem{s.off, s.stride, t0 + p0, g + p0, 0, t0 + std::min(p0 + 16, seg_lens[i]), -1};
+      items[n_items++] = AttnItem{m.slab_off, m.stride, t0 + p0, g + p0, 0, t0 + std::min(p0 + 16, seg_lens[i]), -1,
+                                  m.pre_off, m.pre_stride, m.pre_end};
     g += seg_lens[i];
     last_idx[i] = g - 1;
   }

@@ -206,8 +206,25 @@ cbd_status cbd_stats(const cbd_ctx* ctx, cbd_stats_t* out);
  */
 cbd_status kvslab_alloc(cbd_ctx* ctx, int32_t capacity_tokens, int32_t* seq_id_out);
 
-/* Retire a sequence (EOS or length limit): its slab returns to the arena. */
+/* Retire a sequence (EOS or length limit): its slab returns to the arena. A sequence that live forks
+ * still read (kvslab_fork) keeps its memory until the last of them is freed; its id is retired at once. */
 cbd_status kvslab_free(cbd_ctx* ctx, int32_t seq_id);
+
+/*
+ * Start a sequence from the first prefix_len positions of a live sequence (mlx-bun "Batching" design
+ * note, section 6 "KV memory model", item 3: paged K/V with block-level copy-on-write prefix
+ * sharing). The fork's length is prefix_len; its capacity is capacity_tokens (> prefix_len, counting
+ * the prefix). Whole blocks of 32 keys of the prefix are not copied: the fork reads them from the
+ * parent's slab in every later call, so they occupy the arena once however many forks share them.
+ * The block that holds the prefix's last keys, when prefix_len is not a multiple of 32, is copied
+ * into the fork (on `stream`, from the parent's slab as it stands; positions below prefix_len never
+ * change, so the parent may keep decoding). The fork's own part takes ceil((capacity_tokens -
+ * floor(prefix_len / 32) * 32) / granule) granules. The parent must not itself be a fork
+ * (CBD_E_INVAL); CBD_E_NOSPACE / CBD_E_CAPACITY as kvslab_alloc. A host-only context keeps the
+ * bookkeeping and copies nothing.
+ */
+cbd_status kvslab_fork(cbd_ctx* ctx, int32_t parent_seq_id, int32_t prefix_len, int32_t capacity_tokens,
+                       int32_t* seq_id_out, cbd_stream stream);
 
 /* Current length t_s (tokens held) and capacity of a live slab. */
 cbd_status kvslab_len(const cbd_ctx* ctx, int32_t seq_id, int32_t* len_out);

@@ -231,3 +231,35 @@ def test_affine8_kv_format_host(cbd):
     lim = cbd.Limits(8, 64, 8, 1)
     ctx = ctypes.c_void_p()
     assert lib.cbd_create(ctypes.byref(cfg), None, ctypes.byref(lim), None, 1 << 20, ctypes.byref(ctx)) == cbd.CBD_E_INVAL
+
+
+def test_fork_bookkeeping_host(cbd):
+    """kvslab_fork: validation, the fork's own granules, and a freed parent kept until its forks go."""
+    e = make(cbd, granules=8)
+    per_gran = 256 * synth.TINY.kv_bytes_per_token()
+    par = e.alloc(300)  # 2 granules
+    kid = e.fork(par, 0, 600)  # prefix 0: 3 granules of its own
+    assert e.length(kid) == 0 and e.capacity(kid) == 768
+    assert e.stats()["arena_bytes_used"] == 5 * per_gran
+    for args, status in (((par, 1, 100), cbd.CBD_E_INVAL),      # prefix beyond the parent's length
+                         ((par, 0, 0), cbd.CBD_E_INVAL),        # no room after the prefix
+                         ((kid, 0, 100), cbd.CBD_E_INVAL),      # fork of a fork
+                         ((par, 0, 5000), cbd.CBD_E_CAPACITY),  # beyond max_position
+                         ((par, 0, 4 * 256), cbd.CBD_E_NOSPACE),
+                         ((77, 0, 10), cbd.CBD_E_BADSEQ)):
+        with pytest.raises(cbd.CbdError) as ei:
+            e.fork(*args)
+        assert ei.value.status == status, args
+    e.free(par)  # the fork still reads it: id retired, memory kept
+    with pytest.raises(cbd.CbdError) as ei:
+        e.length(par)
+    assert ei.value.status == cbd.CBD_E_BADSEQ
+    st = e.stats()
+    assert st["live_seqs"] == 1 and st["arena_bytes_used"] == 5 * per_gran
+    other = e.alloc(10)
+    assert other not in (par, kid)  # the retired id is not reused while its memory is held
+    e.free(kid)  # the last fork: the parent's granules return too
+    assert e.stats()["arena_bytes_used"] == 1 * per_gran
+    e.free(other)
+    assert e.stats()["arena_bytes_used"] == 0
+    assert e.alloc(8 * 256) == 0  # the whole arena is one free run again
