@@ -127,6 +127,9 @@ def main():
     ap.add_argument("--prefill-chunk", type=int, default=2048,
                     help="continuous workload: prefill tokens per tick (joiner prompts continue over ticks); "
                          "0 = whole prompts per call")
+    ap.add_argument("--share-prefix", type=int, default=1, choices=[0, 1],
+                    help="continuous workload: joiners fork the prompts' common 1024-token prefix from one "
+                         "prefilled holder sequence (kvslab_fork) and prefill only the rest; 0 = whole prompts")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a device buffer of this many MiB 5 times (a plain copy of known size, "
                          "used to calibrate HBM byte counters), then exit")
@@ -526,6 +529,13 @@ def run_continuous(args, wl, torch, cbd, synth):
         arrive -= arrive[0]
         waiting, live = 0, []  # live: [sid, generated, target, context]
         pending = []  # admitted, prompt not yet fully prefilled: [sid, request, tokens done]
+        holder = None
+        if args.share_prefix:
+            # the common prefix, prefilled once; a joiner forks min(L - 1, 1024) of its positions
+            holder = eng.alloc(1025)
+            eng.prefill_segmented([holder], [1024], torch.from_numpy(prompts[int(np.argmax(plens))][:1024]
+                                                                     .astype(np.int32)).to(dev),
+                                  pf_logits[:1], pf_next[:1])
         dec_ev, pf_ev = [], []
         dec_rows = pf_tokens = done = 0
         max_stall_ms = 0.0
@@ -536,11 +546,13 @@ def run_continuous(args, wl, torch, cbd, synth):
         w0 = time.perf_counter()
         while done < n_req:
             while waiting < n_req and arrive[waiting] <= tick and len(live) + len(pending) < cap:
+                need = int(plens[waiting] + glens[waiting])
+                shared = min(int(plens[waiting]) - 1, 1024) if holder is not None else 0
                 try:
-                    sid = eng.alloc(int(plens[waiting] + glens[waiting]))
+                    sid = eng.fork(holder, shared, need) if shared else eng.alloc(need)
                 except cbd.CbdError:
                     break  # arena full: the request waits
-                pending.append([sid, waiting, 0])
+                pending.append([sid, waiting, shared])
                 waiting += 1
             # one prefill call per tick: the pending prompts in arrival order, at most `chunk` tokens in
             # all (a prompt may continue over several ticks; --prefill-chunk 0: whole prompts)
@@ -596,6 +608,8 @@ def run_continuous(args, wl, torch, cbd, synth):
                 tick += 1
             elif waiting < n_req and not segs and not pending:
                 tick = max(tick + 1, int(np.ceil(arrive[waiting])))
+        if holder is not None:
+            eng.free(holder)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
         dec_ms = sum(a.elapsed_time(b) for a, b in dec_ev)
@@ -609,7 +623,8 @@ def run_continuous(args, wl, torch, cbd, synth):
             "longest_prefill_call_ms": round(max_stall_ms, 1),
             "prefill_tok_s": round(pf_tokens / (pf_ms * 1e-3), 1) if pf_ms else None,
             "wall_tok_s": round(gen / wall, 1), "wall_s": round(wall, 2),
-            "decode_GBps": round(step_bytes / (dec_ms * 1e-3) / 1e9, 1)}
+            "decode_GBps": round(step_bytes / (dec_ms * 1e-3) / 1e9, 1),
+            "prefix_shared": bool(args.share_prefix)}
         log("cap %d: %s" % (cap, json.dumps(results[str(cap)])))
     top = results[str(max(caps))]
     out = {"metric": "continuous batching: decode-only aggregate tok/s at batch cap %d, 8B-shape bf16" % max(caps),
@@ -618,9 +633,11 @@ def run_continuous(args, wl, torch, cbd, synth):
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "continuous: %s, caps %s, Poisson arrivals (offered 1.25 x cap), prompts U[%d,%d] "
                                   "with a 1024-token shared prefix, generation U[64,512], %d requests per cap = 4 cap + 8; "
-                                  "admission %s" % (shape.name, caps, args.ctx_lo, args.ctx_hi, 4 * max(caps) + 8,
-                                                    "in chunks of at most %d tokens per tick" % args.prefill_chunk
-                                                    if args.prefill_chunk > 0 else "of whole prompts"),
+                                  "admission %s%s" % (shape.name, caps, args.ctx_lo, args.ctx_hi, 4 * max(caps) + 8,
+                                                      "in chunks of at most %d tokens per tick" % args.prefill_chunk
+                                                      if args.prefill_chunk > 0 else "of whole prompts",
+                                                      "; joiners fork the shared prefix from one prefilled sequence "
+                                                      "(kvslab_fork)" if args.share_prefix else ""),
                       "parallelism": "single GPU"},
            "caps": results}
     eng.close()
