@@ -22,9 +22,9 @@ from .model import (OracleModel, SeqState, bf16_bits_to_f64, round_to_bf16, f64_
                     rmsnorm, rope_angles, apply_rope, attend_one_head, silu, dequant_int4,
                     greedy)
 from .sampling import philox4x64_10, uniform_draw, nucleus_order, sample_row, sample_rows
-from .kvquant import quantize_affine8, dequantize_affine8
+from .kvquant import quantize_affine8, quantize_affine4, dequantize_affine8
 
 __all__ = ["OracleModel", "SeqState", "bf16_bits_to_f64", "round_to_bf16", "f64_to_bf16_bits",
            "rmsnorm", "rope_angles", "apply_rope", "attend_one_head", "silu", "dequant_int4",
            "greedy", "philox4x64_10", "uniform_draw", "nucleus_order", "sample_row", "sample_rows",
-           "quantize_affine8", "dequantize_affine8"]
+           "quantize_affine8", "quantize_affine4", "dequantize_affine8"]

@@ -1,4 +1,5 @@
-"""Plain CPU definition of affine 8-bit K/V storage (test infrastructure only; see the package docstring).
+"""Plain CPU definition of affine 8-bit and 4-bit K/V storage (test infrastructure only; see the package
+docstring).
 
 Sources (pages as titled; section names as they appear there):
 - mlx-bun "Batching" design note, section 4.3 "Join: adopt, extend, or merge - by layer kind": a
@@ -13,10 +14,11 @@ Readings where the pages are silent (the plainest ones, listed in the design not
 - Affine groups of 64 consecutive elements of one head vector (the head dimension), one group
   per 64 dims; each group stores a scale s and a bias b, and an element is s * code + b.
 - Quantized value x is the bf16 value that a bf16 slab would hold for that element.
-- b = the group minimum, s = (group maximum - b) / 255, code = round-half-even((x - b) / s)
-  clamped to 0..255, and code 0 for a constant group (s = 0). The code is an integer decided by
-  floating point, so it is decided in float32, the storage precision of s and b: the subtraction
-  and the division are single float32 operations (IEEE, rounded to nearest).
+- b = the group minimum, s = (group maximum - b) / L, code = round-half-even((x - b) / s)
+  clamped to 0..L, and code 0 for a constant group (s = 0), with L = 255 (8-bit) or 15 (4-bit).
+  The code is an integer decided by floating point, so it is decided in float32, the storage
+  precision of s and b: the subtraction and the division are single float32 operations (IEEE,
+  rounded to nearest).
 - Dequantized values (what attention reads) are s * code + b evaluated exactly (float64).
 """
 from __future__ import annotations
@@ -33,6 +35,17 @@ def bf16_bits_to_f32(bits) -> np.ndarray:
 
 def quantize_affine8(bits, group: int = 64):
     """bf16 bit patterns [..., D] -> (codes uint8 [..., D], sb float32 [..., D/group, 2] = (scale, bias))."""
+    return quantize_affine(bits, group, 8)
+
+
+def quantize_affine4(bits, group: int = 64):
+    """The 4-bit form: codes 0..15 (one per uint8 here), the same (scale, bias) pairs."""
+    return quantize_affine(bits, group, 4)
+
+
+def quantize_affine(bits, group: int = 64, nbits: int = 8):
+    """Affine codes of nbits bits per element with a (scale, bias) pair per group."""
+    levels = (1 << nbits) - 1
     x = bf16_bits_to_f32(bits)
     d = x.shape[-1]
     if d % group:
@@ -40,10 +53,10 @@ def quantize_affine8(bits, group: int = 64):
     xg = x.reshape(x.shape[:-1] + (d // group, group))
     lo = xg.min(axis=-1)
     hi = xg.max(axis=-1)
-    scale = (hi - lo) / np.float32(KV8_LEVELS)  # float32 operations throughout
+    scale = (hi - lo) / np.float32(levels)  # float32 operations throughout
     safe = np.where(scale > 0, scale, np.float32(1))
     q = np.rint((xg - lo[..., None]) / safe[..., None])
-    q = np.where(scale[..., None] > 0, np.clip(q, 0, KV8_LEVELS), 0)
+    q = np.where(scale[..., None] > 0, np.clip(q, 0, levels), 0)
     codes = q.astype(np.uint8).reshape(x.shape)
     sb = np.stack([scale, lo], axis=-1).astype(np.float32)
     return codes, sb

@@ -24,9 +24,9 @@ body; the plainest Llama/Mistral reading is taken):
   fed one at a time through decode attend to identical keys.
 - int4 affine weights: w = scale * code + bias per group of consecutive
   input-dimension elements.
-- Quantized K/V (``kv_format="affine8"``, module ``kvquant``): the slab keeps
-  the affine 8-bit form of the bf16 value above, written when the token is
-  appended; attention reads its dequantized value.
+- Quantized K/V (``kv_format="affine8"`` or ``"affine4"``, module ``kvquant``):
+  the slab keeps the affine 8-bit or 4-bit form of the bf16 value above,
+  written when the token is appended; attention reads its dequantized value.
 """
 from __future__ import annotations
 
@@ -35,7 +35,7 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-from .kvquant import dequantize_affine8, quantize_affine8
+from .kvquant import dequantize_affine8, quantize_affine
 
 
 # --------------------------------------------------------------------------- number formats
@@ -158,8 +158,8 @@ class OracleModel:
 
     def __init__(self, weights: Dict, cache_all_layers: bool = False, kv_format: str = "bf16",
                  kv_group: int = 64):
-        if kv_format not in ("bf16", "affine8"):
-            raise ValueError("kv_format must be 'bf16' or 'affine8'")
+        if kv_format not in ("bf16", "affine8", "affine4"):
+            raise ValueError("kv_format must be 'bf16', 'affine8' or 'affine4'")
         self.w = weights
         self.cfg = weights["shape"]
         self.kv_format = kv_format
@@ -236,7 +236,7 @@ class OracleModel:
             s.v[l] = np.concatenate([s.v[l], vb])
             return
         for codes, sbs, x in ((s.k, s.k_sb, kb), (s.v, s.v_sb, vb)):
-            c, sb = quantize_affine8(x, self.kv_group)
+            c, sb = quantize_affine(x, self.kv_group, 8 if self.kv_format == "affine8" else 4)
             codes[l] = np.concatenate([codes[l], c])
             sbs[l] = np.concatenate([sbs[l], sb])
 

@@ -81,27 +81,28 @@ def f32_round(x):
     return struct.unpack("<f", struct.pack("<f", x))[0]
 
 
-def affine8_nearest(xs, group):
-    """Affine 8-bit storage by direct search: per group, bias = min, scale = float32((max - min) / 255),
-    and each element takes the code 0..255 whose grid value bias + scale * code is nearest to it
+def affine_nearest(xs, group, levels=255):
+    """Affine storage by direct search: per group, bias = min, scale = float32((max - min) / levels),
+    and each element takes the code 0..levels whose grid value bias + scale * code is nearest to it
     (the lower code on an exact tie is never needed for random inputs). Returns dequantized values."""
     out = []
     for g0 in range(0, len(xs), group):
         grp = xs[g0:g0 + group]
         lo, hi = min(grp), max(grp)
-        s = f32_round((hi - lo) / 255.0)
+        s = f32_round((hi - lo) / float(levels))
         for x in grp:
             if s == 0.0:
                 out.append(lo)
                 continue
-            best = min(range(256), key=lambda c: abs(lo + s * c - x))
+            best = min(range(levels + 1), key=lambda c: abs(lo + s * c - x))
             out.append(lo + s * best)
     return out
 
 
 class BruteModel:
-    def __init__(self, weights, kv_group=None):
-        self.kv_group = kv_group  # None: bf16 slabs; else affine 8-bit slabs with this group
+    def __init__(self, weights, kv_group=None, kv_levels=255):
+        self.kv_group = kv_group  # None: bf16 slabs; else affine slabs with this group and code range
+        self.kv_levels = kv_levels
         self.cfg = cfg = weights["shape"]
         if cfg.weight_format == "int4":
             conv = lambda m: int4_mat(m, cfg.group_size)
@@ -131,8 +132,8 @@ class BruteModel:
             ks = [[bf16_round(z) for z in rope(k[j * dh:(j + 1) * dh], pos, c.rope_theta)] for j in range(hkv)]
             vs = [[bf16_round(z) for z in v[j * dh:(j + 1) * dh]] for j in range(hkv)]
             if self.kv_group:
-                ks = [affine8_nearest(x, self.kv_group) for x in ks]
-                vs = [affine8_nearest(x, self.kv_group) for x in vs]
+                ks = [affine_nearest(x, self.kv_group, self.kv_levels) for x in ks]
+                vs = [affine_nearest(x, self.kv_group, self.kv_levels) for x in vs]
             slab = self.kv[sid][l]
             assert len(slab) == pos
             slab.append((ks, vs))

@@ -12,7 +12,8 @@ import pytest
 
 import synth
 from oracle import (OracleModel, apply_rope, attend_one_head, bf16_bits_to_f64, dequant_int4,
-                    dequantize_affine8, f64_to_bf16_bits, greedy, quantize_affine8, rmsnorm, round_to_bf16,
+                    dequantize_affine8, f64_to_bf16_bits, greedy, quantize_affine4, quantize_affine8, rmsnorm,
+                    round_to_bf16,
                     rope_angles, silu)
 from bruteforce import BruteModel
 
@@ -158,16 +159,16 @@ def test_dequant_closed_form_and_group_index():
 
 # --------------------------------------------------------------------------- whole model vs brute force
 
-def _run_trajectory(weights, prompts, steps, kv_group=None, rtol=1e-10):
+def _run_trajectory(weights, prompts, steps, kv_group=None, rtol=1e-10, kv_bits=8):
     """Oracle: prefill each prompt, then greedy decode; brute: same tokens, one at a time.
-    kv_group: affine 8-bit slabs with that group (None: bf16 slabs)."""
+    kv_group: affine slabs of kv_bits-bit codes with that group (None: bf16 slabs)."""
     if kv_group:
-        orc = OracleModel(weights, cache_all_layers=True, kv_format="affine8", kv_group=kv_group)
+        orc = OracleModel(weights, cache_all_layers=True, kv_format="affine%d" % kv_bits, kv_group=kv_group)
     else:
         orc = OracleModel(weights, cache_all_layers=True)
     ids = [orc.new_sequence() for _ in prompts]
     lg0 = orc.prefill_segmented(ids, prompts)
-    bf = BruteModel(weights, kv_group=kv_group)
+    bf = BruteModel(weights, kv_group=kv_group, kv_levels=(1 << kv_bits) - 1)
     for i in ids:
         bf.add_seq(i)
     brute0 = []
@@ -213,6 +214,13 @@ def test_oracle_matches_scalar_brute_force_kv8():
     w = synth.make_weights(MICRO, seed=8, gain_std=0.2)
     pr = synth.prompts(42, [4, 6], MICRO.vocab)
     _run_trajectory(w, pr, steps=3, kv_group=2, rtol=1e-9)
+
+
+def test_oracle_matches_scalar_brute_force_kv4():
+    """Affine 4-bit slabs, one group per 4-dim head (two codes strictly inside each group's range)."""
+    w = synth.make_weights(MICRO, seed=9, gain_std=0.2)
+    pr = synth.prompts(43, [5, 3], MICRO.vocab)
+    _run_trajectory(w, pr, steps=3, kv_group=4, rtol=1e-9, kv_bits=4)
 
 
 # --------------------------------------------------------------------------- shared prefixes
@@ -294,6 +302,29 @@ def test_affine8_codes_are_nearest_grid_points():
     assert np.all(err <= s[..., None] * (0.5 + 1e-4))
     assert np.all(codes.reshape(6, 2, 2, 64).min(axis=-1) == 0)
     assert np.all(codes.reshape(6, 2, 2, 64).max(axis=-1) == 255)
+
+
+def test_affine4_grid_and_nearest_codes():
+    """4-bit codes: an exact grid comes back exactly (scale (max - min)/15), and random groups take the
+    nearest of the 16 grid values (either neighbour only within float32 rounding of a half)."""
+    rng = np.random.default_rng(4)
+    c = np.concatenate([[0, 15], rng.integers(0, 16, 62)])
+    v = -2.0 + c * 0.25  # s = 1/4, b = -2: bf16 holds every value
+    codes, sb = quantize_affine4(_bf16_bits_of(v))
+    assert np.array_equal(codes, c.astype(np.uint8))
+    assert np.array_equal(sb, np.array([[0.25, -2.0]], dtype=np.float32))
+    assert np.array_equal(dequantize_affine8(codes, sb), v)
+    x = f64_to_bf16_bits(rng.normal(0, 2.0, (5, 3, 128)))
+    xv = bf16_bits_to_f64(x).reshape(5, 3, 2, 64)
+    codes, sb = quantize_affine4(x)
+    s, b = sb[..., 0].astype(np.float64), sb[..., 1].astype(np.float64)
+    assert np.array_equal(sb[..., 0], ((xv.max(axis=-1) - xv.min(axis=-1)) / 15.0).astype(np.float32))
+    nearest = np.argmin(np.abs(b[..., None, None] + s[..., None, None] * np.arange(16) - xv[..., None]), axis=-1)
+    quo = (xv - b[..., None]) / s[..., None]
+    near_half = np.abs(quo - np.floor(quo) - 0.5) < 1e-5
+    cc = codes.reshape(5, 3, 2, 64).astype(np.int64)
+    assert np.array_equal(cc[~near_half], nearest[~near_half]) and codes.max() == 15
+    assert np.all(np.abs(cc - nearest)[near_half] <= 1)
 
 
 def test_affine8_constant_group_and_group_independence():
