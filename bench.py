@@ -26,6 +26,7 @@ Other workloads (``--workload``), each printing its own JSON line:
   128 steps; roofline on decode attention (the K/V stream dominates the step).
 - llama8b-long-kv8: the same with affine 8-bit K/V slabs (codes + float32 scale and bias per
   64 dims): the K/V stream shrinks to 144 of 256 bytes per token, layer and KV head.
+- llama8b-long-kv4: the same with 4-bit codes (80 bytes per token, layer and KV head).
 - continuous: the 8B-shape bf16 model under continuous batching with the batch cap
   swept over 1..64: Poisson arrivals (in decode ticks, offered concurrency about
   1.25 x cap), prompts uniform in [256, 2048] sharing a 1024-token prefix,
@@ -61,6 +62,8 @@ WORKLOADS = {
                      "ctx_hi": 32768, "roofline": "attention", "hist_seed": 5},
     "llama8b-long-kv8": {"shape": "llama3-8b-shape", "steps": 128, "batch": 8, "sweep": "", "ctx_lo": 32768,
                          "ctx_hi": 32768, "roofline": "attention", "hist_seed": 5, "kv_format": "affine8"},
+    "llama8b-long-kv4": {"shape": "llama3-8b-shape", "steps": 128, "batch": 8, "sweep": "", "ctx_lo": 32768,
+                         "ctx_hi": 32768, "roofline": "attention", "hist_seed": 5, "kv_format": "affine4"},
     "continuous": {"shape": "llama3-8b-shape", "steps": 0, "batch": 64, "sweep": "1,2,4,8,16,32,64", "ctx_lo": 256,
                    "ctx_hi": 2048, "roofline": "gate_up", "hist_seed": 2},
     "prefill": {"shape": "llama3-8b-shape", "steps": 8, "batch": 16, "sweep": "", "ctx_lo": 64, "ctx_hi": 1024,
@@ -266,7 +269,7 @@ def main():
         "gate_up": "ksplit_gemm_kernel: gate/up weight stream with fused SwiGLU (%s weights), %s, B=%d" % (
             shape.weight_format, shape.name, B),
         "attention": "%s: RoPE + K/V append + ragged GQA attention, %s K/V, %s, B=%d at %d-token contexts" % (
-            "decode_attention_q8_kernel" if kv_format == "affine8" else "decode_attention_kernel", kv_format,
+            "decode_attention_q8_kernel" if kv_format != "bf16" else "decode_attention_kernel", kv_format,
             shape.name, B, args.ctx_lo),
     }[rk]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

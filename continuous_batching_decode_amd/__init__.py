@@ -21,8 +21,8 @@ CBD_E_UNSUPPORTED = -7
 STATUS_NAMES = {0: "CBD_OK", -1: "CBD_E_INVAL", -2: "CBD_E_NOSPACE", -3: "CBD_E_CAPACITY", -4: "CBD_E_BADSEQ",
                 -5: "CBD_E_HIP", -6: "CBD_E_NODEVICE", -7: "CBD_E_UNSUPPORTED"}
 WEIGHTS_BF16, WEIGHTS_INT4 = 0, 1
-KV_BF16, KV_AFFINE8 = 0, 1
-KV_FORMATS = {"bf16": KV_BF16, "affine8": KV_AFFINE8}
+KV_BF16, KV_AFFINE8, KV_AFFINE4 = 0, 1, 2
+KV_FORMATS = {"bf16": KV_BF16, "affine8": KV_AFFINE8, "affine4": KV_AFFINE4}
 
 # every symbol include/cbd.h declares
 EXPORTS = ["cbd_kv_bytes_per_token", "cbd_slab_granule_tokens", "cbd_create", "cbd_destroy", "cbd_last_error",
@@ -144,7 +144,8 @@ def kv_bytes_per_token(shape, kv_format: str = "bf16") -> int:
 
 
 def model_config(shape, max_position: int, kv_format: str = "bf16") -> ModelConfig:
-    """C config from a shape object (attributes as in synth.ModelShape); kv_format "bf16" or "affine8"."""
+    """C config from a shape object (attributes as in synth.ModelShape); kv_format "bf16", "affine8" or
+    "affine4"."""
     return ModelConfig(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim,
                        shape.ffn_dim, shape.vocab, float(shape.rms_eps), float(shape.rope_theta),
                        WEIGHTS_INT4 if shape.weight_format == "int4" else WEIGHTS_BF16, int(max_position),
@@ -300,7 +301,7 @@ class Engine:
         return k, v
 
     def kvslab_read_q8(self, seq_id: int, start: int, n: int, stream=None):
-        """Stored form of an affine 8-bit slab: codes uint8 [L, n, 2, Hkv, Dh] and (scale, bias)
+        """Stored form of an affine slab: codes uint8 [L, n, 2, Hkv, Dh] (one per byte) and (scale, bias)
         float32 [L, n, 2, Hkv, Dh/64, 2] (device tensors)."""
         import torch
         s = self.shape

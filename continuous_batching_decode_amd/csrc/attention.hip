@@ -570,9 +570,9 @@ namespace {
 // lane loads 16 bytes of the block's K and V records and writes them there), and each lane reads the
 // records of its lane group's 8 keys from LDS right before they are used. This keeps two blocks in
 // flight within two waves per SIMD.
-template <int DH>
+template <int DH, int BITS>
 struct Q8Codes {
-  static constexpr int NW = DH / 32;  // 16-byte code words per lane (two fragments each)
+  static constexpr int NW = DH * BITS / 256;  // 16-byte code words per lane (16 / BITS fragments each)
   u32x4_t c[NW];
 };
 
@@ -592,7 +592,7 @@ struct Q8Recs {
   }
 };
 
-template <int DH>
+template <int DH, int BITS>
 struct Q8Stream {
   const uint8_t* kbase;
   const uint8_t* vbase;
@@ -600,16 +600,16 @@ struct Q8Stream {
   int lane;
   CBD_DEVICE Q8Stream(const uint8_t* k, const uint8_t* v, int l) : kbase(k), vbase(v), lane(l) {
     constexpr int U = Q8Recs<DH>::U;
-    rbase = (l < U ? k + 16 * l : v + 16 * (l < 2 * U ? l - U : 0)) + 32 * DH;
+    rbase = (l < U ? k + 16 * l : v + 16 * (l < 2 * U ? l - U : 0)) + 32 * DH * BITS / 8;
   }
-  CBD_DEVICE void load(Q8Codes<DH>& x, const uint8_t* base, int b) const {
-    const uint8_t* p = base + (int64_t)b * q8_block_bytes(DH) + 16 * lane;
+  CBD_DEVICE void load(Q8Codes<DH, BITS>& x, const uint8_t* base, int b) const {
+    const uint8_t* p = base + (int64_t)b * q_block_bytes(DH, BITS) + 16 * lane;
 #pragma unroll
-    for (int i = 0; i < Q8Codes<DH>::NW; ++i) x.c[i] = load_stream(p + 1024 * i);
+    for (int i = 0; i < Q8Codes<DH, BITS>::NW; ++i) x.c[i] = load_stream(p + 1024 * i);
   }
-  CBD_DEVICE void load_k(Q8Codes<DH>& x, int b) const { load(x, kbase, b); }
-  CBD_DEVICE void load_v(Q8Codes<DH>& x, int b) const { load(x, vbase, b); }
-  CBD_DEVICE void load_r(u32x4_t& r, int b) const { r = load_stream(rbase + (int64_t)b * q8_block_bytes(DH)); }
+  CBD_DEVICE void load_k(Q8Codes<DH, BITS>& x, int b) const { load(x, kbase, b); }
+  CBD_DEVICE void load_v(Q8Codes<DH, BITS>& x, int b) const { load(x, vbase, b); }
+  CBD_DEVICE void load_r(u32x4_t& r, int b) const { r = load_stream(rbase + (int64_t)b * q_block_bytes(DH, BITS)); }
 };
 
 // fragment `half` (0: bytes 0..7, 1: bytes 8..15) of a code word as 8 bf16 operands (exact)
@@ -624,9 +624,28 @@ CBD_DEVICE bf16x8_t code_frag(const u32x4_t& w, int half) {
   return as_frag(r);
 }
 
+// fragment q (0..3) of a 4-bit code word as 8 bf16 operands 128 + code: bf16 holds 128 + n (n < 128)
+// with exponent 7 and mantissa n, so the pattern is 0x4300 | n (exact)
+CBD_DEVICE bf16x8_t code_frag4(const u32x4_t& w, int q) {
+  const uint32_t x = w[q];
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = 0x43004300u | ((x >> (8 * i)) & 15u) | (((x >> (8 * i + 4)) & 15u) << 16);
+  return as_frag(r);
+}
+
+// Fragment f of a block's codes; values are code + OFF (OFF = 128 for 4-bit codes, 0 for 8-bit)
+template <int DH, int BITS>
+CBD_DEVICE bf16x8_t qfrag(const Q8Codes<DH, BITS>& c, int f) {
+  if constexpr (BITS == 8) return code_frag(c.c[f >> 1], f & 1);
+  else return code_frag4(c.c[f >> 2], f & 3);
+}
+template <int BITS>
+constexpr float kQOff = BITS == 4 ? 128.f : 0.f;
+
 // Raw scores of a block for the lane's 8 keys in V order (i < 4: key 4g + i, else 16 + 4g + i - 4).
-template <int DH>
-CBD_DEVICE void q8_scores(const Q8Codes<DH>& K, const f32x4_t* slot, int g, const bf16x8_t (&qh)[DH / 32],
+template <int DH, int BITS>
+CBD_DEVICE void q8_scores(const Q8Codes<DH, BITS>& K, const f32x4_t* slot, int g, const bf16x8_t (&qh)[DH / 32],
                           const bf16x8_t (&ql)[DH / 32], const float (&qs)[DH / kQGroup], float (&sv)[8]) {
   constexpr int NU = DH / 32, NG = DH / kQGroup;
   f32x4_t acc[2][NG];
@@ -639,7 +658,7 @@ CBD_DEVICE void q8_scores(const Q8Codes<DH>& K, const f32x4_t* slot, int g, cons
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int f = h * NU + u, gi = u / 2;
-      const bf16x8_t kf = code_frag(K.c[f >> 1], f & 1);
+      const bf16x8_t kf = qfrag<DH, BITS>(K, f);
       acc[h][gi] = mfma(kf, qh[u], acc[h][gi]);
       acc[h][gi] = mfma(kf, ql[u], acc[h][gi]);
     }
@@ -652,7 +671,8 @@ CBD_DEVICE void q8_scores(const Q8Codes<DH>& K, const f32x4_t* slot, int g, cons
       const int i = 4 * h + e;
       float x = 0.f;
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi) x += R.s(i, gi) * acc[h][gi][e] + R.b(i, gi) * qs[gi];
+      for (int gi = 0; gi < NG; ++gi)
+        x += R.s(i, gi) * acc[h][gi][e] + (R.b(i, gi) - kQOff<BITS> * R.s(i, gi)) * qs[gi];
       sv[i] = x;
     }
 }
@@ -697,8 +717,8 @@ CBD_DEVICE void q8_softmax(float (&sv)[NB][8], float (&p)[NB][8], int b, int g, 
 }
 
 // O^T += codes^T (p s_g)^T per group of dims, and the bias sums, for one block.
-template <int DH>
-CBD_DEVICE void q8_block_pv(const Q8Codes<DH>& V, const f32x4_t* slot, int g, const float (&p)[8], Online<DH>& st,
+template <int DH, int BITS>
+CBD_DEVICE void q8_block_pv(const Q8Codes<DH, BITS>& V, const f32x4_t* slot, int g, const float (&p)[8], Online<DH>& st,
                             float (&bacc)[DH / kQGroup]) {
   constexpr int NG = DH / kQGroup, NT = DH / 16;
   Q8Recs<DH> R;
@@ -710,7 +730,7 @@ CBD_DEVICE void q8_block_pv(const Q8Codes<DH>& V, const f32x4_t* slot, int g, co
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       pg[i] = p[i] * R.s(i, gi);
-      bs += p[i] * R.b(i, gi);
+      bs += p[i] * (R.b(i, gi) - kQOff<BITS> * R.s(i, gi));
     }
     bacc[gi] += bs;
     split8(pg, ph[gi], pl[gi]);
@@ -718,7 +738,7 @@ CBD_DEVICE void q8_block_pv(const Q8Codes<DH>& V, const f32x4_t* slot, int g, co
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int gi = t / 4;
-    const bf16x8_t vf = code_frag(V.c[t >> 1], t & 1);
+    const bf16x8_t vf = qfrag<DH, BITS>(V, t);
     st.o[t] = mfma(vf, ph[gi], st.o[t]);
     st.o[t] = mfma(vf, pl[gi], st.o[t]);
   }
@@ -726,7 +746,7 @@ CBD_DEVICE void q8_block_pv(const Q8Codes<DH>& V, const f32x4_t* slot, int g, co
 
 }  // namespace
 
-template <int DH, int G>
+template <int DH, int G, int BITS>
 __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kernel(AttnArgs a, int n_waves) {
   constexpr int NU = DH / 32;
   constexpr int NT = DH / 16;
@@ -738,7 +758,7 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
   const int j = w % a.n_kv_heads;
   const AttnItem it = uniform_item(a.items, w / a.n_kv_heads);
   const int pos = it.pos;
-  const int64_t region = (int64_t)(it.stride / 32) * q8_block_bytes(DH);
+  const int64_t region = (int64_t)(it.stride / 32) * q_block_bytes(DH, BITS);
   uint8_t* slab = a.arena + it.slab_off;
   uint8_t* kbase = slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * region;
   uint8_t* vbase = slab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * region;
@@ -746,7 +766,7 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
   const int kend = appends ? pos : it.k_end;
   const int b_first = it.k_begin >> 5, b_end = (kend + 31) >> 5;
   const float scale = 1.0f / sqrtf((float)DH);
-  const Q8Stream<DH> kv(kbase, vbase, lane);
+  const Q8Stream<DH, BITS> kv(kbase, vbase, lane);
   __shared__ f32x4_t q8_lds[kAttnWgWaves][2][64];
   f32x4_t* slot0 = q8_lds[threadIdx.x >> 6][0];
   f32x4_t* slot1 = q8_lds[threadIdx.x >> 6][1];
@@ -754,7 +774,7 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
   // blocks b_first and b1 in flight from the start (records first: they are staged first)
   const int last = max(b_end - 1, b_first);
   const int b1 = min(b_first + 1, last);
-  Q8Codes<DH> K0, V0, K1, V1;
+  Q8Codes<DH, BITS> K0, V0, K1, V1;
   u32x4_t R0, R1;
   kv.load_r(R0, b_first);
   kv.load_r(R1, b1);
@@ -845,7 +865,7 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
       klo[gi] = fminf(klo[gi], __shfl_xor(klo[gi], 32, 64));
       khi[gi] = fmaxf(khi[gi], __shfl_xor(khi[gi], 16, 64));
       khi[gi] = fmaxf(khi[gi], __shfl_xor(khi[gi], 32, 64));
-      ks[gi] = q8_scale(klo[gi], khi[gi]);
+      ks[gi] = q8_scale<BITS>(klo[gi], khi[gi]);
     }
     float dot = 0.f;
 #pragma unroll
@@ -855,13 +875,17 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
       uint32_t cw[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t code = q8_code(kvals[u][e], klo[gi], ks[gi]);
-        cw[e >> 2] |= code << (8 * (e & 3));
+        const uint32_t code = q8_code<BITS>(kvals[u][e], klo[gi], ks[gi]);
+        if constexpr (BITS == 8) cw[e >> 2] |= code << (8 * (e & 3));
+        else cw[0] |= code << (4 * e);
         const uint32_t qb = e & 1 ? qhu[e >> 1] >> 16 : qhu[e >> 1] & 0xFFFFu;
         const uint32_t lb = e & 1 ? qlu[e >> 1] >> 16 : qlu[e >> 1] & 0xFFFFu;
         dot += (bf16_to_f32(qb) + bf16_to_f32(lb)) * fmaf(ks[gi], (float)code, klo[gi]);
       }
-      if (c16 == 0) *reinterpret_cast<uint2*>(kbase + kq_off(pos, 32 * u + 8 * g, DH)) = uint2{cw[0], cw[1]};
+      if (c16 == 0) {
+        if constexpr (BITS == 8) *reinterpret_cast<uint2*>(kbase + kq_off(pos, 32 * u + 8 * g, DH)) = uint2{cw[0], cw[1]};
+        else *reinterpret_cast<uint32_t*>(kbase + kq4_off(pos, 32 * u + 8 * g, DH)) = cw[0];
+      }
     }
     dot += __shfl_xor(dot, 16, 64);
     dot += __shfl_xor(dot, 32, 64);
@@ -889,22 +913,25 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
       vlo[gi] = fminf(vlo[gi], __shfl_xor(vlo[gi], 32, 64));
       vhi[gi] = fmaxf(vhi[gi], __shfl_xor(vhi[gi], 16, 64));
       vhi[gi] = fmaxf(vhi[gi], __shfl_xor(vhi[gi], 32, 64));
-      vs[gi] = q8_scale(vlo[gi], vhi[gi]);
+      vs[gi] = q8_scale<BITS>(vlo[gi], vhi[gi]);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int gi = t / 4;
-        const uint32_t code = q8_code(st.o[t][e], vlo[gi], vs[gi]);
+        const uint32_t code = q8_code<BITS>(st.o[t][e], vlo[gi], vs[gi]);
         st.o[t][e] = fmaf(vs[gi], (float)code, vlo[gi]);
-        if (c16 == 0) vbase[vq_off(pos, 16 * t + 4 * g + e, DH)] = (uint8_t)code;
+        if (c16 == 0) {
+          if constexpr (BITS == 8) vbase[vq_off(pos, 16 * t + 4 * g + e, DH)] = (uint8_t)code;
+          else store_nibble(vbase + vq4_off(pos, 16 * t + 4 * g + e, DH), vslab_kk(pos) & 1, code);
+        }
       }
     if (lane == 0)
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
-        *reinterpret_cast<float2*>(kbase + sbq_off(pos, gi, DH)) = float2{ks[gi], klo[gi]};
-        *reinterpret_cast<float2*>(vbase + sbq_off(pos, gi, DH)) = float2{vs[gi], vlo[gi]};
+        *reinterpret_cast<float2*>(kbase + sbq_off(pos, gi, DH, BITS)) = float2{ks[gi], klo[gi]};
+        *reinterpret_cast<float2*>(vbase + sbq_off(pos, gi, DH, BITS)) = float2{vs[gi], vlo[gi]};
       }
   }
 
@@ -919,15 +946,15 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
     kv.load_r(R1, min(b + 3, last));
     __builtin_amdgcn_sched_barrier(0);
     float sv[2][8], p[2][8];
-    q8_scores<DH>(K0, slot0, g, qh, ql, qs, sv[0]);
-    q8_scores<DH>(K1, slot1, g, qh, ql, qs, sv[1]);
+    q8_scores<DH, BITS>(K0, slot0, g, qh, ql, qs, sv[0]);
+    q8_scores<DH, BITS>(K1, slot1, g, qh, ql, qs, sv[1]);
     __builtin_amdgcn_sched_barrier(0);
     kv.load_k(K0, b + 2);
     kv.load_k(K1, min(b + 3, last));
     __builtin_amdgcn_sched_barrier(0);
     q8_softmax<DH, 2>(sv, p, b, g, kend, scale, st, bacc);
-    q8_block_pv<DH>(V0, slot0, g, p[0], st, bacc);
-    q8_block_pv<DH>(V1, slot1, g, p[1], st, bacc);
+    q8_block_pv<DH, BITS>(V0, slot0, g, p[0], st, bacc);
+    q8_block_pv<DH, BITS>(V1, slot1, g, p[1], st, bacc);
     __builtin_amdgcn_sched_barrier(0);
     kv.load_v(V0, b + 2);
     kv.load_v(V1, min(b + 3, last));
@@ -937,16 +964,16 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
   slot1[lane] = __builtin_bit_cast(f32x4_t, R1);
   if (b + 1 < b_end) {  // a last pair
     float sv[2][8], p[2][8];
-    q8_scores<DH>(K0, slot0, g, qh, ql, qs, sv[0]);
-    q8_scores<DH>(K1, slot1, g, qh, ql, qs, sv[1]);
+    q8_scores<DH, BITS>(K0, slot0, g, qh, ql, qs, sv[0]);
+    q8_scores<DH, BITS>(K1, slot1, g, qh, ql, qs, sv[1]);
     q8_softmax<DH, 2>(sv, p, b, g, kend, scale, st, bacc);
-    q8_block_pv<DH>(V0, slot0, g, p[0], st, bacc);
-    q8_block_pv<DH>(V1, slot1, g, p[1], st, bacc);
+    q8_block_pv<DH, BITS>(V0, slot0, g, p[0], st, bacc);
+    q8_block_pv<DH, BITS>(V1, slot1, g, p[1], st, bacc);
   } else if (b < b_end) {  // a last single block
     float sv[1][8], p[1][8];
-    q8_scores<DH>(K0, slot0, g, qh, ql, qs, sv[0]);
+    q8_scores<DH, BITS>(K0, slot0, g, qh, ql, qs, sv[0]);
     q8_softmax<DH, 1>(sv, p, b, g, kend, scale, st, bacc);
-    q8_block_pv<DH>(V0, slot0, g, p[0], st, bacc);
+    q8_block_pv<DH, BITS>(V0, slot0, g, p[0], st, bacc);
   }
   // bias sums over the column's keys (all four lane groups), added to every dim of their group
 #pragma unroll
@@ -1021,7 +1048,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(AttnArgs a, i
 
 // Prefill over affine 8-bit slabs: the tile and column layout of prefill_attention_kernel, blocks
 // streamed one at a time through the code products of the decode kernel.
-template <int DH>
+template <int DH, int BITS>
 __global__ __launch_bounds__(256, 2) void prefill_attention_q8_kernel(AttnArgs a, int n_waves) {
   constexpr int NU = DH / 32;
   constexpr int NT = DH / 16;
@@ -1034,17 +1061,17 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_q8_kernel(AttnArgs a
   const AttnItem it = uniform_item(a.items, w / a.n_heads);
   const int h = w % a.n_heads, j = h / (a.n_heads / a.n_kv_heads);
   const int n_q = it.k_end - it.pos;
-  const int64_t region = (int64_t)(it.stride / 32) * q8_block_bytes(DH);
+  const int64_t region = (int64_t)(it.stride / 32) * q_block_bytes(DH, BITS);
   const uint8_t* slab = a.arena + it.slab_off;
-  const Q8Stream<DH> kv(slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * region,
+  const Q8Stream<DH, BITS> kv(slab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * region,
                         slab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * region, lane);
   // a forked sequence: blocks [0, pb) from the parent's slab, the rest from its own
   const int pb = it.pre_end >> 5;
-  const int64_t pregion = (int64_t)(it.pre_stride / 32) * q8_block_bytes(DH);
+  const int64_t pregion = (int64_t)(it.pre_stride / 32) * q_block_bytes(DH, BITS);
   const uint8_t* pslab = a.arena + it.pre_off;
-  const Q8Stream<DH> kp(pslab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * pregion,
+  const Q8Stream<DH, BITS> kp(pslab + ((int64_t)(a.layer * 2 + 0) * a.n_kv_heads + j) * pregion,
                         pslab + ((int64_t)(a.layer * 2 + 1) * a.n_kv_heads + j) * pregion, lane);
-  Q8Codes<DH> K0, V0;
+  Q8Codes<DH, BITS> K0, V0;
   u32x4_t R0;
   (pb > 0 ? kp : kv).load_r(R0, 0);
   (pb > 0 ? kp : kv).load_k(K0, 0);
@@ -1081,14 +1108,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_q8_kernel(AttnArgs a
   const int b_end = (it.k_end + 31) >> 5;
   for (int b = 0; b < b_end; ++b) {
     const int nb = min(b + 1, b_end - 1);
-    const Q8Stream<DH>& nx = nb < pb ? kp : kv;  // the slab that holds the next block
+    const Q8Stream<DH, BITS>& nx = nb < pb ? kp : kv;  // the slab that holds the next block
     slot[lane] = __builtin_bit_cast(f32x4_t, R0);
     nx.load_r(R0, nb);
     float sv[1][8], p[1][8];
-    q8_scores<DH>(K0, slot, g, qh, ql, qs, sv[0]);
+    q8_scores<DH, BITS>(K0, slot, g, qh, ql, qs, sv[0]);
     nx.load_k(K0, nb);
     q8_softmax<DH, 1>(sv, p, b, g, lim, 1.0f / sqrtf((float)DH), st, bacc);
-    q8_block_pv<DH>(V0, slot, g, p[0], st, bacc);
+    q8_block_pv<DH, BITS>(V0, slot, g, p[0], st, bacc);
     nx.load_v(V0, nb);
   }
 #pragma unroll
@@ -1123,31 +1150,35 @@ hipError_t launch_decode_attention(const AttnArgs& a, int n_items, int head_dim,
   return hipErrorInvalidValue;
 }
 
-template <int DH>
+template <int DH, int BITS>
 static hipError_t launch_decode_q8_dh(int G, dim3 grid, int n_waves, hipStream_t st, const AttnArgs& a) {
   switch (G) {
-    case 1: launch_kernel((decode_attention_q8_kernel<DH, 1>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
-    case 2: launch_kernel((decode_attention_q8_kernel<DH, 2>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
-    case 4: launch_kernel((decode_attention_q8_kernel<DH, 4>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
+    case 1: launch_kernel((decode_attention_q8_kernel<DH, 1, BITS>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
+    case 2: launch_kernel((decode_attention_q8_kernel<DH, 2, BITS>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
+    case 4: launch_kernel((decode_attention_q8_kernel<DH, 4, BITS>), grid, dim3(64 * kAttnWgWaves), 0, st, a, n_waves); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode_attention_q8(const AttnArgs& a, int n_items, int head_dim, hipStream_t st) {
+hipError_t launch_decode_attention_q8(const AttnArgs& a, int n_items, int head_dim, int bits, hipStream_t st) {
   const int G = a.n_heads / a.n_kv_heads;
   const int n_waves = n_items * a.n_kv_heads;
   const dim3 grid((n_waves + kAttnWgWaves - 1) / kAttnWgWaves);
-  if (head_dim == 128) return launch_decode_q8_dh<128>(G, grid, n_waves, st, a);
-  if (head_dim == 64) return launch_decode_q8_dh<64>(G, grid, n_waves, st, a);
+  if (bits == 8 && head_dim == 128) return launch_decode_q8_dh<128, 8>(G, grid, n_waves, st, a);
+  if (bits == 8 && head_dim == 64) return launch_decode_q8_dh<64, 8>(G, grid, n_waves, st, a);
+  if (bits == 4 && head_dim == 128) return launch_decode_q8_dh<128, 4>(G, grid, n_waves, st, a);
+  if (bits == 4 && head_dim == 64) return launch_decode_q8_dh<64, 4>(G, grid, n_waves, st, a);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill_attention_q8(const AttnArgs& a, int n_items, int head_dim, hipStream_t st) {
+hipError_t launch_prefill_attention_q8(const AttnArgs& a, int n_items, int head_dim, int bits, hipStream_t st) {
   const int n_waves = n_items * a.n_heads;
   const dim3 grid((n_waves + 3) / 4);
-  if (head_dim == 128) launch_kernel((prefill_attention_q8_kernel<128>), grid, dim3(256), 0, st, a, n_waves);
-  else if (head_dim == 64) launch_kernel((prefill_attention_q8_kernel<64>), grid, dim3(256), 0, st, a, n_waves);
+  if (bits == 8 && head_dim == 128) launch_kernel((prefill_attention_q8_kernel<128, 8>), grid, dim3(256), 0, st, a, n_waves);
+  else if (bits == 8 && head_dim == 64) launch_kernel((prefill_attention_q8_kernel<64, 8>), grid, dim3(256), 0, st, a, n_waves);
+  else if (bits == 4 && head_dim == 128) launch_kernel((prefill_attention_q8_kernel<128, 4>), grid, dim3(256), 0, st, a, n_waves);
+  else if (bits == 4 && head_dim == 64) launch_kernel((prefill_attention_q8_kernel<64, 4>), grid, dim3(256), 0, st, a, n_waves);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -110,8 +110,13 @@ CBD_DEVICE int64_t vslab_off(int key, int d, int dh) {
 //     byte 1024 i + 16 l and holds fragment 2i in bytes 0..7 and fragment 2i + 1 in bytes 8..15.
 //  records: key kk of the V order (vslab_kk) at byte 32 * Dh + kk * (Dh/64) * 8, group after group.
 //     Lane group g = l/16 owns keys kk = 8g .. 8g + 7: exactly the keys whose scores it holds.
+//
+// Affine 4-bit slabs: the same blocks with 16 * Dh code bytes, two codes per byte (the lower element of
+// the fragment order in the low nibble): a fragment's 8 codes are 4 bytes, and 16-byte word i of lane
+// l (byte 1024 i + 16 l) holds fragments 4i .. 4i + 3, fragment f at bytes 4 (f % 4) .. +3.
 constexpr int kQGroup = 64;
-__host__ __device__ constexpr int q8_block_bytes(int dh) { return 32 * dh + 32 * (dh / kQGroup) * 8; }
+__host__ __device__ constexpr int q_block_bytes(int dh, int bits) { return 32 * dh * bits / 8 + 32 * (dh / kQGroup) * 8; }
+__host__ __device__ constexpr int q8_block_bytes(int dh) { return q_block_bytes(dh, 8); }
 CBD_DEVICE int64_t kq_off(int key, int d, int dh) {
   const int f = ((key >> 4) & 1) * (dh >> 5) + (d >> 5);
   const int lane = (((d & 31) >> 3) << 4) + (key & 15);
@@ -122,17 +127,39 @@ CBD_DEVICE int64_t vq_off(int key, int d, int dh) {
   const int lane = ((kk >> 3) << 4) + (d & 15);
   return (int64_t)(key >> 5) * q8_block_bytes(dh) + ((t >> 1) << 10) + (lane << 4) + ((t & 1) << 3) + (kk & 7);
 }
-CBD_DEVICE int64_t sbq_off(int key, int gi, int dh) {
-  return (int64_t)(key >> 5) * q8_block_bytes(dh) + 32 * dh + ((int64_t)vslab_kk(key) * (dh / kQGroup) + gi) * 8;
+CBD_DEVICE int64_t sbq_off(int key, int gi, int dh, int bits = 8) {
+  return (int64_t)(key >> 5) * q_block_bytes(dh, bits) + 32 * dh * bits / 8 +
+         ((int64_t)vslab_kk(key) * (dh / kQGroup) + gi) * 8;
+}
+// 4-bit codes: byte offset of (key, d); the code is its low nibble when (K: d, V: kk) is even
+CBD_DEVICE int64_t kq4_off(int key, int d, int dh) {
+  const int f = ((key >> 4) & 1) * (dh >> 5) + (d >> 5);
+  const int lane = (((d & 31) >> 3) << 4) + (key & 15);
+  return (int64_t)(key >> 5) * q_block_bytes(dh, 4) + ((f >> 2) << 10) + (lane << 4) + ((f & 3) << 2) + ((d & 7) >> 1);
+}
+CBD_DEVICE int64_t vq4_off(int key, int d, int dh) {
+  const int kk = vslab_kk(key), t = d >> 4;
+  const int lane = ((kk >> 3) << 4) + (d & 15);
+  return (int64_t)(key >> 5) * q_block_bytes(dh, 4) + ((t >> 2) << 10) + (lane << 4) + ((t & 3) << 2) + ((kk & 7) >> 1);
+}
+// Write a 4-bit code into its nibble of a byte whose other nibble another thread may be writing
+// (V: two keys share a byte): clear and set the nibble's bits with word atomics.
+CBD_DEVICE void store_nibble(uint8_t* byte_addr, int high, uint32_t code) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(reinterpret_cast<uintptr_t>(byte_addr) & ~uintptr_t(3));
+  const int sh = 8 * (int)(reinterpret_cast<uintptr_t>(byte_addr) & 3) + 4 * high;
+  atomicAnd(w, ~(15u << sh));
+  atomicOr(w, (code & 15u) << sh);
 }
 
-// Affine 8-bit code of x in a group with minimum lo and scale s = (max - lo) / 255 (q8_scale): the
-// nearest grid point, decided in float32 ((x - lo) / s rounded half to even, clamped to 0..255);
-// a constant group (s = 0) takes code 0.
-CBD_DEVICE float q8_scale(float lo, float hi) { return (hi - lo) / 255.f; }
+// Affine code of x in a group with minimum lo and scale s = (max - lo) / L (q8_scale; L = 255 for 8-bit,
+// 15 for 4-bit codes): the nearest grid point, decided in float32 ((x - lo) / s rounded half to even,
+// clamped to 0..L); a constant group (s = 0) takes code 0.
+template <int BITS = 8>
+CBD_DEVICE float q8_scale(float lo, float hi) { return (hi - lo) / (float)((1 << BITS) - 1); }
+template <int BITS = 8>
 CBD_DEVICE uint32_t q8_code(float x, float lo, float s) {
   if (!(s > 0.f)) return 0u;
-  return (uint32_t)fminf(fmaxf(rintf((x - lo) / s), 0.f), 255.f);
+  return (uint32_t)fminf(fmaxf(rintf((x - lo) / s), 0.f), (float)((1 << BITS) - 1));
 }
 
 // Per-query-row metadata shared by the RoPE/append and attention kernels.

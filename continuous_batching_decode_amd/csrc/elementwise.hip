@@ -137,9 +137,33 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float* qkv, int ld_qkv
   }
 }
 
+// Store the code of (key, dim d) of a K (kv = 0) or V region; lane = d within its group of 64, every
+// lane of the wave calling. 4-bit K: dims d, d + 1 share a byte, written whole by the even lane; 4-bit V:
+// keys kk, kk ^ 1 share a byte, so the nibble is set atomically.
+template <int BITS>
+CBD_DEVICE void store_code(uint8_t* base, int kv, int key, int d, int dh, uint32_t code, int lane) {
+  if constexpr (BITS == 8) {
+    base[kv == 0 ? kq_off(key, d, dh) : vq_off(key, d, dh)] = (uint8_t)code;
+  } else {
+    const uint32_t other = __shfl_xor(code, 1, 64);
+    if (kv == 0) {
+      if ((lane & 1) == 0) base[kq4_off(key, d, dh)] = (uint8_t)(code | (other << 4));
+    } else {
+      store_nibble(base + vq4_off(key, d, dh), vslab_kk(key) & 1, code);
+    }
+  }
+}
+template <int BITS>
+CBD_DEVICE uint32_t load_code(const uint8_t* base, int kv, int key, int d, int dh) {
+  if constexpr (BITS == 8) return base[kv == 0 ? kq_off(key, d, dh) : vq_off(key, d, dh)];
+  const uint32_t b = kv == 0 ? base[kq4_off(key, d, dh)] : base[vq4_off(key, d, dh)];
+  return (b >> (4 * (kv == 0 ? (d & 1) : (vslab_kk(key) & 1)))) & 15u;
+}
+
 // The same for affine 8-bit slabs: queries rotate in place; each (KV head, group of 64 dims) of the
 // row's k (rotated) and v is rounded to bf16 and quantized by one wave (lane = dim), as the
 // quantizing append does.
+template <int BITS>
 __global__ __launch_bounds__(256) void rope_append_q8_kernel(float* qkv, int ld_qkv, const RowMeta* meta, int n_heads,
                                                              int n_kv_heads, int head_dim, int layer, uint8_t* arena,
                                                              const float2* rope_cs) {
@@ -160,7 +184,7 @@ __global__ __launch_bounds__(256) void rope_append_q8_kernel(float* qkv, int ld_
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ng = head_dim / kQGroup, units = 2 * n_kv_heads * ng;
-  const int64_t region = (int64_t)(m.stride / 32) * q8_block_bytes(head_dim);
+  const int64_t region = (int64_t)(m.stride / 32) * q_block_bytes(head_dim, BITS);
   uint8_t* slab = arena + m.slab_off;
   for (int u = wave; u < units; u += 4) {
     const int kv = u / (n_kv_heads * ng), rem = u - kv * n_kv_heads * ng;
@@ -177,9 +201,10 @@ __global__ __launch_bounds__(256) void rope_append_q8_kernel(float* qkv, int ld_
       x = v[j * head_dim + d];
     }
     x = bf16_to_f32(f32_to_bf16(x));
-    const float lo = -wave_max(-x), sc = q8_scale(lo, wave_max(x));
-    base[kv == 0 ? kq_off(m.pos, d, head_dim) : vq_off(m.pos, d, head_dim)] = (uint8_t)q8_code(x, lo, sc);
-    if (lane == 0) *reinterpret_cast<float2*>(base + sbq_off(m.pos, gi, head_dim)) = float2{sc, lo};
+    const float lo = -wave_max(-x), sc = q8_scale<BITS>(lo, wave_max(x));
+    const uint32_t code = q8_code<BITS>(x, lo, sc);
+    store_code<BITS>(base, kv, m.pos, d, head_dim, code, lane);
+    if (lane == 0) *reinterpret_cast<float2*>(base + sbq_off(m.pos, gi, head_dim, BITS)) = float2{sc, lo};
   }
 }
 
@@ -281,28 +306,28 @@ __global__ __launch_bounds__(256) void slab_copy_kernel(uint8_t* arena, int64_t 
 }
 
 // Affine 8-bit slabs: one wave per (token, layer, K or V, KV head, group of 64 dims), lane = dim.
+template <int BITS>
 __global__ __launch_bounds__(256) void slab_q8_kernel(uint8_t* arena, int64_t slab_off, int stride, int pos, int n_all,
                                                       int t_off, int n_kv_heads, int head_dim, const uint16_t* k_in,
                                                       const uint16_t* v_in, uint8_t* codes_out, float* sb_out) {
   const int t = blockIdx.x, l = blockIdx.y, kv = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ng = head_dim / kQGroup, units = n_kv_heads * ng;
-  const int64_t region = (int64_t)(stride / 32) * q8_block_bytes(head_dim);
+  const int64_t region = (int64_t)(stride / 32) * q_block_bytes(head_dim, BITS);
   const int key = pos + t;
   for (int u = wave; u < units; u += 4) {
     const int j = u / ng, gi = u - j * ng, d = gi * kQGroup + lane;
     uint8_t* base = arena + slab_off + ((int64_t)(l * 2 + kv) * n_kv_heads + j) * region;
-    uint8_t* cp = base + (kv == 0 ? kq_off(key, d, head_dim) : vq_off(key, d, head_dim));
-    float2* sbp = reinterpret_cast<float2*>(base + sbq_off(key, gi, head_dim));
+    float2* sbp = reinterpret_cast<float2*>(base + sbq_off(key, gi, head_dim, BITS));
     if (k_in) {
       const uint16_t* in = kv == 0 ? k_in : v_in;
       const float x = bf16_to_f32(in[(((int64_t)l * n_all + t_off + t) * n_kv_heads + j) * head_dim + d]);
-      const float lo = -wave_max(-x), s = q8_scale(lo, wave_max(x));
-      *cp = (uint8_t)q8_code(x, lo, s);
+      const float lo = -wave_max(-x), s = q8_scale<BITS>(lo, wave_max(x));
+      store_code<BITS>(base, kv, key, d, head_dim, q8_code<BITS>(x, lo, s), lane);
       if (lane == 0) *sbp = float2{s, lo};
     } else {
       const int64_t o = (((int64_t)l * n_all + t_off + t) * 2 + kv) * n_kv_heads + j;
-      codes_out[o * head_dim + d] = *cp;
+      codes_out[o * head_dim + d] = (uint8_t)load_code<BITS>(base, kv, key, d, head_dim);
       if (lane == 0) reinterpret_cast<float2*>(sb_out)[o * ng + gi] = *sbp;
     }
   }
@@ -337,10 +362,11 @@ hipError_t launch_rope_append(float* qkv, int ld_qkv, const RowMeta* meta, int r
 }
 
 hipError_t launch_rope_append_q8(float* qkv, int ld_qkv, const RowMeta* meta, int rows, int n_heads, int n_kv_heads,
-                                 int head_dim, int layer, uint8_t* arena, const float* rope_cs, hipStream_t st) {
-  if (head_dim % kQGroup) return hipErrorInvalidValue;
-  launch_kernel(rope_append_q8_kernel, dim3(rows), dim3(256), 0, st, qkv, ld_qkv, meta, n_heads, n_kv_heads,
-                head_dim, layer, arena, reinterpret_cast<const float2*>(rope_cs));
+                                 int head_dim, int layer, uint8_t* arena, const float* rope_cs, int bits,
+                                 hipStream_t st) {
+  if (head_dim % kQGroup || (bits != 8 && bits != 4)) return hipErrorInvalidValue;
+  launch_kernel(bits == 8 ? rope_append_q8_kernel<8> : rope_append_q8_kernel<4>, dim3(rows), dim3(256), 0, st, qkv,
+                ld_qkv, meta, n_heads, n_kv_heads, head_dim, layer, arena, reinterpret_cast<const float2*>(rope_cs));
   return hipGetLastError();
 }
 
@@ -365,10 +391,10 @@ hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int po
 
 hipError_t launch_slab_q8(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_all, int t_off,
                           int n_layers, int n_kv_heads, int head_dim, const uint16_t* k_in, const uint16_t* v_in,
-                          uint8_t* codes_out, float* sb_out, hipStream_t st) {
-  if (head_dim % kQGroup || stride % 32) return hipErrorInvalidValue;
-  launch_kernel(slab_q8_kernel, dim3(n, n_layers, 2), dim3(256), 0, st, arena, slab_off, stride, pos, n_all, t_off,
-                n_kv_heads, head_dim, k_in, v_in, codes_out, sb_out);
+                          uint8_t* codes_out, float* sb_out, int bits, hipStream_t st) {
+  if (head_dim % kQGroup || stride % 32 || (bits != 8 && bits != 4)) return hipErrorInvalidValue;
+  launch_kernel(bits == 8 ? slab_q8_kernel<8> : slab_q8_kernel<4>, dim3(n, n_layers, 2), dim3(256), 0, st, arena,
+                slab_off, stride, pos, n_all, t_off, n_kv_heads, head_dim, k_in, v_in, codes_out, sb_out);
   return hipGetLastError();
 }
 

@@ -114,7 +114,8 @@ hipError_t launch_rope_append(float* qkv, int ld_qkv, const RowMeta* meta, int r
                               int head_dim, int layer, uint8_t* arena, const float* rope_cs, hipStream_t st);
 // the same for affine 8-bit slabs (k and v quantized per KV head and group of 64 dims)
 hipError_t launch_rope_append_q8(float* qkv, int ld_qkv, const RowMeta* meta, int rows, int n_heads, int n_kv_heads,
-                                 int head_dim, int layer, uint8_t* arena, const float* rope_cs, hipStream_t st);
+                                 int head_dim, int layer, uint8_t* arena, const float* rope_cs, int bits,
+                                 hipStream_t st);
 // Attention of each item's query row over its key range of the row's slab.
 struct AttnArgs {
   const float* qkv;          // projections [rows, ld_qkv]: q heads, then k heads, then v heads
@@ -139,8 +140,8 @@ hipError_t launch_decode_attention(const AttnArgs& a, int n_items, int head_dim,
 hipError_t launch_prefill_attention(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
 // decode over affine 8-bit slabs (same items, splits and outputs as launch_decode_attention; the
 // appending item quantizes the new token's K/V into the slab)
-hipError_t launch_decode_attention_q8(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
-hipError_t launch_prefill_attention_q8(const AttnArgs& a, int n_items, int head_dim, hipStream_t st);
+hipError_t launch_decode_attention_q8(const AttnArgs& a, int n_items, int head_dim, int bits, hipStream_t st);
+hipError_t launch_prefill_attention_q8(const AttnArgs& a, int n_items, int head_dim, int bits, hipStream_t st);
 
 // greedy argmax per row, lowest id on ties
 // part: kArgmaxSegments x 64 (max, index) pairs; counters: 64 ints, zero between launches
@@ -180,6 +181,6 @@ hipError_t launch_slab_copy(uint8_t* arena, int64_t slab_off, int stride, int po
 // [L, n_all, 2, Hkv, Dh/64, 2] back (codes_out, sb_out)
 hipError_t launch_slab_q8(uint8_t* arena, int64_t slab_off, int stride, int pos, int n, int n_all, int t_off,
                           int n_layers, int n_kv_heads, int head_dim, const uint16_t* k_in, const uint16_t* v_in,
-                          uint8_t* codes_out, float* sb_out, hipStream_t st);
+                          uint8_t* codes_out, float* sb_out, int bits, hipStream_t st);
 
 }  // namespace cbd

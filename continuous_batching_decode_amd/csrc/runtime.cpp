@@ -97,7 +97,7 @@ struct cbd_ctx {
   cbd_model_config cfg{};
   cbd_limits lim{};
   int fmt = FMT_BF16;
-  bool kv8 = false;  // affine 8-bit slabs
+  int kv_bits = 0;  // affine slabs: 8- or 4-bit codes (0: bf16 slabs)
   int q_dim = 0, kv_dim = 0, qkv_dim = 0;
   const uint16_t* embed = nullptr;
   const uint16_t* final_norm = nullptr;
@@ -205,7 +205,8 @@ bool valid_model(const cbd_model_config* m, std::string* why) {
   }
   if (m->vocab % 64 || (m->n_kv_heads * m->head_dim) % 64) return bad("vocab and kv width must be multiples of 64");
   if (m->max_position < 1) return bad("max_position must be positive");
-  if (m->kv_format != CBD_KV_BF16 && m->kv_format != CBD_KV_AFFINE8) return bad("unknown kv_format");
+  if (m->kv_format != CBD_KV_BF16 && m->kv_format != CBD_KV_AFFINE8 && m->kv_format != CBD_KV_AFFINE4)
+    return bad("unknown kv_format");
   if (!(m->rms_eps >= 0.f) || !(m->rope_theta > 0.f)) return bad("rms_eps >= 0 and rope_theta > 0 required");
   return true;
 }
@@ -321,8 +322,9 @@ struct ProfScope {
 
 extern "C" size_t cbd_kv_bytes_per_token(const cbd_model_config* cfg) {
   if (!cfg) return 0;
-  if (cfg->kv_format == CBD_KV_AFFINE8)
-    return (size_t)cfg->n_layers * 2 * cfg->n_kv_heads * (cfg->head_dim + cfg->head_dim / kQGroup * 8);
+  if (cfg->kv_format == CBD_KV_AFFINE8 || cfg->kv_format == CBD_KV_AFFINE4)
+    return (size_t)cfg->n_layers * 2 * cfg->n_kv_heads *
+           (cfg->head_dim * (cfg->kv_format == CBD_KV_AFFINE8 ? 8 : 4) / 8 + cfg->head_dim / kQGroup * 8);
   return (size_t)cfg->n_layers * 2 * cfg->n_kv_heads * cfg->head_dim * 2;
 }
 
@@ -479,7 +481,7 @@ extern "C" cbd_status cbd_create(const cbd_model_config* cfg, const cbd_weights*
   c->lim = *limits;
   c->host_only = limits->host_only != 0;
   c->fmt = cfg->weight_format == CBD_WEIGHTS_INT4 ? FMT_INT4 : FMT_BF16;
-  c->kv8 = cfg->kv_format == CBD_KV_AFFINE8;
+  c->kv_bits = cfg->kv_format == CBD_KV_AFFINE8 ? 8 : cfg->kv_format == CBD_KV_AFFINE4 ? 4 : 0;
   c->q_dim = cfg->n_heads * cfg->head_dim;
   c->kv_dim = cfg->n_kv_heads * cfg->head_dim;
   c->qkv_dim = c->q_dim + 2 * c->kv_dim;
@@ -598,7 +600,7 @@ extern "C" cbd_status kvslab_alloc(cbd_ctx* c, int32_t capacity_tokens, int32_t*
 
 // Bytes of one block of 32 keys in one (layer, K or V, KV head) region, and of a whole region.
 static int64_t kv_block_bytes(const cbd_ctx* c) {
-  return c->kv8 ? q8_block_bytes(c->cfg.head_dim) : (int64_t)32 * c->cfg.head_dim * 2;
+  return c->kv_bits ? q_block_bytes(c->cfg.head_dim, c->kv_bits) : (int64_t)32 * c->cfg.head_dim * 2;
 }
 static int64_t kv_region_bytes(const cbd_ctx* c, int32_t stride) { return (int64_t)(stride / 32) * kv_block_bytes(c); }
 
@@ -705,10 +707,11 @@ extern "C" cbd_status kvslab_append(cbd_ctx* c, int32_t seq_id, int32_t n_tokens
     return fail(CBD_E_INVAL, "kvslab_append: K/V must be 16-byte aligned device pointers");
   if (c->host_only) return fail(CBD_E_NODEVICE, "kvslab_append: host-only context");
   const int64_t off = row_meta(c, *s, s->len).slab_off;  // positions >= len >= base: the own part
-  if (c->kv8)
+  if (c->kv_bits)
     HIP_TRY(launch_slab_q8(c->arena, off, s->stride, s->len, n_tokens, n_tokens, 0, c->cfg.n_layers,
                            c->cfg.n_kv_heads, c->cfg.head_dim, static_cast<const uint16_t*>(k_dev),
-                           static_cast<const uint16_t*>(v_dev), nullptr, nullptr, static_cast<hipStream_t>(stream)),
+                           static_cast<const uint16_t*>(v_dev), nullptr, nullptr, c->kv_bits,
+                           static_cast<hipStream_t>(stream)),
             "kvslab_append launch");
   else
     HIP_TRY(launch_slab_copy(c->arena, off, s->stride, s->len, n_tokens, n_tokens, 0, c->cfg.n_layers,
@@ -722,7 +725,7 @@ extern "C" cbd_status kvslab_append(cbd_ctx* c, int32_t seq_id, int32_t n_tokens
 extern "C" cbd_status kvslab_read(const cbd_ctx* c, int32_t seq_id, int32_t start, int32_t n_tokens, void* k_out_dev,
                                   void* v_out_dev, cbd_stream stream) {
   if (!c) return fail(CBD_E_INVAL, "kvslab_read: null context");
-  if (c->kv8) return fail(CBD_E_UNSUPPORTED, "kvslab_read: affine 8-bit slabs are read with kvslab_read_q8");
+  if (c->kv_bits) return fail(CBD_E_UNSUPPORTED, "kvslab_read: affine slabs are read with kvslab_read_q8");
   const Slab* s;
   if (cbd_status st = live_slab(c, seq_id, &s)) return st;
   if (start < 0 || n_tokens < 0) return fail(CBD_E_INVAL, "kvslab_read: negative range");
@@ -751,7 +754,7 @@ extern "C" cbd_status kvslab_read(const cbd_ctx* c, int32_t seq_id, int32_t star
 extern "C" cbd_status kvslab_read_q8(const cbd_ctx* c, int32_t seq_id, int32_t start, int32_t n_tokens,
                                      void* codes_out_dev, void* sb_out_dev, cbd_stream stream) {
   if (!c) return fail(CBD_E_INVAL, "kvslab_read_q8: null context");
-  if (!c->kv8) return fail(CBD_E_UNSUPPORTED, "kvslab_read_q8: the context stores bf16 slabs");
+  if (!c->kv_bits) return fail(CBD_E_UNSUPPORTED, "kvslab_read_q8: the context stores bf16 slabs");
   const Slab* s;
   if (cbd_status st = live_slab(c, seq_id, &s)) return st;
   if (start < 0 || n_tokens < 0) return fail(CBD_E_INVAL, "kvslab_read_q8: negative range");
@@ -766,12 +769,12 @@ extern "C" cbd_status kvslab_read_q8(const cbd_ctx* c, int32_t seq_id, int32_t s
   if (cut > start)
     HIP_TRY(launch_slab_q8(c->arena, m.pre_off, m.pre_stride, start, cut - start, n_tokens, 0, c->cfg.n_layers,
                            c->cfg.n_kv_heads, c->cfg.head_dim, nullptr, nullptr, static_cast<uint8_t*>(codes_out_dev),
-                           static_cast<float*>(sb_out_dev), static_cast<hipStream_t>(stream)),
+                           static_cast<float*>(sb_out_dev), c->kv_bits, static_cast<hipStream_t>(stream)),
             "kvslab_read_q8 launch");
   if (end > cut)
     HIP_TRY(launch_slab_q8(c->arena, m.slab_off, s->stride, cut, end - cut, n_tokens, cut - start, c->cfg.n_layers,
                            c->cfg.n_kv_heads, c->cfg.head_dim, nullptr, nullptr, static_cast<uint8_t*>(codes_out_dev),
-                           static_cast<float*>(sb_out_dev), static_cast<hipStream_t>(stream)),
+                           static_cast<float*>(sb_out_dev), c->kv_bits, static_cast<hipStream_t>(stream)),
             "kvslab_read_q8 launch");
   return CBD_OK;
 }
@@ -867,9 +870,10 @@ cbd_status run_layers(cbd_ctx* c, int rows, int x_blocks, const RowMeta* meta_d,
     const bool fused = row_parts_d != nullptr;
     if (!fused) {
       ProfScope p(c, CBD_KERNEL_ROPE_APPEND, (double)rows * (c->qkv_dim * 4.0 + c->q_dim * 4.0 + c->kv_dim * 4.0), 0, st);
-      HIP_TRY((c->kv8 ? launch_rope_append_q8 : launch_rope_append)(c->qkv, c->qkv_dim, meta_d, rows, m.n_heads,
-                                                                      m.n_kv_heads, m.head_dim, l, c->arena,
-                                                                      c->rope_cs, st),
+      HIP_TRY(c->kv_bits ? launch_rope_append_q8(c->qkv, c->qkv_dim, meta_d, rows, m.n_heads, m.n_kv_heads,
+                                                 m.head_dim, l, c->arena, c->rope_cs, c->kv_bits, st)
+                         : launch_rope_append(c->qkv, c->qkv_dim, meta_d, rows, m.n_heads, m.n_kv_heads, m.head_dim,
+                                              l, c->arena, c->rope_cs, st),
               "rope/append");
     }
     {
@@ -890,13 +894,13 @@ cbd_status run_layers(cbd_ctx* c, int rows, int x_blocks, const RowMeta* meta_d,
       at.part_ml = c->part_ml;
       at.row_parts = reinterpret_cast<const int2*>(row_parts_d);
       at.counters = c->attn_counters;
-      const double kvb = kv_keys * (c->kv8 ? m.n_kv_heads * (m.head_dim + m.head_dim / kQGroup * 8.0) * 2.0
+      const double kvb = kv_keys * (c->kv_bits ? m.n_kv_heads * (m.head_dim * c->kv_bits / 8.0 + m.head_dim / kQGroup * 8.0) * 2.0
                                            : c->kv_dim * 2.0 * 2.0);
       ProfScope p(c, CBD_KERNEL_ATTENTION, kvb + (double)rows * c->q_dim * (4.0 + 4.0) + n_parts * 0.0,
                   kv_keys * m.n_heads * m.head_dim * 4.0, st);
-      HIP_TRY(fused ? (c->kv8 ? launch_decode_attention_q8(at, n_items, m.head_dim, st)
+      HIP_TRY(fused ? (c->kv_bits ? launch_decode_attention_q8(at, n_items, m.head_dim, c->kv_bits, st)
                               : launch_decode_attention(at, n_items, m.head_dim, st))
-                    : (c->kv8 ? launch_prefill_attention_q8(at, n_items, m.head_dim, st)
+                    : (c->kv_bits ? launch_prefill_attention_q8(at, n_items, m.head_dim, c->kv_bits, st)
                               : launch_prefill_attention(at, n_items, m.head_dim, st)),
               "attention");
     }

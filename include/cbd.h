@@ -94,8 +94,10 @@ enum { CBD_WEIGHTS_BF16 = 0, CBD_WEIGHTS_INT4 = 1 };
  *                  attend to the stored, quantized keys of their own segment) and kvslab_append
  *                  quantize on append; kvslab_read returns CBD_E_UNSUPPORTED (kvslab_read_q8 reads
  *                  the stored form).
+ *  CBD_KV_AFFINE4: the same with 4-bit codes (maximum code 15, scale = (maximum - bias) / 15), two
+ *                  per byte: 80 bytes per token, layer and KV head at head_dim 128.
  */
-enum { CBD_KV_BF16 = 0, CBD_KV_AFFINE8 = 1 };
+enum { CBD_KV_BF16 = 0, CBD_KV_AFFINE8 = 1, CBD_KV_AFFINE4 = 2 };
 
 typedef struct {
   int32_t n_layers;
@@ -109,7 +111,7 @@ typedef struct {
   float rope_theta;
   int32_t weight_format; /* CBD_WEIGHTS_BF16 or CBD_WEIGHTS_INT4 */
   int32_t max_position;  /* length of the RoPE table: no slab may grow beyond it */
-  int32_t kv_format;     /* CBD_KV_BF16 (0) or CBD_KV_AFFINE8 (1) */
+  int32_t kv_format;     /* CBD_KV_BF16 (0), CBD_KV_AFFINE8 (1) or CBD_KV_AFFINE4 (2) */
 } cbd_model_config;
 
 /*
@@ -165,8 +167,8 @@ typedef struct {
 } cbd_stats_t;
 
 /* Bytes of K and V one token occupies in a slab, over all layers: n_layers * 2 * n_kv_heads *
- * head_dim * 2 for bf16 slabs, n_layers * 2 * n_kv_heads * (head_dim + head_dim / 64 * 8) for
- * affine 8-bit slabs. */
+ * head_dim * 2 for bf16 slabs, n_layers * 2 * n_kv_heads * (head_dim * b / 8 + head_dim / 64 * 8)
+ * for affine slabs of b-bit codes (b = 8 or 4). */
 size_t cbd_kv_bytes_per_token(const cbd_model_config* cfg);
 
 /* Tokens per arena granule: slab capacities are rounded up to a multiple. */
@@ -249,8 +251,9 @@ cbd_status kvslab_read(const cbd_ctx* ctx, int32_t seq_id, int32_t start, int32_
                        void* k_out_dev, void* v_out_dev, cbd_stream stream);
 
 /*
- * Read tokens [start, start + n) of an affine 8-bit slab in its stored form:
- *  codes_out_dev  device uint8 [L, n, 2, n_kv_heads, head_dim] (index 2: 0 = K, 1 = V)
+ * Read tokens [start, start + n) of an affine slab (8- or 4-bit codes) in its stored form:
+ *  codes_out_dev  device uint8 [L, n, 2, n_kv_heads, head_dim] (index 2: 0 = K, 1 = V), one code
+ *                 per byte
  *  sb_out_dev     device float32 [L, n, 2, n_kv_heads, head_dim / 64, 2] (scale, bias)
  * Both 16-byte aligned, caller-owned. CBD_E_UNSUPPORTED on a bf16 context, CBD_E_CAPACITY if
  * start + n > len. For tests and for moving a quantized history out of the arena.

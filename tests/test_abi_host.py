@@ -203,6 +203,7 @@ def test_affine8_kv_format_host(cbd):
     assert cbd.kv_bytes_per_token(synth.LLAMA8B, "affine8") == 32 * 2 * 8 * (128 + 2 * 8)
     assert cbd.kv_bytes_per_token(synth.TINY, "affine8") == 2 * 2 * 2 * (64 + 8)
     assert cbd.kv_bytes_per_token(synth.LLAMA8B, "bf16") == synth.LLAMA8B.kv_bytes_per_token()
+    assert cbd.kv_bytes_per_token(synth.LLAMA8B, "affine4") == 32 * 2 * 8 * (64 + 2 * 8)
     g = cbd.lib().cbd_slab_granule_tokens()
     per_tok = cbd.kv_bytes_per_token(synth.TINY, "affine8")
     e = cbd.Engine({"shape": synth.TINY}, arena_bytes=4 * g * per_tok, host_only=True, max_position=4096,

@@ -37,7 +37,7 @@ def to_dev_bits(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
 
 
-@pytest.mark.parametrize("kv_format", ["bf16", "affine8"])
+@pytest.mark.parametrize("kv_format", ["bf16", "affine8", "affine4"])
 def test_fork_prefill_decode_and_parent_retired(torch, cbd, kv_format):
     """Parent prefilled with 90 tokens; forks at 75 (boundary block copied, holding parent keys past the
     prefix), 64 (whole blocks only) and 0; each fork prefills its own rest, then mixed decode steps with
@@ -102,13 +102,12 @@ def test_fork_prefill_decode_and_parent_retired(torch, cbd, kv_format):
             compare_slab_bits(k.cpu().numpy(), np.stack(orc.seqs[of].k), "K")
             compare_slab_bits(v.cpu().numpy(), np.stack(orc.seqs[of].v), "V")
         else:
+            from test_gpu_kv8 import check_appended
             codes, sb = eng.kvslab_read_q8(f, 0, n)
             torch.cuda.synchronize()
             s = orc.seqs[of]
-            got = dequantize_affine8(codes.cpu().numpy()[:, :, 0], sb.cpu().numpy()[:, :, 0])
-            want = dequantize_affine8(np.stack(s.k), np.stack(s.k_sb))
-            for l in range(shape.n_layers):
-                assert np.max(np.abs(got[l] - want[l])) <= LOGIT_RTOL * np.max(np.abs(want[l]))
+            check_appended(kv_format, codes.cpu().numpy()[:, :, 0], sb.cpu().numpy()[:, :, 0], np.stack(s.k),
+                           np.stack(s.k_sb), "fork K")
     for f, _, _ in forks:
         eng.free(f)
     eng.free(solo)

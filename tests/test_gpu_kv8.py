@@ -1,4 +1,4 @@
-"""GPU parity of affine 8-bit K/V slabs against the oracle.
+"""GPU parity of affine 8-bit and 4-bit K/V slabs against the oracle.
 
 Codes and (scale, bias) pairs are integer / float32 decisions from identical bf16 inputs, so the
 appended history must match the oracle's quantization bit for bit; decode logits follow the logit
@@ -38,9 +38,37 @@ def to_dev_bits(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
 
 
-def _engine(cbd, w, shape, tokens, **kw):
-    per_tok = cbd.kv_bytes_per_token(shape, "affine8")
-    return cbd.Engine(w, arena_bytes=tokens * per_tok, kv_format="affine8", **kw)
+FORMATS = ["affine8", "affine4"]
+
+
+def _engine(cbd, w, shape, tokens, fmt="affine8", **kw):
+    per_tok = cbd.kv_bytes_per_token(shape, fmt)
+    return cbd.Engine(w, arena_bytes=tokens * per_tok, kv_format=fmt, **kw)
+
+
+def _quantize(fmt, x):
+    from oracle.kvquant import quantize_affine
+    return quantize_affine(x, 64, 8 if fmt == "affine8" else 4)
+
+
+def check_appended(fmt, got_codes, got_sb, want_codes, want_sb, what):
+    """K or V of tokens the GPU appended itself ([L, n, Hkv, Dh] codes, [L, n, Hkv, Dh/64, 2] pairs).
+    Their bf16 inputs come from the GPU's own projection and may differ from the oracle's by an ulp, which
+    can move a code across a rounding boundary: every dequantized value lies within one code step of the
+    oracle's (8-bit codes: within the slab rule of the bf16 tests), and few values differ by more than
+    1e-2 of the layer's largest."""
+    from oracle import dequantize_affine8
+    got = dequantize_affine8(got_codes, got_sb)
+    want = dequantize_affine8(want_codes, want_sb)
+    step = np.repeat(np.asarray(want_sb, dtype=np.float64)[..., 0], 64, axis=-1)
+    for l in range(got.shape[0]):
+        big = LOGIT_RTOL * np.max(np.abs(want[l]))
+        err = np.abs(got[l] - want[l])
+        if fmt == "affine8":
+            assert np.max(err) <= big, "%s layer %d: %.4g" % (what, l, np.max(err))
+        else:
+            assert np.all(err <= step[l] * 1.01 + 1e-3 * big / LOGIT_RTOL), "%s layer %d: beyond one step" % (what, l)
+            assert np.mean(err > big) <= 0.05, "%s layer %d: %.3f of the values off" % (what, l, np.mean(err > big))
 
 
 def _special_history(shape, n, seed):
@@ -68,12 +96,12 @@ def _special_history(shape, n, seed):
     return k, v
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("shape", [synth.TINY, MID], ids=["dh64-g2", "dh128-g4"])
-def test_kv8_append_matches_oracle_quantization(torch, cbd, shape):
-    from oracle import quantize_affine8
-    _say("kv8 append codes", shape.name)
+def test_kv8_append_matches_oracle_quantization(torch, cbd, shape, fmt):
+    _say("kv append codes", shape.name, fmt)
     w = synth.make_weights(shape, seed=1)
-    eng = _engine(cbd, w, shape, 8 * 256, max_position=4096)
+    eng = _engine(cbd, w, shape, 8 * 256, fmt, max_position=4096)
     a, b = eng.alloc(700), eng.alloc(300)
     k, v = _special_history(shape, 650, 21)
     # appends of ragged sizes that end inside a 32-key block and across a 256-token granule
@@ -86,7 +114,7 @@ def test_kv8_append_matches_oracle_quantization(torch, cbd, shape):
         torch.cuda.synchronize()
         codes, sb = codes.cpu().numpy(), sb.cpu().numpy()
         for which, x in ((0, kk), (1, vv)):
-            rc, rsb = quantize_affine8(x[:, start:start + n])
+            rc, rsb = _quantize(fmt, x[:, start:start + n])
             assert np.array_equal(codes[:, :, which], rc), "codes %d" % which
             assert np.array_equal(sb[:, :, which].view(np.uint32), rsb.view(np.uint32)), "pairs %d" % which
     with pytest.raises(cbd.CbdError) as ei:
@@ -95,15 +123,16 @@ def test_kv8_append_matches_oracle_quantization(torch, cbd, shape):
     eng.close()
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("shape", [MID, synth.TINY], ids=["dh128-g4", "dh64-g2"])
-def test_kv8_ragged_decode_matches_oracle(torch, cbd, shape):
+def test_kv8_ragged_decode_matches_oracle(torch, cbd, shape, fmt):
     """Ragged histories (one-item and split rows), three teacher-forced decode steps."""
     from oracle import OracleModel, dequantize_affine8, greedy
-    _say("kv8 ragged decode", shape.name)
+    _say("kv ragged decode", shape.name, fmt)
     w = synth.make_weights(shape, seed=3, gain_std=0.1)
     ctx = [0, 1, 31, 32, 33, 700, 2999, 4095]
-    eng = _engine(cbd, w, shape, 64 * 256, max_batch=16, max_prefill_tokens=64, max_position=8192)
-    orc = OracleModel(w, cache_all_layers=True, kv_format="affine8")
+    eng = _engine(cbd, w, shape, 64 * 256, fmt, max_batch=16, max_prefill_tokens=64, max_position=8192)
+    orc = OracleModel(w, cache_all_layers=True, kv_format=fmt)
     ids, oids = [], []
     for r, n in enumerate(ctx):
         i = eng.alloc(n + 4)
@@ -122,7 +151,17 @@ def test_kv8_ragged_decode_matches_oracle(torch, cbd, shape):
         eng.decode_step_batch(ids, torch.from_numpy(tok.astype(np.int32)).cuda(), logits, nxt)
         ref = orc.decode_step_batch(oids, tok)
         torch.cuda.synchronize()
-        errs = assert_logits_close(logits.cpu().numpy(), ref, "step %d" % step)
+        got = logits.cpu().numpy()
+        if fmt == "affine4":
+            # A new token's bf16 K/V may differ from the oracle's by an ulp (its projection), and with 4-bit
+            # codes that can move one code by a step of 1/15 of its group's range. Rows with fewer than 64
+            # keys attend to such a token with a large weight, so they take twice the logit rule.
+            errs = np.max(np.abs(got - ref), axis=1)
+            for r, n in enumerate(ctx):
+                bound = (2 if n < 64 else 1) * LOGIT_RTOL * np.max(np.abs(ref[r]))
+                assert errs[r] <= bound, "step %d row %d: %.4g > %.4g" % (step, r, errs[r], bound)
+        else:
+            errs = assert_logits_close(got, ref, "step %d" % step)
         check_greedy(nxt.cpu().numpy(), ref, errs, "step %d" % step)
         tok = greedy(ref)
     for r, (i, o, n) in enumerate(zip(ids, oids, ctx)):
@@ -132,28 +171,26 @@ def test_kv8_ragged_decode_matches_oracle(torch, cbd, shape):
         if n:  # the history is untouched by the steps
             assert np.array_equal(codes[:, :n], before[r][0].cpu().numpy())
             assert np.array_equal(sb[:, :n], before[r][1].cpu().numpy())
-        # the three appended tokens: dequantized values within the slab rule of the bf16 tests
+        # the three appended tokens
         s = orc.seqs[o]
         for which, oc, osb in ((0, s.k, s.k_sb), (1, s.v, s.v_sb)):
-            got = dequantize_affine8(codes[:, n:, which], sb[:, n:, which])
-            want = dequantize_affine8(np.stack(oc)[:, n:], np.stack(osb)[:, n:])
-            for l in range(shape.n_layers):
-                err = np.max(np.abs(got[l] - want[l]))
-                assert err <= LOGIT_RTOL * np.max(np.abs(want[l])), "row %d layer %d kv %d: %.4g" % (r, l, which, err)
+            check_appended(fmt, codes[:, n:, which], sb[:, n:, which], np.stack(oc)[:, n:], np.stack(osb)[:, n:],
+                           "row %d kv %d" % (r, which))
             assert np.all(codes[:, n:, which].reshape(-1, 64).min(axis=1) == 0)  # min of each group -> 0
     eng.close()
 
 
-def test_kv8_long_context_sampled_rows(torch, cbd):
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_kv8_long_context_sampled_rows(torch, cbd, fmt):
     """Llama-3-8B attention shape (32 query / 8 KV heads, Dh 128) at long contexts, one layer, three
     rows of different lengths (many splits per row); a decode step against the oracle."""
     from oracle import OracleModel
-    _say("kv8 long context")
+    _say("kv long context", fmt)
     shape = synth.ModelShape("kv8-long", 1, 4096, 32, 8, 128, 512, 1024, 500000.0)
     w = synth.make_weights(shape, seed=5, gain_std=0.1)
     ctx = [32767, 9000, 511]
-    eng = _engine(cbd, w, shape, sum((c + 256) // 256 * 256 for c in ctx), max_batch=8, max_position=32768)
-    orc = OracleModel(w, cache_all_layers=True, kv_format="affine8")
+    eng = _engine(cbd, w, shape, sum((c + 256) // 256 * 256 for c in ctx), fmt, max_batch=8, max_position=32768)
+    orc = OracleModel(w, cache_all_layers=True, kv_format=fmt)
     ids, oids = [], []
     for r, n in enumerate(ctx):
         i = eng.alloc(n + 1)
@@ -172,17 +209,18 @@ def test_kv8_long_context_sampled_rows(torch, cbd):
     eng.close()
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("shape", [MID, synth.TINY], ids=["dh128-g4", "dh64-g2"])
-def test_kv8_prefill_continuation_and_decode(torch, cbd, shape):
+def test_kv8_prefill_continuation_and_decode(torch, cbd, shape, fmt):
     """Segmented prefill into affine 8-bit slabs (mixed lengths, one segment continuing its sequence in a
     second call after decode steps), every call's logits and the stored K/V against the oracle."""
     from oracle import OracleModel, dequantize_affine8, greedy
-    _say("kv8 prefill", shape.name)
+    _say("kv prefill", shape.name, fmt)
     w = synth.make_weights(shape, seed=7, gain_std=0.1)
     lens = [1, 31, 32, 33, 100, 115]
     prompts = synth.prompts(23, lens + [45], shape.vocab)
-    eng = _engine(cbd, w, shape, 16 * 256, max_batch=8, max_prefill_tokens=512, max_position=1024)
-    orc = OracleModel(w, cache_all_layers=True, kv_format="affine8")
+    eng = _engine(cbd, w, shape, 16 * 256, fmt, max_batch=8, max_prefill_tokens=512, max_position=1024)
+    orc = OracleModel(w, cache_all_layers=True, kv_format=fmt)
     ids = [eng.alloc(256) for _ in lens]
     oids = [orc.new_sequence() for _ in lens]
 
@@ -215,9 +253,6 @@ def test_kv8_prefill_continuation_and_decode(torch, cbd, shape):
         codes, sb = codes.cpu().numpy(), sb.cpu().numpy()
         s = orc.seqs[oids[r]]
         for which, oc, osb in ((0, s.k, s.k_sb), (1, s.v, s.v_sb)):
-            got = dequantize_affine8(codes[:, :, which], sb[:, :, which])
-            want = dequantize_affine8(np.stack(oc), np.stack(osb))
-            for l in range(shape.n_layers):
-                err = np.max(np.abs(got[l] - want[l]))
-                assert err <= LOGIT_RTOL * np.max(np.abs(want[l])), "row %d layer %d kv %d: %.4g" % (r, l, which, err)
+            check_appended(fmt, codes[:, :, which], sb[:, :, which], np.stack(oc), np.stack(osb),
+                           "row %d kv %d" % (r, which))
     eng.close()
