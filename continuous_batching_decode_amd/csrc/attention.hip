@@ -625,12 +625,17 @@ CBD_DEVICE bf16x8_t code_frag(const u32x4_t& w, int half) {
 }
 
 // fragment q (0..3) of a 4-bit code word as 8 bf16 operands 128 + code: bf16 holds 128 + n (n < 128)
-// with exponent 7 and mantissa n, so the pattern is 0x4300 | n (exact)
+// with exponent 7 and mantissa n, so the pattern is 0x4300 | n (exact). Elements 0..3 are the low
+// nibbles of the fragment's 4 bytes and 4..7 the high ones: two masks, then one byte permute (with
+// 0x43 bytes from a constant) per pair of elements.
 CBD_DEVICE bf16x8_t code_frag4(const u32x4_t& w, int q) {
   const uint32_t x = w[q];
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
   u32x4_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = 0x43004300u | ((x >> (8 * i)) & 15u) | (((x >> (8 * i + 4)) & 15u) << 16);
+  r[0] = __builtin_amdgcn_perm(0x43434343u, lo, 0x04010400u);  // bytes lo.0, 0x43, lo.1, 0x43
+  r[1] = __builtin_amdgcn_perm(0x43434343u, lo, 0x04030402u);  // lo.2, 0x43, lo.3, 0x43
+  r[2] = __builtin_amdgcn_perm(0x43434343u, hi, 0x04010400u);
+  r[3] = __builtin_amdgcn_perm(0x43434343u, hi, 0x04030402u);
   return as_frag(r);
 }
 
@@ -877,7 +882,7 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
       for (int e = 0; e < 8; ++e) {
         const uint32_t code = q8_code<BITS>(kvals[u][e], klo[gi], ks[gi]);
         if constexpr (BITS == 8) cw[e >> 2] |= code << (8 * (e & 3));
-        else cw[0] |= code << (4 * e);
+        else cw[0] |= code << (8 * (e & 3) + 4 * (e >> 2));
         const uint32_t qb = e & 1 ? qhu[e >> 1] >> 16 : qhu[e >> 1] & 0xFFFFu;
         const uint32_t lb = e & 1 ? qlu[e >> 1] >> 16 : qlu[e >> 1] & 0xFFFFu;
         dot += (bf16_to_f32(qb) + bf16_to_f32(lb)) * fmaf(ks[gi], (float)code, klo[gi]);
@@ -924,7 +929,7 @@ __global__ __launch_bounds__(64 * kAttnWgWaves, 2) void decode_attention_q8_kern
         st.o[t][e] = fmaf(vs[gi], (float)code, vlo[gi]);
         if (c16 == 0) {
           if constexpr (BITS == 8) vbase[vq_off(pos, 16 * t + 4 * g + e, DH)] = (uint8_t)code;
-          else store_nibble(vbase + vq4_off(pos, 16 * t + 4 * g + e, DH), vslab_kk(pos) & 1, code);
+          else store_nibble(vbase + vq4_off(pos, 16 * t + 4 * g + e, DH), (vslab_kk(pos) >> 2) & 1, code);
         }
       }
     if (lane == 0)

@@ -111,9 +111,10 @@ CBD_DEVICE int64_t vslab_off(int key, int d, int dh) {
 //  records: key kk of the V order (vslab_kk) at byte 32 * Dh + kk * (Dh/64) * 8, group after group.
 //     Lane group g = l/16 owns keys kk = 8g .. 8g + 7: exactly the keys whose scores it holds.
 //
-// Affine 4-bit slabs: the same blocks with 16 * Dh code bytes, two codes per byte (the lower element of
-// the fragment order in the low nibble): a fragment's 8 codes are 4 bytes, and 16-byte word i of lane
-// l (byte 1024 i + 16 l) holds fragments 4i .. 4i + 3, fragment f at bytes 4 (f % 4) .. +3.
+// Affine 4-bit slabs: the same blocks with 16 * Dh code bytes, two codes per byte: a fragment's 8 codes
+// are 4 bytes, element e in byte e % 4, low nibble for e < 4 and high nibble for e >= 4 (so one mask
+// gives elements 0..3 and a shift and mask elements 4..7, each already one per byte); 16-byte word i
+// of lane l (byte 1024 i + 16 l) holds fragments 4i .. 4i + 3, fragment f at bytes 4 (f % 4) .. +3.
 constexpr int kQGroup = 64;
 __host__ __device__ constexpr int q_block_bytes(int dh, int bits) { return 32 * dh * bits / 8 + 32 * (dh / kQGroup) * 8; }
 __host__ __device__ constexpr int q8_block_bytes(int dh) { return q_block_bytes(dh, 8); }
@@ -131,19 +132,19 @@ CBD_DEVICE int64_t sbq_off(int key, int gi, int dh, int bits = 8) {
   return (int64_t)(key >> 5) * q_block_bytes(dh, bits) + 32 * dh * bits / 8 +
          ((int64_t)vslab_kk(key) * (dh / kQGroup) + gi) * 8;
 }
-// 4-bit codes: byte offset of (key, d); the code is its low nibble when (K: d, V: kk) is even
+// 4-bit codes: byte offset of (key, d); the code is in its high nibble when bit 2 of (K: d, V: kk) is set
 CBD_DEVICE int64_t kq4_off(int key, int d, int dh) {
   const int f = ((key >> 4) & 1) * (dh >> 5) + (d >> 5);
   const int lane = (((d & 31) >> 3) << 4) + (key & 15);
-  return (int64_t)(key >> 5) * q_block_bytes(dh, 4) + ((f >> 2) << 10) + (lane << 4) + ((f & 3) << 2) + ((d & 7) >> 1);
+  return (int64_t)(key >> 5) * q_block_bytes(dh, 4) + ((f >> 2) << 10) + (lane << 4) + ((f & 3) << 2) + (d & 3);
 }
 CBD_DEVICE int64_t vq4_off(int key, int d, int dh) {
   const int kk = vslab_kk(key), t = d >> 4;
   const int lane = ((kk >> 3) << 4) + (d & 15);
-  return (int64_t)(key >> 5) * q_block_bytes(dh, 4) + ((t >> 2) << 10) + (lane << 4) + ((t & 3) << 2) + ((kk & 7) >> 1);
+  return (int64_t)(key >> 5) * q_block_bytes(dh, 4) + ((t >> 2) << 10) + (lane << 4) + ((t & 3) << 2) + (kk & 3);
 }
 // Write a 4-bit code into its nibble of a byte whose other nibble another thread may be writing
-// (V: two keys share a byte): clear and set the nibble's bits with word atomics.
+// (V: keys kk and kk ^ 4 share a byte): clear and set the nibble's bits with word atomics.
 CBD_DEVICE void store_nibble(uint8_t* byte_addr, int high, uint32_t code) {
   uint32_t* w = reinterpret_cast<uint32_t*>(reinterpret_cast<uintptr_t>(byte_addr) & ~uintptr_t(3));
   const int sh = 8 * (int)(reinterpret_cast<uintptr_t>(byte_addr) & 3) + 4 * high;

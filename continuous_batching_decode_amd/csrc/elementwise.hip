@@ -138,18 +138,18 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float* qkv, int ld_qkv
 }
 
 // Store the code of (key, dim d) of a K (kv = 0) or V region; lane = d within its group of 64, every
-// lane of the wave calling. 4-bit K: dims d, d + 1 share a byte, written whole by the even lane; 4-bit V:
-// keys kk, kk ^ 1 share a byte, so the nibble is set atomically.
+// lane of the wave calling. 4-bit K: dims d, d ^ 4 share a byte, written whole by the lane with bit 2
+// clear; 4-bit V: keys kk, kk ^ 4 share a byte, so the nibble is set atomically.
 template <int BITS>
 CBD_DEVICE void store_code(uint8_t* base, int kv, int key, int d, int dh, uint32_t code, int lane) {
   if constexpr (BITS == 8) {
     base[kv == 0 ? kq_off(key, d, dh) : vq_off(key, d, dh)] = (uint8_t)code;
   } else {
-    const uint32_t other = __shfl_xor(code, 1, 64);
+    const uint32_t other = __shfl_xor(code, 4, 64);
     if (kv == 0) {
-      if ((lane & 1) == 0) base[kq4_off(key, d, dh)] = (uint8_t)(code | (other << 4));
+      if ((lane & 4) == 0) base[kq4_off(key, d, dh)] = (uint8_t)(code | (other << 4));
     } else {
-      store_nibble(base + vq4_off(key, d, dh), vslab_kk(key) & 1, code);
+      store_nibble(base + vq4_off(key, d, dh), (vslab_kk(key) >> 2) & 1, code);
     }
   }
 }
@@ -157,7 +157,7 @@ template <int BITS>
 CBD_DEVICE uint32_t load_code(const uint8_t* base, int kv, int key, int d, int dh) {
   if constexpr (BITS == 8) return base[kv == 0 ? kq_off(key, d, dh) : vq_off(key, d, dh)];
   const uint32_t b = kv == 0 ? base[kq4_off(key, d, dh)] : base[vq4_off(key, d, dh)];
-  return (b >> (4 * (kv == 0 ? (d & 1) : (vslab_kk(key) & 1)))) & 15u;
+  return (b >> (4 * (kv == 0 ? (d >> 2) & 1 : (vslab_kk(key) >> 2) & 1))) & 15u;
 }
 
 // The same for affine 8-bit slabs: queries rotate in place; each (KV head, group of 64 dims) of the
