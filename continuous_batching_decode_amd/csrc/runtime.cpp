@@ -7,6 +7,8 @@
 //  - section "decode_step_batch - paint-by-numbers": t_s is the sequence's
 //    own length, captured once per step on the host and used for RoPE, the
 //    append slot and the attention range; after the step t_s += 1.
+// Page "Batching", section 6, item 3: a fork shares its parent's prefix blocks
+// (kvslab_fork); the parent's memory stays allocated while forks read it.
 // Failure containment (page "Batching", section 4.5): arguments are
 // validated before anything is enqueued, so a rejected call changes no slab.
 #include <hip/hip_runtime.h>

@@ -26,6 +26,13 @@
  *  - greedy_argmax / sample_top_p: the token of each logits row, greedy or
  *    seeded temperature / top-p (page "Batching", later revision, section
  *    4.4 and section 8).
+ *  - kvslab_fork: page "Batching", section 6, item 3: a sequence that
+ *    starts from another's first positions shares that prefix's K/V blocks
+ *    (copy-on-write of the block where the prefix ends).
+ *  - kv_format (cbd_model_config): slabs hold bf16 K/V, or affine 8-bit /
+ *    4-bit codes with a (scale, bias) pair per group of 64 dims (page
+ *    "Batching", sections 4.3 and 6: quantized caches as packed values,
+ *    scales and biases).
  *
  * Model body (the pages do not spell it out; plainest Llama/Mistral reading):
  * RMSNorm (y = x / sqrt(mean(x^2) + eps) * g), GQA attention with rotate-half
@@ -36,7 +43,8 @@
  * operands of matrix products in bf16 (or int4-affine dequantized to bf16
  * in registers), activation operands as a bf16 pair hi = bf16(x),
  * lo = bf16(x - hi) (about 16 significant bits); K/V stored in the slabs as
- * bf16 (round to nearest even); logits fp32.
+ * bf16 (round to nearest even), or quantized from that bf16 value; logits
+ * fp32.
  *
  * Memory ownership: the caller owns every device buffer it passes (weights,
  * KV arena, token and logit buffers) and every stream. The library
