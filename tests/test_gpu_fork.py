@@ -141,3 +141,84 @@ def test_fork_long_prefix_decode(torch, cbd):
         assert_logits_close(lg.cpu().numpy(), ref, "step %d" % step)
         tok = (tok + 1) % shape.vocab
     eng.close()
+
+
+@pytest.mark.parametrize("kv_format", ["bf16", "affine8"])
+def test_fork_continuous_schedule(torch, cbd, kv_format):
+    """A continuous-batching schedule whose joiners fork a 40-token shared prefix from a holder sequence:
+    forks at 39 (a prompt inside the prefix), 40, 40; prompts admitted in chunks while others decode;
+    rows retire between steps and their slabs go to later joiners; the holder is freed while its forks
+    still decode. Every call's logits and greedy ids against the oracle (which forks the same way)."""
+    from oracle import OracleModel, greedy
+    _say("fork continuous schedule", kv_format)
+    shape = synth.TINY
+    w = synth.make_weights(shape, seed=12, gain_std=0.1)
+    eng = cbd.Engine(w, arena_bytes=6 * 256 * cbd.kv_bytes_per_token(shape, kv_format), max_batch=8,
+                     max_prefill_tokens=128, max_position=1024, kv_format=kv_format)
+    orc = OracleModel(w, cache_all_layers=True, kv_format=kv_format)
+    shared = synth.prompts(61, [40], shape.vocab)[0]
+    own = dict(zip("ABCD", synth.prompts(62, [0, 25, 9, 30], shape.vocab)))
+    pr = {"A": shared[:40], "B": np.concatenate([shared, own["B"]]), "C": np.concatenate([shared, own["C"]]),
+          "D": np.concatenate([shared, own["D"]])}
+    gid, oid, nxt, done = {}, {}, {}, {}
+
+    def run_prefill(names, segs, what):
+        toks = torch.from_numpy(np.concatenate(segs).astype(np.int32)).cuda()
+        lg = torch.empty((len(names), shape.vocab), dtype=torch.float32, device="cuda")
+        nx = torch.empty(len(names), dtype=torch.int32, device="cuda")
+        eng.prefill_segmented([gid[n] for n in names], [len(x) for x in segs], toks, lg, nx)
+        ref = orc.prefill_segmented([oid[n] for n in names], segs)
+        torch.cuda.synchronize()
+        errs = assert_logits_close(lg.cpu().numpy(), ref, what)
+        check_greedy(nx.cpu().numpy(), ref, errs, what)
+        for n, t in zip(names, greedy(ref)):
+            nxt[n] = int(t)
+
+    def join(items, what):  # (name, end of the prompt part to prefill now); a new name forks first
+        names, segs = [], []
+        for n, hi in items:
+            if n not in gid:
+                p = min(len(pr[n]) - 1, 40)
+                gid[n] = eng.fork(gid["H"], p, 256)
+                oid[n] = orc.fork(oid["H"], p)
+            lo = eng.length(gid[n])
+            names.append(n)
+            segs.append(pr[n][lo:hi])
+        run_prefill(names, segs, what)
+
+    def step(names, what):
+        toks = np.array([nxt[n] for n in names])
+        lg = torch.empty((len(names), shape.vocab), dtype=torch.float32, device="cuda")
+        nx = torch.empty(len(names), dtype=torch.int32, device="cuda")
+        eng.decode_step_batch([gid[n] for n in names], torch.from_numpy(toks.astype(np.int32)).cuda(), lg, nx)
+        ref = orc.decode_step_batch([oid[n] for n in names], toks)
+        torch.cuda.synchronize()
+        errs = assert_logits_close(lg.cpu().numpy(), ref, what)
+        check_greedy(nx.cpu().numpy(), ref, errs, what)
+        for n, t in zip(names, greedy(ref)):
+            nxt[n] = int(t)
+
+    def leave(n):
+        done[n] = eng.length(gid[n])
+        eng.free(gid[n])
+        orc.free_sequence(oid[n])
+
+    gid["H"], oid["H"] = eng.alloc(256), orc.new_sequence()
+    run_prefill(["H"], [shared], "holder")
+    join([("A", 40), ("B", 52)], "t0 A (fork at 39), B first chunk")
+    step(["A"], "t1")
+    join([("B", 65)], "t2 B second chunk")
+    step(["B", "A"], "t2")
+    join([("C", 49)], "t3 C")
+    step(["A", "C", "B"], "t3")
+    leave("A")
+    step(["C", "B"], "t4")
+    join([("D", 70)], "t5 D (takes A's granules)")
+    leave("H")  # forks B, C and D still read its prefix
+    step(["B", "D", "C"], "t5")
+    step(["D", "C", "B"], "t6")
+    for n in ("B", "C", "D"):
+        leave(n)
+    assert done == {"A": 43, "H": 40, "B": 70, "C": 53, "D": 72}
+    assert eng.stats()["arena_bytes_used"] == 0
+    eng.close()
