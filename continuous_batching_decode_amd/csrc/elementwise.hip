@@ -409,10 +409,11 @@ hipError_t launch_slab_q8(uint8_t* arena, int64_t slab_off, int stride, int pos,
 // descend the bit patterns of e (order-preserving for positive floats) byte by byte. A row is cut
 // into kSampleChunks chunks of consecutive ids, one workgroup each, over nine launches: chunk maxima;
 // then the weights (kept as bit patterns in the workspace) with the chunk's mass and its histogram of
-// top bytes; then each level: every workgroup adds the chunks' histograms of the level decided last
-// (the same integer sums in every workgroup), picks the byte where the running mass from the top
-// crosses the target, and histograms its own chunk's next byte inside that prefix. The last launch
-// resolves the ties at the final pattern in id order over the chunks' counts.
+// top bytes, added into the row's histogram with integer atomics (order-free sums); then each level:
+// every workgroup reads the row's histogram of the level decided last, picks the byte where the
+// running mass from the top crosses the target, and adds its own chunk's histogram of the next byte
+// inside that prefix. The last launch resolves the ties at the final pattern in id order over the
+// chunks' counts (kept per chunk).
 #ifndef CBD_SAMPLE_UNR
 #define CBD_SAMPLE_UNR 8
 #endif
@@ -523,18 +524,13 @@ __global__ __launch_bounds__(kSampleThreads) void sample_phase_kernel(const floa
     }
   };
 
-  // Add the chunks' histograms of one byte level (region `pre` of the `lv` bytes above), take off
+  // From the row's histogram of one byte level (region `pre` of the `lv` bytes above), take off
   // the nucleus ties beyond `keep` where the boundary pattern lies in the region, and find the byte
   // where the running mass from the top, starting at `above`, crosses `target` (>= when ge, else >).
   auto decide = [&](const uint64_t* h, int lv, uint32_t pre, uint64_t above, uint64_t target, bool ge,
                     uint32_t cap_bits, uint64_t cap_excess, uint32_t& bin, uint64_t& above_out) {
     const int b = 255 - tid;  // thread t holds byte 255 - t: the scan runs from the top
-    uint64_t m = 0;
-#pragma unroll
-    for (int k = 0; k < CS; ++k) {  // all loads in flight together (clamped: chunks beyond C add 0)
-      const uint64_t v = h[min(k, C - 1) * 256 + b];
-      m += k < C ? v : 0ull;
-    }
+    uint64_t m = h[b];        // the row's histogram (the chunks' ones were added into it)
     if (cap_excess && (lv == 0 || (cap_bits >> (32 - 8 * lv)) == pre) && ((cap_bits >> (24 - 8 * lv)) & 255) == (uint32_t)b)
       m -= cap_excess;
     uint64_t incl = m;
@@ -581,14 +577,16 @@ __global__ __launch_bounds__(kSampleThreads) void sample_phase_kernel(const floa
         }
     });
     __syncthreads();
-    for (int i = tid; i < 256; i += kSampleThreads) {
-      h_out[c * 256 + i] = hm[i];
+    for (int i = tid; i < 256; i += kSampleThreads) {  // masses: added into the row's histogram
+      if (hm[i]) atomicAdd(reinterpret_cast<unsigned long long*>(&h_out[i]), (unsigned long long)hm[i]);
       if (n_out) n_out[c * 256 + i] = hc[i];
     }
   };
 
   if (phase == 0) {  // chunk maxima (greedy: the chunk's maximum and its lowest id)
     if (c == 0 && tid == 0) out[r] = 0;  // stands if no weight is positive
+    if (c == 0)  // the row's histograms of every level start empty
+      for (int i = tid; i < 7 * 256; i += kSampleThreads) H(i >> 8)[i & 255] = 0;
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
     const float inv_t = greedy ? 1.f : 1.f / temp;
