@@ -168,6 +168,12 @@ class OracleModel:
         self._next_id = 0
         self._cache: Dict = {}
         self._cache_all = cache_all_layers
+        # Optional input: a callable (sid, layer, position, which, y, stored) -> stored, consulted for
+        # every K ("k") or V ("v") vector the model computes itself before it enters the slab; y is
+        # the unrounded float64 value [Hkv, Dh] and stored the slab form the model made of it (bf16
+        # bits [1, Hkv, Dh], or (codes, pairs) for affine slabs). What it returns is stored instead:
+        # a slab snapshot given as input. None: the model's own form.
+        self.stored_override = None
 
     # -- weights
     def _matrix(self, m) -> np.ndarray:
@@ -229,16 +235,26 @@ class OracleModel:
         for l in range(self.cfg.n_layers):
             self._store(self.seqs[sid], l, np.asarray(k_bits[l], dtype=np.uint16), np.asarray(v_bits[l], dtype=np.uint16))
 
+    def _encode(self, bits: np.ndarray):
+        """Slab form of bf16 K or V bits [n, Hkv, Dh]: the bits themselves, or affine (codes, pairs)."""
+        if self.kv_format == "bf16":
+            return bits
+        return quantize_affine(bits, self.kv_group, 8 if self.kv_format == "affine8" else 4)
+
+    def _put(self, s: SeqState, l: int, which: str, stored) -> None:
+        """Append a slab form made by _encode to layer l of K ("k") or V ("v")."""
+        if self.kv_format == "bf16":
+            arr = s.k if which == "k" else s.v
+            arr[l] = np.concatenate([arr[l], stored])
+            return
+        codes, sbs = (s.k, s.k_sb) if which == "k" else (s.v, s.v_sb)
+        codes[l] = np.concatenate([codes[l], stored[0]])
+        sbs[l] = np.concatenate([sbs[l], stored[1]])
+
     def _store(self, s: SeqState, l: int, kb: np.ndarray, vb: np.ndarray) -> None:
         """Append bf16 K/V bits [n, Hkv, Dh] to layer l of a slab, in the slab's storage format."""
-        if self.kv_format == "bf16":
-            s.k[l] = np.concatenate([s.k[l], kb])
-            s.v[l] = np.concatenate([s.v[l], vb])
-            return
-        for codes, sbs, x in ((s.k, s.k_sb, kb), (s.v, s.v_sb, vb)):
-            c, sb = quantize_affine(x, self.kv_group, 8 if self.kv_format == "affine8" else 4)
-            codes[l] = np.concatenate([codes[l], c])
-            sbs[l] = np.concatenate([sbs[l], sb])
+        self._put(s, l, "k", self._encode(kb))
+        self._put(s, l, "v", self._encode(vb))
 
     def kv_values(self, sid: int, l: int):
         """Values attention reads from layer l of a slab: (K, V) float64 [len, Hkv, Dh]."""
@@ -271,14 +287,16 @@ class OracleModel:
             s = self.seqs[sid]
             if s.k[l].shape[0] != t:
                 raise ValueError("slab length %d != position %d" % (s.k[l].shape[0], t))
-            kb = f64_to_bf16_bits(apply_rope(k[i], t, c.rope_theta))[None]
-            vb = f64_to_bf16_bits(v[i])[None]
-            self._store(s, l, kb, vb)
+            for which, y in (("k", apply_rope(k[i], t, c.rope_theta)), ("v", v[i])):
+                stored = self._encode(f64_to_bf16_bits(y)[None])
+                if self.stored_override is not None:
+                    stored = self.stored_override(sid, l, t, which, y, stored)
+                self._put(s, l, which, stored)
         o = np.zeros((len(rows), c.n_heads, c.head_dim))
         kv_f64 = {}
         for i, (sid, t) in enumerate(zip(rows, positions)):
-            if sid not in kv_f64:
-                kv_f64[sid] = self.kv_values(sid, l)
+            if sid not in kv_f64:  # one sequence's values at a time (a long slab is large in float64)
+                kv_f64 = {sid: self.kv_values(sid, l)}
             K, V = kv_f64[sid]
             qr = apply_rope(q[i], t, c.rope_theta)
             for hh in range(c.n_heads):
