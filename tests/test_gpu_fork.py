@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_common import MID, LOGIT_RTOL, assert_logits_close, check_greedy, compare_slab_bits
+from gpu_common import MID, GpuStoredKV, assert_logits_close, check_greedy, compare_slab_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -51,12 +51,20 @@ def test_fork_prefill_decode_and_parent_retired(torch, cbd, kv_format):
                      kv_format=kv_format)
     orc = OracleModel(w, cache_all_layers=True, kv_format=kv_format)
     shared, ra, rb, rc, other = synth.prompts(31, [90, 20, 45, 7, 33], shape.vocab)
+    stored = GpuStoredKV(kv_format) if kv_format != "bf16" else None
+    orc.stored_override = stored
+
+    def capture(ids, oids, t0, counts):
+        if stored is not None:
+            stored.capture(torch, eng, list(zip(ids, oids, t0, counts)))
 
     def prefill(ids, oids, segs, what):
         toks = torch.from_numpy(np.concatenate(segs).astype(np.int32)).cuda()
         lg = torch.empty((len(ids), shape.vocab), dtype=torch.float32, device="cuda")
         nx = torch.empty(len(ids), dtype=torch.int32, device="cuda")
+        t0 = [eng.length(i) for i in ids]
         eng.prefill_segmented(ids, [len(x) for x in segs], toks, lg, nx)
+        capture(ids, oids, t0, [len(x) for x in segs])
         ref = orc.prefill_segmented(oids, segs)
         torch.cuda.synchronize()
         errs = assert_logits_close(lg.cpu().numpy(), ref, what)
@@ -66,7 +74,9 @@ def test_fork_prefill_decode_and_parent_retired(torch, cbd, kv_format):
     def decode(ids, oids, toks, what):
         lg = torch.empty((len(ids), shape.vocab), dtype=torch.float32, device="cuda")
         nx = torch.empty(len(ids), dtype=torch.int32, device="cuda")
+        t0 = [eng.length(i) for i in ids]
         eng.decode_step_batch(ids, torch.from_numpy(np.asarray(toks, dtype=np.int32)).cuda(), lg, nx)
+        capture(ids, oids, t0, [1] * len(ids))
         ref = orc.decode_step_batch(oids, np.asarray(toks, dtype=np.int64))
         torch.cuda.synchronize()
         errs = assert_logits_close(lg.cpu().numpy(), ref, what)
@@ -106,8 +116,12 @@ def test_fork_prefill_decode_and_parent_retired(torch, cbd, kv_format):
             codes, sb = eng.kvslab_read_q8(f, 0, n)
             torch.cuda.synchronize()
             s = orc.seqs[of]
-            check_appended(kv_format, codes.cpu().numpy()[:, :, 0], sb.cpu().numpy()[:, :, 0], np.stack(s.k),
-                           np.stack(s.k_sb), "fork K")
+            for w_, oc, osb in ((0, s.k, s.k_sb), (1, s.v, s.v_sb)):
+                check_appended(kv_format, codes.cpu().numpy()[:, :, w_], sb.cpu().numpy()[:, :, w_], np.stack(oc),
+                               np.stack(osb), "fork %s" % "KV"[w_])
+    if stored is not None:
+        stored.assert_consumed()
+        _say("  stored forms checked %d, taken from the GPU %d" % (stored.checked, stored.replaced))
     for f, _, _ in forks:
         eng.free(f)
     eng.free(solo)
@@ -161,12 +175,20 @@ def test_fork_continuous_schedule(torch, cbd, kv_format):
     pr = {"A": shared[:40], "B": np.concatenate([shared, own["B"]]), "C": np.concatenate([shared, own["C"]]),
           "D": np.concatenate([shared, own["D"]])}
     gid, oid, nxt, done = {}, {}, {}, {}
+    stored = GpuStoredKV(kv_format) if kv_format != "bf16" else None
+    orc.stored_override = stored
+
+    def capture(names, t0, counts):
+        if stored is not None:
+            stored.capture(torch, eng, [(gid[n], oid[n], t, c) for n, t, c in zip(names, t0, counts)])
 
     def run_prefill(names, segs, what):
         toks = torch.from_numpy(np.concatenate(segs).astype(np.int32)).cuda()
         lg = torch.empty((len(names), shape.vocab), dtype=torch.float32, device="cuda")
         nx = torch.empty(len(names), dtype=torch.int32, device="cuda")
+        t0 = [eng.length(gid[n]) for n in names]
         eng.prefill_segmented([gid[n] for n in names], [len(x) for x in segs], toks, lg, nx)
+        capture(names, t0, [len(x) for x in segs])
         ref = orc.prefill_segmented([oid[n] for n in names], segs)
         torch.cuda.synchronize()
         errs = assert_logits_close(lg.cpu().numpy(), ref, what)
@@ -190,7 +212,9 @@ def test_fork_continuous_schedule(torch, cbd, kv_format):
         toks = np.array([nxt[n] for n in names])
         lg = torch.empty((len(names), shape.vocab), dtype=torch.float32, device="cuda")
         nx = torch.empty(len(names), dtype=torch.int32, device="cuda")
+        t0 = [eng.length(gid[n]) for n in names]
         eng.decode_step_batch([gid[n] for n in names], torch.from_numpy(toks.astype(np.int32)).cuda(), lg, nx)
+        capture(names, t0, [1] * len(names))
         ref = orc.decode_step_batch([oid[n] for n in names], toks)
         torch.cuda.synchronize()
         errs = assert_logits_close(lg.cpu().numpy(), ref, what)
@@ -220,5 +244,7 @@ def test_fork_continuous_schedule(torch, cbd, kv_format):
     for n in ("B", "C", "D"):
         leave(n)
     assert done == {"A": 43, "H": 40, "B": 70, "C": 53, "D": 72}
+    if stored is not None:
+        stored.assert_consumed()
     assert eng.stats()["arena_bytes_used"] == 0
     eng.close()

@@ -270,7 +270,11 @@ def test_tiny_prefill_and_decode_teacher_forced(torch, cbd, gain_std):
 
 
 def test_tiny_free_running_trajectory(torch, cbd):
-    """Free-running greedy: GPU feeds its own argmax (device-resident), oracle its own."""
+    """Free-running greedy: the GPU feeds its own argmax back on the device for 8 steps. The oracle
+    follows the GPU's trajectory (each step it consumes the tokens the GPU consumed), so every step's
+    logits are compared; each GPU token must be the oracle's greedy choice, except at a step whose
+    oracle top-1/top-2 margin lies within the tie band of that row's error (a tie-ambiguous step, where
+    either token is correct). The trajectory then goes on from the GPU's token on both sides."""
     _say("tiny free-running")
     from oracle import OracleModel, greedy
     shape = synth.TINY
@@ -282,24 +286,23 @@ def test_tiny_free_running_trajectory(torch, cbd):
     orc = OracleModel(w, cache_all_layers=True)
     ids, oids, got, gtok, ref = _prefill_both(torch, cbd, eng, orc, lengths, prompts, 64)
     errs = assert_logits_close(got, ref, "prefill")
-    amb = check_greedy(gtok, ref, errs, "prefill")
-    gpu_traj, orc_traj = [gtok.copy()], [greedy(ref)]
+    ambiguous = check_greedy(gtok, ref, errs, "prefill")
+    differ = int(np.sum(gtok != greedy(ref)))
     tok_dev = torch.from_numpy(gtok.astype(np.int32)).cuda()
     logits = torch.empty((4, shape.vocab), dtype=torch.float32, device="cuda")
-    tok = greedy(ref)
     for step in range(8):
+        fed = tok_dev.cpu().numpy().astype(np.int64)  # what the GPU consumes this step (its own argmax)
         nxt = torch.empty(4, dtype=torch.int32, device="cuda")
         eng.decode_step_batch(ids, tok_dev, logits, nxt)
         tok_dev = nxt
-        ref = orc.decode_step_batch(oids, tok)
-        tok = greedy(ref)
+        ref = orc.decode_step_batch(oids, fed)
         torch.cuda.synchronize()
-        gpu_traj.append(nxt.cpu().numpy())
-        orc_traj.append(tok)
-    g, o = np.stack(gpu_traj), np.stack(orc_traj)
-    if amb == 0:
-        assert np.array_equal(g, o), (g, o)
-    _say("free-running tokens identical:", bool(np.array_equal(g, o)))
+        errs = assert_logits_close(logits.cpu().numpy(), ref, "step %d" % step)
+        g = nxt.cpu().numpy()
+        ambiguous += check_greedy(g, ref, errs, "step %d" % step)  # fails on a non-ambiguous difference
+        differ += int(np.sum(g != greedy(ref)))
+    _say("free-running: %d tie-ambiguous row-steps, %d tokens differing from the oracle's choice" % (ambiguous, differ))
+    assert differ <= ambiguous
     eng.close()
 
 
