@@ -174,6 +174,25 @@ def pack_bf16_device(w_rowmajor_dev, stream=None):
     return out
 
 
+def _tensor(t, dtype: str, min_numel: int, name: str) -> int:
+    """Device pointer of a tensor passed to the library, after checking what the C ABI assumes of it:
+    a contiguous tensor on the GPU of the expected element type holding at least min_numel elements.
+    Raises ValueError otherwise (the library would read or write out of bounds)."""
+    import torch
+    want = getattr(torch, dtype)
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != want:
+        raise ValueError("%s must be %s, not %s" % (name, dtype, str(t.dtype).replace("torch.", "")))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.numel() < min_numel:
+        raise ValueError("%s holds %d elements, %d needed" % (name, t.numel(), min_numel))
+    return t.data_ptr()
+
+
 def _stream_ptr(stream) -> Optional[int]:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -286,9 +305,14 @@ class Engine:
 
     def append(self, seq_id: int, k_dev, v_dev, stream=None) -> None:
         """k_dev, v_dev: device int16 tensors holding bf16 bits, [L, n, Hkv, Dh]."""
-        n = int(k_dev.shape[1])
-        _check(self.lib.kvslab_append(self.ctx, int(seq_id), n, k_dev.data_ptr(), v_dev.data_ptr(),
-                                      _stream_ptr(stream)))
+        s = self.shape
+        n = int(k_dev.shape[1]) if k_dev.dim() == 4 else -1
+        if tuple(k_dev.shape) != (s.n_layers, n, s.n_kv_heads, s.head_dim) or tuple(v_dev.shape) != tuple(k_dev.shape):
+            raise ValueError("k and v must both be [L, n, Hkv, Dh] = [%d, n, %d, %d]" % (s.n_layers, s.n_kv_heads,
+                                                                                      s.head_dim))
+        kp = _tensor(k_dev, "int16", k_dev.numel(), "k")
+        vp = _tensor(v_dev, "int16", v_dev.numel(), "v")
+        _check(self.lib.kvslab_append(self.ctx, int(seq_id), n, kp, vp, _stream_ptr(stream)))
 
     def read(self, seq_id: int, start: int, n: int, stream=None):
         """Slab positions [start, start+n) as device int16 tensors (bf16 bits) [L, n, Hkv, Dh]."""
@@ -320,35 +344,54 @@ class Engine:
     # -- hot path
     def decode_step_batch(self, seq_ids: Sequence[int], last_tokens_dev, logits_dev, next_tokens_dev=None,
                           stream=None) -> None:
-        _check(self.lib.decode_step_batch(self.ctx, _ids(seq_ids), len(seq_ids), last_tokens_dev.data_ptr(),
-                                          logits_dev.data_ptr(),
-                                          next_tokens_dev.data_ptr() if next_tokens_dev is not None else None,
-                                          _stream_ptr(stream)))
+        """last_tokens_dev: int32 [B]; logits_dev: float32 [B, vocab]; next_tokens_dev: int32 [B] or None."""
+        B, V = len(seq_ids), self.shape.vocab
+        tp = _tensor(last_tokens_dev, "int32", B, "last_tokens")
+        lp = _tensor(logits_dev, "float32", B * V, "logits")
+        np_ = _tensor(next_tokens_dev, "int32", B, "next_tokens") if next_tokens_dev is not None else None
+        _check(self.lib.decode_step_batch(self.ctx, _ids(seq_ids), B, tp, lp, np_, _stream_ptr(stream)))
 
     def prefill_segmented(self, seq_ids: Sequence[int], seg_lens: Sequence[int], tokens_dev, last_logits_dev,
                           next_tokens_dev=None, stream=None) -> None:
-        _check(self.lib.prefill_segmented(self.ctx, _ids(seq_ids), _ids(seg_lens), len(seq_ids),
-                                          tokens_dev.data_ptr(), last_logits_dev.data_ptr(),
-                                          next_tokens_dev.data_ptr() if next_tokens_dev is not None else None,
+        """tokens_dev: int32 [sum(seg_lens)]; last_logits_dev: float32 [K, vocab]; next_tokens_dev: int32 [K]."""
+        K, V = len(seq_ids), self.shape.vocab
+        tp = _tensor(tokens_dev, "int32", sum(int(n) for n in seg_lens), "tokens")
+        lp = _tensor(last_logits_dev, "float32", K * V, "last_logits")
+        np_ = _tensor(next_tokens_dev, "int32", K, "next_tokens") if next_tokens_dev is not None else None
+        _check(self.lib.prefill_segmented(self.ctx, _ids(seq_ids), _ids(seg_lens), K, tp, lp, np_,
                                           _stream_ptr(stream)))
 
     def greedy_argmax(self, logits_dev, tokens_dev, stream=None) -> None:
-        _check(self.lib.greedy_argmax(self.ctx, logits_dev.data_ptr(), int(logits_dev.shape[0]),
-                                      tokens_dev.data_ptr(), _stream_ptr(stream)))
+        """logits_dev: float32 [rows, vocab]; tokens_dev: int32 [rows]."""
+        rows = int(logits_dev.shape[0])
+        lp = _tensor(logits_dev, "float32", rows * self.shape.vocab, "logits")
+        tp = _tensor(tokens_dev, "int32", rows, "tokens")
+        _check(self.lib.greedy_argmax(self.ctx, lp, rows, tp, _stream_ptr(stream)))
 
     def sample_top_p(self, logits_dev, temperature, top_p, seeds, sample_index, tokens_dev, stream=None) -> None:
         """Seeded temperature / top-p sampling of each logits row (host lists of per-row parameters)."""
         rows = int(logits_dev.shape[0])
+        for name, xs in (("temperature", temperature), ("top_p", top_p), ("seeds", seeds),
+                         ("sample_index", sample_index)):
+            if len(xs) < rows:
+                raise ValueError("%s: %d values for %d rows" % (name, len(xs), rows))
+        lp = _tensor(logits_dev, "float32", rows * self.shape.vocab, "logits")
+        tp = _tensor(tokens_dev, "int32", rows, "tokens")
         F = ctypes.c_float * max(rows, 1)
         U = ctypes.c_uint64 * max(rows, 1)
-        _check(self.lib.sample_top_p(self.ctx, logits_dev.data_ptr(), rows, F(*[float(x) for x in temperature]),
-                                     F(*[float(x) for x in top_p]), U(*[int(x) for x in seeds]),
-                                     U(*[int(x) for x in sample_index]), tokens_dev.data_ptr(), _stream_ptr(stream)))
+        _check(self.lib.sample_top_p(self.ctx, lp, rows, F(*[float(x) for x in temperature[:rows]]),
+                                     F(*[float(x) for x in top_p[:rows]]), U(*[int(x) for x in seeds[:rows]]),
+                                     U(*[int(x) for x in sample_index[:rows]]), tp, _stream_ptr(stream)))
 
     def linear(self, w_ptrs: Matrix, N: int, K: int, x_dev, y_dev, splits: int = 0, stream=None) -> None:
         """y_dev[b] = W x_dev[b]; x_dev fp32 [rows, K] device tensor, y_dev fp32 [rows, N]."""
-        _check(self.lib.cbd_linear(self.ctx, ctypes.byref(w_ptrs), int(N), int(K), x_dev.data_ptr(),
-                                   int(x_dev.shape[0]), y_dev.data_ptr(), int(splits), _stream_ptr(stream)))
+        rows = int(x_dev.shape[0])
+        if x_dev.dim() != 2 or int(x_dev.shape[1]) != int(K):
+            raise ValueError("x must be [rows, K] with K = %d" % K)
+        xp = _tensor(x_dev, "float32", rows * int(K), "x")
+        yp = _tensor(y_dev, "float32", rows * int(N), "y")
+        _check(self.lib.cbd_linear(self.ctx, ctypes.byref(w_ptrs), int(N), int(K), xp, rows, yp, int(splits),
+                                   _stream_ptr(stream)))
 
     # -- per-kernel event timing
     def profile_begin(self, kinds: Sequence[str], max_launches: int = 1 << 16, every: int = 1) -> None:
