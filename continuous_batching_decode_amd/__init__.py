@@ -28,7 +28,8 @@ KV_FORMATS = {"bf16": KV_BF16, "affine8": KV_AFFINE8, "affine4": KV_AFFINE4}
 EXPORTS = ["cbd_kv_bytes_per_token", "cbd_slab_granule_tokens", "cbd_create", "cbd_destroy", "cbd_last_error",
            "cbd_stats", "kvslab_alloc", "kvslab_free", "kvslab_len", "kvslab_capacity", "kvslab_append",
            "kvslab_read", "decode_step_batch", "prefill_segmented", "greedy_argmax", "cbd_linear", "cbd_pack_int4",
-           "cbd_profile_begin", "cbd_profile_end", "cbd_pack_bf16", "sample_top_p", "kvslab_read_q8", "kvslab_fork"]
+           "cbd_profile_begin", "cbd_profile_end", "cbd_pack_bf16", "sample_top_p", "kvslab_read_q8", "kvslab_fork",
+           "cbd_greedy_argmax_noalloc"]
 
 KERNEL_KINDS = ["embed", "norm", "qkv", "rope_append", "attention", "attn_combine", "o_proj", "gate_up", "down",
                 "lm_head", "argmax", "sample"]
@@ -102,6 +103,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "decode_step_batch": (i32, [ctx_p, P(i32), i32, vp, vp, vp, vp]),
         "prefill_segmented": (i32, [ctx_p, P(i32), P(i32), i32, vp, vp, vp, vp]),
         "greedy_argmax": (i32, [ctx_p, vp, i32, vp, vp]),
+        "cbd_greedy_argmax_noalloc": (i32, [vp, i32, i32, vp, vp]),
         "sample_top_p": (i32, [ctx_p, vp, i32, P(ctypes.c_float), P(ctypes.c_float), P(ctypes.c_uint64),
                                P(ctypes.c_uint64), vp, vp]),
         "cbd_linear": (i32, [ctx_p, P(Matrix), i32, i32, vp, i32, vp, i32, vp]),
@@ -197,6 +199,17 @@ def _stream_ptr(stream) -> Optional[int]:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+def greedy_argmax_noalloc(logits_dev, tokens_dev, stream=None) -> None:
+    """Context-free greedy selection over rows of logits (float32 [rows, vocab] device tensor) into
+    tokens_dev (int32 [rows]); the library allocates nothing (cbd_greedy_argmax_noalloc)."""
+    if logits_dev.dim() != 2:
+        raise ValueError("logits must be [rows, vocab]")
+    rows, vocab = int(logits_dev.shape[0]), int(logits_dev.shape[1])
+    lp = _tensor(logits_dev, "float32", rows * vocab, "logits")
+    tp = _tensor(tokens_dev, "int32", rows, "tokens")
+    _check(lib().cbd_greedy_argmax_noalloc(lp, rows, vocab, tp, _stream_ptr(stream)))
 
 
 class Engine:

@@ -6,6 +6,8 @@
 // Position discipline (page "Batching", section 5): a row's position is read
 // once per step from its metadata and used for both the query and the key
 // rotation and for the slab slot the key is written to.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -817,3 +819,67 @@ hipError_t launch_sample_top_p(const float* logits, int rows, int vocab, const S
 }
 
 }  // namespace cbd
+
+// ---------------------------------------------------------------------------- scratch-free argmax
+//
+// cbd_greedy_argmax_noalloc: greedy_argmax without a context, for callers that cannot allocate
+// device memory (code under stream capture, tight serving loops). Its kernel's segment partials and
+// arrival counters live in `scratch`, a file-scope device array: one copy per GPU, loaded with the
+// code object and held until the process ends. Host code reaches it only through the device address
+// hipGetSymbolAddress returns for the current device (the array's name is a host-side stand-in),
+// looked up once per device on the first call there. Every call on a GPU shares that GPU's array:
+// calls that overlap on one GPU (several streams or threads) race.
+
+namespace {
+constexpr int kNoallocRows = 64;
+constexpr size_t kNoallocPartBytes = (size_t)kNoallocRows * cbd::kArgmaxSegments * 2 * sizeof(float);
+constexpr size_t kNoallocBytes = kNoallocPartBytes + kNoallocRows * sizeof(int32_t);
+constexpr int kNoallocMaxDevices = 64;
+static_assert(kNoallocPartBytes % 256 == 0, "counters start 256-byte aligned");
+
+__global__ __launch_bounds__(64) void clear_counters_kernel(int32_t* counters, int n) {
+  if ((int)threadIdx.x < n) counters[threadIdx.x] = 0;
+}
+
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_dev[kNoallocMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoallocBytes];
+
+extern "C" cbd_status cbd_greedy_argmax_noalloc(const float* logits_dev, int32_t rows, int32_t vocab,
+                                                int32_t* tokens_dev, cbd_stream stream) {
+  if (rows < 0 || rows > kNoallocRows)
+    return cbd::record_error(CBD_E_INVAL, "cbd_greedy_argmax_noalloc: rows must be in 0..64 (scratch holds 64 rows)");
+  if (rows == 0) return CBD_OK;
+  if (vocab < 4 || vocab % 4 || vocab > (1 << 30))
+    return cbd::record_error(CBD_E_INVAL, "cbd_greedy_argmax_noalloc: vocab must be a multiple of 4 in 4..2^30");
+  if (!logits_dev || !tokens_dev || (reinterpret_cast<uintptr_t>(logits_dev) & 15))
+    return cbd::record_error(CBD_E_INVAL, "cbd_greedy_argmax_noalloc: null or misaligned pointer");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoallocMaxDevices)
+    return cbd::record_error(CBD_E_HIP, "cbd_greedy_argmax_noalloc: no current device");
+  uint8_t* base;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+      void* p = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return cbd::record_error(CBD_E_HIP, "cbd_greedy_argmax_noalloc: scratch address: %s", hipGetErrorString(e));
+      g_scratch_dev[dev] = static_cast<uint8_t*>(p);
+    }
+    base = g_scratch_dev[dev];
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* part = reinterpret_cast<float*>(base);
+  int32_t* counters = reinterpret_cast<int32_t*>(base + kNoallocPartBytes);
+  // the counters of the previous call are zero when it completed; cleared anyway (a kernel, not a
+  // memset node, so the call can be captured into a graph)
+  cbd::launch_kernel(clear_counters_kernel, dim3(1), dim3(64), 0, st, counters, (int)rows);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = cbd::launch_argmax(logits_dev, rows, vocab, part, counters, tokens_dev, st);
+  if (e != hipSuccess) return cbd::record_error(CBD_E_HIP, "cbd_greedy_argmax_noalloc: %s", hipGetErrorString(e));
+  return CBD_OK;
+}
+

@@ -5,8 +5,12 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "../../include/cbd.h"
 
 namespace cbd {
+
+// Record the message of a failing call (cbd_last_error) and return its status.
+cbd_status record_error(cbd_status s, const char* fmt, ...);
 
 // Profiling hook. When start is set, the next kernel launched from this thread goes through
 // hipExtLaunchKernelGGL, which stamps start/stop at that kernel's own begin and end (no dispatch

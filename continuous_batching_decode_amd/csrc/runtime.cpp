@@ -282,6 +282,16 @@ int plan_decode_items(const cbd_ctx* c, const std::vector<RowMeta>& rows, AttnIt
 }  // namespace
 
 namespace cbd {
+cbd_status record_error(cbd_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
 LaunchEvents& launch_events() {
   static thread_local LaunchEvents ev{nullptr, nullptr};
   return ev;

@@ -317,6 +317,26 @@ cbd_status greedy_argmax(cbd_ctx* ctx, const float* logits_dev, int32_t rows, in
                          cbd_stream stream);
 
 /*
+ * greedy_argmax without a context and without allocating: for callers that
+ * cannot allocate device memory (code under stream capture, tight serving
+ * loops, harnesses that forbid it). The same selection (lowest id among the
+ * maxima of each row; token 0 for a row of NaNs) and the same kernel.
+ *  logits_dev  device fp32 [rows, vocab], 16-byte aligned (caller-owned)
+ *  rows        0..64 (0: no-op); more rows fail with CBD_E_INVAL
+ *  vocab       a multiple of 4 in 4..2^30
+ *  tokens_dev  device int32 [rows] (caller-owned), written on the stream
+ * The kernel's workspace (per-row partial maxima and arrival counters, 33 KB)
+ * is a static device array of the library: one copy per GPU, held until the
+ * process ends; the first call on a device looks up its address. Every call
+ * on one GPU shares that GPU's copy: calls that overlap on one GPU (several
+ * streams or threads at once) race and must be serialized by the caller.
+ * Calls no hipMalloc/hipFree and enqueues no memset (two kernels on the
+ * stream). CBD_E_HIP: no current device or a failed launch.
+ */
+cbd_status cbd_greedy_argmax_noalloc(const float* logits_dev, int32_t rows, int32_t vocab, int32_t* tokens_dev,
+                                     cbd_stream stream);
+
+/*
  * Seeded per-row sampling over rows of logits (page "Batching", later
  * revision, section 4.4 "The decode step": a row's random draw is selected by
  * its request's seed and local sample index, independently of the other rows;
