@@ -133,6 +133,14 @@ def main():
     ap.add_argument("--share-prefix", type=int, default=1, choices=[0, 1],
                     help="continuous workload: joiners fork the prompts' common 1024-token prefix from one "
                          "prefilled holder sequence (kvslab_fork) and prefill only the rest; 0 = whole prompts")
+    ap.add_argument("--parity-rows", type=int, default=0,
+                    help="decode workloads: run the oracle (parity and cpu baseline) on the first this many rows "
+                         "only (0 = all rows; long-context workloads run it only when this is set)")
+    ap.add_argument("--fill", default="seeded", choices=["seeded", "copy"],
+                    help="decode workloads: 'copy' draws row 0's K/V history and copies it on the device to the "
+                         "other rows (the same bytes streamed, less host time for 32k-token histories)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default workload: skip the compact int4, prefill and 32k-context sub-benchmarks")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a device buffer of this many MiB 5 times (a plain copy of known size, "
                          "used to calibrate HBM byte counters), then exit")
@@ -193,8 +201,11 @@ def main():
     ids = [eng.alloc(c) for c in caps]
     hist = []
     long_ctx = args.workload.startswith("llama8b-long")
-    keep = not args.no_cpu_baseline and not long_ctx  # the oracle needs the histories
-    for r in range(B):
+    oracle_rows = B if args.parity_rows <= 0 else min(B, args.parity_rows)
+    run_oracle = not args.no_cpu_baseline and (not long_ctx or args.parity_rows > 0)
+    drawn = B if args.fill == "seeded" else 1  # rows whose history is drawn on the host
+    for r in range(drawn):
+        keep = run_oracle and r < oracle_rows  # the oracle needs these histories
         # seeded K/V, appended in chunks of tokens (the same values as synth.kv_history of the whole row)
         n = int(ctx[r])
         std = shape.weight_std * float(np.sqrt(shape.d_model))
@@ -212,13 +223,17 @@ def main():
                 vs.append(vc)
         if keep:
             hist.append((np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)))
-    if n_rows > B and kv_format != "bf16":
-        raise SystemExit("a sweep beyond B copies bf16 slabs; not available with %s K/V" % kv_format)
-    for r in range(B, n_rows):
-        # sweep-only rows reuse the histories of the main rows (device copies)
-        src = r % B
-        k, v = eng.read(ids[src], 0, int(ctx[src]))
+    if (n_rows > B or drawn < B) and kv_format != "bf16":
+        raise SystemExit("rows filled by device copies of bf16 slabs; not available with %s K/V" % kv_format)
+    for r in range(drawn, n_rows):
+        # rows not drawn on the host (sweep-only rows; with --fill copy every row past 0) copy the history
+        # of a drawn row on the device
+        src = r % B if r >= B else 0
+        k, v = eng.read(ids[src], 0, min(int(ctx[src]), int(ctx[r])))
         eng.append(ids[r], k, v)
+        if drawn < B and r < B and int(ctx[r]) > int(ctx[src]):
+            raise SystemExit("--fill copy needs rows no longer than row 0")
+        del k, v
     torch.cuda.synchronize()
     log("slabs ready: contexts %s" % list(ctx_main))
 
@@ -349,29 +364,29 @@ def main():
 
     cpu = None
     parity = None
-    if not args.no_cpu_baseline and not long_ctx:
+    if run_oracle:
         from oracle import OracleModel, greedy
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:  # pragma: no cover
-            cores = 1
-        log("cpu baseline: oracle, one decode step of the %d rows (BLAS threads %d)" % (B, cores))
+        cores, blas = host_cores()
+        R = oracle_rows
+        log("cpu baseline: oracle, one decode step of %d of the %d rows (host cores %d, BLAS threads %d)" % (
+            R, B, cores, blas))
         orc = OracleModel(weights)
         oids = []
-        for r in range(B):
+        for r in range(R):
             o = orc.new_sequence()
             orc.append_history(o, hist[r][0], hist[r][1])
             oids.append(o)
+        hist = None
         c0 = time.perf_counter()
-        ref = orc.decode_step_batch(oids, first_tok[:B].astype(np.int64))
+        ref = orc.decode_step_batch(oids, first_tok[:R].astype(np.int64))
         csecs = time.perf_counter() - c0
-        cpu = {"value": round(B / csecs, 4), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
-               "sample": "one decode_step_batch of the same %d rows at their seeded contexts (float64, all 32 "
-                         "layers + lm_head), %.1f s" % (B, csecs)}
-        errs = np.max(np.abs(first_logits - ref), axis=1) / np.max(np.abs(ref), axis=1)
+        cpu = {"value": round(R / csecs, 4), "unit": "tok/s", "cores": int(cores), "blas_threads": int(blas),
+               "kind": "oracle",
+               "sample": "one decode_step_batch of %d of the %d rows at their seeded contexts (float64, all %d "
+                         "layers + lm_head), %.1f s" % (R, B, shape.n_layers, csecs)}
+        errs = np.max(np.abs(first_logits[:R] - ref), axis=1) / np.max(np.abs(ref), axis=1)
         parity = {"max_rel_err": float(np.max(errs)), "tol": 1e-2,
-                  "greedy_match": int(np.sum(greedy(first_logits) == greedy(ref))), "rows": B}
+                  "greedy_match": int(np.sum(greedy(first_logits[:R]) == greedy(ref))), "rows": R}
         log("cpu baseline %.2f s/step; parity %s" % (csecs, parity))
         if sampling is not None:
             # the sampled tokens against the oracle's selection on the same (GPU) logits rows
@@ -382,7 +397,8 @@ def main():
     out = {"metric": METRIC, "value": round(tokps, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16" if shape.weight_format == "bf16" else "int4-affine/bf16",
-           "data": "synthetic",
+           "data": "synthetic" if args.fill == "seeded" else
+                   "synthetic (row 0's seeded history copied on the device to the other rows)",
            "config": {"workload": "%s: %s decode_step_batch, B=%d, contexts U[%d,%d], greedy, %d layers" % (
                args.workload, shape.name, B, args.ctx_lo, args.ctx_hi, shape.n_layers),
                "batch": B, "contexts": [int(c) for c in ctx_main], "kv_format": kv_format,
@@ -392,7 +408,64 @@ def main():
            "roofline": roofline, "cpu_baseline": cpu, "parity_first_step": parity, "sweep": sweep_out,
            "kernel_breakdown": breakdown, "sampling": sampling}
     eng.close()
+    if args.workload == "llama8b-b8" and not args.no_extras:
+        del eng, weights, logits
+        torch.cuda.empty_cache()
+        out["extras"] = run_extras(args)
     print(json.dumps(out), flush=True)
+
+
+def host_cores():
+    """(host cores this process may run on, BLAS threads numpy uses)."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    return cores, blas
+
+
+# compact runs of the other workloads folded into the default line: each is its own bench.py process
+# (fresh device memory), with a bounded oracle sample for parity
+EXTRAS = [
+    ("mistral7b_int4_b8", ["--workload", "mistral7b-int4", "--steps", "32", "--warmup", "4", "--sweep", "",
+                           "--no-breakdown", "--parity-rows", "2"]),
+    ("prefill_16seg", ["--workload", "prefill", "--steps", "4", "--warmup", "1", "--no-breakdown"]),
+    ("llama8b_long_32k_b8", ["--workload", "llama8b-long", "--steps", "16", "--warmup", "2", "--no-breakdown",
+                             "--parity-rows", "1", "--fill", "copy"]),
+]
+
+
+def run_extras(args):
+    import subprocess
+    res = {}
+    for name, extra in EXTRAS:
+        cmd = [sys.executable, os.path.abspath(__file__)] + extra
+        log("extra %s: %s" % (name, " ".join(extra)))
+        t0 = time.time()
+        try:
+            p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=None, text=True, timeout=400)
+            line = [l for l in p.stdout.splitlines() if l.startswith("{")][-1] if p.returncode == 0 else None
+        except subprocess.TimeoutExpired:
+            line, p = None, None
+        if line is None:
+            res[name] = {"error": "rc %s" % (p.returncode if p is not None else "timeout")}
+            continue
+        d = json.loads(line)
+        rf = d.get("roofline") or {}
+        res[name] = {"value": d["value"], "unit": d["unit"], "ms_per_step": d["ms_per_step"], "steps": d["steps"],
+                     "workload": d["config"]["workload"], "data": d.get("data"),
+                     "hbm_frac_step": d.get("hbm_frac_step"),
+                     "roofline": {k: rf.get(k) for k in ("bound", "achieved", "peak", "unit", "frac", "kernel",
+                                                         "avg_launch_us")},
+                     "parity": d.get("parity_first_step") or d.get("parity_last_logits"),
+                     "cpu_baseline": d.get("cpu_baseline"), "wall_s": round(time.time() - t0, 1)}
+        log("extra %s: %s" % (name, json.dumps(res[name])))
+    return res
 
 
 def run_prefill(args, wl, torch, cbd, synth):
@@ -465,11 +538,7 @@ def run_prefill(args, wl, torch, cbd, synth):
     parity = None
     if not args.no_cpu_baseline:
         from oracle import OracleModel
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:  # pragma: no cover
-            cores = 1
+        cores, blas = host_cores()
         j = int(np.argmin(lens))  # the shortest segment: a bounded sample of the same workload
         got = logits[j].cpu().numpy().astype(np.float64)
         log("cpu baseline: oracle prefill of segment %d (%d tokens, all %d layers + lm_head)" % (j, lens[j],
@@ -479,7 +548,8 @@ def run_prefill(args, wl, torch, cbd, synth):
         c0 = time.perf_counter()
         ref = orc.prefill(sid, prompts[j].astype(np.int64))
         csecs = time.perf_counter() - c0
-        cpu = {"value": round(lens[j] / csecs, 3), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+        cpu = {"value": round(lens[j] / csecs, 3), "unit": "tok/s", "cores": int(cores), "blas_threads": int(blas),
+               "kind": "oracle",
                "sample": "prefill of the shortest of the 16 segments (%d tokens, float64, all 32 layers + lm_head), "
                          "%.1f s" % (lens[j], csecs)}
         err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
