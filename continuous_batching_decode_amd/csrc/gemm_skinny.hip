@@ -502,12 +502,26 @@ ksplit_gemm_kernel(SkinnyArgs a, int splits) {
     for (int i = 0; i < RT; ++i)
 #pragma unroll
       for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < splits; ++sp)
+    // several splits' loads in flight (one memory latency per MB splits), added in split order
+    constexpr int MB = RT * NB <= 4 ? 4 : (RT * NB <= 8 ? 2 : 1);
+    for (int sp0 = 0; sp0 < splits; sp0 += MB) {
+      f32x4_t t[MB][RT][NB];
 #pragma unroll
-      for (int i = 0; i < RT; ++i)
+      for (int u = 0; u < MB; ++u)
 #pragma unroll
-        for (int c = 0; c < NB; ++c)
-          acc[i][c] += load_agent_x4(a.part, (int)((base + (int64_t)sp * TILE_F + ((i * NB + c) * 64 + lane) * 4) * 4));
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+          for (int c = 0; c < NB; ++c)
+            t[u][i][c] = load_agent_x4(
+                a.part, (int)((base + (int64_t)min(sp0 + u, splits - 1) * TILE_F + ((i * NB + c) * 64 + lane) * 4) * 4));
+#pragma unroll
+      for (int u = 0; u < MB; ++u)
+        if (sp0 + u < splits)
+#pragma unroll
+          for (int i = 0; i < RT; ++i)
+#pragma unroll
+            for (int c = 0; c < NB; ++c) acc[i][c] += t[u][i][c];
+    }
     if (lane == 0) __hip_atomic_store(a.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   float inv[NB];
@@ -835,14 +849,26 @@ __global__ __launch_bounds__(64 * WN * WM, 2) void dense_gemm_kernel(SkinnyArgs 
     for (int i = 0; i < RT; ++i)
 #pragma unroll
       for (int c = 0; c < NB; ++c) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (holder)
-      for (int sp = 0; sp < splits; ++sp)
+    constexpr int MB = NB <= 4 ? 2 : 1;  // splits whose loads are in flight together (registers)
+    if (holder)  // added in split order
+      for (int sp0 = 0; sp0 < splits; sp0 += MB) {
+        f32x4_t t[MB][RT][NB];
 #pragma unroll
-        for (int i = 0; i < RT; ++i)
+        for (int u = 0; u < MB; ++u)
 #pragma unroll
-          for (int c = 0; c < NB; ++c)
-            acc[i][c] += load_agent_x4(
-                a.part, (int)((base + (int64_t)sp * TILE_F + ((wave * RT + i) * NB + c) * 128 + l32 * 4) * 4));
+          for (int i = 0; i < RT; ++i)
+#pragma unroll
+            for (int c = 0; c < NB; ++c)
+              t[u][i][c] = load_agent_x4(a.part, (int)((base + (int64_t)min(sp0 + u, splits - 1) * TILE_F +
+                                                        ((wave * RT + i) * NB + c) * 128 + l32 * 4) * 4));
+#pragma unroll
+        for (int u = 0; u < MB; ++u)
+          if (sp0 + u < splits)
+#pragma unroll
+            for (int i = 0; i < RT; ++i)
+#pragma unroll
+              for (int c = 0; c < NB; ++c) acc[i][c] += t[u][i][c];
+      }
     if (tid == 0) __hip_atomic_store(a.counters + tn, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
@@ -1032,6 +1058,23 @@ __global__ __launch_bounds__(64 * kWideWaves, (NB == 8 && RT == 4) ? 1 : 2) void
       }
     }
 
+  // the residual rows this wave's epilogue adds to (groups c = wave + NW q), requested before the
+  // merge and the norm so that their latency overlaps them
+  constexpr int NQ = NB / NW > 0 ? NB / NW : 1;
+  float4 hpre[NQ][RT][1];
+  auto prefetch_h = [&]() {
+    if constexpr (EPI == EPI_RESIDUAL) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int row = 8 * (wave + NW * q) + (lane & 7);
+        if (wave + NW * q < NB && row < a.rows && holder)
+#pragma unroll
+          for (int i = 0; i < RT; ++i)
+            hpre[q][i][0] = *reinterpret_cast<const float4*>(a.out + (int64_t)row * a.ldo + sub_row[i] + 4 * (lane >> 4));
+      }
+    }
+  };
+
   if (splits > 1) {
     constexpr int TILE_F = NB * RT * 32 * 4;  // floats of one workgroup's partial tile
     const int64_t base = (int64_t)tile * splits * TILE_F;
@@ -1047,18 +1090,33 @@ __global__ __launch_bounds__(64 * kWideWaves, (NB == 8 && RT == 4) ? 1 : 2) void
       s_last = __hip_atomic_fetch_add(a.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
     __syncthreads();
     if (!s_last) return;
+    prefetch_h();
+    // the splits' partial tiles with up to 4 splits' loads in flight (one memory latency per 4
+    // splits), added in split order
 #pragma unroll
     for (int c = 0; c < NB; ++c)
       if (c % NW == wave) {
 #pragma unroll
         for (int i = 0; i < RT; ++i) acc[i][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (holder)
-          for (int sp = 0; sp < splits; ++sp)
+          for (int sp0 = 0; sp0 < splits; sp0 += 4) {
+            f32x4_t t[4][RT];
 #pragma unroll
-            for (int i = 0; i < RT; ++i)
-              acc[i][c] += load_agent_x4(a.part, (int)((base + (int64_t)sp * TILE_F + ((c * RT + i) * 32 + l32) * 4) * 4));
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int i = 0; i < RT; ++i)
+                t[u][i] = load_agent_x4(
+                    a.part, (int)((base + (int64_t)min(sp0 + u, splits - 1) * TILE_F + ((c * RT + i) * 32 + l32) * 4) * 4));
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (sp0 + u < splits)
+#pragma unroll
+                for (int i = 0; i < RT; ++i) acc[i][c] += t[u][i];
+          }
       }
     if (tid == 0) __hip_atomic_store(a.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    prefetch_h();
   }
 
   // 1/rms of the rows (the same fixed order as the other kernels: per group of 16 partials in order,
@@ -1088,7 +1146,8 @@ __global__ __launch_bounds__(64 * kWideWaves, (NB == 8 && RT == 4) ? 1 : 2) void
 #pragma unroll
       for (int i = 0; i < RT; ++i) one[i][0] = acc[i][c];
       const float inv[1] = {a.ss ? inv_s[8 * c + (lane & 7)] : 1.f};
-      epilogue<RT, 1, EPI>(a, one, sub_row, 8 * c, a.rows - 8 * c, inv, lane, nullptr);
+      epilogue<RT, 1, EPI>(a, one, sub_row, 8 * c, a.rows - 8 * c, inv, lane,
+                           EPI == EPI_RESIDUAL ? &hpre[c / NW] : nullptr);
     }
 }
 
