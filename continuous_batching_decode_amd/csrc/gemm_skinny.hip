@@ -53,13 +53,27 @@ namespace {
 
 CBD_DEVICE bf16x8_t load_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
+// Constants of the int4 inner loops held in registers: gfx9 VALU instructions with three operands
+// take no literal, so with the constants in registers widening a code pair and unpacking a (scale,
+// bias) half are one instruction each (v_and_or_b32, v_and_b32).
+struct Int4Consts {
+  uint32_t bf16_128;  // 0x43004300: the bf16 pattern of 128 in both halves
+  uint32_t pair_mask; // 0x000F000F: one code in each half
+  uint32_t hi_mask;   // 0xFFFF0000
+  CBD_DEVICE static Int4Consts make() {
+    Int4Consts k{0x43004300u, 0x000F000Fu, 0xFFFF0000u};
+    asm volatile("" : "+v"(k.bf16_128), "+v"(k.pair_mask), "+v"(k.hi_mask));
+    return k;
+  }
+};
+
 // 8 int4 codes of one packed word -> bf16 (128 + q) in input order.
-CBD_DEVICE bf16x8_t widen_codes(uint32_t w) {
+CBD_DEVICE bf16x8_t widen_codes(uint32_t w, const Int4Consts& k) {
   u32x4_t r;
-  r[0] = (w & 0x000F000Fu) | 0x43004300u;
-  r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  r[0] = (w & k.pair_mask) | k.bf16_128;
+  r[1] = ((w >> 4) & k.pair_mask) | k.bf16_128;
+  r[2] = ((w >> 8) & k.pair_mask) | k.bf16_128;
+  r[3] = ((w >> 12) & k.pair_mask) | k.bf16_128;
   return as_frag(r);
 }
 
@@ -217,7 +231,7 @@ CBD_DEVICE void epilogue(const SkinnyArgs& a, f32x4_t (&acc)[RT][NB], const int 
 // fragments 2,3 the next). X[j][c] = activation fragment j of 8-row group c (hi and lo columns).
 template <int RT, int NB>
 CBD_DEVICE void int4_block(f32x4_t (&acc)[RT][NB], const u32x4_t (&Wq)[RT], const uint4 (&SB)[RT][2],
-                           const bf16x8_t (&X)[4][NB]) {
+                           const bf16x8_t (&X)[4][NB], const Int4Consts& k) {
   const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const bf16x8_t ones = as_frag(ones_u);
 #pragma unroll
@@ -232,14 +246,14 @@ CBD_DEVICE void int4_block(f32x4_t (&acc)[RT][NB], const u32x4_t (&Wq)[RT], cons
     }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      const bf16x8_t A0 = widen_codes(Wq[i][2 * h]), A1 = widen_codes(Wq[i][2 * h + 1]);
+      const bf16x8_t A0 = widen_codes(Wq[i][2 * h], k), A1 = widen_codes(Wq[i][2 * h + 1], k);
       const uint4 sb = SB[i][h];
       float sc[4], bc[4];
       const uint32_t pr[4] = {sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sc[e] = bf16_to_f32(pr[e] & 0xFFFFu);
-        bc[e] = bf16_to_f32(pr[e] >> 16) - 128.0f * sc[e];
+      for (int e = 0; e < 4; ++e) {  // (scale, bias) as bf16 halves: scale = low half, bias = high half
+        sc[e] = __uint_as_float(pr[e] << 16);
+        bc[e] = fmaf(-128.0f, sc[e], __uint_as_float(pr[e] & k.hi_mask));
       }
 #pragma unroll
       for (int c = 0; c < NB; ++c) {
@@ -247,7 +261,7 @@ CBD_DEVICE void int4_block(f32x4_t (&acc)[RT][NB], const u32x4_t (&Wq)[RT], cons
         t = mfma(A0, X[2 * h][c], t);
         t = mfma(A1, X[2 * h + 1][c], t);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][c][e] += sc[e] * t[e] + bc[e] * xsum[c][e];
+        for (int e = 0; e < 4; ++e) acc[i][c][e] = fmaf(bc[e], xsum[c][e], fmaf(sc[e], t[e], acc[i][c][e]));
       }
     }
   }
@@ -417,6 +431,7 @@ ksplit_gemm_kernel(SkinnyArgs a, int splits) {
     }
   } else {
     // int4: 128 inputs per stage; the same two-buffer pipeline as the bf16 path
+    const Int4Consts kc = Int4Consts::make();
     struct QBuf {
       u32x4_t Wq[RT];
       uint4 SB[RT][2];
@@ -440,24 +455,24 @@ ksplit_gemm_kernel(SkinnyArgs a, int splits) {
     ss_store();
     int st = 0;
     for (; st + 3 < total; st += 2) {
-      int4_block<RT, NB>(acc, b0.Wq, b0.SB, b0.X);
+      int4_block<RT, NB>(acc, b0.Wq, b0.SB, b0.X, kc);
       __builtin_amdgcn_sched_barrier(0);
       qload(b0, st + 2);
       __builtin_amdgcn_sched_barrier(0);
-      int4_block<RT, NB>(acc, b1.Wq, b1.SB, b1.X);
+      int4_block<RT, NB>(acc, b1.Wq, b1.SB, b1.X, kc);
       __builtin_amdgcn_sched_barrier(0);
       qload(b1, st + 3);
       __builtin_amdgcn_sched_barrier(0);
     }
-    int4_block<RT, NB>(acc, b0.Wq, b0.SB, b0.X);
+    int4_block<RT, NB>(acc, b0.Wq, b0.SB, b0.X, kc);
     if (st + 2 < total) {
       __builtin_amdgcn_sched_barrier(0);
       qload(b0, st + 2);
       __builtin_amdgcn_sched_barrier(0);
-      int4_block<RT, NB>(acc, b1.Wq, b1.SB, b1.X);
-      int4_block<RT, NB>(acc, b0.Wq, b0.SB, b0.X);
+      int4_block<RT, NB>(acc, b1.Wq, b1.SB, b1.X, kc);
+      int4_block<RT, NB>(acc, b0.Wq, b0.SB, b0.X, kc);
     } else {
-      int4_block<RT, NB>(acc, b1.Wq, b1.SB, b1.X);
+      int4_block<RT, NB>(acc, b1.Wq, b1.SB, b1.X, kc);
     }
   }
 
@@ -611,6 +626,7 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
     }
   } else {
     const int spc = KC / 128, total = Kr / 128;
+    const Int4Consts kc = Int4Consts::make();
     for (int st = 0; st < total; ++st) {
       if (st % spc == 0) stage_x(kbeg + (st / spc) * KC);
       u32x4_t Wq[RT];
@@ -624,7 +640,7 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int c = 0; c < NB; ++c) X[j][c] = xlds(c, kf0 + j);
-      int4_block<RT, NB>(acc, Wq, SB, X);
+      int4_block<RT, NB>(acc, Wq, SB, X, kc);
     }
   }
 
