@@ -23,11 +23,18 @@ def hipcc() -> str:
     return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
 
 
+def defines() -> list:
+    """Build options from the environment: CBD_DEFINES="NAME=VALUE ..." adds -DNAME=VALUE per item
+    (e.g. CBD_VALU_ROWS=4 CBD_VALU_DEPTH=2 for the vector-ALU small-batch products)."""
+    return ["-D" + d for d in os.environ.get("CBD_DEFINES", "").split() if d]
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source into libcbd.so (always rebuilds). Returns the library path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC] + srcs + ["-o", tmp]
+    cmd = ([hipcc()] + HIPCC_FLAGS + defines() + ["-I", os.path.join(ROOT, "include"), "-I", CSRC] + srcs +
+           ["-o", tmp])
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)

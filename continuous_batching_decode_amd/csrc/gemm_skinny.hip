@@ -285,6 +285,20 @@ CBD_DEVICE void load_scales(const SkinnyArgs& a, const int (&sub_row)[RT], int k
 
 // ============================================================================ k split
 
+// Build options for comparing vector-ALU inner products with the matrix cores at small batches:
+// CBD_VALU_ROWS = n > 0 makes the bf16 k-split kernel with one 8-row group use fp32 FMAs whenever
+// the batch has at most n rows, with CBD_VALU_DEPTH 32-input chunks in flight per wave. Off (0) by
+// default: the matrix-core path measured faster at every batch of 1..4 rows.
+#ifndef CBD_VALU_ROWS
+#define CBD_VALU_ROWS 0
+#endif
+#ifndef CBD_VALU_DEPTH
+#define CBD_VALU_DEPTH 4
+#endif
+constexpr int VALU_ROWS = CBD_VALU_ROWS;
+constexpr int VALU_DEPTH = CBD_VALU_DEPTH;
+static_assert(VALU_ROWS >= 0 && VALU_ROWS <= 8, "at most one 8-row group");
+
 // Largest workgroup an instantiation is compiled for: 16 waves leave 128 registers per lane, enough
 // for one subtile and one column tile; int4 with two row groups gets 4 waves (its stages hold the
 // codes, their scales and 8 activation fragments); the others get 8 waves (256 registers).
@@ -370,7 +384,100 @@ ksplit_gemm_kernel(SkinnyArgs a, int splits) {
     }
   }
 
+  bool valu_done = false;
+  if constexpr (FMT == FMT_BF16 && NB == 1 && VALU_ROWS > 0) {
+    // Vector-ALU inner products (a build option kept for comparison with the matrix cores at
+    // B <= VALU_ROWS). Lane l holds inputs 8g..8g+7 (g = l/16) of row l%16 of each 32-input chunk;
+    // the activations it needs are columns b (hi) and 8 + b (lo) of the fragment's lanes 16g + b and
+    // 16g + 8 + b. Every lane keeps RT x VALU_ROWS partial sums; a VALU_DEPTH-chunk ring of loads.
+    const int chunks = kw / 32;
+    if (rows_valid <= VALU_ROWS && chunks % VALU_DEPTH == 0) {
+      constexpr int BV = VALU_ROWS > 0 ? VALU_ROWS : 1;  // (array extents of the default build)
+      const uint16_t* xg = xr[0] - 8 * lane + 128 * (lane >> 4);
+      struct VBuf {
+        u32x4_t A[RT];
+        u32x4_t H[BV], L[BV];
+      };
+      auto vload = [&](VBuf& f, int ch) {
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+          f.A[i] = load_stream(reinterpret_cast<const uint16_t*>(wr[i]) + (int64_t)ch * 512);
+#pragma unroll
+        for (int b = 0; b < BV; ++b) {
+          f.H[b] = *reinterpret_cast<const u32x4_t*>(xg + ch * 512 + 8 * b);
+          f.L[b] = *reinterpret_cast<const u32x4_t*>(xg + ch * 512 + 8 * (8 + b));
+        }
+      };
+      float pv[RT][BV];
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int b = 0; b < BV; ++b) pv[i][b] = 0.f;
+      auto vcompute = [&](const VBuf& f) {
+        float xv[BV][8];
+#pragma unroll
+        for (int b = 0; b < BV; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {  // word q: input 2q in the low half, 2q + 1 in the high half
+            xv[b][2 * q] = __uint_as_float(f.H[b][q] << 16) + __uint_as_float(f.L[b][q] << 16);
+            xv[b][2 * q + 1] = __uint_as_float(f.H[b][q] & 0xFFFF0000u) + __uint_as_float(f.L[b][q] & 0xFFFF0000u);
+          }
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float w0 = __uint_as_float(f.A[i][q] << 16), w1 = __uint_as_float(f.A[i][q] & 0xFFFF0000u);
+#pragma unroll
+            for (int b = 0; b < BV; ++b) pv[i][b] = fmaf(w1, xv[b][2 * q + 1], fmaf(w0, xv[b][2 * q], pv[i][b]));
+          }
+      };
+      VBuf vb[VALU_DEPTH];
+#pragma unroll
+      for (int j = 0; j < VALU_DEPTH; ++j) {
+        vload(vb[j], j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      ss_store();
+      int ch = 0;
+      for (; ch + VALU_DEPTH < chunks; ch += VALU_DEPTH) {
+#pragma unroll
+        for (int j = 0; j < VALU_DEPTH; ++j) {
+          vcompute(vb[j]);
+          __builtin_amdgcn_sched_barrier(0);
+          vload(vb[j], ch + VALU_DEPTH + j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < VALU_DEPTH; ++j) vcompute(vb[j]);
+      // sums over the 4 input groups, then into the matrix-core accumulator layout: lane l holds
+      // rows 4g + e of column l%16; columns b < BV (hi) take the whole product, all others zero
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int b = 0; b < BV; ++b) {
+          pv[i][b] += __shfl_xor(pv[i][b], 16, 64);
+          pv[i][b] += __shfl_xor(pv[i][b], 32, 64);
+        }
+      const int col = lane & 15;
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = 0.f;
+#pragma unroll
+          for (int b = 0; b < BV; ++b) {
+            const float t = __shfl(pv[i][b], 4 * (lane >> 4) + e, 64);
+            if (col == b) v = t;
+          }
+          acc[i][0][e] = v;
+        }
+      valu_done = true;
+    }
+  }
+
   if constexpr (FMT == FMT_BF16) {
+   if (!valu_done) {
     struct Buf {
       u32x4_t A[UC][RT];
       bf16x8_t X[UC][NB];
@@ -429,6 +536,7 @@ ksplit_gemm_kernel(SkinnyArgs a, int splits) {
     } else {
       compute(b1);
     }
+   }
   } else {
     // int4: 128 inputs per stage; the same two-buffer pipeline as the bf16 path
     const Int4Consts kc = Int4Consts::make();
