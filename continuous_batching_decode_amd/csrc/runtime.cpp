@@ -217,21 +217,32 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 // Build the (row, key range) work items of one decode step. The attention kernel runs one wave per
 // item and KV head and streams keys in blocks of 32, so ranges start at multiples of 32. Ranges are
-// sized so that about kDecodeWaves waves cover the step's keys (two per SIMD of the chip), at least
-// kMinChunk keys each; every split of a row gets a partial slot.
+// sized so that about kDecodeWaves waves cover the step's keys, at least kMinChunk keys each; every
+// split of a row gets a partial slot. Steps of at most kFewRows rows over bf16 or 8-bit K/V aim at
+// kDecodeWavesFew waves (one per SIMD): a wave with two bf16 blocks in flight streams about 13 GB/s,
+// so about 600 waves already reach the HBM rate, and more waves only add splits that the merges pay
+// for (32k-token rows: 188 -> 170 us per layer). Larger batches (each row needs few splits; more waves
+// even out the tail) and 4-bit K/V (a fifth of the bytes per key: more waves to reach the rate) keep
+// two per SIMD.
 #ifndef CBD_DECODE_WAVES
 #define CBD_DECODE_WAVES 2048
 #endif
+#ifndef CBD_DECODE_WAVES_FEW
+#define CBD_DECODE_WAVES_FEW 1024
+#endif
+constexpr size_t kFewRows = 16;
 #ifndef CBD_DECODE_MIN_CHUNK
 #define CBD_DECODE_MIN_CHUNK 256
 #endif
-constexpr int64_t kDecodeWaves = CBD_DECODE_WAVES;
+constexpr int64_t kDecodeWaves = CBD_DECODE_WAVES, kDecodeWavesFew = CBD_DECODE_WAVES_FEW;
 constexpr int64_t kMinChunk = CBD_DECODE_MIN_CHUNK;
 constexpr int64_t kMaxSplits = 64;
 int plan_decode_items(const cbd_ctx* c, const std::vector<RowMeta>& rows, AttnItem* items, int32_t* row_parts) {
   int64_t total = 0;
   for (const RowMeta& r : rows) total += r.pos + 1;
-  const int64_t per_wave = (total * c->cfg.n_kv_heads + kDecodeWaves - 1) / kDecodeWaves;
+  const int64_t waves =
+      rows.size() <= kFewRows && c->cfg.kv_format != CBD_KV_AFFINE4 ? kDecodeWavesFew : kDecodeWaves;
+  const int64_t per_wave = (total * c->cfg.n_kv_heads + waves - 1) / waves;
   int64_t longest = 0;
   bool forked = false;
   for (const RowMeta& r : rows) {
