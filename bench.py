@@ -82,10 +82,12 @@ T0 = time.time()
 
 
 # per workload: the committed counter summary of its roofline kernel and that kernel's source file
+ATTN_SRC = os.path.join(ROOT, "continuous_batching_decode_amd", "csrc", "attention.hip")
 COMMITTED = {
     "llama8b-b8": (TRAFFIC_FILE, KERNEL_SRC),
-    "llama8b-long-kv8": (os.path.join(ROOT, "profiles", "traffic_attention_q8_llama8b_long.md"),
-                         os.path.join(ROOT, "continuous_batching_decode_amd", "csrc", "attention.hip")),
+    "mistral7b-int4": (os.path.join(ROOT, "profiles", "traffic_gate_up_int4_mistral7b_b8.md"), KERNEL_SRC),
+    "llama8b-long": (os.path.join(ROOT, "profiles", "traffic_attention_llama8b_long.md"), ATTN_SRC),
+    "llama8b-long-kv8": (os.path.join(ROOT, "profiles", "traffic_attention_q8_llama8b_long.md"), ATTN_SRC),
 }
 
 
@@ -460,8 +462,9 @@ def run_extras(args):
         res[name] = {"value": d["value"], "unit": d["unit"], "ms_per_step": d["ms_per_step"], "steps": d["steps"],
                      "workload": d["config"]["workload"], "data": d.get("data"),
                      "hbm_frac_step": d.get("hbm_frac_step"),
-                     "roofline": {k: rf.get(k) for k in ("bound", "achieved", "peak", "unit", "frac", "kernel",
-                                                         "avg_launch_us")},
+                     "roofline": {k: rf.get(k) for k in ("bound", "achieved", "peak", "unit", "frac", "traffic",
+                                                         "kernel", "avg_launch_us", "trace_avg_launch_us",
+                                                         "frac_at_trace_avg")},
                      "parity": d.get("parity_first_step") or d.get("parity_last_logits"),
                      "cpu_baseline": d.get("cpu_baseline"), "wall_s": round(time.time() - t0, 1)}
         log("extra %s: %s" % (name, json.dumps(res[name])))
