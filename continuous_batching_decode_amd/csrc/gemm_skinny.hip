@@ -810,6 +810,10 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
 #ifndef CBD_DENSE_DEPTH
 #define CBD_DENSE_DEPTH 2
 #endif
+#ifndef CBD_DENSE_READ_AHEAD
+#define CBD_DENSE_READ_AHEAD 1
+#endif
+constexpr bool DENSE_READ_AHEAD = CBD_DENSE_READ_AHEAD != 0;
 namespace {
 // LDS of a dense workgroup: two stages of (4 wn + nbw wm) fragments, 1/rms per activation row
 inline size_t dense_lds(int wn, int wm, int nbw) {
@@ -930,6 +934,59 @@ __global__ __launch_bounds__(64 * WN * WM, 2) void dense_gemm_kernel(SkinnyArgs 
         for (int c = 0; c < 4; ++c) acc[i][c0 + c] = mfma(A[i], X[c], acc[i][c0 + c]);
     }
   };
+  if constexpr (NBW == 8 && DENSE_READ_AHEAD) {
+    // Prefill tiles: the operands of the next stage are read from LDS while the matrix cores still
+    // work on this one, so a stage starts with its first operands in registers. Stage s: first half
+    // (activation groups 0..3, taken group by group; each freed X register receives group 4 + c of
+    // the stage); put stage s + 1 into the other buffer and synchronise (every wave is then done
+    // with that buffer's previous contents: their reads completed before the last barrier); second
+    // half (groups 4..7): groups 4 and 5 first, their registers receiving groups 0 and 1 of stage
+    // s + 1; then subtile by subtile with groups 6 and 7, each freed A register receiving the
+    // subtile of stage s + 1; groups 2 and 3 of stage s + 1 last. Register use stays at 4 A and
+    // 4 X fragments.
+    const uint16_t* xw = lds + (NWF + NBW * wm) * 512 + 8 * lane;
+    auto rdA = [&](int buf, int i) { return *reinterpret_cast<const bf16x8_t*>(lds + buf * STAGE + fa[i] * 512 + 8 * lane); };
+    auto rdX = [&](int buf, int c) { return *reinterpret_cast<const bf16x8_t*>(xw + buf * STAGE + c * 512); };
+    bf16x8_t A[RT], X[4];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) A[i] = rdA(0, i);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) X[c] = rdX(0, c);
+    for (int kf = 0; kf < nk; kf += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const int buf = j & 1, nbuf = buf ^ 1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+          for (int i = 0; i < RT; ++i) acc[i][c] = mfma(A[i], X[c], acc[i][c]);
+          X[c] = rdX(buf, 4 + c);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        put(rr[j], nbuf);
+        __syncthreads();
+        fetch(rr[j], min(kf + j + 1 + D, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int i = 0; i < RT; ++i) acc[i][4 + c] = mfma(A[i], X[c], acc[i][4 + c]);
+          X[c] = rdX(nbuf, c);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+          acc[i][6] = mfma(A[i], X[2], acc[i][6]);
+          acc[i][7] = mfma(A[i], X[3], acc[i][7]);
+          A[i] = rdA(nbuf, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        X[2] = rdX(nbuf, 2);
+        X[3] = rdX(nbuf, 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
   // stage s is in LDS buffer s & 1; register set s % D holds stage s + 1 and is put after computing
   // s, then refilled with stage s + 1 + D. nk is a multiple of D (and even), so the loop body has no
   // branch and the load waits stay exact.
@@ -942,6 +999,7 @@ __global__ __launch_bounds__(64 * WN * WM, 2) void dense_gemm_kernel(SkinnyArgs 
       fetch(rr[j], min(kf + j + 1 + D, nk - 1));
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
   }
 
   if (splits > 1) {
