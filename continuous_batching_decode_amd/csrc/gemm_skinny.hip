@@ -801,19 +801,17 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
 // Many activation rows: WN x WM waves of 64 weight rows x 8*NBW activation rows each, so a
 // workgroup covers TN = 64 WN weight rows x TM = 8 NBW WM activation rows (prefill: 256 x 128 with
 // 64 x 64 waves; decode steps: 128 x 64 or 128 x 32 with 64 x 32 waves). Each stage copies one
-// 32-input fragment column of both operands to LDS (the fragments are already MFMA operands),
-// double-buffered with one barrier per stage and two stages of loads in flight. SwiGLU tiles hold
-// TN/2 gate rows and the matching up rows. bf16 weights only. With splits > 1 (one row tile),
-// workgroup (tile, s) adds the inputs [s K/splits, (s + 1) K/splits); the last workgroup of a tile
-// to arrive adds the partial tiles in order (agent-scope 16-byte accesses and an arrival counter, as
-// the row split).
+// 32-input fragment column to LDS (the fragments are already MFMA operands), double-buffered with
+// one barrier per stage and two stages of loads in flight: both operands for tiles of 4 activation
+// groups per wave, the activations only for tiles of 8 (their weight operands go straight to
+// registers). SwiGLU tiles hold TN/2 gate rows and the matching up rows. bf16 weights only. With
+// splits > 1 (one row tile), workgroup (tile, s) adds the inputs [s K/splits, (s + 1) K/splits);
+// the last workgroup of a tile to arrive adds the partial tiles in order (agent-scope 16-byte
+// accesses and an arrival counter, as the row split).
 #ifndef CBD_DENSE_DEPTH
 #define CBD_DENSE_DEPTH 2
 #endif
-#ifndef CBD_DENSE_READ_AHEAD
-#define CBD_DENSE_READ_AHEAD 1
-#endif
-constexpr bool DENSE_READ_AHEAD = CBD_DENSE_READ_AHEAD != 0;
+
 namespace {
 // LDS of a dense workgroup: two stages of (4 wn + nbw wm) fragments, 1/rms per activation row
 inline size_t dense_lds(int wn, int wm, int nbw) {
@@ -892,18 +890,19 @@ __global__ __launch_bounds__(64 * WN * WM, 2) void dense_gemm_kernel(SkinnyArgs 
       *reinterpret_cast<u32x4_t*>(lds + buf * STAGE + (wave + NW * i) * 512 + 8 * lane) = r[i];
   };
   u32x4_t rr[D][PER];
-
-  fetch(rr[0], 0);
-  put(rr[0], 0);
-  __syncthreads();
-  // stages past the last refetch the last one (unused): loads stay unconditional
-  // (scheduling barriers keep the loads in register-set order here and in the loop, so that the
-  // waits at the loop head count the same outstanding loads on entry and on the back edge)
+  auto prologue = [&]() {
+    fetch(rr[0], 0);
+    put(rr[0], 0);
+    __syncthreads();
+    // stages past the last refetch the last one (unused): loads stay unconditional
+    // (scheduling barriers keep the loads in register-set order here and in the loop, so that the
+    // waits at the loop head count the same outstanding loads on entry and on the back edge)
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    fetch(rr[j], min(1 + j, nk - 1));
-    __builtin_amdgcn_sched_barrier(0);
-  }
+    for (int j = 0; j < D; ++j) {
+      fetch(rr[j], min(1 + j, nk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
   f32x4_t acc[RT][NB];
 #pragma unroll
@@ -934,59 +933,104 @@ __global__ __launch_bounds__(64 * WN * WM, 2) void dense_gemm_kernel(SkinnyArgs 
         for (int c = 0; c < 4; ++c) acc[i][c0 + c] = mfma(A[i], X[c], acc[i][c0 + c]);
     }
   };
-  if constexpr (NBW == 8 && DENSE_READ_AHEAD) {
-    // Prefill tiles: the operands of the next stage are read from LDS while the matrix cores still
-    // work on this one, so a stage starts with its first operands in registers. Stage s: first half
-    // (activation groups 0..3, taken group by group; each freed X register receives group 4 + c of
-    // the stage); put stage s + 1 into the other buffer and synchronise (every wave is then done
+  if constexpr (NBW == 8) {
+    // Tiles of 8 activation groups per wave (prefill; 64-row decode lm_head): the weight operands
+    // are loaded straight into registers (a ring of two stages: the set a stage used is refilled
+    // with the stage after next once its products are issued), and the LDS stages hold the
+    // activation fragments only, double-buffered. The two waves sharing weight rows load the same
+    // fragments (the second from L2). The activations of the next stage are read from LDS while the
+    // matrix cores still work on this one, so a stage starts with its first operands in registers.
+    // Stage s: first half (groups 0..3, group by group; each freed X register receives group 4 + c
+    // of the stage); put stage s + 1 into the other buffer and synchronise (every wave is then done
     // with that buffer's previous contents: their reads completed before the last barrier); second
     // half (groups 4..7): groups 4 and 5 first, their registers receiving groups 0 and 1 of stage
-    // s + 1; then subtile by subtile with groups 6 and 7, each freed A register receiving the
-    // subtile of stage s + 1; groups 2 and 3 of stage s + 1 last. Register use stays at 4 A and
-    // 4 X fragments.
-    const uint16_t* xw = lds + (NWF + NBW * wm) * 512 + 8 * lane;
-    auto rdA = [&](int buf, int i) { return *reinterpret_cast<const bf16x8_t*>(lds + buf * STAGE + fa[i] * 512 + 8 * lane); };
-    auto rdX = [&](int buf, int c) { return *reinterpret_cast<const bf16x8_t*>(xw + buf * STAGE + c * 512); };
-    bf16x8_t A[RT], X[4];
+    // s + 1; then groups 6 and 7, after which their registers receive groups 2 and 3 of stage s + 1.
+    // Measured against staging the weights through LDS as well (prefill gate/up at 7797 tokens):
+    // 3303 -> 3203 us with the read-ahead, 3222 us for neither.
+    constexpr int FX = NBW * WM, PX = FX / NW;  // activation fragments per stage, copies per thread
+    static_assert(FX % NW == 0, "activation fragments split evenly over the waves");
+    constexpr int SX = FX * 512;
+    const uint16_t* xsrc[PX];
 #pragma unroll
-    for (int i = 0; i < RT; ++i) A[i] = rdA(0, i);
+    for (int p = 0; p < PX; ++p)
+      xsrc[p] = a.x + ((int64_t)((m0 >> 3) + wave + NW * p) * nk_all + kf0) * 512 + 8 * lane;
+    const uint16_t* wsrc[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int grow = dense_row<EPI, NWF>(a, n0, fa[i]);
+      const int sg = seg_of(a, grow);
+      wsrc[i] = reinterpret_cast<const uint16_t*>(a.w[sg]) +
+                ((int64_t)((grow - seg_begin(a, sg)) >> 4) * nk_all + kf0) * 512 + 8 * lane;
+    }
+    auto xfetch = [&](u32x4_t (&r)[PX], int kf) {
+#pragma unroll
+      for (int p = 0; p < PX; ++p) r[p] = *reinterpret_cast<const u32x4_t*>(xsrc[p] + (int64_t)kf * 512);
+    };
+    auto xput = [&](const u32x4_t (&r)[PX], int buf) {
+#pragma unroll
+      for (int p = 0; p < PX; ++p)
+        *reinterpret_cast<u32x4_t*>(lds + buf * SX + (wave + NW * p) * 512 + 8 * lane) = r[p];
+    };
+    auto wfetch = [&](u32x4_t (&w)[RT], int kf) {  // cached loads: the other activation tiles reuse them
+#pragma unroll
+      for (int i = 0; i < RT; ++i) w[i] = *reinterpret_cast<const u32x4_t*>(wsrc[i] + (int64_t)kf * 512);
+    };
+    const uint16_t* xw = lds + (NBW * wm) * 512 + 8 * lane;
+    auto rdX = [&](int buf, int c) { return *reinterpret_cast<const bf16x8_t*>(xw + buf * SX + c * 512); };
+    u32x4_t xr[D][PX], W[2][RT];
+    xfetch(xr[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wfetch(W[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wfetch(W[1], min(1, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    xput(xr[0], 0);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      xfetch(xr[j], min(1 + j, nk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bf16x8_t X[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) X[c] = rdX(0, c);
     for (int kf = 0; kf < nk; kf += D) {
 #pragma unroll
-      for (int j = 0; j < D; ++j) {
+      for (int j = 0; j < D; ++j) {  // stage s = kf + j: activations in buffer s & 1, weights in W[s & 1]
         const int buf = j & 1, nbuf = buf ^ 1;
+        u32x4_t (&A)[RT] = W[j & 1];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
 #pragma unroll
-          for (int i = 0; i < RT; ++i) acc[i][c] = mfma(A[i], X[c], acc[i][c]);
+          for (int i = 0; i < RT; ++i) acc[i][c] = mfma(as_frag(A[i]), X[c], acc[i][c]);
           X[c] = rdX(buf, 4 + c);
           __builtin_amdgcn_sched_barrier(0);
         }
-        put(rr[j], nbuf);
+        xput(xr[j], nbuf);
         __syncthreads();
-        fetch(rr[j], min(kf + j + 1 + D, nk - 1));
+        xfetch(xr[j], min(kf + j + 1 + D, nk - 1));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
-          for (int i = 0; i < RT; ++i) acc[i][4 + c] = mfma(A[i], X[c], acc[i][4 + c]);
+          for (int i = 0; i < RT; ++i) acc[i][4 + c] = mfma(as_frag(A[i]), X[c], acc[i][4 + c]);
           X[c] = rdX(nbuf, c);
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
-          acc[i][6] = mfma(A[i], X[2], acc[i][6]);
-          acc[i][7] = mfma(A[i], X[3], acc[i][7]);
-          A[i] = rdA(nbuf, i);
-          __builtin_amdgcn_sched_barrier(0);
+          acc[i][6] = mfma(as_frag(A[i]), X[2], acc[i][6]);
+          acc[i][7] = mfma(as_frag(A[i]), X[3], acc[i][7]);
         }
+        __builtin_amdgcn_sched_barrier(0);
         X[2] = rdX(nbuf, 2);
         X[3] = rdX(nbuf, 3);
+        wfetch(A, min(kf + j + 2, nk - 1));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   } else {
+  prologue();
   // stage s is in LDS buffer s & 1; register set s % D holds stage s + 1 and is put after computing
   // s, then refilled with stage s + 1 + D. nk is a multiple of D (and even), so the loop body has no
   // branch and the load waits stay exact.
