@@ -267,18 +267,35 @@ CBD_DEVICE void int4_block(f32x4_t (&acc)[RT][NB], const u32x4_t (&Wq)[RT], cons
   }
 }
 
-// scale/bias pairs of output rows 4g..4g+3 of each subtile for groups (k0/64, k0/64 + 1)
+// Where the scale/bias pairs of output rows 4g..4g+3 of each subtile are: group j of subtile i at
+// p[i] + j * stride[i] (bf16 elements). Computed once per wave, before the stream: the segment
+// lookup indexes the kernel arguments dynamically, which the compiler serves with scalar memory
+// loads and a wait, so it stays out of the loop.
 template <int RT>
-CBD_DEVICE void load_scales(const SkinnyArgs& a, const int (&sub_row)[RT], int k0, int g, uint4 (&SB)[RT][2]) {
+struct ScaleRows {
+  const uint16_t* p[RT];
+  int64_t stride[RT];
+};
+template <int RT>
+CBD_DEVICE ScaleRows<RT> scale_rows(const SkinnyArgs& a, const int (&sub_row)[RT], int g) {
+  ScaleRows<RT> r;
 #pragma unroll
   for (int i = 0; i < RT; ++i) {
     const int s = seg_of(a, sub_row[i]);
-    const int sb = seg_begin(a, s), rows = a.seg_end[s] - sb;
-    const uint16_t* ar = reinterpret_cast<const uint16_t*>(a.aux[s]) + (int64_t)(sub_row[i] - sb + 4 * g) * 2;
+    const int sb = seg_begin(a, s);
+    r.p[i] = reinterpret_cast<const uint16_t*>(a.aux[s]) + (int64_t)(sub_row[i] - sb + 4 * g) * 2;
+    r.stride[i] = (int64_t)(a.seg_end[s] - sb) * 2;
+  }
+  return r;
+}
+// scale/bias pairs of groups (k0/64, k0/64 + 1)
+template <int RT>
+CBD_DEVICE void load_scales(const ScaleRows<RT>& r, int k0, uint4 (&SB)[RT][2]) {
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      SB[i][h] = *reinterpret_cast<const uint4*>(ar + (int64_t)((k0 >> 6) + h) * rows * 2);
-  }
+      SB[i][h] = *reinterpret_cast<const uint4*>(r.p[i] + (int64_t)((k0 >> 6) + h) * r.stride[i]);
 }
 
 }  // namespace
@@ -540,6 +557,7 @@ ksplit_gemm_kernel(SkinnyArgs a, int splits) {
   } else {
     // int4: 128 inputs per stage; the same two-buffer pipeline as the bf16 path
     const Int4Consts kc = Int4Consts::make();
+    const ScaleRows<RT> srows = scale_rows<RT>(a, sub_row, lane >> 4);
     struct QBuf {
       u32x4_t Wq[RT];
       uint4 SB[RT][2];
@@ -548,7 +566,7 @@ ksplit_gemm_kernel(SkinnyArgs a, int splits) {
     auto qload = [&](QBuf& f, int st) {
 #pragma unroll
       for (int i = 0; i < RT; ++i) f.Wq[i] = load_stream(reinterpret_cast<const uint32_t*>(wr[i]) + (int64_t)st * 256);
-      load_scales<RT>(a, sub_row, k0 + st * 128, lane >> 4, f.SB);
+      load_scales<RT>(srows, k0 + st * 128, f.SB);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -735,6 +753,7 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
   } else {
     const int spc = KC / 128, total = Kr / 128;
     const Int4Consts kc = Int4Consts::make();
+    const ScaleRows<RT> srows = scale_rows<RT>(a, sub_row, lane >> 4);
     for (int st = 0; st < total; ++st) {
       if (st % spc == 0) stage_x(kbeg + (st / spc) * KC);
       u32x4_t Wq[RT];
@@ -742,7 +761,7 @@ __global__ __launch_bounds__(256) void rowsplit_gemm_kernel(SkinnyArgs a) {
       bf16x8_t X[4][NB];
 #pragma unroll
       for (int i = 0; i < RT; ++i) Wq[i] = load_stream(reinterpret_cast<const uint32_t*>(wr[i]) + (int64_t)st * 256);
-      load_scales<RT>(a, sub_row, kbeg + st * 128, lane >> 4, SB);
+      load_scales<RT>(srows, kbeg + st * 128, SB);
       const int kf0 = (st % spc) * 4;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
