@@ -274,7 +274,7 @@ CBD_DEVICE void int4_block(f32x4_t (&acc)[RT][NB], const u32x4_t (&Wq)[RT], cons
 template <int RT>
 struct ScaleRows {
   const uint16_t* p[RT];
-  int64_t stride[RT];
+  uint32_t stride[RT];  // (a table holds K/64 x N pairs: element offsets fit 32 bits)
 };
 template <int RT>
 CBD_DEVICE ScaleRows<RT> scale_rows(const SkinnyArgs& a, const int (&sub_row)[RT], int g) {
@@ -284,7 +284,7 @@ CBD_DEVICE ScaleRows<RT> scale_rows(const SkinnyArgs& a, const int (&sub_row)[RT
     const int s = seg_of(a, sub_row[i]);
     const int sb = seg_begin(a, s);
     r.p[i] = reinterpret_cast<const uint16_t*>(a.aux[s]) + (int64_t)(sub_row[i] - sb + 4 * g) * 2;
-    r.stride[i] = (int64_t)(a.seg_end[s] - sb) * 2;
+    r.stride[i] = (uint32_t)(a.seg_end[s] - sb) * 2u;
   }
   return r;
 }
@@ -295,7 +295,7 @@ CBD_DEVICE void load_scales(const ScaleRows<RT>& r, int k0, uint4 (&SB)[RT][2]) 
   for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      SB[i][h] = *reinterpret_cast<const uint4*>(r.p[i] + (int64_t)((k0 >> 6) + h) * r.stride[i]);
+      SB[i][h] = *reinterpret_cast<const uint4*>(r.p[i] + (uint32_t)((k0 >> 6) + h) * r.stride[i]);
 }
 
 }  // namespace
