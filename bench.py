@@ -164,12 +164,19 @@ def main():
         n = args.copy_probe_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)  # device-to-device copy: n bytes read, n bytes written
-        for _ in range(5):
-            torch.bitwise_not(src, out=dst)  # the same traffic through an elementwise kernel
-        torch.cuda.synchronize()
-        log("copy probe: 2 x 5 passes over %d MiB" % args.copy_probe_mib)
+        rates = {}
+        for name, op in (("copy", lambda: dst.copy_(src)),  # device-to-device copy: n bytes read, n written
+                         ("elementwise", lambda: torch.bitwise_not(src, out=dst))):  # the same traffic
+            op()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                op()
+            e1.record()
+            torch.cuda.synchronize()
+            rates[name] = round(2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        log("copy probe: 2 x 5 passes over %d MiB: %s GB/s (bytes read + written)" % (args.copy_probe_mib, rates))
+        print(json.dumps({"copy_probe_mib": args.copy_probe_mib, "GBps_read_plus_written": rates}), flush=True)
         return
 
     if args.workload == "continuous":
