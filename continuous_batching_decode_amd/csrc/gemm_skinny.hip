@@ -321,7 +321,7 @@ static_assert(VALU_ROWS >= 0 && VALU_ROWS <= 8, "at most one 8-row group");
 // codes, their scales and 8 activation fragments); the others get 8 waves (256 registers).
 template <int RT, int NB, int EPI, int FMT, int UC>
 __global__ __launch_bounds__(((RT == 1 && NB == 1) ? 1024 : (FMT == FMT_INT4 && NB > 1) ? 256 : 512)) void
-ksplit_gemm_kernel(SkinnyArgs a, int splits) {
+ksplit_gemm_kernel(SkinnyArgs a, int splits, int split_from) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int ROWS = 8 * NB;  // activation rows: NB groups of 8
   constexpr int NACC = RT * NB * 4;
@@ -329,8 +329,18 @@ ksplit_gemm_kernel(SkinnyArgs a, int splits) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // workgroup (tile, split) takes inputs [split K/splits, (split + 1) K/splits), its waves a
   // contiguous 1/nw of that range each
-  const int tile = blockIdx.x / splits, split = blockIdx.x - tile * splits, xblk = blockIdx.y;
-  const int K = a.K, kw = K / (nw * splits), k0 = split * (K / splits) + wave * kw;
+  // Tiles below split_from take one workgroup each (the whole K); the others take `splits`
+  // workgroups, so that the work per compute unit evens out when the tiles are not a whole
+  // multiple of the units (ns: this workgroup's split count).
+  int tile, split, ns;
+  if ((int)blockIdx.x < split_from) {
+    tile = blockIdx.x, split = 0, ns = 1;
+  } else {
+    const int r = blockIdx.x - split_from;
+    tile = split_from + r / splits, split = r - (r / splits) * splits, ns = splits;
+  }
+  const int xblk = blockIdx.y;
+  const int K = a.K, kw = K / (nw * ns), k0 = split * (K / ns) + wave * kw;
   const int col0 = xblk * ROWS;
   const int rows_valid = min(ROWS, a.rows - col0);
   float* red = reinterpret_cast<float*>(smem);              // [nw-1][NACC][64]
@@ -624,11 +634,11 @@ ksplit_gemm_kernel(SkinnyArgs a, int splits) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][c][e] += src[((i * NB + c) * 4 + e) * 64 + lane];
   }
-  if (splits > 1) {
+  if (ns > 1) {
     // K split over workgroups (to even out the work per compute unit): wave 0 of each stores its
     // sums (agent scope); the last to arrive adds the splits in order
     constexpr int TILE_F = NACC * 64;
-    const int64_t base = (int64_t)tile * splits * TILE_F;
+    const int64_t base = (int64_t)(tile - split_from) * splits * TILE_F;
 #pragma unroll
     for (int i = 0; i < RT; ++i)
 #pragma unroll
@@ -1477,6 +1487,9 @@ static size_t ksplit_lds(int nw, int rt, int nb) {
 #ifndef CBD_WIDE_KS
 #define CBD_WIDE_KS 1
 #endif
+#ifndef CBD_KS_MIXED_SPLIT
+#define CBD_KS_MIXED_SPLIT 1
+#endif
 #ifndef CBD_KS_MAX_SPLITS
 #define CBD_KS_MAX_SPLITS 4
 #endif
@@ -1638,6 +1651,19 @@ SkinnyPlan plan_skinny(int epi, int fmt, int N, int K, int rows, int x_blocks, i
              K % (p.splits * 2 * nw * ks_unit) == 0 && K / (p.splits * 2 * nw) >= 2 * ks_unit)
         p.splits *= 2;
     }
+    // Tiles a whole number of units plus half a unit (QKV: 384 on 256 units, gate/up: 896) leave half
+    // the units one tile more than the others: the last half-unit of tiles is split in two instead,
+    // so that every unit gets the same inputs and only those tiles pay the merge (8B shape, B = 8:
+    // gate/up 40.5 -> 39.5 us, QKV 13.6 -> 13.2 us; B = 16 +1.5%). Not for int4 weights, whose
+    // shorter streams do not repay the merge (Mistral-7B gate/up 21.7 -> 22.5 us).
+    if (force == 0 && CBD_KS_MIXED_SPLIT && fmt == FMT_BF16 && p.splits == 1) {
+      const int units = plan_compute_units();
+      if (ks_tiles > units && ks_tiles % units == units / 2 && K % (2 * nw * ks_unit) == 0 &&
+          K / (2 * nw) >= 2 * ks_unit) {
+        p.splits = 2;
+        p.split_from = ks_tiles - units / 2;
+      }
+    }
     while (fmt == FMT_BF16 && p.uc > 1 && K / (nw * p.splits) < 2 * step * p.uc) p.uc /= 2;
     p.waves = nw;
     return p;
@@ -1688,28 +1714,29 @@ static hipError_t launch_rs(const SkinnyArgs& a, const SkinnyPlan& p, int x_bloc
 
 template <int RT, int EPI, int FMT, int UC>
 static hipError_t launch_ks(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t st) {
-  const dim3 grid(p.row_blocks * p.splits, 1);
+  if (p.split_from < 0 || p.split_from > p.row_blocks || (p.split_from > 0 && p.splits < 2)) return hipErrorInvalidValue;
+  const dim3 grid(p.split_from + (p.row_blocks - p.split_from) * p.splits, 1);
   if constexpr (FMT == FMT_INT4) {  // one or two 8-row groups (the plan never asks for more)
     if (p.nb == 1)
       launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
-                    st, a, p.splits);
+                    st, a, p.splits, p.split_from);
     else if (p.nb == 2)
       launch_kernel((ksplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 2),
-                    st, a, p.splits);
+                    st, a, p.splits, p.split_from);
     else
       return hipErrorInvalidValue;
   } else if (p.nb == 1) {
     launch_kernel((ksplit_gemm_kernel<RT, 1, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 1),
-                  st, a, p.splits);
+                  st, a, p.splits, p.split_from);
   } else if (p.nb == 2) {
     launch_kernel((ksplit_gemm_kernel<RT, 2, EPI, FMT, UC>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 2),
-                  st, a, p.splits);
+                  st, a, p.splits, p.split_from);
   } else if (p.nb == 4) {
     launch_kernel((ksplit_gemm_kernel<RT, 4, EPI, FMT, (UC > 2 ? 2 : UC)>), grid, dim3(64 * p.waves),
-                  ksplit_lds(p.waves, RT, 4), st, a, p.splits);
+                  ksplit_lds(p.waves, RT, 4), st, a, p.splits, p.split_from);
   } else if (p.nb == 8) {
     launch_kernel((ksplit_gemm_kernel<RT, 8, EPI, FMT, 1>), grid, dim3(64 * p.waves), ksplit_lds(p.waves, RT, 8),
-                  st, a, p.splits);
+                  st, a, p.splits, p.split_from);
   } else {
     return hipErrorInvalidValue;
   }

@@ -79,6 +79,7 @@ struct SkinnyArgs {
 //    L2); K split over `splits` workgroups; decode steps of 9..64 rows.
 struct SkinnyPlan {
   int kind, nb, rt, uc, row_blocks, splits, kc, waves;
+  int split_from;  // k split: tiles below take one workgroup (the whole K), the rest `splits` each
 };
 
 bool skinny_shape_ok(int fmt, int K);
