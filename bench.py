@@ -152,8 +152,8 @@ def main():
         if getattr(args, k) is None:
             setattr(args, k, wl[k])
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (each GPU would run its own "
-              "independent engine; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (data parallel: each GPU "
+              "would run its own independent engine over its own sequences). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
